@@ -1,0 +1,313 @@
+/*
+ * decoprune.h — C ABI of libdecoprune, the history-KV compaction path of
+ * DeCoPrune for autoregressive chunked video diffusion, on one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Source of the method.  Citations name the web page
+ *   "DeCoPrune이 디노이징 불일치로 비디오 KV 캐시를 85% 줄인다"
+ *   (onedev.kr/papers/726), called "the DeCoPrune page" below,
+ * and one of its sections:
+ *   무엇인가 (what it is), 어떻게 동작하나 (how it works),
+ *   무엇과 다른가 (how it differs), 어떻게 쓰나 (how to use it),
+ *   전제와 한계 (premises and limits).
+ *
+ * The path, one prune step:
+ *   1. dp_score_mask    per-token discrepancy l = (1/d)||x0_hat(tau*) - x_final||^2
+ *                       and the threshold mask with sink/window protection;
+ *   2. dp_compact_index ascending list of kept token rows;
+ *   3. dp_gather_kv     physical gather K[m], V[m] of every layer into a shorter
+ *                       dense cache (optionally re-rotating K while copying);
+ *   4. dp_rope_reindex  in-place RoPE temporal re-indexing of retained keys,
+ *                       t~ = q0 - g(q0 - t).
+ * plus the head-specialised ragged variant (DeCoPrune-HS, dp_hs_*) and the
+ * pruning-ratio counter (dp_pr_*).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers documented "device" are HIP device pointers on the current
+ *     device; "host" pointers are read before the call returns.
+ *   - stream is a hipStream_t passed as void*; NULL is the null stream.  Every
+ *     compute call only enqueues work on that stream and returns; results are
+ *     visible to later work on the same stream.  No call synchronises the
+ *     device, allocates memory, or keeps state between calls, except the
+ *     thread-local error text of dp_last_error().
+ *   - The caller owns every buffer.  Scratch memory comes from a caller
+ *     workspace sized by the matching *_workspace_bytes() function.
+ *   - All argument checks run on the host before the first HIP call.  A failed
+ *     check returns DP_EINVAL / DP_EALIGN / DP_ERANGE / DP_EUNSUPPORTED and
+ *     enqueues nothing.  A failed launch returns DP_EHIP.  dp_last_error()
+ *     then describes the failure.  No C++ exception crosses this boundary.
+ *   - Conditions only the device can see (a kept count above a destination
+ *     capacity) are clamped on the device and reported by writing
+ *     DP_ECAPACITY to the optional device word dev_error.
+ *   - Token rows are indexed with int32 (seq_len < 2^31); element offsets and
+ *     ragged offsets are 64-bit.
+ */
+#ifndef DECOPRUNE_H
+#define DECOPRUNE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DP_ABI_VERSION 1
+
+typedef enum {
+  DP_OK = 0,
+  DP_EINVAL = 1,        /* null pointer, bad size or inconsistent ranges       */
+  DP_EALIGN = 2,        /* pointer or row size not aligned as required          */
+  DP_ERANGE = 3,        /* size beyond a documented limit                       */
+  DP_ECAPACITY = 4,     /* device-side only: more kept rows than capacity       */
+  DP_EHIP = 5,          /* a HIP launch or runtime call failed                  */
+  DP_EUNSUPPORTED = 6   /* valid request outside what this build implements    */
+} dp_status;
+
+typedef enum { DP_F32 = 0, DP_BF16 = 1 } dp_dtype;
+
+/* DP_MODE_SCORE: scored rows keep by the threshold test; rows that are neither
+ *   sink, window nor scored (history compacted by earlier steps) are kept.
+ * DP_MODE_STREAMING: only sink and window rows are kept (the Streaming policy
+ *   the HS variant gives its static heads) [DeCoPrune page, 무엇과 다른가]. */
+typedef enum { DP_MODE_SCORE = 0, DP_MODE_STREAMING = 1 } dp_mode;
+
+int         dp_abi_version(void);
+const char* dp_status_str(int status);
+/* Text of the last non-OK return on the calling thread ("" if none). */
+const char* dp_last_error(void);
+
+/* ------------------------------------------------------------------------- *
+ * 1. Score and mask            [DeCoPrune page, 어떻게 동작하나]
+ *
+ * The page scores each token of a freshly generated chunk by the mean squared
+ * gap between the clean prediction recorded at the probe step tau* and the
+ * final denoised output, thresholds it with gamma into a binary mask that
+ * every layer shares, keeps the high-discrepancy tokens, always keeps the sink
+ * chunk and keeps the w most recent chunks dense.
+ *
+ * Rows of the cache, t in [0, seq_len):
+ *   [0, sink_len)                         sink: keep = 1
+ *   [scored_begin, scored_begin+n_scored) scored: keep = (l >= gamma),
+ *                                         or !(l >= gamma) when reversed
+ *                                         (the reversed-criterion ablation of
+ *                                         [DeCoPrune page, 전제와 한계]);
+ *                                         keep = 0 in DP_MODE_STREAMING
+ *   [seq_len-window_len, seq_len)         window: keep = 1
+ *   any other row                         keep = 1 (SCORE) / 0 (STREAMING)
+ * Requires sink_len <= scored_begin and
+ * scored_begin + n_scored <= seq_len - window_len.
+ * A NaN score fails "l >= gamma", so the reversed mask is the exact complement.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int64_t seq_len;       /* T rows in the cache, 1 <= T < 2^31            */
+  int64_t sink_len;      /* rows [0, sink_len) always kept                */
+  int64_t window_len;    /* rows [T - window_len, T) always kept          */
+  int64_t scored_begin;  /* first scored row                              */
+  int64_t n_scored;      /* number of scored rows (may be 0)              */
+  float   gamma;         /* threshold, keep iff l >= gamma                */
+  int32_t reversed;      /* 0 or 1                                        */
+  int32_t mode;          /* dp_mode                                       */
+  int32_t reserved;      /* must be 0                                     */
+} dp_mask_policy;
+
+/* x0_hat, x_final: device fp32 [n_scored][row_stride]; row i is cache row
+ *   scored_begin + i, channels [0, d) are used.  May be NULL when n_scored is
+ *   0 or mode is DP_MODE_STREAMING (then not read).  4-byte aligned.
+ * d: 1..256.  row_stride >= d (in floats).
+ * ell_out: device fp32 [n_scored] or NULL; receives l of every scored row.
+ * keep_out: device uint8 [seq_len], receives 0/1 for every row.
+ * l is evaluated in fp32: e_c = x0_hat - x_final, q_c = e_c*e_c (no fused
+ * multiply-add), q padded with +0 to the next power of two P >= d and summed
+ * by the pairwise tree q_c += q_{c+h} for h = P/2, P/4, ..., 1; then
+ * l = (float)((double)q_0 / d). */
+dp_status dp_score_mask(const float* x0_hat, const float* x_final, int32_t d,
+                        int64_t row_stride, const dp_mask_policy* policy,
+                        float* ell_out, uint8_t* keep_out, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * 2. Kept-index list           [DeCoPrune page, 어떻게 동작하나]
+ *
+ * idx_out[j] is the j-th row t (ascending) with keep[t] != 0, so that the
+ * gathered cache K[m], V[m] keeps the original token order.  *n_kept (device
+ * int64) receives the count.  When row_frame_src/row_frame_dst are both
+ * non-NULL, row_frame_dst[j] = row_frame_src[idx_out[j]] (the latent frame of
+ * each kept row, used by the RoPE re-index).
+ * keep: device uint8 [seq_len]; idx_out: device int32, capacity seq_len;
+ * workspace: device, >= dp_compact_workspace_bytes(seq_len) bytes, 4-aligned.
+ * Two launches, no host synchronisation.
+ * ------------------------------------------------------------------------- */
+size_t    dp_compact_workspace_bytes(int64_t seq_len);
+dp_status dp_compact_index(const uint8_t* keep, int64_t seq_len, int32_t* idx_out,
+                           int64_t* n_kept, const int32_t* row_frame_src,
+                           int32_t* row_frame_dst, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * RoPE temporal re-index parameters   [DeCoPrune page, 무엇과 다른가]
+ *
+ * The page moves the temporal coordinate of old context keys to
+ * t~ = q0 - g(q0 - t), where g leaves recent offsets unchanged and compresses
+ * older ones linearly; only the temporal phase of the keys changes.  Readings
+ * used here: positions are latent-frame indices; q0 is the first frame of the
+ * chunk about to be generated; g(D) = D for D <= knee and
+ * knee + (D - knee) * inv_factor otherwise (continuous at the knee).
+ * A key row carries the phase p of its frame; it is rotated by
+ * theta_j * (t~ - p) on every temporal pair j, and p becomes t~.
+ *
+ * Temporal pairs are dims (2j, 2j+1) of each head row for
+ * j in [pair_begin, pair_begin + n_pairs); the standard RoPE rotation
+ * (a, b) -> (a cos - b sin, a sin + b cos) is applied in fp32 with
+ * cos/sin the fp32 roundings of the fp64 cos/sin of the fp32 angle
+ * theta_j * delta, products and sums rounded separately (no fused
+ * multiply-add), and the result stored back rounded to nearest even.
+ * Rows whose frame has delta == 0 are not written.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t      pair_begin;   /* first temporal pair                              */
+  int32_t      n_pairs;      /* pairs in the temporal block, >= 1               */
+  const float* theta;        /* device fp32 [n_pairs] angular frequencies       */
+  int32_t      n_frames;     /* frames described by frame_t/frame_phase, >= 1   */
+  int32_t      reserved;     /* must be 0                                        */
+  const float* frame_t;      /* device fp32 [n_frames] original index t        */
+  float*       frame_phase;  /* device fp32 [n_frames] phase p; set to t~      */
+  float        q0;           /* query origin (frames)                            */
+  float        knee;         /* offsets <= knee are left unchanged               */
+  float        inv_factor;   /* 1/c, the linear compression of older offsets     */
+} dp_rope;
+
+/* Workspace of a re-index (per-frame delta and cos/sin table). */
+size_t dp_rope_workspace_bytes(int32_t n_frames, int32_t n_pairs);
+
+/* ------------------------------------------------------------------------- *
+ * 3. Physical gather           [DeCoPrune page, 어떻게 동작하나]
+ *
+ * When a non-sink chunk leaves the dense window, every layer keeps only the
+ * selected entries, so the KV sequence really gets shorter.  For every layer
+ * l < n_layers and j < min(*n_kept, dst_capacity):
+ *   k_dst[l][j][:][:] = k_src[l][idx[j]][:][:]   (bit copy)
+ *   v_dst[l][j][:][:] = v_src[l][idx[j]][:][:]   (if v_src != NULL)
+ * All layers, K and V in one launch.  Caches are token-major
+ * [rows][n_heads][head_dim] of dtype, one device allocation per layer, given
+ * as device arrays of n_layers device pointers.  Each layer base is 16-byte
+ * aligned and n_heads*head_dim*elem_size is a multiple of 16.
+ * If *n_kept > dst_capacity the copy is clamped and *dev_error = DP_ECAPACITY.
+ * idx entries must lie in [0, src_rows) (as dp_compact_index produces).
+ * With fused_rope != NULL, K rows are re-rotated while copied (section 4);
+ * row_frame (device int32 [dst_capacity]) then gives the frame of gathered row
+ * j and workspace must hold dp_rope_workspace_bytes(); V is never rotated.
+ * Source and destination must not overlap.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* const* k_src;  /* device array [n_layers] of device layer bases  */
+  const void* const* v_src;  /* same, or NULL for a K-only gather               */
+  void* const*       k_dst;  /* device array [n_layers] of device layer bases  */
+  void* const*       v_dst;  /* NULL iff v_src is NULL                          */
+  int32_t n_layers;          /* >= 1                                            */
+  int32_t n_heads;           /* >= 1                                            */
+  int32_t head_dim;          /* >= 2, even                                      */
+  int32_t dtype;             /* dp_dtype                                        */
+  int64_t src_rows;          /* rows of each source layer                       */
+  int64_t dst_capacity;      /* rows of each destination layer                  */
+  int32_t* dev_error;        /* device int32 or NULL                            */
+} dp_kv;
+
+dp_status dp_gather_kv(const dp_kv* kv, const int32_t* idx, const int64_t* n_kept,
+                       const int32_t* row_frame, const dp_rope* fused_rope,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * 4. In-place RoPE re-index    [DeCoPrune page, 무엇과 다른가]
+ *
+ * Re-rotates, in place, the temporal pairs of every head of rows
+ * [0, min(rows_capacity, *n_rows)) of each layer k_layers[l]
+ * (token-major [rows][n_heads][head_dim]) as described above.  n_rows is a
+ * device int64 or NULL (then rows_capacity rows).  row_frame: device int32
+ * [rows_capacity], frame of each row, in [0, n_frames).  Each frame's
+ * phase is advanced once per call, so every retained row of a listed frame
+ * must be in the range re-indexed by this call.
+ * ------------------------------------------------------------------------- */
+dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_heads,
+                          int32_t head_dim, int32_t dtype, int64_t rows_capacity,
+                          const int64_t* n_rows, const int32_t* row_frame,
+                          const dp_rope* rope, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * 5. DeCoPrune-HS: head-specialised ragged cache   [DeCoPrune page, 무엇과 다른가]
+ *
+ * The page splits heads into dynamic heads, which follow the DeCoPrune mask,
+ * and static heads, which follow the Streaming policy (sink + recent window).
+ * Here every (layer, head) names a class c = head_class[l*n_heads + h] in
+ * [0, n_classes); class c keeps the rows of its own kept-index list
+ * class_idx[c] (length *class_len[c], produced by dp_compact_index from the
+ * class's mask).  Head (l, h) gets n_{l,h} = class_len[head_class[l,h]] rows.
+ *
+ * dp_hs_offsets: offsets[0] = 0, offsets[i+1] = offsets[i] + n_i over
+ *   i = l*n_heads + h in row-major order; offsets is device int64
+ *   [n_layers*n_heads + 1].  One launch.
+ * dp_hs_gather_kv: for each (l, h) and j < n_{l,h}:
+ *   k_out[offsets[l,h] + j][:] = k_src[l][class_idx[c][j]][h][:]
+ *   (and V).  Output is packed per head, [offsets[L*H]][head_dim].  Rows
+ *   beyond out_capacity are dropped and *dev_error = DP_ECAPACITY.
+ *   class_capacity (host int64 [n_classes]) bounds each class's list length
+ *   (sizes the grid; lists longer than it are clamped and flagged).
+ *   With fused_rope, K is re-rotated while copied; class_row_frame (device
+ *   array [n_classes] of device int32 lists) gives the frame of each listed row.
+ * dp_hs_rope_reindex: in-place re-index of a ragged K cache laid out as above.
+ * class_idx / class_row_frame are device arrays of n_classes device pointers;
+ * class_len is device int64 [n_classes].  n_classes <= DP_HS_MAX_CLASSES.
+ * ------------------------------------------------------------------------- */
+#define DP_HS_MAX_CLASSES 8
+
+typedef struct {
+  const void* const* k_src;  /* device array [n_layers], token-major layers     */
+  const void* const* v_src;  /* same, or NULL                                   */
+  void*   k_out;             /* device [out_capacity][head_dim]                 */
+  void*   v_out;             /* NULL iff v_src is NULL                          */
+  int32_t n_layers, n_heads, head_dim, dtype;
+  int64_t src_rows;          /* rows of each source layer                       */
+  int64_t out_capacity;      /* head-rows available in k_out / v_out            */
+  int32_t* dev_error;        /* device int32 or NULL                            */
+} dp_kv_hs;
+
+dp_status dp_hs_offsets(const uint8_t* head_class, int32_t n_layers, int32_t n_heads,
+                        const int64_t* class_len, int32_t n_classes, int64_t* offsets,
+                        void* stream);
+
+dp_status dp_hs_gather_kv(const dp_kv_hs* kv, const uint8_t* head_class,
+                          int32_t n_classes, const int32_t* const* class_idx,
+                          const int64_t* class_len, const int64_t* class_capacity,
+                          const int64_t* offsets, const int32_t* const* class_row_frame,
+                          const dp_rope* fused_rope, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+dp_status dp_hs_rope_reindex(void* k_ragged, int32_t n_layers, int32_t n_heads,
+                             int32_t head_dim, int32_t dtype, const uint8_t* head_class,
+                             int32_t n_classes, const int64_t* class_len,
+                             const int64_t* class_capacity, const int64_t* offsets,
+                             const int32_t* const* class_row_frame, const dp_rope* rope,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * 6. Pruning ratio             [DeCoPrune page, 어떻게 쓰나 and 전제와 한계]
+ *
+ * The page measures efficiency as the cumulative reduction, against FullKV,
+ * of the history KV positions attention can see, counted per chunk, layer and
+ * head; it is not a peak-memory or total-compute saving.  A counter adds, per
+ * step, the visible positions (sum over layers and heads of kept rows) and the
+ * FullKV positions (layers * heads * full history rows).
+ * PR = 1 - visible / full (0 when full is 0).  Host-only, no HIP call.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int64_t visible;
+  int64_t full;
+} dp_pr_counter;
+
+dp_status dp_pr_add(dp_pr_counter* acc, int64_t visible_positions, int64_t full_positions);
+double    dp_pr_value(const dp_pr_counter* acc);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DECOPRUNE_H */

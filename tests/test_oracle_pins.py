@@ -1,0 +1,372 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test checks one oracle step against a closed form, an invariant the
+DeCoPrune page states, a library routine, or brute force, chosen so that a
+plausible slip (a dropped term, a wrong sign, an off-by-one, a transposed
+index) fails at least one of them.  Page sections cited:
+[DeCoPrune page, 어떻게 동작하나] score, mask, gather;
+[DeCoPrune page, 무엇과 다른가] RoPE re-index, HS;
+[DeCoPrune page, 어떻게 쓰나] pruning ratio.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import dpsynth
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# --------------------------------------------------------------------------
+# Score: l = (1/d) ||x0_hat - x_final||^2
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [1, 2, 3, 5, 12, 16, 48, 64, 100, 256])
+def test_score_equal_inputs_is_positive_zero(d):
+    x = np.random.default_rng(d).standard_normal((7, d)).astype(np.float32)
+    ell = oracle.score_f32(x, x.copy())
+    assert np.all(ell == 0) and not np.any(np.signbit(ell))
+
+
+@pytest.mark.parametrize("d", [1, 3, 16, 48, 64, 200])
+def test_score_single_channel_closed_form(d):
+    # one nonzero channel at every position c: l = RN32(e*e) / d
+    rng = np.random.default_rng(1)
+    for c in range(d):
+        e = np.float32(rng.uniform(0.1, 3.0))
+        a = np.zeros((1, d), np.float32)
+        a[0, c] = e
+        b = np.zeros((1, d), np.float32)
+        want = np.float32(float(np.float32(e * e)) / d)
+        assert oracle.score_f32(a, b)[0] == want, c
+
+
+@pytest.mark.parametrize("d", [4, 5, 12, 16, 48, 64, 100, 256])
+def test_score_integer_inputs_exact(d):
+    # small integers: every square and partial sum is exact in fp32, so the
+    # result is the exact rational sum/d rounded once to fp32
+    rng = np.random.default_rng(d + 100)
+    a = rng.integers(-20, 21, size=(50, d)).astype(np.float32)
+    b = rng.integers(-20, 21, size=(50, d)).astype(np.float32)
+    ell = oracle.score_f32(a, b)
+    for i in range(50):
+        s = sum(int(x) ** 2 for x in (a[i].astype(np.int64) - b[i].astype(np.int64)))
+        assert ell[i] == np.float32(Fraction(s, d).numerator / Fraction(s, d).denominator), i
+
+
+def test_score_row_stride_reads_only_d_channels():
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((9, 40)).astype(np.float32)
+    b = rng.standard_normal((9, 40)).astype(np.float32)
+    full = oracle.score_f32(a[:, :24].copy(), b[:, :24].copy())
+    strided = oracle.score_f32(a, b, d=24)
+    assert np.array_equal(full, strided)
+
+
+@pytest.mark.parametrize("d", [16, 48, 64, 256])
+def test_score_f32_within_pairwise_error_bound_of_f64(d):
+    rng = np.random.default_rng(d)
+    x0 = rng.standard_normal((4000, d)).astype(np.float32)
+    xf = (x0 + rng.uniform(0.01, 2.0, (4000, 1)) * rng.standard_normal((4000, d))).astype(np.float32)
+    l32 = oracle.score_f32(x0, xf).astype(np.float64)
+    e = x0.astype(np.float64) - xf.astype(np.float64)
+    l64 = (e * e).sum(axis=1) / d           # brute force, float64 (numpy)
+    # pairwise summation: |err| <= (log2 P + 3) u * sum|q|, u = 2^-24
+    P = 1 << (d - 1).bit_length()
+    bound = (np.log2(P) + 3) * 2.0 ** -24 * l64
+    assert np.all(np.abs(l32 - l64) <= bound + 1e-45)
+    assert np.allclose(oracle.score_f64(x0, xf), l64, rtol=1e-14, atol=0)
+
+
+def test_score_mean_is_sigma_squared_for_non_power_of_two_d():
+    # E[l] = sigma^2 when x0_hat = x_final + sigma N(0,1): dividing by the
+    # padded width instead of d, or dropping channels, would miss by >20%.
+    d, n, sigma = 48, 40000, 0.5
+    rng = np.random.default_rng(7)
+    xf = rng.standard_normal((n, d)).astype(np.float32)
+    x0 = (xf + sigma * rng.standard_normal((n, d))).astype(np.float32)
+    m = oracle.score_f32(x0, xf).astype(np.float64).mean()
+    assert abs(m - sigma ** 2) < 0.01 * sigma ** 2
+
+
+# --------------------------------------------------------------------------
+# Mask
+# --------------------------------------------------------------------------
+def _policy_rows(T=600, sink=64, window=128, sb=64, ns=300):
+    return dict(seq_len=T, sink_len=sink, window_len=window, scored_begin=sb, n_scored=ns)
+
+
+def test_mask_gamma_zero_keeps_everything():
+    rng = np.random.default_rng(0)
+    ell = np.abs(rng.standard_normal(300)).astype(np.float32)
+    ell[::7] = 0.0
+    keep = oracle.mask(ell, gamma=0.0, **_policy_rows())
+    assert keep.dtype == np.uint8 and np.all(keep == 1)
+
+
+def test_mask_reversed_is_complement_on_scored_rows():
+    rng = np.random.default_rng(1)
+    ell = np.abs(rng.standard_normal(300)).astype(np.float32) * 0.2
+    ell[5] = np.nan
+    p = _policy_rows()
+    a = oracle.mask(ell, gamma=0.1, **p)
+    b = oracle.mask(ell, gamma=0.1, reversed=True, **p)
+    s = slice(64, 364)
+    assert np.array_equal(a[s] ^ b[s], np.ones(300, np.uint8))
+    outside = np.r_[0:64, 364:600]
+    assert np.array_equal(a[outside], b[outside])
+    assert a[64 + 5] == 0 and b[64 + 5] == 1        # NaN: dropped, reversed keeps it
+
+
+def test_mask_threshold_tie_and_count():
+    g = np.float32(0.1)
+    ell = np.array([g, np.nextafter(g, np.float32(0)), np.nextafter(g, np.float32(1)), 0, np.inf],
+                   np.float32)
+    keep = oracle.mask(ell, seq_len=5, sink_len=0, window_len=0, scored_begin=0, n_scored=5,
+                       gamma=g)
+    assert keep.tolist() == [1, 0, 1, 0, 1]
+    rng = np.random.default_rng(3)
+    ell = (rng.random(300) * 0.2).astype(np.float32)
+    keep = oracle.mask(ell, gamma=0.1, **_policy_rows())
+    assert keep[64:364].sum() == np.count_nonzero(ell >= np.float32(0.1))
+
+
+def test_mask_sink_window_and_history_rows():
+    rng = np.random.default_rng(2)
+    ell = np.zeros(200, np.float32)          # nothing passes gamma
+    p = dict(seq_len=1000, sink_len=100, window_len=300, scored_begin=400, n_scored=200)
+    keep = oracle.mask(ell, gamma=0.1, **p)
+    assert np.all(keep[:100] == 1) and np.all(keep[700:] == 1)
+    assert np.all(keep[400:600] == 0)
+    assert np.all(keep[100:400] == 1) and np.all(keep[600:700] == 1)   # earlier history kept
+    st = oracle.mask(None, gamma=0.1, streaming=True, **p)
+    assert np.array_equal(st, np.r_[np.ones(100), np.zeros(600), np.ones(300)].astype(np.uint8))
+    # gamma = +inf with the whole middle scored is the streaming mask
+    q = dict(seq_len=1000, sink_len=100, window_len=300, scored_begin=100, n_scored=600)
+    ell = rng.random(600).astype(np.float32)
+    assert np.array_equal(oracle.mask(ell, gamma=np.inf, **q),
+                          oracle.mask(None, gamma=0.1, streaming=True, **q))
+
+
+# --------------------------------------------------------------------------
+# Compaction and gather
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,rate", [(0, 0.5), (1, 1.0), (1, 0.0), (1000, 0.0), (1000, 1.0),
+                                    (4097, 0.15), (70001, 0.5)])
+def test_compact_is_flatnonzero(T, rate):
+    keep = (np.random.default_rng(T).random(T) < rate).astype(np.uint8)
+    idx = oracle.compact(keep)
+    assert idx.dtype == np.int32
+    assert np.array_equal(idx, np.flatnonzero(keep))
+    assert idx.shape[0] == int(keep.sum())
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.uint16, np.int8])
+def test_gather_is_numpy_take(dtype):
+    rng = np.random.default_rng(4)
+    src = rng.integers(0, 2 ** 8 if dtype == np.int8 else 2 ** 15, size=(3, 50, 2, 8)).astype(dtype)
+    keep = (rng.random(50) < 0.4).astype(np.uint8)
+    keep[:5] = 1
+    idx = np.flatnonzero(keep)
+    out = oracle.gather(src, idx)
+    assert np.array_equal(out.view(np.uint8), src[:, idx].view(np.uint8))
+    assert np.array_equal(out[:, :5], src[:, :5])       # sink rows bit-identical
+    rf = rng.integers(0, 9, 50).astype(np.int32)
+    assert np.array_equal(oracle.gather_i32(rf, idx), rf[idx])
+
+
+# --------------------------------------------------------------------------
+# RoPE re-index
+# --------------------------------------------------------------------------
+def _t_new_exact(q0, knee, c, t):
+    D = Fraction(q0) - Fraction(t)
+    g = D if D <= knee else Fraction(knee) + (D - Fraction(knee)) / c
+    return Fraction(q0) - g
+
+
+def test_reindex_positions_tiny_closed_form():
+    # q0 = 8, knee 2, factor 4, frames 0..7: t~ = q0 - (knee + (D - knee)/4)
+    t = np.arange(8, dtype=np.float32)
+    delta, _, _, ph = oracle.rope_frames(t, t, 8.0, 2.0, 0.25, dpsynth.rope_theta(8))
+    assert ph.tolist() == [4.5, 4.75, 5.0, 5.25, 5.5, 5.75, 6.0, 7.0]
+    assert delta.tolist() == [4.5, 3.75, 3.0, 2.25, 1.5, 0.75, 0.0, 0.0]
+
+
+def test_reindex_positions_minute_history_closed_form():
+    # 240 frames, q0 = 240, knee 12 (the 3-chunk window), factor 8
+    t = np.arange(240, dtype=np.float32)
+    _, _, _, ph = oracle.rope_frames(t, t, 240.0, 12.0, 0.125, dpsynth.rope_theta(44))
+    want = [float(_t_new_exact(240, 12, 8, i)) for i in range(240)]
+    assert ph.tolist() == want
+    assert ph[0] == 199.5 and ph[227] == 227.875 and np.array_equal(ph[228:], t[228:])
+    assert np.all(np.diff(ph) > 0)        # order of keys is preserved
+
+
+def test_reindex_factor_one_is_identity():
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((30, 2, 64)).astype(np.float32)
+    rf = (np.arange(30) // 4).astype(np.int32)
+    t = np.arange(8, dtype=np.float32)
+    tab = oracle.rope_frames(t, t, 8.0, 2.0, 1.0, dpsynth.rope_theta(8))
+    assert np.all(tab[0] == 0)
+    k2 = oracle.rope_rows(k.copy(), rf, 0, tab)
+    assert np.array_equal(k2.view(np.uint32), k.view(np.uint32))
+
+
+def _rot_f64(k, rf, pair_begin, theta, delta):
+    """Independent float64 complex-multiplication form of the rotation."""
+    out = k.astype(np.float64).copy()
+    npairs = theta.shape[0]
+    lo, hi = 2 * pair_begin, 2 * (pair_begin + npairs)
+    z = out[..., lo:hi:2] + 1j * out[..., lo + 1:hi:2]
+    ang = delta[rf][:, None, None] * theta.astype(np.float64)[None, None, :]
+    z = z * np.exp(1j * ang)
+    out[..., lo:hi:2] = z.real
+    out[..., lo + 1:hi:2] = z.imag
+    return out
+
+
+@pytest.mark.parametrize("pair_begin,npairs", [(0, 8), (4, 12), (0, 32)])
+def test_reindex_rotation_matches_complex_multiplication(pair_begin, npairs):
+    rng = np.random.default_rng(npairs)
+    k = rng.standard_normal((64, 2, 64)).astype(np.float32)
+    rf = (np.arange(64) // 8).astype(np.int32)
+    theta = dpsynth.rope_theta(npairs)
+    t = np.arange(8, dtype=np.float32)
+    tab = oracle.rope_frames(t, t, 8.0, 2.0, 0.25, theta)
+    got = oracle.rope_rows(k.copy(), rf, pair_begin, tab).astype(np.float64)
+    want = _rot_f64(k, rf, pair_begin, theta, tab[0].astype(np.float64))
+    assert np.max(np.abs(got - want)) < 2e-6
+    # dims outside the temporal block are untouched bit for bit
+    mask = np.ones(64, bool)
+    mask[2 * pair_begin: 2 * (pair_begin + npairs)] = False
+    assert np.array_equal(got[..., mask], k.astype(np.float64)[..., mask])
+    # window frames (delta 0) are untouched bit for bit
+    assert np.array_equal(got[48:], k[48:].astype(np.float64))
+
+
+def test_reindex_relative_position_identity():
+    # After the re-index, a key of frame t scores against a query at q0 as if
+    # it sat at offset g(q0 - t): <R(q0) u, k'> = <R(g) u, v>, with k = R(t) v.
+    rng = np.random.default_rng(11)
+    npairs, q0, knee, c = 16, 20.0, 4.0, 3.0
+    theta = dpsynth.rope_theta(npairs)
+    th = theta.astype(np.float64)
+    frames = np.arange(20, dtype=np.float32)
+    v = rng.standard_normal((20, 2 * npairs))
+    vz = v[:, 0::2] + 1j * v[:, 1::2]
+    kz = vz * np.exp(1j * np.outer(frames.astype(np.float64), th))
+    k = np.empty((20, 1, 2 * npairs), np.float32)
+    k[:, 0, 0::2], k[:, 0, 1::2] = kz.real, kz.imag
+    tab = oracle.rope_frames(frames, frames, q0, knee, np.float32(1.0 / c), theta)
+    k2 = oracle.rope_rows(k.copy(), np.arange(20, dtype=np.int32), 0, tab).astype(np.float64)
+    k2z = k2[:, 0, 0::2] + 1j * k2[:, 0, 1::2]
+    u = rng.standard_normal(npairs) + 1j * rng.standard_normal(npairs)
+    for f in range(20):
+        g = float(Fraction(q0) - _t_new_exact(q0, knee, Fraction(c), f))
+        lhs = np.real(np.vdot(u * np.exp(1j * th * q0), k2z[f]))
+        rhs = np.real(np.vdot(u * np.exp(1j * th * g), vz[f]))
+        assert abs(lhs - rhs) < 1e-4 * (1 + abs(rhs)), f
+
+
+def test_reindex_rotations_compose():
+    # two re-index passes (q0 then q0') equal one pass to q0' from the start
+    rng = np.random.default_rng(12)
+    theta = dpsynth.rope_theta(44)
+    t = np.arange(24, dtype=np.float32)
+    k = rng.standard_normal((24, 3, 128)).astype(np.float32)
+    rf = np.arange(24, dtype=np.int32)
+    tab1 = oracle.rope_frames(t, t, 16.0, 12.0, 0.125, theta)
+    k1 = oracle.rope_rows(k.copy(), rf, 0, tab1)
+    tab2 = oracle.rope_frames(t, tab1[3], 24.0, 12.0, 0.125, theta)
+    k12 = oracle.rope_rows(k1, rf, 0, tab2)
+    tab3 = oracle.rope_frames(t, t, 24.0, 12.0, 0.125, theta)
+    k3 = oracle.rope_rows(k.copy(), rf, 0, tab3)
+    assert np.array_equal(tab2[3], tab3[3])
+    assert np.max(np.abs(k12 - k3)) < 1e-5
+
+
+def test_reindex_bf16_storage_rounds_to_nearest_even():
+    # torch's fp32 -> bf16 conversion (round to nearest, ties to even) is the
+    # reference; the sample is large enough to contain exact ties
+    import torch
+    rng = np.random.default_rng(13)
+    kb = torch.from_numpy(rng.standard_normal((6000, 2, 64)).astype(np.float32) * 3).to(torch.bfloat16)
+    k16 = kb.view(torch.int16).numpy().view(np.uint16).copy()
+    k32 = kb.to(torch.float32).numpy().copy()
+    rf = (np.arange(6000) // 1000).astype(np.int32)
+    t = np.arange(8, dtype=np.float32)
+    tab = oracle.rope_frames(t, t, 8.0, 2.0, 0.25, dpsynth.rope_theta(32))
+    r32 = oracle.rope_rows(k32, rf, 0, tab)
+    r16 = oracle.rope_rows(k16, rf, 0, tab)
+    ties = np.count_nonzero((r32.view(np.uint32) & 0xFFFF) == 0x8000)
+    assert ties > 0
+    want = torch.from_numpy(r32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(r16, want)
+
+
+# --------------------------------------------------------------------------
+# DeCoPrune-HS
+# --------------------------------------------------------------------------
+def test_hs_offsets_and_heads():
+    rng = np.random.default_rng(14)
+    L, H, T, D = 3, 6, 200, 8
+    src = rng.integers(0, 2 ** 15, size=(L, T, H, D)).astype(np.uint16)
+    cls = rng.integers(0, 2, size=(L, H)).astype(np.uint8)
+    ell = rng.random(120).astype(np.float32) * 0.2
+    p = dict(seq_len=T, sink_len=20, window_len=60, scored_begin=20, n_scored=120)
+    stat = oracle.compact(oracle.mask(None, gamma=0.1, streaming=True, **p))
+    dyn = oracle.compact(oracle.mask(ell, gamma=0.1, **p))
+    lens = np.array([len(stat), len(dyn)], np.int64)
+    off = oracle.hs_offsets(cls, lens)
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(lens[cls.ravel()])]))
+    out = np.zeros((off[-1], D), np.uint16)
+    for l in range(L):
+        oracle.hs_gather_layer(src[l], l, cls, [stat, dyn], off, out)
+    for l in range(L):
+        for h in range(H):
+            i = l * H + h
+            rows = stat if cls[l, h] == 0 else dyn
+            assert np.array_equal(out[off[i]:off[i + 1]], src[l][rows, h]), (l, h)
+
+
+# --------------------------------------------------------------------------
+# Pruning ratio
+# --------------------------------------------------------------------------
+def test_pruning_ratio_integer_identity():
+    assert oracle.pr(0, 10) == 1.0 and oracle.pr(10, 10) == 0.0 and oracle.pr(0, 0) == 0.0
+    L, H, T, n = 40, 40, 31200, 25896
+    assert oracle.pr(L * H * n, L * H * T) == 1 - n / T
+
+
+# --------------------------------------------------------------------------
+# Input generator sanity (not method arithmetic)
+# --------------------------------------------------------------------------
+def test_kv_table_is_standard_normal_quantiles():
+    t = dpsynth.kv_table("f32").view(np.float32)
+    assert np.array_equal(t, -t[::-1])
+    assert abs(t.mean()) < 1e-6 and abs(t.std() - 1) < 2e-3
+    b = dpsynth.kv_table("bf16")
+    assert b.dtype == np.uint16 and b.shape == (65536,)
+
+
+def test_kv_host_twin_is_deterministic_and_row_addressable():
+    a = dpsynth.kv_layer_host("bf16", 0, 1, 2, 50, 16)
+    b = dpsynth.kv_rows_host("bf16", 0, 1, 2, [7, 3], 50, 16)
+    assert np.array_equal(a[[7, 3]], b)
+    c = dpsynth.kv_rows_host("bf16", 0, 2, 2, [7, 3], 50, 16)
+    assert not np.array_equal(b, c)
+
+
+def test_reindex_trig_table_is_rounded_fp64_trig_of_fp32_angle():
+    # cos/sin entries are the fp32 roundings of the float64 cos/sin of the
+    # fp32 angle theta_j * delta_f (Python's math module as the reference)
+    import math
+    theta = dpsynth.rope_theta(44)
+    t = np.arange(240, dtype=np.float32)
+    delta, c, s, _ = oracle.rope_frames(t, t, 240.0, 12.0, 0.125, theta)
+    for f in range(0, 240, 7):
+        for j in range(44):
+            ang = float(np.float32(theta[j]) * np.float32(delta[f]))
+            assert c[f, j] == np.float32(math.cos(ang)) and s[f, j] == np.float32(math.sin(ang))

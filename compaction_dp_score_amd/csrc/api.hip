@@ -1,0 +1,334 @@
+// C ABI of libdecoprune: argument checks on the host, then stream-ordered
+// launches.  See include/decoprune.h for the contract of every entry point.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "dp_internal.h"
+
+namespace dp {
+
+size_t compact_ws_bytes(int64_t T);
+size_t rope_ws_bytes(int32_t n_frames, int32_t n_pairs);
+uint64_t hs_tiles(const int64_t* class_cap, int32_t n_classes);
+int hs_max_heads();
+
+namespace {
+thread_local char g_err[512] = "";
+constexpr int64_t kMaxRows = (int64_t)1 << 31;      // int32 row indices
+constexpr int64_t kMaxVec = (int64_t)1 << 31;       // 16-byte vectors per launch slab
+}  // namespace
+
+dp_status fail(dp_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dp_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DP_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return DP_OK;
+}
+
+namespace {
+
+void ok() { g_err[0] = '\0'; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+dp_status check_shape(int32_t n_layers, int32_t n_heads, int32_t head_dim, int32_t dtype,
+                      const char* who) {
+  if (n_layers < 1 || n_heads < 1 || head_dim < 2 || (head_dim & 1))
+    return fail(DP_EINVAL, "%s: need n_layers >= 1, n_heads >= 1, even head_dim >= 2", who);
+  if (dtype != DP_F32 && dtype != DP_BF16) return fail(DP_EINVAL, "%s: unknown dtype %d", who, dtype);
+  if (((int64_t)head_dim * elem_size(dtype)) % 16 != 0)
+    return fail(DP_EALIGN, "%s: head_dim * element size must be a multiple of 16 bytes", who);
+  return DP_OK;
+}
+
+dp_status check_rope(const dp_rope* r, int32_t head_dim, int32_t dtype, const void* ws,
+                     size_t ws_bytes, const char* who) {
+  if (r->n_pairs < 1 || r->pair_begin < 0 || r->n_frames < 1 || r->reserved != 0)
+    return fail(DP_EINVAL, "%s: rope needs n_pairs >= 1, pair_begin >= 0, n_frames >= 1", who);
+  if (2 * ((int64_t)r->pair_begin + r->n_pairs) > head_dim)
+    return fail(DP_ERANGE, "%s: temporal pairs [%d, %d) exceed head_dim/2 = %d", who,
+                r->pair_begin, r->pair_begin + r->n_pairs, head_dim / 2);
+  if ((2 * (int64_t)r->pair_begin * elem_size(dtype)) % 16 != 0)
+    return fail(DP_EALIGN, "%s: the temporal block must start on a 16-byte boundary", who);
+  if (!r->theta || !r->frame_t || !r->frame_phase)
+    return fail(DP_EINVAL, "%s: rope theta, frame_t and frame_phase are required", who);
+  if (!ws || !aligned(ws, 16))
+    return fail(ws ? DP_EALIGN : DP_EINVAL, "%s: rope workspace must be a 16-byte aligned pointer", who);
+  if (ws_bytes < rope_ws_bytes(r->n_frames, r->n_pairs))
+    return fail(DP_EINVAL, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes,
+                rope_ws_bytes(r->n_frames, r->n_pairs));
+  return DP_OK;
+}
+
+int64_t tv_count_of(const dp_rope* r, int32_t dtype) {
+  const int esz = elem_size(dtype);
+  const int64_t b = (2 * (int64_t)r->pair_begin * esz) / 16;
+  const int64_t e = (2 * ((int64_t)r->pair_begin + r->n_pairs) * esz + 15) / 16;
+  return e - b;
+}
+
+}  // namespace
+}  // namespace dp
+
+using namespace dp;
+
+extern "C" {
+
+int dp_abi_version(void) { return DP_ABI_VERSION; }
+
+const char* dp_status_str(int s) {
+  switch (s) {
+    case DP_OK: return "DP_OK";
+    case DP_EINVAL: return "DP_EINVAL";
+    case DP_EALIGN: return "DP_EALIGN";
+    case DP_ERANGE: return "DP_ERANGE";
+    case DP_ECAPACITY: return "DP_ECAPACITY";
+    case DP_EHIP: return "DP_EHIP";
+    case DP_EUNSUPPORTED: return "DP_EUNSUPPORTED";
+    default: return "DP_UNKNOWN";
+  }
+}
+
+const char* dp_last_error(void) { return g_err; }
+
+dp_status dp_score_mask(const float* x0_hat, const float* x_final, int32_t d,
+                        int64_t row_stride, const dp_mask_policy* p, float* ell_out,
+                        uint8_t* keep_out, void* stream) {
+  if (!p || !keep_out) return fail(DP_EINVAL, "dp_score_mask: policy and keep_out are required");
+  if (p->seq_len < 1 || p->seq_len >= kMaxRows)
+    return fail(DP_ERANGE, "dp_score_mask: seq_len %lld outside [1, 2^31)", (long long)p->seq_len);
+  if (p->sink_len < 0 || p->window_len < 0 || p->n_scored < 0 || p->scored_begin < p->sink_len ||
+      p->scored_begin + p->n_scored > p->seq_len - p->window_len)
+    return fail(DP_EINVAL,
+                "dp_score_mask: need 0 <= sink_len <= scored_begin and scored_begin + n_scored <= "
+                "seq_len - window_len");
+  if ((p->mode != DP_MODE_SCORE && p->mode != DP_MODE_STREAMING) ||
+      (p->reversed != 0 && p->reversed != 1) || p->reserved != 0)
+    return fail(DP_EINVAL, "dp_score_mask: mode, reversed or reserved out of range");
+  const bool scoring = p->mode == DP_MODE_SCORE && p->n_scored > 0;
+  if (scoring) {
+    if (!x0_hat || !x_final) return fail(DP_EINVAL, "dp_score_mask: x0_hat and x_final are required");
+    if (d < 1 || d > 256) return fail(DP_ERANGE, "dp_score_mask: d = %d outside [1, 256]", d);
+    if (row_stride < d) return fail(DP_EINVAL, "dp_score_mask: row_stride < d");
+    if (!aligned(x0_hat, 4) || !aligned(x_final, 4) || (ell_out && !aligned(ell_out, 4)))
+      return fail(DP_EALIGN, "dp_score_mask: float arrays must be 4-byte aligned");
+    if (row_stride > ((int64_t)1 << 40) / p->n_scored)
+      return fail(DP_ERANGE, "dp_score_mask: input too large");
+  }
+  (void)hipGetLastError();
+  dp_status st = launch_score_mask(x0_hat, x_final, d, row_stride, *p, scoring ? ell_out : nullptr,
+                                   keep_out, (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+size_t dp_compact_workspace_bytes(int64_t seq_len) {
+  return compact_ws_bytes(seq_len < 0 ? 0 : seq_len);
+}
+
+dp_status dp_compact_index(const uint8_t* keep, int64_t seq_len, int32_t* idx_out,
+                           int64_t* n_kept, const int32_t* row_frame_src,
+                           int32_t* row_frame_dst, void* ws, size_t ws_bytes, void* stream) {
+  if (seq_len < 0 || seq_len >= kMaxRows)
+    return fail(DP_ERANGE, "dp_compact_index: seq_len %lld outside [0, 2^31)", (long long)seq_len);
+  if ((seq_len > 0 && (!keep || !idx_out)) || !n_kept || !ws)
+    return fail(DP_EINVAL, "dp_compact_index: keep, idx_out, n_kept and workspace are required");
+  if ((row_frame_src == nullptr) != (row_frame_dst == nullptr))
+    return fail(DP_EINVAL, "dp_compact_index: row_frame_src and row_frame_dst go together");
+  if (!aligned(n_kept, 8) || !aligned(ws, 4) || (idx_out && !aligned(idx_out, 4)))
+    return fail(DP_EALIGN, "dp_compact_index: n_kept must be 8-byte, idx and workspace 4-byte aligned");
+  if (ws_bytes < compact_ws_bytes(seq_len))
+    return fail(DP_EINVAL, "dp_compact_index: workspace of %zu bytes < %zu needed", ws_bytes,
+                compact_ws_bytes(seq_len));
+  (void)hipGetLastError();
+  dp_status st = launch_compact(keep, seq_len, idx_out, n_kept, row_frame_src, row_frame_dst,
+                                (int32_t*)ws, (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+size_t dp_rope_workspace_bytes(int32_t n_frames, int32_t n_pairs) {
+  if (n_frames < 0 || n_pairs < 0) return 0;
+  return rope_ws_bytes(n_frames, n_pairs);
+}
+
+dp_status dp_gather_kv(const dp_kv* kv, const int32_t* idx, const int64_t* n_kept,
+                       const int32_t* row_frame, const dp_rope* rope, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!kv || !idx || !n_kept) return fail(DP_EINVAL, "dp_gather_kv: kv, idx and n_kept are required");
+  dp_status st = check_shape(kv->n_layers, kv->n_heads, kv->head_dim, kv->dtype, "dp_gather_kv");
+  if (st != DP_OK) return st;
+  if (!kv->k_src || !kv->k_dst || ((kv->v_src == nullptr) != (kv->v_dst == nullptr)))
+    return fail(DP_EINVAL, "dp_gather_kv: k_src/k_dst required, v_src/v_dst go together");
+  if (kv->src_rows < 0 || kv->src_rows >= kMaxRows || kv->dst_capacity < 0)
+    return fail(DP_ERANGE, "dp_gather_kv: src_rows outside [0, 2^31) or negative capacity");
+  const int64_t rv = (int64_t)kv->n_heads * kv->head_dim * elem_size(kv->dtype) / 16;
+  if (kv->dst_capacity > kMaxVec / rv)
+    return fail(DP_ERANGE, "dp_gather_kv: a destination layer over 32 GiB is not supported");
+  const int n_kv = kv->v_src ? 2 : 1;
+  if ((int64_t)kv->n_layers * n_kv > 65535) return fail(DP_ERANGE, "dp_gather_kv: too many layers");
+  if (!aligned(n_kept, 8) || (kv->dev_error && !aligned(kv->dev_error, 4)))
+    return fail(DP_EALIGN, "dp_gather_kv: n_kept must be 8-byte aligned");
+  if (rope) {
+    st = check_rope(rope, kv->head_dim, kv->dtype, ws, ws_bytes, "dp_gather_kv");
+    if (st != DP_OK) return st;
+    if (!row_frame) return fail(DP_EINVAL, "dp_gather_kv: fused re-index needs row_frame");
+  }
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  RopeView view{};
+  if (rope) {
+    st = launch_rope_prepare(*rope, ws, &view, kv->dtype, kv->head_dim, s);
+    if (st != DP_OK) return st;
+  }
+  st = launch_gather(*kv, idx, n_kept, row_frame, rope ? &view : nullptr, s);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_heads,
+                          int32_t head_dim, int32_t dtype, int64_t rows_capacity,
+                          const int64_t* n_rows, const int32_t* row_frame, const dp_rope* rope,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!k_layers || !row_frame || !rope)
+    return fail(DP_EINVAL, "dp_rope_reindex: k_layers, row_frame and rope are required");
+  dp_status st = check_shape(n_layers, n_heads, head_dim, dtype, "dp_rope_reindex");
+  if (st != DP_OK) return st;
+  st = check_rope(rope, head_dim, dtype, ws, ws_bytes, "dp_rope_reindex");
+  if (st != DP_OK) return st;
+  if (n_layers > 65535) return fail(DP_ERANGE, "dp_rope_reindex: too many layers");
+  if (rows_capacity < 0 || rows_capacity >= kMaxRows ||
+      rows_capacity * n_heads * tv_count_of(rope, dtype) >= kMaxVec)
+    return fail(DP_ERANGE, "dp_rope_reindex: rows_capacity out of range");
+  if (n_rows && !aligned(n_rows, 8)) return fail(DP_EALIGN, "dp_rope_reindex: n_rows alignment");
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  RopeView view{};
+  st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, s);
+  if (st != DP_OK) return st;
+  st = launch_reindex(k_layers, n_layers, n_heads, head_dim, dtype, rows_capacity, n_rows,
+                      row_frame, view, s);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+dp_status dp_hs_offsets(const uint8_t* head_class, int32_t n_layers, int32_t n_heads,
+                        const int64_t* class_len, int32_t n_classes, int64_t* offsets,
+                        void* stream) {
+  if (!head_class || !class_len || !offsets)
+    return fail(DP_EINVAL, "dp_hs_offsets: head_class, class_len and offsets are required");
+  if (n_layers < 1 || n_heads < 1 || n_classes < 1 || n_classes > DP_HS_MAX_CLASSES)
+    return fail(DP_EINVAL, "dp_hs_offsets: need n_layers, n_heads >= 1 and 1 <= n_classes <= %d",
+                DP_HS_MAX_CLASSES);
+  if ((int64_t)n_layers * n_heads >= kMaxRows) return fail(DP_ERANGE, "dp_hs_offsets: too many heads");
+  if (!aligned(class_len, 8) || !aligned(offsets, 8))
+    return fail(DP_EALIGN, "dp_hs_offsets: int64 arrays must be 8-byte aligned");
+  (void)hipGetLastError();
+  dp_status st = launch_hs_offsets(head_class, n_layers, n_heads, class_len, n_classes, offsets,
+                                   (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+static dp_status check_hs_common(int32_t n_layers, int32_t n_heads, int32_t head_dim,
+                                 int32_t dtype, const uint8_t* head_class, int32_t n_classes,
+                                 const int64_t* class_len, const int64_t* class_cap,
+                                 const int64_t* offsets, const char* who) {
+  dp_status st = check_shape(n_layers, n_heads, head_dim, dtype, who);
+  if (st != DP_OK) return st;
+  if (n_heads > hs_max_heads()) return fail(DP_ERANGE, "%s: n_heads > %d", who, hs_max_heads());
+  if (!head_class || !class_len || !class_cap || !offsets)
+    return fail(DP_EINVAL, "%s: head_class, class_len, class_capacity and offsets are required", who);
+  if (n_classes < 1 || n_classes > DP_HS_MAX_CLASSES)
+    return fail(DP_EINVAL, "%s: n_classes outside [1, %d]", who, DP_HS_MAX_CLASSES);
+  for (int c = 0; c < n_classes; ++c)
+    if (class_cap[c] < 0 || class_cap[c] >= kMaxRows)
+      return fail(DP_ERANGE, "%s: class_capacity[%d] outside [0, 2^31)", who, c);
+  if (hs_tiles(class_cap, n_classes) >= ((uint64_t)1 << 31))
+    return fail(DP_ERANGE, "%s: class capacities too large", who);
+  if (n_layers > 65535 / 2) return fail(DP_ERANGE, "%s: too many layers", who);
+  return DP_OK;
+}
+
+dp_status dp_hs_gather_kv(const dp_kv_hs* kv, const uint8_t* head_class, int32_t n_classes,
+                          const int32_t* const* class_idx, const int64_t* class_len,
+                          const int64_t* class_cap, const int64_t* offsets,
+                          const int32_t* const* class_rf, const dp_rope* rope, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!kv || !class_idx) return fail(DP_EINVAL, "dp_hs_gather_kv: kv and class_idx are required");
+  dp_status st = check_hs_common(kv->n_layers, kv->n_heads, kv->head_dim, kv->dtype, head_class,
+                                 n_classes, class_len, class_cap, offsets, "dp_hs_gather_kv");
+  if (st != DP_OK) return st;
+  if (!kv->k_src || !kv->k_out || ((kv->v_src == nullptr) != (kv->v_out == nullptr)))
+    return fail(DP_EINVAL, "dp_hs_gather_kv: k_src/k_out required, v_src/v_out go together");
+  if (!aligned(kv->k_out, 16) || (kv->v_out && !aligned(kv->v_out, 16)))
+    return fail(DP_EALIGN, "dp_hs_gather_kv: outputs must be 16-byte aligned");
+  if (kv->src_rows < 0 || kv->src_rows >= kMaxRows || kv->out_capacity < 0)
+    return fail(DP_ERANGE, "dp_hs_gather_kv: src_rows or out_capacity out of range");
+  if (rope) {
+    st = check_rope(rope, kv->head_dim, kv->dtype, ws, ws_bytes, "dp_hs_gather_kv");
+    if (st != DP_OK) return st;
+    if (!class_rf) return fail(DP_EINVAL, "dp_hs_gather_kv: fused re-index needs class_row_frame");
+  }
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  RopeView view{};
+  if (rope) {
+    st = launch_rope_prepare(*rope, ws, &view, kv->dtype, kv->head_dim, s);
+    if (st != DP_OK) return st;
+  }
+  st = launch_hs_gather(*kv, head_class, n_classes, class_idx, class_len, class_cap, offsets,
+                        class_rf, rope ? &view : nullptr, s);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layers,
+                             int32_t n_heads, int32_t head_dim, int32_t dtype, const uint8_t* head_class, int32_t n_classes,
+                             const int64_t* class_len, const int64_t* class_cap,
+                             const int64_t* offsets, const int32_t* const* class_rf,
+                             const dp_rope* rope, void* ws, size_t ws_bytes, void* stream) {
+  if (!k_ragged || !class_rf || !rope)
+    return fail(DP_EINVAL, "dp_hs_rope_reindex: k_ragged, class_row_frame and rope are required");
+  dp_status st = check_hs_common(n_layers, n_heads, head_dim, dtype, head_class, n_classes,
+                                 class_len, class_cap, offsets, "dp_hs_rope_reindex");
+  if (st != DP_OK) return st;
+  if (!aligned(k_ragged, 16)) return fail(DP_EALIGN, "dp_hs_rope_reindex: k_ragged alignment");
+  if (k_capacity < 0) return fail(DP_ERANGE, "dp_hs_rope_reindex: negative k_capacity");
+  st = check_rope(rope, head_dim, dtype, ws, ws_bytes, "dp_hs_rope_reindex");
+  if (st != DP_OK) return st;
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  RopeView view{};
+  st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, s);
+  if (st != DP_OK) return st;
+  st = launch_hs_reindex(k_ragged, k_capacity, n_layers, n_heads, head_dim, dtype, head_class, n_classes,
+                         class_len, class_cap, offsets, class_rf, view, s);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+dp_status dp_pr_add(dp_pr_counter* acc, int64_t visible, int64_t full) {
+  if (!acc) return fail(DP_EINVAL, "dp_pr_add: counter is required");
+  if (visible < 0 || full < 0 || visible > full)
+    return fail(DP_EINVAL, "dp_pr_add: need 0 <= visible <= full");
+  acc->visible += visible;
+  acc->full += full;
+  ok();
+  return DP_OK;
+}
+
+double dp_pr_value(const dp_pr_counter* acc) {
+  if (!acc || acc->full == 0) return 0.0;
+  return 1.0 - (double)acc->visible / (double)acc->full;
+}
+
+}  // extern "C"

@@ -254,7 +254,9 @@ dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_hea
  *   (sizes the grid; lists longer than it are clamped and flagged).
  *   With fused_rope, K is re-rotated while copied; class_row_frame (device
  *   array [n_classes] of device int32 lists) gives the frame of each listed row.
- * dp_hs_rope_reindex: in-place re-index of a ragged K cache laid out as above.
+ * dp_hs_rope_reindex: in-place re-index of a ragged K cache laid out as above;
+ *   k_capacity is the number of head rows in k_ragged (rows beyond it are
+ *   skipped).
  * class_idx / class_row_frame are device arrays of n_classes device pointers;
  * class_len is device int64 [n_classes].  n_classes <= DP_HS_MAX_CLASSES.
  * ------------------------------------------------------------------------- */
@@ -282,8 +284,9 @@ dp_status dp_hs_gather_kv(const dp_kv_hs* kv, const uint8_t* head_class,
                           const dp_rope* fused_rope, void* workspace,
                           size_t workspace_bytes, void* stream);
 
-dp_status dp_hs_rope_reindex(void* k_ragged, int32_t n_layers, int32_t n_heads,
-                             int32_t head_dim, int32_t dtype, const uint8_t* head_class,
+dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layers,
+                             int32_t n_heads, int32_t head_dim, int32_t dtype,
+                             const uint8_t* head_class,
                              int32_t n_classes, const int64_t* class_len,
                              const int64_t* class_capacity, const int64_t* offsets,
                              const int32_t* const* class_row_frame, const dp_rope* rope,

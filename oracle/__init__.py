@@ -214,3 +214,32 @@ def hs_gather_layer(src_layer, layer, head_class, class_lists, offsets, out):
 def pr(visible, full):
     """Pruning ratio 1 - visible/full [DeCoPrune page, 어떻게 쓰나]."""
     return lib().oracle_pr(int(visible), int(full))
+
+
+# --------------------------------------------------------------------------
+# One whole prune step, step by step in the page's order
+# --------------------------------------------------------------------------
+def prune_step(x0_hat, x_final, d, policy, k, v, row_frame=None, rope=None,
+               pair_begin=0):
+    """k, v: [L, T, H, D] (float32 or uint16 bf16 bits); policy: dict with
+    seq_len, sink_len, window_len, scored_begin, n_scored, gamma, reversed,
+    streaming.  rope: None or dict theta, frame_t, frame_phase, q0, knee,
+    inv_factor.  Returns dict ell, keep, idx, k, v, row_frame, tables."""
+    streaming = bool(policy.get("streaming", False))
+    ell = None
+    if not streaming and policy["n_scored"] > 0:
+        ell = score_f32(np.asarray(x0_hat)[:, :d], np.asarray(x_final)[:, :d], d)
+    keep = mask(ell, policy["seq_len"], policy["sink_len"], policy["window_len"],
+                policy["scored_begin"], policy["n_scored"], policy["gamma"],
+                policy.get("reversed", False), streaming)
+    idx = compact(keep)
+    k2 = gather(k, idx)
+    v2 = gather(v, idx) if v is not None else None
+    rf2 = gather_i32(row_frame, idx) if row_frame is not None else None
+    tables = None
+    if rope is not None:
+        tables = rope_frames(rope["frame_t"], rope["frame_phase"], rope["q0"], rope["knee"],
+                             rope["inv_factor"], rope["theta"])
+        for l in range(k2.shape[0]):
+            rope_rows(k2[l], rf2, pair_begin, tables)
+    return dict(ell=ell, keep=keep, idx=idx, k=k2, v=v2, row_frame=rf2, tables=tables)

@@ -1,0 +1,216 @@
+"""libdecoprune loads, exports every symbol of include/decoprune.h, and rejects
+bad arguments on the host before any HIP call (these tests never reach a
+launch, so they run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import compaction_dp_score_amd as dp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decoprune.h")
+
+FAKE = 0x10000          # a 64 KiB-aligned non-null address; never dereferenced here
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) == 14, names
+    lib = ctypes.CDLL(dp.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(dp.EXPORTED) == names
+
+
+def test_version_and_status_strings():
+    assert dp.dp_abi_version() == 1
+    assert dp.dp_status_str(dp.DP_OK) == "DP_OK"
+    assert dp.dp_status_str(dp.DP_ECAPACITY) == "DP_ECAPACITY"
+    assert dp.dp_status_str(99) == "DP_UNKNOWN"
+
+
+def test_struct_layouts_match_header(tmp_path):
+    # the ctypes mirrors have the size and field offsets gcc gives the header
+    structs = {"dp_mask_policy": dp.dp_mask_policy, "dp_rope": dp.dp_rope, "dp_kv": dp.dp_kv,
+               "dp_kv_hs": dp.dp_kv_hs, "dp_pr_counter": dp.dp_pr_counter}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "decoprune.h"', 'int main(void){']
+    for name, cls in structs.items():
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (name, name))
+        for f, _ in cls._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (name, f, name, f))
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)],
+                   check=True)
+    out = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                 check=True).stdout.splitlines())
+    for name, cls in structs.items():
+        assert int(out[name]) == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert int(out["%s.%s" % (name, f)]) == getattr(cls, f).offset, (name, f)
+
+
+def _status(fn, *args):
+    return getattr(dp, "_lib_" + fn)(*args)
+
+
+def _policy(**kw):
+    p = dict(seq_len=1000, sink_len=100, window_len=200, scored_begin=100, n_scored=300,
+             gamma=0.1)
+    p.update(kw)
+    return dp.make_policy(**p)
+
+
+@pytest.mark.parametrize("kw,d,stride,want", [
+    (dict(seq_len=0), 16, 16, dp.DP_ERANGE),
+    (dict(seq_len=1 << 31), 16, 16, dp.DP_ERANGE),
+    (dict(scored_begin=50), 16, 16, dp.DP_EINVAL),          # scored overlaps the sink
+    (dict(n_scored=800), 16, 16, dp.DP_EINVAL),             # scored overlaps the window
+    (dict(window_len=-1), 16, 16, dp.DP_EINVAL),
+    (dict(), 0, 16, dp.DP_ERANGE),
+    (dict(), 257, 300, dp.DP_ERANGE),
+    (dict(), 16, 8, dp.DP_EINVAL),
+])
+def test_score_mask_rejects(kw, d, stride, want):
+    p = _policy(**kw)
+    st = _status("score_mask", FAKE, FAKE, d, stride, ctypes.byref(p), None, FAKE, None)
+    assert st == want, dp.dp_last_error()
+    assert dp.dp_last_error()
+
+
+def test_score_mask_rejects_bad_mode_and_pointers():
+    p = _policy()
+    p.mode = 2
+    assert _status("score_mask", FAKE, FAKE, 16, 16, ctypes.byref(p), None, FAKE, None) == dp.DP_EINVAL
+    p = _policy()
+    assert _status("score_mask", None, FAKE, 16, 16, ctypes.byref(p), None, FAKE, None) == dp.DP_EINVAL
+    assert _status("score_mask", FAKE + 2, FAKE, 16, 16, ctypes.byref(p), None, FAKE, None) == dp.DP_EALIGN
+    assert _status("score_mask", FAKE, FAKE, 16, 16, None, None, FAKE, None) == dp.DP_EINVAL
+    with pytest.raises(dp.DPError) as e:
+        dp.dp_score_mask(None, None, 16, 16, _policy(scored_begin=0), None, None, stream=0)
+    assert e.value.status == dp.DP_EINVAL
+
+
+def test_compact_rejects():
+    need = dp.dp_compact_workspace_bytes(10000)
+    assert need >= 4 * 3
+    assert _status("compact", FAKE, 10000, FAKE, FAKE, None, None, FAKE, need - 1, None) == dp.DP_EINVAL
+    assert _status("compact", FAKE, -1, FAKE, FAKE, None, None, FAKE, need, None) == dp.DP_ERANGE
+    assert _status("compact", FAKE, 10000, FAKE, FAKE + 4, None, None, FAKE, need, None) == dp.DP_EALIGN
+    assert _status("compact", FAKE, 10000, FAKE, FAKE, FAKE, None, FAKE, need, None) == dp.DP_EINVAL
+    assert _status("compact", None, 10000, FAKE, FAKE, None, None, FAKE, need, None) == dp.DP_EINVAL
+
+
+def _kv(**kw):
+    kv = dp.dp_kv()
+    f = dict(k_src=FAKE, v_src=FAKE, k_dst=FAKE, v_dst=FAKE, n_layers=2, n_heads=4, head_dim=64,
+             dtype=dp.DP_BF16, src_rows=1000, dst_capacity=1000, dev_error=None)
+    f.update(kw)
+    for k, v in f.items():
+        setattr(kv, k, v)
+    return kv
+
+
+def _rope(**kw):
+    r = dp.dp_rope()
+    f = dict(pair_begin=0, n_pairs=8, theta=FAKE, n_frames=10, reserved=0, frame_t=FAKE,
+             frame_phase=FAKE, q0=10.0, knee=2.0, inv_factor=0.25)
+    f.update(kw)
+    for k, v in f.items():
+        setattr(r, k, v)
+    return r
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(head_dim=63), dp.DP_EINVAL),
+    (dict(head_dim=4), dp.DP_EALIGN),                    # 8-byte bf16 head rows
+    (dict(dtype=7), dp.DP_EINVAL),
+    (dict(v_dst=None), dp.DP_EINVAL),
+    (dict(k_src=None), dp.DP_EINVAL),
+    (dict(n_layers=0), dp.DP_EINVAL),
+    (dict(src_rows=1 << 31), dp.DP_ERANGE),
+    (dict(dst_capacity=1 << 40), dp.DP_ERANGE),
+    (dict(n_layers=40000), dp.DP_ERANGE),
+])
+def test_gather_rejects(kw, want):
+    kv = _kv(**kw)
+    assert _status("gather", ctypes.byref(kv), FAKE, FAKE, None, None, None, 0, None) == want
+
+
+@pytest.mark.parametrize("kw,ws,want", [
+    (dict(n_pairs=40), None, dp.DP_ERANGE),              # 2*40 > head_dim 64
+    (dict(pair_begin=2), None, dp.DP_EALIGN),            # bf16 block must start on 16 bytes
+    (dict(n_pairs=0), None, dp.DP_EINVAL),
+    (dict(theta=None), None, dp.DP_EINVAL),
+    (dict(), 8, dp.DP_EINVAL),                           # workspace too small
+    (dict(reserved=1), None, dp.DP_EINVAL),
+])
+def test_fused_rope_rejects(kw, ws, want):
+    kv = _kv()
+    r = _rope(**kw)
+    ws_bytes = dp.dp_rope_workspace_bytes(r.n_frames, max(r.n_pairs, 1)) if ws is None else ws
+    st = _status("gather", ctypes.byref(kv), FAKE, FAKE, FAKE, ctypes.byref(r), FAKE, ws_bytes, None)
+    assert st == want, dp.dp_last_error()
+
+
+def test_fused_rope_needs_row_frame_and_aligned_workspace():
+    kv, r = _kv(), _rope()
+    nb = dp.dp_rope_workspace_bytes(10, 8)
+    assert _status("gather", ctypes.byref(kv), FAKE, FAKE, None, ctypes.byref(r), FAKE, nb, None) == dp.DP_EINVAL
+    assert _status("gather", ctypes.byref(kv), FAKE, FAKE, FAKE, ctypes.byref(r), FAKE + 8, nb, None) == dp.DP_EALIGN
+
+
+def test_reindex_rejects():
+    r = _rope()
+    nb = dp.dp_rope_workspace_bytes(10, 8)
+    f = lambda *a: _status("reindex", *a)
+    assert f(None, 1, 4, 64, 1, 100, None, FAKE, ctypes.byref(r), FAKE, nb, None) == dp.DP_EINVAL
+    assert f(FAKE, 1, 4, 64, 1, -1, None, FAKE, ctypes.byref(r), FAKE, nb, None) == dp.DP_ERANGE
+    assert f(FAKE, 1, 4, 64, 1, 100, FAKE + 4, FAKE, ctypes.byref(r), FAKE, nb, None) == dp.DP_EALIGN
+    r2 = _rope(pair_begin=1)
+    assert f(FAKE, 1, 4, 64, 0, 100, None, FAKE, ctypes.byref(r2), FAKE, nb, None) == dp.DP_EALIGN
+
+
+def test_hs_rejects():
+    caps = (ctypes.c_int64 * 2)(10, 10)
+    assert _status("hs_offsets", FAKE, 2, 4, FAKE, 9, FAKE, None) == dp.DP_EINVAL
+    assert _status("hs_offsets", FAKE, 2, 4, FAKE + 4, 2, FAKE, None) == dp.DP_EALIGN
+    kv = dp.dp_kv_hs()
+    kv.k_src, kv.v_src, kv.k_out, kv.v_out = FAKE, FAKE, FAKE, FAKE
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = 2, 2000, 64, dp.DP_BF16
+    kv.src_rows, kv.out_capacity = 100, 100
+    assert _status("hs_gather", ctypes.byref(kv), FAKE, 2, FAKE, FAKE, caps, FAKE, None, None,
+                   None, 0, None) == dp.DP_ERANGE
+    kv.n_heads = 4
+    bad = (ctypes.c_int64 * 2)(10, -1)
+    assert _status("hs_gather", ctypes.byref(kv), FAKE, 2, FAKE, FAKE, bad, FAKE, None, None,
+                   None, 0, None) == dp.DP_ERANGE
+    kv.k_out = FAKE + 8
+    assert _status("hs_gather", ctypes.byref(kv), FAKE, 2, FAKE, FAKE, caps, FAKE, None, None,
+                   None, 0, None) == dp.DP_EALIGN
+    r = _rope()
+    assert _status("hs_reindex", FAKE, 100, 2, 4, 64, 1, FAKE, 2, FAKE, caps, FAKE, None,
+                   ctypes.byref(r), FAKE, 4096, None) == dp.DP_EINVAL
+
+
+def test_pruning_ratio_counter():
+    c = dp.dp_pr_counter()
+    assert dp.dp_pr_value(c) == 0.0
+    L, H, T, n = 40, 40, 31200, 25896
+    dp.dp_pr_add(c, L * H * n, L * H * T)
+    assert dp.dp_pr_value(c) == 1 - n / T
+    dp.dp_pr_add(c, 0, L * H * 6240)                 # a step that drops a whole chunk
+    assert dp.dp_pr_value(c) == 1 - (L * H * n) / (L * H * (T + 6240))
+    with pytest.raises(dp.DPError):
+        dp.dp_pr_add(c, 5, 4)

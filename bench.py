@@ -1,0 +1,319 @@
+"""Benchmark of one DeCoPrune prune step on one MI355X.
+
+Default workload ("eviction"): a single chunk-eviction step at the shape of
+the DeCoPrune page's setup (section 전제와 한계: 832x480 video, 4 latent
+frames per chunk, gamma = 0.10): 40 layers x 40 heads x head_dim 128 bf16
+K and V, 5 chunks of 6,240 tokens (sink + the chunk leaving the window + a
+3-chunk window), d = 64 score channels.  One step enqueues
+
+  dp_score_mask -> dp_compact_index -> dp_gather_kv (fused RoPE re-index)
+
+over all 40 layers, K and V, with every input resident in HBM.  The frame
+phase table is restored before each step so every step re-indexes from the
+same state (a 20-float device copy).
+
+Printed: one JSON line with the step's algorithmic HBM bytes per second, the
+tokens scored per second, a roofline record of the dominant kernel (the
+gather) timed with HIP events on its stream, and the CPU oracle timed on a
+bounded layer sample of the same workload on the host cores.
+
+Other workloads (--workload reindex | prefix | hs) time the other shapes.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s (10^9 B/s)
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gather_eviction_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="eviction", choices=["eviction", "reindex", "prefix", "hs"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gather.hip", "dp_internal.h"):
+        with open(os.path.join(ROOT, "compaction_dp_score_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(per_launch_alg_bytes):
+    """HBM bytes per gather launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    kv = {}
+    for line in open(PROFILE_TRAFFIC):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != kernel_sources_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on the current stream (the stream every launch goes to)."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(torch.cuda.current_stream())
+        self.pairs.append([e, None])
+
+    def stop(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(torch.cuda.current_stream())
+        self.pairs[-1][1] = e
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+def setup_eviction(dev):
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    from compaction_dp_score_amd.step import PruneStep
+    w = dpsynth.WORKLOADS["eviction"]
+    T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
+    k_src, v_src, k_dst, v_dst = [], [], [], []
+    for l in range(L):
+        k = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+        v = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+        dpsynth.kv_fill_device(k, "bf16", w.seed, dpsynth.STREAM_K, l, T, H * D)
+        dpsynth.kv_fill_device(v, "bf16", w.seed, dpsynth.STREAM_V, l, T, H * D)
+        k_src.append(k)
+        v_src.append(v)
+        k_dst.append(torch.empty_like(k))
+        v_dst.append(torch.empty_like(v))
+    x0, xf = dpsynth.score_inputs(w)
+    theta = dpsynth.rope_theta(w.rope_pairs, w.rope_base)
+    ft, fp = dpsynth.frame_tables(w)
+    rope = dict(theta=torch.from_numpy(theta).to(dev), frame_t=torch.from_numpy(ft).to(dev),
+                frame_phase=torch.from_numpy(fp).to(dev), q0=w.q0, knee=w.rope_knee,
+                inv_factor=1.0 / w.rope_factor)
+    phase0 = rope["frame_phase"].clone()
+    step = PruneStep(k_src=k_src, v_src=v_src, k_dst=k_dst, v_dst=v_dst, seq_len=T,
+                     sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
+                     n_scored=w.n_scored, gamma=w.gamma, d=w.d,
+                     row_frame=torch.from_numpy(dpsynth.row_frame(w)).to(dev), rope=rope)
+    x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
+    gt = Timer()
+
+    def run(timed):
+        rope["frame_phase"].copy_(phase0)
+        dp.dp_score_mask(x0d, xfd, w.d, w.d, step.policy, step.ell, step.keep)
+        dp.dp_compact_index(step.keep, T, step.idx, step.n_kept, step.row_frame_src,
+                            step.row_frame_dst, step.ws_compact)
+        if timed:
+            gt.start()
+        dp.dp_gather_kv(step.kv, step.idx, step.n_kept, step.row_frame_dst, step.rope,
+                        step.ws_rope)
+        if timed:
+            gt.stop()
+
+    def accounting():
+        n = int(step.n_kept.item())
+        row = H * D * 2
+        gather = n * row * 2 * 2 * L
+        score = w.n_scored * (8 * w.d) + T
+        index = 2 * T + 4 * n + 8 * n
+        return dict(n_kept=n, gather_bytes=gather,
+                    step_bytes=gather + score + index, n_scored=w.n_scored,
+                    config={"workload": "eviction", "layers": L, "heads": H, "head_dim": D,
+                            "kv_dtype": "bf16", "tokens": T, "chunk_tokens": w.chunk_tokens,
+                            "sink_chunks": w.sink_chunks, "window_chunks": w.window_chunks,
+                            "scored_tokens": w.n_scored, "d": w.d, "gamma": w.gamma,
+                            "rope_pairs": w.rope_pairs, "rope_knee_frames": w.rope_knee,
+                            "rope_factor": w.rope_factor, "kept_tokens": n,
+                            "pr_step": 1 - n / T})
+
+    def cpu_baseline(seconds):
+        return cpu_baseline_eviction(w, x0, xf, theta, ft, fp, seconds)
+
+    return run, gt, accounting, cpu_baseline
+
+
+def cpu_baseline_eviction(w, x0, xf, theta, ft, fp, seconds):
+    """Oracle (as it is) on a layer sample of the eviction step: score, mask
+    and index once, then gather of K and V plus the K re-index on as many
+    layers as fit the time budget; scaled to 40 layers."""
+    import dpsynth
+    import oracle
+    T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    tile_rows = 624                                  # 1/50 of the cache, tiled over the layer
+    tile = dpsynth.kv_rows_host("bf16", w.seed, dpsynth.STREAM_K, 0, np.arange(tile_rows), T, H * D)
+    rf = dpsynth.row_frame(w)
+    tables_in = (ft, fp)
+    t0 = time.perf_counter()
+    ell = oracle.score_f32(x0, xf, w.d)
+    keep = oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin, w.n_scored, w.gamma)
+    idx = oracle.compact(keep)
+    rf2 = oracle.gather_i32(rf, idx)
+    tables = oracle.rope_frames(tables_in[0], tables_in[1], w.q0, w.rope_knee,
+                                np.float32(1.0 / w.rope_factor), theta)
+    t_once = time.perf_counter() - t0
+    n_layers = max(1, min(L, cores))
+    src = np.empty((n_layers, T, H, D), np.uint16)
+    for l in range(n_layers):
+        src[l].reshape(T // tile_rows, tile_rows, H * D)[:] = tile[None]
+    per_layer = []
+    done = 0
+    t_start = time.perf_counter()
+    while done < L:
+        t1 = time.perf_counter()
+        kd = oracle.gather(src, idx)                 # K of n_layers layers
+        vd = oracle.gather(src, idx)                 # V
+        for l in range(n_layers):
+            oracle.rope_rows(kd[l], rf2, 0, tables)
+        per_layer.append((time.perf_counter() - t1) / n_layers)
+        done += n_layers
+        del kd, vd
+        if time.perf_counter() - t_start > seconds:
+            break
+    t_layer = float(np.median(per_layer))
+    total = t_once + L * t_layer
+    n = idx.shape[0]
+    step_bytes = n * H * D * 2 * 2 * 2 * L + w.n_scored * 8 * w.d + T + 2 * T + 12 * n
+    return {"value": step_bytes / total / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "score+mask+index of the full step once, then gather of K and V plus "
+                      "the K re-index on %d layers at a time (%d layer passes timed, median); "
+                      "time scaled to 40 layers: %.2f s per step" % (n_layers, done, total),
+            "step_seconds": total, "tokens_scored_per_s": w.n_scored / total}
+
+
+def setup_reindex(dev):
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    w = dpsynth.WORKLOADS["reindex"]
+    T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
+    keep = dpsynth.retained_keep(w)
+    kept = np.flatnonzero(keep)
+    rows = kept.shape[0]
+    rf_full = dpsynth.row_frame(w)
+    rf = torch.from_numpy(rf_full[kept].astype(np.int32)).to(dev)
+    ks = []
+    for l in range(L):
+        k = torch.empty((rows, H, D), dtype=torch.bfloat16, device=dev)
+        dpsynth.kv_fill_device(k, "bf16", w.seed, dpsynth.STREAM_K, l, rows, H * D)
+        ks.append(k)
+    arr = dp.ptr_array(ks, dev)
+    theta = torch.from_numpy(dpsynth.rope_theta(w.rope_pairs, w.rope_base)).to(dev)
+    ft, fp = dpsynth.frame_tables(w)
+    ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(fp).to(dev)
+    phase0 = fpd.clone()
+    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    ws = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                     dtype=torch.float32, device=dev)
+    gt = Timer()
+    moved_rows = int(np.count_nonzero(rf_full[kept] < (w.n_frames - w.window_chunks * w.frames_per_chunk)))
+
+    def run(timed):
+        fpd.copy_(phase0)
+        if timed:
+            gt.start()
+        dp.dp_rope_reindex(arr, L, H, D, dp.DP_BF16, rows, None, rf, rope, ws)
+        if timed:
+            gt.stop()
+
+    def accounting():
+        b = moved_rows * H * (2 * w.rope_pairs * 2) * 2 * L
+        return dict(n_kept=rows, gather_bytes=b, step_bytes=b, n_scored=0,
+                    config={"workload": "reindex", "layers": L, "heads": H, "head_dim": D,
+                            "kv_dtype": "bf16", "retained_rows": rows, "reindexed_rows": moved_rows,
+                            "rope_pairs": w.rope_pairs, "q0": w.q0})
+
+    return run, gt, accounting, None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the compaction path on a single "
+              "MI355X (pass --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import compaction_dp_score_amd  # noqa: F401  (fails loudly if the library is missing)
+    dev = torch.device("cuda:0")
+    setups = {"eviction": setup_eviction, "reindex": setup_reindex}
+    if args.workload not in setups:
+        print("workload %s is not wired into bench.py yet" % args.workload, file=sys.stderr)
+        sys.exit(2)
+    run, gt, accounting, cpu = setups[args.workload](dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        run(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        run(True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    acc = accounting()
+    gbs = acc["step_bytes"] / (ms * 1e-3) / 1e9
+    g_ms = gt.mean_ms()
+    g_gbs = acc["gather_bytes"] / (g_ms * 1e-3) / 1e9
+    traffic = read_traffic(acc["gather_bytes"])
+    kernel = "gather_kernel" if args.workload == "eviction" else "reindex_kernel"
+    rec = {
+        "metric": "compacted KV GB/s (read+write) per prune step, % of HBM peak; tokens scored/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": acc["config"],
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_scored_per_s": (acc["n_scored"] / (ms * 1e-3)) if acc["n_scored"] else None,
+        "step_bytes": acc["step_bytes"],
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(g_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": acc["gather_bytes"],
+                     "launch_ms": round(g_ms, 4)},
+    }
+    if cpu is not None and not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu(args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

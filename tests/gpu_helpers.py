@@ -49,7 +49,10 @@ def keys_close(got_bits, want_bits, tol):
     g, w = as_float(got_bits), as_float(want_bits)
     gn, wn = np.isnan(g), np.isnan(w)
     assert np.array_equal(gn, wn)
-    d = np.abs(g[~gn].astype(np.float64) - w[~wn].astype(np.float64))
+    g64, w64 = g[~gn].astype(np.float64), w[~wn].astype(np.float64)
+    same = g64 == w64                     # also equal infinities
+    with np.errstate(invalid="ignore"):
+        d = np.where(same, 0.0, np.abs(g64 - w64))
     worst = float(d.max()) if d.size else 0.0
     exact = int(np.count_nonzero(got_bits != want_bits))
     return worst <= tol, worst, exact

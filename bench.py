@@ -181,7 +181,7 @@ def cpu_baseline_eviction(w, x0, xf, theta, ft, fp, seconds):
     tables = oracle.rope_frames(tables_in[0], tables_in[1], w.q0, w.rope_knee,
                                 np.float32(1.0 / w.rope_factor), theta)
     t_once = time.perf_counter() - t0
-    n_layers = max(1, min(L, cores))
+    n_layers = max(1, min(L, cores, 8))
     src = np.empty((n_layers, T, H, D), np.uint16)
     for l in range(n_layers):
         src[l].reshape(T // tile_rows, tile_rows, H * D)[:] = tile[None]
@@ -254,6 +254,25 @@ def setup_reindex(dev):
     return run, gt, accounting, None
 
 
+def copy_ceiling(dev, nbytes=8 << 30, reps=5):
+    """Read+write GB/s of a plain 16-byte-vector device copy of nbytes, in
+    the same run (the practical HBM ceiling a gather can approach)."""
+    import dpsynth
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dpsynth.device_copy(dst, src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dpsynth.device_copy(dst, src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -310,6 +329,7 @@ def main():
                      "traffic": traffic, "bytes_per_launch": acc["gather_bytes"],
                      "launch_ms": round(g_ms, 4)},
     }
+    rec["copy_ceiling_gbs"] = round(copy_ceiling(dev), 2)
     if cpu is not None and not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu(args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -263,6 +263,8 @@ def _fill():
                                    ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p,
                                    ctypes.c_void_p]
         L.dpsynth_fill.restype = ctypes.c_int
+        L.dpsynth_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.dpsynth_copy.restype = ctypes.c_int
         _fill_lib = L
     return _fill_lib
 
@@ -290,3 +292,16 @@ def kv_fill_device(tensor, dtype: str, seed: int, stream: int, layer: int, src_r
     if rc != 0:
         raise RuntimeError("dpsynth_fill failed (%d)" % rc)
     return tensor
+
+
+def device_copy(dst, src):
+    """Plain 16-byte-vector copy of a contiguous device tensor (bandwidth and
+    counter reference; not part of the method)."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nbytes and nbytes % 16 == 0
+    st = torch.cuda.current_stream(src.device).cuda_stream
+    rc = _fill().dpsynth_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                              nbytes // 16, ctypes.c_void_p(st))
+    if rc != 0:
+        raise RuntimeError("dpsynth_copy failed (%d)" % rc)

@@ -2,6 +2,10 @@
 // picked by the SplitMix64 output function (Steele, Lea and Flood, 2014) of a
 // seeded Weyl sequence.  Input generation only; no part of the compaction
 // method lives here.
+//
+// Also a plain 16-byte-vector copy of a known size, the reference the
+// benchmark uses for the device-to-device bandwidth ceiling and to scale
+// hardware byte counters.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,7 +27,25 @@ __global__ __launch_bounds__(256) void fill_kernel(T* __restrict__ dst, uint64_t
     dst[i] = table[mix(skey, key_base + (uint64_t)i) >> 48];
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void calib_copy_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
 }  // namespace
+
+extern "C" int dpsynth_copy(void* dst, const void* src, int64_t n16, void* stream) {
+  if (n16 <= 0) return 0;
+  if (!dst || !src || (((uintptr_t)dst | (uintptr_t)src) & 15u)) return 1;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks >= ((int64_t)1 << 31)) return 1;
+  hipLaunchKernelGGL(calib_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4*)src, (u32x4*)dst, n16);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 extern "C" int dpsynth_fill(void* dst, int dtype, uint64_t skey, uint64_t key_base,
                             int64_t n, const void* table, void* stream) {

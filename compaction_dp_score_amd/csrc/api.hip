@@ -174,7 +174,8 @@ dp_status dp_gather_kv(const dp_kv* kv, const int32_t* idx, const int64_t* n_kep
   if (kv->dst_capacity > kMaxVec / rv)
     return fail(DP_ERANGE, "dp_gather_kv: a destination layer over 32 GiB is not supported");
   const int n_kv = kv->v_src ? 2 : 1;
-  if ((int64_t)kv->n_layers * n_kv > 65535) return fail(DP_ERANGE, "dp_gather_kv: too many layers");
+  if ((int64_t)kv->n_layers * n_kv * ((kv->dst_capacity * rv + 255) / 256) >= kMaxVec)
+    return fail(DP_ERANGE, "dp_gather_kv: layers x capacity too large for one launch");
   if (!aligned(n_kept, 8) || (kv->dev_error && !aligned(kv->dev_error, 4)))
     return fail(DP_EALIGN, "dp_gather_kv: n_kept must be 8-byte aligned");
   if (rope) {

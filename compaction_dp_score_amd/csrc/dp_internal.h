@@ -75,37 +75,56 @@ __device__ __forceinline__ void rotate_pair(float a, float b, float c, float s, 
   b2 = as + bc;
 }
 
-// Rotate the pairs of one 16-byte vector of keys.  dtype 1: bf16, 4 pairs;
-// dtype 0: fp32, 2 pairs.  cs points at {cos, sin} of the vector's first pair;
-// only the first n_valid pairs are rotated.
-__device__ __forceinline__ u32x4 rotate_vec(u32x4 v, int dtype, const f32x2* cs, int n_valid) {
+// Two fp32 values to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_hw(float lo, float hi) {
+  f32x2 in = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(in, bf16x2));
+}
+
+// Rotate the pairs of one 16-byte vector of keys given its {cos, sin} table
+// entries t01 = (c0 s0 c1 s1) and t23 = (c2 s2 c3 s3).  dtype 1: bf16, 4 pairs;
+// dtype 0: fp32, 2 pairs (t23 unused).  Only the first n_valid pairs change;
+// the result is selected per pair, without branches.
+__device__ __forceinline__ u32x4 rotate_vec_tab(u32x4 v, int dtype, f32x4 t01, f32x4 t23,
+                                                int n_valid) {
   if (dtype == DP_BF16) {
+    const float cc[4] = {t01.x, t01.z, t23.x, t23.z};
+    const float ss[4] = {t01.y, t01.w, t23.y, t23.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (q < n_valid) {
-        f32x2 t = cs[q];
-        float a2, b2;
-        rotate_pair(bf16_lo(v[q]), bf16_hi(v[q]), t.x, t.y, a2, b2);
-        v[q] = pack_bf16(a2, b2);
-      }
+      float a2, b2;
+      rotate_pair(bf16_lo(v[q]), bf16_hi(v[q]), cc[q], ss[q], a2, b2);
+      const uint32_t r = pack_bf16_hw(a2, b2);
+      v[q] = q < n_valid ? r : v[q];
     }
   } else {
+    const float cc[2] = {t01.x, t01.z};
+    const float ss[2] = {t01.y, t01.w};
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      if (q < n_valid) {
-        f32x2 t = cs[q];
-        float a2, b2;
-        rotate_pair(__uint_as_float(v[2 * q]), __uint_as_float(v[2 * q + 1]), t.x, t.y, a2, b2);
-        v[2 * q] = __float_as_uint(a2);
-        v[2 * q + 1] = __float_as_uint(b2);
-      }
+      float a2, b2;
+      rotate_pair(__uint_as_float(v[2 * q]), __uint_as_float(v[2 * q + 1]), cc[q], ss[q], a2, b2);
+      v[2 * q] = q < n_valid ? __float_as_uint(a2) : v[2 * q];
+      v[2 * q + 1] = q < n_valid ? __float_as_uint(b2) : v[2 * q + 1];
     }
   }
   return v;
 }
 
+// Same, reading the table at cs (16-byte aligned; the table is padded so that
+// the entries of four pairs are readable).
+__device__ __forceinline__ u32x4 rotate_vec(u32x4 v, int dtype, const f32x2* cs, int n_valid) {
+  const f32x4* t = reinterpret_cast<const f32x4*>(cs);
+  const f32x4 t01 = t[0];
+  const f32x4 t23 = dtype == DP_BF16 ? t[1] : t01;
+  return rotate_vec_tab(v, dtype, t01, t23, n_valid);
+}
+
 // Layout of the RoPE workspace: delta[n_frames] (fp32, padded to 16 bytes),
-// then {cos, sin}[n_frames][pairs_padded] with pairs_padded a multiple of 4.
+// then {cos, sin}[n_frames][pairs_padded] with pairs_padded a multiple of 4,
+// then a 32-byte tail so that four pairs can always be read from any vector's
+// first pair.
 struct RopeView {
   const float* delta;
   const f32x2* cs;

@@ -4,15 +4,19 @@
 // when a non-sink chunk leaves the window, each layer keeps only the selected
 // entries K[m], V[m], so the KV sequence length really shrinks.
 //
-// One launch covers all layers and both K and V: blockIdx.y = (layer, K|V),
-// blockIdx.x walks the destination slab of that layer as a flat array of
-// 16-byte vectors.  Vector i of the slab is column c = i mod RV of destination
-// row j = i div RV (RV = row bytes / 16, division by multiply-high), read from
-// source row idx[j].  Consecutive lanes read and write consecutive 16-byte
-// vectors of the same row, so every wavefront moves 1 KiB contiguous on both
-// sides; a row is 10 KiB for 40 heads x 128 bf16.  Optionally the K vectors of
-// the temporal RoPE block are re-rotated in registers on the way (no extra
-// HBM bytes).  HBM-bound: 2 x row bytes per kept row per layer and tensor.
+// One launch covers all layers and both K and V.  The destination of each
+// (layer, K|V) slab is a flat array of 16-byte vectors; vector i is column
+// c = i mod RV of destination row j = i div RV (RV = row bytes / 16, division
+// by multiply-high), read from source row idx[j].  The grid is 1-D and sized
+// by the destination capacity; every workgroup reads the kept count first and
+// derives (slab, tile) from its linear id with the number of live tiles per
+// slab, so the live workgroups are dense at the front of the dispatch order
+// and the surplus ones sit at the tail and exit at once.  Consecutive lanes
+// read and write consecutive 16-byte vectors of one row (a row is 10 KiB for
+// 40 heads x 128 bf16), with non-temporal loads and stores: the data is used
+// once.  Optionally the K vectors of the temporal RoPE block are re-rotated
+// in registers on the way (no extra HBM bytes).  HBM-bound: 2 x row bytes per
+// kept row per layer and tensor.
 #include "dp_internal.h"
 
 namespace dp {
@@ -31,6 +35,7 @@ struct GatherArgs {
   FastDiv div_row;     // RV: 16-byte vectors per row
   FastDiv div_head;    // vectors per head row
   uint32_t total_cap;  // dst_cap * RV
+  uint32_t n_slabs;    // n_layers * n_kv
   int32_t n_kv;        // 1 (K only) or 2
   int32_t dtype;
   int32_t has_rope;
@@ -38,59 +43,58 @@ struct GatherArgs {
   RopeView rope;
 };
 
-template <int U>
+template <bool ROPE>
 __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
   const int64_t nk = *a.n_kept;
   const int64_t n = nk < a.dst_cap ? nk : a.dst_cap;
-  if (nk > a.dst_cap && a.dev_error && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+  if (nk > a.dst_cap && a.dev_error && blockIdx.x == 0 && threadIdx.x == 0)
     *a.dev_error = DP_ECAPACITY;
-  const uint32_t total = (uint32_t)(n * (int64_t)a.div_row.d);
-  const uint32_t first = blockIdx.x * (kBlock * U);
-  if (first >= total) return;
-  const int layer = blockIdx.y / a.n_kv;
-  const bool is_v = (blockIdx.y % a.n_kv) == 1;
+  const uint32_t per_slab = (uint32_t)(n * (int64_t)a.div_row.d);
+  const uint32_t tiles = (per_slab + kBlock - 1) / kBlock;
+  if (tiles == 0) return;
+  const uint32_t slab = blockIdx.x / tiles;
+  if (slab >= a.n_slabs) return;
+  const uint32_t i = (blockIdx.x - slab * tiles) * kBlock + threadIdx.x;
+  const int layer = (int)(slab / a.n_kv);
+  const bool is_v = (slab % a.n_kv) == 1;
   const u32x4* __restrict__ src =
       reinterpret_cast<const u32x4*>(is_v ? a.v_src[layer] : a.k_src[layer]);
   u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(is_v ? a.v_dst[layer] : a.k_dst[layer]);
-  const bool rope = a.has_rope && !is_v;
-
-  u32x4 v[U];
-  uint32_t jrow[U], col[U];
-  bool ok[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t i = first + u * kBlock + threadIdx.x;
-    ok[u] = false;
-    if (i < total) {
-      const uint32_t j = fdiv(i, a.div_row);
-      const uint32_t c = i - j * a.div_row.d;
-      const int32_t s = a.idx[j];
-      jrow[u] = j;
-      col[u] = c;
-      if ((uint32_t)s < (uint64_t)a.src_rows) {   // out-of-range entries are skipped
-        v[u] = src[(int64_t)s * a.div_row.d + c];
-        ok[u] = true;
-      }
-    }
+  if (i >= per_slab) return;
+  const uint32_t j = fdiv(i, a.div_row);
+  const uint32_t c = i - j * a.div_row.d;
+  if (ROPE && !is_v) {
+    // K with the fused re-index.  Vector loads retire in issue order, so all
+    // lookups the rotation needs are requested before the HBM load of the
+    // data: the source row and the frame together, then the frame's phase
+    // step and {cos, sin} (L2 hits that return while the data is in flight).
+    // Every lane takes the same straight-line path; lanes outside the
+    // temporal block read entry 0 and keep their data.
+    const uint32_t h = fdiv(c, a.div_head);
+    const int tv = (int)(c - h * a.div_head.d) - a.rope.tv_begin;
+    const bool in_block = tv >= 0 && tv < a.rope.tv_count;
+    const int32_t s = a.idx[j];
+    const int f = a.row_frame[j];
+    const bool sv = (uint32_t)s < (uint64_t)a.src_rows;   // out-of-range entries are skipped
+    const bool fv = (uint32_t)f < (uint32_t)a.rope.n_frames;
+    const int fc = fv ? f : 0;
+    const int p0 = in_block ? tv * a.rope.ppv : 0;
+    const f32x4* t = reinterpret_cast<const f32x4*>(a.rope.cs + (int64_t)fc * a.rope.pairs_padded + p0);
+    const float dl = a.rope.delta[fc];
+    const f32x4 t01 = t[0];       // the table has a 32-byte tail, so t[1] is readable
+    const f32x4 t23 = t[1];
+    u32x4 v = __builtin_nontemporal_load(src + (int64_t)(sv ? s : 0) * a.div_row.d + c);
+    __builtin_amdgcn_sched_barrier(0);   // the phase-step test stays after the data load
+    const int nv = min(a.rope.ppv, a.rope.n_pairs - p0);
+    const u32x4 r = rotate_vec_tab(v, a.dtype, t01, t23, nv);
+    if (in_block && fv && dl != 0.0f) v = r;
+    if (sv) __builtin_nontemporal_store(v, dst + i);
+    return;
   }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (!ok[u]) continue;
-    u32x4 w = v[u];
-    if (rope) {
-      const uint32_t h = fdiv(col[u], a.div_head);
-      const int tv = (int)(col[u] - h * a.div_head.d) - a.rope.tv_begin;
-      if (tv >= 0 && tv < a.rope.tv_count) {
-        const int f = a.row_frame[jrow[u]];
-        if ((uint32_t)f < (uint32_t)a.rope.n_frames && a.rope.delta[f] != 0.0f) {
-          const int p0 = tv * a.rope.ppv;
-          const int nv = min(a.rope.ppv, a.rope.n_pairs - p0);
-          w = rotate_vec(w, a.dtype, a.rope.cs + (int64_t)f * a.rope.pairs_padded + p0, nv);
-        }
-      }
-    }
-    __builtin_nontemporal_store(w, dst + first + u * kBlock + threadIdx.x);
-  }
+  const int32_t s = a.idx[j];
+  if ((uint32_t)s >= (uint64_t)a.src_rows) return;        // out-of-range entries are skipped
+  const u32x4 v = __builtin_nontemporal_load(src + (int64_t)s * a.div_row.d + c);
+  __builtin_nontemporal_store(v, dst + i);
 }
 
 }  // namespace
@@ -117,10 +121,13 @@ dp_status launch_gather(const dp_kv& kv, const int32_t* idx, const int64_t* n_ke
   a.row_frame = row_frame;
   if (rope) a.rope = *rope;
   else a.rope = RopeView{};
+  a.n_slabs = (uint32_t)(kv.n_layers * a.n_kv);
   if (a.total_cap == 0) return DP_OK;
-  constexpr int U = 1;
-  const uint32_t gx = (uint32_t)(((uint64_t)a.total_cap + kBlock * U - 1) / (kBlock * U));
-  hipLaunchKernelGGL(gather_kernel<U>, dim3(gx, kv.n_layers * a.n_kv), dim3(kBlock), 0, s, a);
+  const uint64_t gx = (uint64_t)a.n_slabs * (((uint64_t)a.total_cap + kBlock - 1) / kBlock);
+  if (rope)
+    hipLaunchKernelGGL(gather_kernel<true>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(gather_kernel<false>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("gather_kernel");
 }
 

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
 size_t rope_ws_bytes(int32_t n_frames, int32_t n_pairs) {
   size_t pp = (size_t)((n_pairs + 3) / 4) * 4;
   size_t dbytes = ((size_t)n_frames * 4 + 15) / 16 * 16;
-  return dbytes + (size_t)n_frames * pp * sizeof(f32x2);
+  return dbytes + (size_t)n_frames * pp * sizeof(f32x2) + 32;   // 32-byte tail: see gather
 }
 
 dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dtype,

@@ -141,7 +141,7 @@ def _rope(**kw):
     (dict(n_layers=0), dp.DP_EINVAL),
     (dict(src_rows=1 << 31), dp.DP_ERANGE),
     (dict(dst_capacity=1 << 40), dp.DP_ERANGE),
-    (dict(n_layers=40000), dp.DP_ERANGE),
+    (dict(n_layers=40000, dst_capacity=1000000), dp.DP_ERANGE),
 ])
 def test_gather_rejects(kw, want):
     kv = _kv(**kw)

@@ -32,7 +32,20 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s (10^9 B/s)
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gather_eviction_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+CALIB_BYTES = 8 << 30          # size of the calibration copy run in every bench process
+
+# dominant kernel of each workload: (rocprof name prefix, sources it is built from)
+KERNELS = {
+    "eviction": ("gather_kernel", ("gather.hip", "dp_internal.h")),
+    "prefix": ("gather_kernel", ("gather.hip", "dp_internal.h")),
+    "reindex": ("reindex_kernel", ("rope.hip", "dp_internal.h")),
+    "hs": ("hs_gather_kernel", ("hs.hip", "dp_internal.h")),
+}
+
+
+def traffic_path(workload):
+    return os.path.join(PROFILES, "%s_%s_traffic.txt" % (KERNELS[workload][0], workload))
 
 
 def parse():
@@ -44,29 +57,34 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary of --workload from two rocprofv3 --pmc "
+                         "output directories (FETCH_SIZE, WRITE_SIZE) and exit")
     return ap.parse_args()
 
 
-def kernel_sources_sha():
+def kernel_sources_sha(workload):
     import hashlib
     h = hashlib.sha256()
-    for f in ("gather.hip", "dp_internal.h"):
+    for f in KERNELS[workload][1]:
         with open(os.path.join(ROOT, "compaction_dp_score_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(per_launch_alg_bytes):
-    """HBM bytes per gather launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def read_traffic(workload):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel
+    source; else None."""
+    path = traffic_path(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PROFILE_TRAFFIC):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != kernel_sources_sha():
+    if kv.get("source_sha") != kernel_sources_sha(workload):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -254,7 +272,7 @@ def setup_reindex(dev):
     return run, gt, accounting, None
 
 
-def copy_ceiling(dev, nbytes=8 << 30, reps=5):
+def copy_ceiling(dev, nbytes, reps=5):
     """Read+write GB/s of a plain 16-byte-vector device copy of nbytes, in
     the same run (the practical HBM ceiling a gather can approach)."""
     import dpsynth
@@ -273,8 +291,219 @@ def copy_ceiling(dev, nbytes=8 << 30, reps=5):
     return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
+def summarize_pmc(workload, fetch_dir, write_dir):
+    """Per-launch HBM bytes of the workload's dominant kernel from rocprofv3
+    counter CSVs, each counter scaled by what it reads for the calibration
+    copy (CALIB_BYTES read and written by calib_copy_kernel in the same run)."""
+    import csv
+    import glob
+    kname = KERNELS[workload][0]
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        assert files, "no counter_collection.csv under %s" % d
+        vals = {"kernel": [], "calib": []}
+        for fn in files:
+            for r in csv.DictReader(open(fn)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                if ("::" + kname + "<") in name or ("::" + kname + "(") in name:
+                    vals["kernel"].append(float(r["Counter_Value"]))
+                elif "calib_copy_kernel" in name:
+                    vals["calib"].append(float(r["Counter_Value"]))
+        assert vals["kernel"] and vals["calib"], (d, counter, {k: len(v) for k, v in vals.items()})
+        return (sum(vals["kernel"]) / len(vals["kernel"]), len(vals["kernel"]),
+                sum(vals["calib"]) / len(vals["calib"]))
+
+    fk, fn_, fc = per_kernel(fetch_dir, "FETCH_SIZE")
+    wk, wn, wc = per_kernel(write_dir, "WRITE_SIZE")
+    fscale = CALIB_BYTES / (fc * 1024.0)
+    wscale = CALIB_BYTES / (wc * 1024.0)
+    rd = fk * 1024.0 * fscale
+    wr = wk * 1024.0 * wscale
+    path = traffic_path(workload)
+    with open(path, "w") as out:
+        out.write("# HBM traffic of %s on the %s workload, per dispatch, from rocprofv3 counters\n"
+                  % (kname, workload))
+        out.write("# commands (from the repository root; %s as the dominant kernel):\n" % kname)
+        out.write("#   rocprofv3 --pmc FETCH_SIZE -d %s -o run -f csv -- python bench.py "
+                  "--workload %s --no-cpu-baseline --steps 2 --warmup 0\n" % (fetch_dir, workload))
+        out.write("#   rocprofv3 --pmc WRITE_SIZE -d %s -o run -f csv -- python bench.py "
+                  "--workload %s --no-cpu-baseline --steps 2 --warmup 0\n" % (write_dir, workload))
+        out.write("#   python bench.py --workload %s --summarize-pmc %s %s\n"
+                  % (workload, fetch_dir, write_dir))
+        out.write("# scale: each counter divided by what it reads for calib_copy_kernel, which\n"
+                  "# reads and writes %d bytes (a plain 16-byte-vector copy)\n" % CALIB_BYTES)
+        out.write("kernel: %s\n" % kname)
+        out.write("source_sha: %s\n" % kernel_sources_sha(workload))
+        out.write("dispatches_fetch: %d\n" % fn_)
+        out.write("dispatches_write: %d\n" % wn)
+        out.write("fetch_kib_per_dispatch: %.1f\n" % fk)
+        out.write("write_kib_per_dispatch: %.1f\n" % wk)
+        out.write("calib_fetch_kib: %.1f\n" % fc)
+        out.write("calib_write_kib: %.1f\n" % wc)
+        out.write("fetch_scale: %.4f\n" % fscale)
+        out.write("write_scale: %.4f\n" % wscale)
+        out.write("hbm_read_bytes_per_launch: %.0f\n" % rd)
+        out.write("hbm_write_bytes_per_launch: %.0f\n" % wr)
+        out.write("hbm_bytes_per_launch: %.0f\n" % (rd + wr))
+    print(open(path).read())
+
+
+def _fill_layers(dev, w, rows, layers, stream_id):
+    import dpsynth
+    out = []
+    for l in layers:
+        t = torch.empty((rows, w.n_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        dpsynth.kv_fill_device(t, "bf16", w.seed, stream_id, l, rows, w.n_heads * w.head_dim)
+        out.append(t)
+    return out
+
+
+def setup_prefix(dev, slab_layers=20):
+    """Prefix pruning of a 58-chunk observed context: all 57 non-sink chunks
+    scored (d = 64) and compacted.  40 layers of K+V are 296.5 GB, more than
+    one GPU's 288 GB, so a step is timed on one 20-layer slab (the other slab
+    is the same launch on other layers)."""
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    from compaction_dp_score_amd.step import PruneStep
+    w = dpsynth.WORKLOADS["prefix"]
+    T, H, D = w.seq_len, w.n_heads, w.head_dim
+    x0, xf = dpsynth.score_inputs(w)
+    x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
+    k_src = _fill_layers(dev, w, T, range(slab_layers), dpsynth.STREAM_K)
+    v_src = _fill_layers(dev, w, T, range(slab_layers), dpsynth.STREAM_V)
+    # the kept count sizes the destination (one host read, outside the timing)
+    probe = PruneStep(k_src=k_src[:1], v_src=None, k_dst=[k_src[0][:1]], v_dst=None, seq_len=T,
+                      sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
+                      n_scored=w.n_scored, gamma=w.gamma, d=w.d)
+    dp.dp_score_mask(x0d, xfd, w.d, w.d, probe.policy, None, probe.keep)
+    dp.dp_compact_index(probe.keep, T, probe.idx, probe.n_kept, None, None, probe.ws_compact)
+    cap = int(probe.n_kept.item())
+    del probe
+    k_dst = [torch.empty((cap, H, D), dtype=torch.bfloat16, device=dev) for _ in range(slab_layers)]
+    v_dst = [torch.empty((cap, H, D), dtype=torch.bfloat16, device=dev) for _ in range(slab_layers)]
+    step = PruneStep(k_src=k_src, v_src=v_src, k_dst=k_dst, v_dst=v_dst, seq_len=T,
+                     sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
+                     n_scored=w.n_scored, gamma=w.gamma, d=w.d)
+    gt = Timer()
+
+    def run(timed):
+        dp.dp_score_mask(x0d, xfd, w.d, w.d, step.policy, None, step.keep)
+        dp.dp_compact_index(step.keep, T, step.idx, step.n_kept, None, None, step.ws_compact)
+        if timed:
+            gt.start()
+        dp.dp_gather_kv(step.kv, step.idx, step.n_kept)
+        if timed:
+            gt.stop()
+
+    def accounting():
+        n = int(step.n_kept.item())
+        gather = n * H * D * 2 * 2 * 2 * slab_layers
+        score = w.n_scored * 8 * w.d + T
+        index = 2 * T + 4 * n
+        return dict(n_kept=n, gather_bytes=gather, step_bytes=gather + score + index,
+                    n_scored=w.n_scored,
+                    config={"workload": "prefix", "layers_in_slab": slab_layers, "layers": 40,
+                            "heads": H, "head_dim": D, "kv_dtype": "bf16", "tokens": T,
+                            "scored_tokens": w.n_scored, "d": w.d, "gamma": w.gamma,
+                            "kept_tokens": n, "pr_step": 1 - n / T})
+
+    return run, gt, accounting, None
+
+
+def setup_hs(dev):
+    """DeCoPrune-HS: 30-chunk history (187,200 tokens), per layer a seeded
+    half of the heads static (sink + 3-chunk window), the rest dynamic (the
+    shared gamma mask); ragged per-head output plus the RoPE re-index fused
+    into the gather (44 pairs, knee 12 frames, factor 8, q0 = 120)."""
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    w = dpsynth.WORKLOADS["hs"]
+    T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
+    x0, xf = dpsynth.score_inputs(w)
+    x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
+    cls = dpsynth.hs_head_class(w)
+    head_class = torch.from_numpy(cls.ravel().copy()).to(dev)
+    k_src = _fill_layers(dev, w, T, range(L), dpsynth.STREAM_K)
+    v_src = _fill_layers(dev, w, T, range(L), dpsynth.STREAM_V)
+    rf = torch.from_numpy(dpsynth.row_frame(w)).to(dev)
+    pol_static = dp.make_policy(T, w.sink_len, w.window_len, w.scored_begin, w.n_scored, w.gamma,
+                                mode=dp.DP_MODE_STREAMING)
+    pol_dyn = dp.make_policy(T, w.sink_len, w.window_len, w.scored_begin, w.n_scored, w.gamma)
+    keeps = [torch.empty(T, dtype=torch.uint8, device=dev) for _ in range(2)]
+    lists = [torch.empty(T, dtype=torch.int32, device=dev) for _ in range(2)]
+    rfs = [torch.empty(T, dtype=torch.int32, device=dev) for _ in range(2)]
+    lens = torch.zeros(2, dtype=torch.int64, device=dev)
+    ws_c = torch.empty(dp.dp_compact_workspace_bytes(T) // 4 + 1, dtype=torch.int32, device=dev)
+    offsets = torch.empty(L * H + 1, dtype=torch.int64, device=dev)
+    cidx, crf = dp.ptr_array(lists, dev), dp.ptr_array(rfs, dev)
+    caps = [T, T]
+
+    def index_part():
+        dp.dp_score_mask(None, None, w.d, w.d, pol_static, None, keeps[0])
+        dp.dp_score_mask(x0d, xfd, w.d, w.d, pol_dyn, None, keeps[1])
+        for c in range(2):
+            dp.dp_compact_index(keeps[c], T, lists[c], lens[c:c + 1], rf, rfs[c], ws_c)
+        dp.dp_hs_offsets(head_class, L, H, lens, 2, offsets)
+
+    index_part()
+    total = int(offsets[-1].item())
+    k_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    v_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    kv = dp.dp_kv_hs()
+    arrs = [dp.ptr_array(k_src, dev), dp.ptr_array(v_src, dev)]
+    kv.k_src, kv.v_src = arrs[0].data_ptr(), arrs[1].data_ptr()
+    kv.k_out, kv.v_out = k_out.data_ptr(), v_out.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dp.DP_BF16
+    kv.src_rows, kv.out_capacity = T, total
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    theta = torch.from_numpy(dpsynth.rope_theta(w.rope_pairs, w.rope_base)).to(dev)
+    ft, fp = dpsynth.frame_tables(w)
+    ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(fp).to(dev)
+    phase0 = fpd.clone()
+    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    ws = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                     dtype=torch.float32, device=dev)
+    gt = Timer()
+    keep_alive = [arrs, k_out, v_out, cidx, crf]
+
+    def run(timed):
+        fpd.copy_(phase0)
+        index_part()
+        if timed:
+            gt.start()
+        dp.dp_hs_gather_kv(kv, head_class, 2, cidx, lens, caps, offsets, crf, rope, ws)
+        if timed:
+            gt.stop()
+
+    def accounting():
+        assert keep_alive
+        tot = int(offsets[-1].item())
+        ln = lens.cpu().numpy()
+        gather = tot * D * 2 * 2 * 2
+        score = w.n_scored * 8 * w.d + 2 * T
+        index = 4 * T + 8 * int(ln.sum()) + 8 * (L * H + 1)
+        return dict(n_kept=tot, gather_bytes=gather, step_bytes=gather + score + index,
+                    n_scored=w.n_scored,
+                    config={"workload": "hs", "layers": L, "heads": H, "head_dim": D,
+                            "kv_dtype": "bf16", "tokens": T, "static_heads_per_layer": int(
+                                (cls == 0).sum(axis=1)[0]), "static_rows": int(ln[0]),
+                            "dynamic_rows": int(ln[1]), "head_rows": tot,
+                            "pr_step": 1 - tot / (L * H * T), "rope_pairs": w.rope_pairs,
+                            "q0": w.q0})
+
+    return run, gt, accounting, None
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.workload, *args.summarize_pmc)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs the compaction path on a single "
               "MI355X (pass --gpus 1)", file=sys.stderr)
@@ -284,7 +513,8 @@ def main():
         sys.exit(2)
     import compaction_dp_score_amd  # noqa: F401  (fails loudly if the library is missing)
     dev = torch.device("cuda:0")
-    setups = {"eviction": setup_eviction, "reindex": setup_reindex}
+    setups = {"eviction": setup_eviction, "reindex": setup_reindex, "prefix": setup_prefix,
+              "hs": setup_hs}
     if args.workload not in setups:
         print("workload %s is not wired into bench.py yet" % args.workload, file=sys.stderr)
         sys.exit(2)
@@ -305,8 +535,8 @@ def main():
     gbs = acc["step_bytes"] / (ms * 1e-3) / 1e9
     g_ms = gt.mean_ms()
     g_gbs = acc["gather_bytes"] / (g_ms * 1e-3) / 1e9
-    traffic = read_traffic(acc["gather_bytes"])
-    kernel = "gather_kernel" if args.workload == "eviction" else "reindex_kernel"
+    traffic = read_traffic(args.workload)
+    kernel = KERNELS[args.workload][0]
     rec = {
         "metric": "compacted KV GB/s (read+write) per prune step, % of HBM peak; tokens scored/s",
         "value": round(gbs, 2),
@@ -329,7 +559,7 @@ def main():
                      "traffic": traffic, "bytes_per_launch": acc["gather_bytes"],
                      "launch_ms": round(g_ms, 4)},
     }
-    rec["copy_ceiling_gbs"] = round(copy_ceiling(dev), 2)
+    rec["copy_ceiling_gbs"] = round(copy_ceiling(dev, CALIB_BYTES), 2)
     if cpu is not None and not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu(args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -1,0 +1,328 @@
+"""GPU parity at the full sizes of the five workloads, in the launch
+configuration bench.py times (one gather launch over all layers, K and V).
+
+Mask, kept-index list, counts, offsets and frame phases are compared with the
+oracle on every row; gathered / re-indexed K and V on sampled rows, whose
+expected values the oracle computes one by one from inputs regenerated on the
+host (the key/value generator is counter-based).  Bars: bit-exact for masks,
+indices and V; keys within max-abs 2e-2 (bf16) / 1e-5 (fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import compaction_dp_score_amd as dp
+import dpsynth
+import oracle
+from compaction_dp_score_amd.step import PruneStep
+from gpu_helpers import bits, device, keys_close
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _sample_rows(n, boundaries, k=48, seed=0):
+    rng = np.random.default_rng(seed)
+    pts = {0, 1, n - 2, n - 1}
+    for b in boundaries:
+        for d in (-2, -1, 0, 1):
+            if 0 <= b + d < n:
+                pts.add(int(b + d))
+    pts.update(int(x) for x in rng.integers(0, n, k))
+    return np.array(sorted(p for p in pts if 0 <= p < n), np.int64)
+
+
+def _fill(dev, w, rows, layers, stream_id):
+    out = []
+    for l in layers:
+        t = torch.empty((rows, w.n_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        dpsynth.kv_fill_device(t, "bf16", w.seed, stream_id, l, rows, w.n_heads * w.head_dim)
+        out.append(t)
+    return out
+
+
+def _expected_rows(w, layer, stream_id, src_rows, total_rows):
+    r = dpsynth.kv_rows_host("bf16", w.seed, stream_id, layer, src_rows, total_rows,
+                             w.n_heads * w.head_dim)
+    return np.ascontiguousarray(r.reshape(len(src_rows), w.n_heads, w.head_dim))
+
+
+def _rope_host(w, q0=None):
+    theta = dpsynth.rope_theta(w.rope_pairs, w.rope_base)
+    ft, fp = dpsynth.frame_tables(w)
+    return dict(theta=theta, frame_t=ft, frame_phase=fp, q0=w.q0 if q0 is None else q0,
+                knee=w.rope_knee, inv_factor=np.float32(1.0 / w.rope_factor))
+
+
+def _rope_dev(host, dev):
+    return dict(theta=torch.from_numpy(host["theta"]).to(dev),
+                frame_t=torch.from_numpy(host["frame_t"]).to(dev),
+                frame_phase=torch.from_numpy(host["frame_phase"].copy()).to(dev),
+                q0=host["q0"], knee=host["knee"], inv_factor=float(host["inv_factor"]))
+
+
+def _tables(host):
+    return oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
+                              host["inv_factor"], host["theta"])
+
+
+def test_eviction_step_full_size():
+    """40 layers x 40 heads x 128 bf16, K and V, 31,200 tokens; score, mask,
+    index and gather with the fused re-index in one step."""
+    dev = device()
+    w = dpsynth.WORKLOADS["eviction"]
+    T, L = w.seq_len, w.n_layers
+    x0, xf = dpsynth.score_inputs(w)
+    k_src = _fill(dev, w, T, range(L), dpsynth.STREAM_K)
+    v_src = _fill(dev, w, T, range(L), dpsynth.STREAM_V)
+    k_dst = [torch.empty_like(t) for t in k_src]
+    v_dst = [torch.empty_like(t) for t in v_src]
+    host = _rope_host(w)
+    rope = _rope_dev(host, dev)
+    rf = dpsynth.row_frame(w)
+    step = PruneStep(k_src=k_src, v_src=v_src, k_dst=k_dst, v_dst=v_dst, seq_len=T,
+                     sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
+                     n_scored=w.n_scored, gamma=w.gamma, d=w.d,
+                     row_frame=torch.from_numpy(rf).to(dev), rope=rope, keep_ell=True)
+    step.run(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev))
+    torch.cuda.synchronize()
+
+    ell = oracle.score_f32(x0, xf, w.d)
+    keep = oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin, w.n_scored, w.gamma)
+    idx = oracle.compact(keep)
+    n = idx.shape[0]
+    assert np.array_equal(step.ell.cpu().numpy().view(np.uint32), ell.view(np.uint32))
+    assert np.array_equal(step.keep.cpu().numpy(), keep)
+    assert int(step.n_kept.item()) == n and int(step.dev_error.item()) == 0
+    assert np.array_equal(step.idx[:n].cpu().numpy(), idx)
+    tables = _tables(host)
+    assert np.array_equal(rope["frame_phase"].cpu().numpy(), tables[3])
+    rf2 = oracle.gather_i32(rf, idx)
+    assert np.array_equal(step.row_frame_dst[:n].cpu().numpy(), rf2)
+    # PR of this step (pruning ratio against FullKV)
+    c = dp.dp_pr_counter()
+    dp.dp_pr_add(c, L * w.n_heads * n, L * w.n_heads * T)
+    assert abs(dp.dp_pr_value(c) - oracle.pr(n, T)) < 1e-15
+
+    js = _sample_rows(n, [w.sink_len, int(np.searchsorted(idx, T - w.window_len))])
+    inexact = 0
+    for l in (0, 13, 27, L - 1):
+        got_k = bits(k_dst[l][torch.from_numpy(js).to(dev)])
+        got_v = bits(v_dst[l][torch.from_numpy(js).to(dev)])
+        want_v = _expected_rows(w, l, dpsynth.STREAM_V, idx[js], T)
+        want_k = _expected_rows(w, l, dpsynth.STREAM_K, idx[js], T)
+        oracle.rope_rows(want_k, rf2[js], 0, tables)
+        assert np.array_equal(got_v, want_v), l
+        ok, worst, ne = keys_close(got_k, want_k, TOL_BF16)
+        assert ok, (l, worst)
+        inexact += ne
+    print("eviction: %d kept, %d non-identical sampled key elements" % (n, inexact))
+    del step, k_src, v_src, k_dst, v_dst
+    _free()
+
+
+def test_reindex_full_size():
+    """Re-index of the retained cache of a one-minute history: 40 x 40 x 128
+    bf16 keys, 240 frames, q0 = 240, knee 12, factor 8."""
+    dev = device()
+    w = dpsynth.WORKLOADS["reindex"]
+    L, H, D = w.n_layers, w.n_heads, w.head_dim
+    kept = np.flatnonzero(dpsynth.retained_keep(w))
+    rows = kept.shape[0]
+    rf = dpsynth.row_frame(w)[kept].astype(np.int32)
+    ks = _fill(dev, w, rows, range(L), dpsynth.STREAM_K)
+    host = _rope_host(w)
+    rd = _rope_dev(host, dev)
+    rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
+                        host["inv_factor"])
+    ws = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                     dtype=torch.float32, device=dev)
+    arr = dp.ptr_array(ks, dev)
+    dp.dp_rope_reindex(arr, L, H, D, dp.DP_BF16, rows, None, torch.from_numpy(rf).to(dev), rope, ws)
+    torch.cuda.synchronize()
+    tables = _tables(host)
+    assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
+    js = _sample_rows(rows, [w.sink_len, int(np.searchsorted(kept, w.seq_len - w.window_len))],
+                      seed=1)
+    inexact = 0
+    for l in (0, 19, L - 1):
+        got = bits(ks[l][torch.from_numpy(js).to(dev)])
+        want = _expected_rows(w, l, dpsynth.STREAM_K, js, rows)
+        oracle.rope_rows(want, rf[js], 0, tables)
+        ok, worst, ne = keys_close(got, want, TOL_BF16)
+        assert ok, (l, worst)
+        inexact += ne
+    print("reindex: %d retained rows, %d non-identical sampled key elements" % (rows, inexact))
+    del ks
+    _free()
+
+
+def test_prefix_full_size_slab():
+    """Prefix pruning: 361,920 tokens, 57 scored chunks, one 20-layer slab of
+    K and V (the 40-layer cache exceeds one GPU's memory)."""
+    dev = device()
+    w = dpsynth.WORKLOADS["prefix"]
+    T, H, D = w.seq_len, w.n_heads, w.head_dim
+    slab = list(range(20, 40))                 # the second slab
+    x0, xf = dpsynth.score_inputs(w)
+    ell = oracle.score_f32(x0, xf, w.d)
+    keep = oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin, w.n_scored, w.gamma)
+    idx = oracle.compact(keep)
+    n = idx.shape[0]
+    k_src = _fill(dev, w, T, slab, dpsynth.STREAM_K)
+    v_src = _fill(dev, w, T, slab, dpsynth.STREAM_V)
+    k_dst = [torch.empty((n, H, D), dtype=torch.bfloat16, device=dev) for _ in slab]
+    v_dst = [torch.empty((n, H, D), dtype=torch.bfloat16, device=dev) for _ in slab]
+    step = PruneStep(k_src=k_src, v_src=v_src, k_dst=k_dst, v_dst=v_dst, seq_len=T,
+                     sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
+                     n_scored=w.n_scored, gamma=w.gamma, d=w.d, keep_ell=True)
+    step.run(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(step.ell.cpu().numpy().view(np.uint32), ell.view(np.uint32))
+    assert np.array_equal(step.keep.cpu().numpy(), keep)
+    assert int(step.n_kept.item()) == n and int(step.dev_error.item()) == 0
+    assert np.array_equal(step.idx[:n].cpu().numpy(), idx)
+    # per-chunk keep rates vary widely by construction
+    rates = keep[w.sink_len:].reshape(-1, w.chunk_tokens).mean(axis=1)
+    assert rates.min() < 0.05 and rates.max() > 0.4
+    js = _sample_rows(n, [w.sink_len, n // 2], seed=2)
+    for i, l in ((0, slab[0]), (len(slab) - 1, slab[-1])):
+        sel = torch.from_numpy(js).to(dev)
+        assert np.array_equal(bits(k_dst[i][sel]), _expected_rows(w, l, dpsynth.STREAM_K, idx[js], T))
+        assert np.array_equal(bits(v_dst[i][sel]), _expected_rows(w, l, dpsynth.STREAM_V, idx[js], T))
+    del step, k_src, v_src, k_dst, v_dst
+    _free()
+
+
+def test_hs_full_size():
+    """DeCoPrune-HS: 40 x 40 x 128 bf16, 187,200 tokens, seeded half of the
+    heads static per layer; ragged per-head output with the fused re-index."""
+    dev = device()
+    w = dpsynth.WORKLOADS["hs"]
+    T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
+    x0, xf = dpsynth.score_inputs(w)
+    cls = dpsynth.hs_head_class(w)
+    rf = dpsynth.row_frame(w)
+    # oracle: class lists and offsets
+    ell = oracle.score_f32(x0, xf, w.d)
+    lst_s = oracle.compact(oracle.mask(None, T, w.sink_len, w.window_len, w.scored_begin,
+                                       w.n_scored, w.gamma, streaming=True))
+    lst_d = oracle.compact(oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin,
+                                       w.n_scored, w.gamma))
+    lens = np.array([len(lst_s), len(lst_d)], np.int64)
+    off = oracle.hs_offsets(cls, lens)
+    # GPU
+    head_class = torch.from_numpy(cls.ravel().copy()).to(dev)
+    k_src = _fill(dev, w, T, range(L), dpsynth.STREAM_K)
+    v_src = _fill(dev, w, T, range(L), dpsynth.STREAM_V)
+    x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
+    keeps = [torch.empty(T, dtype=torch.uint8, device=dev) for _ in range(2)]
+    dp.dp_score_mask(None, None, w.d, w.d, dp.make_policy(T, w.sink_len, w.window_len,
+                     w.scored_begin, w.n_scored, w.gamma, mode=dp.DP_MODE_STREAMING), None, keeps[0])
+    dp.dp_score_mask(x0d, xfd, w.d, w.d, dp.make_policy(T, w.sink_len, w.window_len,
+                     w.scored_begin, w.n_scored, w.gamma), None, keeps[1])
+    lists = [torch.empty(T, dtype=torch.int32, device=dev) for _ in range(2)]
+    rfs = [torch.empty(T, dtype=torch.int32, device=dev) for _ in range(2)]
+    glens = torch.zeros(2, dtype=torch.int64, device=dev)
+    ws_c = torch.empty(dp.dp_compact_workspace_bytes(T) // 4 + 1, dtype=torch.int32, device=dev)
+    rf_d = torch.from_numpy(rf).to(dev)
+    for c in range(2):
+        dp.dp_compact_index(keeps[c], T, lists[c], glens[c:c + 1], rf_d, rfs[c], ws_c)
+    offsets = torch.empty(L * H + 1, dtype=torch.int64, device=dev)
+    dp.dp_hs_offsets(head_class, L, H, glens, 2, offsets)
+    torch.cuda.synchronize()
+    assert np.array_equal(glens.cpu().numpy(), lens)
+    assert np.array_equal(offsets.cpu().numpy(), off)
+    total = int(off[-1])
+    k_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    v_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    kv = dp.dp_kv_hs()
+    arrs = [dp.ptr_array(k_src, dev), dp.ptr_array(v_src, dev)]
+    kv.k_src, kv.v_src = arrs[0].data_ptr(), arrs[1].data_ptr()
+    kv.k_out, kv.v_out = k_out.data_ptr(), v_out.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dp.DP_BF16
+    kv.src_rows, kv.out_capacity = T, total
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    host = _rope_host(w)
+    rd = _rope_dev(host, dev)
+    rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
+                        host["inv_factor"])
+    ws = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                     dtype=torch.float32, device=dev)
+    dp.dp_hs_gather_kv(kv, head_class, 2, dp.ptr_array(lists, dev), glens, [T, T], offsets,
+                       dp.ptr_array(rfs, dev), rope, ws)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    tables = _tables(host)
+    assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
+    rng = np.random.default_rng(3)
+    inexact = 0
+    for l, h in [(0, 0), (7, 13), (21, 39), (L - 1, H - 1)] + [
+            (int(a), int(b)) for a, b in zip(rng.integers(0, L, 6), rng.integers(0, H, 6))]:
+        i = l * H + h
+        lst = lst_s if cls[l, h] == 0 else lst_d
+        js = _sample_rows(len(lst), [w.sink_len], k=24, seed=i)
+        src_rows = lst[js]
+        want_k = _expected_rows(w, l, dpsynth.STREAM_K, src_rows, T)[:, h, :].copy()
+        want_v = _expected_rows(w, l, dpsynth.STREAM_V, src_rows, T)[:, h, :].copy()
+        oracle.rope_headrows(want_k, rf[src_rows], 0, tables)
+        sel = torch.from_numpy(off[i] + js).to(dev)
+        assert np.array_equal(bits(v_out[sel]), want_v), (l, h)
+        ok, worst, ne = keys_close(bits(k_out[sel]), want_k, TOL_BF16)
+        assert ok, (l, h, worst)
+        inexact += ne
+    print("hs: %d head rows, PR %.4f, %d non-identical sampled key elements"
+          % (total, 1 - total / (L * H * T), inexact))
+    del k_src, v_src, k_out, v_out
+    _free()
+
+
+@pytest.mark.parametrize("reversed_", [False, True])
+def test_tiny_workload_every_row(reversed_):
+    """The tiny workload (1 layer, 2 heads, head_dim 64, fp32, 8 chunks of 64
+    tokens, d = 16): every output row against the oracle, for the criterion and
+    for the reversed one (its complement on the scored rows)."""
+    dev = device()
+    w = dpsynth.WORKLOADS["tiny"]
+    T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
+    x0, xf = dpsynth.score_inputs(w)
+    kh = np.stack([dpsynth.kv_layer_host("f32", w.seed, dpsynth.STREAM_K, l, T, H * D)
+                   for l in range(L)]).reshape(L, T, H, D)
+    vh = np.stack([dpsynth.kv_layer_host("f32", w.seed, dpsynth.STREAM_V, l, T, H * D)
+                   for l in range(L)]).reshape(L, T, H, D)
+    rf = dpsynth.row_frame(w)
+    host = _rope_host(w)
+    rope = _rope_dev(host, dev)
+    k_src = [torch.from_numpy(kh[l]).to(dev) for l in range(L)]
+    v_src = [torch.from_numpy(vh[l]).to(dev) for l in range(L)]
+    k_dst = [torch.zeros_like(t) for t in k_src]
+    v_dst = [torch.zeros_like(t) for t in v_src]
+    step = PruneStep(k_src=k_src, v_src=v_src, k_dst=k_dst, v_dst=v_dst, seq_len=T,
+                     sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
+                     n_scored=w.n_scored, gamma=w.gamma, d=w.d, reversed=reversed_,
+                     row_frame=torch.from_numpy(rf).to(dev), rope=rope, keep_ell=True)
+    step.run(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev))
+    torch.cuda.synchronize()
+    pol = dict(seq_len=T, sink_len=w.sink_len, window_len=w.window_len,
+               scored_begin=w.scored_begin, n_scored=w.n_scored, gamma=w.gamma,
+               reversed=reversed_)
+    want = oracle.prune_step(x0, xf, w.d, pol, kh, vh, rf, host)
+    n = want["idx"].shape[0]
+    assert np.array_equal(step.keep.cpu().numpy(), want["keep"])
+    assert int(step.n_kept.item()) == n
+    assert np.array_equal(step.idx[:n].cpu().numpy(), want["idx"])
+    for l in range(L):
+        assert np.array_equal(bits(v_dst[l][:n]), want["v"][l].view(np.uint32))
+        ok, worst, ne = keys_close(bits(k_dst[l][:n]), want["k"][l].view(np.uint32), 1e-5)
+        assert ok, worst
+        assert np.all(bits(k_dst[l][n:]) == 0)
+    # the sink chunk and the window are kept, whatever the criterion
+    assert np.all(want["keep"][:w.sink_len] == 1) and np.all(want["keep"][T - w.window_len:] == 1)
+    print("tiny (reversed=%s): %d of %d kept, PR %.4f" % (reversed_, n, T, oracle.pr(n, T)))

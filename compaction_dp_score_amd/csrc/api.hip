@@ -68,12 +68,6 @@ dp_status check_rope(const dp_rope* r, int32_t head_dim, int32_t dtype, const vo
   return DP_OK;
 }
 
-int64_t tv_count_of(const dp_rope* r, int32_t dtype) {
-  const int esz = elem_size(dtype);
-  const int64_t b = (2 * (int64_t)r->pair_begin * esz) / 16;
-  const int64_t e = (2 * ((int64_t)r->pair_begin + r->n_pairs) * esz + 15) / 16;
-  return e - b;
-}
 
 }  // namespace
 }  // namespace dp
@@ -205,10 +199,10 @@ dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_hea
   if (st != DP_OK) return st;
   st = check_rope(rope, head_dim, dtype, ws, ws_bytes, "dp_rope_reindex");
   if (st != DP_OK) return st;
-  if (n_layers > 65535) return fail(DP_ERANGE, "dp_rope_reindex: too many layers");
-  if (rows_capacity < 0 || rows_capacity >= kMaxRows ||
-      rows_capacity * n_heads * tv_count_of(rope, dtype) >= kMaxVec)
-    return fail(DP_ERANGE, "dp_rope_reindex: rows_capacity out of range");
+  const int64_t per_row = (int64_t)n_heads * (head_dim * elem_size(dtype) / 16);
+  if (rows_capacity < 0 || rows_capacity >= kMaxRows || rows_capacity * per_row >= kMaxVec ||
+      (rows_capacity * per_row + 255) / 256 * n_layers >= kMaxVec)
+    return fail(DP_ERANGE, "dp_rope_reindex: rows_capacity x layers out of range");
   if (n_rows && !aligned(n_rows, 8)) return fail(DP_EALIGN, "dp_rope_reindex: n_rows alignment");
   (void)hipGetLastError();
   hipStream_t s = (hipStream_t)stream;
@@ -253,9 +247,8 @@ static dp_status check_hs_common(int32_t n_layers, int32_t n_heads, int32_t head
   for (int c = 0; c < n_classes; ++c)
     if (class_cap[c] < 0 || class_cap[c] >= kMaxRows)
       return fail(DP_ERANGE, "%s: class_capacity[%d] outside [0, 2^31)", who, c);
-  if (hs_tiles(class_cap, n_classes) >= ((uint64_t)1 << 31))
-    return fail(DP_ERANGE, "%s: class capacities too large", who);
-  if (n_layers > 65535 / 2) return fail(DP_ERANGE, "%s: too many layers", who);
+  if (hs_tiles(class_cap, n_classes) * (uint64_t)n_layers * 2 >= ((uint64_t)1 << 31))
+    return fail(DP_ERANGE, "%s: class capacities x layers too large for one launch", who);
   return DP_OK;
 }
 

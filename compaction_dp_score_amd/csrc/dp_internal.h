@@ -134,6 +134,13 @@ struct RopeView {
   int32_t tv_begin;    // first 16-byte vector of the temporal block in a head row
   int32_t tv_count;    // vectors touched by the temporal block
   int32_t ppv;         // pairs per 16-byte vector: 4 (bf16) or 2 (fp32)
+  // In-place passes rewrite whole 128-byte lines: vectors [wv_begin,
+  // wv_begin + wv_count) of a head row cover the temporal block rounded out to
+  // 128-byte boundaries (clamped to the head row); vectors outside the block
+  // are written back unchanged.  A partly written line costs the memory
+  // controller a read-modify-write, which measured slower than the extra bytes.
+  int32_t wv_begin;
+  int32_t wv_count;
 };
 
 // ---------------------------------------------------------------------------

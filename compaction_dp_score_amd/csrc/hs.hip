@@ -11,8 +11,8 @@
 //   kRT head rows (head_dim elements each) to that head's contiguous run in the
 //   packed output, so every head's writes are kRT * head-row bytes contiguous.
 //   Optionally re-rotates the temporal K vectors on the way.
-// hs_reindex_kernel: the same walk over a packed ragged K cache, touching only
-//   the temporal vectors, in place.
+// hs_reindex_kernel: the same walk over a packed ragged K cache, in place,
+//   rewriting the whole 128-byte lines that hold the temporal pairs.
 #include "dp_internal.h"
 
 namespace dp {
@@ -71,9 +71,9 @@ struct HsArgs {
   int64_t src_rows;
   int64_t out_cap;
   int64_t class_cap[DP_HS_MAX_CLASSES];
-  uint32_t tile_base[DP_HS_MAX_CLASSES + 1];
   int32_t n_classes;
   int32_t n_heads;
+  int32_t n_layers;
   int32_t n_kv;
   int32_t dtype;
   int32_t has_rope;
@@ -82,93 +82,161 @@ struct HsArgs {
   RopeView rope;
 };
 
-// Common prologue: class, first entry, live rows, head list of the class in
-// this layer.  Returns the number of heads (0: nothing to do).
-__device__ int hs_setup(const HsArgs& a, int layer, int& cls, int64_t& j0, int& rows,
-                        int* heads, int64_t* head_off) {
-  cls = 0;
-  while (cls + 1 < a.n_classes && blockIdx.x >= a.tile_base[cls + 1]) ++cls;
-  j0 = (int64_t)(blockIdx.x - a.tile_base[cls]) * kRT;
-  int64_t len = a.class_len[cls];
-  if (len > a.class_cap[cls]) {
-    if (a.dev_error && blockIdx.x == a.tile_base[cls] && threadIdx.x == 0) *a.dev_error = DP_ECAPACITY;
-    len = a.class_cap[cls];
-  }
-  if (j0 >= len) return 0;
-  rows = (int)min((int64_t)kRT, len - j0);
-  __shared__ int nh_s;
-  if (threadIdx.x == 0) {
-    int nh = 0;
-    const uint8_t* hc = a.head_class + (int64_t)layer * a.n_heads;
-    for (int h = 0; h < a.n_heads; ++h)
-      if (hc[h] == cls) {
-        heads[nh] = h;
-        head_off[nh] = a.offsets[(int64_t)layer * a.n_heads + h];
-        ++nh;
+// Per-workgroup state shared by the gather and the re-index.
+struct HsTile {
+  int cls;          // class of this tile
+  int64_t j0;       // first entry of the class list
+  int rows;         // live entries in the tile (<= kRT)
+  int nh;           // heads of the class in this layer
+  int slab;         // (layer, K|V) index
+};
+
+// Maps the 1-D workgroup id to (slab, class, tile) using the device-side class
+// lengths, so live workgroups are dense at the front and surplus ones leave at
+// once; then lists the class's heads of this layer (a wavefront ballot, in head
+// order) with their output offsets, and each tile row's source index, frame and
+// phase step, all into LDS.  Returns false when the workgroup has no work.
+__device__ bool hs_setup(const HsArgs& a, int n_slab_per_layer, HsTile& tl, int* heads,
+                         int64_t* head_off, int32_t* s_src, int* s_f, float* s_dl) {
+  uint32_t pre[DP_HS_MAX_CLASSES + 1];
+  int64_t lens[DP_HS_MAX_CLASSES];
+  pre[0] = 0;
+  bool overflow = false;
+#pragma unroll
+  for (int c = 0; c < DP_HS_MAX_CLASSES; ++c) {
+    int64_t len = 0;
+    if (c < a.n_classes) {
+      len = a.class_len[c];
+      if (len > a.class_cap[c]) {
+        overflow = true;
+        len = a.class_cap[c];
       }
-    nh_s = nh;
+      if (len < 0) len = 0;
+    }
+    lens[c] = len;
+    pre[c + 1] = pre[c] + (uint32_t)((len + kRT - 1) / kRT);
+  }
+  if (overflow && a.dev_error && blockIdx.x == 0 && threadIdx.x == 0) *a.dev_error = DP_ECAPACITY;
+  const uint32_t live = pre[a.n_classes];
+  if (live == 0) return false;
+  const uint32_t slab = blockIdx.x / live;
+  if (slab >= (uint32_t)(a.n_layers * n_slab_per_layer)) return false;
+  const uint32_t r = blockIdx.x - slab * live;
+  int cls = 0;
+#pragma unroll
+  for (int c = 1; c < DP_HS_MAX_CLASSES; ++c)
+    if (c < a.n_classes && r >= pre[c]) cls = c;
+  tl.cls = cls;
+  tl.slab = (int)slab;
+  tl.j0 = (int64_t)(r - pre[cls]) * kRT;
+  tl.rows = (int)min((int64_t)kRT, lens[cls] - tl.j0);
+  const int layer = (int)slab / n_slab_per_layer;
+
+  __shared__ int nh_s;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {                      // wave 0: the class's heads, in order
+    const uint8_t* hc = a.head_class + (int64_t)layer * a.n_heads;
+    int base = 0;
+    for (int h0 = 0; h0 < a.n_heads; h0 += 64) {
+      const int h = h0 + lane;
+      const bool m = h < a.n_heads && hc[h] == cls;
+      const uint64_t mask = __ballot(m);
+      if (m) {
+        const int rank = base + __popcll(mask & (lane == 0 ? 0ull : (~0ull >> (64 - lane))));
+        heads[rank] = h;
+        head_off[rank] = a.offsets[(int64_t)layer * a.n_heads + h];
+      }
+      base += __popcll(mask);
+    }
+    if (lane == 0) nh_s = base;
+  } else if (threadIdx.x < 64 + kRT) {         // wave 1: the tile rows
+    const int rr = threadIdx.x - 64;
+    int32_t src = -1;
+    int f = 0;
+    float dl = 0.0f;
+    if (rr < tl.rows) {
+      const int64_t j = tl.j0 + rr;
+      if (a.class_idx) src = a.class_idx[cls][j];
+      if (a.has_rope) {
+        f = a.class_rf[cls][j];
+        if ((uint32_t)f < (uint32_t)a.rope.n_frames) dl = a.rope.delta[f];
+        else f = 0;
+      }
+    }
+    s_src[rr] = src;
+    s_f[rr] = f;
+    s_dl[rr] = dl;
   }
   __syncthreads();
-  return nh_s;
+  tl.nh = nh_s;
+  return tl.nh > 0;
 }
 
 template <int U>
 __global__ __launch_bounds__(kBlock) void hs_gather_kernel(HsArgs a) {
   __shared__ int heads[kMaxHeads];
   __shared__ int64_t head_off[kMaxHeads];
-  const int layer = blockIdx.y / a.n_kv;
-  const bool is_v = (blockIdx.y % a.n_kv) == 1;
-  int cls, rows;
-  int64_t j0;
-  const int nh = hs_setup(a, layer, cls, j0, rows, heads, head_off);
-  if (nh == 0) return;
+  __shared__ int32_t s_src[kRT];
+  __shared__ int s_f[kRT];
+  __shared__ float s_dl[kRT];
+  HsTile tl;
+  if (!hs_setup(a, a.n_kv, tl, heads, head_off, s_src, s_f, s_dl)) return;
+  const int layer = tl.slab / a.n_kv;
+  const bool is_v = (tl.slab % a.n_kv) == 1;
   const u32x4* __restrict__ src =
       reinterpret_cast<const u32x4*>(is_v ? a.v_src[layer] : a.k_src[layer]);
   u32x4* __restrict__ out = reinterpret_cast<u32x4*>(is_v ? a.v_out : a.k_out);
-  const int32_t* __restrict__ list = a.class_idx[cls];
-  const int32_t* __restrict__ rf = a.has_rope ? a.class_rf[cls] : nullptr;
   const bool rope = a.has_rope && !is_v;
-  const uint32_t per_head = (uint32_t)kRT * a.vph;
-  const uint32_t total = (uint32_t)nh * per_head;
+  const uint32_t total = (uint32_t)tl.nh * kRT * a.vph;
   bool overflow = false;
-  for (uint32_t base = 0; base < total; base += kBlock * U) {
+  for (uint32_t b0 = 0; b0 < total; b0 += kBlock * U) {
     u32x4 v[U];
     int64_t dst_i[U];
+    f32x4 t01[U], t23[U];
+    int nv[U];
+    bool rot[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t i = base + u * kBlock + threadIdx.x;
+      const uint32_t i = b0 + u * kBlock + threadIdx.x;
       dst_i[u] = -1;
+      rot[u] = false;
       if (i < total) {
         const uint32_t t = fdiv(i, a.div_inner);           // (head, row)
         const uint32_t q = i - t * a.div_inner.d;           // vector in the head row
         const int r = (int)(t & (kRT - 1));
         const int k = (int)(t >> kLogRT);
-        if (r < rows) {
-          const int64_t j = j0 + r;
-          const int32_t s = list[j];
-          const int64_t o = head_off[k] + j;
+        const int32_t s = s_src[r];
+        if (r < tl.rows && (uint32_t)s < (uint64_t)a.src_rows) {
+          const int64_t o = head_off[k] + tl.j0 + r;
           if (o >= a.out_cap) {
             overflow = true;
-          } else if ((uint32_t)s < (uint64_t)a.src_rows) {
-            v[u] = src[((int64_t)s * a.n_heads + heads[k]) * a.vph + q];
+          } else {
+            dst_i[u] = o * a.vph + q;
             if (rope) {
               const int tv = (int)q - a.rope.tv_begin;
-              const int f = rf[j];
-              if (tv >= 0 && tv < a.rope.tv_count && (uint32_t)f < (uint32_t)a.rope.n_frames &&
-                  a.rope.delta[f] != 0.0f) {
+              if (tv >= 0 && tv < a.rope.tv_count && s_dl[r] != 0.0f) {
                 const int p0 = tv * a.rope.ppv;
-                const int nv = min(a.rope.ppv, a.rope.n_pairs - p0);
-                v[u] = rotate_vec(v[u], a.dtype, a.rope.cs + (int64_t)f * a.rope.pairs_padded + p0, nv);
+                nv[u] = min(a.rope.ppv, a.rope.n_pairs - p0);
+                const f32x4* tp = reinterpret_cast<const f32x4*>(
+                    a.rope.cs + (int64_t)s_f[r] * a.rope.pairs_padded + p0);
+                t01[u] = tp[0];
+                t23[u] = tp[1];
+                rot[u] = true;
               }
             }
-            dst_i[u] = o * a.vph + q;
+            v[u] = __builtin_nontemporal_load(src + ((int64_t)s * a.n_heads + heads[k]) * a.vph + q);
           }
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (dst_i[u] >= 0) __builtin_nontemporal_store(v[u], out + dst_i[u]);
+    for (int u = 0; u < U; ++u) {
+      if (dst_i[u] >= 0) {
+        u32x4 w = v[u];
+        if (rot[u]) w = rotate_vec_tab(w, a.dtype, t01[u], t23[u], nv[u]);
+        __builtin_nontemporal_store(w, out + dst_i[u]);
+      }
+    }
   }
   if (overflow && a.dev_error) *a.dev_error = DP_ECAPACITY;
 }
@@ -177,62 +245,58 @@ template <int U>
 __global__ __launch_bounds__(kBlock) void hs_reindex_kernel(HsArgs a) {
   __shared__ int heads[kMaxHeads];
   __shared__ int64_t head_off[kMaxHeads];
-  const int layer = blockIdx.y;
-  int cls, rows;
-  int64_t j0;
-  const int nh = hs_setup(a, layer, cls, j0, rows, heads, head_off);
-  if (nh == 0) return;
+  __shared__ int32_t s_src[kRT];
+  __shared__ int s_f[kRT];
+  __shared__ float s_dl[kRT];
+  HsTile tl;
+  if (!hs_setup(a, 1, tl, heads, head_off, s_src, s_f, s_dl)) return;
+  bool any = false;
+  for (int r = 0; r < tl.rows; ++r) any = any || s_dl[r] != 0.0f;
+  if (!any) return;
   u32x4* __restrict__ kbuf = reinterpret_cast<u32x4*>(a.k_out);
-  const int32_t* __restrict__ rf = a.class_rf[cls];
-  const uint32_t total = (uint32_t)nh * kRT * a.div_inner.d;
-  for (uint32_t base = 0; base < total; base += kBlock * U) {
+  const uint32_t total = (uint32_t)tl.nh * kRT * a.div_inner.d;
+  for (uint32_t b0 = 0; b0 < total; b0 += kBlock * U) {
     u32x4 v[U];
     int64_t at[U];
-    int fr[U], tvs[U];
+    f32x4 t01[U], t23[U];
+    int nv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t i = base + u * kBlock + threadIdx.x;
+      const uint32_t i = b0 + u * kBlock + threadIdx.x;
       at[u] = -1;
       if (i < total) {
         const uint32_t t = fdiv(i, a.div_inner);
-        const int tv = (int)(i - t * a.div_inner.d);
+        const int wq = a.rope.wv_begin + (int)(i - t * a.div_inner.d);   // vector in the head row
         const int r = (int)(t & (kRT - 1));
         const int k = (int)(t >> kLogRT);
-        if (r < rows) {
-          const int64_t j = j0 + r;
-          const int f = rf[j];
-          const int64_t o = head_off[k] + j;
-          if (o < a.out_cap && (uint32_t)f < (uint32_t)a.rope.n_frames && a.rope.delta[f] != 0.0f) {
-            at[u] = o * a.vph + a.rope.tv_begin + tv;
-            fr[u] = f;
-            tvs[u] = tv;
+        if (r < tl.rows && s_dl[r] != 0.0f) {
+          const int64_t o = head_off[k] + tl.j0 + r;
+          if (o < a.out_cap) {
+            at[u] = o * a.vph + wq;
+            const int tv = wq - a.rope.tv_begin;
+            const bool in_block = tv >= 0 && tv < a.rope.tv_count;
+            const int p0 = in_block ? tv * a.rope.ppv : 0;
+            nv[u] = in_block ? min(a.rope.ppv, a.rope.n_pairs - p0) : 0;
+            const f32x4* tp = reinterpret_cast<const f32x4*>(
+                a.rope.cs + (int64_t)s_f[r] * a.rope.pairs_padded + p0);
+            t01[u] = tp[0];
+            t23[u] = tp[1];
             v[u] = __builtin_nontemporal_load(kbuf + at[u]);
           }
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (at[u] >= 0) {
-        const int p0 = tvs[u] * a.rope.ppv;
-        const int nv = min(a.rope.ppv, a.rope.n_pairs - p0);
-        __builtin_nontemporal_store(
-            rotate_vec(v[u], a.dtype, a.rope.cs + (int64_t)fr[u] * a.rope.pairs_padded + p0, nv),
-            kbuf + at[u]);
-      }
-    }
+    for (int u = 0; u < U; ++u)
+      if (at[u] >= 0)
+        __builtin_nontemporal_store(rotate_vec_tab(v[u], a.dtype, t01[u], t23[u], nv[u]),
+                                    kbuf + at[u]);
   }
 }
 
-void fill_tiles(HsArgs& a, const int64_t* class_cap, int32_t n_classes) {
+void fill_caps(HsArgs& a, const int64_t* class_cap, int32_t n_classes) {
   a.n_classes = n_classes;
-  uint32_t acc = 0;
-  for (int c = 0; c < DP_HS_MAX_CLASSES; ++c) {
-    a.tile_base[c] = acc;
-    a.class_cap[c] = c < n_classes ? class_cap[c] : 0;
-    if (c < n_classes) acc += (uint32_t)((class_cap[c] + kRT - 1) / kRT);
-  }
-  a.tile_base[DP_HS_MAX_CLASSES] = acc;
+  for (int c = 0; c < DP_HS_MAX_CLASSES; ++c) a.class_cap[c] = c < n_classes ? class_cap[c] : 0;
 }
 
 }  // namespace
@@ -272,42 +336,45 @@ dp_status launch_hs_gather(const dp_kv_hs& kv, const uint8_t* head_class, int32_
   a.src_rows = kv.src_rows;
   a.out_cap = kv.out_capacity;
   a.n_heads = kv.n_heads;
+  a.n_layers = kv.n_layers;
   a.n_kv = kv.v_src ? 2 : 1;
   a.dtype = kv.dtype;
   a.has_rope = rope != nullptr;
   if (rope) a.rope = *rope;
   a.vph = (uint32_t)(kv.head_dim * elem_size(kv.dtype) / 16);
   a.div_inner = make_fastdiv(a.vph);
-  fill_tiles(a, class_cap, n_classes);
-  const uint32_t gx = a.tile_base[DP_HS_MAX_CLASSES];
+  fill_caps(a, class_cap, n_classes);
+  const uint64_t gx = hs_tiles(class_cap, n_classes) * (uint64_t)(kv.n_layers * a.n_kv);
   if (gx == 0) return DP_OK;
-  hipLaunchKernelGGL(hs_gather_kernel<4>, dim3(gx, kv.n_layers * a.n_kv), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(hs_gather_kernel<4>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("hs_gather_kernel");
 }
 
-dp_status launch_hs_reindex(void* k, int64_t k_cap, int32_t L, int32_t H, int32_t head_dim, int32_t dtype,
-                            const uint8_t* head_class, int32_t n_classes,
+dp_status launch_hs_reindex(void* k, int64_t k_cap, int32_t L, int32_t H, int32_t head_dim,
+                            int32_t dtype, const uint8_t* head_class, int32_t n_classes,
                             const int64_t* class_len, const int64_t* class_cap,
                             const int64_t* offsets, const int32_t* const* class_rf,
                             const RopeView& rope, hipStream_t s) {
   HsArgs a{};
   a.k_out = k;
   a.head_class = head_class;
+  a.class_idx = nullptr;
   a.class_rf = class_rf;
   a.class_len = class_len;
   a.offsets = offsets;
   a.out_cap = k_cap;
   a.n_heads = H;
+  a.n_layers = L;
   a.n_kv = 1;
   a.dtype = dtype;
   a.has_rope = 1;
   a.rope = rope;
   a.vph = (uint32_t)(head_dim * elem_size(dtype) / 16);
-  a.div_inner = make_fastdiv((uint32_t)rope.tv_count);
-  fill_tiles(a, class_cap, n_classes);
-  const uint32_t gx = a.tile_base[DP_HS_MAX_CLASSES];
+  a.div_inner = make_fastdiv((uint32_t)rope.wv_count);
+  fill_caps(a, class_cap, n_classes);
+  const uint64_t gx = hs_tiles(class_cap, n_classes) * (uint64_t)L;
   if (gx == 0) return DP_OK;
-  hipLaunchKernelGGL(hs_reindex_kernel<4>, dim3(gx, L), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(hs_reindex_kernel<4>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("hs_reindex_kernel");
 }
 

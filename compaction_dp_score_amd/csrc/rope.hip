@@ -7,9 +7,11 @@
 //   D = q0 - t, g(D), t~ = q0 - g(D), delta = t~ - p (p: phase the keys
 //   carry), and for each temporal pair j the {cos, sin} of theta_j * delta
 //   (fp32 angle, fp64 sincos, rounded to fp32); then p <- t~.
-// reindex_kernel: in place over the temporal 16-byte vectors of every
-//   (row, head) of each layer; rows of frames with delta == 0 are neither read
-//   nor written.  HBM-bound: 2 * 2*n_pairs*elem bytes per re-indexed head row.
+// reindex_kernel: in place over every (row, head) of each layer, touching the
+//   128-byte lines that hold the temporal pairs; rows of frames with delta == 0
+//   are neither read nor written.  HBM-bound: the method needs
+//   2 * 2*n_pairs*elem bytes per re-indexed head row; whole-line rewriting moves
+//   2 * (lines * 128) bytes (512 of 352 for 44 bf16 pairs).
 #include "dp_internal.h"
 
 namespace dp {
@@ -54,55 +56,72 @@ struct ReindexArgs {
   const int32_t* row_frame;
   const int64_t* n_rows;
   int64_t rows_cap;
-  FastDiv div_row;    // vectors per row  = H * tv_count
-  FastDiv div_head;   // vectors per head = tv_count
+  FastDiv div_row;    // vectors per row  = H * wv_count
+  FastDiv div_head;   // vectors per head = wv_count
   uint32_t vph;       // 16-byte vectors per head row
   uint32_t n_heads;
-  uint32_t total_cap; // rows_cap * H * tv_count
+  uint32_t n_layers;
   int32_t dtype;
   RopeView rope;
 };
 
-template <int U>
+// One 16-byte vector per lane over the written span of every (row, head) of
+// a layer; the 1-D grid is sized by capacity and each workgroup derives
+// (layer, tile) from the device-side row count, so surplus workgroups sit at
+// the tail.  With rows of >= kBlock vectors a workgroup spans at most two
+// rows: their frames and phase steps are uniform loads, and a workgroup whose
+// rows both have delta == 0 (the recent window) leaves before touching the
+// keys; otherwise each lane looks its row up.  The {cos, sin} loads go out
+// with the data load; vectors outside the temporal block are written back
+// unchanged so that whole 128-byte lines are rewritten.
+template <bool TWO_ROWS>
 __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
-  const uint32_t first = blockIdx.x * (kBlock * U);
   int64_t n = a.rows_cap;
   if (a.n_rows) n = min(n, *a.n_rows);
-  const uint32_t total = (uint32_t)min((int64_t)a.total_cap, n * (int64_t)a.div_row.d);
-  if (first >= total) return;
-  u32x4* base = reinterpret_cast<u32x4*>(a.layers[blockIdx.y]);
-  u32x4 v[U];
-  int64_t addr[U];
-  int frame[U];
-  uint32_t tv_of[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    uint32_t i = first + u * kBlock + threadIdx.x;
-    addr[u] = -1;
-    if (i < total) {
-      uint32_t j = fdiv(i, a.div_row);
-      uint32_t rem = i - j * a.div_row.d;
-      uint32_t h = fdiv(rem, a.div_head);
-      uint32_t tv = rem - h * a.div_head.d;
-      int f = a.row_frame[j];
-      // a frame outside the table is skipped rather than read out of bounds
-      if ((uint32_t)f < (uint32_t)a.rope.n_frames && a.rope.delta[f] != 0.0f) {
-        frame[u] = f;
-        tv_of[u] = tv;
-        addr[u] = ((int64_t)j * a.n_heads + h) * a.vph + a.rope.tv_begin + tv;
-        v[u] = __builtin_nontemporal_load(base + addr[u]);
-      }
-    }
+  const uint32_t per_row = a.div_row.d;
+  const uint32_t per_layer = (uint32_t)(n * (int64_t)per_row);
+  const uint32_t tiles = (per_layer + kBlock - 1) / kBlock;
+  if (tiles == 0) return;
+  const uint32_t layer = blockIdx.x / tiles;
+  if (layer >= a.n_layers) return;
+  const uint32_t first = (blockIdx.x - layer * tiles) * kBlock;
+  const uint32_t i = first + threadIdx.x;
+  float dl;
+  int f;
+  uint32_t j;
+  if (TWO_ROWS) {
+    const uint32_t ja = fdiv(first, a.div_row);
+    const uint32_t jb = (int64_t)ja + 1 < n ? ja + 1 : ja;
+    const int fa = a.row_frame[ja], fb = a.row_frame[jb];
+    // a frame outside the table is skipped rather than read out of bounds
+    const float da = (uint32_t)fa < (uint32_t)a.rope.n_frames ? a.rope.delta[fa] : 0.0f;
+    const float db = (uint32_t)fb < (uint32_t)a.rope.n_frames ? a.rope.delta[fb] : 0.0f;
+    if (da == 0.0f && db == 0.0f) return;
+    if (i >= per_layer) return;
+    j = fdiv(i, a.div_row);
+    dl = j == ja ? da : db;
+    f = j == ja ? fa : fb;
+  } else {
+    if (i >= per_layer) return;
+    j = fdiv(i, a.div_row);
+    f = a.row_frame[j];
+    dl = (uint32_t)f < (uint32_t)a.rope.n_frames ? a.rope.delta[f] : 0.0f;
   }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (addr[u] >= 0) {
-      int p0 = (int)tv_of[u] * a.rope.ppv;
-      int nv = min(a.rope.ppv, a.rope.n_pairs - p0);
-      const f32x2* cs = a.rope.cs + (int64_t)frame[u] * a.rope.pairs_padded + p0;
-      __builtin_nontemporal_store(rotate_vec(v[u], a.dtype, cs, nv), base + addr[u]);
-    }
-  }
+  if (dl == 0.0f) return;
+  const uint32_t rem = i - j * per_row;
+  const uint32_t h = fdiv(rem, a.div_head);
+  const int wq = a.rope.wv_begin + (int)(rem - h * a.div_head.d);   // vector in the head row
+  const int tv = wq - a.rope.tv_begin;
+  const bool in_block = tv >= 0 && tv < a.rope.tv_count;
+  const int p0 = in_block ? tv * a.rope.ppv : 0;
+  const f32x4* t = reinterpret_cast<const f32x4*>(a.rope.cs + (int64_t)f * a.rope.pairs_padded + p0);
+  const f32x4 t01 = t[0];     // the table has a 32-byte tail, so t[1] is readable
+  const f32x4 t23 = t[1];
+  u32x4* __restrict__ p =
+      reinterpret_cast<u32x4*>(a.layers[layer]) + ((int64_t)j * a.n_heads + h) * a.vph + wq;
+  u32x4 v = __builtin_nontemporal_load(p);
+  if (in_block) v = rotate_vec_tab(v, a.dtype, t01, t23, min(a.rope.ppv, a.rope.n_pairs - p0));
+  __builtin_nontemporal_store(v, p);
 }
 
 }  // namespace
@@ -133,7 +152,12 @@ dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dt
   view->tv_begin = (2 * r.pair_begin * esz) / 16;
   const int end_bytes = 2 * (r.pair_begin + r.n_pairs) * esz;
   view->tv_count = (end_bytes + 15) / 16 - view->tv_begin;
-  (void)head_dim;
+  const int vph = head_dim * esz / 16;
+  const int wb = view->tv_begin / 8 * 8;
+  int we = (view->tv_begin + view->tv_count + 7) / 8 * 8;
+  if (we > vph) we = vph;
+  view->wv_begin = wb;
+  view->wv_count = we - wb;
   return DP_OK;
 }
 
@@ -145,17 +169,19 @@ dp_status launch_reindex(void* const* k, int32_t n_layers, int32_t n_heads, int3
   a.row_frame = row_frame;
   a.n_rows = n_rows;
   a.rows_cap = rows_cap;
-  a.div_row = make_fastdiv((uint32_t)(n_heads * rope.tv_count));
-  a.div_head = make_fastdiv((uint32_t)rope.tv_count);
+  a.div_row = make_fastdiv((uint32_t)(n_heads * rope.wv_count));
+  a.div_head = make_fastdiv((uint32_t)rope.wv_count);
   a.vph = (uint32_t)(head_dim * elem_size(dtype) / 16);
   a.n_heads = (uint32_t)n_heads;
-  a.total_cap = (uint32_t)(rows_cap * n_heads * rope.tv_count);
+  a.n_layers = (uint32_t)n_layers;
   a.dtype = dtype;
   a.rope = rope;
-  if (a.total_cap == 0) return DP_OK;
-  constexpr int U = 4;
-  const uint32_t gx = (uint32_t)(((uint64_t)a.total_cap + kBlock * U - 1) / (kBlock * U));
-  hipLaunchKernelGGL(reindex_kernel<U>, dim3(gx, n_layers), dim3(kBlock), 0, s, a);
+  const uint64_t gx = ((uint64_t)rows_cap * a.div_row.d + kBlock - 1) / kBlock * (uint64_t)n_layers;
+  if (gx == 0) return DP_OK;
+  if (a.div_row.d >= (uint32_t)kBlock)
+    hipLaunchKernelGGL(reindex_kernel<true>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(reindex_kernel<false>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("reindex_kernel");
 }
 

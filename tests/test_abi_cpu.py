@@ -214,3 +214,4 @@ def test_pruning_ratio_counter():
     assert dp.dp_pr_value(c) == 1 - (L * H * n) / (L * H * (T + 6240))
     with pytest.raises(dp.DPError):
         dp.dp_pr_add(c, 5, 4)
+

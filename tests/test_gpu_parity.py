@@ -266,6 +266,8 @@ ROPE_CASES = [  # L, T, H, D, dtype, tokens_per_frame, pair_begin, n_pairs
     (1, 3000, 3, 64, dp.DP_BF16, 64, 4, 6),        # block ends inside a 16-byte vector
     (2, 2048, 2, 64, dp.DP_F32, 64, 2, 8),
     (1, 1500, 5, 32, dp.DP_F32, 50, 0, 16),        # every dim is temporal
+    (1, 1300, 24, 128, dp.DP_BF16, 100, 0, 44),    # rows of 384 vectors: a workgroup spans <= 2 rows
+    (2, 999, 16, 128, dp.DP_BF16, 37, 0, 44),      # rows of exactly 256 vectors, ragged frames
 ]
 
 

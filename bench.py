@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--summarize-stats", metavar="STATS_DIR",
+                    help="write the kernel-statistics summary of --workload from a rocprofv3 "
+                         "--kernel-trace --stats output directory and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary of --workload from two rocprofv3 --pmc "
                          "output directories (FETCH_SIZE, WRITE_SIZE) and exit")
@@ -499,8 +502,40 @@ def setup_hs(dev):
     return run, gt, accounting, None
 
 
+def summarize_stats(workload, stats_dir):
+    """Short text summary of rocprofv3's kernel statistics CSV."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    assert files, "no kernel_stats.csv under %s" % stats_dir
+    kname = KERNELS[workload][0]
+    lines = ["# rocprofv3 kernel statistics, %s workload (bench.py --workload %s)" % (workload, workload),
+             "# commands (from the repository root):",
+             "#   rocprofv3 --kernel-trace --stats -d %s -o run -f csv -- python bench.py "
+             "--workload %s --no-cpu-baseline --steps 10" % (stats_dir, workload),
+             "#   python bench.py --workload %s --summarize-stats %s" % (workload, stats_dir),
+             "# dominant kernel: %s; times in ns; fill_kernel and calib_copy_kernel are input" % kname,
+             "# generation and the copy-ceiling reference, not part of the step",
+             "kernel | calls | avg_ns | min_ns | max_ns | total_ns | pct"]
+    for r in csv.DictReader(open(files[0])):
+        name = r["Name"].replace("(anonymous namespace)", "anon")
+        m = re.search(r"(\w+)(<[^>()]*>)?\(", name)
+        short = m.group(1) + (m.group(2) or "") if m else name[:60]
+        lines.append("%s | %s | %.0f | %s | %s | %s | %.2f" % (
+            short, r["Calls"], float(r["AverageNs"]), r["MinNs"], r["MaxNs"],
+            r["TotalDurationNs"], float(r["Percentage"])))
+    path = os.path.join(PROFILES, "%s_%s_kernel_stats.txt" % (kname, workload))
+    with open(path, "w") as out:
+        out.write("\n".join(lines) + "\n")
+    print(open(path).read())
+
+
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(args.workload, args.summarize_stats)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.workload, *args.summarize_pmc)
         return

@@ -147,10 +147,15 @@ def setup_eviction(dev):
                      row_frame=torch.from_numpy(dpsynth.row_frame(w)).to(dev), rope=rope)
     x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
     gt = Timer()
+    st = Timer()
 
     def run(timed):
         rope["frame_phase"].copy_(phase0)
+        if timed:
+            st.start()
         dp.dp_score_mask(x0d, xfd, w.d, w.d, step.policy, step.ell, step.keep)
+        if timed:
+            st.stop()
         dp.dp_compact_index(step.keep, T, step.idx, step.n_kept, step.row_frame_src,
                             step.row_frame_dst, step.ws_compact)
         if timed:
@@ -166,7 +171,7 @@ def setup_eviction(dev):
         gather = n * row * 2 * 2 * L
         score = w.n_scored * (8 * w.d) + T
         index = 2 * T + 4 * n + 8 * n
-        return dict(n_kept=n, gather_bytes=gather,
+        return dict(n_kept=n, gather_bytes=gather, score_timer=st, score_bytes_per_token=8 * w.d + 1,
                     step_bytes=gather + score + index, n_scored=w.n_scored,
                     config={"workload": "eviction", "layers": L, "heads": H, "head_dim": D,
                             "kv_dtype": "bf16", "tokens": T, "chunk_tokens": w.chunk_tokens,
@@ -392,9 +397,14 @@ def setup_prefix(dev, slab_layers=20):
                      sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
                      n_scored=w.n_scored, gamma=w.gamma, d=w.d)
     gt = Timer()
+    st = Timer()
 
     def run(timed):
+        if timed:
+            st.start()
         dp.dp_score_mask(x0d, xfd, w.d, w.d, step.policy, None, step.keep)
+        if timed:
+            st.stop()
         dp.dp_compact_index(step.keep, T, step.idx, step.n_kept, None, None, step.ws_compact)
         if timed:
             gt.start()
@@ -408,7 +418,7 @@ def setup_prefix(dev, slab_layers=20):
         score = w.n_scored * 8 * w.d + T
         index = 2 * T + 4 * n
         return dict(n_kept=n, gather_bytes=gather, step_bytes=gather + score + index,
-                    n_scored=w.n_scored,
+                    n_scored=w.n_scored, score_timer=st, score_bytes_per_token=8 * w.d + 1,
                     config={"workload": "prefix", "layers_in_slab": slab_layers, "layers": 40,
                             "heads": H, "head_dim": D, "kv_dtype": "bf16", "tokens": T,
                             "scored_tokens": w.n_scored, "d": w.d, "gamma": w.gamma,
@@ -587,13 +597,21 @@ def main():
         "data": "synthetic",
         "config": acc["config"],
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "tokens_scored_per_s": (acc["n_scored"] / (ms * 1e-3)) if acc["n_scored"] else None,
+        "tokens_scored_per_s": None,
         "step_bytes": acc["step_bytes"],
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(g_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": acc["gather_bytes"],
                      "launch_ms": round(g_ms, 4)},
     }
+    if acc.get("score_timer") is not None:
+        s_ms = acc["score_timer"].mean_ms()
+        tps = acc["n_scored"] / (s_ms * 1e-3)
+        rec["tokens_scored_per_s"] = round(tps, 1)
+        rec["score_kernel"] = {
+            "ms": round(s_ms, 5), "tokens": acc["n_scored"],
+            "roofline_tokens_per_s": round(HBM_PEAK_GBS * 1e9 / acc["score_bytes_per_token"], 1),
+            "frac": round(tps * acc["score_bytes_per_token"] / (HBM_PEAK_GBS * 1e9), 4)}
     rec["copy_ceiling_gbs"] = round(copy_ceiling(dev, CALIB_BYTES), 2)
     if cpu is not None and not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu(args.cpu_seconds)

@@ -63,6 +63,11 @@ class dp_kv_hs(ctypes.Structure):
                 ("src_rows", _i64), ("out_capacity", _i64), ("dev_error", _P)]
 
 
+class dp_kv_inplace(ctypes.Structure):
+    _fields_ = [("k_layers", _P), ("v_layers", _P), ("n_layers", _i32), ("n_heads", _i32),
+                ("head_dim", _i32), ("dtype", _i32), ("capacity", _i64), ("dev_error", _P)]
+
+
 class dp_pr_counter(ctypes.Structure):
     _fields_ = [("visible", _i64), ("full", _i64)]
 
@@ -85,6 +90,7 @@ _lib_gather = _sig("dp_gather_kv", [ctypes.POINTER(dp_kv), _P, _P, _P, ctypes.PO
                                     ctypes.c_size_t, _P])
 _lib_reindex = _sig("dp_rope_reindex", [_P, _i32, _i32, _i32, _i32, _i64, _P, _P,
                                         ctypes.POINTER(dp_rope), _P, ctypes.c_size_t, _P])
+_lib_append = _sig("dp_append_kept", [ctypes.POINTER(dp_kv_inplace), _i64, _i64, _P, _P, _P, _P, _P])
 _lib_hs_offsets = _sig("dp_hs_offsets", [_P, _i32, _i32, _P, _i32, _P, _P])
 _lib_hs_gather = _sig("dp_hs_gather_kv", [ctypes.POINTER(dp_kv_hs), _P, _i32, _P, _P,
                                           ctypes.POINTER(_i64), _P, _P, ctypes.POINTER(dp_rope),
@@ -97,7 +103,7 @@ _lib_pr_value = _sig("dp_pr_value", [ctypes.POINTER(dp_pr_counter)], ctypes.c_do
 
 EXPORTED = ["dp_abi_version", "dp_status_str", "dp_last_error", "dp_score_mask",
             "dp_compact_workspace_bytes", "dp_compact_index", "dp_rope_workspace_bytes",
-            "dp_gather_kv", "dp_rope_reindex", "dp_hs_offsets", "dp_hs_gather_kv",
+            "dp_gather_kv", "dp_rope_reindex", "dp_append_kept", "dp_hs_offsets", "dp_hs_gather_kv",
             "dp_hs_rope_reindex", "dp_pr_add", "dp_pr_value"]
 
 
@@ -207,6 +213,11 @@ def dp_rope_reindex(k_layers, n_layers, n_heads, head_dim, dtype, rows_capacity,
     _check(_lib_reindex(_ptr(k_layers), n_layers, n_heads, head_dim, dtype, rows_capacity,
                         _ptr(n_rows), _ptr(row_frame), ctypes.byref(rope), _ptr(workspace),
                         ws_bytes, _stream(stream)))
+
+
+def dp_append_kept(kv, slot_begin, slot_rows, idx, n_kept, tail, row_frame=None, stream=None):
+    _check(_lib_append(ctypes.byref(kv), int(slot_begin), int(slot_rows), _ptr(idx), _ptr(n_kept),
+                       _ptr(tail), _ptr(row_frame), _stream(stream)))
 
 
 def dp_hs_offsets(head_class, n_layers, n_heads, class_len, n_classes, offsets, stream=None):

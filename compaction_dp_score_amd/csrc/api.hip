@@ -215,6 +215,33 @@ dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_hea
   return st;
 }
 
+dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t slot_rows,
+                         const int32_t* idx, const int64_t* n_kept, int64_t* tail,
+                         int32_t* row_frame, void* stream) {
+  if (!kv || !n_kept || !tail || (slot_rows > 0 && !idx))
+    return fail(DP_EINVAL, "dp_append_kept: kv, idx, n_kept and tail are required");
+  dp_status st = check_shape(kv->n_layers, kv->n_heads, kv->head_dim, kv->dtype, "dp_append_kept");
+  if (st != DP_OK) return st;
+  if (!kv->k_layers) return fail(DP_EINVAL, "dp_append_kept: k_layers is required");
+  if (kv->capacity < 0 || kv->capacity >= kMaxRows || slot_begin < 0 || slot_rows < 0 ||
+      slot_begin + slot_rows > kv->capacity)
+    return fail(DP_ERANGE, "dp_append_kept: need 0 <= slot_begin, slot_begin + slot_rows <= "
+                "capacity < 2^31");
+  const int64_t rv = (int64_t)kv->n_heads * kv->head_dim * elem_size(kv->dtype) / 16;
+  const int n_kv = kv->v_layers ? 2 : 1;
+  if (slot_rows * rv >= kMaxVec ||
+      (int64_t)kv->n_layers * n_kv * ((slot_rows * rv + 255) / 256) >= kMaxVec)
+    return fail(DP_ERANGE, "dp_append_kept: slot too large for one launch");
+  if (!aligned(n_kept, 8) || !aligned(tail, 8) || (idx && !aligned(idx, 4)) ||
+      (row_frame && !aligned(row_frame, 4)) || (kv->dev_error && !aligned(kv->dev_error, 4)))
+    return fail(DP_EALIGN, "dp_append_kept: misaligned count, tail, index or frame array");
+  (void)hipGetLastError();
+  st = launch_append(*kv, slot_begin, slot_rows, idx, n_kept, tail, row_frame,
+                     (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
 dp_status dp_hs_offsets(const uint8_t* head_class, int32_t n_layers, int32_t n_heads,
                         const int64_t* class_len, int32_t n_classes, int64_t* offsets,
                         void* stream) {

@@ -1,0 +1,115 @@
+// dp_append_kept: segment-append compaction in place.
+//
+// The DeCoPrune page (section 어떻게 동작하나) compacts a chunk when it leaves
+// the dense window.  With the cache kept as [sink | window ring | history] in
+// one buffer per layer, only the kept rows of the slot that holds the leaving
+// chunk move: they are appended at the history tail.  append_kernel copies them
+// for all layers, K and V, in one 1-D launch (one 16-byte vector per lane,
+// non-temporal, dense mapping from the device-side kept count, like the
+// out-of-place gather); append_finish_kernel then retires the slot's row frames
+// (-1) and advances the tail.  Both launches re-derive the appended span from
+// the same device values, and the finish launch runs after the copy on the
+// stream, so the tail is never read after it changes.
+#include "dp_internal.h"
+
+namespace dp {
+namespace {
+
+struct AppendArgs {
+  void* const* k_layers;
+  void* const* v_layers;
+  const int32_t* idx;
+  const int64_t* n_kept;
+  int64_t* tail;
+  int32_t* row_frame;
+  int32_t* dev_error;
+  int64_t capacity;
+  int64_t slot_begin;
+  int64_t slot_rows;
+  FastDiv div_row;     // 16-byte vectors per row
+  uint32_t n_slabs;    // n_layers * n_kv
+  int32_t n_kv;
+};
+
+// The appended span [t0, t0 + n); false (with the status) when it would pass
+// the capacity or overlap the slot.
+__device__ __forceinline__ bool append_span(const AppendArgs& a, int64_t& t0, int64_t& n,
+                                            int& err) {
+  const int64_t nk = *a.n_kept;
+  t0 = *a.tail;
+  n = nk < 0 ? 0 : (nk > a.slot_rows ? a.slot_rows : nk);
+  err = DP_OK;
+  if (t0 < 0 || t0 + n > a.capacity) err = DP_ECAPACITY;
+  else if (n > 0 && t0 < a.slot_begin + a.slot_rows && t0 + n > a.slot_begin) err = DP_ERANGE;
+  return err == DP_OK;
+}
+
+__global__ __launch_bounds__(kBlock) void append_kernel(AppendArgs a) {
+  int64_t t0, n;
+  int err;
+  if (!append_span(a, t0, n, err)) return;            // reported by append_finish_kernel
+  const uint32_t per_slab = (uint32_t)(n * (int64_t)a.div_row.d);
+  const uint32_t tiles = (per_slab + kBlock - 1) / kBlock;
+  if (tiles == 0) return;
+  const uint32_t slab = blockIdx.x / tiles;
+  if (slab >= a.n_slabs) return;
+  const uint32_t i = (blockIdx.x - slab * tiles) * kBlock + threadIdx.x;
+  if (i >= per_slab) return;
+  const int layer = (int)(slab / a.n_kv);
+  const bool is_v = (slab % a.n_kv) == 1;
+  u32x4* __restrict__ base = reinterpret_cast<u32x4*>(is_v ? a.v_layers[layer] : a.k_layers[layer]);
+  const uint32_t j = fdiv(i, a.div_row);
+  const uint32_t c = i - j * a.div_row.d;
+  const int32_t s = a.idx[j];
+  if ((uint64_t)(uint32_t)s >= (uint64_t)a.slot_rows) return;   // out-of-range entries are skipped
+  const u32x4 v =
+      __builtin_nontemporal_load(base + (a.slot_begin + s) * (int64_t)a.div_row.d + c);
+  __builtin_nontemporal_store(v, base + (t0 + j) * (int64_t)a.div_row.d + c);
+  if (a.row_frame && slab == 0 && c == 0) a.row_frame[t0 + j] = a.row_frame[a.slot_begin + s];
+}
+
+__global__ __launch_bounds__(kBlock) void append_finish_kernel(AppendArgs a) {
+  int64_t t0, n;
+  int err;
+  const bool ok = append_span(a, t0, n, err);
+  __syncthreads();                                     // every lane has read *tail
+  if (!ok) {
+    if (threadIdx.x == 0 && a.dev_error) *a.dev_error = err;
+    return;
+  }
+  if (a.row_frame)
+    for (int64_t r = threadIdx.x; r < a.slot_rows; r += kBlock) a.row_frame[a.slot_begin + r] = -1;
+  if (threadIdx.x == 0) *a.tail = t0 + n;
+}
+
+}  // namespace
+
+dp_status launch_append(const dp_kv_inplace& kv, int64_t slot_begin, int64_t slot_rows,
+                        const int32_t* idx, const int64_t* n_kept, int64_t* tail,
+                        int32_t* row_frame, hipStream_t s) {
+  AppendArgs a;
+  a.k_layers = kv.k_layers;
+  a.v_layers = kv.v_layers;
+  a.idx = idx;
+  a.n_kept = n_kept;
+  a.tail = tail;
+  a.row_frame = row_frame;
+  a.dev_error = kv.dev_error;
+  a.capacity = kv.capacity;
+  a.slot_begin = slot_begin;
+  a.slot_rows = slot_rows;
+  a.div_row = make_fastdiv((uint32_t)((int64_t)kv.n_heads * kv.head_dim * elem_size(kv.dtype) / 16));
+  a.n_kv = kv.v_layers ? 2 : 1;
+  a.n_slabs = (uint32_t)(kv.n_layers * a.n_kv);
+  const uint64_t gx =
+      (uint64_t)a.n_slabs * (((uint64_t)slot_rows * a.div_row.d + kBlock - 1) / kBlock);
+  if (gx > 0) {
+    hipLaunchKernelGGL(append_kernel, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+    dp_status st = check_launch("append_kernel");
+    if (st != DP_OK) return st;
+  }
+  hipLaunchKernelGGL(append_finish_kernel, dim3(1), dim3(kBlock), 0, s, a);
+  return check_launch("append_finish_kernel");
+}
+
+}  // namespace dp

@@ -234,6 +234,39 @@ dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_hea
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * 4b. Segment-append compaction in place     [DeCoPrune page, 어떻게 동작하나]
+ *
+ * The page compacts a chunk when it leaves the dense window; only that chunk's
+ * rows change state.  With the cache laid out per layer as
+ *   [sink | window ring of chunk slots | history]        (rows [0, *tail))
+ * in one buffer of `capacity` rows, the kept rows of the slot holding the
+ * leaving chunk are appended at the history tail, so the sink, the other
+ * window slots and earlier history never move and the visible cache stays
+ * one contiguous row range.  For every layer l and j < n = *n_kept:
+ *   K[l][*tail + j] = K[l][slot_begin + idx[j]]     (bit copy; V likewise)
+ *   row_frame[*tail + j] = row_frame[slot_begin + idx[j]]   (if row_frame)
+ * then row_frame[slot_begin .. slot_begin + slot_rows) = -1 (the slot's rows are
+ * retired: the re-index skips them until the next chunk is written into the
+ * slot together with its frames) and *tail += n.  idx holds slot-relative rows
+ * (dp_compact_index over the slot's keep mask), ascending, in [0, slot_rows).
+ * Device-side checks: if the appended rows would pass `capacity` or overlap
+ * the slot, nothing is copied or advanced and *dev_error = DP_ECAPACITY or
+ * DP_ERANGE.  Two launches on `stream`.  The old keys are then re-indexed in
+ * place with dp_rope_reindex over rows [0, *tail) (n_rows = tail).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  void* const* k_layers;     /* device array [n_layers]: [capacity][n_heads][head_dim] */
+  void* const* v_layers;     /* same, or NULL                                          */
+  int32_t n_layers, n_heads, head_dim, dtype;
+  int64_t capacity;          /* rows of each layer buffer, < 2^31                      */
+  int32_t* dev_error;        /* device int32 or NULL                                   */
+} dp_kv_inplace;
+
+dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t slot_rows,
+                         const int32_t* idx, const int64_t* n_kept, int64_t* tail,
+                         int32_t* row_frame, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * 5. DeCoPrune-HS: head-specialised ragged cache   [DeCoPrune page, 무엇과 다른가]
  *
  * The page splits heads into dynamic heads, which follow the DeCoPrune mask,

@@ -37,6 +37,8 @@ def lib():
         L.oracle_compact.restype = i64
         L.oracle_gather.argtypes = [P, i64, i64, i64, P, i64, P, i64]
         L.oracle_gather_i32.argtypes = [P, P, i64, P]
+        L.oracle_append_kept.argtypes = [P, i64, i64, i64, i64, i64, P, i64, i64, P]
+        L.oracle_append_kept.restype = i64
         L.oracle_rope_frames.argtypes = [i32, P, P, f32, f32, f32, i32, P, P, P, P]
         L.oracle_rope_rows.argtypes = [P, i32, i64, i32, i32, i32, i32, P, P, P, P]
         L.oracle_rope_headrows.argtypes = [P, i32, i64, i32, i32, i32, P, P, P, P]
@@ -131,6 +133,21 @@ def gather_i32(src, idx):
     if idx.shape[0]:
         lib().oracle_gather_i32(_p(s), _p(idx), idx.shape[0], _p(out))
     return out
+
+
+def append_kept(buf, slot_begin, slot_rows, idx, tail, row_frame=None):
+    """In place on buf [L, capacity, ...]: append the kept rows idx (slot-relative)
+    of the slot at the tail; returns the new tail (-1: refused, unchanged)."""
+    assert buf.flags.c_contiguous
+    idx = _c(idx, np.int32)
+    assert idx.size == 0 or (idx.min() >= 0 and idx.max() < slot_rows)
+    L, cap = buf.shape[0], buf.shape[1]
+    row_bytes = int(np.prod(buf.shape[2:], dtype=np.int64)) * buf.itemsize
+    if row_frame is not None:
+        assert row_frame.dtype == np.int32 and row_frame.flags.c_contiguous
+    rf = _p(row_frame) if row_frame is not None else None
+    return lib().oracle_append_kept(_p(buf), L, cap, row_bytes, slot_begin, slot_rows,
+                                    _p(idx) if idx.size else None, idx.shape[0], tail, rf)
 
 
 # --------------------------------------------------------------------------

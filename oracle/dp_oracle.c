@@ -136,6 +136,30 @@ void oracle_gather_i32(const int32_t* src, const int32_t* idx, int64_t n, int32_
 }
 
 /* ---------------------------------------------------------------------- *
+ * Segment-append compaction in place [DeCoPrune page, 어떻게 동작하나]: when a
+ * chunk leaves the window, only its kept rows change place: they are copied
+ * from the chunk's slot to the history tail of the same buffer (every layer),
+ * their frames with them; the slot's frames become -1 (retired).  buf holds
+ * n_layers slabs of capacity rows of row_bytes.  Returns the new tail, or -1
+ * (nothing changed) if the rows would pass the capacity or overlap the slot.
+ * ---------------------------------------------------------------------- */
+int64_t oracle_append_kept(uint8_t* buf, int64_t n_layers, int64_t capacity, int64_t row_bytes,
+                           int64_t slot_begin, int64_t slot_rows, const int32_t* idx, int64_t n,
+                           int64_t tail, int32_t* row_frame) {
+  if (tail < 0 || tail + n > capacity) return -1;
+  if (n > 0 && tail < slot_begin + slot_rows && tail + n > slot_begin) return -1;
+  for (int64_t l = 0; l < n_layers; ++l)
+    for (int64_t j = 0; j < n; ++j)
+      memcpy(buf + (l * capacity + tail + j) * row_bytes,
+             buf + (l * capacity + slot_begin + (int64_t)idx[j]) * row_bytes, (size_t)row_bytes);
+  if (row_frame) {
+    for (int64_t j = 0; j < n; ++j) row_frame[tail + j] = row_frame[slot_begin + idx[j]];
+    for (int64_t r = 0; r < slot_rows; ++r) row_frame[slot_begin + r] = -1;
+  }
+  return tail + n;
+}
+
+/* ---------------------------------------------------------------------- *
  * RoPE temporal re-index [DeCoPrune page, 무엇과 다른가]: old keys move to
  * t~ = q0 - g(q0 - t), g keeps recent offsets and compresses older ones
  * linearly; only the key's temporal phase changes.

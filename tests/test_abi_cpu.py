@@ -24,7 +24,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(dp.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -41,7 +41,8 @@ def test_version_and_status_strings():
 def test_struct_layouts_match_header(tmp_path):
     # the ctypes mirrors have the size and field offsets gcc gives the header
     structs = {"dp_mask_policy": dp.dp_mask_policy, "dp_rope": dp.dp_rope, "dp_kv": dp.dp_kv,
-               "dp_kv_hs": dp.dp_kv_hs, "dp_pr_counter": dp.dp_pr_counter}
+               "dp_kv_hs": dp.dp_kv_hs, "dp_pr_counter": dp.dp_pr_counter,
+               "dp_kv_inplace": dp.dp_kv_inplace}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "decoprune.h"', 'int main(void){']
     for name, cls in structs.items():
         lines.append('printf("%s %%zu\\n", sizeof(%s));' % (name, name))
@@ -215,3 +216,35 @@ def test_pruning_ratio_counter():
     with pytest.raises(dp.DPError):
         dp.dp_pr_add(c, 5, 4)
 
+
+
+def _inplace(**kw):
+    kv = dp.dp_kv_inplace()
+    f = dict(k_layers=FAKE, v_layers=FAKE, n_layers=2, n_heads=4, head_dim=64, dtype=dp.DP_BF16,
+             capacity=1000, dev_error=None)
+    f.update(kw)
+    for k, v in f.items():
+        setattr(kv, k, v)
+    return kv
+
+
+@pytest.mark.parametrize("kw,slot,want", [
+    (dict(), (900, 200), dp.DP_ERANGE),              # slot passes the capacity
+    (dict(), (-1, 10), dp.DP_ERANGE),
+    (dict(capacity=1 << 31), (0, 10), dp.DP_ERANGE),
+    (dict(k_layers=None), (0, 10), dp.DP_EINVAL),
+    (dict(head_dim=7), (0, 10), dp.DP_EINVAL),
+    (dict(head_dim=6), (0, 10), dp.DP_EALIGN),
+])
+def test_append_kept_rejects(kw, slot, want):
+    kv = _inplace(**kw)
+    st = _status("append", ctypes.byref(kv), slot[0], slot[1], FAKE, FAKE, FAKE, None, None)
+    assert st == want, dp.dp_last_error()
+
+
+def test_append_kept_rejects_missing_and_misaligned():
+    kv = _inplace()
+    assert _status("append", ctypes.byref(kv), 0, 10, None, FAKE, FAKE, None, None) == dp.DP_EINVAL
+    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, None, None, None) == dp.DP_EINVAL
+    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE + 4, FAKE, None, None) == dp.DP_EALIGN
+    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, FAKE, FAKE + 2, None) == dp.DP_EALIGN

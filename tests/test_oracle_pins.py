@@ -176,6 +176,30 @@ def test_gather_is_numpy_take(dtype):
     assert np.array_equal(oracle.gather_i32(rf, idx), rf[idx])
 
 
+def test_append_kept_is_numpy_indexing():
+    rng = np.random.default_rng(15)
+    L, cap, H, D = 2, 200, 3, 8
+    buf = rng.integers(0, 2 ** 15, size=(L, cap, H, D)).astype(np.uint16)
+    rf = rng.integers(0, 50, cap).astype(np.int32)
+    before, rf0 = buf.copy(), rf.copy()
+    slot_begin, slot_rows, tail = 10, 40, 120
+    idx = np.flatnonzero(rng.random(slot_rows) < 0.4).astype(np.int32)
+    t2 = oracle.append_kept(buf, slot_begin, slot_rows, idx, tail, rf)
+    n = idx.shape[0]
+    assert t2 == tail + n
+    assert np.array_equal(buf[:, tail:tail + n], before[:, slot_begin + idx])
+    untouched = np.ones(cap, bool)
+    untouched[tail:tail + n] = False
+    assert np.array_equal(buf[:, untouched], before[:, untouched])
+    assert np.array_equal(rf[tail:tail + n], rf0[slot_begin + idx])
+    assert np.all(rf[slot_begin:slot_begin + slot_rows] == -1)
+    # refused: past the capacity, or overlapping the slot -- nothing changes
+    b2, r2 = buf.copy(), rf.copy()
+    assert oracle.append_kept(buf, slot_begin, slot_rows, idx, cap - n + 1, rf) == -1
+    assert oracle.append_kept(buf, slot_begin, slot_rows, idx, slot_begin + 5, rf) == -1
+    assert np.array_equal(buf, b2) and np.array_equal(rf, r2)
+
+
 # --------------------------------------------------------------------------
 # RoPE re-index
 # --------------------------------------------------------------------------

@@ -17,7 +17,9 @@ tokens scored per second, a roofline record of the dominant kernel (the
 gather) timed with HIP events on its stream, and the CPU oracle timed on a
 bounded layer sample of the same workload on the host cores.
 
-Other workloads (--workload reindex | prefix | hs) time the other shapes.
+Other workloads (--workload reindex | prefix | hs | append) time the other
+shapes; "append" is the same eviction step in the ring layout, where only the
+leaving chunk's kept rows move and the old keys are re-indexed in place.
 """
 import argparse
 import json
@@ -41,6 +43,7 @@ KERNELS = {
     "prefix": ("gather_kernel", ("gather.hip", "dp_internal.h")),
     "reindex": ("reindex_kernel", ("rope.hip", "dp_internal.h")),
     "hs": ("hs_gather_kernel", ("hs.hip", "dp_internal.h")),
+    "append": ("reindex_kernel", ("rope.hip", "dp_internal.h")),
 }
 
 
@@ -53,7 +56,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="eviction", choices=["eviction", "reindex", "prefix", "hs"])
+    ap.add_argument("--workload", default="eviction",
+                    choices=["eviction", "reindex", "prefix", "hs", "append"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -369,6 +373,91 @@ def _fill_layers(dev, w, rows, layers, stream_id):
     return out
 
 
+def setup_append(dev):
+    """The eviction step in the ring layout: per layer one buffer
+    [sink | ring of 4 chunk slots | history]; the chunk in ring slot 0 leaves
+    the window: it is scored (6,240 tokens), its kept rows are appended at the
+    history tail (K and V, 40 layers), and the old keys (the sink and the
+    history, here the appended rows) are re-indexed in place for q0 = 20 by
+    one dp_rope_prepare and two dp_rope_apply calls.  The tail, the slot's row frames
+    and the phase table are restored before each step (small device copies)."""
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    w = dpsynth.WORKLOADS["eviction"]
+    T, H, D, L, C = w.seq_len, w.n_heads, w.head_dim, w.n_layers, w.chunk_tokens
+    cap = T + C                                     # room for one chunk of history
+    slot_begin = C                                  # ring slot 0 holds the leaving chunk
+    ks = _fill_layers(dev, w, cap, range(L), dpsynth.STREAM_K)
+    vs = _fill_layers(dev, w, cap, range(L), dpsynth.STREAM_V)
+    x0, xf = dpsynth.score_inputs(w)
+    x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
+    rf_full = np.full(cap, -1, np.int32)
+    rf_full[:T] = dpsynth.row_frame(w)
+    rf0 = torch.from_numpy(rf_full).to(dev)
+    rf = rf0.clone()
+    kv = dp.dp_kv_inplace()
+    arr_k, arr_v = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
+    kv.k_layers, kv.v_layers = arr_k.data_ptr(), arr_v.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dp.DP_BF16
+    kv.capacity = cap
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    tail0 = torch.tensor([T], dtype=torch.int64, device=dev)
+    tail = tail0.clone()
+    pol = dp.make_policy(C, 0, 0, 0, C, w.gamma)
+    keep = torch.empty(C, dtype=torch.uint8, device=dev)
+    idx = torch.empty(C, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_c = torch.empty(dp.dp_compact_workspace_bytes(C) // 4 + 1, dtype=torch.int32, device=dev)
+    theta = torch.from_numpy(dpsynth.rope_theta(w.rope_pairs, w.rope_base)).to(dev)
+    ft, fp = dpsynth.frame_tables(w)
+    ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(fp).to(dev)
+    phase0 = fpd.clone()
+    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    gt = Timer()
+    at = Timer()
+    keep_alive = [arr_k, arr_v]
+
+    def run(timed):
+        tail.copy_(tail0)
+        rf.copy_(rf0)
+        fpd.copy_(phase0)
+        dp.dp_score_mask(x0d, xfd, w.d, w.d, pol, None, keep)
+        dp.dp_compact_index(keep, C, idx, nk, None, None, ws_c)
+        if timed:
+            at.start()
+        dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf)
+        if timed:
+            at.stop()
+        dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+        if timed:
+            gt.start()
+        # old keys only: the sink, and the history [T, tail); the window ring is skipped
+        dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, 0, w.sink_len, None, rf, rope, ws_r)
+        dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, T, cap, tail, rf, rope, ws_r)
+        if timed:
+            gt.stop()
+
+    def accounting():
+        assert keep_alive and err.item() == 0
+        n = int(nk.item())
+        append = n * H * D * 2 * 2 * 2 * L
+        rotated = (w.sink_len + n) * H * L            # head rows whose frame moves
+        reindex = rotated * 2 * w.rope_pairs * 2 * 2
+        score = C * (8 * w.d + 1)
+        return dict(n_kept=n, gather_bytes=reindex, step_bytes=append + reindex + score,
+                    n_scored=C, append_timer=at, append_bytes=append,
+                    config={"workload": "append", "layout": "sink | ring of 4 chunk slots | history",
+                            "layers": L, "heads": H, "head_dim": D, "kv_dtype": "bf16",
+                            "tokens": T, "scored_tokens": C, "kept_tokens": n,
+                            "appended_bytes": append, "reindexed_head_rows": rotated,
+                            "rope_pairs": w.rope_pairs, "q0": w.q0})
+
+    return run, gt, accounting, None
+
+
 def setup_prefix(dev, slab_layers=20):
     """Prefix pruning of a 58-chunk observed context: all 57 non-sink chunks
     scored (d = 64) and compacted.  40 layers of K+V are 296.5 GB, more than
@@ -559,7 +648,7 @@ def main():
     import compaction_dp_score_amd  # noqa: F401  (fails loudly if the library is missing)
     dev = torch.device("cuda:0")
     setups = {"eviction": setup_eviction, "reindex": setup_reindex, "prefix": setup_prefix,
-              "hs": setup_hs}
+              "hs": setup_hs, "append": setup_append}
     if args.workload not in setups:
         print("workload %s is not wired into bench.py yet" % args.workload, file=sys.stderr)
         sys.exit(2)
@@ -612,6 +701,10 @@ def main():
             "ms": round(s_ms, 5), "tokens": acc["n_scored"],
             "roofline_tokens_per_s": round(HBM_PEAK_GBS * 1e9 / acc["score_bytes_per_token"], 1),
             "frac": round(tps * acc["score_bytes_per_token"] / (HBM_PEAK_GBS * 1e9), 4)}
+    if acc.get("append_timer") is not None:
+        a_ms = acc["append_timer"].mean_ms()
+        rec["append_kernel"] = {"ms": round(a_ms, 5), "bytes": acc["append_bytes"],
+                                "gbs": round(acc["append_bytes"] / (a_ms * 1e-3) / 1e9, 2)}
     rec["copy_ceiling_gbs"] = round(copy_ceiling(dev, CALIB_BYTES), 2)
     if cpu is not None and not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu(args.cpu_seconds)

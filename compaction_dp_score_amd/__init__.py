@@ -90,6 +90,9 @@ _lib_gather = _sig("dp_gather_kv", [ctypes.POINTER(dp_kv), _P, _P, _P, ctypes.PO
                                     ctypes.c_size_t, _P])
 _lib_reindex = _sig("dp_rope_reindex", [_P, _i32, _i32, _i32, _i32, _i64, _P, _P,
                                         ctypes.POINTER(dp_rope), _P, ctypes.c_size_t, _P])
+_lib_rope_prepare = _sig("dp_rope_prepare", [ctypes.POINTER(dp_rope), _i32, _i32, _P, ctypes.c_size_t, _P])
+_lib_rope_apply = _sig("dp_rope_apply", [_P, _i32, _i32, _i32, _i32, _i64, _i64, _P, _P,
+                                         ctypes.POINTER(dp_rope), _P, ctypes.c_size_t, _P])
 _lib_append = _sig("dp_append_kept", [ctypes.POINTER(dp_kv_inplace), _i64, _i64, _P, _P, _P, _P, _P])
 _lib_hs_offsets = _sig("dp_hs_offsets", [_P, _i32, _i32, _P, _i32, _P, _P])
 _lib_hs_gather = _sig("dp_hs_gather_kv", [ctypes.POINTER(dp_kv_hs), _P, _i32, _P, _P,
@@ -103,7 +106,8 @@ _lib_pr_value = _sig("dp_pr_value", [ctypes.POINTER(dp_pr_counter)], ctypes.c_do
 
 EXPORTED = ["dp_abi_version", "dp_status_str", "dp_last_error", "dp_score_mask",
             "dp_compact_workspace_bytes", "dp_compact_index", "dp_rope_workspace_bytes",
-            "dp_gather_kv", "dp_rope_reindex", "dp_append_kept", "dp_hs_offsets", "dp_hs_gather_kv",
+            "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_append_kept",
+            "dp_hs_offsets", "dp_hs_gather_kv",
             "dp_hs_rope_reindex", "dp_pr_add", "dp_pr_value"]
 
 
@@ -213,6 +217,20 @@ def dp_rope_reindex(k_layers, n_layers, n_heads, head_dim, dtype, rows_capacity,
     _check(_lib_reindex(_ptr(k_layers), n_layers, n_heads, head_dim, dtype, rows_capacity,
                         _ptr(n_rows), _ptr(row_frame), ctypes.byref(rope), _ptr(workspace),
                         ws_bytes, _stream(stream)))
+
+
+def dp_rope_prepare(rope, head_dim, dtype, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib_rope_prepare(ctypes.byref(rope), head_dim, dtype, _ptr(workspace), ws_bytes,
+                             _stream(stream)))
+
+
+def dp_rope_apply(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_capacity, n_rows,
+                  row_frame, rope, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib_rope_apply(_ptr(k_layers), n_layers, n_heads, head_dim, dtype, int(row_begin),
+                           int(rows_capacity), _ptr(n_rows), _ptr(row_frame), ctypes.byref(rope),
+                           _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dp_append_kept(kv, slot_begin, slot_rows, idx, n_kept, tail, row_frame=None, stream=None):

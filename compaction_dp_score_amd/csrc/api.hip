@@ -189,28 +189,75 @@ dp_status dp_gather_kv(const dp_kv* kv, const int32_t* idx, const int64_t* n_kep
   return st;
 }
 
+static dp_status check_reindex(void* const* k_layers, int32_t n_layers, int32_t n_heads,
+                               int32_t head_dim, int32_t dtype, int64_t row_begin,
+                               int64_t rows_capacity, const int64_t* n_rows,
+                               const int32_t* row_frame, const dp_rope* rope, const void* ws,
+                               size_t ws_bytes, const char* who) {
+  if (!k_layers || !row_frame || !rope)
+    return fail(DP_EINVAL, "%s: k_layers, row_frame and rope are required", who);
+  dp_status st = check_shape(n_layers, n_heads, head_dim, dtype, who);
+  if (st != DP_OK) return st;
+  st = check_rope(rope, head_dim, dtype, ws, ws_bytes, who);
+  if (st != DP_OK) return st;
+  const int64_t per_row = (int64_t)n_heads * (head_dim * elem_size(dtype) / 16);
+  const int64_t span = rows_capacity - row_begin;
+  if (row_begin < 0 || rows_capacity < 0 || rows_capacity >= kMaxRows || span * per_row >= kMaxVec ||
+      (span > 0 && (span * per_row + 255) / 256 * n_layers >= kMaxVec))
+    return fail(DP_ERANGE, "%s: rows x layers out of range", who);
+  if (n_rows && !aligned(n_rows, 8)) return fail(DP_EALIGN, "%s: n_rows alignment", who);
+  return DP_OK;
+}
+
 dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_heads,
                           int32_t head_dim, int32_t dtype, int64_t rows_capacity,
                           const int64_t* n_rows, const int32_t* row_frame, const dp_rope* rope,
                           void* ws, size_t ws_bytes, void* stream) {
-  if (!k_layers || !row_frame || !rope)
-    return fail(DP_EINVAL, "dp_rope_reindex: k_layers, row_frame and rope are required");
-  dp_status st = check_shape(n_layers, n_heads, head_dim, dtype, "dp_rope_reindex");
+  dp_status st = check_reindex(k_layers, n_layers, n_heads, head_dim, dtype, 0, rows_capacity,
+                               n_rows, row_frame, rope, ws, ws_bytes, "dp_rope_reindex");
   if (st != DP_OK) return st;
-  st = check_rope(rope, head_dim, dtype, ws, ws_bytes, "dp_rope_reindex");
-  if (st != DP_OK) return st;
-  const int64_t per_row = (int64_t)n_heads * (head_dim * elem_size(dtype) / 16);
-  if (rows_capacity < 0 || rows_capacity >= kMaxRows || rows_capacity * per_row >= kMaxVec ||
-      (rows_capacity * per_row + 255) / 256 * n_layers >= kMaxVec)
-    return fail(DP_ERANGE, "dp_rope_reindex: rows_capacity x layers out of range");
-  if (n_rows && !aligned(n_rows, 8)) return fail(DP_EALIGN, "dp_rope_reindex: n_rows alignment");
   (void)hipGetLastError();
   hipStream_t s = (hipStream_t)stream;
   RopeView view{};
   st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, s);
   if (st != DP_OK) return st;
-  st = launch_reindex(k_layers, n_layers, n_heads, head_dim, dtype, rows_capacity, n_rows,
+  st = launch_reindex(k_layers, n_layers, n_heads, head_dim, dtype, 0, rows_capacity, n_rows,
                       row_frame, view, s);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+dp_status dp_rope_prepare(const dp_rope* rope, int32_t head_dim, int32_t dtype, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!rope) return fail(DP_EINVAL, "dp_rope_prepare: rope is required");
+  dp_status st = check_shape(1, 1, head_dim, dtype, "dp_rope_prepare");
+  if (st != DP_OK) return st;
+  st = check_rope(rope, head_dim, dtype, ws, ws_bytes, "dp_rope_prepare");
+  if (st != DP_OK) return st;
+  (void)hipGetLastError();
+  RopeView view{};
+  st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+dp_status dp_rope_apply(void* const* k_layers, int32_t n_layers, int32_t n_heads, int32_t head_dim,
+                        int32_t dtype, int64_t row_begin, int64_t rows_capacity,
+                        const int64_t* n_rows, const int32_t* row_frame, const dp_rope* rope,
+                        const void* ws, size_t ws_bytes, void* stream) {
+  dp_status st = check_reindex(k_layers, n_layers, n_heads, head_dim, dtype, row_begin,
+                               rows_capacity, n_rows, row_frame, rope, ws, ws_bytes,
+                               "dp_rope_apply");
+  if (st != DP_OK) return st;
+  if (rows_capacity <= row_begin) {
+    ok();
+    return DP_OK;
+  }
+  (void)hipGetLastError();
+  RopeView view{};
+  rope_view(*rope, ws, &view, dtype, head_dim);
+  st = launch_reindex(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_capacity,
+                      n_rows, row_frame, view, (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }
@@ -229,9 +276,8 @@ dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t sl
                 "capacity < 2^31");
   const int64_t rv = (int64_t)kv->n_heads * kv->head_dim * elem_size(kv->dtype) / 16;
   const int n_kv = kv->v_layers ? 2 : 1;
-  if (slot_rows * rv >= kMaxVec ||
-      (int64_t)kv->n_layers * n_kv * ((slot_rows * rv + 255) / 256) >= kMaxVec)
-    return fail(DP_ERANGE, "dp_append_kept: slot too large for one launch");
+  if (slot_rows * rv >= kMaxVec || (int64_t)kv->n_layers * n_kv > 65535)
+    return fail(DP_ERANGE, "dp_append_kept: slot or layer count too large for one launch");
   if (!aligned(n_kept, 8) || !aligned(tail, 8) || (idx && !aligned(idx, 4)) ||
       (row_frame && !aligned(row_frame, 4)) || (kv->dev_error && !aligned(kv->dev_error, 4)))
     return fail(DP_EALIGN, "dp_append_kept: misaligned count, tail, index or frame array");

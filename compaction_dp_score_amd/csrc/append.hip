@@ -4,9 +4,9 @@
 // the dense window.  With the cache kept as [sink | window ring | history] in
 // one buffer per layer, only the kept rows of the slot that holds the leaving
 // chunk move: they are appended at the history tail.  append_kernel copies them
-// for all layers, K and V, in one 1-D launch (one 16-byte vector per lane,
-// non-temporal, dense mapping from the device-side kept count, like the
-// out-of-place gather); append_finish_kernel then retires the slot's row frames
+// for all layers, K and V, in one launch (grid y = layer and K|V; a fixed
+// number of workgroups per slab stride over the live tiles; one 16-byte vector
+// per lane, non-temporal); append_finish_kernel then retires the slot's row frames
 // (-1) and advances the tail.  Both launches re-derive the appended span from
 // the same device values, and the finish launch runs after the copy on the
 // stream, so the tail is never read after it changes.
@@ -14,6 +14,8 @@
 
 namespace dp {
 namespace {
+
+constexpr uint32_t kAppendBlocksPerSlab = 1024;
 
 struct AppendArgs {
   void* const* k_layers;
@@ -50,22 +52,23 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendArgs a) {
   if (!append_span(a, t0, n, err)) return;            // reported by append_finish_kernel
   const uint32_t per_slab = (uint32_t)(n * (int64_t)a.div_row.d);
   const uint32_t tiles = (per_slab + kBlock - 1) / kBlock;
-  if (tiles == 0) return;
-  const uint32_t slab = blockIdx.x / tiles;
-  if (slab >= a.n_slabs) return;
-  const uint32_t i = (blockIdx.x - slab * tiles) * kBlock + threadIdx.x;
-  if (i >= per_slab) return;
-  const int layer = (int)(slab / a.n_kv);
-  const bool is_v = (slab % a.n_kv) == 1;
+  const int layer = (int)(blockIdx.y / a.n_kv);
+  const bool is_v = (blockIdx.y % a.n_kv) == 1;
   u32x4* __restrict__ base = reinterpret_cast<u32x4*>(is_v ? a.v_layers[layer] : a.k_layers[layer]);
-  const uint32_t j = fdiv(i, a.div_row);
-  const uint32_t c = i - j * a.div_row.d;
-  const int32_t s = a.idx[j];
-  if ((uint64_t)(uint32_t)s >= (uint64_t)a.slot_rows) return;   // out-of-range entries are skipped
-  const u32x4 v =
-      __builtin_nontemporal_load(base + (a.slot_begin + s) * (int64_t)a.div_row.d + c);
-  __builtin_nontemporal_store(v, base + (t0 + j) * (int64_t)a.div_row.d + c);
-  if (a.row_frame && slab == 0 && c == 0) a.row_frame[t0 + j] = a.row_frame[a.slot_begin + s];
+  // A chunk keeps a small share of its rows, so the grid is a fixed number of
+  // workgroups per slab that stride over the live tiles (no idle workgroups).
+  for (uint32_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const uint32_t i = t * kBlock + threadIdx.x;
+    if (i >= per_slab) break;
+    const uint32_t j = fdiv(i, a.div_row);
+    const uint32_t c = i - j * a.div_row.d;
+    const int32_t s = a.idx[j];
+    if ((uint64_t)(uint32_t)s >= (uint64_t)a.slot_rows) continue;   // out-of-range entries skipped
+    const u32x4 v =
+        __builtin_nontemporal_load(base + (a.slot_begin + s) * (int64_t)a.div_row.d + c);
+    __builtin_nontemporal_store(v, base + (t0 + j) * (int64_t)a.div_row.d + c);
+    if (a.row_frame && blockIdx.y == 0 && c == 0) a.row_frame[t0 + j] = a.row_frame[a.slot_begin + s];
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void append_finish_kernel(AppendArgs a) {
@@ -101,10 +104,10 @@ dp_status launch_append(const dp_kv_inplace& kv, int64_t slot_begin, int64_t slo
   a.div_row = make_fastdiv((uint32_t)((int64_t)kv.n_heads * kv.head_dim * elem_size(kv.dtype) / 16));
   a.n_kv = kv.v_layers ? 2 : 1;
   a.n_slabs = (uint32_t)(kv.n_layers * a.n_kv);
-  const uint64_t gx =
-      (uint64_t)a.n_slabs * (((uint64_t)slot_rows * a.div_row.d + kBlock - 1) / kBlock);
+  const uint64_t tiles_cap = ((uint64_t)slot_rows * a.div_row.d + kBlock - 1) / kBlock;
+  const uint32_t gx = (uint32_t)(tiles_cap < kAppendBlocksPerSlab ? tiles_cap : kAppendBlocksPerSlab);
   if (gx > 0) {
-    hipLaunchKernelGGL(append_kernel, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(append_kernel, dim3(gx, a.n_slabs), dim3(kBlock), 0, s, a);
     dp_status st = check_launch("append_kernel");
     if (st != DP_OK) return st;
   }

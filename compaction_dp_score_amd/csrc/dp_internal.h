@@ -162,9 +162,11 @@ dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dt
                               int head_dim, hipStream_t s);
 dp_status launch_gather(const dp_kv& kv, const int32_t* idx, const int64_t* n_kept,
                         const int32_t* row_frame, const RopeView* rope, hipStream_t s);
+void rope_view(const dp_rope& r, const void* ws, RopeView* view, int dtype, int head_dim);
 dp_status launch_reindex(void* const* k, int32_t n_layers, int32_t n_heads, int32_t head_dim,
-                         int32_t dtype, int64_t rows_cap, const int64_t* n_rows,
-                         const int32_t* row_frame, const RopeView& rope, hipStream_t s);
+                         int32_t dtype, int64_t row_begin, int64_t rows_cap,
+                         const int64_t* n_rows, const int32_t* row_frame, const RopeView& rope,
+                         hipStream_t s);
 dp_status launch_append(const dp_kv_inplace& kv, int64_t slot_begin, int64_t slot_rows,
                         const int32_t* idx, const int64_t* n_kept, int64_t* tail,
                         int32_t* row_frame, hipStream_t s);

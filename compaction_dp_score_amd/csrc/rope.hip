@@ -55,6 +55,7 @@ struct ReindexArgs {
   void* const* layers;
   const int32_t* row_frame;
   const int64_t* n_rows;
+  int64_t row_begin;
   int64_t rows_cap;
   FastDiv div_row;    // vectors per row  = H * wv_count
   FastDiv div_head;   // vectors per head = wv_count
@@ -76,23 +77,25 @@ struct ReindexArgs {
 // unchanged so that whole 128-byte lines are rewritten.
 template <bool TWO_ROWS>
 __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
-  int64_t n = a.rows_cap;
-  if (a.n_rows) n = min(n, *a.n_rows);
+  int64_t end = a.rows_cap;
+  if (a.n_rows) end = min(end, *a.n_rows);
+  const int64_t n = end - a.row_begin;               // rows [row_begin, end)
+  if (n <= 0) return;
   const uint32_t per_row = a.div_row.d;
   const uint32_t per_layer = (uint32_t)(n * (int64_t)per_row);
   const uint32_t tiles = (per_layer + kBlock - 1) / kBlock;
-  if (tiles == 0) return;
   const uint32_t layer = blockIdx.x / tiles;
   if (layer >= a.n_layers) return;
   const uint32_t first = (blockIdx.x - layer * tiles) * kBlock;
   const uint32_t i = first + threadIdx.x;
+  const int32_t* __restrict__ rframe = a.row_frame + a.row_begin;
   float dl;
   int f;
   uint32_t j;
   if (TWO_ROWS) {
     const uint32_t ja = fdiv(first, a.div_row);
     const uint32_t jb = (int64_t)ja + 1 < n ? ja + 1 : ja;
-    const int fa = a.row_frame[ja], fb = a.row_frame[jb];
+    const int fa = rframe[ja], fb = rframe[jb];
     // a frame outside the table is skipped rather than read out of bounds
     const float da = (uint32_t)fa < (uint32_t)a.rope.n_frames ? a.rope.delta[fa] : 0.0f;
     const float db = (uint32_t)fb < (uint32_t)a.rope.n_frames ? a.rope.delta[fb] : 0.0f;
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
   } else {
     if (i >= per_layer) return;
     j = fdiv(i, a.div_row);
-    f = a.row_frame[j];
+    f = rframe[j];
     dl = (uint32_t)f < (uint32_t)a.rope.n_frames ? a.rope.delta[f] : 0.0f;
   }
   if (dl == 0.0f) return;
@@ -117,8 +120,8 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
   const f32x4* t = reinterpret_cast<const f32x4*>(a.rope.cs + (int64_t)f * a.rope.pairs_padded + p0);
   const f32x4 t01 = t[0];     // the table has a 32-byte tail, so t[1] is readable
   const f32x4 t23 = t[1];
-  u32x4* __restrict__ p =
-      reinterpret_cast<u32x4*>(a.layers[layer]) + ((int64_t)j * a.n_heads + h) * a.vph + wq;
+  u32x4* __restrict__ p = reinterpret_cast<u32x4*>(a.layers[layer]) +
+                          ((a.row_begin + (int64_t)j) * a.n_heads + h) * a.vph + wq;
   u32x4 v = __builtin_nontemporal_load(p);
   if (in_block) v = rotate_vec_tab(v, a.dtype, t01, t23, min(a.rope.ppv, a.rope.n_pairs - p0));
   __builtin_nontemporal_store(v, p);
@@ -132,16 +135,11 @@ size_t rope_ws_bytes(int32_t n_frames, int32_t n_pairs) {
   return dbytes + (size_t)n_frames * pp * sizeof(f32x2) + 32;   // 32-byte tail: see gather
 }
 
-dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dtype,
-                              int head_dim, hipStream_t s) {
+void rope_view(const dp_rope& r, const void* ws, RopeView* view, int dtype, int head_dim) {
   const int32_t pp = (r.n_pairs + 3) / 4 * 4;
   const size_t dbytes = ((size_t)r.n_frames * 4 + 15) / 16 * 16;
-  float* delta = reinterpret_cast<float*>(ws);
-  f32x2* cs = reinterpret_cast<f32x2*>(reinterpret_cast<char*>(ws) + dbytes);
-  hipLaunchKernelGGL(rope_prepare_kernel, dim3(r.n_frames), dim3(64), 0, s, r.theta, r.n_pairs,
-                     pp, r.frame_t, r.frame_phase, r.q0, r.knee, r.inv_factor, delta, cs);
-  dp_status st = check_launch("rope_prepare_kernel");
-  if (st != DP_OK) return st;
+  const float* delta = reinterpret_cast<const float*>(ws);
+  const f32x2* cs = reinterpret_cast<const f32x2*>(reinterpret_cast<const char*>(ws) + dbytes);
   const int esz = elem_size(dtype);
   view->delta = delta;
   view->cs = cs;
@@ -158,16 +156,31 @@ dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dt
   if (we > vph) we = vph;
   view->wv_begin = wb;
   view->wv_count = we - wb;
+}
+
+dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dtype,
+                              int head_dim, hipStream_t s) {
+  const int32_t pp = (r.n_pairs + 3) / 4 * 4;
+  const size_t dbytes = ((size_t)r.n_frames * 4 + 15) / 16 * 16;
+  float* delta = reinterpret_cast<float*>(ws);
+  f32x2* cs = reinterpret_cast<f32x2*>(reinterpret_cast<char*>(ws) + dbytes);
+  hipLaunchKernelGGL(rope_prepare_kernel, dim3(r.n_frames), dim3(64), 0, s, r.theta, r.n_pairs,
+                     pp, r.frame_t, r.frame_phase, r.q0, r.knee, r.inv_factor, delta, cs);
+  dp_status st = check_launch("rope_prepare_kernel");
+  if (st != DP_OK) return st;
+  rope_view(r, ws, view, dtype, head_dim);
   return DP_OK;
 }
 
 dp_status launch_reindex(void* const* k, int32_t n_layers, int32_t n_heads, int32_t head_dim,
-                         int32_t dtype, int64_t rows_cap, const int64_t* n_rows,
-                         const int32_t* row_frame, const RopeView& rope, hipStream_t s) {
+                         int32_t dtype, int64_t row_begin, int64_t rows_cap,
+                         const int64_t* n_rows, const int32_t* row_frame, const RopeView& rope,
+                         hipStream_t s) {
   ReindexArgs a;
   a.layers = k;
   a.row_frame = row_frame;
   a.n_rows = n_rows;
+  a.row_begin = row_begin;
   a.rows_cap = rows_cap;
   a.div_row = make_fastdiv((uint32_t)(n_heads * rope.wv_count));
   a.div_head = make_fastdiv((uint32_t)rope.wv_count);
@@ -176,7 +189,8 @@ dp_status launch_reindex(void* const* k, int32_t n_layers, int32_t n_heads, int3
   a.n_layers = (uint32_t)n_layers;
   a.dtype = dtype;
   a.rope = rope;
-  const uint64_t gx = ((uint64_t)rows_cap * a.div_row.d + kBlock - 1) / kBlock * (uint64_t)n_layers;
+  const uint64_t span = rows_cap > row_begin ? (uint64_t)(rows_cap - row_begin) : 0;
+  const uint64_t gx = (span * a.div_row.d + kBlock - 1) / kBlock * (uint64_t)n_layers;
   if (gx == 0) return DP_OK;
   if (a.div_row.d >= (uint32_t)kBlock)
     hipLaunchKernelGGL(reindex_kernel<true>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);

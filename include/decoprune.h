@@ -233,6 +233,23 @@ dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_hea
                           const dp_rope* rope, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Two-phase form of the same re-index, for caches whose re-indexed rows are
+ * not one range (the [sink | window ring | history] layout of dp_append_kept):
+ * dp_rope_prepare computes the per-frame phase steps and {cos, sin} table into
+ * the workspace and advances frame_phase, once per step; dp_rope_apply then
+ * re-rotates rows [row_begin, min(rows_capacity, *n_rows)) (n_rows device or
+ * NULL) of every layer from that table, and may be called for several row
+ * ranges.  The dp_rope passed to both must describe the same tables; apply
+ * reads only its pair layout and frame count.  head_dim and dtype are those
+ * of the keys apply will rotate. */
+dp_status dp_rope_prepare(const dp_rope* rope, int32_t head_dim, int32_t dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+dp_status dp_rope_apply(void* const* k_layers, int32_t n_layers, int32_t n_heads,
+                        int32_t head_dim, int32_t dtype, int64_t row_begin,
+                        int64_t rows_capacity, const int64_t* n_rows, const int32_t* row_frame,
+                        const dp_rope* rope, const void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* ------------------------------------------------------------------------- *
  * 4b. Segment-append compaction in place     [DeCoPrune page, 어떻게 동작하나]
  *
@@ -252,7 +269,9 @@ dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_hea
  * Device-side checks: if the appended rows would pass `capacity` or overlap
  * the slot, nothing is copied or advanced and *dev_error = DP_ECAPACITY or
  * DP_ERANGE.  Two launches on `stream`.  The old keys are then re-indexed in
- * place with dp_rope_reindex over rows [0, *tail) (n_rows = tail).
+ * place: dp_rope_prepare once, then dp_rope_apply over the sink rows and over
+ * the history rows [history_begin, *tail) (n_rows = tail); the window slots
+ * need no re-index while they are in the window.
  * ------------------------------------------------------------------------- */
 typedef struct {
   void* const* k_layers;     /* device array [n_layers]: [capacity][n_heads][head_dim] */

@@ -24,7 +24,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(dp.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -248,3 +248,18 @@ def test_append_kept_rejects_missing_and_misaligned():
     assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, None, None, None) == dp.DP_EINVAL
     assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE + 4, FAKE, None, None) == dp.DP_EALIGN
     assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, FAKE, FAKE + 2, None) == dp.DP_EALIGN
+
+
+def test_rope_prepare_and_apply_reject():
+    r = _rope()
+    nb = dp.dp_rope_workspace_bytes(10, 8)
+    assert _status("rope_prepare", None, 64, 1, FAKE, nb, None) == dp.DP_EINVAL
+    assert _status("rope_prepare", ctypes.byref(r), 64, 1, FAKE, nb - 1, None) == dp.DP_EINVAL
+    assert _status("rope_prepare", ctypes.byref(r), 63, 1, FAKE, nb, None) == dp.DP_EINVAL
+    f = lambda *a: _status("rope_apply", *a)
+    assert f(FAKE, 1, 4, 64, 1, -1, 100, None, FAKE, ctypes.byref(r), FAKE, nb, None) == dp.DP_ERANGE
+    assert f(FAKE, 1, 4, 64, 1, 0, 1 << 31, None, FAKE, ctypes.byref(r), FAKE, nb, None) == dp.DP_ERANGE
+    assert f(FAKE, 1, 4, 64, 1, 0, 100, None, None, ctypes.byref(r), FAKE, nb, None) == dp.DP_EINVAL
+    assert f(FAKE, 1, 4, 64, 1, 0, 100, FAKE + 4, FAKE, ctypes.byref(r), FAKE, nb, None) == dp.DP_EALIGN
+    # an empty range is accepted without any launch
+    assert f(FAKE, 1, 4, 64, 1, 50, 50, None, FAKE, ctypes.byref(r), FAKE, nb, None) == dp.DP_OK

@@ -199,7 +199,9 @@ def test_ring_rollout_matches_oracle_and_out_of_place():
         dp.dp_compact_index(keep, C, idx, nk, None, None, wsc)
         dp.dp_append_kept(kv, sb, C, idx, nk, tail, rf_d)
         rope = dp.make_rope(th_d, ft_d, phase_d, q0, KNEE, 1.0 / FACTOR)
-        dp.dp_rope_reindex(arr_k, L, H, D, dp.DP_BF16, cap, tail, rf_d, rope, ws)
+        dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws)                  # old keys only:
+        dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, 0, C, None, rf_d, rope, ws)        # sink
+        dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, C + R * C, cap, tail, rf_d, rope, ws)  # history
         c_new = R + 1 + s
         for l in range(L):                          # the model writes the new chunk into the slot
             k[l][sb:sb + C] = bf16_from_bits(k_new[l], dev)

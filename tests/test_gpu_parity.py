@@ -356,6 +356,45 @@ def test_rope_reindex_in_place(L, T, H, D, dtype, tpf, pb, npairs, device_rows):
     assert np.array_equal(devt["frame_phase"].cpu().numpy(), tables[3])
 
 
+@pytest.mark.parametrize("L,T,H,D,dtype,tpf,pb,npairs", ROPE_CASES[:1] + ROPE_CASES[2:3] + ROPE_CASES[4:5])
+def test_rope_prepare_then_apply_on_two_ranges(L, T, H, D, dtype, tpf, pb, npairs):
+    """One prepare, then apply on [a, b) and on [c, *n_rows): the same rotation as
+    the one-call re-index on those rows; every other row is untouched."""
+    dev = device()
+    rng = np.random.default_rng(T * 5 + D)
+    kb = _layers(rng, L, T, H, D, dtype, scale=3.0)
+    n_frames = (T + tpf - 1) // tpf
+    rf = (np.arange(T) // tpf).astype(np.int32)
+    host, devt = _rope_inputs(rng, n_frames, npairs, float(n_frames), 5.0, 8.0, dev, True)
+    k = _dev_layers(kb, dtype, dev)
+    arr = dp.ptr_array(k, dev)
+    a, b, c, e = 3, T // 3, T // 2 + 7, T - 11
+    rope = dp.make_rope(devt["theta"], devt["frame_t"], devt["frame_phase"], host["q0"],
+                        host["knee"], host["inv_factor"], pb)
+    ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, npairs) // 4, dtype=torch.float32,
+                     device=dev)
+    rfd = to_dev(rf, dev)
+    dp.dp_rope_prepare(rope, D, dtype, ws)
+    dp.dp_rope_apply(arr, L, H, D, dtype, a, b, None, rfd, rope, ws)
+    dp.dp_rope_apply(arr, L, H, D, dtype, c, T, torch.tensor([e], dtype=torch.int64, device=dev),
+                     rfd, rope, ws)
+    dp.dp_rope_apply(arr, L, H, D, dtype, b, b, None, rfd, rope, ws)      # empty range
+    torch.cuda.synchronize()
+    kk = (kb.view(np.float32) if dtype == dp.DP_F32 else kb).copy()
+    tables = oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
+                                host["inv_factor"], host["theta"])
+    assert np.array_equal(devt["frame_phase"].cpu().numpy(), tables[3])
+    for l in range(L):
+        for lo, hi in ((a, b), (c, e)):
+            sub = np.ascontiguousarray(kk[l][lo:hi])
+            oracle.rope_rows(sub, rf[lo:hi], pb, tables)
+            kk[l][lo:hi] = sub
+        want = kk[l].view(np.uint32) if dtype == dp.DP_F32 else kk[l]
+        ok, worst, ne = keys_close(bits(k[l]), want, TOL[dtype])
+        assert ok, (l, worst)
+        assert ne == 0, ne
+
+
 def test_rope_reindex_factor_one_is_identity():
     dev = device()
     rng = np.random.default_rng(21)

@@ -44,6 +44,7 @@ def lib():
         L.oracle_rope_headrows.argtypes = [P, i32, i64, i32, i32, i32, P, P, P, P]
         L.oracle_hs_offsets.argtypes = [P, i32, i32, P, P]
         L.oracle_hs_gather_layer.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P]
+        L.oracle_attention.argtypes = [P, P, P, P, i64, i64, i32, i32, ctypes.c_double, P]
         L.oracle_pr.argtypes = [i64, i64]
         L.oracle_pr.restype = ctypes.c_double
         _lib = L
@@ -225,6 +226,22 @@ def hs_gather_layer(src_layer, layer, head_class, class_lists, offsets, out):
     assert out.flags.c_contiguous and out.dtype == s.dtype
     lib().oracle_hs_gather_layer(_p(s), layer, H, s.shape[2], s.itemsize, _p(hc), _p(cat),
                                  _p(base), _p(lens), _p(off), _p(out))
+    return out
+
+
+def attention(q, k, v, rows, n_kv=None, scale=None):
+    """Attention of the listed query rows over keys [0, n_kv) (float64 result
+    [len(rows), H, D]); q, k, v: [rows, H, D] bf16 bit patterns (uint16)."""
+    q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    assert q.dtype == k.dtype == v.dtype == np.uint16
+    H, D = q.shape[1], q.shape[2]
+    n_kv = k.shape[0] if n_kv is None else n_kv
+    assert 1 <= n_kv <= k.shape[0] and v.shape[0] >= n_kv
+    rows = _c(rows, np.int64)
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < q.shape[0])
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    out = np.empty((rows.shape[0], H, D), np.float64)
+    lib().oracle_attention(_p(q), _p(k), _p(v), _p(rows), rows.shape[0], n_kv, H, D, scale, _p(out))
     return out
 
 

@@ -28,6 +28,8 @@
 #include <stdint.h>
 #include <string.h>
 
+static float bf16_to_f32(uint16_t h);
+
 #define ORACLE_ABI 1
 int oracle_abi(void) { return ORACLE_ABI; }
 
@@ -303,6 +305,47 @@ void oracle_hs_gather_layer(const uint8_t* src, int32_t layer, int32_t n_heads,
     for (int64_t j = 0; j < class_len[c]; ++j)
       memcpy(out + (offsets[i] + j) * hb, src + ((int64_t)list[j] * n_heads + h) * hb,
              (size_t)hb);
+  }
+}
+
+/* ---------------------------------------------------------------------- *
+ * Attention of a chunk over the retained cache [DeCoPrune page, 무엇인가:
+ * each chunk attends to the KV cache of the history; 전제와 한계: the
+ * continuation speed-up comes from the shorter cache].  For the queries
+ * listed in rows (n_rows of them) and every head h:
+ *   O[i][h][:] = sum_j softmax_j(scale * <Q[i][h], K[j][h]>) V[j][h][:],  j < n_kv,
+ * evaluated in float64 from bf16 inputs; out is [n_rows][H][D] float64.
+ * Q, K, V: token-major [rows][H][D] bf16 bit patterns.
+ * ---------------------------------------------------------------------- */
+void oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const int64_t* rows, int64_t n_rows, int64_t n_kv, int32_t H, int32_t D,
+                      double scale, double* out) {
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < n_rows * H; ++r) {
+    const int64_t qi = rows[r / H];
+    const int32_t h = (int32_t)(r % H);
+    const uint16_t* qv = q + (qi * H + h) * (int64_t)D;
+    double m = -INFINITY;
+    double* o = out + r * (int64_t)D;
+    for (int32_t c = 0; c < D; ++c) o[c] = 0.0;
+    double l = 0.0;
+    for (int64_t j = 0; j < n_kv; ++j) {          /* running max and sum, float64 */
+      const uint16_t* kv = k + (j * H + h) * (int64_t)D;
+      double s = 0.0;
+      for (int32_t c = 0; c < D; ++c) s += (double)bf16_to_f32(qv[c]) * (double)bf16_to_f32(kv[c]);
+      s *= scale;
+      const uint16_t* vv = v + (j * H + h) * (int64_t)D;
+      if (s > m) {
+        double corr = exp(m - s);
+        l *= corr;
+        for (int32_t c = 0; c < D; ++c) o[c] *= corr;
+        m = s;
+      }
+      double p = exp(s - m);
+      l += p;
+      for (int32_t c = 0; c < D; ++c) o[c] += p * (double)bf16_to_f32(vv[c]);
+    }
+    for (int32_t c = 0; c < D; ++c) o[c] /= l;
   }
 }
 

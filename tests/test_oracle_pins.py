@@ -356,6 +356,51 @@ def test_hs_offsets_and_heads():
 
 
 # --------------------------------------------------------------------------
+# Attention over the retained cache
+# --------------------------------------------------------------------------
+def _bf16(rng, shape, scale=1.0):
+    import torch
+    x = torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32)).to(torch.bfloat16)
+    return x.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _f(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_attention_matches_numpy_softmax():
+    rng = np.random.default_rng(16)
+    nq, nk, H, D = 7, 300, 3, 32
+    q, k, v = _bf16(rng, (nq, H, D)), _bf16(rng, (nk, H, D)), _bf16(rng, (nk, H, D))
+    rows = np.array([0, 3, 6])
+    got = oracle.attention(q, k, v, rows, n_kv=250)
+    qf, kf, vf = _f(q), _f(k), _f(v)
+    for a, i in enumerate(rows):
+        for h in range(H):
+            s = kf[:250, h] @ qf[i, h] / np.sqrt(D)          # numpy float64 reference
+            p = np.exp(s - s.max())
+            want = (p / p.sum()) @ vf[:250, h]
+            assert np.allclose(got[a, h], want, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(17)
+    nk, H, D = 64, 2, 16
+    k, v = _bf16(rng, (nk, H, D)), _bf16(rng, (nk, H, D))
+    zero_q = np.zeros((1, H, D), np.uint16)
+    # a zero query weights every key equally: the output is the mean of V
+    got = oracle.attention(zero_q, k, v, [0])
+    assert np.allclose(got[0], _f(v).mean(axis=0), rtol=1e-12, atol=1e-14)
+    # a single key gives that key's value exactly
+    got = oracle.attention(_bf16(rng, (1, H, D)), k, v, [0], n_kv=1)
+    assert np.array_equal(got[0], _f(v)[0])
+    # a query strongly aligned with one key selects its value
+    q = k[5:6].copy()
+    got = oracle.attention(q, k, v, [0], scale=1e4)
+    assert np.allclose(got[0], _f(v)[5], atol=1e-9)
+
+
+# --------------------------------------------------------------------------
 # Pruning ratio
 # --------------------------------------------------------------------------
 def test_pruning_ratio_integer_identity():

@@ -44,6 +44,7 @@ KERNELS = {
     "reindex": ("reindex_kernel", ("rope.hip", "dp_internal.h")),
     "hs": ("hs_gather_kernel", ("hs.hip", "dp_internal.h")),
     "append": ("reindex_kernel", ("rope.hip", "dp_internal.h")),
+    "attention": ("attn_fwd_kernel", ("attention.hip", "dp_internal.h")),
 }
 
 
@@ -57,7 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="eviction",
-                    choices=["eviction", "reindex", "prefix", "hs", "append"])
+                    choices=["eviction", "reindex", "prefix", "hs", "append", "attention"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -284,6 +285,30 @@ def setup_reindex(dev):
     return run, gt, accounting, None
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+
+
+def flops_record(args, acc, ms, k_ms):
+    """JSON record of a contraction workload (attention): TFLOP/s against the
+    dense bf16 MFMA peak."""
+    tf = acc["step_flops"] / (ms * 1e-3) / 1e12
+    ktf = acc["flops_per_launch"] / (k_ms * 1e-3) / 1e12
+    rec = {"metric": "attention TFLOP/s over the compacted cache", "value": round(tf, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": acc["config"],
+           "roofline": {"bound": "mfma", "kernel": KERNELS[args.workload][0],
+                        "achieved": round(ktf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(ktf / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": None, "flops_per_launch": acc["flops_per_launch"],
+                        "launch_ms": round(k_ms, 4)}}
+    if acc.get("full_ms"):
+        rec["fullkv"] = {"ms": round(acc["full_ms"], 4),
+                         "tflops": round(acc["full_flops"] / (acc["full_ms"] * 1e-3) / 1e12, 2),
+                         "speedup_of_compaction": round(acc["full_ms"] / k_ms, 3)}
+    return rec
+
+
 def copy_ceiling(dev, nbytes, reps=5):
     """Read+write GB/s of a plain 16-byte-vector device copy of nbytes, in
     the same run (the practical HBM ceiling a gather can approach)."""
@@ -454,6 +479,63 @@ def setup_append(dev):
                             "tokens": T, "scored_tokens": C, "kept_tokens": n,
                             "appended_bytes": append, "reindexed_head_rows": rotated,
                             "rope_pairs": w.rope_pairs, "q0": w.q0})
+
+    return run, gt, accounting, None
+
+
+def setup_attention(dev, layers=4):
+    """Attention of a new chunk (6,240 queries, 40 heads x 128, bf16) over the
+    cache a one-minute history leaves after compaction: sink + 15 % of the 56
+    prunable chunks + the 3-chunk window + the chunk itself (83,412 rows).  A
+    step is one dp_attention launch per layer over `layers` layers (each its own
+    cache).  For context the same launch over the FullKV cache (all 60 chunks
+    + the chunk, 380,640 rows) is timed once per layer, which gives the
+    attention-side speed-up of the compaction."""
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    w = dpsynth.WORKLOADS["reindex"]
+    H, D, C = w.n_heads, w.head_dim, w.chunk_tokens
+    n_ret = int(dpsynth.retained_keep(w).sum()) + C
+    n_full = w.seq_len + C
+    q = torch.empty((C, H, D), dtype=torch.bfloat16, device=dev)
+    dpsynth.kv_fill_device(q, "bf16", w.seed, 3, 0, C, H * D)
+    ks = _fill_layers(dev, w, n_ret, range(layers), dpsynth.STREAM_K)
+    vs = _fill_layers(dev, w, n_ret, range(layers), dpsynth.STREAM_V)
+    o = torch.empty_like(q)
+    scale = 1.0 / float(np.sqrt(D))
+    gt = Timer()
+
+    def run(timed):
+        for l in range(layers):
+            if timed and l == 0:
+                gt.start()
+            dp.dp_attention(q, ks[l], vs[l], o, C, n_ret, None, H, D, dp.DP_BF16, scale)
+            if timed and l == 0:
+                gt.stop()
+
+    def full_ms(reps=3):
+        kf = torch.empty((n_full, H, D), dtype=torch.bfloat16, device=dev)
+        vf = torch.empty((n_full, H, D), dtype=torch.bfloat16, device=dev)
+        dpsynth.kv_fill_device(kf, "bf16", w.seed, dpsynth.STREAM_K, 0, n_full, H * D)
+        dpsynth.kv_fill_device(vf, "bf16", w.seed, dpsynth.STREAM_V, 0, n_full, H * D)
+        dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale)
+        b.record()
+        torch.cuda.synchronize()
+        del kf, vf
+        return a.elapsed_time(b) / reps
+
+    def accounting():
+        flops = 4.0 * C * n_ret * D * H
+        return dict(n_kept=n_ret, gather_bytes=None, flops_per_launch=flops,
+                    step_flops=flops * layers, n_scored=0, full_ms=full_ms(),
+                    full_flops=4.0 * C * n_full * D * H,
+                    config={"workload": "attention", "layers": layers, "heads": H, "head_dim": D,
+                            "dtype": "bf16", "queries": C, "kv_rows": n_ret,
+                            "fullkv_rows": n_full})
 
     return run, gt, accounting, None
 
@@ -648,7 +730,7 @@ def main():
     import compaction_dp_score_amd  # noqa: F401  (fails loudly if the library is missing)
     dev = torch.device("cuda:0")
     setups = {"eviction": setup_eviction, "reindex": setup_reindex, "prefix": setup_prefix,
-              "hs": setup_hs, "append": setup_append}
+              "hs": setup_hs, "append": setup_append, "attention": setup_attention}
     if args.workload not in setups:
         print("workload %s is not wired into bench.py yet" % args.workload, file=sys.stderr)
         sys.exit(2)
@@ -666,6 +748,9 @@ def main():
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     acc = accounting()
+    if acc.get("flops_per_launch"):
+        print(json.dumps(flops_record(args, acc, ms, gt.mean_ms())), flush=True)
+        return
     gbs = acc["step_bytes"] / (ms * 1e-3) / 1e9
     g_ms = gt.mean_ms()
     g_gbs = acc["gather_bytes"] / (g_ms * 1e-3) / 1e9

@@ -383,6 +383,27 @@ dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layer
   return st;
 }
 
+dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
+                       int64_t kv_capacity, const int64_t* n_kv, int32_t n_heads,
+                       int32_t head_dim, int32_t dtype, float scale, void* stream) {
+  if (!q || !k || !v || !o) return fail(DP_EINVAL, "dp_attention: q, k, v and o are required");
+  if (dtype != DP_BF16 || head_dim != 128)
+    return fail(DP_EUNSUPPORTED, "dp_attention: only bf16 with head_dim 128 is implemented");
+  if (n_heads < 1 || n_q < 0 || kv_capacity < 0 || n_q >= kMaxRows || kv_capacity >= kMaxRows)
+    return fail(DP_ERANGE, "dp_attention: need n_heads >= 1 and 0 <= n_q, kv_capacity < 2^31");
+  if ((n_q + 127) / 128 * (int64_t)n_heads >= kMaxVec)
+    return fail(DP_ERANGE, "dp_attention: too many query tiles for one launch");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (n_kv && !aligned(n_kv, 8)))
+    return fail(DP_EALIGN, "dp_attention: tensors must be 16-byte aligned");
+  if (!(scale == scale)) return fail(DP_EINVAL, "dp_attention: scale is NaN");
+  (void)hipGetLastError();
+  dp_status st = launch_attention(q, k, v, o, n_q, kv_capacity, n_kv, n_heads, scale,
+                                  (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
 dp_status dp_pr_add(dp_pr_counter* acc, int64_t visible, int64_t full) {
   if (!acc) return fail(DP_EINVAL, "dp_pr_add: counter is required");
   if (visible < 0 || full < 0 || visible > full)

@@ -1,0 +1,248 @@
+// dp_attention: attention of a chunk's queries over the compacted KV cache.
+//
+// The DeCoPrune page (sections 무엇인가 and 전제와 한계) motivates the
+// compaction by the cost of each new chunk attending to the whole history KV
+// cache; the continuation speed-up it reports comes from this step running
+// over the shorter cache.  For every head h and query i < n_q:
+//   O[i][h] = sum_{j < n_kv} softmax_j(scale * <Q[i][h], K[j][h]>) V[j][h]
+// with bf16 inputs and outputs, fp32 accumulation and an online softmax.
+//
+// Workgroup = 128 queries of one head, 4 wavefronts of 32 queries.  Per tile of
+// 64 keys (staged in LDS: K row-major, V transposed):
+//   S^T = K Q^T    v_mfma_f32_32x32x16_bf16, Q held in registers as the B
+//                  operand, so a lane owns one query and 16 of its scores and
+//                  the softmax statistics stay in the lane (plus its partner
+//                  lane 32 apart, which owns the other 16 keys of the tile);
+//   O^T += V^T P^T the probabilities are fed back from the S^T accumulators as
+//                  the B operand without moving between lanes: the order of the
+//                  contraction over keys is permuted to match, and the V^T
+//                  operand reads the same permutation from LDS.
+// Query tiles of one head are placed on one XCD (workgroup i runs on XCD
+// i mod 8), so the key/value tiles they all stream are shared in that XCD's L2.
+#include "dp_internal.h"
+
+namespace dp {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;          // head_dim
+constexpr int kBM = 128;         // queries per workgroup
+constexpr int kBN = 64;          // keys per tile
+constexpr int kKP = kD + 8;      // K tile row pitch (bf16 elements)
+constexpr int kVP = kBN + 8;     // V^T tile row pitch (bf16 elements)
+constexpr int kXcds = 8;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  const int64_t* n_kv;
+  int64_t n_q;
+  int64_t kv_cap;
+  int64_t row;        // elements per token row: n_heads * head_dim
+  int32_t n_heads;
+  int32_t n_qt;       // query tiles per head
+  int32_t xcd_map;    // 1: group the query tiles of a head on one XCD
+  float c;            // scale * log2(e)
+};
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * kKP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVP];
+
+  int head, qt;
+  if (a.xcd_map) {
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    head = (slot / a.n_qt) * kXcds + xcd;
+    qt = slot % a.n_qt;
+  } else {
+    head = blockIdx.x / a.n_qt;
+    qt = blockIdx.x % a.n_qt;
+  }
+  if (head >= a.n_heads) return;
+  int64_t nkv = a.kv_cap;
+  if (a.n_kv) nkv = min(nkv, *a.n_kv);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int64_t qi = (int64_t)qt * kBM + wave * 32 + l32;
+  const bool qvalid = qi < a.n_q;
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qi][d] for d = 16 ds + 8 hf + e.
+  bf16x8 qb[kD / 16];
+  {
+    const uint16_t* qrow = a.q + (qvalid ? qi : 0) * a.row + (int64_t)head * kD;
+#pragma unroll
+    for (int ds = 0; ds < kD / 16; ++ds) {
+      u32x4 r = {0u, 0u, 0u, 0u};
+      if (qvalid) r = *reinterpret_cast<const u32x4*>(qrow + ds * 16 + hf * 8);
+      qb[ds] = __builtin_bit_cast(bf16x8, r);
+    }
+  }
+
+  f32x16 o[kD / 32];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+
+  // Each thread moves 4 consecutive keys of one 8-element chunk: K rows go to
+  // LDS as 16-byte writes, V is transposed in registers and written as four
+  // keys per 8-byte write.  The next tile's loads are issued before the current
+  // tile's MFMAs so that their latency is hidden.
+  const int key4 = (threadIdx.x >> 4) * 4, ch = threadIdx.x & 15;
+  u32x4 kr[4], vr[4];
+  auto load_tile = [&](int64_t kv0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      kr[u] = u32x4{0u, 0u, 0u, 0u};
+      vr[u] = u32x4{0u, 0u, 0u, 0u};
+      if (kv0 + key4 + u < nkv) {
+        const int64_t off = (kv0 + key4 + u) * a.row + (int64_t)head * kD + ch * 8;
+        kr[u] = *reinterpret_cast<const u32x4*>(a.k + off);
+        vr[u] = *reinterpret_cast<const u32x4*>(a.v + off);
+      }
+    }
+  };
+  load_tile(0);
+  for (int64_t kv0 = 0; kv0 < nkv; kv0 += kBN) {
+    // ---- stage K (row-major) and V (transposed) of 64 keys in LDS ----
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(Ks + (key4 + u) * kKP + ch * 8) = kr[u];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {            // element e of the chunk for the 4 keys
+      const int sh = (e & 1) * 16;
+      u32x2 w;
+      w[0] = ((vr[0][e >> 1] >> sh) & 0xFFFFu) | (((vr[1][e >> 1] >> sh) & 0xFFFFu) << 16);
+      w[1] = ((vr[2][e >> 1] >> sh) & 0xFFFFu) | (((vr[3][e >> 1] >> sh) & 0xFFFFu) << 16);
+      *reinterpret_cast<u32x2*>(Vt + (ch * 8 + e) * kVP + key4) = w;
+    }
+    __syncthreads();
+    if (kv0 + kBN < nkv) load_tile(kv0 + kBN);
+
+    // ---- S^T = K Q^T for two 32-key tiles ----
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
+#pragma unroll
+      for (int ds = 0; ds < kD / 16; ++ds) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + l32) * kKP + ds * 16 + hf * 8);
+        s[kt] = mfma(ka, qb[ds], s[kt]);
+      }
+    }
+
+    // ---- online softmax (base 2), lane-local per query plus partner lane ----
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t key = kv0 + kt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+        const float t = key < nkv ? s[kt][i] * a.c : -INFINITY;
+        s[kt][i] = t;
+        mt = fmaxf(mt, t);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(m, mt);
+    const float corr = __builtin_amdgcn_exp2f(m - mn);
+    float ls = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[kt][i] - mn);
+        s[kt][i] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 32, 64);
+    l = l * corr + ls;
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
+
+    // ---- P^T as B operands: key step ks takes accumulator entries 8 (ks & 1) .. +8 of
+    // tile ks >> 1, i.e. keys 32 (ks>>1) + 16 (ks&1) + 8 (e>>2) + 4 hf + (e&3) ----
+    bf16x8 pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack_bf16_hw(s[ks >> 1][8 * (ks & 1) + 2 * e], s[ks >> 1][8 * (ks & 1) + 2 * e + 1]);
+      pb[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    // ---- O^T += V^T P^T, V^T read in the same key order ----
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt) {
+      const uint16_t* vrow = Vt + (dt * 32 + l32) * kVP;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int base = (ks >> 1) * 32 + 16 * (ks & 1) + 4 * hf;
+        u32x4 w;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + base);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + base + 8);
+        w[0] = lo[0];
+        w[1] = lo[1];
+        w[2] = hi[0];
+        w[3] = hi[1];
+        o[dt] = mfma(__builtin_bit_cast(bf16x8, w), pb[ks], o[dt]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- O[qi][head][d], d = 32 dt + 8 g + 4 hf + (0..3) ----
+  if (qvalid) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    uint16_t* orow = a.o + qi * a.row + (int64_t)head * kD;
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16_hw(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
+        w[1] = pack_bf16_hw(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + dt * 32 + 8 * g + 4 * hf) = w;
+      }
+  }
+}
+
+}  // namespace
+
+dp_status launch_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
+                           int64_t kv_cap, const int64_t* n_kv, int32_t n_heads, float scale,
+                           hipStream_t s) {
+  AttnArgs a;
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.k = reinterpret_cast<const uint16_t*>(k);
+  a.v = reinterpret_cast<const uint16_t*>(v);
+  a.o = reinterpret_cast<uint16_t*>(o);
+  a.n_kv = n_kv;
+  a.n_q = n_q;
+  a.kv_cap = kv_cap;
+  a.row = (int64_t)n_heads * kD;
+  a.n_heads = n_heads;
+  a.n_qt = (int32_t)((n_q + kBM - 1) / kBM);
+  a.xcd_map = n_heads % kXcds == 0;
+  a.c = scale * 1.4426950408889634f;
+  const uint64_t blocks = (uint64_t)a.n_qt * n_heads;
+  if (blocks == 0) return DP_OK;
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+  return check_launch("attn_fwd_kernel");
+}
+
+}  // namespace dp

@@ -170,6 +170,9 @@ dp_status launch_reindex(void* const* k, int32_t n_layers, int32_t n_heads, int3
 dp_status launch_append(const dp_kv_inplace& kv, int64_t slot_begin, int64_t slot_rows,
                         const int32_t* idx, const int64_t* n_kept, int64_t* tail,
                         int32_t* row_frame, hipStream_t s);
+dp_status launch_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
+                           int64_t kv_cap, const int64_t* n_kv, int32_t n_heads, float scale,
+                           hipStream_t s);
 dp_status launch_hs_offsets(const uint8_t* head_class, int32_t L, int32_t H,
                             const int64_t* class_len, int32_t n_classes, int64_t* offsets,
                             hipStream_t s);

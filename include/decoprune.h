@@ -345,6 +345,26 @@ dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layer
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * 7. Attention over the compacted cache   [DeCoPrune page, 무엇인가 and 전제와 한계]
+ *
+ * The page's motivation: every new chunk attends to the KV cache of the whole
+ * history, so its cost grows with the rollout; the continuation speed-up it
+ * reports comes from this attention running over the compacted cache.  For
+ * each head h and query i < n_q:
+ *   o[i][h][:] = sum_{j < n} softmax_j(scale * <q[i][h], k[j][h]>) v[j][h][:]
+ * with n = min(kv_capacity, *n_kv) (n_kv device int64, or NULL for
+ * kv_capacity); n = 0 gives zeros.  q, o: [n_q][n_heads][head_dim];
+ * k, v: [kv_capacity][n_heads][head_dim] (one layer of the cache, e.g. the
+ * ring layout's rows [0, tail) including the chunk itself); all bf16, 16-byte
+ * aligned, o not overlapping the inputs.  fp32 accumulation and softmax;
+ * head_dim 128 and bf16 only (DP_EUNSUPPORTED otherwise).  No mask: every
+ * query sees every cached row.  One launch.
+ * ------------------------------------------------------------------------- */
+dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
+                       int64_t kv_capacity, const int64_t* n_kv, int32_t n_heads,
+                       int32_t head_dim, int32_t dtype, float scale, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * 6. Pruning ratio             [DeCoPrune page, 어떻게 쓰나 and 전제와 한계]
  *
  * The page measures efficiency as the cumulative reduction, against FullKV,

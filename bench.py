@@ -45,6 +45,7 @@ KERNELS = {
     "hs": ("hs_gather_kernel", ("hs.hip", "dp_internal.h")),
     "append": ("reindex_kernel", ("rope.hip", "dp_internal.h")),
     "attention": ("attn_fwd_kernel", ("attention.hip", "dp_internal.h")),
+    "hs_attention": ("attn_fwd_kernel", ("attention.hip", "dp_internal.h")),
 }
 
 
@@ -58,7 +59,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="eviction",
-                    choices=["eviction", "reindex", "prefix", "hs", "append", "attention"])
+                    choices=["eviction", "reindex", "prefix", "hs", "append", "attention",
+                             "hs_attention"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -293,7 +295,8 @@ def flops_record(args, acc, ms, k_ms):
     dense bf16 MFMA peak."""
     tf = acc["step_flops"] / (ms * 1e-3) / 1e12
     ktf = acc["flops_per_launch"] / (k_ms * 1e-3) / 1e12
-    rec = {"metric": "attention TFLOP/s over the compacted cache", "value": round(tf, 2),
+    rec = {"metric": acc.get("metric", "attention TFLOP/s over the compacted cache"),
+           "value": round(tf, 2),
            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": acc["config"],
@@ -540,6 +543,91 @@ def setup_attention(dev, layers=4):
     return run, gt, accounting, None
 
 
+def setup_hs_attention(dev, layers=4):
+    """Attention of a new chunk (6,240 queries, 40 heads x 128, bf16) over the
+    ragged DeCoPrune-HS cache of the 30-chunk HS workload: per layer a seeded
+    half of the heads static (sink + 3-chunk window, 24,960 rows), the others
+    the shared gamma mask (49,134 rows), each followed by the chunk's own 6,240
+    rows.  The per-head lengths and offsets are computed on the device
+    (score, mask, index, offsets); the cache contents are synthetic.  A step is
+    one dp_hs_attention launch per layer over `layers` layers of one packed
+    cache.  For context the dense launch over the FullKV cache (30 chunks + the
+    chunk, 193,440 rows) is timed once per layer."""
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    w = dpsynth.WORKLOADS["hs"]
+    T, H, D, C = w.seq_len, w.n_heads, w.head_dim, w.chunk_tokens
+    x0, xf = dpsynth.score_inputs(w)
+    x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
+    cls = dpsynth.hs_head_class(w)[:layers]
+    head_class = torch.from_numpy(cls.ravel().copy()).to(dev)
+    keeps = [torch.empty(T, dtype=torch.uint8, device=dev) for _ in range(2)]
+    lists = [torch.empty(T, dtype=torch.int32, device=dev) for _ in range(2)]
+    lens = torch.zeros(2, dtype=torch.int64, device=dev)
+    ws_c = torch.empty(dp.dp_compact_workspace_bytes(T) // 4 + 1, dtype=torch.int32, device=dev)
+    dp.dp_score_mask(None, None, w.d, w.d, dp.make_policy(T, w.sink_len, w.window_len,
+                     w.scored_begin, w.n_scored, w.gamma, mode=dp.DP_MODE_STREAMING), None, keeps[0])
+    dp.dp_score_mask(x0d, xfd, w.d, w.d, dp.make_policy(T, w.sink_len, w.window_len,
+                     w.scored_begin, w.n_scored, w.gamma), None, keeps[1])
+    for c in range(2):
+        dp.dp_compact_index(keeps[c], T, lists[c], lens[c:c + 1], None, None, ws_c)
+    offsets = torch.empty(layers * H + 1, dtype=torch.int64, device=dev)
+    dp.dp_hs_offsets(head_class, layers, H, lens, 2, offsets)
+    off = offsets.cpu().numpy()
+    total = int(off[-1])
+    kr = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    vr = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    dpsynth.kv_fill_device(kr, "bf16", w.seed, dpsynth.STREAM_K, 0, total, D)
+    dpsynth.kv_fill_device(vr, "bf16", w.seed, dpsynth.STREAM_V, 0, total, D)
+    q = torch.empty((C, H, D), dtype=torch.bfloat16, device=dev)
+    dpsynth.kv_fill_device(q, "bf16", w.seed, 3, 0, C, H * D)
+    kc = _fill_layers(dev, w, C, range(layers), dpsynth.STREAM_K)
+    vc = _fill_layers(dev, w, C, range(layers), dpsynth.STREAM_V)
+    o = torch.empty_like(q)
+    scale = 1.0 / float(np.sqrt(D))
+    gt = Timer()
+    n_full = T + C
+
+    def run(timed):
+        for l in range(layers):
+            if timed and l == 0:
+                gt.start()
+            dp.dp_hs_attention(q, kr, vr, total, offsets, l, kc[l], vc[l], C, o, C, H, D,
+                               dp.DP_BF16, scale)
+            if timed and l == 0:
+                gt.stop()
+
+    def full_ms(reps=3):
+        kf = torch.empty((n_full, H, D), dtype=torch.bfloat16, device=dev)
+        vf = torch.empty((n_full, H, D), dtype=torch.bfloat16, device=dev)
+        dpsynth.kv_fill_device(kf, "bf16", w.seed, dpsynth.STREAM_K, 0, n_full, H * D)
+        dpsynth.kv_fill_device(vf, "bf16", w.seed, dpsynth.STREAM_V, 0, n_full, H * D)
+        dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale)
+        b.record()
+        torch.cuda.synchronize()
+        del kf, vf
+        return a.elapsed_time(b) / reps
+
+    def accounting():
+        n0 = np.diff(off[:H + 1])                       # layer 0's head runs (the timed launch)
+        flops = 4.0 * C * D * float((n0 + C).sum())
+        return dict(n_kept=int(n0.sum()), gather_bytes=None, flops_per_launch=flops,
+                    step_flops=4.0 * C * D * float(total + layers * H * C), n_scored=0,
+                    full_ms=full_ms(), full_flops=4.0 * C * n_full * D * H,
+                    metric="attention TFLOP/s over the ragged DeCoPrune-HS cache",
+                    config={"workload": "hs_attention", "layers": layers, "heads": H,
+                            "head_dim": D, "dtype": "bf16", "queries": C,
+                            "head_rows_static": int(lens[0].item()),
+                            "head_rows_dynamic": int(lens[1].item()), "chunk_rows": C,
+                            "fullkv_rows": n_full})
+
+    return run, gt, accounting, None
+
+
 def setup_prefix(dev, slab_layers=20):
     """Prefix pruning of a 58-chunk observed context: all 57 non-sink chunks
     scored (d = 64) and compacted.  40 layers of K+V are 296.5 GB, more than
@@ -730,7 +818,8 @@ def main():
     import compaction_dp_score_amd  # noqa: F401  (fails loudly if the library is missing)
     dev = torch.device("cuda:0")
     setups = {"eviction": setup_eviction, "reindex": setup_reindex, "prefix": setup_prefix,
-              "hs": setup_hs, "append": setup_append, "attention": setup_attention}
+              "hs": setup_hs, "append": setup_append, "attention": setup_attention,
+              "hs_attention": setup_hs_attention}
     if args.workload not in setups:
         print("workload %s is not wired into bench.py yet" % args.workload, file=sys.stderr)
         sys.exit(2)

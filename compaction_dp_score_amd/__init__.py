@@ -102,6 +102,8 @@ _lib_hs_reindex = _sig("dp_hs_rope_reindex", [_P, _i64, _i32, _i32, _i32, _i32, 
                                               ctypes.POINTER(_i64), _P, _P, ctypes.POINTER(dp_rope),
                                               _P, ctypes.c_size_t, _P])
 _lib_attention = _sig("dp_attention", [_P, _P, _P, _P, _i64, _i64, _P, _i32, _i32, _i32, _f32, _P])
+_lib_hs_attention = _sig("dp_hs_attention", [_P, _P, _P, _i64, _P, _i32, _P, _P, _i64, _P, _i64,
+                                              _i32, _i32, _i32, _f32, _P])
 _lib_pr_add = _sig("dp_pr_add", [ctypes.POINTER(dp_pr_counter), _i64, _i64])
 _lib_pr_value = _sig("dp_pr_value", [ctypes.POINTER(dp_pr_counter)], ctypes.c_double)
 
@@ -109,7 +111,7 @@ EXPORTED = ["dp_abi_version", "dp_status_str", "dp_last_error", "dp_score_mask",
             "dp_compact_workspace_bytes", "dp_compact_index", "dp_rope_workspace_bytes",
             "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_append_kept",
             "dp_hs_offsets", "dp_hs_gather_kv",
-            "dp_hs_rope_reindex", "dp_attention", "dp_pr_add", "dp_pr_value"]
+            "dp_hs_rope_reindex", "dp_attention", "dp_hs_attention", "dp_pr_add", "dp_pr_value"]
 
 
 def dp_abi_version():
@@ -273,6 +275,14 @@ def dp_attention(q, k, v, o, n_q, kv_capacity, n_kv, n_heads, head_dim, dtype, s
                  stream=None):
     _check(_lib_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(n_q), int(kv_capacity),
                           _ptr(n_kv), n_heads, head_dim, dtype, float(scale), _stream(stream)))
+
+
+def dp_hs_attention(q, k_ragged, v_ragged, ragged_capacity, offsets, layer, k_chunk, v_chunk,
+                    n_chunk, o, n_q, n_heads, head_dim, dtype, scale, stream=None):
+    _check(_lib_hs_attention(_ptr(q), _ptr(k_ragged), _ptr(v_ragged), int(ragged_capacity),
+                             _ptr(offsets), int(layer), _ptr(k_chunk), _ptr(v_chunk), int(n_chunk),
+                             _ptr(o), int(n_q), n_heads, head_dim, dtype, float(scale),
+                             _stream(stream)))
 
 
 def dp_pr_add(counter, visible_positions, full_positions):

@@ -396,10 +396,43 @@ dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (n_kv && !aligned(n_kv, 8)))
     return fail(DP_EALIGN, "dp_attention: tensors must be 16-byte aligned");
-  if (!(scale == scale)) return fail(DP_EINVAL, "dp_attention: scale is NaN");
+  if (!(scale > 0.0f && scale <= 3.0e38f))
+    return fail(DP_EINVAL, "dp_attention: scale must be positive and finite");
   (void)hipGetLastError();
   dp_status st = launch_attention(q, k, v, o, n_q, kv_capacity, n_kv, n_heads, scale,
                                   (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+dp_status dp_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
+                          int64_t ragged_capacity, const int64_t* offsets, int32_t layer,
+                          const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
+                          int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
+                          float scale, void* stream) {
+  if (!q || !k_ragged || !v_ragged || !offsets || !o)
+    return fail(DP_EINVAL, "dp_hs_attention: q, k_ragged, v_ragged, offsets and o are required");
+  if (!k_chunk != !v_chunk)
+    return fail(DP_EINVAL, "dp_hs_attention: k_chunk and v_chunk are both given or both NULL");
+  if (dtype != DP_BF16 || head_dim != 128)
+    return fail(DP_EUNSUPPORTED, "dp_hs_attention: only bf16 with head_dim 128 is implemented");
+  if (n_heads < 1 || layer < 0 || n_q < 0 || n_q >= kMaxRows || ragged_capacity < 0 ||
+      ragged_capacity >= ((int64_t)1 << 40) || (k_chunk && (n_chunk < 0 || n_chunk >= kMaxRows)))
+    return fail(DP_ERANGE, "dp_hs_attention: need n_heads >= 1, layer >= 0, 0 <= n_q, n_chunk "
+                           "< 2^31 and 0 <= ragged_capacity < 2^40");
+  if ((int64_t)layer * n_heads >= kMaxRows)
+    return fail(DP_ERANGE, "dp_hs_attention: layer * n_heads beyond the offsets range");
+  if ((n_q + 127) / 128 * (int64_t)n_heads >= kMaxVec)
+    return fail(DP_ERANGE, "dp_hs_attention: too many query tiles for one launch");
+  if (!aligned(q, 16) || !aligned(k_ragged, 16) || !aligned(v_ragged, 16) || !aligned(o, 16) ||
+      !aligned(offsets, 8) || (k_chunk && (!aligned(k_chunk, 16) || !aligned(v_chunk, 16))))
+    return fail(DP_EALIGN, "dp_hs_attention: tensors must be 16-byte aligned (offsets 8)");
+  if (!(scale > 0.0f && scale <= 3.0e38f))
+    return fail(DP_EINVAL, "dp_hs_attention: scale must be positive and finite");
+  (void)hipGetLastError();
+  dp_status st = launch_hs_attention(q, k_ragged, v_ragged, ragged_capacity,
+                                     offsets + (int64_t)layer * n_heads, k_chunk, v_chunk,
+                                     n_chunk, o, n_q, n_heads, scale, (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }

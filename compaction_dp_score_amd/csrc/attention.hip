@@ -19,6 +19,12 @@
 //                  operand reads the same permutation from LDS.
 // Query tiles of one head are placed on one XCD (workgroup i runs on XCD
 // i mod 8), so the key/value tiles they all stream are shared in that XCD's L2.
+//
+// A head's keys come in up to two segments, streamed one after the other:
+// segment 0 is either the dense token-major cache [rows][heads][head_dim] or,
+// for DeCoPrune-HS, the head's own run of rows in the packed per-head cache
+// (offsets from dp_hs_offsets, consecutive rows head_dim apart); segment 1 is
+// an optional dense block (the chunk's own keys next to a ragged history).
 #include "dp_internal.h"
 
 namespace dp {
@@ -37,12 +43,16 @@ constexpr int kXcds = 8;
 
 struct AttnArgs {
   const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
   uint16_t* o;
-  const int64_t* n_kv;
+  const uint16_t* k0;  // segment 0
+  const uint16_t* v0;
+  const int64_t* n_kv; // dense segment 0: device count, or NULL
+  const int64_t* off;  // ragged segment 0: device head-row offsets of this layer's heads, or NULL
+  int64_t cap0;        // rows (dense) or head rows (ragged) of segment 0
+  const uint16_t* k1;  // segment 1: dense [n1][heads][head_dim], or NULL
+  const uint16_t* v1;
+  int64_t n1;
   int64_t n_q;
-  int64_t kv_cap;
   int64_t row;        // elements per token row: n_heads * head_dim
   int32_t n_heads;
   int32_t n_qt;       // query tiles per head
@@ -68,8 +78,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     qt = blockIdx.x % a.n_qt;
   }
   if (head >= a.n_heads) return;
-  int64_t nkv = a.kv_cap;
-  if (a.n_kv) nkv = min(nkv, *a.n_kv);
+  // segment 0 of this head: base element, key stride, count (device values clamped
+  // to the capacity, so no key outside [0, cap0) is read)
+  int64_t base0, stride0, n0;
+  if (a.off) {
+    const int64_t lo = min(max(a.off[head], (int64_t)0), a.cap0);
+    const int64_t hi = min(max(a.off[head + 1], lo), a.cap0);
+    base0 = lo * kD;
+    stride0 = kD;
+    n0 = hi - lo;
+  } else {
+    base0 = (int64_t)head * kD;
+    stride0 = a.row;
+    n0 = a.cap0;
+    if (a.n_kv) n0 = max(min(n0, *a.n_kv), (int64_t)0);
+  }
+  const int64_t n1 = a.k1 ? a.n1 : 0;
+  const int64_t t0 = (n0 + kBN - 1) / kBN;
+  const int64_t n_tiles = t0 + (n1 + kBN - 1) / kBN;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -101,20 +127,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // tile's MFMAs so that their latency is hidden.
   const int key4 = (threadIdx.x >> 4) * 4, ch = threadIdx.x & 15;
   u32x4 kr[4], vr[4];
-  auto load_tile = [&](int64_t kv0) {
+  auto load_tile = [&](int64_t t) {
+    const bool s1 = t >= t0;                       // uniform per workgroup
+    const uint16_t* kp = s1 ? a.k1 : a.k0;
+    const uint16_t* vp = s1 ? a.v1 : a.v0;
+    const int64_t stride = s1 ? a.row : stride0;
+    const int64_t base = (s1 ? (int64_t)head * kD : base0) + ch * 8;
+    const int64_t n = s1 ? n1 : n0;
+    const int64_t kv0 = (s1 ? t - t0 : t) * kBN;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       kr[u] = u32x4{0u, 0u, 0u, 0u};
       vr[u] = u32x4{0u, 0u, 0u, 0u};
-      if (kv0 + key4 + u < nkv) {
-        const int64_t off = (kv0 + key4 + u) * a.row + (int64_t)head * kD + ch * 8;
-        kr[u] = *reinterpret_cast<const u32x4*>(a.k + off);
-        vr[u] = *reinterpret_cast<const u32x4*>(a.v + off);
+      if (kv0 + key4 + u < n) {
+        const int64_t off = base + (kv0 + key4 + u) * stride;
+        kr[u] = *reinterpret_cast<const u32x4*>(kp + off);
+        vr[u] = *reinterpret_cast<const u32x4*>(vp + off);
       }
     }
   };
-  load_tile(0);
-  for (int64_t kv0 = 0; kv0 < nkv; kv0 += kBN) {
+  if (n_tiles > 0) load_tile(0);
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    const int64_t kv0 = (t >= t0 ? t - t0 : t) * kBN;   // first key of the tile in its segment
+    const int64_t nkv = t >= t0 ? n1 : n0;
     // ---- stage K (row-major) and V (transposed) of 64 keys in LDS ----
 #pragma unroll
     for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(Ks + (key4 + u) * kKP + ch * 8) = kr[u];
@@ -127,7 +162,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       *reinterpret_cast<u32x2*>(Vt + (ch * 8 + e) * kVP + key4) = w;
     }
     __syncthreads();
-    if (kv0 + kBN < nkv) load_tile(kv0 + kBN);
+    if (t + 1 < n_tiles) load_tile(t + 1);
 
     // ---- S^T = K Q^T for two 32-key tiles ----
     f32x16 s[2];
@@ -143,35 +178,47 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
 
     // ---- online softmax (base 2), lane-local per query plus partner lane ----
+    // Scores are kept unscaled; with c > 0 the scaled maximum is c * max.  Keys
+    // past the segment's end exist only in its last tile.
+    const int64_t lim = nkv - kv0;                     // valid keys in this tile (> 0)
+    if (lim < kBN) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3) >= lim) s[kt][i] = -INFINITY;
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t key = kv0 + kt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        const float t = key < nkv ? s[kt][i] * a.c : -INFINITY;
-        s[kt][i] = t;
-        mt = fmaxf(mt, t);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);
-    const float corr = __builtin_amdgcn_exp2f(m - mn);
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kt][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.c;
+    // The reference m is raised only when a score exceeds it by more than 2^8
+    // (decided for the whole wavefront, so the rescale is skipped together);
+    // below that the probabilities exp2(c s - m) stay under 256, which fp32
+    // sums and the bf16 probabilities carry without loss of relative precision.
+    if (__builtin_amdgcn_ballot_w64(mt > m + 8.0f)) {
+      const float mn = fmaxf(m, mt);
+      const float corr = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      l *= corr;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
+    }
     float ls = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kt][i] - mn);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], a.c, -m));
         s[kt][i] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 32, 64);
-    l = l * corr + ls;
-    m = mn;
-#pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
+    l += ls;
 
     // ---- P^T as B operands: key step ks takes accumulator entries 8 (ks & 1) .. +8 of
     // tile ks >> 1, i.e. keys 32 (ks>>1) + 16 (ks&1) + 8 (e>>2) + 4 hf + (e&3) ----
@@ -223,17 +270,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
 }  // namespace
 
-dp_status launch_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
-                           int64_t kv_cap, const int64_t* n_kv, int32_t n_heads, float scale,
-                           hipStream_t s) {
-  AttnArgs a;
+namespace {
+
+dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_heads, float scale,
+                 hipStream_t s) {
   a.q = reinterpret_cast<const uint16_t*>(q);
-  a.k = reinterpret_cast<const uint16_t*>(k);
-  a.v = reinterpret_cast<const uint16_t*>(v);
   a.o = reinterpret_cast<uint16_t*>(o);
-  a.n_kv = n_kv;
   a.n_q = n_q;
-  a.kv_cap = kv_cap;
   a.row = (int64_t)n_heads * kD;
   a.n_heads = n_heads;
   a.n_qt = (int32_t)((n_q + kBM - 1) / kBM);
@@ -243,6 +286,34 @@ dp_status launch_attention(const void* q, const void* k, const void* v, void* o,
   if (blocks == 0) return DP_OK;
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
   return check_launch("attn_fwd_kernel");
+}
+
+}  // namespace
+
+dp_status launch_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
+                           int64_t kv_cap, const int64_t* n_kv, int32_t n_heads, float scale,
+                           hipStream_t s) {
+  AttnArgs a{};
+  a.k0 = reinterpret_cast<const uint16_t*>(k);
+  a.v0 = reinterpret_cast<const uint16_t*>(v);
+  a.n_kv = n_kv;
+  a.cap0 = kv_cap;
+  return launch(a, q, o, n_q, n_heads, scale, s);
+}
+
+dp_status launch_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
+                              int64_t ragged_capacity, const int64_t* head_offsets,
+                              const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
+                              int64_t n_q, int32_t n_heads, float scale, hipStream_t s) {
+  AttnArgs a{};
+  a.k0 = reinterpret_cast<const uint16_t*>(k_ragged);
+  a.v0 = reinterpret_cast<const uint16_t*>(v_ragged);
+  a.off = head_offsets;
+  a.cap0 = ragged_capacity;
+  a.k1 = reinterpret_cast<const uint16_t*>(k_chunk);
+  a.v1 = reinterpret_cast<const uint16_t*>(v_chunk);
+  a.n1 = k_chunk ? n_chunk : 0;
+  return launch(a, q, o, n_q, n_heads, scale, s);
 }
 
 }  // namespace dp

@@ -173,6 +173,10 @@ dp_status launch_append(const dp_kv_inplace& kv, int64_t slot_begin, int64_t slo
 dp_status launch_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
                            int64_t kv_cap, const int64_t* n_kv, int32_t n_heads, float scale,
                            hipStream_t s);
+dp_status launch_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
+                              int64_t ragged_capacity, const int64_t* head_offsets,
+                              const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
+                              int64_t n_q, int32_t n_heads, float scale, hipStream_t s);
 dp_status launch_hs_offsets(const uint8_t* head_class, int32_t L, int32_t H,
                             const int64_t* class_len, int32_t n_classes, int64_t* offsets,
                             hipStream_t s);

@@ -356,13 +356,33 @@ dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layer
  * kv_capacity); n = 0 gives zeros.  q, o: [n_q][n_heads][head_dim];
  * k, v: [kv_capacity][n_heads][head_dim] (one layer of the cache, e.g. the
  * ring layout's rows [0, tail) including the chunk itself); all bf16, 16-byte
- * aligned, o not overlapping the inputs.  fp32 accumulation and softmax;
- * head_dim 128 and bf16 only (DP_EUNSUPPORTED otherwise).  No mask: every
- * query sees every cached row.  One launch.
+ * aligned, o not overlapping the inputs.  scale > 0 and finite (DP_EINVAL
+ * otherwise).  fp32 accumulation and softmax; head_dim 128 and bf16 only
+ * (DP_EUNSUPPORTED otherwise).  No mask: every query sees every cached row.
+ * One launch.
  * ------------------------------------------------------------------------- */
 dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
                        int64_t kv_capacity, const int64_t* n_kv, int32_t n_heads,
                        int32_t head_dim, int32_t dtype, float scale, void* stream);
+
+/* dp_hs_attention: the same attention over the ragged DeCoPrune-HS cache
+ *   [DeCoPrune page, 무엇인가 (DeCoPrune-HS: static heads see only the sink
+ *   and the recent window, dynamic heads the pruned history)].  Head h of
+ *   layer `layer` sees its own run of the packed per-head cache,
+ *     k_ragged[offsets[layer*n_heads + h] + j][:],  j < n_{layer,h}
+ *   (offsets as written by dp_hs_offsets, device int64, at least
+ *   (layer+1)*n_heads + 1 entries; runs are clamped to [0, ragged_capacity)
+ *   head rows, so no row outside k_ragged is read), followed by the n_chunk
+ *   rows of an optional dense block k_chunk, v_chunk [n_chunk][n_heads][head_dim]
+ *   (the chunk's own keys; both NULL for none).  q, o: [n_q][n_heads][head_dim].
+ *   bf16, head_dim 128 (DP_EUNSUPPORTED otherwise); scale as for dp_attention;
+ *   fp32 accumulation and softmax; a head with no rows gives zeros.  One launch.
+ * ------------------------------------------------------------------------- */
+dp_status dp_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
+                          int64_t ragged_capacity, const int64_t* offsets, int32_t layer,
+                          const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
+                          int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
+                          float scale, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * 6. Pruning ratio             [DeCoPrune page, 어떻게 쓰나 and 전제와 한계]

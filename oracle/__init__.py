@@ -245,6 +245,32 @@ def attention(q, k, v, rows, n_kv=None, scale=None):
     return out
 
 
+def hs_attention(q, k_ragged, v_ragged, offsets, layer, rows, k_chunk=None, v_chunk=None,
+                 scale=None):
+    """Attention over the ragged DeCoPrune-HS cache [DeCoPrune page, 무엇인가
+    (DeCoPrune-HS)]: head h of ``layer`` attends to its own run
+    k_ragged[offsets[layer*H + h] : offsets[layer*H + h + 1]] ([head rows, D])
+    followed by the dense chunk rows k_chunk[:, h] ([n_chunk, H, D], optional).
+    Evaluated head by head with ``attention``; a head with no rows gives zeros.
+    Returns float64 [len(rows), H, D]."""
+    q = np.ascontiguousarray(q)
+    H, D = q.shape[1], q.shape[2]
+    off = np.asarray(offsets, np.int64)
+    rows = np.asarray(rows, np.int64)
+    out = np.zeros((rows.shape[0], H, D), np.float64)
+    for h in range(H):
+        lo, hi = int(off[layer * H + h]), int(off[layer * H + h + 1])
+        kh, vh = k_ragged[lo:hi], v_ragged[lo:hi]
+        if k_chunk is not None:
+            kh = np.concatenate([kh, k_chunk[:, h]])
+            vh = np.concatenate([vh, v_chunk[:, h]])
+        if kh.shape[0] == 0:
+            continue
+        out[:, h] = attention(np.ascontiguousarray(q[:, h:h + 1]), kh[:, None], vh[:, None],
+                              rows, scale=scale)[:, 0]
+    return out
+
+
 def pr(visible, full):
     """Pruning ratio 1 - visible/full [DeCoPrune page, 어떻게 쓰나]."""
     return lib().oracle_pr(int(visible), int(full))

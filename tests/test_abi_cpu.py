@@ -24,7 +24,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     lib = ctypes.CDLL(dp.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -263,3 +263,39 @@ def test_rope_prepare_and_apply_reject():
     assert f(FAKE, 1, 4, 64, 1, 0, 100, FAKE + 4, FAKE, ctypes.byref(r), FAKE, nb, None) == dp.DP_EALIGN
     # an empty range is accepted without any launch
     assert f(FAKE, 1, 4, 64, 1, 50, 50, None, FAKE, ctypes.byref(r), FAKE, nb, None) == dp.DP_OK
+
+
+def test_attention_rejects():
+    B = dp.DP_BF16
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("q", FAKE), ("k", FAKE), ("v", FAKE), ("o", FAKE), ("n_q", 100), ("cap", 100),
+        ("n_kv", None), ("H", 8), ("D", 128), ("dtype", B), ("scale", 0.1), ("s", None))]
+    assert _status("attention", *args(q=None)) == dp.DP_EINVAL
+    assert _status("attention", *args(D=64)) == dp.DP_EUNSUPPORTED
+    assert _status("attention", *args(dtype=dp.DP_F32)) == dp.DP_EUNSUPPORTED
+    assert _status("attention", *args(H=0)) == dp.DP_ERANGE
+    assert _status("attention", *args(cap=-1)) == dp.DP_ERANGE
+    assert _status("attention", *args(n_q=1 << 31)) == dp.DP_ERANGE
+    assert _status("attention", *args(k=FAKE + 8)) == dp.DP_EALIGN
+    assert _status("attention", *args(n_kv=FAKE + 4)) == dp.DP_EALIGN
+    for bad in (float("nan"), 0.0, -0.5, float("inf")):
+        assert _status("attention", *args(scale=bad)) == dp.DP_EINVAL
+
+
+def test_hs_attention_rejects():
+    B = dp.DP_BF16
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("q", FAKE), ("kr", FAKE), ("vr", FAKE), ("cap", 1000), ("off", FAKE), ("layer", 3),
+        ("kc", FAKE), ("vc", FAKE), ("nc", 50), ("o", FAKE), ("n_q", 100), ("H", 8), ("D", 128),
+        ("dtype", B), ("scale", 0.1), ("s", None))]
+    assert _status("hs_attention", *args(off=None)) == dp.DP_EINVAL
+    assert _status("hs_attention", *args(vc=None)) == dp.DP_EINVAL       # chunk K without V
+    assert _status("hs_attention", *args(D=96)) == dp.DP_EUNSUPPORTED
+    assert _status("hs_attention", *args(layer=-1)) == dp.DP_ERANGE
+    assert _status("hs_attention", *args(cap=1 << 40)) == dp.DP_ERANGE
+    assert _status("hs_attention", *args(nc=-1)) == dp.DP_ERANGE
+    assert _status("hs_attention", *args(layer=1 << 30)) == dp.DP_ERANGE
+    assert _status("hs_attention", *args(off=FAKE + 4)) == dp.DP_EALIGN
+    assert _status("hs_attention", *args(kc=FAKE + 2)) == dp.DP_EALIGN
+    for bad in (float("nan"), 0.0, -0.5, float("inf")):
+        assert _status("hs_attention", *args(scale=bad)) == dp.DP_EINVAL

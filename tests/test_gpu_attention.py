@@ -104,3 +104,115 @@ def test_attention_eviction_shape_sampled():
     err = _check(got, want, "eviction shape")
     print("eviction-shape attention: max |err| %.2e over %d sampled queries x %d heads"
           % (err, len(rows), H))
+
+
+def _ragged_case(rng, lens, H, D, pad):
+    off = np.concatenate([[0], np.cumsum(np.asarray(lens, np.int64).ravel())]).astype(np.int64)
+    kr = random_bf16_bits(rng, (int(off[-1]) + pad, D))
+    vr = random_bf16_bits(rng, (int(off[-1]) + pad, D))
+    return off, kr, vr
+
+
+@pytest.mark.parametrize("H", [5, 8])
+@pytest.mark.parametrize("n_chunk", [0, 1, 70])
+@pytest.mark.parametrize("layer", [0, 1])
+def test_hs_attention_matches_oracle(H, n_chunk, layer):
+    """Ragged per-head runs of awkward lengths (empty, one row, around a tile),
+    optionally followed by the chunk's dense rows; rows beyond the capacity
+    hold NaN and are never read."""
+    dev = device()
+    rng = np.random.default_rng(100 * H + 10 * n_chunk + layer)
+    D, n_q = 128, 133
+    base = [0, 1, 63, 64, 65, 200, 7, 129]
+    lens = np.array([[base[(h + l) % 8] for h in range(H)] for l in range(2)], np.int64)
+    pad = 40
+    off, kr, vr = _ragged_case(rng, lens, H, D, pad)
+    cap = int(off[-1])
+    kr[cap:] = 0x7FC0
+    vr[cap:] = 0x7FC0
+    q = random_bf16_bits(rng, (n_q, H, D))
+    kc = random_bf16_bits(rng, (max(n_chunk, 1), H, D))
+    vc = random_bf16_bits(rng, (max(n_chunk, 1), H, D))
+    od = torch.zeros((n_q, H, D), dtype=torch.bfloat16, device=dev)
+    scale = 1.0 / np.sqrt(D)
+    kcd = bf16_from_bits(kc, dev) if n_chunk else None
+    vcd = bf16_from_bits(vc, dev) if n_chunk else None
+    dp.dp_hs_attention(bf16_from_bits(q, dev), bf16_from_bits(kr, dev), bf16_from_bits(vr, dev),
+                       cap, torch.from_numpy(off).to(dev), layer, kcd, vcd, n_chunk, od, n_q, H, D,
+                       dp.DP_BF16, scale)
+    torch.cuda.synchronize()
+    want = oracle.hs_attention(q, kr, vr, off, layer, np.arange(n_q),
+                               kc[:n_chunk] if n_chunk else None,
+                               vc[:n_chunk] if n_chunk else None, scale=scale)
+    err = _check(bits(od), want, ("hs", H, n_chunk, layer))
+    print("hs attention H=%d chunk=%d layer=%d: max |err| %.2e" % (H, n_chunk, layer, err))
+
+
+def test_hs_attention_clamps_runs_to_capacity():
+    """Offsets past the capacity are clamped: the last heads see fewer rows."""
+    dev = device()
+    rng = np.random.default_rng(7)
+    H, D, n_q = 8, 128, 40
+    lens = np.array([[30, 10, 50, 20, 64, 1, 0, 90]], np.int64)
+    off, kr, vr = _ragged_case(rng, lens, H, D, 0)
+    cap = int(off[-1]) - 100                                 # cuts the last run and part of the one before
+    q = random_bf16_bits(rng, (n_q, H, D))
+    od = torch.zeros((n_q, H, D), dtype=torch.bfloat16, device=dev)
+    dp.dp_hs_attention(bf16_from_bits(q, dev), bf16_from_bits(kr, dev), bf16_from_bits(vr, dev),
+                       cap, torch.from_numpy(off).to(dev), 0, None, None, 0, od, n_q, H, D,
+                       dp.DP_BF16, 0.1)
+    torch.cuda.synchronize()
+    want = oracle.hs_attention(q, kr, vr, np.minimum(off, cap), 0, np.arange(n_q), scale=0.1)
+    _check(bits(od), want, "clamp")
+
+
+def test_hs_attention_hs_shape_sampled():
+    """DeCoPrune-HS shape: 40 heads x 128, per-head runs with the class
+    lengths of the 30-chunk HS workload (static heads: sink + window,
+    dynamic heads: the gamma mask), layer 1 of a two-layer packed cache,
+    followed by the 6,240 chunk rows.  Every head runs; seven queries of six
+    heads (static and dynamic) are checked."""
+    dev = device()
+    w = dpsynth.WORKLOADS["hs"]
+    T, H, D = w.seq_len, w.n_heads, w.head_dim
+    x0, xf = dpsynth.score_inputs(w)
+    ell = oracle.score_f32(x0, xf, w.d)
+    n_s = int(oracle.mask(None, T, w.sink_len, w.window_len, w.scored_begin, w.n_scored,
+                          w.gamma, streaming=True).sum())
+    n_d = int(oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin, w.n_scored,
+                          w.gamma).sum())
+    cls = dpsynth.hs_head_class(w)[:2]
+    off = oracle.hs_offsets(cls, np.array([n_s, n_d], np.int64))
+    total, n_q = int(off[-1]), w.chunk_tokens
+    kr = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    vr = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    dpsynth.kv_fill_device(kr, "bf16", 5, dpsynth.STREAM_K, 0, total, D)
+    dpsynth.kv_fill_device(vr, "bf16", 5, dpsynth.STREAM_V, 0, total, D)
+    q = torch.empty((n_q, H, D), dtype=torch.bfloat16, device=dev)
+    kc = torch.empty((n_q, H, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty((n_q, H, D), dtype=torch.bfloat16, device=dev)
+    dpsynth.kv_fill_device(q, "bf16", 6, 3, 0, n_q, H * D)
+    dpsynth.kv_fill_device(kc, "bf16", 6, dpsynth.STREAM_K, 0, n_q, H * D)
+    dpsynth.kv_fill_device(vc, "bf16", 6, dpsynth.STREAM_V, 0, n_q, H * D)
+    o = torch.empty_like(q)
+    dp.dp_hs_attention(q, kr, vr, total, torch.from_numpy(off).to(dev), 1, kc, vc, n_q, o, n_q,
+                       H, D, dp.DP_BF16, 1.0 / np.sqrt(D))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 3000, 6111, 6239])
+    static = np.flatnonzero(cls[1] == 0)[:3]
+    dynamic = np.flatnonzero(cls[1] == 1)[:3]
+    heads = np.concatenate([static, dynamic])
+    # the checked heads' runs, re-packed on the host, and their chunk columns
+    runs = [np.arange(off[H + h], off[H + h + 1]) for h in heads]
+    sub_off = np.concatenate([[0], np.cumsum([r.shape[0] for r in runs])]).astype(np.int64)
+    all_rows = np.concatenate(runs)
+    krh = dpsynth.kv_rows_host("bf16", 5, dpsynth.STREAM_K, 0, all_rows, total, D)
+    vrh = dpsynth.kv_rows_host("bf16", 5, dpsynth.STREAM_V, 0, all_rows, total, D)
+    kch = dpsynth.kv_layer_host("bf16", 6, dpsynth.STREAM_K, 0, n_q, H * D).reshape(n_q, H, D)
+    vch = dpsynth.kv_layer_host("bf16", 6, dpsynth.STREAM_V, 0, n_q, H * D).reshape(n_q, H, D)
+    qh = np.zeros((n_q, len(heads), D), np.uint16)
+    qh[rows] = dpsynth.kv_rows_host("bf16", 6, 3, 0, rows, n_q, H * D).reshape(len(rows), H, D)[:, heads]
+    want = oracle.hs_attention(qh, krh, vrh, sub_off, 0, rows, kch[:, heads], vch[:, heads])
+    got = bits(o[torch.from_numpy(rows).to(dev)])[:, heads]
+    err = _check(got, want, "hs shape")
+    print("hs-shape attention: runs %d / %d rows, max |err| %.2e" % (n_s, n_d, err))

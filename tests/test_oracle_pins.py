@@ -400,6 +400,54 @@ def test_attention_closed_forms():
     assert np.allclose(got[0], _f(v)[5], atol=1e-9)
 
 
+def test_hs_attention_per_head_runs_against_numpy():
+    """Each head of the chosen layer sees exactly its own run followed by the
+    chunk rows; a head with no rows gives zeros (numpy float64 softmax)."""
+    rng = np.random.default_rng(18)
+    L, H, D, nq, nc = 2, 4, 16, 5, 9
+    lens = np.array([[3, 0, 7, 1], [0, 12, 5, 64]], np.int64)        # per (layer, head)
+    off = np.concatenate([[0], np.cumsum(lens.ravel())]).astype(np.int64)
+    kr, vr = _bf16(rng, (off[-1], D)), _bf16(rng, (off[-1], D))
+    kc, vc = _bf16(rng, (nc, H, D)), _bf16(rng, (nc, H, D))
+    q = _bf16(rng, (nq, H, D))
+    rows = np.array([0, 2, 4])
+    for layer in range(L):
+        for chunk in (False, True):
+            got = oracle.hs_attention(q, kr, vr, off, layer, rows, kc if chunk else None,
+                                      vc if chunk else None, scale=0.3)
+            for h in range(H):
+                lo, hi = off[layer * H + h], off[layer * H + h + 1]
+                kh, vh = _f(kr[lo:hi]), _f(vr[lo:hi])
+                if chunk:
+                    kh, vh = np.concatenate([kh, _f(kc[:, h])]), np.concatenate([vh, _f(vc[:, h])])
+                for a, i in enumerate(rows):
+                    if kh.shape[0] == 0:
+                        assert np.all(got[a, h] == 0)
+                        continue
+                    sc = kh @ _f(q[i, h]) * 0.3
+                    p = np.exp(sc - sc.max())
+                    assert np.allclose(got[a, h], (p / p.sum()) @ vh, rtol=1e-12, atol=1e-13)
+
+
+def test_hs_attention_with_shared_runs_equals_dense_attention():
+    """When every head's run lists the same cache rows, the ragged attention
+    is the dense attention over those rows followed by the chunk."""
+    rng = np.random.default_rng(19)
+    T, H, D, nq = 40, 3, 16, 6
+    k, v = _bf16(rng, (T, H, D)), _bf16(rng, (T, H, D))
+    q = _bf16(rng, (nq, H, D))
+    keep = np.flatnonzero(rng.random(T) < 0.5)
+    n = keep.shape[0]
+    kr = np.concatenate([k[keep, h] for h in range(H)])             # head-major runs
+    vr = np.concatenate([v[keep, h] for h in range(H)])
+    off = np.arange(H + 1, dtype=np.int64) * n
+    kc, vc = k[-4:], v[-4:]
+    got = oracle.hs_attention(q, kr, vr, off, 0, np.arange(nq), kc, vc)
+    want = oracle.attention(q, np.concatenate([k[keep], kc]), np.concatenate([v[keep], vc]),
+                            np.arange(nq))
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-15)
+
+
 # --------------------------------------------------------------------------
 # Pruning ratio
 # --------------------------------------------------------------------------

@@ -121,29 +121,31 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
   float m = -INFINITY, l = 0.0f;
 
-  // Each thread moves 4 consecutive keys of one 8-element chunk: K rows go to
-  // LDS as 16-byte writes, V is transposed in registers and written as four
-  // keys per 8-byte write.  The next tile's loads are issued before the current
-  // tile's MFMAs so that their latency is hidden.
-  const int key4 = (threadIdx.x >> 4) * 4, ch = threadIdx.x & 15;
+  // Each thread moves 4 consecutive keys of one 8-element chunk of K and of V.
+  // K rows go to LDS as 16-byte writes (the 16 lanes of a key cover its row);
+  // V is transposed in registers and written as four keys per 8-byte write,
+  // with the keys varying fastest across lanes so that the lanes of a write
+  // fall in distinct banks.  The next tile's loads are issued before the
+  // current tile's MFMAs so that their latency is hidden.
+  const int key4 = (threadIdx.x >> 4) * 4, ch = threadIdx.x & 15;        // K
+  const int vkey4 = (threadIdx.x & 15) * 4, vch = threadIdx.x >> 4;      // V
   u32x4 kr[4], vr[4];
   auto load_tile = [&](int64_t t) {
     const bool s1 = t >= t0;                       // uniform per workgroup
     const uint16_t* kp = s1 ? a.k1 : a.k0;
     const uint16_t* vp = s1 ? a.v1 : a.v0;
     const int64_t stride = s1 ? a.row : stride0;
-    const int64_t base = (s1 ? (int64_t)head * kD : base0) + ch * 8;
+    const int64_t base = s1 ? (int64_t)head * kD : base0;
     const int64_t n = s1 ? n1 : n0;
     const int64_t kv0 = (s1 ? t - t0 : t) * kBN;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       kr[u] = u32x4{0u, 0u, 0u, 0u};
       vr[u] = u32x4{0u, 0u, 0u, 0u};
-      if (kv0 + key4 + u < n) {
-        const int64_t off = base + (kv0 + key4 + u) * stride;
-        kr[u] = *reinterpret_cast<const u32x4*>(kp + off);
-        vr[u] = *reinterpret_cast<const u32x4*>(vp + off);
-      }
+      if (kv0 + key4 + u < n)
+        kr[u] = *reinterpret_cast<const u32x4*>(kp + base + ch * 8 + (kv0 + key4 + u) * stride);
+      if (kv0 + vkey4 + u < n)
+        vr[u] = *reinterpret_cast<const u32x4*>(vp + base + vch * 8 + (kv0 + vkey4 + u) * stride);
     }
   };
   if (n_tiles > 0) load_tile(0);
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       u32x2 w;
       w[0] = ((vr[0][e >> 1] >> sh) & 0xFFFFu) | (((vr[1][e >> 1] >> sh) & 0xFFFFu) << 16);
       w[1] = ((vr[2][e >> 1] >> sh) & 0xFFFFu) | (((vr[3][e >> 1] >> sh) & 0xFFFFu) << 16);
-      *reinterpret_cast<u32x2*>(Vt + (ch * 8 + e) * kVP + key4) = w;
+      *reinterpret_cast<u32x2*>(Vt + (vch * 8 + e) * kVP + vkey4) = w;
     }
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(t + 1);

@@ -17,6 +17,7 @@ namespace {
 thread_local char g_err[512] = "";
 constexpr int64_t kMaxRows = (int64_t)1 << 31;      // int32 row indices
 constexpr int64_t kMaxVec = (int64_t)1 << 31;       // 16-byte vectors per launch slab
+constexpr int32_t kMaxAttnHeads = 65536;           // 64 key rows of a tile addressed in 32 bits
 }  // namespace
 
 dp_status fail(dp_status s, const char* fmt, ...) {
@@ -389,8 +390,9 @@ dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int
   if (!q || !k || !v || !o) return fail(DP_EINVAL, "dp_attention: q, k, v and o are required");
   if (dtype != DP_BF16 || head_dim != 128)
     return fail(DP_EUNSUPPORTED, "dp_attention: only bf16 with head_dim 128 is implemented");
-  if (n_heads < 1 || n_q < 0 || kv_capacity < 0 || n_q >= kMaxRows || kv_capacity >= kMaxRows)
-    return fail(DP_ERANGE, "dp_attention: need n_heads >= 1 and 0 <= n_q, kv_capacity < 2^31");
+  if (n_heads < 1 || n_heads > kMaxAttnHeads || n_q < 0 || kv_capacity < 0 || n_q >= kMaxRows ||
+      kv_capacity >= kMaxRows)
+    return fail(DP_ERANGE, "dp_attention: need 1 <= n_heads <= 65536 and 0 <= n_q, kv_capacity < 2^31");
   if ((n_q + 127) / 128 * (int64_t)n_heads >= kMaxVec)
     return fail(DP_ERANGE, "dp_attention: too many query tiles for one launch");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -416,9 +418,10 @@ dp_status dp_hs_attention(const void* q, const void* k_ragged, const void* v_rag
     return fail(DP_EINVAL, "dp_hs_attention: k_chunk and v_chunk are both given or both NULL");
   if (dtype != DP_BF16 || head_dim != 128)
     return fail(DP_EUNSUPPORTED, "dp_hs_attention: only bf16 with head_dim 128 is implemented");
-  if (n_heads < 1 || layer < 0 || n_q < 0 || n_q >= kMaxRows || ragged_capacity < 0 ||
+  if (n_heads < 1 || n_heads > kMaxAttnHeads || layer < 0 || n_q < 0 || n_q >= kMaxRows ||
+      ragged_capacity < 0 ||
       ragged_capacity >= ((int64_t)1 << 40) || (k_chunk && (n_chunk < 0 || n_chunk >= kMaxRows)))
-    return fail(DP_ERANGE, "dp_hs_attention: need n_heads >= 1, layer >= 0, 0 <= n_q, n_chunk "
+    return fail(DP_ERANGE, "dp_hs_attention: need 1 <= n_heads <= 65536, layer >= 0, 0 <= n_q, n_chunk "
                            "< 2^31 and 0 <= ragged_capacity < 2^40");
   if ((int64_t)layer * n_heads >= kMaxRows)
     return fail(DP_ERANGE, "dp_hs_attention: layer * n_heads beyond the offsets range");

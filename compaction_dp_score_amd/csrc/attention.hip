@@ -38,8 +38,10 @@ constexpr int kD = 128;          // head_dim
 constexpr int kBM = 128;         // queries per workgroup
 constexpr int kBN = 64;          // keys per tile
 constexpr int kKP = kD + 8;      // K tile row pitch (bf16 elements)
-constexpr int kVP = kBN + 8;     // V^T tile row pitch (bf16 elements)
+constexpr int kVP = kBN + 4;     // V^T tile row pitch (bf16 elements): 34 dwords, so the
+                                 // 32 rows one 8-byte read spans fall in distinct banks
 constexpr int kXcds = 8;
+constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor, dword 3
 
 struct AttnArgs {
   const uint16_t* q;
@@ -64,6 +66,7 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+template <bool RAGGED>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * kKP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVP];
@@ -71,8 +74,35 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   int head, qt;
   if (a.xcd_map) {
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-    head = (slot / a.n_qt) * kXcds + xcd;
+    const int j = slot / a.n_qt;                 // j-th head placed on this XCD
     qt = slot % a.n_qt;
+    head = j * kXcds + xcd;
+    if (RAGGED && a.n_heads <= kBlock) {
+      // Ragged runs differ in length, so heads are ranked by length (longest
+      // first, ties by index) and dealt to the XCDs in snake order: every XCD
+      // gets the same number of heads and nearly the same number of keys, and
+      // the longest heads start first.
+      __shared__ int64_t len_s[kBlock];
+      __shared__ int head_of_rank[kBlock];
+      const int t = threadIdx.x;
+      if (t < a.n_heads) {
+        const int64_t lo = min(max(a.off[t], (int64_t)0), a.cap0);
+        const int64_t hi = min(max(a.off[t + 1], lo), a.cap0);
+        len_s[t] = hi - lo;
+      }
+      __syncthreads();
+      if (t < a.n_heads) {
+        const int64_t mine = len_s[t];
+        int rank = 0;
+        for (int u = 0; u < a.n_heads; ++u) {
+          const int64_t other = len_s[u];
+          rank += (other > mine) | ((other == mine) & (u < t));
+        }
+        head_of_rank[rank] = t;
+      }
+      __syncthreads();
+      head = head_of_rank[j * kXcds + ((j & 1) ? kXcds - 1 - xcd : xcd)];
+    }
   } else {
     head = blockIdx.x / a.n_qt;
     qt = blockIdx.x % a.n_qt;
@@ -81,7 +111,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // segment 0 of this head: base element, key stride, count (device values clamped
   // to the capacity, so no key outside [0, cap0) is read)
   int64_t base0, stride0, n0;
-  if (a.off) {
+  if (RAGGED) {
     const int64_t lo = min(max(a.off[head], (int64_t)0), a.cap0);
     const int64_t hi = min(max(a.off[head + 1], lo), a.cap0);
     base0 = lo * kD;
@@ -93,7 +123,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     n0 = a.cap0;
     if (a.n_kv) n0 = max(min(n0, *a.n_kv), (int64_t)0);
   }
-  const int64_t n1 = a.k1 ? a.n1 : 0;
+  const int64_t n1 = RAGGED && a.k1 ? a.n1 : 0;
   const int64_t t0 = (n0 + kBN - 1) / kBN;
   const int64_t n_tiles = t0 + (n1 + kBN - 1) / kBN;
 
@@ -130,28 +160,38 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int key4 = (threadIdx.x >> 4) * 4, ch = threadIdx.x & 15;        // K
   const int vkey4 = (threadIdx.x & 15) * 4, vch = threadIdx.x >> 4;      // V
   u32x4 kr[4], vr[4];
+  // Tile loads go through buffer descriptors whose base is the tile's first
+  // row and whose size ends at the segment's last valid row, so rows past it
+  // read as zeros without a per-lane branch (gfx9 buffer range check; the lane
+  // offsets stay below 64 rows of the segment's stride, validated on the host).
   auto load_tile = [&](int64_t t) {
-    const bool s1 = t >= t0;                       // uniform per workgroup
+    const bool s1 = RAGGED && t >= t0;             // uniform per workgroup
     const uint16_t* kp = s1 ? a.k1 : a.k0;
     const uint16_t* vp = s1 ? a.v1 : a.v0;
     const int64_t stride = s1 ? a.row : stride0;
     const int64_t base = s1 ? (int64_t)head * kD : base0;
     const int64_t n = s1 ? n1 : n0;
     const int64_t kv0 = (s1 ? t - t0 : t) * kBN;
+    const int64_t off = base + kv0 * stride;
+    const uint32_t bytes = (uint32_t)(min(n - kv0, (int64_t)kBN) * stride * 2);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kp + off), 0, (int)bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vp + off), 0, (int)bytes, kBufferWord3);
+    const uint32_t st2 = (uint32_t)stride * 2u;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      kr[u] = u32x4{0u, 0u, 0u, 0u};
-      vr[u] = u32x4{0u, 0u, 0u, 0u};
-      if (kv0 + key4 + u < n)
-        kr[u] = *reinterpret_cast<const u32x4*>(kp + base + ch * 8 + (kv0 + key4 + u) * stride);
-      if (kv0 + vkey4 + u < n)
-        vr[u] = *reinterpret_cast<const u32x4*>(vp + base + vch * 8 + (kv0 + vkey4 + u) * stride);
+      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rk, (int)((key4 + u) * st2 + ch * 16), 0, 0));
+      vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rv, (int)((vkey4 + u) * st2 + vch * 16), 0, 0));
     }
   };
   if (n_tiles > 0) load_tile(0);
   for (int64_t t = 0; t < n_tiles; ++t) {
-    const int64_t kv0 = (t >= t0 ? t - t0 : t) * kBN;   // first key of the tile in its segment
-    const int64_t nkv = t >= t0 ? n1 : n0;
+    const bool in1 = RAGGED && t >= t0;
+    const int64_t kv0 = (in1 ? t - t0 : t) * kBN;   // first key of the tile in its segment
+    const int64_t nkv = in1 ? n1 : n0;
     // ---- stage K (row-major) and V (transposed) of 64 keys in LDS ----
 #pragma unroll
     for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(Ks + (key4 + u) * kKP + ch * 8) = kr[u];
@@ -286,7 +326,10 @@ dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_hea
   a.c = scale * 1.4426950408889634f;
   const uint64_t blocks = (uint64_t)a.n_qt * n_heads;
   if (blocks == 0) return DP_OK;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+  if (a.off)
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
   return check_launch("attn_fwd_kernel");
 }
 

@@ -356,10 +356,10 @@ dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layer
  * kv_capacity); n = 0 gives zeros.  q, o: [n_q][n_heads][head_dim];
  * k, v: [kv_capacity][n_heads][head_dim] (one layer of the cache, e.g. the
  * ring layout's rows [0, tail) including the chunk itself); all bf16, 16-byte
- * aligned, o not overlapping the inputs.  scale > 0 and finite (DP_EINVAL
- * otherwise).  fp32 accumulation and softmax; head_dim 128 and bf16 only
- * (DP_EUNSUPPORTED otherwise).  No mask: every query sees every cached row.
- * One launch.
+ * aligned, o not overlapping the inputs; 1 <= n_heads <= 65536 (DP_ERANGE);
+ * scale > 0 and finite (DP_EINVAL otherwise).  fp32 accumulation and softmax;
+ * head_dim 128 and bf16 only (DP_EUNSUPPORTED otherwise).  No mask: every
+ * query sees every cached row.  One launch.
  * ------------------------------------------------------------------------- */
 dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
                        int64_t kv_capacity, const int64_t* n_kv, int32_t n_heads,

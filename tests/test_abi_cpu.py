@@ -274,6 +274,7 @@ def test_attention_rejects():
     assert _status("attention", *args(D=64)) == dp.DP_EUNSUPPORTED
     assert _status("attention", *args(dtype=dp.DP_F32)) == dp.DP_EUNSUPPORTED
     assert _status("attention", *args(H=0)) == dp.DP_ERANGE
+    assert _status("attention", *args(H=65537)) == dp.DP_ERANGE
     assert _status("attention", *args(cap=-1)) == dp.DP_ERANGE
     assert _status("attention", *args(n_q=1 << 31)) == dp.DP_ERANGE
     assert _status("attention", *args(k=FAKE + 8)) == dp.DP_EALIGN
@@ -292,6 +293,7 @@ def test_hs_attention_rejects():
     assert _status("hs_attention", *args(vc=None)) == dp.DP_EINVAL       # chunk K without V
     assert _status("hs_attention", *args(D=96)) == dp.DP_EUNSUPPORTED
     assert _status("hs_attention", *args(layer=-1)) == dp.DP_ERANGE
+    assert _status("hs_attention", *args(H=65537)) == dp.DP_ERANGE
     assert _status("hs_attention", *args(cap=1 << 40)) == dp.DP_ERANGE
     assert _status("hs_attention", *args(nc=-1)) == dp.DP_ERANGE
     assert _status("hs_attention", *args(layer=1 << 30)) == dp.DP_ERANGE

@@ -6,7 +6,8 @@ frames per chunk, gamma = 0.10): 40 layers x 40 heads x head_dim 128 bf16
 K and V, 5 chunks of 6,240 tokens (sink + the chunk leaving the window + a
 3-chunk window), d = 64 score channels.  One step enqueues
 
-  dp_score_mask -> dp_compact_index -> dp_gather_kv (fused RoPE re-index)
+  dp_score_index (score, mask and kept-index list in one launch)
+    -> dp_gather_kv (fused RoPE re-index)
 
 over all 40 layers, K and V, with every input resident in HBM.  The frame
 phase table is restored before each step so every step re-indexes from the
@@ -14,12 +15,15 @@ same state (a 20-float device copy).
 
 Printed: one JSON line with the step's algorithmic HBM bytes per second, the
 tokens scored per second, a roofline record of the dominant kernel (the
-gather) timed with HIP events on its stream, and the CPU oracle timed on a
-bounded layer sample of the same workload on the host cores.
+gather) timed with HIP events on its stream, the index phase timed both as
+one launch and as dp_score_mask + dp_compact_index, and the CPU oracle timed
+on a bounded layer sample of the same workload on the host cores.
 
-Other workloads (--workload reindex | prefix | hs | append) time the other
-shapes; "append" is the same eviction step in the ring layout, where only the
-leaving chunk's kept rows move and the old keys are re-indexed in place.
+Other workloads (--workload reindex | prefix | hs | append | attention |
+hs_attention) time the other shapes; "append" is the same eviction step in the
+ring layout, where only the leaving chunk's kept rows move and the old keys
+are re-indexed in place; the attention workloads time the next chunk's
+attention over the compacted (or ragged HS) cache in TFLOP/s.
 """
 import argparse
 import json
@@ -125,6 +129,34 @@ class Timer:
 # --------------------------------------------------------------------------
 # workloads
 # --------------------------------------------------------------------------
+def index_compare(step, x0d, xfd, d, reps=20):
+    """Time the index phase both ways on the step's buffers (outside the timed
+    steps): dp_score_index (one launch) and dp_score_mask + dp_compact_index
+    (four launches).  Returns mean microseconds per call of each."""
+    import compaction_dp_score_amd as dp
+
+    def fused():
+        dp.dp_score_index(x0d, xfd, d, d, step.policy, None, step.keep, step.idx, step.n_kept,
+                          step.row_frame_src, step.row_frame_dst, step.ws_index, step.dev_error)
+
+    def separate():
+        dp.dp_score_mask(x0d, xfd, d, d, step.policy, None, step.keep)
+        dp.dp_compact_index(step.keep, step.seq_len, step.idx, step.n_kept, step.row_frame_src,
+                            step.row_frame_dst, step.ws_compact)
+
+    out = {}
+    for name, fn in (("fused_us", fused), ("separate_us", separate)):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = round(a.elapsed_time(b) * 1e3 / reps, 2)
+    return out
+
+
 def setup_eviction(dev):
     import compaction_dp_score_amd as dp
     import dpsynth
@@ -160,12 +192,11 @@ def setup_eviction(dev):
         rope["frame_phase"].copy_(phase0)
         if timed:
             st.start()
-        dp.dp_score_mask(x0d, xfd, w.d, w.d, step.policy, step.ell, step.keep)
+        dp.dp_score_index(x0d, xfd, w.d, w.d, step.policy, step.ell, step.keep, step.idx,
+                          step.n_kept, step.row_frame_src, step.row_frame_dst, step.ws_index,
+                          step.dev_error)
         if timed:
             st.stop()
-        dp.dp_compact_index(step.keep, T, step.idx, step.n_kept, step.row_frame_src,
-                            step.row_frame_dst, step.ws_compact)
-        if timed:
             gt.start()
         dp.dp_gather_kv(step.kv, step.idx, step.n_kept, step.row_frame_dst, step.rope,
                         step.ws_rope)
@@ -174,12 +205,13 @@ def setup_eviction(dev):
 
     def accounting():
         n = int(step.n_kept.item())
+        assert int(step.dev_error.item()) == 0
         row = H * D * 2
         gather = n * row * 2 * 2 * L
-        score = w.n_scored * (8 * w.d) + T
-        index = 2 * T + 4 * n + 8 * n
-        return dict(n_kept=n, gather_bytes=gather, score_timer=st, score_bytes_per_token=8 * w.d + 1,
-                    step_bytes=gather + score + index, n_scored=w.n_scored,
+        index = w.n_scored * (8 * w.d) + T + 12 * n        # scores in, keep out, idx + frames
+        return dict(n_kept=n, gather_bytes=gather, score_timer=st, index_bytes=index,
+                    index_compare=index_compare(step, x0d, xfd, w.d),
+                    step_bytes=gather + index, n_scored=w.n_scored,
                     config={"workload": "eviction", "layers": L, "heads": H, "head_dim": D,
                             "kv_dtype": "bf16", "tokens": T, "chunk_tokens": w.chunk_tokens,
                             "sink_chunks": w.sink_chunks, "window_chunks": w.window_chunks,
@@ -661,11 +693,10 @@ def setup_prefix(dev, slab_layers=20):
     def run(timed):
         if timed:
             st.start()
-        dp.dp_score_mask(x0d, xfd, w.d, w.d, step.policy, None, step.keep)
+        dp.dp_score_index(x0d, xfd, w.d, w.d, step.policy, None, step.keep, step.idx,
+                          step.n_kept, None, None, step.ws_index, step.dev_error)
         if timed:
             st.stop()
-        dp.dp_compact_index(step.keep, T, step.idx, step.n_kept, None, None, step.ws_compact)
-        if timed:
             gt.start()
         dp.dp_gather_kv(step.kv, step.idx, step.n_kept)
         if timed:
@@ -673,11 +704,12 @@ def setup_prefix(dev, slab_layers=20):
 
     def accounting():
         n = int(step.n_kept.item())
+        assert int(step.dev_error.item()) == 0
         gather = n * H * D * 2 * 2 * 2 * slab_layers
-        score = w.n_scored * 8 * w.d + T
-        index = 2 * T + 4 * n
-        return dict(n_kept=n, gather_bytes=gather, step_bytes=gather + score + index,
-                    n_scored=w.n_scored, score_timer=st, score_bytes_per_token=8 * w.d + 1,
+        index = w.n_scored * 8 * w.d + T + 4 * n            # scores in, keep out, idx out
+        return dict(n_kept=n, gather_bytes=gather, step_bytes=gather + index,
+                    n_scored=w.n_scored, score_timer=st, index_bytes=index,
+                    index_compare=index_compare(step, x0d, xfd, w.d),
                     config={"workload": "prefix", "layers_in_slab": slab_layers, "layers": 40,
                             "heads": H, "head_dim": D, "kv_dtype": "bf16", "tokens": T,
                             "scored_tokens": w.n_scored, "d": w.d, "gamma": w.gamma,
@@ -871,10 +903,12 @@ def main():
         s_ms = acc["score_timer"].mean_ms()
         tps = acc["n_scored"] / (s_ms * 1e-3)
         rec["tokens_scored_per_s"] = round(tps, 1)
-        rec["score_kernel"] = {
-            "ms": round(s_ms, 5), "tokens": acc["n_scored"],
-            "roofline_tokens_per_s": round(HBM_PEAK_GBS * 1e9 / acc["score_bytes_per_token"], 1),
-            "frac": round(tps * acc["score_bytes_per_token"] / (HBM_PEAK_GBS * 1e9), 4)}
+        ibytes = acc["index_bytes"]
+        rec["score_index_kernel"] = {
+            "ms": round(s_ms, 5), "tokens_scored": acc["n_scored"], "bytes": ibytes,
+            "gbs": round(ibytes / (s_ms * 1e-3) / 1e9, 2),
+            "frac": round(ibytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            **acc.get("index_compare", {})}
     if acc.get("append_timer") is not None:
         a_ms = acc["append_timer"].mean_ms()
         rec["append_kernel"] = {"ms": round(a_ms, 5), "bytes": acc["append_bytes"],

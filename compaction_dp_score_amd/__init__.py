@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-DP_OK, DP_EINVAL, DP_EALIGN, DP_ERANGE, DP_ECAPACITY, DP_EHIP, DP_EUNSUPPORTED = range(7)
+DP_OK, DP_EINVAL, DP_EALIGN, DP_ERANGE, DP_ECAPACITY, DP_EHIP, DP_EUNSUPPORTED, DP_ESTALL = range(8)
 DP_F32, DP_BF16 = 0, 1
 DP_MODE_SCORE, DP_MODE_STREAMING = 0, 1
 DP_HS_MAX_CLASSES = 8
@@ -101,6 +101,9 @@ _lib_hs_gather = _sig("dp_hs_gather_kv", [ctypes.POINTER(dp_kv_hs), _P, _i32, _P
 _lib_hs_reindex = _sig("dp_hs_rope_reindex", [_P, _i64, _i32, _i32, _i32, _i32, _P, _i32, _P,
                                               ctypes.POINTER(_i64), _P, _P, ctypes.POINTER(dp_rope),
                                               _P, ctypes.c_size_t, _P])
+_lib_si_ws = _sig("dp_score_index_workspace_bytes", [_i64], ctypes.c_size_t)
+_lib_score_index = _sig("dp_score_index", [_P, _P, _i32, _i64, ctypes.POINTER(dp_mask_policy), _P,
+                                           _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P])
 _lib_attention = _sig("dp_attention", [_P, _P, _P, _P, _i64, _i64, _P, _i32, _i32, _i32, _f32, _P])
 _lib_hs_attention = _sig("dp_hs_attention", [_P, _P, _P, _i64, _P, _i32, _P, _P, _i64, _P, _i64,
                                               _i32, _i32, _i32, _f32, _P])
@@ -111,7 +114,8 @@ EXPORTED = ["dp_abi_version", "dp_status_str", "dp_last_error", "dp_score_mask",
             "dp_compact_workspace_bytes", "dp_compact_index", "dp_rope_workspace_bytes",
             "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_append_kept",
             "dp_hs_offsets", "dp_hs_gather_kv",
-            "dp_hs_rope_reindex", "dp_attention", "dp_hs_attention", "dp_pr_add", "dp_pr_value"]
+            "dp_hs_rope_reindex", "dp_attention", "dp_hs_attention", "dp_score_index_workspace_bytes",
+            "dp_score_index", "dp_pr_add", "dp_pr_value"]
 
 
 def dp_abi_version():
@@ -194,6 +198,21 @@ def dp_score_mask(x0_hat, x_final, d, row_stride, policy, ell_out, keep_out, str
 
 def dp_compact_workspace_bytes(seq_len):
     return _lib_compact_ws(seq_len)
+
+
+def dp_score_index_workspace_bytes(seq_len):
+    return _lib_si_ws(int(seq_len))
+
+
+def dp_score_index(x0_hat, x_final, d, row_stride, policy, ell_out, keep_out, idx_out, n_kept,
+                   row_frame_src, row_frame_dst, workspace, dev_error=None, stream=None):
+    """Score, mask and kept-index list in one launch; the workspace must be
+    zero-filled before its first use (torch.zeros) and is reused as is."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib_score_index(_ptr(x0_hat), _ptr(x_final), d, int(row_stride), ctypes.byref(policy),
+                            _ptr(ell_out), _ptr(keep_out), _ptr(idx_out), _ptr(n_kept),
+                            _ptr(row_frame_src), _ptr(row_frame_dst), _ptr(workspace), ws_bytes,
+                            _ptr(dev_error), _stream(stream)))
 
 
 def dp_compact_index(keep, seq_len, idx_out, n_kept, row_frame_src, row_frame_dst, workspace,

@@ -8,7 +8,6 @@
 
 namespace dp {
 
-size_t compact_ws_bytes(int64_t T);
 size_t rope_ws_bytes(int32_t n_frames, int32_t n_pairs);
 uint64_t hs_tiles(const int64_t* class_cap, int32_t n_classes);
 int hs_max_heads();
@@ -17,6 +16,7 @@ namespace {
 thread_local char g_err[512] = "";
 constexpr int64_t kMaxRows = (int64_t)1 << 31;      // int32 row indices
 constexpr int64_t kMaxVec = (int64_t)1 << 31;       // 16-byte vectors per launch slab
+constexpr uint32_t kScoreIndexSpinLimit = 1u << 20;   // polls before DP_ESTALL
 constexpr int32_t kMaxAttnHeads = 65536;           // 64 key rows of a tile addressed in 32 bits
 }  // namespace
 
@@ -88,39 +88,83 @@ const char* dp_status_str(int s) {
     case DP_ECAPACITY: return "DP_ECAPACITY";
     case DP_EHIP: return "DP_EHIP";
     case DP_EUNSUPPORTED: return "DP_EUNSUPPORTED";
+    case DP_ESTALL: return "DP_ESTALL";
     default: return "DP_UNKNOWN";
   }
 }
 
 const char* dp_last_error(void) { return g_err; }
 
+// Checks shared by dp_score_mask and dp_score_index; *scoring tells whether
+// rows are scored (score mode with n_scored > 0).
+static dp_status check_score(const float* x0_hat, const float* x_final, int32_t d,
+                             int64_t row_stride, const dp_mask_policy* p, const float* ell_out,
+                             const char* fn, bool* scoring) {
+  if (p->seq_len < 1 || p->seq_len >= kMaxRows)
+    return fail(DP_ERANGE, "%s: seq_len %lld outside [1, 2^31)", fn, (long long)p->seq_len);
+  if (p->sink_len < 0 || p->window_len < 0 || p->n_scored < 0 || p->scored_begin < p->sink_len ||
+      p->scored_begin + p->n_scored > p->seq_len - p->window_len)
+    return fail(DP_EINVAL,
+                "%s: need 0 <= sink_len <= scored_begin and scored_begin + n_scored <= "
+                "seq_len - window_len", fn);
+  if ((p->mode != DP_MODE_SCORE && p->mode != DP_MODE_STREAMING) ||
+      (p->reversed != 0 && p->reversed != 1) || p->reserved != 0)
+    return fail(DP_EINVAL, "%s: mode, reversed or reserved out of range", fn);
+  *scoring = p->mode == DP_MODE_SCORE && p->n_scored > 0;
+  if (*scoring) {
+    if (!x0_hat || !x_final) return fail(DP_EINVAL, "%s: x0_hat and x_final are required", fn);
+    if (d < 1 || d > 256) return fail(DP_ERANGE, "%s: d = %d outside [1, 256]", fn, d);
+    if (row_stride < d) return fail(DP_EINVAL, "%s: row_stride < d", fn);
+    if (!aligned(x0_hat, 4) || !aligned(x_final, 4) || (ell_out && !aligned(ell_out, 4)))
+      return fail(DP_EALIGN, "%s: float arrays must be 4-byte aligned", fn);
+    if (row_stride > ((int64_t)1 << 40) / p->n_scored)
+      return fail(DP_ERANGE, "%s: input too large", fn);
+  }
+  return DP_OK;
+}
+
 dp_status dp_score_mask(const float* x0_hat, const float* x_final, int32_t d,
                         int64_t row_stride, const dp_mask_policy* p, float* ell_out,
                         uint8_t* keep_out, void* stream) {
   if (!p || !keep_out) return fail(DP_EINVAL, "dp_score_mask: policy and keep_out are required");
-  if (p->seq_len < 1 || p->seq_len >= kMaxRows)
-    return fail(DP_ERANGE, "dp_score_mask: seq_len %lld outside [1, 2^31)", (long long)p->seq_len);
-  if (p->sink_len < 0 || p->window_len < 0 || p->n_scored < 0 || p->scored_begin < p->sink_len ||
-      p->scored_begin + p->n_scored > p->seq_len - p->window_len)
-    return fail(DP_EINVAL,
-                "dp_score_mask: need 0 <= sink_len <= scored_begin and scored_begin + n_scored <= "
-                "seq_len - window_len");
-  if ((p->mode != DP_MODE_SCORE && p->mode != DP_MODE_STREAMING) ||
-      (p->reversed != 0 && p->reversed != 1) || p->reserved != 0)
-    return fail(DP_EINVAL, "dp_score_mask: mode, reversed or reserved out of range");
-  const bool scoring = p->mode == DP_MODE_SCORE && p->n_scored > 0;
-  if (scoring) {
-    if (!x0_hat || !x_final) return fail(DP_EINVAL, "dp_score_mask: x0_hat and x_final are required");
-    if (d < 1 || d > 256) return fail(DP_ERANGE, "dp_score_mask: d = %d outside [1, 256]", d);
-    if (row_stride < d) return fail(DP_EINVAL, "dp_score_mask: row_stride < d");
-    if (!aligned(x0_hat, 4) || !aligned(x_final, 4) || (ell_out && !aligned(ell_out, 4)))
-      return fail(DP_EALIGN, "dp_score_mask: float arrays must be 4-byte aligned");
-    if (row_stride > ((int64_t)1 << 40) / p->n_scored)
-      return fail(DP_ERANGE, "dp_score_mask: input too large");
-  }
+  bool scoring = false;
+  dp_status st = check_score(x0_hat, x_final, d, row_stride, p, ell_out, "dp_score_mask", &scoring);
+  if (st != DP_OK) return st;
   (void)hipGetLastError();
-  dp_status st = launch_score_mask(x0_hat, x_final, d, row_stride, *p, scoring ? ell_out : nullptr,
-                                   keep_out, (hipStream_t)stream);
+  st = launch_score_mask(x0_hat, x_final, d, row_stride, *p, scoring ? ell_out : nullptr,
+                         keep_out, (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+size_t dp_score_index_workspace_bytes(int64_t seq_len) {
+  return score_index_ws_bytes(seq_len < 0 ? 0 : seq_len);
+}
+
+dp_status dp_score_index(const float* x0_hat, const float* x_final, int32_t d,
+                         int64_t row_stride, const dp_mask_policy* p, float* ell_out,
+                         uint8_t* keep_out, int32_t* idx_out, int64_t* n_kept,
+                         const int32_t* row_frame_src, int32_t* row_frame_dst, void* ws,
+                         size_t ws_bytes, int32_t* dev_error, void* stream) {
+  if (!p || !idx_out || !n_kept || !ws)
+    return fail(DP_EINVAL, "dp_score_index: policy, idx_out, n_kept and workspace are required");
+  if ((row_frame_src == nullptr) != (row_frame_dst == nullptr))
+    return fail(DP_EINVAL, "dp_score_index: row_frame_src and row_frame_dst go together");
+  bool scoring = false;
+  dp_status st = check_score(x0_hat, x_final, d, row_stride, p, ell_out, "dp_score_index", &scoring);
+  if (st != DP_OK) return st;
+  if (!aligned(n_kept, 8) || !aligned(ws, 8) || !aligned(idx_out, 4) ||
+      (row_frame_src && (!aligned(row_frame_src, 4) || !aligned(row_frame_dst, 4))) ||
+      (dev_error && !aligned(dev_error, 4)))
+    return fail(DP_EALIGN, "dp_score_index: n_kept and workspace must be 8-byte, index arrays "
+                           "4-byte aligned");
+  if (ws_bytes < score_index_ws_bytes(p->seq_len))
+    return fail(DP_EINVAL, "dp_score_index: workspace of %zu bytes < %zu needed", ws_bytes,
+                score_index_ws_bytes(p->seq_len));
+  (void)hipGetLastError();
+  st = launch_score_index(x0_hat, x_final, d, row_stride, *p, scoring ? ell_out : nullptr,
+                          keep_out, idx_out, n_kept, row_frame_src, row_frame_dst, ws, dev_error,
+                          kScoreIndexSpinLimit, (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }

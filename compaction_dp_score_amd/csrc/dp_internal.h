@@ -156,6 +156,12 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 dp_status launch_score_mask(const float* x0, const float* xf, int32_t d, int64_t stride,
                             const dp_mask_policy& pol, float* ell, uint8_t* keep,
                             hipStream_t s);
+size_t score_index_ws_bytes(int64_t T);
+dp_status launch_score_index(const float* x0, const float* xf, int32_t d, int64_t stride,
+                             const dp_mask_policy& pol, float* ell, uint8_t* keep, int32_t* idx,
+                             int64_t* n_kept, const int32_t* rf_src, int32_t* rf_dst, void* ws,
+                             int32_t* dev_error, uint32_t spin_limit, hipStream_t s);
+size_t compact_ws_bytes(int64_t T);
 dp_status launch_compact(const uint8_t* keep, int64_t T, int32_t* idx, int64_t* n_kept,
                          const int32_t* rf_src, int32_t* rf_dst, int32_t* ws, hipStream_t s);
 dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dtype,

@@ -61,7 +61,9 @@ typedef enum {
   DP_ERANGE = 3,        /* size beyond a documented limit                       */
   DP_ECAPACITY = 4,     /* device-side only: more kept rows than capacity       */
   DP_EHIP = 5,          /* a HIP launch or runtime call failed                  */
-  DP_EUNSUPPORTED = 6   /* valid request outside what this build implements    */
+  DP_EUNSUPPORTED = 6,  /* valid request outside what this build implements    */
+  DP_ESTALL = 7         /* device-side only: a bounded wait between workgroups
+                           ran out (results of that call are not valid)        */
 } dp_status;
 
 typedef enum { DP_F32 = 0, DP_BF16 = 1 } dp_dtype;
@@ -142,6 +144,37 @@ dp_status dp_compact_index(const uint8_t* keep, int64_t seq_len, int32_t* idx_ou
                            int64_t* n_kept, const int32_t* row_frame_src,
                            int32_t* row_frame_dst, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * 1+2. Score, mask and kept-index list in one launch
+ *                              [DeCoPrune page, 어떻게 동작하나]
+ *
+ * The same results as dp_score_mask followed by dp_compact_index (bit for
+ * bit: ell_out, keep_out, idx_out, *n_kept and row_frame_dst) from one call.
+ * When at most 1024 tiles cover the rows (scored rows in tiles of four rows
+ * per lane group, e.g. 64 rows at d = 64; other rows in tiles of 256 to 2048
+ * rows), it is a single launch: workgroups score and mask their tile and find
+ * the output offset of its kept rows by a decoupled look-back over the tiles
+ * before them.  Longer scored ranges run as the separate score and compaction
+ * kernels, which are faster there (the one-launch form serialises on its tile
+ * ticket).  ell_out and keep_out may be NULL (not written).  idx_out: device
+ * int32, capacity seq_len; n_kept: device int64.
+ * workspace: device, >= dp_score_index_workspace_bytes(seq_len) bytes,
+ * 8-byte aligned, zero-filled before its first use; every call leaves it ready
+ * for the next call, so it is cleared once, not per call (calls that share a
+ * workspace must be ordered on one stream).  dev_error (device int32 or NULL)
+ * receives DP_ESTALL if a workgroup's bounded wait for its predecessors ran
+ * out, or if the workspace was not zero-filled; the outputs of that call are
+ * then not valid and the workspace must be zero-filled again.
+ * Policy and score arguments are checked as for dp_score_mask.
+ * ------------------------------------------------------------------------- */
+size_t    dp_score_index_workspace_bytes(int64_t seq_len);
+dp_status dp_score_index(const float* x0_hat, const float* x_final, int32_t d,
+                         int64_t row_stride, const dp_mask_policy* policy, float* ell_out,
+                         uint8_t* keep_out, int32_t* idx_out, int64_t* n_kept,
+                         const int32_t* row_frame_src, int32_t* row_frame_dst,
+                         void* workspace, size_t workspace_bytes, int32_t* dev_error,
+                         void* stream);
 
 /* ------------------------------------------------------------------------- *
  * RoPE temporal re-index parameters   [DeCoPrune page, 무엇과 다른가]

@@ -24,7 +24,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     lib = ctypes.CDLL(dp.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -35,6 +35,7 @@ def test_version_and_status_strings():
     assert dp.dp_abi_version() == 1
     assert dp.dp_status_str(dp.DP_OK) == "DP_OK"
     assert dp.dp_status_str(dp.DP_ECAPACITY) == "DP_ECAPACITY"
+    assert dp.dp_status_str(dp.DP_ESTALL) == "DP_ESTALL"
     assert dp.dp_status_str(99) == "DP_UNKNOWN"
 
 
@@ -301,3 +302,23 @@ def test_hs_attention_rejects():
     assert _status("hs_attention", *args(kc=FAKE + 2)) == dp.DP_EALIGN
     for bad in (float("nan"), 0.0, -0.5, float("inf")):
         assert _status("hs_attention", *args(scale=bad)) == dp.DP_EINVAL
+
+
+def test_score_index_rejects():
+    pol = _policy()
+    ws_need = dp.dp_score_index_workspace_bytes(1000)
+    assert ws_need == 16 + 8 * 1024 + 16 + 1000             # control, states, scratch, mask
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("x0", FAKE), ("xf", FAKE), ("d", 16), ("stride", 16), ("pol", ctypes.byref(pol)),
+        ("ell", None), ("keep", None), ("idx", FAKE), ("n", FAKE), ("rfs", None), ("rfd", None),
+        ("ws", FAKE), ("wsb", ws_need), ("err", None), ("s", None))]
+    assert _status("score_index", *args(idx=None)) == dp.DP_EINVAL
+    assert _status("score_index", *args(ws=None)) == dp.DP_EINVAL
+    assert _status("score_index", *args(rfs=FAKE)) == dp.DP_EINVAL     # src without dst
+    assert _status("score_index", *args(wsb=ws_need - 1)) == dp.DP_EINVAL
+    assert _status("score_index", *args(ws=FAKE + 4)) == dp.DP_EALIGN
+    assert _status("score_index", *args(n=FAKE + 4)) == dp.DP_EALIGN
+    assert _status("score_index", *args(d=300)) == dp.DP_ERANGE
+    assert _status("score_index", *args(x0=None)) == dp.DP_EINVAL
+    bad = _policy(scored_begin=50)                           # before the end of the sink
+    assert _status("score_index", *args(pol=ctypes.byref(bad))) == dp.DP_EINVAL

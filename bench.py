@@ -66,6 +66,9 @@ def parse():
                     choices=["eviction", "reindex", "prefix", "hs", "append", "attention",
                              "hs_attention"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fullkv", action="store_true",
+                    help="attention workloads: skip the context timing over the uncompacted "
+                         "cache (profiling runs, so that every dispatch is a timed one)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--summarize-stats", metavar="STATS_DIR",
@@ -84,6 +87,12 @@ def kernel_sources_sha(workload):
         with open(os.path.join(ROOT, "compaction_dp_score_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def profile_flags(workload):
+    """bench.py flags of the profiling runs of a workload."""
+    extra = " --no-fullkv" if workload in ("attention", "hs_attention") else ""
+    return "--no-cpu-baseline" + extra
 
 
 def read_traffic(workload):
@@ -325,6 +334,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 def flops_record(args, acc, ms, k_ms):
     """JSON record of a contraction workload (attention): TFLOP/s against the
     dense bf16 MFMA peak."""
+    k_ms = k_ms / acc.get("timer_launches", 1)
     tf = acc["step_flops"] / (ms * 1e-3) / 1e12
     ktf = acc["flops_per_launch"] / (k_ms * 1e-3) / 1e12
     rec = {"metric": acc.get("metric", "attention TFLOP/s over the compacted cache"),
@@ -335,7 +345,8 @@ def flops_record(args, acc, ms, k_ms):
            "roofline": {"bound": "mfma", "kernel": KERNELS[args.workload][0],
                         "achieved": round(ktf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(ktf / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "traffic": None, "flops_per_launch": acc["flops_per_launch"],
+                        "traffic": read_traffic(args.workload),
+                        "flops_per_launch": acc["flops_per_launch"],
                         "launch_ms": round(k_ms, 4)}}
     if acc.get("full_ms"):
         rec["fullkv"] = {"ms": round(acc["full_ms"], 4),
@@ -400,9 +411,11 @@ def summarize_pmc(workload, fetch_dir, write_dir):
                   % (kname, workload))
         out.write("# commands (from the repository root; %s as the dominant kernel):\n" % kname)
         out.write("#   rocprofv3 --pmc FETCH_SIZE -d %s -o run -f csv -- python bench.py "
-                  "--workload %s --no-cpu-baseline --steps 2 --warmup 0\n" % (fetch_dir, workload))
+                  "--workload %s %s --steps 2 --warmup 0\n" % (fetch_dir, workload,
+                                                             profile_flags(workload)))
         out.write("#   rocprofv3 --pmc WRITE_SIZE -d %s -o run -f csv -- python bench.py "
-                  "--workload %s --no-cpu-baseline --steps 2 --warmup 0\n" % (write_dir, workload))
+                  "--workload %s %s --steps 2 --warmup 0\n" % (write_dir, workload,
+                                                             profile_flags(workload)))
         out.write("#   python bench.py --workload %s --summarize-pmc %s %s\n"
                   % (workload, fetch_dir, write_dir))
         out.write("# scale: each counter divided by what it reads for calib_copy_kernel, which\n"
@@ -566,7 +579,8 @@ def setup_attention(dev, layers=4):
     def accounting():
         flops = 4.0 * C * n_ret * D * H
         return dict(n_kept=n_ret, gather_bytes=None, flops_per_launch=flops,
-                    step_flops=flops * layers, n_scored=0, full_ms=full_ms(),
+                    step_flops=flops * layers, n_scored=0,
+                    full_ms=None if ARGS.no_fullkv else full_ms(),
                     full_flops=4.0 * C * n_full * D * H,
                     config={"workload": "attention", "layers": layers, "heads": H, "head_dim": D,
                             "dtype": "bf16", "queries": C, "kv_rows": n_ret,
@@ -621,13 +635,13 @@ def setup_hs_attention(dev, layers=4):
     n_full = T + C
 
     def run(timed):
+        if timed:
+            gt.start()
         for l in range(layers):
-            if timed and l == 0:
-                gt.start()
             dp.dp_hs_attention(q, kr, vr, total, offsets, l, kc[l], vc[l], C, o, C, H, D,
                                dp.DP_BF16, scale)
-            if timed and l == 0:
-                gt.stop()
+        if timed:
+            gt.stop()
 
     def full_ms(reps=3):
         kf = torch.empty((n_full, H, D), dtype=torch.bfloat16, device=dev)
@@ -645,11 +659,13 @@ def setup_hs_attention(dev, layers=4):
         return a.elapsed_time(b) / reps
 
     def accounting():
-        n0 = np.diff(off[:H + 1])                       # layer 0's head runs (the timed launch)
-        flops = 4.0 * C * D * float((n0 + C).sum())
-        return dict(n_kept=int(n0.sum()), gather_bytes=None, flops_per_launch=flops,
-                    step_flops=4.0 * C * D * float(total + layers * H * C), n_scored=0,
-                    full_ms=full_ms(), full_flops=4.0 * C * n_full * D * H,
+        # the timer spans the `layers` launches (their head runs differ), so the
+        # per-launch figure is the mean over them
+        step_flops = 4.0 * C * D * float(total + layers * H * C)
+        return dict(n_kept=total, gather_bytes=None, flops_per_launch=step_flops / layers,
+                    timer_launches=layers, step_flops=step_flops, n_scored=0,
+                    full_ms=None if ARGS.no_fullkv else full_ms(),
+                    full_flops=4.0 * C * n_full * D * H,
                     metric="attention TFLOP/s over the ragged DeCoPrune-HS cache",
                     config={"workload": "hs_attention", "layers": layers, "heads": H,
                             "head_dim": D, "dtype": "bf16", "queries": C,
@@ -814,7 +830,7 @@ def summarize_stats(workload, stats_dir):
     lines = ["# rocprofv3 kernel statistics, %s workload (bench.py --workload %s)" % (workload, workload),
              "# commands (from the repository root):",
              "#   rocprofv3 --kernel-trace --stats -d %s -o run -f csv -- python bench.py "
-             "--workload %s --no-cpu-baseline --steps 10" % (stats_dir, workload),
+             "--workload %s %s --steps 10" % (stats_dir, workload, profile_flags(workload)),
              "#   python bench.py --workload %s --summarize-stats %s" % (workload, stats_dir),
              "# dominant kernel: %s; times in ns; fill_kernel and calib_copy_kernel are input" % kname,
              "# generation and the copy-ceiling reference, not part of the step",
@@ -832,8 +848,12 @@ def summarize_stats(workload, stats_dir):
     print(open(path).read())
 
 
+ARGS = None   # parsed command line (the attention setups read --no-fullkv)
+
+
 def main():
-    args = parse()
+    global ARGS
+    args = ARGS = parse()
     if args.summarize_stats:
         summarize_stats(args.workload, args.summarize_stats)
         return

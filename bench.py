@@ -43,13 +43,13 @@ CALIB_BYTES = 8 << 30          # size of the calibration copy run in every bench
 
 # dominant kernel of each workload: (rocprof name prefix, sources it is built from)
 KERNELS = {
-    "eviction": ("gather_kernel", ("gather.hip", "dp_internal.h")),
-    "prefix": ("gather_kernel", ("gather.hip", "dp_internal.h")),
-    "reindex": ("reindex_kernel", ("rope.hip", "dp_internal.h")),
-    "hs": ("hs_gather_kernel", ("hs.hip", "dp_internal.h")),
-    "append": ("reindex_kernel", ("rope.hip", "dp_internal.h")),
-    "attention": ("attn_fwd_kernel", ("attention.hip", "dp_internal.h")),
-    "hs_attention": ("attn_fwd_kernel", ("attention.hip", "dp_internal.h")),
+    "eviction": ("gather_kernel", ("gather.hip", "dp_device.h")),
+    "prefix": ("gather_kernel", ("gather.hip", "dp_device.h")),
+    "reindex": ("reindex_kernel", ("rope.hip", "dp_device.h")),
+    "hs": ("hs_gather_kernel", ("hs.hip", "dp_device.h")),
+    "append": ("reindex_kernel", ("rope.hip", "dp_device.h")),
+    "attention": ("attn_fwd_kernel", ("attention.hip", "dp_device.h")),
+    "hs_attention": ("attn_fwd_kernel", ("attention.hip", "dp_device.h")),
 }
 
 
@@ -348,6 +348,7 @@ def flops_record(args, acc, ms, k_ms):
                         "traffic": read_traffic(args.workload),
                         "flops_per_launch": acc["flops_per_launch"],
                         "launch_ms": round(k_ms, 4)}}
+    rec["copy_ceiling_gbs"] = round(copy_ceiling(torch.device("cuda:0"), CALIB_BYTES), 2)
     if acc.get("full_ms"):
         rec["fullkv"] = {"ms": round(acc["full_ms"], 4),
                          "tflops": round(acc["full_flops"] / (acc["full_ms"] * 1e-3) / 1e12, 2),
@@ -521,7 +522,7 @@ def setup_append(dev):
         reindex = rotated * 2 * w.rope_pairs * 2 * 2
         score = C * (8 * w.d + 1)
         return dict(n_kept=n, gather_bytes=reindex, step_bytes=append + reindex + score,
-                    n_scored=C, append_timer=at, append_bytes=append,
+                    n_scored=C, append_timer=at, append_bytes=append, timer_launches=2,
                     config={"workload": "append", "layout": "sink | ring of 4 chunk slots | history",
                             "layers": L, "heads": H, "head_dim": D, "kv_dtype": "bf16",
                             "tokens": T, "scored_tokens": C, "kept_tokens": n,
@@ -895,7 +896,9 @@ def main():
     gbs = acc["step_bytes"] / (ms * 1e-3) / 1e9
     g_ms = gt.mean_ms()
     g_gbs = acc["gather_bytes"] / (g_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(args.workload)             # per dispatch
+    if traffic is not None:
+        traffic *= acc.get("timer_launches", 1)         # over the timed region
     kernel = KERNELS[args.workload][0]
     rec = {
         "metric": "compacted KV GB/s (read+write) per prune step, % of HBM peak; tokens scored/s",

@@ -93,7 +93,10 @@ _lib_reindex = _sig("dp_rope_reindex", [_P, _i32, _i32, _i32, _i32, _i64, _P, _P
 _lib_rope_prepare = _sig("dp_rope_prepare", [ctypes.POINTER(dp_rope), _i32, _i32, _P, ctypes.c_size_t, _P])
 _lib_rope_apply = _sig("dp_rope_apply", [_P, _i32, _i32, _i32, _i32, _i64, _i64, _P, _P,
                                          ctypes.POINTER(dp_rope), _P, ctypes.c_size_t, _P])
-_lib_append = _sig("dp_append_kept", [ctypes.POINTER(dp_kv_inplace), _i64, _i64, _P, _P, _P, _P, _P])
+_lib_rope_shift = _sig("dp_rope_shift", [_P, _i32, _i32, _i32, _i32, _i64, _i64, _P, _P, _i32, _i32,
+                                         _f32, _P])
+_lib_append = _sig("dp_append_kept", [ctypes.POINTER(dp_kv_inplace), _i64, _i64, _P, _P, _P, _P,
+                                        ctypes.POINTER(dp_rope), _P, ctypes.c_size_t, _P])
 _lib_hs_offsets = _sig("dp_hs_offsets", [_P, _i32, _i32, _P, _i32, _P, _P])
 _lib_hs_gather = _sig("dp_hs_gather_kv", [ctypes.POINTER(dp_kv_hs), _P, _i32, _P, _P,
                                           ctypes.POINTER(_i64), _P, _P, ctypes.POINTER(dp_rope),
@@ -112,7 +115,7 @@ _lib_pr_value = _sig("dp_pr_value", [ctypes.POINTER(dp_pr_counter)], ctypes.c_do
 
 EXPORTED = ["dp_abi_version", "dp_status_str", "dp_last_error", "dp_score_mask",
             "dp_compact_workspace_bytes", "dp_compact_index", "dp_rope_workspace_bytes",
-            "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_append_kept",
+            "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_rope_shift", "dp_append_kept",
             "dp_hs_offsets", "dp_hs_gather_kv",
             "dp_hs_rope_reindex", "dp_attention", "dp_hs_attention", "dp_score_index_workspace_bytes",
             "dp_score_index", "dp_pr_add", "dp_pr_value"]
@@ -176,6 +179,7 @@ def make_rope(theta, frame_t, frame_phase, q0, knee, inv_factor, pair_begin=0):
     r.frame_t = frame_t.data_ptr()
     r.frame_phase = frame_phase.data_ptr()
     r.q0, r.knee, r.inv_factor = float(q0), float(knee), float(inv_factor)
+    r._tensors = (theta, frame_t, frame_phase)   # the struct holds raw pointers: keep them alive
     return r
 
 
@@ -255,9 +259,21 @@ def dp_rope_apply(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_
                            _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def dp_append_kept(kv, slot_begin, slot_rows, idx, n_kept, tail, row_frame=None, stream=None):
+def dp_rope_shift(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_capacity, n_rows,
+                  theta, pair_begin, n_pairs, delta, stream=None):
+    """k_layers: device int64 tensor of layer base pointers (ptr_array)."""
+    _check(_lib_rope_shift(_ptr(k_layers), n_layers, n_heads, head_dim, dtype, int(row_begin),
+                           int(rows_capacity), _ptr(n_rows), _ptr(theta), pair_begin, n_pairs,
+                           float(delta), _stream(stream)))
+
+
+def dp_append_kept(kv, slot_begin, slot_rows, idx, n_kept, tail, row_frame=None, fused_rope=None,
+                   workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib_append(ctypes.byref(kv), int(slot_begin), int(slot_rows), _ptr(idx), _ptr(n_kept),
-                       _ptr(tail), _ptr(row_frame), _stream(stream)))
+                       _ptr(tail), _ptr(row_frame),
+                       ctypes.byref(fused_rope) if fused_rope is not None else None,
+                       _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dp_hs_offsets(head_class, n_layers, n_heads, class_len, n_classes, offsets, stream=None):

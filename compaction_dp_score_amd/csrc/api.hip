@@ -307,9 +307,40 @@ dp_status dp_rope_apply(void* const* k_layers, int32_t n_layers, int32_t n_heads
   return st;
 }
 
+dp_status dp_rope_shift(void* const* k_layers, int32_t n_layers, int32_t n_heads,
+                        int32_t head_dim, int32_t dtype, int64_t row_begin,
+                        int64_t rows_capacity, const int64_t* n_rows, const float* theta,
+                        int32_t pair_begin, int32_t n_pairs, float delta, void* stream) {
+  const char* who = "dp_rope_shift";
+  if (!k_layers || !theta) return fail(DP_EINVAL, "%s: k_layers and theta are required", who);
+  dp_status st = check_shape(n_layers, n_heads, head_dim, dtype, who);
+  if (st != DP_OK) return st;
+  if (n_pairs < 1 || pair_begin < 0 || n_pairs > 4096)
+    return fail(DP_EINVAL, "%s: need 1 <= n_pairs <= 4096 and pair_begin >= 0", who);
+  if (2 * ((int64_t)pair_begin + n_pairs) > head_dim)
+    return fail(DP_ERANGE, "%s: temporal pairs [%d, %d) exceed head_dim/2 = %d", who, pair_begin,
+                pair_begin + n_pairs, head_dim / 2);
+  if ((2 * (int64_t)pair_begin * elem_size(dtype)) % 16 != 0)
+    return fail(DP_EALIGN, "%s: the temporal block must start on a 16-byte boundary", who);
+  if (!(delta - delta == 0.0f)) return fail(DP_EINVAL, "%s: delta must be finite", who);
+  const int64_t per_row = (int64_t)n_heads * (head_dim * elem_size(dtype) / 16);
+  const int64_t span = rows_capacity - row_begin;
+  if (row_begin < 0 || rows_capacity < 0 || rows_capacity >= kMaxRows || span * per_row >= kMaxVec ||
+      n_layers > 65535)
+    return fail(DP_ERANGE, "%s: rows x layers out of range", who);
+  if (n_rows && !aligned(n_rows, 8)) return fail(DP_EALIGN, "%s: n_rows alignment", who);
+  if (!aligned(theta, 4)) return fail(DP_EALIGN, "%s: theta alignment", who);
+  (void)hipGetLastError();
+  st = launch_rope_shift(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_capacity,
+                         n_rows, theta, pair_begin, n_pairs, delta, (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
 dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t slot_rows,
                          const int32_t* idx, const int64_t* n_kept, int64_t* tail,
-                         int32_t* row_frame, void* stream) {
+                         int32_t* row_frame, const dp_rope* fused_rope, const void* ws,
+                         size_t ws_bytes, void* stream) {
   if (!kv || !n_kept || !tail || (slot_rows > 0 && !idx))
     return fail(DP_EINVAL, "dp_append_kept: kv, idx, n_kept and tail are required");
   dp_status st = check_shape(kv->n_layers, kv->n_heads, kv->head_dim, kv->dtype, "dp_append_kept");
@@ -326,9 +357,16 @@ dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t sl
   if (!aligned(n_kept, 8) || !aligned(tail, 8) || (idx && !aligned(idx, 4)) ||
       (row_frame && !aligned(row_frame, 4)) || (kv->dev_error && !aligned(kv->dev_error, 4)))
     return fail(DP_EALIGN, "dp_append_kept: misaligned count, tail, index or frame array");
+  RopeView view{};
+  if (fused_rope) {
+    if (!row_frame) return fail(DP_EINVAL, "dp_append_kept: a fused re-index needs row_frame");
+    st = check_rope(fused_rope, kv->head_dim, kv->dtype, ws, ws_bytes, "dp_append_kept");
+    if (st != DP_OK) return st;
+    rope_view(*fused_rope, ws, &view, kv->dtype, kv->head_dim);
+  }
   (void)hipGetLastError();
   st = launch_append(*kv, slot_begin, slot_rows, idx, n_kept, tail, row_frame,
-                     (hipStream_t)stream);
+                     fused_rope ? &view : nullptr, (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }

@@ -9,7 +9,10 @@
 // per lane, non-temporal); append_finish_kernel then retires the slot's row frames
 // (-1) and advances the tail.  Both launches re-derive the appended span from
 // the same device values, and the finish launch runs after the copy on the
-// stream, so the tail is never read after it changes.
+// stream, so the tail is never read after it changes.  Optionally the K rows
+// are re-rotated on the way by their frames' phase steps (the first re-index of
+// a chunk that has just left the window), as the gather does: the lookups go
+// out before the data load and the rotation costs no extra HBM bytes.
 #include "dp_internal.h"
 
 namespace dp {
@@ -29,8 +32,12 @@ struct AppendArgs {
   int64_t slot_begin;
   int64_t slot_rows;
   FastDiv div_row;     // 16-byte vectors per row
+  FastDiv div_head;    // 16-byte vectors per head row
   uint32_t n_slabs;    // n_layers * n_kv
   int32_t n_kv;
+  int32_t dtype;
+  int32_t has_rope;
+  RopeView rope;
 };
 
 // The appended span [t0, t0 + n); false (with the status) when it would pass
@@ -57,17 +64,43 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendArgs a) {
   u32x4* __restrict__ base = reinterpret_cast<u32x4*>(is_v ? a.v_layers[layer] : a.k_layers[layer]);
   // A chunk keeps a small share of its rows, so the grid is a fixed number of
   // workgroups per slab that stride over the live tiles (no idle workgroups).
+  const bool rope = a.has_rope && !is_v;
   for (uint32_t t = blockIdx.x; t < tiles; t += gridDim.x) {
     const uint32_t i = t * kBlock + threadIdx.x;
     if (i >= per_slab) break;
     const uint32_t j = fdiv(i, a.div_row);
     const uint32_t c = i - j * a.div_row.d;
     const int32_t s = a.idx[j];
-    if ((uint64_t)(uint32_t)s >= (uint64_t)a.slot_rows) continue;   // out-of-range entries skipped
-    const u32x4 v =
-        __builtin_nontemporal_load(base + (a.slot_begin + s) * (int64_t)a.div_row.d + c);
-    __builtin_nontemporal_store(v, base + (t0 + j) * (int64_t)a.div_row.d + c);
-    if (a.row_frame && blockIdx.y == 0 && c == 0) a.row_frame[t0 + j] = a.row_frame[a.slot_begin + s];
+    const bool sv = (uint64_t)(uint32_t)s < (uint64_t)a.slot_rows;  // out-of-range entries skipped
+    const int64_t src = (a.slot_begin + (sv ? s : 0)) * (int64_t)a.div_row.d + c;
+    if (rope) {
+      // the row's frame, its phase step and {cos, sin} are requested before the
+      // data (vector loads retire in order); lanes outside the temporal block
+      // read entry 0 and keep their data
+      const uint32_t h = fdiv(c, a.div_head);
+      const int tv = (int)(c - h * a.div_head.d) - a.rope.tv_begin;
+      const bool in_block = tv >= 0 && tv < a.rope.tv_count;
+      const int f = a.row_frame[a.slot_begin + (sv ? s : 0)];
+      const bool fv = (uint32_t)f < (uint32_t)a.rope.n_frames;
+      const int fc = fv ? f : 0;
+      const int p0 = in_block ? tv * a.rope.ppv : 0;
+      const f32x4* tb =
+          reinterpret_cast<const f32x4*>(a.rope.cs + (int64_t)fc * a.rope.pairs_padded + p0);
+      const float dl = a.rope.delta[fc];
+      const f32x4 t01 = tb[0];     // the table has a 32-byte tail, so tb[1] is readable
+      const f32x4 t23 = tb[1];
+      u32x4 v = __builtin_nontemporal_load(base + src);
+      __builtin_amdgcn_sched_barrier(0);
+      const int nv = min(a.rope.ppv, a.rope.n_pairs - p0);
+      const u32x4 r = rotate_vec_tab(v, a.dtype, t01, t23, nv);
+      if (in_block && fv && dl != 0.0f) v = r;
+      if (sv) __builtin_nontemporal_store(v, base + (t0 + j) * (int64_t)a.div_row.d + c);
+    } else if (sv) {
+      const u32x4 v = __builtin_nontemporal_load(base + src);
+      __builtin_nontemporal_store(v, base + (t0 + j) * (int64_t)a.div_row.d + c);
+    }
+    if (sv && a.row_frame && blockIdx.y == 0 && c == 0)
+      a.row_frame[t0 + j] = a.row_frame[a.slot_begin + s];
   }
 }
 
@@ -89,7 +122,7 @@ __global__ __launch_bounds__(kBlock) void append_finish_kernel(AppendArgs a) {
 
 dp_status launch_append(const dp_kv_inplace& kv, int64_t slot_begin, int64_t slot_rows,
                         const int32_t* idx, const int64_t* n_kept, int64_t* tail,
-                        int32_t* row_frame, hipStream_t s) {
+                        int32_t* row_frame, const RopeView* rope, hipStream_t s) {
   AppendArgs a;
   a.k_layers = kv.k_layers;
   a.v_layers = kv.v_layers;
@@ -102,6 +135,10 @@ dp_status launch_append(const dp_kv_inplace& kv, int64_t slot_begin, int64_t slo
   a.slot_begin = slot_begin;
   a.slot_rows = slot_rows;
   a.div_row = make_fastdiv((uint32_t)((int64_t)kv.n_heads * kv.head_dim * elem_size(kv.dtype) / 16));
+  a.div_head = make_fastdiv((uint32_t)(kv.head_dim * elem_size(kv.dtype) / 16));
+  a.dtype = kv.dtype;
+  a.has_rope = rope != nullptr;
+  a.rope = rope ? *rope : RopeView{};
   a.n_kv = kv.v_layers ? 2 : 1;
   a.n_slabs = (uint32_t)(kv.n_layers * a.n_kv);
   const uint64_t tiles_cap = ((uint64_t)slot_rows * a.div_row.d + kBlock - 1) / kBlock;

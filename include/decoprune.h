@@ -283,6 +283,25 @@ dp_status dp_rope_apply(void* const* k_layers, int32_t n_layers, int32_t n_heads
                         const dp_rope* rope, const void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* dp_rope_shift: the steady-state re-index [DeCoPrune page, 무엇과 다른가].
+ * A frame past the knee before and after a step moves by the same amount as
+ * every other such frame: q0 advances F frames per step, so t~ advances by
+ * F * (1 - 1/c) (3.5 frames for 4-frame chunks and c = 8).  A row range that
+ * holds only such rows (in the ring layout: the sink and the history appended
+ * before this step) is therefore rotated by one uniform step delta, with no
+ * row frames and no per-frame table: every temporal pair j of rows
+ * [row_begin, min(rows_capacity, *n_rows)) of every layer is rotated by
+ * theta_j * delta, with cos/sin, rounding and storage as in section 4 (the
+ * result equals dp_rope_apply on those rows bit for bit when each of their
+ * frames has step delta).  theta: device fp32 [n_pairs]; delta finite
+ * (0 writes nothing).  Frame phases are not touched: the caller's
+ * dp_rope_prepare of the step advances every frame.  One launch.
+ * ------------------------------------------------------------------------- */
+dp_status dp_rope_shift(void* const* k_layers, int32_t n_layers, int32_t n_heads,
+                        int32_t head_dim, int32_t dtype, int64_t row_begin,
+                        int64_t rows_capacity, const int64_t* n_rows, const float* theta,
+                        int32_t pair_begin, int32_t n_pairs, float delta, void* stream);
+
 /* ------------------------------------------------------------------------- *
  * 4b. Segment-append compaction in place     [DeCoPrune page, 어떻게 동작하나]
  *
@@ -305,6 +324,14 @@ dp_status dp_rope_apply(void* const* k_layers, int32_t n_layers, int32_t n_heads
  * place: dp_rope_prepare once, then dp_rope_apply over the sink rows and over
  * the history rows [history_begin, *tail) (n_rows = tail); the window slots
  * need no re-index while they are in the window.
+ * fused_rope (or NULL): the K rows are re-rotated while copied, each by its
+ * frame's phase step, from the tables a dp_rope_prepare of this step wrote
+ * into workspace (fused_rope is read for its pair layout and frame count, as by
+ * dp_rope_apply; row_frame is then required).  This is the first re-index of a
+ * chunk that has just left the window.  In the steady state the other old
+ * keys all move by one uniform step, so a step is: dp_rope_shift over the sink
+ * and over [history_begin, *tail) (before this call, so the tail is the old
+ * one), dp_rope_prepare, then this call with the fused re-index.
  * ------------------------------------------------------------------------- */
 typedef struct {
   void* const* k_layers;     /* device array [n_layers]: [capacity][n_heads][head_dim] */
@@ -316,7 +343,8 @@ typedef struct {
 
 dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t slot_rows,
                          const int32_t* idx, const int64_t* n_kept, int64_t* tail,
-                         int32_t* row_frame, void* stream);
+                         int32_t* row_frame, const dp_rope* fused_rope,
+                         const void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * 5. DeCoPrune-HS: head-specialised ragged cache   [DeCoPrune page, 무엇과 다른가]

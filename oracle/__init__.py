@@ -41,6 +41,7 @@ def lib():
         L.oracle_append_kept.restype = i64
         L.oracle_rope_frames.argtypes = [i32, P, P, f32, f32, f32, i32, P, P, P, P]
         L.oracle_rope_rows.argtypes = [P, i32, i64, i32, i32, i32, i32, P, P, P, P]
+        L.oracle_rope_uniform.argtypes = [i32, P, f32, P, P]
         L.oracle_rope_headrows.argtypes = [P, i32, i64, i32, i32, i32, P, P, P, P]
         L.oracle_hs_offsets.argtypes = [P, i32, i32, P, P]
         L.oracle_hs_gather_layer.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P]
@@ -166,6 +167,17 @@ def rope_frames(frame_t, frame_phase, q0, knee, inv_factor, theta):
     lib().oracle_rope_frames(nf, _p(ft), _p(ph), np.float32(q0), np.float32(knee),
                              np.float32(inv_factor), npairs, _p(th), _p(delta), _p(c), _p(s))
     return delta, c, s, ph
+
+
+def rope_uniform(theta, delta):
+    """Tables of one uniform phase step delta for every row (frame 0 of a
+    one-frame table); use with rope_rows and row_frame all 0."""
+    th = _c(theta, np.float32)
+    n = th.shape[0]
+    c = np.empty((1, n), np.float32)
+    s = np.empty((1, n), np.float32)
+    lib().oracle_rope_uniform(n, _p(th), np.float32(delta), _p(c), _p(s))
+    return np.array([delta], np.float32), c, s, None
 
 
 def _dtype_code(a):

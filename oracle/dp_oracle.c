@@ -197,6 +197,22 @@ void oracle_rope_frames(int32_t n_frames, const float* frame_t, float* frame_pha
   }
 }
 
+/* ---------------------------------------------------------------------- *
+ * Uniform phase step [DeCoPrune page, 무엇과 다른가]: once a frame is past the
+ * knee before and after a step, t~ moves by the same amount for every such
+ * frame (q0 advances F frames: F (1 - 1/c)), so the keys of all of them are
+ * rotated by one table: per pair j, angle = theta_j * delta (fp32), cos and
+ * sin the fp32 roundings of the fp64 values (as oracle_rope_frames).
+ * ---------------------------------------------------------------------- */
+void oracle_rope_uniform(int32_t n_pairs, const float* theta, float delta, float* cos_tab,
+                         float* sin_tab) {
+  for (int32_t j = 0; j < n_pairs; ++j) {
+    float angle = theta[j] * delta;
+    cos_tab[j] = (float)cos((double)angle);
+    sin_tab[j] = (float)sin((double)angle);
+  }
+}
+
 static float bf16_to_f32(uint16_t h) {
   uint32_t u = (uint32_t)h << 16;
   float f;

@@ -24,7 +24,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     lib = ctypes.CDLL(dp.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -239,16 +239,47 @@ def _inplace(**kw):
 ])
 def test_append_kept_rejects(kw, slot, want):
     kv = _inplace(**kw)
-    st = _status("append", ctypes.byref(kv), slot[0], slot[1], FAKE, FAKE, FAKE, None, None)
+    st = _status("append", ctypes.byref(kv), slot[0], slot[1], FAKE, FAKE, FAKE, None, None, None,
+                 0, None)
     assert st == want, dp.dp_last_error()
 
 
 def test_append_kept_rejects_missing_and_misaligned():
     kv = _inplace()
-    assert _status("append", ctypes.byref(kv), 0, 10, None, FAKE, FAKE, None, None) == dp.DP_EINVAL
-    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, None, None, None) == dp.DP_EINVAL
-    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE + 4, FAKE, None, None) == dp.DP_EALIGN
-    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, FAKE, FAKE + 2, None) == dp.DP_EALIGN
+    assert _status("append", ctypes.byref(kv), 0, 10, None, FAKE, FAKE, None, None, None, 0,
+                   None) == dp.DP_EINVAL
+    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, None, None, None, None, 0,
+                   None) == dp.DP_EINVAL
+    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE + 4, FAKE, None, None, None, 0,
+                   None) == dp.DP_EALIGN
+    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, FAKE, FAKE + 2, None, None, 0,
+                   None) == dp.DP_EALIGN
+
+
+def test_append_kept_fused_rope_and_shift_reject():
+    kv = dp.dp_kv_inplace()
+    kv.k_layers, kv.v_layers = FAKE, FAKE
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = 2, 4, 64, dp.DP_BF16
+    kv.capacity = 1000
+    r = _rope()
+    # a fused re-index needs the row frames and a large enough workspace
+    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, FAKE, None, ctypes.byref(r),
+                   FAKE, 1 << 20, None) == dp.DP_EINVAL
+    assert _status("append", ctypes.byref(kv), 0, 10, FAKE, FAKE, FAKE, FAKE, ctypes.byref(r),
+                   FAKE, 8, None) == dp.DP_EINVAL
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("k", FAKE), ("L", 2), ("H", 4), ("D", 64), ("dt", dp.DP_BF16), ("rb", 0), ("cap", 1000),
+        ("n", None), ("theta", FAKE), ("pb", 0), ("np", 12), ("delta", 3.5), ("s", None))]
+    assert _status("rope_shift", *args(theta=None)) == dp.DP_EINVAL
+    assert _status("rope_shift", *args(np=0)) == dp.DP_EINVAL
+    assert _status("rope_shift", *args(np=40)) == dp.DP_ERANGE            # past head_dim/2
+    assert _status("rope_shift", *args(pb=2)) == dp.DP_EALIGN             # block start not 16 B
+    assert _status("rope_shift", *args(delta=float("inf"))) == dp.DP_EINVAL
+    assert _status("rope_shift", *args(delta=float("nan"))) == dp.DP_EINVAL
+    assert _status("rope_shift", *args(rb=-1)) == dp.DP_ERANGE
+    assert _status("rope_shift", *args(n=FAKE + 4)) == dp.DP_EALIGN
+    assert _status("rope_shift", *args(D=7)) == dp.DP_EINVAL
+    assert _status("rope_shift", *args(cap=0)) == dp.DP_OK                 # empty range: nothing
 
 
 def test_rope_prepare_and_apply_reject():

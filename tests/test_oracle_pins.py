@@ -294,6 +294,59 @@ def test_reindex_relative_position_identity():
         assert abs(lhs - rhs) < 1e-4 * (1 + abs(rhs)), f
 
 
+def test_steady_state_phase_step_is_uniform():
+    """Rollout of the one-minute setup (4 frames per chunk, knee 12, factor 8):
+    once a frame is past the knee before and after a step, its phase step is
+    F (1 - 1/c) = 3.5 frames exactly, whatever its frame; frames crossing the
+    knee step by less, window frames not at all (exact rationals)."""
+    F, knee, c = 4, 12, 8
+    theta = dpsynth.rope_theta(44)
+    t = np.arange(240, dtype=np.float32)
+    ph = t.copy()
+    for step in range(1, 20):
+        q0 = 4 * F + F * step                       # the chunk about to be generated
+        prev_q0 = q0 - F
+        visible = t < q0
+        delta, cos_t, sin_t, ph_new = oracle.rope_frames(t, ph, float(q0), float(knee),
+                                                         np.float32(1.0 / c), theta)
+        for f in np.flatnonzero(visible):
+            before = prev_q0 - f > knee and step > 1
+            after = q0 - f > knee
+            d = Fraction(float(delta[f]))
+            assert d == _t_new_exact(q0, knee, c, int(f)) - Fraction(float(ph[f])), (step, f)
+            if before and after:
+                assert d == Fraction(F) * (1 - Fraction(1, c)), (step, f)
+            elif not after:
+                assert d == 0, (step, f)
+            else:                                   # first step past the knee
+                assert d > 0, (step, f)
+        # the uniform tables equal the per-frame tables of every such frame
+        steady = [f for f in np.flatnonzero(visible)
+                  if step > 1 and prev_q0 - f > knee and q0 - f > knee]
+        if steady:
+            _, cu, su, _ = oracle.rope_uniform(theta, 3.5)
+            for f in steady:
+                assert np.array_equal(cos_t[f].view(np.uint32), cu[0].view(np.uint32))
+                assert np.array_equal(sin_t[f].view(np.uint32), su[0].view(np.uint32))
+        ph = ph_new
+
+
+def test_uniform_shift_matches_per_frame_rows():
+    """A uniform step over rows of many frames is the per-frame re-index with
+    every frame's step equal to it (bitwise), and the float64 rotation."""
+    rng = np.random.default_rng(13)
+    theta = dpsynth.rope_theta(12)
+    k = rng.standard_normal((40, 3, 64)).astype(np.float32)
+    tab = oracle.rope_uniform(theta, 3.5)
+    got = oracle.rope_rows(k.copy(), np.zeros(40, np.int32), 2, tab)
+    want = _rot_f64(k, np.zeros(40, np.int64), 2, theta, np.array([3.5]))
+    assert np.max(np.abs(got - want)) < 2e-6
+    per = (np.full(10, 3.5, np.float32),) + tuple(
+        np.repeat(x, 10, axis=0) for x in oracle.rope_uniform(theta, 3.5)[1:3]) + (None,)
+    got2 = oracle.rope_rows(k.copy(), (np.arange(40) // 4).astype(np.int32), 2, per)
+    assert np.array_equal(got.view(np.uint32), got2.view(np.uint32))
+
+
 def test_reindex_rotations_compose():
     # two re-index passes (q0 then q0') equal one pass to q0' from the start
     rng = np.random.default_rng(12)

@@ -50,6 +50,7 @@ KERNELS = {
     "append": ("reindex_kernel", ("rope.hip", "dp_device.h")),
     "attention": ("attn_fwd_kernel", ("attention.hip", "dp_device.h")),
     "hs_attention": ("attn_fwd_kernel", ("attention.hip", "dp_device.h")),
+    "steady": ("shift_kernel", ("rope.hip", "dp_device.h")),
 }
 
 
@@ -64,7 +65,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="eviction",
                     choices=["eviction", "reindex", "prefix", "hs", "append", "attention",
-                             "hs_attention"])
+                             "hs_attention", "steady"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullkv", action="store_true",
                     help="attention workloads: skip the context timing over the uncompacted "
@@ -532,6 +533,124 @@ def setup_append(dev):
     return run, gt, accounting, None
 
 
+def setup_steady(dev):
+    """A steady-state step of the one-minute rollout in the ring layout: per
+    layer [sink | ring of 4 chunk slots (chunks 56-59) | history (the retained
+    rows of chunks 1-55) | room for one chunk].  Chunk 56 leaves the window for
+    q0 = 240: it is scored and indexed in one launch; every old key (sink and
+    history, all past the knee at q0 = 236 and 240) moves by the uniform step
+    F (1 - 1/c) = 3.5 frames (two dp_rope_shift launches); dp_rope_prepare
+    writes the per-frame tables and dp_append_kept appends the chunk's kept
+    rows with their first re-index fused.  The tail, the slot's row frames and
+    the phase table are restored before each step.  For context the general
+    path (append, then dp_rope_apply over the sink and the whole history) is
+    timed on the same buffers."""
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    w = dpsynth.WORKLOADS["reindex"]
+    H, D, L, C, tpf = w.n_heads, w.head_dim, w.n_layers, w.chunk_tokens, w.tokens_per_frame
+    keep_full = dpsynth.retained_keep(w)
+    hist_rows = np.flatnonzero(keep_full[C:56 * C]) + C          # retained rows of chunks 1..55
+    n_hist = hist_rows.shape[0]
+    hb = 5 * C                                                    # sink + 4 ring slots
+    cap = hb + n_hist + C
+    slot_begin = C                                                # ring slot 0: chunk 56
+    rf_host = np.full(cap, -1, np.int32)
+    rf_host[:C] = np.arange(C) // tpf
+    rf_host[C:hb] = (56 * C + np.arange(4 * C)) // tpf
+    rf_host[hb:hb + n_hist] = hist_rows // tpf
+    ks = _fill_layers(dev, w, cap, range(L), dpsynth.STREAM_K)
+    vs = _fill_layers(dev, w, cap, range(L), dpsynth.STREAM_V)
+    x0, xf = dpsynth.score_inputs(dpsynth.WORKLOADS["eviction"])  # one chunk of scores
+    x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
+    rf0 = torch.from_numpy(rf_host).to(dev)
+    rf = rf0.clone()
+    kv = dp.dp_kv_inplace()
+    arr_k, arr_v = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
+    kv.k_layers, kv.v_layers = arr_k.data_ptr(), arr_v.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dp.DP_BF16
+    kv.capacity = cap
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    tail0 = torch.tensor([hb + n_hist], dtype=torch.int64, device=dev)
+    tail = tail0.clone()
+    pol = dp.make_policy(C, 0, 0, 0, C, w.gamma)
+    keep = torch.empty(C, dtype=torch.uint8, device=dev)
+    idx = torch.empty(C, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64, device=dev)
+    theta = torch.from_numpy(dpsynth.rope_theta(w.rope_pairs, w.rope_base)).to(dev)
+    ft, fp = dpsynth.frame_tables(w)
+    ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(fp).to(dev)
+    ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    # the phases the old keys carry after the previous step (q0 = 236)
+    dp.dp_rope_prepare(dp.make_rope(theta, ftd, fpd, w.q0 - 4, w.rope_knee, 1.0 / w.rope_factor),
+                       D, dp.DP_BF16, ws_r)
+    phase0 = fpd.clone()
+    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    step_frames = 4 * (1.0 - 1.0 / w.rope_factor)                 # 3.5
+    ws_s = torch.empty(dp.dp_rope_shift_workspace_bytes(w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    gt = Timer()
+    keep_alive = [arr_k, arr_v]
+
+    def restore():
+        tail.copy_(tail0)
+        rf.copy_(rf0)
+        fpd.copy_(phase0)
+
+    def run(timed):
+        restore()
+        dp.dp_score_index(x0d, xfd, w.d, w.d, pol, None, keep, idx, nk, None, None, ws_si, err)
+        if timed:
+            gt.start()
+        dp.dp_rope_shift(arr_k, L, H, D, dp.DP_BF16, 0, C, None, theta, 0, w.rope_pairs,
+                         step_frames, ws_s)
+        dp.dp_rope_shift(arr_k, L, H, D, dp.DP_BF16, hb, cap, tail, theta, 0, w.rope_pairs,
+                         step_frames, ws_s)
+        if timed:
+            gt.stop()
+        dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+        dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf, rope, ws_r)
+
+    def general_ms(reps=5):
+        def once():
+            restore()
+            dp.dp_score_index(x0d, xfd, w.d, w.d, pol, None, keep, idx, nk, None, None, ws_si,
+                              err)
+            dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf)
+            dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+            dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, 0, C, None, rf, rope, ws_r)
+            dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, hb, cap, tail, rf, rope, ws_r)
+        once()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            once()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def accounting():
+        assert keep_alive and err.item() == 0
+        n = int(nk.item())
+        shifted = (C + n_hist) * H * L                  # head rows moved by the uniform step
+        shift_bytes = shifted * 2 * w.rope_pairs * 2 * 2
+        append = n * H * D * 2 * 2 * 2 * L
+        score = C * (8 * w.d + 1)
+        return dict(n_kept=n, gather_bytes=shift_bytes, timer_launches=2,
+                    step_bytes=shift_bytes + append + score, n_scored=C,
+                    context={"general_path_ms_per_step": round(general_ms(), 4)},
+                    config={"workload": "steady", "layout": "sink | ring of 4 chunk slots | history",
+                            "layers": L, "heads": H, "head_dim": D, "kv_dtype": "bf16",
+                            "history_rows": int(n_hist), "scored_tokens": C, "kept_tokens": n,
+                            "shifted_head_rows": shifted, "uniform_step_frames": step_frames,
+                            "rope_pairs": w.rope_pairs, "q0": w.q0})
+
+    return run, gt, accounting, None
+
+
 def setup_attention(dev, layers=4):
     """Attention of a new chunk (6,240 queries, 40 heads x 128, bf16) over the
     cache a one-minute history leaves after compaction: sink + 15 % of the 56
@@ -872,7 +991,7 @@ def main():
     dev = torch.device("cuda:0")
     setups = {"eviction": setup_eviction, "reindex": setup_reindex, "prefix": setup_prefix,
               "hs": setup_hs, "append": setup_append, "attention": setup_attention,
-              "hs_attention": setup_hs_attention}
+              "hs_attention": setup_hs_attention, "steady": setup_steady}
     if args.workload not in setups:
         print("workload %s is not wired into bench.py yet" % args.workload, file=sys.stderr)
         sys.exit(2)
@@ -936,6 +1055,8 @@ def main():
         a_ms = acc["append_timer"].mean_ms()
         rec["append_kernel"] = {"ms": round(a_ms, 5), "bytes": acc["append_bytes"],
                                 "gbs": round(acc["append_bytes"] / (a_ms * 1e-3) / 1e9, 2)}
+    if acc.get("context"):
+        rec["context"] = acc["context"]
     rec["copy_ceiling_gbs"] = round(copy_ceiling(dev, CALIB_BYTES), 2)
     if cpu is not None and not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu(args.cpu_seconds)

@@ -93,8 +93,9 @@ _lib_reindex = _sig("dp_rope_reindex", [_P, _i32, _i32, _i32, _i32, _i64, _P, _P
 _lib_rope_prepare = _sig("dp_rope_prepare", [ctypes.POINTER(dp_rope), _i32, _i32, _P, ctypes.c_size_t, _P])
 _lib_rope_apply = _sig("dp_rope_apply", [_P, _i32, _i32, _i32, _i32, _i64, _i64, _P, _P,
                                          ctypes.POINTER(dp_rope), _P, ctypes.c_size_t, _P])
+_lib_rope_shift_ws = _sig("dp_rope_shift_workspace_bytes", [_i32], ctypes.c_size_t)
 _lib_rope_shift = _sig("dp_rope_shift", [_P, _i32, _i32, _i32, _i32, _i64, _i64, _P, _P, _i32, _i32,
-                                         _f32, _P])
+                                         _f32, _P, ctypes.c_size_t, _P])
 _lib_append = _sig("dp_append_kept", [ctypes.POINTER(dp_kv_inplace), _i64, _i64, _P, _P, _P, _P,
                                         ctypes.POINTER(dp_rope), _P, ctypes.c_size_t, _P])
 _lib_hs_offsets = _sig("dp_hs_offsets", [_P, _i32, _i32, _P, _i32, _P, _P])
@@ -115,7 +116,8 @@ _lib_pr_value = _sig("dp_pr_value", [ctypes.POINTER(dp_pr_counter)], ctypes.c_do
 
 EXPORTED = ["dp_abi_version", "dp_status_str", "dp_last_error", "dp_score_mask",
             "dp_compact_workspace_bytes", "dp_compact_index", "dp_rope_workspace_bytes",
-            "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_rope_shift", "dp_append_kept",
+            "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_rope_shift_workspace_bytes",
+            "dp_rope_shift", "dp_append_kept",
             "dp_hs_offsets", "dp_hs_gather_kv",
             "dp_hs_rope_reindex", "dp_attention", "dp_hs_attention", "dp_score_index_workspace_bytes",
             "dp_score_index", "dp_pr_add", "dp_pr_value"]
@@ -259,12 +261,17 @@ def dp_rope_apply(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_
                            _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def dp_rope_shift_workspace_bytes(n_pairs):
+    return _lib_rope_shift_ws(int(n_pairs))
+
+
 def dp_rope_shift(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_capacity, n_rows,
-                  theta, pair_begin, n_pairs, delta, stream=None):
+                  theta, pair_begin, n_pairs, delta, workspace, stream=None):
     """k_layers: device int64 tensor of layer base pointers (ptr_array)."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib_rope_shift(_ptr(k_layers), n_layers, n_heads, head_dim, dtype, int(row_begin),
                            int(rows_capacity), _ptr(n_rows), _ptr(theta), pair_begin, n_pairs,
-                           float(delta), _stream(stream)))
+                           float(delta), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dp_append_kept(kv, slot_begin, slot_rows, idx, n_kept, tail, row_frame=None, fused_rope=None,

@@ -307,12 +307,18 @@ dp_status dp_rope_apply(void* const* k_layers, int32_t n_layers, int32_t n_heads
   return st;
 }
 
+size_t dp_rope_shift_workspace_bytes(int32_t n_pairs) {
+  return rope_shift_ws_bytes(n_pairs < 1 ? 1 : n_pairs);
+}
+
 dp_status dp_rope_shift(void* const* k_layers, int32_t n_layers, int32_t n_heads,
                         int32_t head_dim, int32_t dtype, int64_t row_begin,
                         int64_t rows_capacity, const int64_t* n_rows, const float* theta,
-                        int32_t pair_begin, int32_t n_pairs, float delta, void* stream) {
+                        int32_t pair_begin, int32_t n_pairs, float delta, void* ws,
+                        size_t ws_bytes, void* stream) {
   const char* who = "dp_rope_shift";
-  if (!k_layers || !theta) return fail(DP_EINVAL, "%s: k_layers and theta are required", who);
+  if (!k_layers || !theta || !ws)
+    return fail(DP_EINVAL, "%s: k_layers, theta and workspace are required", who);
   dp_status st = check_shape(n_layers, n_heads, head_dim, dtype, who);
   if (st != DP_OK) return st;
   if (n_pairs < 1 || pair_begin < 0 || n_pairs > 4096)
@@ -325,14 +331,18 @@ dp_status dp_rope_shift(void* const* k_layers, int32_t n_layers, int32_t n_heads
   if (!(delta - delta == 0.0f)) return fail(DP_EINVAL, "%s: delta must be finite", who);
   const int64_t per_row = (int64_t)n_heads * (head_dim * elem_size(dtype) / 16);
   const int64_t span = rows_capacity - row_begin;
-  if (row_begin < 0 || rows_capacity < 0 || rows_capacity >= kMaxRows || span * per_row >= kMaxVec ||
-      n_layers > 65535)
+  if (row_begin < 0 || rows_capacity < 0 || rows_capacity >= kMaxRows || span * per_row >= kMaxVec)
     return fail(DP_ERANGE, "%s: rows x layers out of range", who);
   if (n_rows && !aligned(n_rows, 8)) return fail(DP_EALIGN, "%s: n_rows alignment", who);
-  if (!aligned(theta, 4)) return fail(DP_EALIGN, "%s: theta alignment", who);
+  if (!aligned(theta, 4) || !aligned(ws, 16)) return fail(DP_EALIGN, "%s: theta or workspace alignment", who);
+  if (ws_bytes < rope_shift_ws_bytes(n_pairs))
+    return fail(DP_EINVAL, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes,
+                rope_shift_ws_bytes(n_pairs));
+  if (span > 0 && (span * per_row + 255) / 256 * n_layers >= kMaxVec)
+    return fail(DP_ERANGE, "%s: rows x layers out of range", who);
   (void)hipGetLastError();
   st = launch_rope_shift(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_capacity,
-                         n_rows, theta, pair_begin, n_pairs, delta, (hipStream_t)stream);
+                         n_rows, theta, pair_begin, n_pairs, delta, ws, (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }

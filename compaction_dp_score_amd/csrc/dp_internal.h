@@ -32,10 +32,11 @@ dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dt
 dp_status launch_gather(const dp_kv& kv, const int32_t* idx, const int64_t* n_kept,
                         const int32_t* row_frame, const RopeView* rope, hipStream_t s);
 void rope_view(const dp_rope& r, const void* ws, RopeView* view, int dtype, int head_dim);
+size_t rope_shift_ws_bytes(int32_t n_pairs);
 dp_status launch_rope_shift(void* const* k, int32_t n_layers, int32_t n_heads, int32_t head_dim,
                             int32_t dtype, int64_t row_begin, int64_t rows_cap,
                             const int64_t* n_rows, const float* theta, int32_t pair_begin,
-                            int32_t n_pairs, float delta, hipStream_t s);
+                            int32_t n_pairs, float delta, void* ws, hipStream_t s);
 dp_status launch_reindex(void* const* k, int32_t n_layers, int32_t n_heads, int32_t head_dim,
                          int32_t dtype, int64_t row_begin, int64_t rows_cap,
                          const int64_t* n_rows, const int32_t* row_frame, const RopeView& rope,

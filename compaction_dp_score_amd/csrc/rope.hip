@@ -12,12 +12,12 @@
 //   are neither read nor written.  HBM-bound: the method needs
 //   2 * 2*n_pairs*elem bytes per re-indexed head row; whole-line rewriting moves
 //   2 * (lines * 128) bytes (512 of 352 for 44 bf16 pairs).
-// shift_kernel: the steady-state form.  Once a frame is past the knee before
-//   and after a step, its phase step is the same for every such frame (q0
-//   advances F frames: F (1 - 1/c)), so a row range holding only such frames is
-//   rotated by one uniform step: no row frames and no per-frame table.  Each
-//   workgroup builds the {cos, sin} table of that step in LDS (fp32 angle, fp64
-//   sincos, as rope_prepare_kernel) and strides over the range.
+// shift_table_kernel + shift_kernel: the steady-state form.  Once a frame is
+//   past the knee before and after a step, its phase step is the same for every
+//   such frame (q0 advances F frames: F (1 - 1/c)), so a row range holding only
+//   such frames is rotated by one uniform step: one {cos, sin} table (written
+//   by a one-workgroup launch) and no row frames; the rotation pass has the
+//   layout of reindex_kernel.
 #include "dp_internal.h"
 
 namespace dp {
@@ -133,33 +133,16 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
   __builtin_nontemporal_store(v, p);
 }
 
-constexpr uint32_t kShiftBlocksPerLayer = 128;
-
-struct ShiftArgs {
-  void* const* layers;
-  const int64_t* n_rows;
-  int64_t row_begin;
-  int64_t rows_cap;
-  const float* theta;
-  float delta;
-  int32_t n_pairs;
-  int32_t pairs_padded;
-  FastDiv div_row;    // written vectors per row = H * wv_count
-  FastDiv div_head;   // written vectors per head row = wv_count
-  uint32_t vph;       // 16-byte vectors per head row
-  uint32_t n_heads;
-  int32_t dtype;
-  int32_t tv_begin, tv_count, ppv, wv_begin;
-};
-
-// grid (workgroups per layer, layer); dynamic LDS: {cos, sin}[pairs_padded + 4]
-__global__ __launch_bounds__(kBlock) void shift_kernel(ShiftArgs a) {
-  extern __shared__ f32x4 shift_tab[];
-  f32x2* cs = reinterpret_cast<f32x2*>(shift_tab);
-  for (int j = threadIdx.x; j < a.pairs_padded + 4; j += kBlock) {
+// The {cos, sin} table of one uniform step, for every pair (fp32 angle, fp64
+// sincos, as rope_prepare_kernel), padded with the identity so that four pairs
+// can be read from any vector's first pair.
+__global__ __launch_bounds__(64) void shift_table_kernel(const float* __restrict__ theta,
+                                                         int32_t n_pairs, int32_t entries,
+                                                         float delta, f32x2* __restrict__ cs) {
+  for (int j = threadIdx.x; j < entries; j += 64) {
     f32x2 v = {1.0f, 0.0f};
-    if (j < a.n_pairs) {
-      float ang = a.theta[j] * a.delta;
+    if (j < n_pairs) {
+      float ang = theta[j] * delta;
       double sd, cd;
       sincos((double)ang, &sd, &cd);
       v.x = (float)cd;
@@ -167,29 +150,53 @@ __global__ __launch_bounds__(kBlock) void shift_kernel(ShiftArgs a) {
     }
     cs[j] = v;
   }
-  __syncthreads();
+}
+
+struct ShiftArgs {
+  void* const* layers;
+  const int64_t* n_rows;
+  int64_t row_begin;
+  int64_t rows_cap;
+  const f32x2* cs;    // the step's table
+  int32_t n_pairs;
+  FastDiv div_row;    // written vectors per row = H * wv_count
+  FastDiv div_head;   // written vectors per head row = wv_count
+  uint32_t vph;       // 16-byte vectors per head row
+  uint32_t n_heads;
+  uint32_t n_layers;
+  int32_t dtype;
+  int32_t tv_begin, tv_count, ppv, wv_begin;
+};
+
+// One 16-byte vector per lane over the written span of every (row, head) of a
+// layer, as reindex_kernel, with the same table for every row (no row frames).
+__global__ __launch_bounds__(kBlock) void shift_kernel(ShiftArgs a) {
   int64_t end = a.rows_cap;
   if (a.n_rows) end = min(end, *a.n_rows);
   const int64_t n = end - a.row_begin;                 // rows [row_begin, end)
   if (n <= 0) return;
   const uint32_t per_row = a.div_row.d;
   const uint32_t per_layer = (uint32_t)(n * (int64_t)per_row);
-  u32x4* __restrict__ base =
-      reinterpret_cast<u32x4*>(a.layers[blockIdx.y]) + a.row_begin * a.n_heads * a.vph;
-  for (uint32_t i = blockIdx.x * kBlock + threadIdx.x; i < per_layer; i += gridDim.x * kBlock) {
-    const uint32_t j = fdiv(i, a.div_row);
-    const uint32_t rem = i - j * per_row;
-    const uint32_t h = fdiv(rem, a.div_head);
-    const int wq = a.wv_begin + (int)(rem - h * a.div_head.d);   // vector in the head row
-    const int tv = wq - a.tv_begin;
-    const bool in_block = tv >= 0 && tv < a.tv_count;
-    const int p0 = in_block ? tv * a.ppv : 0;
-    const f32x4* t = reinterpret_cast<const f32x4*>(cs + p0);
-    u32x4* p = base + ((int64_t)j * a.n_heads + h) * a.vph + wq;
-    u32x4 v = __builtin_nontemporal_load(p);
-    if (in_block) v = rotate_vec_tab(v, a.dtype, t[0], t[1], min(a.ppv, a.n_pairs - p0));
-    __builtin_nontemporal_store(v, p);
-  }
+  const uint32_t tiles = (per_layer + kBlock - 1) / kBlock;
+  const uint32_t layer = blockIdx.x / tiles;
+  if (layer >= a.n_layers) return;
+  const uint32_t i = (blockIdx.x - layer * tiles) * kBlock + threadIdx.x;
+  if (i >= per_layer) return;
+  const uint32_t j = fdiv(i, a.div_row);
+  const uint32_t rem = i - j * per_row;
+  const uint32_t h = fdiv(rem, a.div_head);
+  const int wq = a.wv_begin + (int)(rem - h * a.div_head.d);   // vector in the head row
+  const int tv = wq - a.tv_begin;
+  const bool in_block = tv >= 0 && tv < a.tv_count;
+  const int p0 = in_block ? tv * a.ppv : 0;
+  const f32x4* t = reinterpret_cast<const f32x4*>(a.cs + p0);
+  const f32x4 t01 = t[0];     // the table is padded, so t[1] is readable
+  const f32x4 t23 = t[1];
+  u32x4* __restrict__ p = reinterpret_cast<u32x4*>(a.layers[layer]) +
+                          ((a.row_begin + (int64_t)j) * a.n_heads + h) * a.vph + wq;
+  u32x4 v = __builtin_nontemporal_load(p);
+  if (in_block) v = rotate_vec_tab(v, a.dtype, t01, t23, min(a.ppv, a.n_pairs - p0));
+  __builtin_nontemporal_store(v, p);
 }
 
 }  // namespace
@@ -265,10 +272,14 @@ dp_status launch_reindex(void* const* k, int32_t n_layers, int32_t n_heads, int3
   return check_launch("reindex_kernel");
 }
 
+size_t rope_shift_ws_bytes(int32_t n_pairs) {
+  return (size_t)((n_pairs + 3) / 4 * 4 + 4) * sizeof(f32x2);
+}
+
 dp_status launch_rope_shift(void* const* k, int32_t n_layers, int32_t n_heads, int32_t head_dim,
                             int32_t dtype, int64_t row_begin, int64_t rows_cap,
                             const int64_t* n_rows, const float* theta, int32_t pair_begin,
-                            int32_t n_pairs, float delta, hipStream_t s) {
+                            int32_t n_pairs, float delta, void* ws, hipStream_t s) {
   if (delta == 0.0f || rows_cap <= row_begin) return DP_OK;   // nothing moves
   dp_rope r{};
   r.pair_begin = pair_begin;
@@ -276,28 +287,31 @@ dp_status launch_rope_shift(void* const* k, int32_t n_layers, int32_t n_heads, i
   r.n_frames = 1;
   RopeView view{};
   rope_view(r, nullptr, &view, dtype, head_dim);               // pair layout only
+  f32x2* cs = reinterpret_cast<f32x2*>(ws);
+  hipLaunchKernelGGL(shift_table_kernel, dim3(1), dim3(64), 0, s, theta, n_pairs,
+                     view.pairs_padded + 4, delta, cs);
+  dp_status st = check_launch("shift_table_kernel");
+  if (st != DP_OK) return st;
   ShiftArgs a;
   a.layers = k;
   a.n_rows = n_rows;
   a.row_begin = row_begin;
   a.rows_cap = rows_cap;
-  a.theta = theta;
-  a.delta = delta;
+  a.cs = cs;
   a.n_pairs = n_pairs;
-  a.pairs_padded = view.pairs_padded;
   a.div_row = make_fastdiv((uint32_t)(n_heads * view.wv_count));
   a.div_head = make_fastdiv((uint32_t)view.wv_count);
   a.vph = (uint32_t)(head_dim * elem_size(dtype) / 16);
   a.n_heads = (uint32_t)n_heads;
+  a.n_layers = (uint32_t)n_layers;
   a.dtype = dtype;
   a.tv_begin = view.tv_begin;
   a.tv_count = view.tv_count;
   a.ppv = view.ppv;
   a.wv_begin = view.wv_begin;
-  const uint64_t tiles = ((uint64_t)(rows_cap - row_begin) * a.div_row.d + kBlock - 1) / kBlock;
-  const uint32_t gx = (uint32_t)(tiles < kShiftBlocksPerLayer ? tiles : kShiftBlocksPerLayer);
-  const size_t lds = (size_t)(view.pairs_padded + 4) * sizeof(f32x2);
-  hipLaunchKernelGGL(shift_kernel, dim3(gx, n_layers), dim3(kBlock), lds, s, a);
+  const uint64_t gx =
+      ((uint64_t)(rows_cap - row_begin) * a.div_row.d + kBlock - 1) / kBlock * (uint64_t)n_layers;
+  hipLaunchKernelGGL(shift_kernel, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("shift_kernel");
 }
 

@@ -294,13 +294,18 @@ dp_status dp_rope_apply(void* const* k_layers, int32_t n_layers, int32_t n_heads
  * theta_j * delta, with cos/sin, rounding and storage as in section 4 (the
  * result equals dp_rope_apply on those rows bit for bit when each of their
  * frames has step delta).  theta: device fp32 [n_pairs]; delta finite
- * (0 writes nothing).  Frame phases are not touched: the caller's
- * dp_rope_prepare of the step advances every frame.  One launch.
+ * (0 writes nothing).  workspace: device, 16-byte aligned, at least
+ * dp_rope_shift_workspace_bytes(n_pairs) bytes (the step's {cos, sin} table;
+ * calls that share it must be ordered on one stream).  Frame phases are not
+ * touched: the caller's dp_rope_prepare of the step advances every frame.
+ * Two launches (the table, then the rotation).
  * ------------------------------------------------------------------------- */
+size_t    dp_rope_shift_workspace_bytes(int32_t n_pairs);
 dp_status dp_rope_shift(void* const* k_layers, int32_t n_layers, int32_t n_heads,
                         int32_t head_dim, int32_t dtype, int64_t row_begin,
                         int64_t rows_capacity, const int64_t* n_rows, const float* theta,
-                        int32_t pair_begin, int32_t n_pairs, float delta, void* stream);
+                        int32_t pair_begin, int32_t n_pairs, float delta, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * 4b. Segment-append compaction in place     [DeCoPrune page, 어떻게 동작하나]

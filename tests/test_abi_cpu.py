@@ -24,7 +24,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     lib = ctypes.CDLL(dp.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -269,7 +269,8 @@ def test_append_kept_fused_rope_and_shift_reject():
                    FAKE, 8, None) == dp.DP_EINVAL
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("k", FAKE), ("L", 2), ("H", 4), ("D", 64), ("dt", dp.DP_BF16), ("rb", 0), ("cap", 1000),
-        ("n", None), ("theta", FAKE), ("pb", 0), ("np", 12), ("delta", 3.5), ("s", None))]
+        ("n", None), ("theta", FAKE), ("pb", 0), ("np", 12), ("delta", 3.5), ("ws", FAKE),
+        ("wsb", 4096), ("s", None))]
     assert _status("rope_shift", *args(theta=None)) == dp.DP_EINVAL
     assert _status("rope_shift", *args(np=0)) == dp.DP_EINVAL
     assert _status("rope_shift", *args(np=40)) == dp.DP_ERANGE            # past head_dim/2
@@ -279,6 +280,10 @@ def test_append_kept_fused_rope_and_shift_reject():
     assert _status("rope_shift", *args(rb=-1)) == dp.DP_ERANGE
     assert _status("rope_shift", *args(n=FAKE + 4)) == dp.DP_EALIGN
     assert _status("rope_shift", *args(D=7)) == dp.DP_EINVAL
+    assert _status("rope_shift", *args(ws=None)) == dp.DP_EINVAL
+    assert _status("rope_shift", *args(wsb=8)) == dp.DP_EINVAL
+    assert _status("rope_shift", *args(ws=FAKE + 8)) == dp.DP_EALIGN
+    assert dp.dp_rope_shift_workspace_bytes(44) == (44 + 4) * 8
     assert _status("rope_shift", *args(cap=0)) == dp.DP_OK                 # empty range: nothing
 
 

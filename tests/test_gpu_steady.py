@@ -29,6 +29,11 @@ def _layers(rng, L, T, H, D, dtype, dev):
     return b.view(np.uint32), [to_dev(b[l], dev) for l in range(L)]
 
 
+def _sws(npairs, dev):
+    return torch.empty(dp.dp_rope_shift_workspace_bytes(npairs) // 4 + 4, dtype=torch.float32,
+                       device=dev)
+
+
 def _host(b, dtype):
     return b if dtype == dp.DP_BF16 else b.view(np.float32)
 
@@ -48,7 +53,8 @@ def test_rope_shift_matches_oracle(L, T, H, D, dtype, pb, npairs, rb, cap, dev_r
     n_rows = cap - 3 if dev_rows else cap                    # a device count below the capacity
     nd = torch.tensor([n_rows], dtype=torch.int64, device=dev) if dev_rows else None
     arr = dp.ptr_array(k, dev)
-    dp.dp_rope_shift(arr, L, H, D, dtype, rb, cap, nd, to_dev(theta, dev), pb, npairs, 3.5)
+    dp.dp_rope_shift(arr, L, H, D, dtype, rb, cap, nd, to_dev(theta, dev), pb, npairs, 3.5,
+                     _sws(npairs, dev))
     torch.cuda.synchronize()
     tab = oracle.rope_uniform(theta, 3.5)
     for l in range(L):
@@ -64,7 +70,7 @@ def test_rope_shift_zero_step_writes_nothing():
     rng = np.random.default_rng(3)
     kb, k = _layers(rng, 1, 50, 2, 64, dp.DP_BF16, dev)
     dp.dp_rope_shift(dp.ptr_array(k, dev), 1, 2, 64, dp.DP_BF16, 0, 50, None,
-                     to_dev(dpsynth.rope_theta(8), dev), 0, 8, 0.0)
+                     to_dev(dpsynth.rope_theta(8), dev), 0, 8, 0.0, _sws(8, dev))
     torch.cuda.synchronize()
     assert np.array_equal(bits(k[0]), kb[0])
 
@@ -92,7 +98,7 @@ def test_rope_shift_equals_apply_when_every_frame_steps_uniformly():
     dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws)
     dp.dp_rope_apply(dp.ptr_array(k1, dev), L, H, D, dp.DP_BF16, 0, T, None, rf, rope, ws)
     dp.dp_rope_shift(dp.ptr_array(k2, dev), L, H, D, dp.DP_BF16, 0, T, None, th, 0, npairs,
-                     F * (1 - 1 / c))
+                     F * (1 - 1 / c), _sws(npairs, dev))
     torch.cuda.synchronize()
     for l in range(L):
         assert np.array_equal(bits(k1[l]), bits(k2[l])), l
@@ -179,6 +185,7 @@ def test_steady_ring_rollout_equals_general_path_and_oracle():
     rf = np.full(cap, -1, np.int32)
     rf[:hist] = np.arange(hist) // TPF
     th_d, ft_d = to_dev(theta, dev), to_dev(frame_t, dev)
+    sws = _sws(NPAIRS, dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     paths = {}
     for name in ("general", "steady"):
@@ -220,9 +227,9 @@ def test_steady_ring_rollout_equals_general_path_and_oracle():
                                      p["ws"])
                 else:                            # every old key moves by the uniform step
                     dp.dp_rope_shift(p["ak"], L, H, D, dp.DP_BF16, 0, C, None, th_d, 0, NPAIRS,
-                                     STEP)
+                                     STEP, sws)
                     dp.dp_rope_shift(p["ak"], L, H, D, dp.DP_BF16, hist, cap, p["tail"], th_d, 0,
-                                     NPAIRS, STEP)
+                                     NPAIRS, STEP, sws)
                     dp.dp_rope_prepare(rope, D, dp.DP_BF16, p["ws"])
                 dp.dp_append_kept(p["kv"], sb, C, idx, nk, p["tail"], p["rf"], rope, p["ws"])
             for l in range(L):                   # the model writes the next chunk into the slot

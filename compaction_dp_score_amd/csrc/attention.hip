@@ -197,26 +197,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(Ks + (key4 + u) * kKP + ch * 8) = kr[u];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {            // element e of the chunk for the 4 keys
-      const int sh = (e & 1) * 16;
+      // byte permutes: the low (even e) or high (odd e) halves of two keys' words
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       u32x2 w;
-      w[0] = ((vr[0][e >> 1] >> sh) & 0xFFFFu) | (((vr[1][e >> 1] >> sh) & 0xFFFFu) << 16);
-      w[1] = ((vr[2][e >> 1] >> sh) & 0xFFFFu) | (((vr[3][e >> 1] >> sh) & 0xFFFFu) << 16);
+      w[0] = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
+      w[1] = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
       *reinterpret_cast<u32x2*>(Vt + (vch * 8 + e) * kVP + vkey4) = w;
     }
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(t + 1);
 
-    // ---- S^T = K Q^T for two 32-key tiles ----
+    // ---- S^T = K Q^T for two 32-key tiles: the two accumulation chains are
+    // interleaved so that consecutive MFMAs do not wait on each other ----
     f32x16 s[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
 #pragma unroll
-      for (int ds = 0; ds < kD / 16; ++ds) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + l32) * kKP + ds * 16 + hf * 8);
-        s[kt] = mfma(ka, qb[ds], s[kt]);
-      }
+    for (int ds = 0; ds < kD / 16; ++ds) {
+      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(Ks + l32 * kKP + ds * 16 + hf * 8);
+      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(Ks + (32 + l32) * kKP + ds * 16 + hf * 8);
+      s[0] = mfma(ka0, qb[ds], s[0]);
+      s[1] = mfma(ka1, qb[ds], s[1]);
     }
 
     // ---- online softmax (base 2), lane-local per query plus partner lane ----
@@ -274,22 +277,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       pb[ks] = __builtin_bit_cast(bf16x8, w);
     }
 
-    // ---- O^T += V^T P^T, V^T read in the same key order ----
+    // ---- O^T += V^T P^T, V^T read in the same key order; per key step the four
+    // dim tiles' fragments are read together and feed independent accumulators ----
 #pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) {
-      const uint16_t* vrow = Vt + (dt * 32 + l32) * kVP;
+    for (int ks = 0; ks < 4; ++ks) {
+      const int base = (ks >> 1) * 32 + 16 * (ks & 1) + 4 * hf;
+      bf16x8 va[kD / 32];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int base = (ks >> 1) * 32 + 16 * (ks & 1) + 4 * hf;
-        u32x4 w;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + base);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + base + 8);
-        w[0] = lo[0];
-        w[1] = lo[1];
-        w[2] = hi[0];
-        w[3] = hi[1];
-        o[dt] = mfma(__builtin_bit_cast(bf16x8, w), pb[ks], o[dt]);
+      for (int dt = 0; dt < kD / 32; ++dt) {
+        const uint16_t* vrow = Vt + (dt * 32 + l32) * kVP + base;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+        va[dt] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) o[dt] = mfma(va[dt], pb[ks], o[dt]);
     }
     __syncthreads();
   }

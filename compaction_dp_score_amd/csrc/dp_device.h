@@ -47,6 +47,14 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
   return (t + ((n - t) >> 1)) >> (f.l - 1);
 }
 
+// A read through the constant address space: a wave-uniform address becomes a
+// scalar load.  Only for arrays that the kernel reading them does not write
+// (the scalar cache is not kept coherent with the kernel's own stores).
+template <class T>
+__device__ __forceinline__ T uniform_load(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32.  Widening is exact.  Narrowing rounds to nearest, ties to
 // even, and keeps NaN a quiet NaN.

@@ -22,6 +22,7 @@
 namespace dp {
 namespace {
 
+
 struct GatherArgs {
   const void* const* k_src;
   const void* const* v_src;
@@ -64,17 +65,27 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
   const uint32_t j = fdiv(i, a.div_row);
   const uint32_t c = i - j * a.div_row.d;
   if (ROPE && !is_v) {
-    // K with the fused re-index.  Vector loads retire in issue order, so all
-    // lookups the rotation needs are requested before the HBM load of the
-    // data: the source row and the frame together, then the frame's phase
-    // step and {cos, sin} (L2 hits that return while the data is in flight).
-    // Every lane takes the same straight-line path; lanes outside the
-    // temporal block read entry 0 and keep their data.
+    // K with the fused re-index.  All lookups the rotation needs are requested
+    // before the HBM load of the data (vector loads retire in issue order):
+    // the source row and the frame (scalar loads when the wavefront lies in
+    // one row, as it does for rows of a multiple of 64 vectors), then the
+    // frame's phase step and {cos, sin} (L2 hits that return while the data is
+    // in flight).  Lanes outside the temporal block read entry 0 and keep
+    // their data.
     const uint32_t h = fdiv(c, a.div_head);
     const int tv = (int)(c - h * a.div_head.d) - a.rope.tv_begin;
     const bool in_block = tv >= 0 && tv < a.rope.tv_count;
-    const int32_t s = a.idx[j];
-    const int f = a.row_frame[j];
+    const uint32_t j0 = __builtin_amdgcn_readfirstlane(j);
+    const bool one_row = __builtin_amdgcn_ballot_w64(j != j0) == 0;
+    int32_t s;
+    int f;
+    if (one_row) {
+      s = uniform_load(a.idx + j0);
+      f = uniform_load(a.row_frame + j0);
+    } else {
+      s = a.idx[j];
+      f = a.row_frame[j];
+    }
     const bool sv = (uint32_t)s < (uint64_t)a.src_rows;   // out-of-range entries are skipped
     const bool fv = (uint32_t)f < (uint32_t)a.rope.n_frames;
     const int fc = fv ? f : 0;

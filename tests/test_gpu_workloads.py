@@ -326,3 +326,97 @@ def test_tiny_workload_every_row(reversed_):
     # the sink chunk and the window are kept, whatever the criterion
     assert np.all(want["keep"][:w.sink_len] == 1) and np.all(want["keep"][T - w.window_len:] == 1)
     print("tiny (reversed=%s): %d of %d kept, PR %.4f" % (reversed_, n, T, oracle.pr(n, T)))
+
+
+def test_steady_step_full_size():
+    """The steady-state step of the one-minute rollout in the ring layout, as
+    bench.py times it: 40 x 40 x 128 bf16, [sink | 4 ring slots | history of
+    the retained rows of chunks 1-55 | room]; chunk 56 leaves the window for
+    q0 = 240.  The sink and history move by the uniform step 3.5 frames
+    (dp_rope_shift), the leaving chunk's kept rows are appended with their
+    first re-index fused.  Sampled rows of three layers against the oracle."""
+    dev = device()
+    w = dpsynth.WORKLOADS["reindex"]
+    L, H, D, C, tpf = w.n_layers, w.n_heads, w.head_dim, w.chunk_tokens, w.tokens_per_frame
+    hist_rows = np.flatnonzero(dpsynth.retained_keep(w)[C:56 * C]) + C
+    n_hist = hist_rows.shape[0]
+    hb = 5 * C
+    cap = hb + n_hist + C
+    slot_begin = C
+    rf = np.full(cap, -1, np.int32)
+    rf[:C] = np.arange(C) // tpf
+    rf[C:hb] = (56 * C + np.arange(4 * C)) // tpf
+    rf[hb:hb + n_hist] = hist_rows // tpf
+    ks = _fill(dev, w, cap, range(L), dpsynth.STREAM_K)
+    vs = _fill(dev, w, cap, range(L), dpsynth.STREAM_V)
+    we = dpsynth.WORKLOADS["eviction"]
+    x0, xf = dpsynth.score_inputs(we)
+    widx = oracle.compact(oracle.mask(oracle.score_f32(x0, xf, we.d), C, 0, 0, 0, C, w.gamma))
+    n = widx.shape[0]
+    host = _rope_host(w, q0=w.q0 - 4)                 # phases after the previous step (q0 = 236)
+    phase0 = _tables(host)[3]
+    host = dict(host, q0=w.q0, frame_phase=phase0)
+    rd = _rope_dev(host, dev)
+    # device step
+    kv = dp.dp_kv_inplace()
+    ak, av = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
+    kv.k_layers, kv.v_layers = ak.data_ptr(), av.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dp.DP_BF16
+    kv.capacity = cap
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    keep = torch.empty(C, dtype=torch.uint8, device=dev)
+    idx = torch.empty(C, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64,
+                        device=dev)
+    dp.dp_score_index(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev), we.d, we.d,
+                      dp.make_policy(C, 0, 0, 0, C, w.gamma), None, keep, idx, nk, None, None,
+                      ws_si, err)
+    tail = torch.tensor([hb + n_hist], dtype=torch.int64, device=dev)
+    rf_d = torch.from_numpy(rf).to(dev)
+    ws_s = torch.empty(dp.dp_rope_shift_workspace_bytes(w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    step = 4 * (1 - 1 / w.rope_factor)
+    dp.dp_rope_shift(ak, L, H, D, dp.DP_BF16, 0, C, None, rd["theta"], 0, w.rope_pairs, step, ws_s)
+    dp.dp_rope_shift(ak, L, H, D, dp.DP_BF16, hb, cap, tail, rd["theta"], 0, w.rope_pairs, step,
+                     ws_s)
+    rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
+                        host["inv_factor"])
+    ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+    dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf_d, rope, ws_r)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and nk.item() == n and tail.item() == hb + n_hist + n
+    tables = _tables(host)
+    assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
+    uniform = oracle.rope_uniform(host["theta"], step)
+    old_rows = np.concatenate([_sample_rows(C, [], k=16, seed=2),
+                               hb + _sample_rows(n_hist, [], k=32, seed=3)])
+    ring_rows = C + _sample_rows(4 * C, [C, 2 * C, 3 * C], k=8, seed=4)
+    app = _sample_rows(n, [], k=24, seed=5)
+    src = slot_begin + widx[app]
+    assert np.array_equal(rf_d.cpu().numpy()[hb + n_hist + app], rf[src])
+    inexact = 0
+    for l in (0, 19, L - 1):
+        got = bits(ks[l][torch.from_numpy(old_rows).to(dev)])
+        want = _expected_rows(w, l, dpsynth.STREAM_K, old_rows, cap)
+        oracle.rope_rows(want, np.zeros(len(old_rows), np.int32), 0, uniform)
+        ok, worst, ne = keys_close(got, want, TOL_BF16)
+        assert ok, ("old keys", l, worst)
+        inexact += ne
+        got = bits(ks[l][torch.from_numpy(ring_rows).to(dev)])
+        assert np.array_equal(got, _expected_rows(w, l, dpsynth.STREAM_K, ring_rows, cap)), l
+        got = bits(ks[l][torch.from_numpy(hb + n_hist + app).to(dev)])
+        want = _expected_rows(w, l, dpsynth.STREAM_K, src, cap)
+        oracle.rope_rows(want, rf[src], 0, tables)
+        ok, worst, ne = keys_close(got, want, TOL_BF16)
+        assert ok, ("appended keys", l, worst)
+        inexact += ne
+        got = bits(vs[l][torch.from_numpy(hb + n_hist + app).to(dev)])
+        assert np.array_equal(got, _expected_rows(w, l, dpsynth.STREAM_V, src, cap)), l
+    print("steady step: %d history rows, %d appended, %d non-identical sampled key elements"
+          % (n_hist, n, inexact))
+    del ks, vs
+    _free()

@@ -453,6 +453,52 @@ def test_attention_closed_forms():
     assert np.allclose(got[0], _f(v)[5], atol=1e-9)
 
 
+def test_attention_invariants_and_two_key_closed_form():
+    """Properties that fix softmax attention without restating it: the order of
+    keys does not matter; adding a vector c to every value row adds c to the
+    output (the weights sum to 1); a key listed twice weighs twice; with two
+    keys the weight of the first is the logistic function of the score gap."""
+    rng = np.random.default_rng(21)
+    nq, nk, H, D = 4, 37, 2, 16
+    q, k, v = _bf16(rng, (nq, H, D)), _bf16(rng, (nk, H, D)), _bf16(rng, (nk, H, D))
+    rows = np.arange(nq)
+    base = oracle.attention(q, k, v, rows, scale=0.25)
+    perm = rng.permutation(nk)
+    assert np.allclose(oracle.attention(q, k[perm], v[perm], rows, scale=0.25), base,
+                       rtol=1e-12, atol=1e-14)
+    # values on a grid of eighths, so that v and v + 1/2 are both exact in bf16
+    import torch
+    grid = rng.integers(-32, 33, (nk, H, D)) / 8.0
+
+    def as_bf16(x):
+        t = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+        assert np.array_equal(t.float().numpy().astype(np.float64), x)
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    vg = oracle.attention(q, k, as_bf16(grid), rows, scale=0.25)
+    vs = oracle.attention(q, k, as_bf16(grid + 0.5), rows, scale=0.25)
+    assert np.allclose(vs, vg + 0.5, rtol=1e-12, atol=1e-12)
+    # two keys: the logistic weight; listing key 0 twice adds log 2 to its score gap
+    k2, v2 = k[:2].copy(), v[:2].copy()
+    got = oracle.attention(q, k2, v2, rows, scale=0.25)
+    qf, kf, vf2 = _f(q), _f(k2), _f(v2)
+    for i in range(nq):
+        for h in range(H):
+            gap = 0.25 * (qf[i, h] @ kf[0, h] - qf[i, h] @ kf[1, h])
+            w0 = 1.0 / (1.0 + np.exp(-gap))                  # logistic weight of key 0
+            assert np.allclose(got[i, h], w0 * vf2[0, h] + (1 - w0) * vf2[1, h],
+                               rtol=1e-12, atol=1e-13)
+    k3 = np.concatenate([k2, k2[:1]])
+    v3 = np.concatenate([v2, v2[:1]])
+    got3 = oracle.attention(q, k3, v3, rows, scale=0.25)
+    for i in range(nq):
+        for h in range(H):
+            gap = 0.25 * (qf[i, h] @ kf[0, h] - qf[i, h] @ kf[1, h]) + np.log(2.0)
+            w0 = 1.0 / (1.0 + np.exp(-gap))
+            assert np.allclose(got3[i, h], w0 * vf2[0, h] + (1 - w0) * vf2[1, h],
+                               rtol=1e-12, atol=1e-13)
+
+
 def test_hs_attention_per_head_runs_against_numpy():
     """Each head of the chosen layer sees exactly its own run followed by the
     chunk rows; a head with no rows gives zeros (numpy float64 softmax)."""

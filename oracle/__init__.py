@@ -46,6 +46,8 @@ def lib():
         L.oracle_hs_offsets.argtypes = [P, i32, i32, P, P]
         L.oracle_hs_gather_layer.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_attention.argtypes = [P, P, P, P, i64, i64, i32, i32, ctypes.c_double, P]
+        L.oracle_attention_f64.argtypes = [P, P, P, P, i64, i64, i32, i32, ctypes.c_double, P]
+        L.oracle_rope_rows_f64.argtypes = [P, i64, i32, i32, i32, i32, P, P, P]
         L.oracle_pr.argtypes = [i64, i64]
         L.oracle_pr.restype = ctypes.c_double
         _lib = L
@@ -245,6 +247,8 @@ def attention(q, k, v, rows, n_kv=None, scale=None):
     """Attention of the listed query rows over keys [0, n_kv) (float64 result
     [len(rows), H, D]); q, k, v: [rows, H, D] bf16 bit patterns (uint16)."""
     q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    if q.dtype == np.float64 or k.dtype == np.float64 or v.dtype == np.float64:
+        return _attention_f64(q, k, v, rows, n_kv, scale)
     assert q.dtype == k.dtype == v.dtype == np.uint16
     H, D = q.shape[1], q.shape[2]
     n_kv = k.shape[0] if n_kv is None else n_kv
@@ -255,6 +259,41 @@ def attention(q, k, v, rows, n_kv=None, scale=None):
     out = np.empty((rows.shape[0], H, D), np.float64)
     lib().oracle_attention(_p(q), _p(k), _p(v), _p(rows), rows.shape[0], n_kv, H, D, scale, _p(out))
     return out
+
+
+def _f64(a):
+    """float64 values of bf16 bit patterns (uint16) or of a float array."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _attention_f64(q, k, v, rows, n_kv, scale):
+    """attention() over float64 values (bf16 inputs are widened exactly)."""
+    q, k, v = (np.ascontiguousarray(_f64(x)) for x in (q, k, v))
+    H, D = q.shape[1], q.shape[2]
+    n_kv = k.shape[0] if n_kv is None else n_kv
+    assert 1 <= n_kv <= k.shape[0] and v.shape[0] >= n_kv
+    rows = _c(rows, np.int64)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    out = np.empty((rows.shape[0], H, D), np.float64)
+    lib().oracle_attention_f64(_p(q), _p(k), _p(v), _p(rows), rows.shape[0], n_kv, H, D, scale,
+                               _p(out))
+    return out
+
+
+def rope_rows_f64(k, row_frame, pair_begin, step, theta):
+    """Exact float64 re-index of k [rows, H, D] (float64, in place): pair j of
+    row r rotated by theta_j * step[row_frame[r]]."""
+    assert k.dtype == np.float64 and k.flags.c_contiguous and k.ndim == 3
+    rf = _c(row_frame, np.int32)
+    st = _c(step, np.float64)
+    th = _c(theta, np.float64)
+    assert 2 * (pair_begin + th.shape[0]) <= k.shape[2]
+    lib().oracle_rope_rows_f64(_p(k), k.shape[0], k.shape[1], k.shape[2], pair_begin,
+                               th.shape[0], _p(rf), _p(st), _p(th))
+    return k
 
 
 def hs_attention(q, k_ragged, v_ragged, offsets, layer, rows, k_chunk=None, v_chunk=None,

@@ -365,6 +365,62 @@ void oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   }
 }
 
+/* Same attention over float64 inputs (q, k, v: [rows][H][D] doubles), for
+ * references that must not round the re-indexed keys to a storage type. */
+void oracle_attention_f64(const double* q, const double* k, const double* v,
+                          const int64_t* rows, int64_t n_rows, int64_t n_kv, int32_t H,
+                          int32_t D, double scale, double* out) {
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < n_rows * H; ++r) {
+    const int64_t qi = rows[r / H];
+    const int32_t h = (int32_t)(r % H);
+    const double* qv = q + (qi * H + h) * (int64_t)D;
+    double m = -INFINITY;
+    double* o = out + r * (int64_t)D;
+    for (int32_t c = 0; c < D; ++c) o[c] = 0.0;
+    double l = 0.0;
+    for (int64_t j = 0; j < n_kv; ++j) {
+      const double* kv = k + (j * H + h) * (int64_t)D;
+      double s = 0.0;
+      for (int32_t c = 0; c < D; ++c) s += qv[c] * kv[c];
+      s *= scale;
+      const double* vv = v + (j * H + h) * (int64_t)D;
+      if (s > m) {
+        double corr = exp(m - s);
+        l *= corr;
+        for (int32_t c = 0; c < D; ++c) o[c] *= corr;
+        m = s;
+      }
+      double p = exp(s - m);
+      l += p;
+      for (int32_t c = 0; c < D; ++c) o[c] += p * vv[c];
+    }
+    for (int32_t c = 0; c < D; ++c) o[c] /= l;
+  }
+}
+
+/* Exact re-index in float64 [DeCoPrune page, 무엇과 다른가]: pair j of every
+ * head of row r rotated by theta_j * step[row_frame[r]], with no rounding to a
+ * storage type (reference for paths that rotate keys and queries differently). */
+void oracle_rope_rows_f64(double* k, int64_t n_rows, int32_t n_heads, int32_t head_dim,
+                          int32_t pair_begin, int32_t n_pairs, const int32_t* row_frame,
+                          const double* step, const double* theta) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const double d = step[row_frame[r]];
+    if (d == 0.0) continue;
+    for (int32_t h = 0; h < n_heads; ++h) {
+      double* x = k + (r * n_heads + h) * (int64_t)head_dim;
+      for (int32_t j = 0; j < n_pairs; ++j) {
+        const double c = cos(theta[j] * d), sn = sin(theta[j] * d);
+        const double a = x[2 * (pair_begin + j)], b = x[2 * (pair_begin + j) + 1];
+        x[2 * (pair_begin + j)] = a * c - b * sn;
+        x[2 * (pair_begin + j) + 1] = a * sn + b * c;
+      }
+    }
+  }
+}
+
 /* ---------------------------------------------------------------------- *
  * Pruning ratio [DeCoPrune page, 어떻게 쓰나]: 1 - visible / FullKV positions.
  * ---------------------------------------------------------------------- */

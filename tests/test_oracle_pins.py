@@ -331,6 +331,44 @@ def test_steady_state_phase_step_is_uniform():
         ph = ph_new
 
 
+def test_compressed_axis_decomposition():
+    """Past the knee, t~ = q0 - knee - (q0 - t - knee)/c splits into a part of
+    the key alone, t/c, and a part the same for every such key,
+    A = (1 - 1/c)(q0 - knee) (exact rationals), so keys can be kept at phase t/c
+    and the query rotated back by A; within the knee t~ = t."""
+    for q0, knee, c in ((240, 12, 8), (20, 12, 8), (8, 2, 4), (41, 5, 3)):
+        A = (1 - Fraction(1, c)) * (q0 - knee)
+        for t in range(q0):
+            tn = _t_new_exact(q0, knee, Fraction(c), t)
+            if q0 - t > knee:
+                assert tn == Fraction(t, c) + A, (q0, t)
+            else:
+                assert tn == t, (q0, t)
+
+
+def test_rope_rows_f64_invariants():
+    """The float64 re-index: rotations compose, pair norms are kept, and it
+    agrees with the fp32-storage re-index within fp32 rounding."""
+    rng = np.random.default_rng(22)
+    theta = dpsynth.rope_theta(12)
+    k = rng.standard_normal((30, 2, 32))
+    rf = (np.arange(30) // 3).astype(np.int32)
+    d1 = rng.uniform(-20, 20, 10)
+    d2 = rng.uniform(-20, 20, 10)
+    a = oracle.rope_rows_f64(oracle.rope_rows_f64(k.copy(), rf, 2, d1, theta), rf, 2, d2, theta)
+    b = oracle.rope_rows_f64(k.copy(), rf, 2, d1 + d2, theta)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+    norm = lambda x: x[..., 4:28:2] ** 2 + x[..., 5:28:2] ** 2
+    assert np.allclose(norm(a), norm(k), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(a[..., :4], k[..., :4]) and np.array_equal(a[..., 28:], k[..., 28:])
+    tab = oracle.rope_uniform(theta, np.float32(3.5))
+    k32 = k.astype(np.float32)
+    g = oracle.rope_rows(k32.copy(), np.zeros(30, np.int32), 2, tab).astype(np.float64)
+    e = oracle.rope_rows_f64(k32.astype(np.float64), np.zeros(30, np.int32), 2,
+                             np.array([3.5]), theta.astype(np.float32).astype(np.float64))
+    assert np.max(np.abs(g - e)) < 1e-5
+
+
 def test_uniform_shift_matches_per_frame_rows():
     """A uniform step over rows of many frames is the per-frame re-index with
     every frame's step equal to it (bitwise), and the float64 rotation."""

@@ -19,11 +19,15 @@ gather) timed with HIP events on its stream, the index phase timed both as
 one launch and as dp_score_mask + dp_compact_index, and the CPU oracle timed
 on a bounded layer sample of the same workload on the host cores.
 
-Other workloads (--workload reindex | prefix | hs | append | attention |
-hs_attention) time the other shapes; "append" is the same eviction step in the
-ring layout, where only the leaving chunk's kept rows move and the old keys
-are re-indexed in place; the attention workloads time the next chunk's
-attention over the compacted (or ragged HS) cache in TFLOP/s.
+Other workloads (--workload reindex | prefix | hs | append | steady |
+steady_lazy | attention | hs_attention | attention_lag) time the other shapes;
+"append" is the same eviction step in the ring layout, where only the leaving
+chunk's kept rows move and the old keys are re-indexed in place; "steady" is a
+later step of the one-minute rollout in that layout (old keys moved by one
+uniform phase step), "steady_lazy" the same step with the old keys on the
+compressed time axis (none rewritten); the attention workloads time the next
+chunk's attention over the compacted (ragged HS, or compressed-axis) cache in
+TFLOP/s.
 """
 import argparse
 import json
@@ -51,6 +55,8 @@ KERNELS = {
     "attention": ("attn_fwd_kernel", ("attention.hip", "dp_device.h")),
     "hs_attention": ("attn_fwd_kernel", ("attention.hip", "dp_device.h")),
     "steady": ("shift_kernel", ("rope.hip", "dp_device.h")),
+    "steady_lazy": ("append_kernel", ("append.hip", "dp_device.h")),
+    "attention_lag": ("attn_fwd_kernel", ("attention.hip", "dp_device.h")),
 }
 
 
@@ -65,7 +71,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="eviction",
                     choices=["eviction", "reindex", "prefix", "hs", "append", "attention",
-                             "hs_attention", "steady"])
+                             "hs_attention", "steady", "steady_lazy", "attention_lag"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullkv", action="store_true",
                     help="attention workloads: skip the context timing over the uncompacted "
@@ -92,7 +98,7 @@ def kernel_sources_sha(workload):
 
 def profile_flags(workload):
     """bench.py flags of the profiling runs of a workload."""
-    extra = " --no-fullkv" if workload in ("attention", "hs_attention") else ""
+    extra = " --no-fullkv" if workload in ("attention", "hs_attention", "attention_lag") else ""
     return "--no-cpu-baseline" + extra
 
 
@@ -350,6 +356,8 @@ def flops_record(args, acc, ms, k_ms):
                         "flops_per_launch": acc["flops_per_launch"],
                         "launch_ms": round(k_ms, 4)}}
     rec["copy_ceiling_gbs"] = round(copy_ceiling(torch.device("cuda:0"), CALIB_BYTES), 2)
+    if acc.get("context"):
+        rec["context"] = acc["context"]
     if acc.get("full_ms"):
         rec["fullkv"] = {"ms": round(acc["full_ms"], 4),
                          "tflops": round(acc["full_flops"] / (acc["full_ms"] * 1e-3) / 1e12, 2),
@@ -647,6 +655,197 @@ def setup_steady(dev):
                             "history_rows": int(n_hist), "scored_tokens": C, "kept_tokens": n,
                             "shifted_head_rows": shifted, "uniform_step_frames": step_frames,
                             "rope_pairs": w.rope_pairs, "q0": w.q0})
+
+    return run, gt, accounting, None
+
+
+def setup_steady_lazy(dev):
+    """The steady-state step of setup_steady on the compressed time axis: the
+    old keys (sink and history) carry the phase t/c since they passed the
+    knee, so no old key is rewritten when q0 advances; attention turns the
+    query back by the common term instead (dp_attention_lag).  Per step: the
+    leaving chunk 56 is scored and indexed in one launch, dp_rope_prepare
+    writes the per-frame tables (axis DP_AXIS_COMPRESSED: chunk 56's frames
+    move from t to t/c, every other frame stays) and dp_append_kept appends
+    its kept rows with that re-index fused.  The tail, the slot's row frames
+    and the phase table are restored before each step.  For context the same
+    step on the page's axis (two uniform shifts over the 32.4 GB of old keys,
+    then the same append) is timed on the same buffers."""
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    w = dpsynth.WORKLOADS["reindex"]
+    H, D, L, C, tpf = w.n_heads, w.head_dim, w.n_layers, w.chunk_tokens, w.tokens_per_frame
+    keep_full = dpsynth.retained_keep(w)
+    hist_rows = np.flatnonzero(keep_full[C:56 * C]) + C          # retained rows of chunks 1..55
+    n_hist = hist_rows.shape[0]
+    hb = 5 * C                                                    # sink + 4 ring slots
+    cap = hb + n_hist + C
+    slot_begin = C                                                # ring slot 0: chunk 56
+    rf_host = np.full(cap, -1, np.int32)
+    rf_host[:C] = np.arange(C) // tpf
+    rf_host[C:hb] = (56 * C + np.arange(4 * C)) // tpf
+    rf_host[hb:hb + n_hist] = hist_rows // tpf
+    ks = _fill_layers(dev, w, cap, range(L), dpsynth.STREAM_K)
+    vs = _fill_layers(dev, w, cap, range(L), dpsynth.STREAM_V)
+    x0, xf = dpsynth.score_inputs(dpsynth.WORKLOADS["eviction"])  # one chunk of scores
+    x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
+    rf0 = torch.from_numpy(rf_host).to(dev)
+    rf = rf0.clone()
+    kv = dp.dp_kv_inplace()
+    arr_k, arr_v = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
+    kv.k_layers, kv.v_layers = arr_k.data_ptr(), arr_v.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dp.DP_BF16
+    kv.capacity = cap
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    tail0 = torch.tensor([hb + n_hist], dtype=torch.int64, device=dev)
+    tail = tail0.clone()
+    pol = dp.make_policy(C, 0, 0, 0, C, w.gamma)
+    keep = torch.empty(C, dtype=torch.uint8, device=dev)
+    idx = torch.empty(C, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64, device=dev)
+    theta = torch.from_numpy(dpsynth.rope_theta(w.rope_pairs, w.rope_base)).to(dev)
+    ft, fp = dpsynth.frame_tables(w)
+    ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(fp).to(dev)
+    ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    # the phases after the previous step (q0 = 236) on the compressed axis
+    dp.dp_rope_prepare(dp.make_rope(theta, ftd, fpd, w.q0 - 4, w.rope_knee, 1.0 / w.rope_factor,
+                                    axis=dp.DP_AXIS_COMPRESSED), D, dp.DP_BF16, ws_r)
+    phase0 = fpd.clone()
+    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
+                        axis=dp.DP_AXIS_COMPRESSED)
+    page_rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    step_frames = 4 * (1.0 - 1.0 / w.rope_factor)                 # 3.5
+    ws_s = torch.empty(dp.dp_rope_shift_workspace_bytes(w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    gt = Timer()
+    keep_alive = [arr_k, arr_v]
+
+    def restore():
+        tail.copy_(tail0)
+        rf.copy_(rf0)
+        fpd.copy_(phase0)
+
+    def run(timed):
+        restore()
+        dp.dp_score_index(x0d, xfd, w.d, w.d, pol, None, keep, idx, nk, None, None, ws_si, err)
+        dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+        if timed:
+            gt.start()
+        dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf, rope, ws_r)
+        if timed:
+            gt.stop()
+
+    def page_axis_ms(reps=5):
+        def once():
+            restore()
+            dp.dp_score_index(x0d, xfd, w.d, w.d, pol, None, keep, idx, nk, None, None, ws_si,
+                              err)
+            dp.dp_rope_shift(arr_k, L, H, D, dp.DP_BF16, 0, C, None, theta, 0, w.rope_pairs,
+                             step_frames, ws_s)
+            dp.dp_rope_shift(arr_k, L, H, D, dp.DP_BF16, hb, cap, tail, theta, 0, w.rope_pairs,
+                             step_frames, ws_s)
+            dp.dp_rope_prepare(page_rope, D, dp.DP_BF16, ws_r)
+            dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf, page_rope, ws_r)
+        once()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            once()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def accounting():
+        assert keep_alive and err.item() == 0
+        n = int(nk.item())
+        append = n * H * D * 2 * 2 * 2 * L
+        score = C * (8 * w.d + 1)
+        return dict(n_kept=n, gather_bytes=append, step_bytes=append + score, n_scored=C,
+                    context={"page_axis_step_ms": round(page_axis_ms(), 4)},
+                    config={"workload": "steady_lazy",
+                            "layout": "sink | ring of 4 chunk slots | history",
+                            "time_axis": "compressed (old keys at phase t/c)",
+                            "layers": L, "heads": H, "head_dim": D, "kv_dtype": "bf16",
+                            "history_rows": int(n_hist), "scored_tokens": C, "kept_tokens": n,
+                            "appended_bytes": append, "rope_pairs": w.rope_pairs, "q0": w.q0})
+
+    return run, gt, accounting, None
+
+
+def setup_attention_lag(dev, layers=4):
+    """Attention of the next chunk (6,240 queries, 40 heads x 128, bf16) over
+    the same 83,412-row cache as the attention workload, in the ring layout
+    [sink | window chunks 57-59 + the chunk | history: retained rows of chunks
+    1-56] with the old keys on the compressed time axis (re-indexed once to
+    phase t/c, here in the setup): one dp_attention_lag launch per layer, the
+    query turned back by (1 - 1/c)(q0 - knee) = 199.5 frames for the sink and
+    the history.  For context dp_attention over the same buffers is timed
+    once per layer (the cost of the lag)."""
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    w = dpsynth.WORKLOADS["reindex"]
+    H, D, C = w.n_heads, w.head_dim, w.chunk_tokens
+    rf_host, plain_begin, plain_end = dpsynth.ring_layout(w)
+    n = rf_host.shape[0]
+    q = torch.empty((C, H, D), dtype=torch.bfloat16, device=dev)
+    dpsynth.kv_fill_device(q, "bf16", w.seed, 3, 0, C, H * D)
+    ks = _fill_layers(dev, w, n, range(layers), dpsynth.STREAM_K)
+    vs = _fill_layers(dev, w, n, range(layers), dpsynth.STREAM_V)
+    theta = torch.from_numpy(dpsynth.rope_theta(w.rope_pairs, w.rope_base)).to(dev)
+    n_frames = w.n_frames + w.frames_per_chunk           # through the chunk's own frames
+    ft = np.arange(n_frames, dtype=np.float32)
+    ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(ft.copy()).to(dev)
+    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
+                        axis=dp.DP_AXIS_COMPRESSED)
+    ws_r = torch.empty(dp.dp_rope_workspace_bytes(n_frames, w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    rf = torch.from_numpy(rf_host).to(dev)
+    arr_k = dp.ptr_array(ks, dev)
+    dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+    dp.dp_rope_apply(arr_k, layers, H, D, dp.DP_BF16, 0, n, None, rf, rope, ws_r)
+    lag = (1.0 - 1.0 / w.rope_factor) * (w.q0 - w.rope_knee)
+    o = torch.empty_like(q)
+    scale = 1.0 / float(np.sqrt(D))
+    gt = Timer()
+
+    def launch(l):
+        dp.dp_attention_lag(q, ks[l], vs[l], o, C, n, None, plain_begin, plain_end, theta, 0,
+                            w.rope_pairs, lag, H, D, dp.DP_BF16, scale)
+
+    def run(timed):
+        for l in range(layers):
+            if timed and l == 0:
+                gt.start()
+            launch(l)
+            if timed and l == 0:
+                gt.stop()
+
+    def dense_ms(reps=3):
+        dp.dp_attention(q, ks[0], vs[0], o, C, n, None, H, D, dp.DP_BF16, scale)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dp.dp_attention(q, ks[0], vs[0], o, C, n, None, H, D, dp.DP_BF16, scale)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def accounting():
+        flops = 4.0 * C * n * D * H
+        rec = dict(n_kept=n, gather_bytes=None, flops_per_launch=flops,
+                   step_flops=flops * layers, n_scored=0,
+                   metric="attention TFLOP/s over the compacted cache, old keys on the "
+                          "compressed time axis",
+                   config={"workload": "attention_lag", "layers": layers, "heads": H,
+                           "head_dim": D, "dtype": "bf16", "queries": C, "kv_rows": n,
+                           "plain_rows": [plain_begin, plain_end], "lag_frames": lag,
+                           "rope_pairs": w.rope_pairs})
+        if not ARGS.no_fullkv:
+            rec["context"] = {"dense_attention_ms": round(dense_ms(), 4)}
+        return rec
 
     return run, gt, accounting, None
 
@@ -991,7 +1190,8 @@ def main():
     dev = torch.device("cuda:0")
     setups = {"eviction": setup_eviction, "reindex": setup_reindex, "prefix": setup_prefix,
               "hs": setup_hs, "append": setup_append, "attention": setup_attention,
-              "hs_attention": setup_hs_attention, "steady": setup_steady}
+              "hs_attention": setup_hs_attention, "steady": setup_steady,
+              "steady_lazy": setup_steady_lazy, "attention_lag": setup_attention_lag}
     if args.workload not in setups:
         print("workload %s is not wired into bench.py yet" % args.workload, file=sys.stderr)
         sys.exit(2)

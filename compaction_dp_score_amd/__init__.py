@@ -28,6 +28,7 @@ DP_OK, DP_EINVAL, DP_EALIGN, DP_ERANGE, DP_ECAPACITY, DP_EHIP, DP_EUNSUPPORTED, 
 DP_F32, DP_BF16 = 0, 1
 DP_MODE_SCORE, DP_MODE_STREAMING = 0, 1
 DP_HS_MAX_CLASSES = 8
+DP_AXIS_PAGE, DP_AXIS_COMPRESSED = 0, 1
 
 _P = ctypes.c_void_p
 _i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -47,7 +48,7 @@ class dp_mask_policy(ctypes.Structure):
 
 class dp_rope(ctypes.Structure):
     _fields_ = [("pair_begin", _i32), ("n_pairs", _i32), ("theta", _P), ("n_frames", _i32),
-                ("reserved", _i32), ("frame_t", _P), ("frame_phase", _P), ("q0", _f32),
+                ("axis", _i32), ("frame_t", _P), ("frame_phase", _P), ("q0", _f32),
                 ("knee", _f32), ("inv_factor", _f32)]
 
 
@@ -109,6 +110,8 @@ _lib_si_ws = _sig("dp_score_index_workspace_bytes", [_i64], ctypes.c_size_t)
 _lib_score_index = _sig("dp_score_index", [_P, _P, _i32, _i64, ctypes.POINTER(dp_mask_policy), _P,
                                            _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P])
 _lib_attention = _sig("dp_attention", [_P, _P, _P, _P, _i64, _i64, _P, _i32, _i32, _i32, _f32, _P])
+_lib_attention_lag = _sig("dp_attention_lag", [_P, _P, _P, _P, _i64, _i64, _P, _i64, _i64, _P,
+                                                _i32, _i32, _f32, _i32, _i32, _i32, _f32, _P])
 _lib_hs_attention = _sig("dp_hs_attention", [_P, _P, _P, _i64, _P, _i32, _P, _P, _i64, _P, _i64,
                                               _i32, _i32, _i32, _f32, _P])
 _lib_pr_add = _sig("dp_pr_add", [ctypes.POINTER(dp_pr_counter), _i64, _i64])
@@ -119,7 +122,7 @@ EXPORTED = ["dp_abi_version", "dp_status_str", "dp_last_error", "dp_score_mask",
             "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_rope_shift_workspace_bytes",
             "dp_rope_shift", "dp_append_kept",
             "dp_hs_offsets", "dp_hs_gather_kv",
-            "dp_hs_rope_reindex", "dp_attention", "dp_hs_attention", "dp_score_index_workspace_bytes",
+            "dp_hs_rope_reindex", "dp_attention", "dp_attention_lag", "dp_hs_attention", "dp_score_index_workspace_bytes",
             "dp_score_index", "dp_pr_add", "dp_pr_value"]
 
 
@@ -170,14 +173,16 @@ def ptr_array(tensors, device):
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
 
 
-def make_rope(theta, frame_t, frame_phase, q0, knee, inv_factor, pair_begin=0):
-    """A dp_rope over device tensors theta [n_pairs], frame_t/frame_phase [n_frames]."""
+def make_rope(theta, frame_t, frame_phase, q0, knee, inv_factor, pair_begin=0, axis=0):
+    """A dp_rope over device tensors theta [n_pairs], frame_t/frame_phase [n_frames].
+
+    axis: DP_AXIS_PAGE (0) or DP_AXIS_COMPRESSED (1)."""
     r = dp_rope()
     r.pair_begin = pair_begin
     r.n_pairs = theta.numel()
     r.theta = theta.data_ptr()
     r.n_frames = frame_t.numel()
-    r.reserved = 0
+    r.axis = int(axis)
     r.frame_t = frame_t.data_ptr()
     r.frame_phase = frame_phase.data_ptr()
     r.q0, r.knee, r.inv_factor = float(q0), float(knee), float(inv_factor)
@@ -317,6 +322,14 @@ def dp_attention(q, k, v, o, n_q, kv_capacity, n_kv, n_heads, head_dim, dtype, s
                  stream=None):
     _check(_lib_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(n_q), int(kv_capacity),
                           _ptr(n_kv), n_heads, head_dim, dtype, float(scale), _stream(stream)))
+
+
+def dp_attention_lag(q, k, v, o, n_q, kv_capacity, n_kv, plain_begin, plain_end, theta,
+                     pair_begin, n_pairs, lag, n_heads, head_dim, dtype, scale, stream=None):
+    _check(_lib_attention_lag(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(n_q), int(kv_capacity),
+                              _ptr(n_kv), int(plain_begin), int(plain_end), _ptr(theta),
+                              int(pair_begin), int(n_pairs), float(lag), n_heads, head_dim, dtype,
+                              float(scale), _stream(stream)))
 
 
 def dp_hs_attention(q, k_ragged, v_ragged, ragged_capacity, offsets, layer, k_chunk, v_chunk,

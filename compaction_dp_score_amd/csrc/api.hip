@@ -52,8 +52,10 @@ dp_status check_shape(int32_t n_layers, int32_t n_heads, int32_t head_dim, int32
 
 dp_status check_rope(const dp_rope* r, int32_t head_dim, int32_t dtype, const void* ws,
                      size_t ws_bytes, const char* who) {
-  if (r->n_pairs < 1 || r->pair_begin < 0 || r->n_frames < 1 || r->reserved != 0)
-    return fail(DP_EINVAL, "%s: rope needs n_pairs >= 1, pair_begin >= 0, n_frames >= 1", who);
+  if (r->n_pairs < 1 || r->pair_begin < 0 || r->n_frames < 1 ||
+      (r->axis != DP_AXIS_PAGE && r->axis != DP_AXIS_COMPRESSED))
+    return fail(DP_EINVAL, "%s: rope needs n_pairs >= 1, pair_begin >= 0, n_frames >= 1 and a "
+                           "known axis", who);
   if (2 * ((int64_t)r->pair_begin + r->n_pairs) > head_dim)
     return fail(DP_ERANGE, "%s: temporal pairs [%d, %d) exceed head_dim/2 = %d", who,
                 r->pair_begin, r->pair_begin + r->n_pairs, head_dim / 2);
@@ -495,6 +497,41 @@ dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int
   (void)hipGetLastError();
   dp_status st = launch_attention(q, k, v, o, n_q, kv_capacity, n_kv, n_heads, scale,
                                   (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+dp_status dp_attention_lag(const void* q, const void* k, const void* v, void* o, int64_t n_q,
+                           int64_t kv_capacity, const int64_t* n_kv, int64_t plain_begin,
+                           int64_t plain_end, const float* theta, int32_t pair_begin,
+                           int32_t n_pairs, float lag, int32_t n_heads, int32_t head_dim,
+                           int32_t dtype, float scale, void* stream) {
+  if (!q || !k || !v || !o || !theta)
+    return fail(DP_EINVAL, "dp_attention_lag: q, k, v, o and theta are required");
+  if (dtype != DP_BF16 || head_dim != 128)
+    return fail(DP_EUNSUPPORTED, "dp_attention_lag: only bf16 with head_dim 128 is implemented");
+  if (n_heads < 1 || n_heads > kMaxAttnHeads || n_q < 0 || kv_capacity < 0 || n_q >= kMaxRows ||
+      kv_capacity >= kMaxRows)
+    return fail(DP_ERANGE, "dp_attention_lag: need 1 <= n_heads <= 65536 and 0 <= n_q, "
+                           "kv_capacity < 2^31");
+  if ((n_q + 127) / 128 * (int64_t)n_heads >= kMaxVec)
+    return fail(DP_ERANGE, "dp_attention_lag: too many query tiles for one launch");
+  if (plain_begin < 0 || plain_end < plain_begin)
+    return fail(DP_ERANGE, "dp_attention_lag: need 0 <= plain_begin <= plain_end");
+  if (n_pairs < 1 || pair_begin < 0 || 2 * ((int64_t)pair_begin + n_pairs) > head_dim)
+    return fail(DP_ERANGE, "dp_attention_lag: temporal pairs [%d, %d + %d) outside head_dim/2",
+                pair_begin, pair_begin, n_pairs);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (n_kv && !aligned(n_kv, 8)) || !aligned(theta, 4))
+    return fail(DP_EALIGN, "dp_attention_lag: tensors must be 16-byte aligned");
+  if (!(scale > 0.0f && scale <= 3.0e38f))
+    return fail(DP_EINVAL, "dp_attention_lag: scale must be positive and finite");
+  if (!(lag >= -3.0e38f && lag <= 3.0e38f))
+    return fail(DP_EINVAL, "dp_attention_lag: lag must be finite");
+  (void)hipGetLastError();
+  dp_status st = launch_attention_lag(q, k, v, o, n_q, kv_capacity, n_kv, plain_begin, plain_end,
+                                      theta, pair_begin, n_pairs, lag, n_heads, scale,
+                                      (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }

@@ -25,6 +25,14 @@
 // for DeCoPrune-HS, the head's own run of rows in the packed per-head cache
 // (offsets from dp_hs_offsets, consecutive rows head_dim apart); segment 1 is
 // an optional dense block (the chunk's own keys next to a ragged history).
+//
+// Compressed time axis (dp_attention_lag): keys past the RoPE knee carry the
+// phase t/c instead of t~ = t/c + A, A the same for all of them, so their
+// scores need the query turned back by A on the temporal pairs.  The dense
+// cache is then streamed as three segments: the lagged rows before the plain
+// range, the lagged rows after it (both against the rotated query) and the
+// plain range (against the query as given); the query fragment is rebuilt
+// once, when the stream reaches the plain range.
 #include "dp_internal.h"
 
 namespace dp {
@@ -43,6 +51,8 @@ constexpr int kVP = kBN + 4;     // V^T tile row pitch (bf16 elements): 34 dword
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor, dword 3
 
+enum { kDense = 0, kRagged = 1, kLag = 2 };
+
 struct AttnArgs {
   const uint16_t* q;
   uint16_t* o;
@@ -60,16 +70,38 @@ struct AttnArgs {
   int32_t n_qt;       // query tiles per head
   int32_t xcd_map;    // 1: group the query tiles of a head on one XCD
   float c;            // scale * log2(e)
+  // kLag: rows outside [plain_begin, plain_end) see the query rotated by
+  // -lag on pairs [pair_begin, pair_begin + n_pairs)
+  int64_t plain_begin;
+  int64_t plain_end;
+  const float* theta;
+  int32_t pair_begin;
+  int32_t n_pairs;
+  float lag;
 };
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <bool RAGGED>
+template <int MODE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
+  constexpr bool RAGGED = MODE == kRagged;
+  constexpr bool LAG = MODE == kLag;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * kKP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVP];
+  __shared__ f32x2 lag_cs[LAG ? kD / 2 : 1];
+  if constexpr (LAG) {
+    // {cos, sin} of the fp32 angle theta_j * (-lag), from fp64 sincos rounded to
+    // fp32: the table the in-place re-index builds for a phase change of -lag
+    for (int j = threadIdx.x; j < a.n_pairs; j += kBlock) {
+      const float ang = a.theta[j] * -a.lag;
+      double sd, cd;
+      sincos((double)ang, &sd, &cd);
+      lag_cs[j] = f32x2{(float)cd, (float)sd};
+    }
+    __syncthreads();
+  }
 
   int head, qt;
   if (a.xcd_map) {
@@ -123,26 +155,55 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     n0 = a.cap0;
     if (a.n_kv) n0 = max(min(n0, *a.n_kv), (int64_t)0);
   }
-  const int64_t n1 = RAGGED && a.k1 ? a.n1 : 0;
+  // kLag: rows [0, pa) and [pb, n) lagged, then [pa, pb) plain (segments 0, 1, 2)
+  const int64_t pa = LAG ? min(a.plain_begin, n0) : 0;
+  const int64_t pb = LAG ? min(max(a.plain_end, a.plain_begin), n0) : 0;
+  const int64_t n1 = RAGGED && a.k1 ? a.n1 : LAG ? n0 - pb : 0;
+  const int64_t n2 = pb - pa;
+  if (LAG) n0 = pa;
   const int64_t t0 = (n0 + kBN - 1) / kBN;
-  const int64_t n_tiles = t0 + (n1 + kBN - 1) / kBN;
+  const int64_t t01 = t0 + (n1 + kBN - 1) / kBN;   // first tile of segment 2
+  const int64_t n_tiles = t01 + (n2 + kBN - 1) / kBN;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
   const int64_t qi = (int64_t)qt * kBM + wave * 32 + l32;
   const bool qvalid = qi < a.n_q;
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qi][d] for d = 16 ds + 8 hf + e.
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qi][d] for d = 16 ds + 8 hf + e,
+  // i.e. pairs 8 ds + 4 hf + (0..3); with `lagged` the temporal pairs are rotated
+  // by -lag (fp32 products and sums rounded separately, then bf16 RNE).
   bf16x8 qb[kD / 16];
-  {
-    const uint16_t* qrow = a.q + (qvalid ? qi : 0) * a.row + (int64_t)head * kD;
+  // The wavefront's 32 query rows are read through one buffer descriptor that
+  // ends at the last valid query, so rows past n_q read as zeros; the lane
+  // offsets are recomputed at each call and hold no registers in between.
+  auto load_q = [&](bool lagged) {
+    const int64_t q_first = (int64_t)qt * kBM + wave * 32;
+    const int64_t q_rows = max(min(a.n_q - q_first, (int64_t)32), (int64_t)0);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.q + q_first * a.row + (int64_t)head * kD), 0, (int)(q_rows * a.row * 2),
+        kBufferWord3);
+    const int q_off = (int)(l32 * (a.row * 2) + hf * 16);
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
-      u32x4 r = {0u, 0u, 0u, 0u};
-      if (qvalid) r = *reinterpret_cast<const u32x4*>(qrow + ds * 16 + hf * 8);
+      u32x4 r = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, q_off + ds * 32,
+                                                                                0, 0));
+      if (LAG && lagged) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = ds * 8 + hf * 4 + u - a.pair_begin;
+          if (j >= 0 && j < a.n_pairs) {
+            const f32x2 cs = lag_cs[j];
+            float a2, b2;
+            rotate_pair(bf16_lo(r[u]), bf16_hi(r[u]), cs.x, cs.y, a2, b2);
+            r[u] = pack_bf16_hw(a2, b2);
+          }
+        }
+      }
       qb[ds] = __builtin_bit_cast(bf16x8, r);
     }
-  }
+  };
+  load_q(LAG && t01 > 0);
 
   f32x16 o[kD / 32];
 #pragma unroll
@@ -164,14 +225,30 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // row and whose size ends at the segment's last valid row, so rows past it
   // read as zeros without a per-lane branch (gfx9 buffer range check; the lane
   // offsets stay below 64 rows of the segment's stride, validated on the host).
+  // first key of tile t in its segment, and the segment's key count
+  // (every captured value is read before the selects: arms that each read a
+  // different captured variable get merged into one read at a selected
+  // address, which keeps the counts in memory and the tile base in VGPRs)
+  const int64_t n0c = n0;
+  auto tile_span = [&](int64_t t, int64_t& kv0, int64_t& n) {
+    const int64_t T0 = t0, T01 = t01, N0 = n0c, N1 = n1, N2 = n2;
+    const bool in2 = LAG && t >= T01;
+    const bool in1 = (RAGGED || LAG) && !in2 && t >= T0;
+    kv0 = (t - (in2 ? T01 : in1 ? T0 : 0)) * kBN;
+    n = in2 ? N2 : in1 ? N1 : N0;
+  };
   auto load_tile = [&](int64_t t) {
     const bool s1 = RAGGED && t >= t0;             // uniform per workgroup
     const uint16_t* kp = s1 ? a.k1 : a.k0;
     const uint16_t* vp = s1 ? a.v1 : a.v0;
     const int64_t stride = s1 ? a.row : stride0;
-    const int64_t base = s1 ? (int64_t)head * kD : base0;
-    const int64_t n = s1 ? n1 : n0;
-    const int64_t kv0 = (s1 ? t - t0 : t) * kBN;
+    int64_t base = s1 ? (int64_t)head * kD : base0;
+    if (LAG) {
+      const int64_t PA = pa, PB = pb, T0 = t0, T01 = t01;
+      base += (t >= T01 ? PA : t >= T0 ? PB : 0) * a.row;
+    }
+    int64_t kv0, n;
+    tile_span(t, kv0, n);
     const int64_t off = base + kv0 * stride;
     const uint32_t bytes = (uint32_t)(min(n - kv0, (int64_t)kBN) * stride * 2);
     const __amdgpu_buffer_rsrc_t rk =
@@ -179,19 +256,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)(vp + off), 0, (int)bytes, kBufferWord3);
     const uint32_t st2 = (uint32_t)stride * 2u;
+    // Only the first key's offset of each operand stays in a register between
+    // tiles; the empty asm stops the compiler from hoisting all eight offsets
+    // out of the tile loop, where they would hold eight VGPRs throughout.
+    uint32_t k_lo = key4 * st2 + ch * 16, v_lo = vkey4 * st2 + vch * 16;
+    asm volatile("" : "+v"(k_lo), "+v"(v_lo));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rk, (int)((key4 + u) * st2 + ch * 16), 0, 0));
+                                            rk, (int)(k_lo + u * st2), 0, 0));
       vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rv, (int)((vkey4 + u) * st2 + vch * 16), 0, 0));
+                                            rv, (int)(v_lo + u * st2), 0, 0));
     }
   };
   if (n_tiles > 0) load_tile(0);
   for (int64_t t = 0; t < n_tiles; ++t) {
-    const bool in1 = RAGGED && t >= t0;
-    const int64_t kv0 = (in1 ? t - t0 : t) * kBN;   // first key of the tile in its segment
-    const int64_t nkv = in1 ? n1 : n0;
+    int64_t kv0, nkv;                                // first key of the tile in its segment
+    tile_span(t, kv0, nkv);
+    if (LAG && t == t01 && t > 0) load_q(false);     // the plain range begins
     // ---- stage K (row-major) and V (transposed) of 64 keys in LDS ----
 #pragma unroll
     for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(Ks + (key4 + u) * kKP + ch * 8) = kr[u];
@@ -328,10 +410,12 @@ dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_hea
   a.c = scale * 1.4426950408889634f;
   const uint64_t blocks = (uint64_t)a.n_qt * n_heads;
   if (blocks == 0) return DP_OK;
-  if (a.off)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+  if (a.theta)
+    hipLaunchKernelGGL(attn_fwd_kernel<kLag>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+  else if (a.off)
+    hipLaunchKernelGGL(attn_fwd_kernel<kRagged>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<kDense>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
   return check_launch("attn_fwd_kernel");
 }
 
@@ -345,6 +429,25 @@ dp_status launch_attention(const void* q, const void* k, const void* v, void* o,
   a.v0 = reinterpret_cast<const uint16_t*>(v);
   a.n_kv = n_kv;
   a.cap0 = kv_cap;
+  return launch(a, q, o, n_q, n_heads, scale, s);
+}
+
+dp_status launch_attention_lag(const void* q, const void* k, const void* v, void* o,
+                               int64_t n_q, int64_t kv_cap, const int64_t* n_kv,
+                               int64_t plain_begin, int64_t plain_end, const float* theta,
+                               int32_t pair_begin, int32_t n_pairs, float lag, int32_t n_heads,
+                               float scale, hipStream_t s) {
+  AttnArgs a{};
+  a.k0 = reinterpret_cast<const uint16_t*>(k);
+  a.v0 = reinterpret_cast<const uint16_t*>(v);
+  a.n_kv = n_kv;
+  a.cap0 = kv_cap;
+  a.plain_begin = plain_begin;
+  a.plain_end = plain_end;
+  a.theta = theta;
+  a.pair_begin = pair_begin;
+  a.n_pairs = n_pairs;
+  a.lag = lag;
   return launch(a, q, o, n_q, n_heads, scale, s);
 }
 

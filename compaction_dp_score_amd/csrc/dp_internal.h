@@ -47,6 +47,11 @@ dp_status launch_append(const dp_kv_inplace& kv, int64_t slot_begin, int64_t slo
 dp_status launch_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
                            int64_t kv_cap, const int64_t* n_kv, int32_t n_heads, float scale,
                            hipStream_t s);
+dp_status launch_attention_lag(const void* q, const void* k, const void* v, void* o,
+                               int64_t n_q, int64_t kv_cap, const int64_t* n_kv,
+                               int64_t plain_begin, int64_t plain_end, const float* theta,
+                               int32_t pair_begin, int32_t n_pairs, float lag, int32_t n_heads,
+                               float scale, hipStream_t s);
 dp_status launch_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
                               int64_t ragged_capacity, const int64_t* head_offsets,
                               const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,

@@ -4,9 +4,10 @@
 // the temporal phase of the keys changes.
 //
 // rope_prepare_kernel: one wavefront per frame computes
-//   D = q0 - t, g(D), t~ = q0 - g(D), delta = t~ - p (p: phase the keys
-//   carry), and for each temporal pair j the {cos, sin} of theta_j * delta
-//   (fp32 angle, fp64 sincos, rounded to fp32); then p <- t~.
+//   D = q0 - t, g(D), t~ = q0 - g(D) (or, on the compressed axis, t/c past
+//   the knee), delta = t~ - p (p: phase the keys carry), and for each temporal
+//   pair j the {cos, sin} of theta_j * delta (fp32 angle, fp64 sincos, rounded
+//   to fp32); then p <- t~.
 // reindex_kernel: in place over every (row, head) of each layer, touching the
 //   128-byte lines that hold the temporal pairs; rows of frames with delta == 0
 //   are neither read nor written.  HBM-bound: the method needs
@@ -26,18 +27,21 @@ namespace {
 __global__ __launch_bounds__(64) void rope_prepare_kernel(
     const float* __restrict__ theta, int32_t n_pairs, int32_t pairs_padded,
     const float* __restrict__ frame_t, float* __restrict__ frame_phase, float q0, float knee,
-    float inv_factor, float* __restrict__ delta, f32x2* __restrict__ cs) {
+    float inv_factor, int axis, float* __restrict__ delta, f32x2* __restrict__ cs) {
   const int f = blockIdx.x;
   const float D = q0 - frame_t[f];
-  float gD;
-  if (D <= knee) {
-    gD = D;
+  float t_new;
+  if (D > knee && axis == DP_AXIS_COMPRESSED) {
+    t_new = frame_t[f] * inv_factor;    // t/c: the part of t~ that is the key's own
   } else {
-    float over = D - knee;
-    float squeezed = over * inv_factor;
-    gD = knee + squeezed;
+    float gD = D;
+    if (D > knee) {
+      float over = D - knee;
+      float squeezed = over * inv_factor;
+      gD = knee + squeezed;
+    }
+    t_new = q0 - gD;
   }
-  const float t_new = q0 - gD;
   const float dl = t_new - frame_phase[f];
   for (int j = threadIdx.x; j < pairs_padded; j += 64) {
     f32x2 v = {1.0f, 0.0f};
@@ -238,7 +242,7 @@ dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dt
   float* delta = reinterpret_cast<float*>(ws);
   f32x2* cs = reinterpret_cast<f32x2*>(reinterpret_cast<char*>(ws) + dbytes);
   hipLaunchKernelGGL(rope_prepare_kernel, dim3(r.n_frames), dim3(64), 0, s, r.theta, r.n_pairs,
-                     pp, r.frame_t, r.frame_phase, r.q0, r.knee, r.inv_factor, delta, cs);
+                     pp, r.frame_t, r.frame_phase, r.q0, r.knee, r.inv_factor, r.axis, delta, cs);
   dp_status st = check_launch("rope_prepare_kernel");
   if (st != DP_OK) return st;
   rope_view(r, ws, view, dtype, head_dim);

@@ -185,6 +185,21 @@ def retained_keep(w: Workload, rate: float = 0.15, seed: Optional[int] = None) -
     return keep
 
 
+def ring_layout(w: Workload, rate: float = 0.15):
+    """Rows of one layer of the ring-layout cache at q0, when the next chunk
+    (index n_chunks) attends: [sink | slots: the window chunks and the next
+    chunk | history: the retained rows of the prunable chunks], the retained
+    rows as retained_keep() draws them.  Returns (row_frame int32 [rows],
+    slot_begin, slot_end); a row's frame is its token index // tokens_per_frame."""
+    C = w.chunk_tokens
+    keep = retained_keep(w, rate)
+    first, last = w.scored_chunks
+    hist = np.flatnonzero(keep[first * C:(last + 1) * C]) + first * C
+    slots = np.arange((last + 1) * C, (w.n_chunks + 1) * C)
+    rows = np.concatenate([np.arange(w.sink_len), slots, hist])
+    return (rows // w.tokens_per_frame).astype(np.int32), w.sink_len, w.sink_len + slots.size
+
+
 def hs_head_class(w: Workload, static_fraction: float = 0.5, seed: Optional[int] = None):
     """[L, H] uint8: 0 = static head, 1 = dynamic head; per layer a seeded
     permutation, the first H*static_fraction heads are static."""
@@ -232,12 +247,14 @@ def _splitmix(keys: np.ndarray, skey: np.uint64) -> np.ndarray:
 
 
 def kv_rows_host(dtype: str, seed: int, stream: int, layer: int, rows, src_rows: int,
-                 row_elems: int) -> np.ndarray:
+                 row_elems: int, cols=None) -> np.ndarray:
     """Host twin of the device fill: the elements of ``rows`` of one layer,
-    [len(rows), row_elems] as uint16 (bf16 bits) or float32."""
+    [len(rows), row_elems] as uint16 (bf16 bits) or float32; with ``cols``
+    only those element columns, [len(rows), len(cols)]."""
     rows = np.asarray(rows, np.uint64)
+    cols = np.arange(row_elems, dtype=np.uint64) if cols is None else np.asarray(cols, np.uint64)
     keys = ((np.uint64(layer) * np.uint64(src_rows) + rows[:, None]) * np.uint64(row_elems)
-            + np.arange(row_elems, dtype=np.uint64)[None, :])
+            + cols[None, :])
     z = _splitmix(keys, stream_key(seed, stream))
     out = kv_table(dtype)[(z >> np.uint64(48)).astype(np.int64)]
     return out.view(np.float32) if dtype == "f32" else out

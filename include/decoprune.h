@@ -195,13 +195,23 @@ dp_status dp_score_index(const float* x0_hat, const float* x_final, int32_t d,
  * theta_j * delta, products and sums rounded separately (no fused
  * multiply-add), and the result stored back rounded to nearest even.
  * Rows whose frame has delta == 0 are not written.
+ *
+ * Phase axis.  DP_AXIS_PAGE: the phase a key gets is t~ itself.
+ * DP_AXIS_COMPRESSED: past the knee t~ = t/c + A with A = (1 - 1/c)(q0 - knee)
+ * the same for every such key, so a key past the knee gets phase
+ * t * inv_factor (= t/c) once, when it first passes the knee, and keeps it;
+ * attention then rotates the query back by A for those keys
+ * (dp_attention_lag), which gives the scores of the page's t~ without
+ * rewriting old keys at every step.  Keys within the knee keep phase t.
  * ------------------------------------------------------------------------- */
+typedef enum { DP_AXIS_PAGE = 0, DP_AXIS_COMPRESSED = 1 } dp_axis;
+
 typedef struct {
   int32_t      pair_begin;   /* first temporal pair                              */
   int32_t      n_pairs;      /* pairs in the temporal block, >= 1               */
   const float* theta;        /* device fp32 [n_pairs] angular frequencies       */
   int32_t      n_frames;     /* frames described by frame_t/frame_phase, >= 1   */
-  int32_t      reserved;     /* must be 0                                        */
+  int32_t      axis;         /* dp_axis                                          */
   const float* frame_t;      /* device fp32 [n_frames] original index t        */
   float*       frame_phase;  /* device fp32 [n_frames] phase p; set to t~      */
   float        q0;           /* query origin (frames)                            */
@@ -430,6 +440,32 @@ dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layer
 dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
                        int64_t kv_capacity, const int64_t* n_kv, int32_t n_heads,
                        int32_t head_dim, int32_t dtype, float scale, void* stream);
+
+/* dp_attention_lag: the same attention over a cache whose keys past the knee
+ *   are kept on the compressed time axis (dp_rope.axis = DP_AXIS_COMPRESSED)
+ *   [DeCoPrune page, 어떻게 쓰나 (the temporal re-index t~ = q0 - g(q0 - t))].
+ *   Past the knee t~ = t/c + A with A = (1 - 1/c)(q0 - knee) common to all such
+ *   keys; a key stored at phase t/c scores against the query turned back by A
+ *   exactly as the key at phase t~ scores against the query (RoPE scores depend
+ *   on the phase difference only), so the old keys need no rewrite when q0
+ *   advances.  Rows j in [plain_begin, plain_end) (the window and the chunk,
+ *   within the knee) see q as given; every other row j < n sees q with the
+ *   temporal pairs [pair_begin, pair_begin + n_pairs) rotated by -lag (lag = A
+ *   in frames; the angle fp32 theta[p] * -lag, fp64 sincos rounded to fp32,
+ *   products and sums rounded separately, bf16 round-to-nearest-even: the
+ *   rotation dp_rope_apply makes for a phase change of -lag).  theta: device
+ *   fp32 [n_pairs].  Other arguments, layout, n, limits and errors as for
+ *   dp_attention; plain_begin >= 0 and plain_end >= plain_begin (DP_ERANGE;
+ *   both clamped to n); n_pairs >= 1, pair_begin >= 0 and
+ *   2 (pair_begin + n_pairs) <= head_dim (DP_ERANGE); lag finite (DP_EINVAL).
+ *   With plain_begin = 0 and plain_end >= n this is dp_attention, bit for bit.
+ *   One launch.
+ * ------------------------------------------------------------------------- */
+dp_status dp_attention_lag(const void* q, const void* k, const void* v, void* o, int64_t n_q,
+                           int64_t kv_capacity, const int64_t* n_kv, int64_t plain_begin,
+                           int64_t plain_end, const float* theta, int32_t pair_begin,
+                           int32_t n_pairs, float lag, int32_t n_heads, int32_t head_dim,
+                           int32_t dtype, float scale, void* stream);
 
 /* dp_hs_attention: the same attention over the ragged DeCoPrune-HS cache
  *   [DeCoPrune page, 무엇인가 (DeCoPrune-HS: static heads see only the sink

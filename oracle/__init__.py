@@ -40,6 +40,7 @@ def lib():
         L.oracle_append_kept.argtypes = [P, i64, i64, i64, i64, i64, P, i64, i64, P]
         L.oracle_append_kept.restype = i64
         L.oracle_rope_frames.argtypes = [i32, P, P, f32, f32, f32, i32, P, P, P, P]
+        L.oracle_rope_frames_compressed.argtypes = [i32, P, P, f32, f32, f32, i32, P, P, P, P]
         L.oracle_rope_rows.argtypes = [P, i32, i64, i32, i32, i32, i32, P, P, P, P]
         L.oracle_rope_uniform.argtypes = [i32, P, f32, P, P]
         L.oracle_rope_headrows.argtypes = [P, i32, i64, i32, i32, i32, P, P, P, P]
@@ -157,8 +158,10 @@ def append_kept(buf, slot_begin, slot_rows, idx, tail, row_frame=None):
 # --------------------------------------------------------------------------
 # RoPE re-index [DeCoPrune page, 무엇과 다른가]
 # --------------------------------------------------------------------------
-def rope_frames(frame_t, frame_phase, q0, knee, inv_factor, theta):
-    """Per-frame delta and cos/sin tables; returns (delta, cos, sin, new_phase)."""
+def rope_frames(frame_t, frame_phase, q0, knee, inv_factor, theta, compressed=False):
+    """Per-frame delta and cos/sin tables; returns (delta, cos, sin, new_phase).
+    compressed: the phase a key past the knee takes is t/c (the compressed
+    time axis) instead of t~."""
     ft = _c(frame_t, np.float32)
     ph = _c(frame_phase, np.float32).copy()
     th = _c(theta, np.float32)
@@ -166,8 +169,9 @@ def rope_frames(frame_t, frame_phase, q0, knee, inv_factor, theta):
     delta = np.empty(nf, np.float32)
     c = np.empty((nf, npairs), np.float32)
     s = np.empty((nf, npairs), np.float32)
-    lib().oracle_rope_frames(nf, _p(ft), _p(ph), np.float32(q0), np.float32(knee),
-                             np.float32(inv_factor), npairs, _p(th), _p(delta), _p(c), _p(s))
+    fn = lib().oracle_rope_frames_compressed if compressed else lib().oracle_rope_frames
+    fn(nf, _p(ft), _p(ph), np.float32(q0), np.float32(knee), np.float32(inv_factor), npairs,
+       _p(th), _p(delta), _p(c), _p(s))
     return delta, c, s, ph
 
 

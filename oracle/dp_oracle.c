@@ -198,6 +198,33 @@ void oracle_rope_frames(int32_t n_frames, const float* frame_t, float* frame_pha
 }
 
 /* ---------------------------------------------------------------------- *
+ * Compressed time axis (a re-parametrisation of the re-index above, not a
+ * step the page names): past the knee t~ = q0 - knee - (q0 - t - knee)/c
+ * = t/c + (1 - 1/c)(q0 - knee), and the second term is the same for every
+ * such key, so a key may carry the phase t/c and leave the common term to
+ * the query.  oracle_rope_frames_compressed: per frame f
+ *   D = q0 - t_f;  t' = t_f * inv_factor if D > knee, else q0 - D (as above);
+ *   delta_f = t' - p_f;  p_f <- t';  cos/sin tables as oracle_rope_frames.
+ * ---------------------------------------------------------------------- */
+void oracle_rope_frames_compressed(int32_t n_frames, const float* frame_t, float* frame_phase,
+                                   float q0, float knee, float inv_factor, int32_t n_pairs,
+                                   const float* theta, float* delta, float* cos_tab,
+                                   float* sin_tab) {
+  for (int32_t f = 0; f < n_frames; ++f) {
+    float D = q0 - frame_t[f];
+    float t_new = D > knee ? frame_t[f] * inv_factor : q0 - D;
+    float dl = t_new - frame_phase[f];
+    delta[f] = dl;
+    frame_phase[f] = t_new;
+    for (int32_t j = 0; j < n_pairs; ++j) {
+      float angle = theta[j] * dl;
+      cos_tab[(int64_t)f * n_pairs + j] = (float)cos((double)angle);
+      sin_tab[(int64_t)f * n_pairs + j] = (float)sin((double)angle);
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------- *
  * Uniform phase step [DeCoPrune page, 무엇과 다른가]: once a frame is past the
  * knee before and after a step, t~ moves by the same amount for every such
  * frame (q0 advances F frames: F (1 - 1/c)), so the keys of all of them are

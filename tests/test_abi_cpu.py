@@ -24,7 +24,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     lib = ctypes.CDLL(dp.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -126,7 +126,7 @@ def _kv(**kw):
 
 def _rope(**kw):
     r = dp.dp_rope()
-    f = dict(pair_begin=0, n_pairs=8, theta=FAKE, n_frames=10, reserved=0, frame_t=FAKE,
+    f = dict(pair_begin=0, n_pairs=8, theta=FAKE, n_frames=10, axis=0, frame_t=FAKE,
              frame_phase=FAKE, q0=10.0, knee=2.0, inv_factor=0.25)
     f.update(kw)
     for k, v in f.items():
@@ -156,7 +156,8 @@ def test_gather_rejects(kw, want):
     (dict(n_pairs=0), None, dp.DP_EINVAL),
     (dict(theta=None), None, dp.DP_EINVAL),
     (dict(), 8, dp.DP_EINVAL),                           # workspace too small
-    (dict(reserved=1), None, dp.DP_EINVAL),
+    (dict(axis=2), None, dp.DP_EINVAL),
+    (dict(axis=-1), None, dp.DP_EINVAL),
 ])
 def test_fused_rope_rejects(kw, ws, want):
     kv = _kv()
@@ -318,6 +319,33 @@ def test_attention_rejects():
     assert _status("attention", *args(n_kv=FAKE + 4)) == dp.DP_EALIGN
     for bad in (float("nan"), 0.0, -0.5, float("inf")):
         assert _status("attention", *args(scale=bad)) == dp.DP_EINVAL
+
+
+def test_attention_lag_rejects():
+    B = dp.DP_BF16
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("q", FAKE), ("k", FAKE), ("v", FAKE), ("o", FAKE), ("n_q", 100), ("cap", 100),
+        ("n_kv", None), ("pb", 10), ("pe", 40), ("theta", FAKE), ("p0", 0), ("np", 44),
+        ("lag", 12.5), ("H", 8), ("D", 128), ("dtype", B), ("scale", 0.1), ("s", None))]
+    f = lambda **kw: _status("attention_lag", *args(**kw))
+    assert f(theta=None) == dp.DP_EINVAL
+    assert f(o=None) == dp.DP_EINVAL
+    assert f(D=64) == dp.DP_EUNSUPPORTED
+    assert f(dtype=dp.DP_F32) == dp.DP_EUNSUPPORTED
+    assert f(H=0) == dp.DP_ERANGE
+    assert f(H=65537) == dp.DP_ERANGE
+    assert f(cap=1 << 31) == dp.DP_ERANGE
+    assert f(pb=-1) == dp.DP_ERANGE
+    assert f(pb=50, pe=49) == dp.DP_ERANGE
+    assert f(np=0) == dp.DP_ERANGE
+    assert f(p0=-1) == dp.DP_ERANGE
+    assert f(p0=20, np=45) == dp.DP_ERANGE          # pairs past head_dim / 2
+    assert f(theta=FAKE + 2) == dp.DP_EALIGN
+    assert f(v=FAKE + 8) == dp.DP_EALIGN
+    for bad in (float("nan"), 0.0, float("inf")):
+        assert f(scale=bad) == dp.DP_EINVAL
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        assert f(lag=bad) == dp.DP_EINVAL
 
 
 def test_hs_attention_rejects():

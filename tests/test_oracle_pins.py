@@ -346,6 +346,35 @@ def test_compressed_axis_decomposition():
                 assert tn == t, (q0, t)
 
 
+def test_compressed_axis_tables():
+    """The compressed-axis frame tables: within the knee they are the page's
+    tables bit for bit; past the knee the phase is t/c and adding the common
+    term A gives the page's t~ exactly (multiples of 1/c are exact in fp32);
+    a frame already at t/c stays (delta 0); the rotation the table encodes
+    is that of the fp64 angle theta_j (t/c - t)."""
+    theta = dpsynth.rope_theta(44)
+    for q0, knee, c in ((240.0, 12.0, 8.0), (20.0, 12.0, 8.0), (8.0, 4.0, 4.0)):
+        t = np.arange(int(q0) + 4, dtype=np.float32)
+        page = oracle.rope_frames(t, t, q0, knee, np.float32(1 / c), theta)
+        comp = oracle.rope_frames(t, t, q0, knee, np.float32(1 / c), theta, compressed=True)
+        inside = q0 - t <= knee
+        for a, b in zip(page[:3], comp[:3]):
+            assert np.array_equal(a[inside], b[inside])
+        A = (1 - 1 / c) * (q0 - knee)
+        past = ~inside
+        assert np.array_equal(comp[3][past].astype(np.float64), t[past] / c)
+        assert np.array_equal(comp[3][past].astype(np.float64) + A, page[3][past].astype(np.float64))
+        assert np.array_equal(comp[0][past].astype(np.float64), t[past] / c - t[past])
+        ang = np.float32(theta[None, :]) * comp[0][:, None]
+        assert np.array_equal(comp[1], np.cos(ang.astype(np.float64)).astype(np.float32))
+        assert np.array_equal(comp[2], np.sin(ang.astype(np.float64)).astype(np.float32))
+        again = oracle.rope_frames(t, comp[3], q0 + 4, knee, np.float32(1 / c), theta,
+                                   compressed=True)
+        still = q0 - t > knee                       # past the knee before and after
+        assert np.all(again[0][still] == 0) and np.all(again[1][still] == 1)
+        assert np.all(again[2][still] == 0)
+
+
 def test_rope_rows_f64_invariants():
     """The float64 re-index: rotations compose, pair norms are kept, and it
     agrees with the fp32-storage re-index within fp32 rounding."""

@@ -41,13 +41,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;          // LDS pointers
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kD = 128;          // head_dim
 constexpr int kBM = 128;         // queries per workgroup
 constexpr int kBN = 64;          // keys per tile
-constexpr int kKP = kD + 8;      // K tile row pitch (bf16 elements)
-constexpr int kVP = kBN + 4;     // V^T tile row pitch (bf16 elements): 34 dwords, so the
-                                 // 32 rows one 8-byte read spans fall in distinct banks
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor, dword 3
 
@@ -88,8 +89,12 @@ template <int MODE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
   constexpr bool RAGGED = MODE == kRagged;
   constexpr bool LAG = MODE == kLag;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * kKP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVP];
+  __shared__ __attribute__((aligned(1024))) uint8_t Kb0[kBN * 256], Kb1[kBN * 256];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kBN * 256], Vb1[kBN * 256];
+  lds_u8* const kb0 = (lds_u8*)Kb0;
+  lds_u8* const kb1 = (lds_u8*)Kb1;
+  lds_u8* const vb0 = (lds_u8*)Vb0;
+  lds_u8* const vb1 = (lds_u8*)Vb1;
   __shared__ f32x2 lag_cs[LAG ? kD / 2 : 1];
   if constexpr (LAG) {
     // {cos, sin} of the fp32 angle theta_j * (-lag), from fp64 sincos rounded to
@@ -203,30 +208,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       qb[ds] = __builtin_bit_cast(bf16x8, r);
     }
   };
-  load_q(LAG && t01 > 0);
 
-  f32x16 o[kD / 32];
-#pragma unroll
-  for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
-  float m = -INFINITY, l = 0.0f;
-
-  // Each thread moves 4 consecutive keys of one 8-element chunk of K and of V.
-  // K rows go to LDS as 16-byte writes (the 16 lanes of a key cover its row);
-  // V is transposed in registers and written as four keys per 8-byte write,
-  // with the keys varying fastest across lanes so that the lanes of a write
-  // fall in distinct banks.  The next tile's loads are issued before the
-  // current tile's MFMAs so that their latency is hidden.
-  const int key4 = (threadIdx.x >> 4) * 4, ch = threadIdx.x & 15;        // K
-  const int vkey4 = (threadIdx.x & 15) * 4, vch = threadIdx.x >> 4;      // V
-  u32x4 kr[4], vr[4];
-  // Tile loads go through buffer descriptors whose base is the tile's first
-  // row and whose size ends at the segment's last valid row, so rows past it
-  // read as zeros without a per-lane branch (gfx9 buffer range check; the lane
-  // offsets stay below 64 rows of the segment's stride, validated on the host).
-  // first key of tile t in its segment, and the segment's key count
-  // (every captured value is read before the selects: arms that each read a
+  // ---- key/value tiles: straight from HBM into LDS, double-buffered ----
+  // A tile is 64 rows of 256 bytes for K and for V, unpadded; each wavefront
+  // moves 4 KiB of each with four 16-byte-per-lane loads whose LDS target is
+  // the next 1 KiB (lane L writes bytes 16 L of it), so row r = 16 wave + 4 u
+  // + L / 16 lands in position L % 16.  The lane loads the global chunk that
+  // belongs there under an XOR swizzle of the row's 16-byte chunks: K chunk c
+  // sits at position c ^ (r & 15) (the 8 rows one 16-byte fragment read serves
+  // per pass hit distinct banks), V chunk c at c ^ 2 (r & 7) (the 4 rows one
+  // transposing read serves per 16 lanes hit distinct banks).  Descriptors end
+  // at the segment's last valid row, so rows past it arrive as zeros.
+  // first key of tile t in its segment, and the segment's key count (every
+  // captured value is read before the selects: arms that each read a
   // different captured variable get merged into one read at a selected
   // address, which keeps the counts in memory and the tile base in VGPRs)
   const int64_t n0c = n0;
@@ -237,7 +231,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     kv0 = (t - (in2 ? T01 : in1 ? T0 : 0)) * kBN;
     n = in2 ? N2 : in1 ? N1 : N0;
   };
-  auto load_tile = [&](int64_t t) {
+  const int dma_row = wave * 16 + (lane >> 4), dma_pos = lane & 15;
+  // (which operands to load is a flag, not a null LDS pointer: LDS offset 0 is
+  // a valid buffer address)
+  auto load_tile = [&](int64_t t, lds_u8* kdst, lds_u8* vdst, bool do_k, bool do_v) {
     const bool s1 = RAGGED && t >= t0;             // uniform per workgroup
     const uint16_t* kp = s1 ? a.k1 : a.k0;
     const uint16_t* vp = s1 ? a.v1 : a.v0;
@@ -251,62 +248,79 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     tile_span(t, kv0, n);
     const int64_t off = base + kv0 * stride;
     const uint32_t bytes = (uint32_t)(min(n - kv0, (int64_t)kBN) * stride * 2);
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kp + off), 0, (int)bytes, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vp + off), 0, (int)bytes, kBufferWord3);
     const uint32_t st2 = (uint32_t)stride * 2u;
-    // Only the first key's offset of each operand stays in a register between
-    // tiles; the empty asm stops the compiler from hoisting all eight offsets
-    // out of the tile loop, where they would hold eight VGPRs throughout.
-    uint32_t k_lo = key4 * st2 + ch * 16, v_lo = vkey4 * st2 + vch * 16;
-    asm volatile("" : "+v"(k_lo), "+v"(v_lo));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rk, (int)(k_lo + u * st2), 0, 0));
-      vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rv, (int)(v_lo + u * st2), 0, 0));
+      const int r = dma_row + 4 * u;
+      const uint32_t row_off = (uint32_t)r * st2;
+      if (do_k) {
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kp + off), 0, (int)bytes, kBufferWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, kdst + (wave * 4 + u) * 1024, 16, row_off + ((dma_pos ^ (r & 15)) << 4), 0, 0, 0);
+      }
+      if (do_v) {
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vp + off), 0, (int)bytes, kBufferWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, vdst + (wave * 4 + u) * 1024, 16, row_off + ((dma_pos ^ ((r & 7) << 1)) << 4), 0,
+            0, 0);
+      }
     }
   };
-  if (n_tiles > 0) load_tile(0);
-  for (int64_t t = 0; t < n_tiles; ++t) {
-    int64_t kv0, nkv;                                // first key of the tile in its segment
-    tile_span(t, kv0, nkv);
-    if (LAG && t == t01 && t > 0) load_q(false);     // the plain range begins
-    // ---- stage K (row-major) and V (transposed) of 64 keys in LDS ----
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(Ks + (key4 + u) * kKP + ch * 8) = kr[u];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {            // element e of the chunk for the 4 keys
-      // byte permutes: the low (even e) or high (odd e) halves of two keys' words
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 w;
-      w[0] = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
-      w[1] = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
-      *reinterpret_cast<u32x2*>(Vt + (vch * 8 + e) * kVP + vkey4) = w;
-    }
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1);
 
-    // ---- S^T = K Q^T for two 32-key tiles: the two accumulation chains are
-    // interleaved so that consecutive MFMAs do not wait on each other ----
-    f32x16 s[2];
+  // ---- fragment addresses (bytes within a tile) ----
+  // K for S^T = K Q^T: lane (l32, hf) reads row kt 32 + l32, chunk 2 ds + hf.
+  uint32_t k_off[kD / 16];
+#pragma unroll
+  for (int ds = 0; ds < kD / 16; ++ds)
+    k_off[ds] = l32 * 256 + (((2 * ds + hf) ^ (l32 & 15)) << 4);
+  // V^T for O^T += V^T P^T, through ds_read_b64_tr_b16: within each 16 lanes,
+  // lane i returns element i % 4 of the 8 bytes lanes 4 k + i / 4 (k = 0..3)
+  // point at.  Lane L (sub = L & 15, group (hf, half) = L >> 4) points at key
+  // row 16 ks + 8 w + 4 hf + sub / 4, dims 32 dt + 16 half + 4 (sub % 4) .. +3,
+  // so it receives V[16 ks + 8 w + 4 hf + k][32 dt + l32], k = 0..3: the keys
+  // the P^T operand lists for contraction slots 4 w .. 4 w + 3.
+  uint32_t v_off[kD / 32];
+  {
+    const int sub = lane & 15, half = (lane >> 4) & 1;
+    const int vrow = 4 * hf + (sub >> 2);                  // row within 8, = row & 7
+    const int lo = 2 * half + ((sub & 3) >> 1);            // chunk bits 0..1 before the swizzle
+    const uint32_t v_a = vrow * 256 + ((lo ^ ((2 * vrow) & 3)) << 4) + 8 * (sub & 1);
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt) v_off[dt] = v_a + ((dt ^ (vrow >> 1)) << 6);
+  }
+
+  f32x16 o[kD / 32];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+
+  // S^T of one tile: two 32-key halves, interleaved accumulation chains
+  auto s_tile = [&](const lds_u8* kb, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
-      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(Ks + l32 * kKP + ds * 16 + hf * 8);
-      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(Ks + (32 + l32) * kKP + ds * 16 + hf * 8);
+      const bf16x8 ka0 = *reinterpret_cast<const lds_bf16x8*>(kb + k_off[ds]);
+      const bf16x8 ka1 = *reinterpret_cast<const lds_bf16x8*>(kb + k_off[ds] + 32 * 256);
       s[0] = mfma(ka0, qb[ds], s[0]);
       s[1] = mfma(ka1, qb[ds], s[1]);
     }
-
-    // ---- online softmax (base 2), lane-local per query plus partner lane ----
-    // Scores are kept unscaled; with c > 0 the scaled maximum is c * max.  Keys
-    // past the segment's end exist only in its last tile.
+  };
+  // mask the keys past the segment's end (last tile only), then the running
+  // maximum: raised only when a score exceeds it by more than 2^8 (decided for
+  // the whole wavefront, so the rescale is skipped together); below that the
+  // probabilities exp2(c s - m) stay under 256, which fp32 sums and the bf16
+  // probabilities carry without loss of relative precision.  Scores are kept
+  // unscaled; with c > 0 the scaled maximum is c * max.
+  auto s_max = [&](f32x16 (&s)[2], int64_t t) {
+    int64_t kv0, nkv;
+    tile_span(t, kv0, nkv);
     const int64_t lim = nkv - kv0;                     // valid keys in this tile (> 0)
     if (lim < kBN) {
 #pragma unroll
@@ -321,10 +335,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kt][i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.c;
-    // The reference m is raised only when a score exceeds it by more than 2^8
-    // (decided for the whole wavefront, so the rescale is skipped together);
-    // below that the probabilities exp2(c s - m) stay under 256, which fp32
-    // sums and the bf16 probabilities carry without loss of relative precision.
     if (__builtin_amdgcn_ballot_w64(mt > m + 8.0f)) {
       const float mn = fmaxf(m, mt);
       const float corr = __builtin_amdgcn_exp2f(m - mn);
@@ -335,47 +345,82 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
     }
+  };
+  // probabilities, their sum, and P^T as B operands: key step ks takes
+  // accumulator entries 8 (ks & 1) .. +8 of tile ks >> 1, i.e. keys
+  // 32 (ks >> 1) + 16 (ks & 1) + 8 (e >> 2) + 4 hf + (e & 3)
+  auto s_exp = [&](f32x16 (&s)[2], bf16x8 (&pt)[4]) {
     float ls = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], a.c, -m));
-        s[kt][i] = p;
-        ls += p;
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], a.c, -m));
+        s[kt][i] = pr;
+        ls += pr;
       }
     ls += __shfl_xor(ls, 32, 64);
     l += ls;
-
-    // ---- P^T as B operands: key step ks takes accumulator entries 8 (ks & 1) .. +8 of
-    // tile ks >> 1, i.e. keys 32 (ks>>1) + 16 (ks&1) + 8 (e>>2) + 4 hf + (e&3) ----
-    bf16x8 pb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         w[e] = pack_bf16_hw(s[ks >> 1][8 * (ks & 1) + 2 * e], s[ks >> 1][8 * (ks & 1) + 2 * e + 1]);
-      pb[ks] = __builtin_bit_cast(bf16x8, w);
+      pt[ks] = __builtin_bit_cast(bf16x8, w);
     }
-
-    // ---- O^T += V^T P^T, V^T read in the same key order; per key step the four
-    // dim tiles' fragments are read together and feed independent accumulators ----
+  };
+  // O^T += V^T P^T; per key step the four dim tiles' fragments are read
+  // together and feed independent accumulators
+  auto o_tile = [&](const lds_u8* vb, const bf16x8 (&pt)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int base = (ks >> 1) * 32 + 16 * (ks & 1) + 4 * hf;
       bf16x8 va[kD / 32];
 #pragma unroll
       for (int dt = 0; dt < kD / 32; ++dt) {
-        const uint16_t* vrow = Vt + (dt * 32 + l32) * kVP + base;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        va[dt] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        const lds_u8* src = vb + v_off[dt] + ks * 4096;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 2048));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        va[dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
       }
 #pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt) o[dt] = mfma(va[dt], pb[ks], o[dt]);
+      for (int dt = 0; dt < kD / 32; ++dt) o[dt] = mfma(va[dt], pt[ks], o[dt]);
     }
+  };
+
+  // ---- software pipeline: while the probabilities of tile t are formed, the
+  // MFMAs of S(t + 1) run; tile t + 2's K and tile t + 1's V are in flight ----
+  // Buffers alternate with the parity of t (Kb[(t + 1) & 1] holds K(t + 1),
+  // Vb[t & 1] holds V(t)); the loop is unrolled twice so that every buffer and
+  // score array is named statically.
+  f32x16 sa[2], sb[2];
+  bf16x8 pt[4];
+  auto step = [&](int64_t t, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const lds_u8* k_next,
+                  lds_u8* k_free, const lds_u8* v_cur, lds_u8* v_free) {
+    __builtin_amdgcn_s_waitcnt(0);             // this wavefront's K(t + 1), V(t) have landed
+    __syncthreads();                           // ... everyone's; K(t), V(t - 1) are free
+    if (t + 2 < n_tiles) load_tile(t + 2, k_free, v_free, true, false);
+    if (t + 1 < n_tiles) load_tile(t + 1, k_free, v_free, false, true);
+    const bool more = t + 1 < n_tiles;
+    if (LAG && more && t + 1 == t01) load_q(false);   // the plain range begins
+    if (more) s_tile(k_next, s_nxt);
+    s_exp(s_cur, pt);
+    o_tile(v_cur, pt);
+    if (more) s_max(s_nxt, t + 1);
+  };
+  if (n_tiles > 0) {
+    load_tile(0, kb0, vb0, true, true);
+    if (n_tiles > 1) load_tile(1, kb1, vb1, true, false);
+    load_q(LAG && t01 > 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    s_tile(kb0, sa);
+    s_max(sa, 0);
+    for (int64_t t = 0; t < n_tiles; t += 2) {
+      step(t, sa, sb, kb1, kb0, vb0, vb1);
+      if (t + 1 < n_tiles) step(t + 1, sb, sa, kb0, kb1, vb1, vb0);
+    }
   }
 
   // ---- O[qi][head][d], d = 32 dt + 8 g + 4 hf + (0..3) ----

@@ -323,11 +323,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     tile_span(t, kv0, nkv);
     const int64_t lim = nkv - kv0;                     // valid keys in this tile (> 0)
     if (lim < kBN) {
+      // key kt 32 + 8 (i >> 2) + 4 hf + (i & 3) is past the end: compare the
+      // constant part against one per-lane bound (32-bit, nothing hoisted)
+      const int rem = (int)lim - 4 * hf;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (kt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3) >= lim) s[kt][i] = -INFINITY;
+          if (kt * 32 + 8 * (i >> 2) + (i & 3) >= rem) s[kt][i] = -INFINITY;
     }
     float mt = -INFINITY;
 #pragma unroll
@@ -404,7 +407,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     if (t + 1 < n_tiles) load_tile(t + 1, k_free, v_free, false, true);
     const bool more = t + 1 < n_tiles;
     if (LAG && more && t + 1 == t01) load_q(false);   // the plain range begins
-    if (more) s_tile(k_next, s_nxt);
+    s_tile(k_next, s_nxt);       // past the last tile: stale LDS, result unused (keeps
+                                 // the MFMAs in the same block as the softmax work)
     s_exp(s_cur, pt);
     o_tile(v_cur, pt);
     if (more) s_max(s_nxt, t + 1);

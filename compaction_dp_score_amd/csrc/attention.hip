@@ -81,6 +81,14 @@ struct AttnArgs {
   float lag;
 };
 
+// The two values a lane and its partner 32 lanes away hold, in lane order
+// (v_permlane32_swap: a VALU exchange, no LDS round trip).
+__device__ __forceinline__ f32x2 with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -337,7 +345,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kt][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.c;
+    const f32x2 mp = with_partner(mt);
+    mt = fmaxf(mp.x, mp.y) * a.c;
     if (__builtin_amdgcn_ballot_w64(mt > m + 8.0f)) {
       const float mn = fmaxf(m, mt);
       const float corr = __builtin_amdgcn_exp2f(m - mn);
@@ -362,8 +371,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         s[kt][i] = pr;
         ls += pr;
       }
-    ls += __shfl_xor(ls, 32, 64);
-    l += ls;
+    const f32x2 lp = with_partner(ls);
+    l += lp.x + lp.y;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       u32x4 w;

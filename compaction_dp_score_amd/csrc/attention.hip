@@ -7,8 +7,9 @@
 //   O[i][h] = sum_{j < n_kv} softmax_j(scale * <Q[i][h], K[j][h]>) V[j][h]
 // with bf16 inputs and outputs, fp32 accumulation and an online softmax.
 //
-// Workgroup = 128 queries of one head, 4 wavefronts of 32 queries.  Per tile of
-// 64 keys (staged in LDS: K row-major, V transposed):
+// Workgroup = 256 queries of one head, 8 wavefronts of 32 queries (one
+// workgroup per CU: two wavefronts per SIMD).  Per tile of 64 keys (K and V
+// row-major in LDS, brought in by the load unit itself, double-buffered):
 //   S^T = K Q^T    v_mfma_f32_32x32x16_bf16, Q held in registers as the B
 //                  operand, so a lane owns one query and 16 of its scores and
 //                  the softmax statistics stay in the lane (plus its partner
@@ -16,7 +17,9 @@
 //   O^T += V^T P^T the probabilities are fed back from the S^T accumulators as
 //                  the B operand without moving between lanes: the order of the
 //                  contraction over keys is permuted to match, and the V^T
-//                  operand reads the same permutation from LDS.
+//                  operand is read in the same order by transposing LDS reads.
+// The MFMAs of the next tile's S^T are issued while the current tile's
+// probabilities are formed.
 // Query tiles of one head are placed on one XCD (workgroup i runs on XCD
 // i mod 8), so the key/value tiles they all stream are shared in that XCD's L2.
 //
@@ -47,7 +50,10 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kD = 128;          // head_dim
-constexpr int kBM = 128;         // queries per workgroup
+constexpr int kWaves = 8;        // wavefronts per workgroup, 32 queries each
+constexpr int kAttnBlock = 64 * kWaves;
+constexpr int kBM = 32 * kWaves; // queries per workgroup
+constexpr int kDmaPerWave = 16 / kWaves;   // 1 KiB tile blocks each wavefront moves per operand
 constexpr int kBN = 64;          // keys per tile
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor, dword 3
@@ -94,7 +100,7 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
   constexpr bool RAGGED = MODE == kRagged;
   constexpr bool LAG = MODE == kLag;
   __shared__ __attribute__((aligned(1024))) uint8_t Kb0[kBN * 256], Kb1[kBN * 256];
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   if constexpr (LAG) {
     // {cos, sin} of the fp32 angle theta_j * (-lag), from fp64 sincos rounded to
     // fp32: the table the in-place re-index builds for a phase change of -lag
-    for (int j = threadIdx.x; j < a.n_pairs; j += kBlock) {
+    for (int j = threadIdx.x; j < a.n_pairs; j += kAttnBlock) {
       const float ang = a.theta[j] * -a.lag;
       double sd, cd;
       sincos((double)ang, &sd, &cd);
@@ -122,13 +128,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int j = slot / a.n_qt;                 // j-th head placed on this XCD
     qt = slot % a.n_qt;
     head = j * kXcds + xcd;
-    if (RAGGED && a.n_heads <= kBlock) {
+    if (RAGGED && a.n_heads <= kAttnBlock) {
       // Ragged runs differ in length, so heads are ranked by length (longest
       // first, ties by index) and dealt to the XCDs in snake order: every XCD
       // gets the same number of heads and nearly the same number of keys, and
       // the longest heads start first.
-      __shared__ int64_t len_s[kBlock];
-      __shared__ int head_of_rank[kBlock];
+      __shared__ int64_t len_s[kAttnBlock];
+      __shared__ int head_of_rank[kAttnBlock];
       const int t = threadIdx.x;
       if (t < a.n_heads) {
         const int64_t lo = min(max(a.off[t], (int64_t)0), a.cap0);
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     kv0 = (t - (in2 ? T01 : in1 ? T0 : 0)) * kBN;
     n = in2 ? N2 : in1 ? N1 : N0;
   };
-  const int dma_row = wave * 16 + (lane >> 4), dma_pos = lane & 15;
+  const int dma_row = wave * 4 * kDmaPerWave + (lane >> 4), dma_pos = lane & 15;
   // (which operands to load is a flag, not a null LDS pointer: LDS offset 0 is
   // a valid buffer address)
   auto load_tile = [&](int64_t t, lds_u8* kdst, lds_u8* vdst, bool do_k, bool do_v) {
@@ -258,20 +264,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const uint32_t bytes = (uint32_t)(min(n - kv0, (int64_t)kBN) * stride * 2);
     const uint32_t st2 = (uint32_t)stride * 2u;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kDmaPerWave; ++u) {
       const int r = dma_row + 4 * u;
       const uint32_t row_off = (uint32_t)r * st2;
       if (do_k) {
         const __amdgpu_buffer_rsrc_t rk =
             __builtin_amdgcn_make_buffer_rsrc((void*)(kp + off), 0, (int)bytes, kBufferWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, kdst + (wave * 4 + u) * 1024, 16, row_off + ((dma_pos ^ (r & 15)) << 4), 0, 0, 0);
+            rk, kdst + (wave * kDmaPerWave + u) * 1024, 16, row_off + ((dma_pos ^ (r & 15)) << 4), 0, 0, 0);
       }
       if (do_v) {
         const __amdgpu_buffer_rsrc_t rv =
             __builtin_amdgcn_make_buffer_rsrc((void*)(vp + off), 0, (int)bytes, kBufferWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, vdst + (wave * 4 + u) * 1024, 16, row_off + ((dma_pos ^ ((r & 7) << 1)) << 4), 0,
+            rv, vdst + (wave * kDmaPerWave + u) * 1024, 16, row_off + ((dma_pos ^ ((r & 7) << 1)) << 4), 0,
             0, 0);
       }
     }
@@ -469,11 +475,11 @@ dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_hea
   const uint64_t blocks = (uint64_t)a.n_qt * n_heads;
   if (blocks == 0) return DP_OK;
   if (a.theta)
-    hipLaunchKernelGGL(attn_fwd_kernel<kLag>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<kLag>, dim3((uint32_t)blocks), dim3(kAttnBlock), 0, s, a);
   else if (a.off)
-    hipLaunchKernelGGL(attn_fwd_kernel<kRagged>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<kRagged>, dim3((uint32_t)blocks), dim3(kAttnBlock), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<kDense>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<kDense>, dim3((uint32_t)blocks), dim3(kAttnBlock), 0, s, a);
   return check_launch("attn_fwd_kernel");
 }
 

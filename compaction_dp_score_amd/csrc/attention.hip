@@ -50,15 +50,22 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kD = 128;          // head_dim
-constexpr int kWaves = 8;        // wavefronts per workgroup, 32 queries each
-constexpr int kAttnBlock = 64 * kWaves;
-constexpr int kBM = 32 * kWaves; // queries per workgroup
-constexpr int kDmaPerWave = 16 / kWaves;   // 1 KiB tile blocks each wavefront moves per operand
+// Wavefronts per workgroup (32 queries each) by mode: dense and lagged caches
+// use 8 (one workgroup per CU, every key/value tile feeds 256 queries); the
+// ragged cache uses 4 (two workgroups per CU: twice as many, smaller units of
+// work balance per-head runs of unequal length better).
+enum { kDense = 0, kRagged = 1, kLag = 2 };
+
+template <int MODE> struct Shape {
+  static constexpr int kWaves = MODE == kRagged ? 4 : 8;
+  static constexpr int kBlock = 64 * kWaves;
+  static constexpr int kBM = 32 * kWaves;          // queries per workgroup
+  static constexpr int kDmaPerWave = 16 / kWaves;  // 1 KiB tile blocks per operand and wavefront
+};
 constexpr int kBN = 64;          // keys per tile
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor, dword 3
 
-enum { kDense = 0, kRagged = 1, kLag = 2 };
 
 struct AttnArgs {
   const uint16_t* q;
@@ -100,9 +107,11 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kAttnBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
   constexpr bool RAGGED = MODE == kRagged;
   constexpr bool LAG = MODE == kLag;
+  constexpr int kAttnBlock = Shape<MODE>::kBlock, kBM = Shape<MODE>::kBM;
+  constexpr int kDmaPerWave = Shape<MODE>::kDmaPerWave;
   __shared__ __attribute__((aligned(1024))) uint8_t Kb0[kBN * 256], Kb1[kBN * 256];
   __shared__ __attribute__((aligned(1024))) uint8_t Vb0[kBN * 256], Vb1[kBN * 256];
   lds_u8* const kb0 = (lds_u8*)Kb0;
@@ -469,17 +478,19 @@ dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_hea
   a.n_q = n_q;
   a.row = (int64_t)n_heads * kD;
   a.n_heads = n_heads;
-  a.n_qt = (int32_t)((n_q + kBM - 1) / kBM);
+  const int bm = a.theta ? Shape<kLag>::kBM : a.off ? Shape<kRagged>::kBM : Shape<kDense>::kBM;
+  a.n_qt = (int32_t)((n_q + bm - 1) / bm);
   a.xcd_map = n_heads % kXcds == 0;
   a.c = scale * 1.4426950408889634f;
   const uint64_t blocks = (uint64_t)a.n_qt * n_heads;
   if (blocks == 0) return DP_OK;
   if (a.theta)
-    hipLaunchKernelGGL(attn_fwd_kernel<kLag>, dim3((uint32_t)blocks), dim3(kAttnBlock), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<kLag>, dim3((uint32_t)blocks), dim3(Shape<kLag>::kBlock), 0, s, a);
   else if (a.off)
-    hipLaunchKernelGGL(attn_fwd_kernel<kRagged>, dim3((uint32_t)blocks), dim3(kAttnBlock), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<kRagged>, dim3((uint32_t)blocks), dim3(Shape<kRagged>::kBlock), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<kDense>, dim3((uint32_t)blocks), dim3(kAttnBlock), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<kDense>, dim3((uint32_t)blocks), dim3(Shape<kDense>::kBlock), 0, s, a);
   return check_launch("attn_fwd_kernel");
 }
 

@@ -102,6 +102,12 @@ __device__ __forceinline__ f32x2 with_partner(float x) {
   return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
+// Workgroup barrier without a memory fence (a fence would also wait for every
+// vector-memory load still in flight).  Callers first wait for the tile loads
+// the barrier publishes; every LDS read before it has been consumed; the memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -183,15 +189,9 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
     n0 = a.cap0;
     if (a.n_kv) n0 = max(min(n0, *a.n_kv), (int64_t)0);
   }
-  // kLag: rows [0, pa) and [pb, n) lagged, then [pa, pb) plain (segments 0, 1, 2)
+  // kLag: rows [0, pa) and [pb, n) lagged, [pa, pb) plain
   const int64_t pa = LAG ? min(a.plain_begin, n0) : 0;
   const int64_t pb = LAG ? min(max(a.plain_end, a.plain_begin), n0) : 0;
-  const int64_t n1 = RAGGED && a.k1 ? a.n1 : LAG ? n0 - pb : 0;
-  const int64_t n2 = pb - pa;
-  if (LAG) n0 = pa;
-  const int64_t t0 = (n0 + kBN - 1) / kBN;
-  const int64_t t01 = t0 + (n1 + kBN - 1) / kBN;   // first tile of segment 2
-  const int64_t n_tiles = t01 + (n2 + kBN - 1) / kBN;
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
@@ -233,61 +233,41 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
   };
 
   // ---- key/value tiles: straight from HBM into LDS, double-buffered ----
-  // A tile is 64 rows of 256 bytes for K and for V, unpadded; each wavefront
-  // moves 4 KiB of each with four 16-byte-per-lane loads whose LDS target is
-  // the next 1 KiB (lane L writes bytes 16 L of it), so row r = 16 wave + 4 u
-  // + L / 16 lands in position L % 16.  The lane loads the global chunk that
-  // belongs there under an XOR swizzle of the row's 16-byte chunks: K chunk c
-  // sits at position c ^ (r & 15) (the 8 rows one 16-byte fragment read serves
-  // per pass hit distinct banks), V chunk c at c ^ 2 (r & 7) (the 4 rows one
-  // transposing read serves per 16 lanes hit distinct banks).  Descriptors end
-  // at the segment's last valid row, so rows past it arrive as zeros.
-  // first key of tile t in its segment, and the segment's key count (every
-  // captured value is read before the selects: arms that each read a
-  // different captured variable get merged into one read at a selected
-  // address, which keeps the counts in memory and the tile base in VGPRs)
-  const int64_t n0c = n0;
-  auto tile_span = [&](int64_t t, int64_t& kv0, int64_t& n) {
-    const int64_t T0 = t0, T01 = t01, N0 = n0c, N1 = n1, N2 = n2;
-    const bool in2 = LAG && t >= T01;
-    const bool in1 = (RAGGED || LAG) && !in2 && t >= T0;
-    kv0 = (t - (in2 ? T01 : in1 ? T0 : 0)) * kBN;
-    n = in2 ? N2 : in1 ? N1 : N0;
-  };
+  // The head's keys are streamed as passes over contiguous row ranges (one per
+  // segment; a lagged cache has up to three), each a software pipeline of its
+  // own.  A tile is 64 rows of 256 bytes for K and for V, unpadded; each
+  // wavefront moves kDmaPerWave KiB of each with 16-byte-per-lane loads whose
+  // LDS target is the next 1 KiB (lane L writes bytes 16 L of it), so row
+  // r = 4 (kDmaPerWave wave + u) + L / 16 lands in position L % 16.  The lane
+  // loads the global chunk that belongs there under an XOR swizzle of the
+  // row's 16-byte chunks: K chunk c sits at position c ^ (r & 15) (the 8 rows
+  // one 16-byte fragment read serves per pass hit distinct banks), V chunk c
+  // at c ^ 2 (r & 7) (the 4 rows one transposing read serves per 16 lanes hit
+  // distinct banks).  Descriptors end at the range's last row, so rows past
+  // it arrive as zeros.
   const int dma_row = wave * 4 * kDmaPerWave + (lane >> 4), dma_pos = lane & 15;
   // (which operands to load is a flag, not a null LDS pointer: LDS offset 0 is
   // a valid buffer address)
-  auto load_tile = [&](int64_t t, lds_u8* kdst, lds_u8* vdst, bool do_k, bool do_v) {
-    const bool s1 = RAGGED && t >= t0;             // uniform per workgroup
-    const uint16_t* kp = s1 ? a.k1 : a.k0;
-    const uint16_t* vp = s1 ? a.v1 : a.v0;
-    const int64_t stride = s1 ? a.row : stride0;
-    int64_t base = s1 ? (int64_t)head * kD : base0;
-    if (LAG) {
-      const int64_t PA = pa, PB = pb, T0 = t0, T01 = t01;
-      base += (t >= T01 ? PA : t >= T0 ? PB : 0) * a.row;
-    }
-    int64_t kv0, n;
-    tile_span(t, kv0, n);
-    const int64_t off = base + kv0 * stride;
-    const uint32_t bytes = (uint32_t)(min(n - kv0, (int64_t)kBN) * stride * 2);
-    const uint32_t st2 = (uint32_t)stride * 2u;
+  auto load_tile = [&](const uint16_t* kp, const uint16_t* vp, uint32_t st2, int64_t rows_left,
+                       lds_u8* kdst, lds_u8* vdst, bool do_k, bool do_v) {
+    const uint32_t bytes = (uint32_t)min(rows_left, (int64_t)kBN) * st2;
 #pragma unroll
     for (int u = 0; u < kDmaPerWave; ++u) {
       const int r = dma_row + 4 * u;
       const uint32_t row_off = (uint32_t)r * st2;
       if (do_k) {
         const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(kp + off), 0, (int)bytes, kBufferWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)bytes, kBufferWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, kdst + (wave * kDmaPerWave + u) * 1024, 16, row_off + ((dma_pos ^ (r & 15)) << 4), 0, 0, 0);
+            rk, kdst + (wave * kDmaPerWave + u) * 1024, 16,
+            row_off + ((dma_pos ^ (r & 15)) << 4), 0, 0, 0);
       }
       if (do_v) {
         const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(vp + off), 0, (int)bytes, kBufferWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)bytes, kBufferWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, vdst + (wave * kDmaPerWave + u) * 1024, 16, row_off + ((dma_pos ^ ((r & 7) << 1)) << 4), 0,
-            0, 0);
+            rv, vdst + (wave * kDmaPerWave + u) * 1024, 16,
+            row_off + ((dma_pos ^ ((r & 7) << 1)) << 4), 0, 0, 0);
       }
     }
   };
@@ -341,10 +321,7 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
   // probabilities exp2(c s - m) stay under 256, which fp32 sums and the bf16
   // probabilities carry without loss of relative precision.  Scores are kept
   // unscaled; with c > 0 the scaled maximum is c * max.
-  auto s_max = [&](f32x16 (&s)[2], int64_t t) {
-    int64_t kv0, nkv;
-    tile_span(t, kv0, nkv);
-    const int64_t lim = nkv - kv0;                     // valid keys in this tile (> 0)
+  auto s_max = [&](f32x16 (&s)[2], int64_t lim) {   // lim: valid keys in the tile (> 0)
     if (lim < kBN) {
       // key kt 32 + 8 (i >> 2) + 4 hf + (i & 3) is past the end: compare the
       // constant part against one per-lane bound (32-bit, nothing hoisted)
@@ -416,39 +393,63 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
     }
   };
 
-  // ---- software pipeline: while the probabilities of tile t are formed, the
-  // MFMAs of S(t + 1) run; tile t + 2's K and tile t + 1's V are in flight ----
-  // Buffers alternate with the parity of t (Kb[(t + 1) & 1] holds K(t + 1),
-  // Vb[t & 1] holds V(t)); the loop is unrolled twice so that every buffer and
-  // score array is named statically.
+  // ---- one pass: a software pipeline over rows [0, n_rows) of a range whose
+  // first K and V rows are at kp and vp, `stride` elements apart.  While the
+  // probabilities of tile t are formed the MFMAs of S(t + 1) run; tile t + 2's K
+  // and tile t + 1's V are in flight.  Buffers alternate with the parity of t
+  // (Kb[(t + 1) & 1] holds K(t + 1), Vb[t & 1] holds V(t)); the loop is unrolled
+  // twice so that every buffer and score array is named statically. ----
   f32x16 sa[2], sb[2];
   bf16x8 pt[4];
-  auto step = [&](int64_t t, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const lds_u8* k_next,
-                  lds_u8* k_free, const lds_u8* v_cur, lds_u8* v_free) {
-    __builtin_amdgcn_s_waitcnt(0);             // this wavefront's K(t + 1), V(t) have landed
-    __syncthreads();                           // ... everyone's; K(t), V(t - 1) are free
-    if (t + 2 < n_tiles) load_tile(t + 2, k_free, v_free, true, false);
-    if (t + 1 < n_tiles) load_tile(t + 1, k_free, v_free, false, true);
-    const bool more = t + 1 < n_tiles;
-    if (LAG && more && t + 1 == t01) load_q(false);   // the plain range begins
-    s_tile(k_next, s_nxt);       // past the last tile: stale LDS, result unused (keeps
+  int q_state = -1;                            // query fragments held: -1 none, 0 plain, 1 lagged
+  auto run_pass = [&](const uint16_t* kp, const uint16_t* vp, int64_t stride, int64_t n_rows,
+                      int q_want) {
+    const int64_t n_tiles = (n_rows + kBN - 1) / kBN;
+    if (n_tiles <= 0) return;
+    const uint32_t st2 = (uint32_t)stride * 2u;
+    const int64_t tile_elems = (int64_t)kBN * stride;
+    auto tk = [&](int64_t t) { return kp + t * tile_elems; };
+    auto tv = [&](int64_t t) { return vp + t * tile_elems; };
+    auto step = [&](int64_t t, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const lds_u8* k_next,
+                    lds_u8* k_free, const lds_u8* v_cur, lds_u8* v_free) {
+      __builtin_amdgcn_s_waitcnt(0);           // this wavefront's K(t + 1), V(t) have landed
+      lds_barrier();                           // ... everyone's; K(t), V(t - 1) are free
+      if (t + 2 < n_tiles)
+        load_tile(tk(t + 2), tv(t + 2), st2, n_rows - (t + 2) * kBN, k_free, v_free, true, false);
+      if (t + 1 < n_tiles)
+        load_tile(tk(t + 1), tv(t + 1), st2, n_rows - (t + 1) * kBN, k_free, v_free, false, true);
+      s_tile(k_next, s_nxt);     // past the last tile: stale LDS, result unused (keeps
                                  // the MFMAs in the same block as the softmax work)
-    s_exp(s_cur, pt);
-    o_tile(v_cur, pt);
-    if (more) s_max(s_nxt, t + 1);
-  };
-  if (n_tiles > 0) {
-    load_tile(0, kb0, vb0, true, true);
-    if (n_tiles > 1) load_tile(1, kb1, vb1, true, false);
-    load_q(LAG && t01 > 0);
+      s_exp(s_cur, pt);
+      o_tile(v_cur, pt);
+      if (t + 1 < n_tiles) s_max(s_nxt, n_rows - (t + 1) * kBN);
+    };
+    if (q_state != q_want) {
+      load_q(LAG && q_want == 1);
+      q_state = q_want;
+    }
+    load_tile(tk(0), tv(0), st2, n_rows, kb0, vb0, true, true);
+    if (n_tiles > 1) load_tile(tk(1), tv(1), st2, n_rows - kBN, kb1, vb1, true, false);
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    lds_barrier();
     s_tile(kb0, sa);
-    s_max(sa, 0);
+    s_max(sa, n_rows);
     for (int64_t t = 0; t < n_tiles; t += 2) {
       step(t, sa, sb, kb1, kb0, vb0, vb1);
       if (t + 1 < n_tiles) step(t + 1, sb, sa, kb0, kb1, vb1, vb0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();                             // the next pass reuses the buffers
+  };
+  if (RAGGED) {
+    run_pass(a.k0 + base0, a.v0 + base0, stride0, n0, 0);
+    if (a.k1) run_pass(a.k1 + (int64_t)head * kD, a.v1 + (int64_t)head * kD, a.row, a.n1, 0);
+  } else if (LAG) {
+    run_pass(a.k0 + base0, a.v0 + base0, a.row, pa, 1);                      // lagged, before
+    run_pass(a.k0 + base0 + pb * a.row, a.v0 + base0 + pb * a.row, a.row, n0 - pb, 1);  // after
+    run_pass(a.k0 + base0 + pa * a.row, a.v0 + base0 + pa * a.row, a.row, pb - pa, 0);  // plain
+  } else {
+    run_pass(a.k0 + base0, a.v0 + base0, stride0, n0, 0);
   }
 
   // ---- O[qi][head][d], d = 32 dt + 8 g + 4 hf + (0..3) ----

@@ -74,8 +74,9 @@ def parse():
                              "hs_attention", "steady", "steady_lazy", "attention_lag"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullkv", action="store_true",
-                    help="attention workloads: skip the context timing over the uncompacted "
-                         "cache (profiling runs, so that every dispatch is a timed one)")
+                    help="skip the context timings that launch the dominant kernel outside the "
+                         "timed steps (attention over the uncompacted cache, the page-axis "
+                         "steady step): profiling runs, so that every dispatch is a timed one")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--summarize-stats", metavar="STATS_DIR",
@@ -98,7 +99,8 @@ def kernel_sources_sha(workload):
 
 def profile_flags(workload):
     """bench.py flags of the profiling runs of a workload."""
-    extra = " --no-fullkv" if workload in ("attention", "hs_attention", "attention_lag") else ""
+    extra = " --no-fullkv" if workload in ("attention", "hs_attention", "attention_lag",
+                                            "steady_lazy") else ""
     return "--no-cpu-baseline" + extra
 
 
@@ -764,7 +766,8 @@ def setup_steady_lazy(dev):
         append = n * H * D * 2 * 2 * 2 * L
         score = C * (8 * w.d + 1)
         return dict(n_kept=n, gather_bytes=append, step_bytes=append + score, n_scored=C,
-                    context={"page_axis_step_ms": round(page_axis_ms(), 4)},
+                    context=None if ARGS.no_fullkv else {"page_axis_step_ms":
+                                                         round(page_axis_ms(), 4)},
                     config={"workload": "steady_lazy",
                             "layout": "sink | ring of 4 chunk slots | history",
                             "time_axis": "compressed (old keys at phase t/c)",

@@ -70,7 +70,14 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendArgs a) {
     if (i >= per_slab) break;
     const uint32_t j = fdiv(i, a.div_row);
     const uint32_t c = i - j * a.div_row.d;
-    const int32_t s = a.idx[j];
+    // When the wavefront's vectors lie in one row (always, when a row is a
+    // multiple of 64 vectors), the row's index entry, frame and phase step are
+    // scalar loads: the index list, the slot's frames and the steps are not
+    // written by this kernel (the frames it writes are at the tail, outside the
+    // slot).
+    const uint32_t j0 = __builtin_amdgcn_readfirstlane(j);
+    const bool one_row = __builtin_amdgcn_ballot_w64(j != j0) == 0;
+    const int32_t s = one_row ? uniform_load(a.idx + j0) : a.idx[j];
     const bool sv = (uint64_t)(uint32_t)s < (uint64_t)a.slot_rows;  // out-of-range entries skipped
     const int64_t src = (a.slot_begin + (sv ? s : 0)) * (int64_t)a.div_row.d + c;
     if (rope) {
@@ -80,13 +87,14 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendArgs a) {
       const uint32_t h = fdiv(c, a.div_head);
       const int tv = (int)(c - h * a.div_head.d) - a.rope.tv_begin;
       const bool in_block = tv >= 0 && tv < a.rope.tv_count;
-      const int f = a.row_frame[a.slot_begin + (sv ? s : 0)];
+      const int32_t* frow = a.row_frame + a.slot_begin + (sv ? s : 0);
+      const int f = one_row ? uniform_load(frow) : *frow;
       const bool fv = (uint32_t)f < (uint32_t)a.rope.n_frames;
       const int fc = fv ? f : 0;
       const int p0 = in_block ? tv * a.rope.ppv : 0;
       const f32x4* tb =
           reinterpret_cast<const f32x4*>(a.rope.cs + (int64_t)fc * a.rope.pairs_padded + p0);
-      const float dl = a.rope.delta[fc];
+      const float dl = one_row ? uniform_load(a.rope.delta + fc) : a.rope.delta[fc];
       const f32x4 t01 = tb[0];     // the table has a 32-byte tail, so tb[1] is readable
       const f32x4 t23 = tb[1];
       u32x4 v = __builtin_nontemporal_load(base + src);

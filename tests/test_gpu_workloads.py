@@ -420,3 +420,91 @@ def test_steady_step_full_size():
           % (n_hist, n, inexact))
     del ks, vs
     _free()
+
+
+def _tables_compressed(host):
+    return oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
+                              host["inv_factor"], host["theta"], compressed=True)
+
+
+def test_steady_lazy_step_full_size():
+    """The steady-state step on the compressed time axis, as bench.py times it
+    (workload steady_lazy): 40 x 40 x 128 bf16, [sink | 4 ring slots | history
+    of the retained rows of chunks 1-55 | room]; chunk 56 leaves the window for
+    q0 = 240.  No old key is written; the leaving chunk's kept rows are
+    appended with its frames moved from phase t to t/c (fused).  Sampled rows
+    of three layers against the oracle's compressed-axis tables."""
+    dev = device()
+    w = dpsynth.WORKLOADS["reindex"]
+    L, H, D, C, tpf = w.n_layers, w.n_heads, w.head_dim, w.chunk_tokens, w.tokens_per_frame
+    hist_rows = np.flatnonzero(dpsynth.retained_keep(w)[C:56 * C]) + C
+    n_hist = hist_rows.shape[0]
+    hb = 5 * C
+    cap = hb + n_hist + C
+    slot_begin = C
+    rf = np.full(cap, -1, np.int32)
+    rf[:C] = np.arange(C) // tpf
+    rf[C:hb] = (56 * C + np.arange(4 * C)) // tpf
+    rf[hb:hb + n_hist] = hist_rows // tpf
+    ks = _fill(dev, w, cap, range(L), dpsynth.STREAM_K)
+    vs = _fill(dev, w, cap, range(L), dpsynth.STREAM_V)
+    we = dpsynth.WORKLOADS["eviction"]
+    x0, xf = dpsynth.score_inputs(we)
+    widx = oracle.compact(oracle.mask(oracle.score_f32(x0, xf, we.d), C, 0, 0, 0, C, w.gamma))
+    n = widx.shape[0]
+    host = _rope_host(w, q0=w.q0 - 4)                 # phases after the previous step (q0 = 236)
+    phase0 = _tables_compressed(host)[3]
+    host = dict(host, q0=w.q0, frame_phase=phase0)
+    rd = _rope_dev(host, dev)
+    kv = dp.dp_kv_inplace()
+    ak, av = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
+    kv.k_layers, kv.v_layers = ak.data_ptr(), av.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dp.DP_BF16
+    kv.capacity = cap
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    keep = torch.empty(C, dtype=torch.uint8, device=dev)
+    idx = torch.empty(C, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64,
+                        device=dev)
+    dp.dp_score_index(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev), we.d, we.d,
+                      dp.make_policy(C, 0, 0, 0, C, w.gamma), None, keep, idx, nk, None, None,
+                      ws_si, err)
+    tail = torch.tensor([hb + n_hist], dtype=torch.int64, device=dev)
+    rf_d = torch.from_numpy(rf).to(dev)
+    rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
+                        host["inv_factor"], axis=dp.DP_AXIS_COMPRESSED)
+    ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+    dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf_d, rope, ws_r)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and nk.item() == n and tail.item() == hb + n_hist + n
+    tables = _tables_compressed(host)
+    assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
+    moved = np.flatnonzero(tables[0] != 0)                   # frames whose phase changes
+    assert np.array_equal(moved, np.arange(224, 228))       # chunk 56 only: t -> t/c
+    old_rows = np.concatenate([_sample_rows(C, [], k=16, seed=2),
+                               hb + _sample_rows(n_hist, [], k=32, seed=3)])
+    ring_rows = C + _sample_rows(4 * C, [C, 2 * C, 3 * C], k=8, seed=4)
+    app = _sample_rows(n, [], k=24, seed=5)
+    src = slot_begin + widx[app]
+    assert np.array_equal(rf_d.cpu().numpy()[hb + n_hist + app], rf[src])
+    inexact = 0
+    for l in (0, 19, L - 1):
+        for rows in (old_rows, ring_rows):                   # never written
+            got = bits(ks[l][torch.from_numpy(rows).to(dev)])
+            assert np.array_equal(got, _expected_rows(w, l, dpsynth.STREAM_K, rows, cap)), l
+        got = bits(ks[l][torch.from_numpy(hb + n_hist + app).to(dev)])
+        want = _expected_rows(w, l, dpsynth.STREAM_K, src, cap)
+        oracle.rope_rows(want, rf[src], 0, tables)
+        ok, worst, ne = keys_close(got, want, TOL_BF16)
+        assert ok, ("appended keys", l, worst)
+        inexact += ne
+        got = bits(vs[l][torch.from_numpy(hb + n_hist + app).to(dev)])
+        assert np.array_equal(got, _expected_rows(w, l, dpsynth.STREAM_V, src, cap)), l
+    print("compressed-axis steady step: %d history rows, %d appended, %d non-identical sampled "
+          "key elements" % (n_hist, n, inexact))
+    del ks, vs
+    _free()

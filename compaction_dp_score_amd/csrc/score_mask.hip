@@ -97,7 +97,6 @@ __device__ __forceinline__ float tree_score(const ScoreArgs& a, f32x4 q) {
 // partial sums).
 __device__ __forceinline__ float group_score(const ScoreArgs& a, int64_t row, bool live,
                                              int lane_in_group) {
-  const int G = a.G;
   f32x4 q = {0.f, 0.f, 0.f, 0.f};
   const int c = 4 * lane_in_group;
   if (live && c < a.d) {

@@ -1183,8 +1183,8 @@ def main():
         summarize_pmc(args.workload, *args.summarize_pmc)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs the compaction path on a single "
-              "MI355X (pass --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the compaction path runs on a single MI355X "
+              "(pass --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -61,7 +61,7 @@ typedef enum {
   DP_ERANGE = 3,        /* size beyond a documented limit                       */
   DP_ECAPACITY = 4,     /* device-side only: more kept rows than capacity       */
   DP_EHIP = 5,          /* a HIP launch or runtime call failed                  */
-  DP_EUNSUPPORTED = 6,  /* valid request outside what this build implements    */
+  DP_EUNSUPPORTED = 6,  /* valid request outside what the library implements   */
   DP_ESTALL = 7         /* device-side only: a bounded wait between workgroups
                            ran out (results of that call are not valid)        */
 } dp_status;

@@ -272,7 +272,8 @@ ROPE_CASES = [  # L, T, H, D, dtype, tokens_per_frame, pair_begin, n_pairs
 
 
 @pytest.mark.parametrize("L,T,H,D,dtype,tpf,pb,npairs", ROPE_CASES)
-def test_gather_with_fused_reindex(L, T, H, D, dtype, tpf, pb, npairs):
+@pytest.mark.parametrize("axis", [dp.DP_AXIS_PAGE, dp.DP_AXIS_COMPRESSED])
+def test_gather_with_fused_reindex(L, T, H, D, dtype, tpf, pb, npairs, axis):
     dev = device()
     rng = np.random.default_rng(T + D)
     kb = _layers(rng, L, T, H, D, dtype, scale=3.0)
@@ -289,7 +290,7 @@ def test_gather_with_fused_reindex(L, T, H, D, dtype, tpf, pb, npairs):
     kv = _kv_struct(k_src, v_src, k_dst, v_dst, T, err, alive)
     idx, n, rf_out = _gpu_idx(keep, dev, rf)
     rope = dp.make_rope(devt["theta"], devt["frame_t"], devt["frame_phase"], host["q0"],
-                        host["knee"], host["inv_factor"], pb)
+                        host["knee"], host["inv_factor"], pb, axis=axis)
     ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, npairs) // 4, dtype=torch.float32,
                      device=dev)
     dp.dp_gather_kv(kv, idx, n, rf_out, rope, ws)
@@ -300,7 +301,8 @@ def test_gather_with_fused_reindex(L, T, H, D, dtype, tpf, pb, npairs):
     assert int(n.item()) == m and err.item() == 0
     wk = oracle.gather(kk, widx)
     tables = oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
-                                host["inv_factor"], host["theta"])
+                                host["inv_factor"], host["theta"],
+                                compressed=axis == dp.DP_AXIS_COMPRESSED)
     wrf = oracle.gather_i32(rf, widx)
     for l in range(L):
         oracle.rope_rows(wk[l], wrf, pb, tables)

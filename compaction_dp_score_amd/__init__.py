@@ -114,6 +114,9 @@ _lib_attention_lag = _sig("dp_attention_lag", [_P, _P, _P, _P, _i64, _i64, _P, _
                                                 _i32, _i32, _f32, _i32, _i32, _i32, _f32, _P])
 _lib_hs_attention = _sig("dp_hs_attention", [_P, _P, _P, _i64, _P, _i32, _P, _P, _i64, _P, _i64,
                                               _i32, _i32, _i32, _f32, _P])
+_lib_hs_attention_lag = _sig("dp_hs_attention_lag", [_P, _P, _P, _i64, _P, _i32, _P, _P, _i64, _P,
+                                                      _i64, _i32, _i32, _i32, _f32, _i64, _P, _i32,
+                                                      _i32, _f32, _P])
 _lib_pr_add = _sig("dp_pr_add", [ctypes.POINTER(dp_pr_counter), _i64, _i64])
 _lib_pr_value = _sig("dp_pr_value", [ctypes.POINTER(dp_pr_counter)], ctypes.c_double)
 
@@ -122,7 +125,8 @@ EXPORTED = ["dp_abi_version", "dp_status_str", "dp_last_error", "dp_score_mask",
             "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_rope_shift_workspace_bytes",
             "dp_rope_shift", "dp_append_kept",
             "dp_hs_offsets", "dp_hs_gather_kv",
-            "dp_hs_rope_reindex", "dp_attention", "dp_attention_lag", "dp_hs_attention", "dp_score_index_workspace_bytes",
+            "dp_hs_rope_reindex", "dp_attention", "dp_attention_lag", "dp_hs_attention",
+            "dp_hs_attention_lag", "dp_score_index_workspace_bytes",
             "dp_score_index", "dp_pr_add", "dp_pr_value"]
 
 
@@ -338,6 +342,16 @@ def dp_hs_attention(q, k_ragged, v_ragged, ragged_capacity, offsets, layer, k_ch
                              _ptr(offsets), int(layer), _ptr(k_chunk), _ptr(v_chunk), int(n_chunk),
                              _ptr(o), int(n_q), n_heads, head_dim, dtype, float(scale),
                              _stream(stream)))
+
+
+def dp_hs_attention_lag(q, k_ragged, v_ragged, ragged_capacity, offsets, layer, k_chunk, v_chunk,
+                        n_chunk, o, n_q, n_heads, head_dim, dtype, scale, plain_tail, theta,
+                        pair_begin, n_pairs, lag, stream=None):
+    _check(_lib_hs_attention_lag(_ptr(q), _ptr(k_ragged), _ptr(v_ragged), int(ragged_capacity),
+                                 _ptr(offsets), int(layer), _ptr(k_chunk), _ptr(v_chunk),
+                                 int(n_chunk), _ptr(o), int(n_q), n_heads, head_dim, dtype,
+                                 float(scale), int(plain_tail), _ptr(theta), int(pair_begin),
+                                 int(n_pairs), float(lag), _stream(stream)))
 
 
 def dp_pr_add(counter, visible_positions, full_positions):

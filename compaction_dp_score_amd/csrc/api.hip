@@ -536,37 +536,70 @@ dp_status dp_attention_lag(const void* q, const void* k, const void* v, void* o,
   return st;
 }
 
+static dp_status hs_attention_impl(const char* who, const void* q, const void* k_ragged,
+                            const void* v_ragged, int64_t ragged_capacity, const int64_t* offsets,
+                            int32_t layer, const void* k_chunk, const void* v_chunk,
+                            int64_t n_chunk, void* o, int64_t n_q, int32_t n_heads,
+                            int32_t head_dim, int32_t dtype, float scale,
+                            const dp::HsLag* lag, void* stream) {
+  if (!q || !k_ragged || !v_ragged || !offsets || !o)
+    return fail(DP_EINVAL, "%s: q, k_ragged, v_ragged, offsets and o are required", who);
+  if (!k_chunk != !v_chunk)
+    return fail(DP_EINVAL, "%s: k_chunk and v_chunk are both given or both NULL", who);
+  if (dtype != DP_BF16 || head_dim != 128)
+    return fail(DP_EUNSUPPORTED, "%s: only bf16 with head_dim 128 is implemented", who);
+  if (n_heads < 1 || n_heads > kMaxAttnHeads || layer < 0 || n_q < 0 || n_q >= kMaxRows ||
+      ragged_capacity < 0 ||
+      ragged_capacity >= ((int64_t)1 << 40) || (k_chunk && (n_chunk < 0 || n_chunk >= kMaxRows)))
+    return fail(DP_ERANGE, "%s: need 1 <= n_heads <= 65536, layer >= 0, 0 <= n_q, n_chunk "
+                           "< 2^31 and 0 <= ragged_capacity < 2^40", who);
+  if ((int64_t)layer * n_heads >= kMaxRows)
+    return fail(DP_ERANGE, "%s: layer * n_heads beyond the offsets range", who);
+  if ((n_q + 127) / 128 * (int64_t)n_heads >= kMaxVec)
+    return fail(DP_ERANGE, "%s: too many query tiles for one launch", who);
+  if (!aligned(q, 16) || !aligned(k_ragged, 16) || !aligned(v_ragged, 16) || !aligned(o, 16) ||
+      !aligned(offsets, 8) || (k_chunk && (!aligned(k_chunk, 16) || !aligned(v_chunk, 16))))
+    return fail(DP_EALIGN, "%s: tensors must be 16-byte aligned (offsets 8)", who);
+  if (!(scale > 0.0f && scale <= 3.0e38f))
+    return fail(DP_EINVAL, "%s: scale must be positive and finite", who);
+  (void)hipGetLastError();
+  dp_status st = launch_hs_attention(q, k_ragged, v_ragged, ragged_capacity,
+                                     offsets + (int64_t)layer * n_heads, k_chunk, v_chunk,
+                                     n_chunk, o, n_q, n_heads, scale, (hipStream_t)stream, lag);
+  if (st == DP_OK) ok();
+  return st;
+}
+
+dp_status dp_hs_attention_lag(const void* q, const void* k_ragged, const void* v_ragged,
+                              int64_t ragged_capacity, const int64_t* offsets, int32_t layer,
+                              const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
+                              int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
+                              float scale, int64_t plain_tail, const float* theta,
+                              int32_t pair_begin, int32_t n_pairs, float lag, void* stream) {
+  if (!theta) return fail(DP_EINVAL, "dp_hs_attention_lag: theta is required");
+  if (dtype != DP_BF16 || head_dim != 128)
+    return fail(DP_EUNSUPPORTED, "dp_hs_attention_lag: only bf16 with head_dim 128 is implemented");
+  if (plain_tail < 0) return fail(DP_ERANGE, "dp_hs_attention_lag: need plain_tail >= 0");
+  if (n_pairs < 1 || pair_begin < 0 || 2 * ((int64_t)pair_begin + n_pairs) > head_dim)
+    return fail(DP_ERANGE, "dp_hs_attention_lag: temporal pairs [%d, %d + %d) outside head_dim/2",
+                pair_begin, pair_begin, n_pairs);
+  if (!aligned(theta, 4)) return fail(DP_EALIGN, "dp_hs_attention_lag: theta must be 4-byte aligned");
+  if (!(lag >= -3.0e38f && lag <= 3.0e38f))
+    return fail(DP_EINVAL, "dp_hs_attention_lag: lag must be finite");
+  const dp::HsLag hl{plain_tail, theta, pair_begin, n_pairs, lag};
+  return hs_attention_impl("dp_hs_attention_lag", q, k_ragged, v_ragged, ragged_capacity, offsets,
+                           layer, k_chunk, v_chunk, n_chunk, o, n_q, n_heads, head_dim, dtype,
+                           scale, &hl, stream);
+}
+
 dp_status dp_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
                           int64_t ragged_capacity, const int64_t* offsets, int32_t layer,
                           const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
                           int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
                           float scale, void* stream) {
-  if (!q || !k_ragged || !v_ragged || !offsets || !o)
-    return fail(DP_EINVAL, "dp_hs_attention: q, k_ragged, v_ragged, offsets and o are required");
-  if (!k_chunk != !v_chunk)
-    return fail(DP_EINVAL, "dp_hs_attention: k_chunk and v_chunk are both given or both NULL");
-  if (dtype != DP_BF16 || head_dim != 128)
-    return fail(DP_EUNSUPPORTED, "dp_hs_attention: only bf16 with head_dim 128 is implemented");
-  if (n_heads < 1 || n_heads > kMaxAttnHeads || layer < 0 || n_q < 0 || n_q >= kMaxRows ||
-      ragged_capacity < 0 ||
-      ragged_capacity >= ((int64_t)1 << 40) || (k_chunk && (n_chunk < 0 || n_chunk >= kMaxRows)))
-    return fail(DP_ERANGE, "dp_hs_attention: need 1 <= n_heads <= 65536, layer >= 0, 0 <= n_q, n_chunk "
-                           "< 2^31 and 0 <= ragged_capacity < 2^40");
-  if ((int64_t)layer * n_heads >= kMaxRows)
-    return fail(DP_ERANGE, "dp_hs_attention: layer * n_heads beyond the offsets range");
-  if ((n_q + 127) / 128 * (int64_t)n_heads >= kMaxVec)
-    return fail(DP_ERANGE, "dp_hs_attention: too many query tiles for one launch");
-  if (!aligned(q, 16) || !aligned(k_ragged, 16) || !aligned(v_ragged, 16) || !aligned(o, 16) ||
-      !aligned(offsets, 8) || (k_chunk && (!aligned(k_chunk, 16) || !aligned(v_chunk, 16))))
-    return fail(DP_EALIGN, "dp_hs_attention: tensors must be 16-byte aligned (offsets 8)");
-  if (!(scale > 0.0f && scale <= 3.0e38f))
-    return fail(DP_EINVAL, "dp_hs_attention: scale must be positive and finite");
-  (void)hipGetLastError();
-  dp_status st = launch_hs_attention(q, k_ragged, v_ragged, ragged_capacity,
-                                     offsets + (int64_t)layer * n_heads, k_chunk, v_chunk,
-                                     n_chunk, o, n_q, n_heads, scale, (hipStream_t)stream);
-  if (st == DP_OK) ok();
-  return st;
+  return hs_attention_impl("dp_hs_attention", q, k_ragged, v_ragged, ragged_capacity, offsets,
+                           layer, k_chunk, v_chunk, n_chunk, o, n_q, n_heads, head_dim, dtype,
+                           scale, nullptr, stream);
 }
 
 dp_status dp_pr_add(dp_pr_counter* acc, int64_t visible, int64_t full) {

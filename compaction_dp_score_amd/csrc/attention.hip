@@ -54,10 +54,10 @@ constexpr int kD = 128;          // head_dim
 // use 8 (one workgroup per CU, every key/value tile feeds 256 queries); the
 // ragged cache uses 4 (two workgroups per CU: twice as many, smaller units of
 // work balance per-head runs of unequal length better).
-enum { kDense = 0, kRagged = 1, kLag = 2 };
+enum { kDense = 0, kRagged = 1, kLag = 2, kRaggedLag = 3 };
 
 template <int MODE> struct Shape {
-  static constexpr int kWaves = MODE == kRagged ? 4 : 8;
+  static constexpr int kWaves = (MODE == kRagged || MODE == kRaggedLag) ? 4 : 8;
   static constexpr int kBlock = 64 * kWaves;
   static constexpr int kBM = 32 * kWaves;          // queries per workgroup
   static constexpr int kDmaPerWave = 16 / kWaves;  // 1 KiB tile blocks per operand and wavefront
@@ -85,9 +85,11 @@ struct AttnArgs {
   int32_t xcd_map;    // 1: group the query tiles of a head on one XCD
   float c;            // scale * log2(e)
   // kLag: rows outside [plain_begin, plain_end) see the query rotated by
-  // -lag on pairs [pair_begin, pair_begin + n_pairs)
+  // -lag on pairs [pair_begin, pair_begin + n_pairs); kRaggedLag: all rows of a
+  // head's run but its last plain_tail do (the chunk block is plain)
   int64_t plain_begin;
   int64_t plain_end;
+  int64_t plain_tail;
   const float* theta;
   int32_t pair_begin;
   int32_t n_pairs;
@@ -114,8 +116,8 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 template <int MODE>
 __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
-  constexpr bool RAGGED = MODE == kRagged;
-  constexpr bool LAG = MODE == kLag;
+  constexpr bool RAGGED = MODE == kRagged || MODE == kRaggedLag;
+  constexpr bool LAG = MODE == kLag || MODE == kRaggedLag;
   constexpr int kAttnBlock = Shape<MODE>::kBlock, kBM = Shape<MODE>::kBM;
   constexpr int kDmaPerWave = Shape<MODE>::kDmaPerWave;
   __shared__ __attribute__((aligned(1024))) uint8_t Kb0[kBN * 256], Kb1[kBN * 256];
@@ -442,7 +444,14 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
     lds_barrier();                             // the next pass reuses the buffers
   };
   if (RAGGED) {
-    run_pass(a.k0 + base0, a.v0 + base0, stride0, n0, 0);
+    if (LAG) {                                 // run: lagged rows, then the plain tail
+      const int64_t tail = min(max(a.plain_tail, (int64_t)0), n0);
+      run_pass(a.k0 + base0, a.v0 + base0, stride0, n0 - tail, 1);
+      run_pass(a.k0 + base0 + (n0 - tail) * stride0, a.v0 + base0 + (n0 - tail) * stride0,
+               stride0, tail, 0);
+    } else {
+      run_pass(a.k0 + base0, a.v0 + base0, stride0, n0, 0);
+    }
     if (a.k1) run_pass(a.k1 + (int64_t)head * kD, a.v1 + (int64_t)head * kD, a.row, a.n1, 0);
   } else if (LAG) {
     run_pass(a.k0 + base0, a.v0 + base0, a.row, pa, 1);                      // lagged, before
@@ -479,17 +488,22 @@ dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_hea
   a.n_q = n_q;
   a.row = (int64_t)n_heads * kD;
   a.n_heads = n_heads;
-  const int bm = a.theta ? Shape<kLag>::kBM : a.off ? Shape<kRagged>::kBM : Shape<kDense>::kBM;
+  const int mode = a.off ? (a.theta ? kRaggedLag : kRagged) : (a.theta ? kLag : kDense);
+  const int bm = mode == kLag ? Shape<kLag>::kBM : mode == kRagged ? Shape<kRagged>::kBM
+               : mode == kRaggedLag ? Shape<kRaggedLag>::kBM : Shape<kDense>::kBM;
   a.n_qt = (int32_t)((n_q + bm - 1) / bm);
   a.xcd_map = n_heads % kXcds == 0;
   a.c = scale * 1.4426950408889634f;
   const uint64_t blocks = (uint64_t)a.n_qt * n_heads;
   if (blocks == 0) return DP_OK;
-  if (a.theta)
+  if (mode == kLag)
     hipLaunchKernelGGL(attn_fwd_kernel<kLag>, dim3((uint32_t)blocks), dim3(Shape<kLag>::kBlock), 0, s, a);
-  else if (a.off)
+  else if (mode == kRagged)
     hipLaunchKernelGGL(attn_fwd_kernel<kRagged>, dim3((uint32_t)blocks), dim3(Shape<kRagged>::kBlock), 0, s,
                        a);
+  else if (mode == kRaggedLag)
+    hipLaunchKernelGGL(attn_fwd_kernel<kRaggedLag>, dim3((uint32_t)blocks),
+                       dim3(Shape<kRaggedLag>::kBlock), 0, s, a);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<kDense>, dim3((uint32_t)blocks), dim3(Shape<kDense>::kBlock), 0, s, a);
   return check_launch("attn_fwd_kernel");
@@ -530,8 +544,16 @@ dp_status launch_attention_lag(const void* q, const void* k, const void* v, void
 dp_status launch_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
                               int64_t ragged_capacity, const int64_t* head_offsets,
                               const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
-                              int64_t n_q, int32_t n_heads, float scale, hipStream_t s) {
+                              int64_t n_q, int32_t n_heads, float scale, hipStream_t s,
+                              const HsLag* lag) {
   AttnArgs a{};
+  if (lag) {
+    a.plain_tail = lag->plain_tail;
+    a.theta = lag->theta;
+    a.pair_begin = lag->pair_begin;
+    a.n_pairs = lag->n_pairs;
+    a.lag = lag->lag;
+  }
   a.k0 = reinterpret_cast<const uint16_t*>(k_ragged);
   a.v0 = reinterpret_cast<const uint16_t*>(v_ragged);
   a.off = head_offsets;

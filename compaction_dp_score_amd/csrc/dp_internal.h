@@ -52,10 +52,20 @@ dp_status launch_attention_lag(const void* q, const void* k, const void* v, void
                                int64_t plain_begin, int64_t plain_end, const float* theta,
                                int32_t pair_begin, int32_t n_pairs, float lag, int32_t n_heads,
                                float scale, hipStream_t s);
+// Lagged ragged attention: the last plain_tail rows of each head's run (and
+// the chunk block) plain, the rest against the query rotated by -lag.
+struct HsLag {
+  int64_t plain_tail;
+  const float* theta;
+  int32_t pair_begin;
+  int32_t n_pairs;
+  float lag;
+};
 dp_status launch_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
                               int64_t ragged_capacity, const int64_t* head_offsets,
                               const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
-                              int64_t n_q, int32_t n_heads, float scale, hipStream_t s);
+                              int64_t n_q, int32_t n_heads, float scale, hipStream_t s,
+                              const HsLag* lag = nullptr);
 dp_status launch_hs_offsets(const uint8_t* head_class, int32_t L, int32_t H,
                             const int64_t* class_len, int32_t n_classes, int64_t* offsets,
                             hipStream_t s);

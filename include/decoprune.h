@@ -486,6 +486,25 @@ dp_status dp_hs_attention(const void* q, const void* k_ragged, const void* v_rag
                           int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
                           float scale, void* stream);
 
+/* dp_hs_attention_lag: dp_hs_attention over a ragged cache whose keys past the
+ *   knee are on the compressed time axis (see dp_attention_lag)
+ *   [DeCoPrune page, 무엇인가 (DeCoPrune-HS) and 어떻게 쓰나 (the temporal
+ *   re-index)].  In each head's run the last plain_tail rows (the window, kept
+ *   by every head and within the knee; the whole run when it is shorter) and
+ *   the chunk block see q as given; every other row of the run sees q with the
+ *   temporal pairs rotated by -lag (rounding as dp_attention_lag).  Other
+ *   arguments, layout, limits and errors as for dp_hs_attention; plain_tail >= 0
+ *   (DP_ERANGE); theta, pair_begin, n_pairs, lag as for dp_attention_lag.  With
+ *   plain_tail >= every run's length this is dp_hs_attention, bit for bit.
+ *   One launch.
+ * ------------------------------------------------------------------------- */
+dp_status dp_hs_attention_lag(const void* q, const void* k_ragged, const void* v_ragged,
+                              int64_t ragged_capacity, const int64_t* offsets, int32_t layer,
+                              const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
+                              int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
+                              float scale, int64_t plain_tail, const float* theta,
+                              int32_t pair_begin, int32_t n_pairs, float lag, void* stream);
+
 /* ------------------------------------------------------------------------- *
  * 6. Pruning ratio             [DeCoPrune page, 어떻게 쓰나 and 전제와 한계]
  *

@@ -24,7 +24,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     lib = ctypes.CDLL(dp.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -366,6 +366,29 @@ def test_hs_attention_rejects():
     assert _status("hs_attention", *args(kc=FAKE + 2)) == dp.DP_EALIGN
     for bad in (float("nan"), 0.0, -0.5, float("inf")):
         assert _status("hs_attention", *args(scale=bad)) == dp.DP_EINVAL
+
+
+def test_hs_attention_lag_rejects():
+    B = dp.DP_BF16
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("q", FAKE), ("kr", FAKE), ("vr", FAKE), ("cap", 1000), ("off", FAKE), ("layer", 3),
+        ("kc", FAKE), ("vc", FAKE), ("nc", 50), ("o", FAKE), ("n_q", 100), ("H", 8), ("D", 128),
+        ("dtype", B), ("scale", 0.1), ("tail", 30), ("theta", FAKE), ("p0", 0), ("np", 44),
+        ("lag", 2.5), ("s", None))]
+    f = lambda **kw: _status("hs_attention_lag", *args(**kw))
+    assert f(theta=None) == dp.DP_EINVAL
+    assert f(off=None) == dp.DP_EINVAL
+    assert f(vc=None) == dp.DP_EINVAL
+    assert f(D=64) == dp.DP_EUNSUPPORTED
+    assert f(tail=-1) == dp.DP_ERANGE
+    assert f(np=0) == dp.DP_ERANGE
+    assert f(p0=30, np=40) == dp.DP_ERANGE
+    assert f(H=65537) == dp.DP_ERANGE
+    assert f(theta=FAKE + 2) == dp.DP_EALIGN
+    assert f(off=FAKE + 4) == dp.DP_EALIGN
+    for bad in (float("nan"), float("inf")):
+        assert f(lag=bad) == dp.DP_EINVAL
+    assert f(scale=0.0) == dp.DP_EINVAL
 
 
 def test_score_index_rejects():

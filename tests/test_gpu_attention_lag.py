@@ -316,3 +316,110 @@ def test_lag_one_minute_ring_shape_sampled():
     err = _check(got, want, "one-minute ring shape")
     print("one-minute ring lag attention: %d rows, max |err| %.2e over %d queries x %d heads"
           % (n, err, len(rows), hd))
+
+
+def _ragged_layout(rng, H, n_sink, n_win, hist_lens, q0, knee, tpf):
+    """Per-head runs [sink | retained history | window] in time order, the
+    frame of every ragged row, and the head offsets."""
+    frames, off = [], [0]
+    for h in range(H):
+        t_sink = np.arange(n_sink) // tpf
+        n_hist = hist_lens[h]
+        t_hist = np.sort(rng.integers(n_sink // tpf + 1, int(q0 - knee), n_hist)) if n_hist else \
+            np.zeros(0, np.int64)
+        t_win = q0 - knee + (np.arange(n_win) * 16) // max(n_win, 1)
+        fr = np.concatenate([t_sink, t_hist, t_win]).astype(np.int32)
+        frames.append(fr)
+        off.append(off[-1] + fr.shape[0])
+    return np.concatenate(frames), np.asarray(off, np.int64)
+
+
+@pytest.mark.parametrize("H,n_chunk,tail_mode", [(8, 70, "window"), (5, 0, "window"),
+                                                 (3, 33, "zero"), (8, 0, "longer")])
+def test_hs_lag_matches_page_axis_oracle(H, n_chunk, tail_mode):
+    """DeCoPrune-HS runs of unequal length (static heads: sink + window; dynamic
+    heads: sink + retained history + window), keys past the knee moved to the
+    compressed axis, then dp_hs_attention_lag with the window as each run's
+    plain tail, against the page-axis oracle per head.  tail_mode: the window
+    length; zero (every row, the window's too, given frames past the knee);
+    longer than every run (every row within the knee)."""
+    dev = device()
+    rng = np.random.default_rng(H * 10 + n_chunk + len(tail_mode))
+    D, tpf, c, knee, q0, n_q = 128, 16, 8.0, 12.0, 240.0, 140
+    n_sink, n_win = 50, 90
+    hist_lens = [0 if h % 2 == 0 or tail_mode == "longer" else int(rng.integers(60, 260))
+                 for h in range(H)]
+    frames, off = _ragged_layout(rng, H, n_sink, n_win, hist_lens, q0, knee, tpf)
+    if tail_mode == "zero":                      # every row past the knee: no plain tail
+        frames = np.minimum(frames, int(q0 - knee) - 1).astype(np.int32)
+    tail = {"window": n_win, "zero": 0, "longer": n_sink + n_win + 100}[tail_mode]
+    if tail_mode == "longer":                    # a tail longer than every run: all plain
+        frames = np.maximum(frames, int(q0 - knee)).astype(np.int32)
+    total = int(off[-1])
+    frame_t = np.arange(int(q0) + 4, dtype=np.float64)
+    kr = random_bf16_bits(rng, (total + 7, D))
+    vr = random_bf16_bits(rng, (total + 7, D))
+    q = random_bf16_bits(rng, (n_q, H, D))
+    kc = random_bf16_bits(rng, (max(n_chunk, 1), H, D))
+    vc = random_bf16_bits(rng, (max(n_chunk, 1), H, D))
+    theta = dpsynth.rope_theta(44)
+    krd = bf16_from_bits(kr, dev)
+    rf_d = to_dev(np.concatenate([frames, np.full(7, -1, np.int32)]), dev)
+    # the packed cache as one [rows, 1 head, D] layer for the re-index
+    _compress([krd.view(total + 7, 1, D)], 1, D, total, [(0, total)], rf_d, to_dev(theta, dev),
+              frame_t, q0, knee, c, 0, dev)
+    lag = (1.0 - 1.0 / c) * (q0 - knee)
+    od = torch.zeros((n_q, H, D), dtype=torch.bfloat16, device=dev)
+    kcd = bf16_from_bits(kc, dev) if n_chunk else None
+    vcd = bf16_from_bits(vc, dev) if n_chunk else None
+    dp.dp_hs_attention_lag(bf16_from_bits(q, dev), krd, bf16_from_bits(vr, dev), total,
+                           to_dev(off, dev), 0, kcd, vcd, n_chunk, od, n_q, H, D, dp.DP_BF16,
+                           1.0 / np.sqrt(D), tail, to_dev(theta, dev), 0, 44, lag)
+    torch.cuda.synchronize()
+    # the lagged rows must be exactly those past the knee
+    past = q0 - frame_t[frames] > knee
+    for h in range(H):
+        lo, hi = int(off[h]), int(off[h + 1])
+        t = min(tail, hi - lo)
+        assert np.all(past[lo:hi - t]) and not np.any(past[hi - t:hi]), h
+    want = np.zeros((n_q, H, D))
+    for h in range(H):
+        lo, hi = int(off[h]), int(off[h + 1])
+        kh = kr[lo:hi][:, None]
+        vh = vr[lo:hi][:, None]
+        fh = frames[lo:hi]
+        if n_chunk:                               # chunk rows: frames within the knee
+            kh = np.concatenate([kh, kc[:n_chunk, h:h + 1]])
+            vh = np.concatenate([vh, vc[:n_chunk, h:h + 1]])
+            fh = np.concatenate([fh, np.full(n_chunk, int(q0), np.int32)])
+        want[:, h] = _page_reference(np.ascontiguousarray(q[:, h:h + 1]), np.ascontiguousarray(kh),
+                                     np.ascontiguousarray(vh), fh, frame_t, q0, knee, c, 0,
+                                     theta, np.arange(n_q))[:, 0]
+    err = _check(bits(od), want, ("hs lag", H, n_chunk, tail_mode))
+    print("hs lag attention H=%d chunk=%d tail=%s: max |err| %.2e" % (H, n_chunk, tail_mode, err))
+
+
+def test_hs_lag_reduces_to_hs_attention():
+    """A plain tail as long as every run, or no plain tail and a zero lag:
+    the same tiles in the same order as dp_hs_attention, bit for bit (a tail
+    that splits a run changes the tile boundaries, hence the summation order)."""
+    dev = device()
+    rng = np.random.default_rng(77)
+    H, D, n_q, n_chunk = 8, 128, 130, 40
+    lens = np.array([0, 1, 63, 64, 65, 200, 7, 129], np.int64)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    total = int(off[-1])
+    kr = bf16_from_bits(random_bf16_bits(rng, (total, D)), dev)
+    vr = bf16_from_bits(random_bf16_bits(rng, (total, D)), dev)
+    q = bf16_from_bits(random_bf16_bits(rng, (n_q, H, D)), dev)
+    kc = bf16_from_bits(random_bf16_bits(rng, (n_chunk, H, D)), dev)
+    vc = bf16_from_bits(random_bf16_bits(rng, (n_chunk, H, D)), dev)
+    offd, theta = to_dev(off, dev), to_dev(dpsynth.rope_theta(44), dev)
+    ref = torch.zeros((n_q, H, D), dtype=torch.bfloat16, device=dev)
+    dp.dp_hs_attention(q, kr, vr, total, offd, 0, kc, vc, n_chunk, ref, n_q, H, D, dp.DP_BF16, 0.09)
+    for tail, lag in ((1000, 123.5), (200, -7.0), (0, 0.0)):
+        od = torch.full((n_q, H, D), 5.0, dtype=torch.bfloat16, device=dev)
+        dp.dp_hs_attention_lag(q, kr, vr, total, offd, 0, kc, vc, n_chunk, od, n_q, H, D,
+                               dp.DP_BF16, 0.09, tail, theta, 0, 44, lag)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(od), bits(ref)), (tail, lag)

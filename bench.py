@@ -980,6 +980,26 @@ def setup_hs_attention(dev, layers=4):
         del kf, vf
         return a.elapsed_time(b) / reps
 
+    def lag_ms(reps=3):
+        # the same launches on the compressed time axis: each run's window tail
+        # (w.window_len rows, within the knee) plain, the rest lagged
+        theta = torch.from_numpy(dpsynth.rope_theta(w.rope_pairs, w.rope_base)).to(dev)
+        lag = (1.0 - 1.0 / w.rope_factor) * (w.q0 - w.rope_knee)
+
+        def once():
+            for l in range(layers):
+                dp.dp_hs_attention_lag(q, kr, vr, total, offsets, l, kc[l], vc[l], C, o, C, H, D,
+                                       dp.DP_BF16, scale, w.window_len, theta, 0, w.rope_pairs,
+                                       lag)
+        once()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            once()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / layers
+
     def accounting():
         # the timer spans the `layers` launches (their head runs differ), so the
         # per-launch figure is the mean over them
@@ -987,6 +1007,8 @@ def setup_hs_attention(dev, layers=4):
         return dict(n_kept=total, gather_bytes=None, flops_per_launch=step_flops / layers,
                     timer_launches=layers, step_flops=step_flops, n_scored=0,
                     full_ms=None if ARGS.no_fullkv else full_ms(),
+                    context=None if ARGS.no_fullkv else
+                    {"compressed_axis_ms_per_launch": round(lag_ms(), 4)},
                     full_flops=4.0 * C * n_full * D * H,
                     metric="attention TFLOP/s over the ragged DeCoPrune-HS cache",
                     config={"workload": "hs_attention", "layers": layers, "heads": H,

@@ -417,7 +417,8 @@ def test_rope_reindex_factor_one_is_identity():
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,D", [(dp.DP_BF16, 64), (dp.DP_F32, 32), (dp.DP_BF16, 128)])
 @pytest.mark.parametrize("fused", [False, True])
-def test_hs_ragged_gather_and_reindex(dtype, D, fused):
+@pytest.mark.parametrize("axis", [dp.DP_AXIS_PAGE, dp.DP_AXIS_COMPRESSED])
+def test_hs_ragged_gather_and_reindex(dtype, D, fused, axis):
     dev = device()
     rng = np.random.default_rng(D + fused)
     L, H, T, tpf = 3, 6, 3000, 50
@@ -480,7 +481,7 @@ def test_hs_ragged_gather_and_reindex(dtype, D, fused):
     crf = dp.ptr_array(rfs, dev)
     caps = [T, T]
     rope = dp.make_rope(devt["theta"], devt["frame_t"], devt["frame_phase"], host["q0"],
-                        host["knee"], host["inv_factor"], 0)
+                        host["knee"], host["inv_factor"], 0, axis=axis)
     ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, npairs) // 4, dtype=torch.float32,
                      device=dev)
     if fused:
@@ -500,7 +501,8 @@ def test_hs_ragged_gather_and_reindex(dtype, D, fused):
         oracle.hs_gather_layer(vb[l], l, cls, [ws_list, wd_list], woff, w_v)
     assert np.array_equal(bits(v_out[:total]), w_v)
     tables = oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
-                                host["inv_factor"], host["theta"])
+                                host["inv_factor"], host["theta"],
+                                compressed=axis == dp.DP_AXIS_COMPRESSED)
     w_rf = np.zeros(total, np.int32)
     for i in range(L * H):
         lst = ws_list if cls.ravel()[i] == 0 else wd_list

@@ -323,7 +323,9 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
   // probabilities exp2(c s - m) stay under 256, which fp32 sums and the bf16
   // probabilities carry without loss of relative precision.  Scores are kept
   // unscaled; with c > 0 the scaled maximum is c * max.
-  auto s_max = [&](f32x16 (&s)[2], int64_t lim) {   // lim: valid keys in the tile (> 0)
+  // (split in three so that the maximum of a full tile, the common case, is
+  // plain VALU work the scheduler can place among the MFMAs of the same block)
+  auto s_mask = [&](f32x16 (&s)[2], int64_t lim) {   // lim: valid keys in the tile (> 0)
     if (lim < kBN) {
       // key kt 32 + 8 (i >> 2) + 4 hf + (i & 3) is past the end: compare the
       // constant part against one per-lane bound (32-bit, nothing hoisted)
@@ -334,13 +336,17 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
         for (int i = 0; i < 16; ++i)
           if (kt * 32 + 8 * (i >> 2) + (i & 3) >= rem) s[kt][i] = -INFINITY;
     }
+  };
+  auto tile_max = [&](const f32x16 (&s)[2]) {          // scaled maximum of the tile
     float mt = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kt][i]);
     const f32x2 mp = with_partner(mt);
-    mt = fmaxf(mp.x, mp.y) * a.c;
+    return fmaxf(mp.x, mp.y) * a.c;
+  };
+  auto update_m = [&](float mt) {
     if (__builtin_amdgcn_ballot_w64(mt > m + 8.0f)) {
       const float mn = fmaxf(m, mt);
       const float corr = __builtin_amdgcn_exp2f(m - mn);
@@ -351,6 +357,10 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
     }
+  };
+  auto s_max = [&](f32x16 (&s)[2], int64_t lim) {
+    s_mask(s, lim);
+    update_m(tile_max(s));
   };
   // probabilities, their sum, and P^T as B operands: key step ks takes
   // accumulator entries 8 (ks & 1) .. +8 of tile ks >> 1, i.e. keys
@@ -423,8 +433,16 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
       s_tile(k_next, s_nxt);     // past the last tile: stale LDS, result unused (keeps
                                  // the MFMAs in the same block as the softmax work)
       s_exp(s_cur, pt);
-      o_tile(v_cur, pt);
-      if (t + 1 < n_tiles) s_max(s_nxt, n_rows - (t + 1) * kBN);
+      float mt = tile_max(s_nxt);  // S(t + 1) as computed; corrected below for a last,
+      o_tile(v_cur, pt);           // partial tile
+      if (t + 1 < n_tiles) {
+        const int64_t lim = n_rows - (t + 1) * kBN;
+        if (lim < kBN) {
+          s_mask(s_nxt, lim);
+          mt = tile_max(s_nxt);
+        }
+        update_m(mt);
+      }
     };
     if (q_state != q_want) {
       load_q(LAG && q_want == 1);

@@ -387,6 +387,17 @@ dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t sl
  *   skipped).
  * class_idx / class_row_frame are device arrays of n_classes device pointers;
  * class_len is device int64 [n_classes].  n_classes <= DP_HS_MAX_CLASSES.
+ *
+ * Ring layout for a rollout (no entry point of its own): the split is fixed
+ * per layer, so a model may order each layer's heads class by class (a
+ * permutation of its projection weights) and keep one token-major cache per
+ * class: static [sink | window ring], dynamic [sink | window ring | history].
+ * All dynamic heads keep the same rows, so an eviction is dp_append_kept over
+ * the dynamic buffers of all layers (n_heads = heads of the class), the static
+ * class only retires the slot, the old keys are re-indexed by dp_rope_apply
+ * (both sinks, the dynamic history), and attention runs per class buffer with
+ * dp_attention (queries of the class's heads, keys [0, *tail) or the static
+ * buffer's rows).
  * ------------------------------------------------------------------------- */
 #define DP_HS_MAX_CLASSES 8
 

@@ -242,11 +242,13 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
   // LDS target is the next 1 KiB (lane L writes bytes 16 L of it), so row
   // r = 4 (kDmaPerWave wave + u) + L / 16 lands in position L % 16.  The lane
   // loads the global chunk that belongs there under an XOR swizzle of the
-  // row's 16-byte chunks: K chunk c sits at position c ^ (r & 15) (the 8 rows
-  // one 16-byte fragment read serves per pass hit distinct banks), V chunk c
-  // at c ^ 2 (r & 7) (the 4 rows one transposing read serves per 16 lanes hit
-  // distinct banks).  Descriptors end at the range's last row, so rows past
-  // it arrive as zeros.
+  // row's 16-byte chunks: K chunk c sits at position c ^ (r & 15) (the 16
+  // rows one 16-byte fragment read serves per pass hit all 64 banks once), V
+  // chunk c at c ^ 4 (r & 3) (a transposing read serves 32 lanes per pass:
+  // 4 rows x 4 chunks of one dim tile, which this places on all 64 banks once;
+  // measured: the former c ^ 2 (r & 7) put them on 32 banks, and bank
+  // conflicts took a third of the LDS cycles).  Descriptors end at the range's
+  // last row, so rows past it arrive as zeros.
   const int dma_row = wave * 4 * kDmaPerWave + (lane >> 4), dma_pos = lane & 15;
   // (which operands to load is a flag, not a null LDS pointer: LDS offset 0 is
   // a valid buffer address)
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
             __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)bytes, kBufferWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rv, vdst + (wave * kDmaPerWave + u) * 1024, 16,
-            row_off + ((dma_pos ^ ((r & 7) << 1)) << 4), 0, 0, 0);
+            row_off + ((dma_pos ^ ((r & 3) << 2)) << 4), 0, 0, 0);
       }
     }
   };
@@ -290,10 +292,10 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
   {
     const int sub = lane & 15, half = (lane >> 4) & 1;
     const int vrow = 4 * hf + (sub >> 2);                  // row within 8, = row & 7
-    const int lo = 2 * half + ((sub & 3) >> 1);            // chunk bits 0..1 before the swizzle
-    const uint32_t v_a = vrow * 256 + ((lo ^ ((2 * vrow) & 3)) << 4) + 8 * (sub & 1);
+    const int lo = 2 * half + ((sub & 3) >> 1);            // chunk bits 0..1 (not swizzled)
+    const uint32_t v_a = vrow * 256 + (lo << 4) + 8 * (sub & 1);
 #pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) v_off[dt] = v_a + ((dt ^ (vrow >> 1)) << 6);
+    for (int dt = 0; dt < kD / 32; ++dt) v_off[dt] = v_a + ((dt ^ (vrow & 3)) << 6);
   }
 
   f32x16 o[kD / 32];

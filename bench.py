@@ -89,11 +89,17 @@ def parse():
 
 
 def kernel_sources_sha(workload):
+    """Hash of the code of the workload's kernel sources, comments and layout
+    whitespace removed (a comment edit does not change the kernel)."""
     import hashlib
+    import re
+    token = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/', re.S)
     h = hashlib.sha256()
     for f in KERNELS[workload][1]:
-        with open(os.path.join(ROOT, "compaction_dp_score_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "compaction_dp_score_amd", "csrc", f)) as fh:
+            text = fh.read()
+        code = token.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

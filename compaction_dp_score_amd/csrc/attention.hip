@@ -35,7 +35,10 @@
 // cache is then streamed as three segments: the lagged rows before the plain
 // range, the lagged rows after it (both against the rotated query) and the
 // plain range (against the query as given); the query fragment is rebuilt
-// once, when the stream reaches the plain range.
+// once, when the stream reaches the plain range.  On the ragged HS cache
+// (dp_hs_attention_lag) each head's run is lagged except its last plain_tail
+// rows, which are streamed after it together with the chunk's own block, both
+// plain.
 #include "dp_internal.h"
 
 namespace dp {

@@ -270,7 +270,7 @@ def cpu_baseline_eviction(w, x0, xf, theta, ft, fp, seconds):
     tables = oracle.rope_frames(tables_in[0], tables_in[1], w.q0, w.rope_knee,
                                 np.float32(1.0 / w.rope_factor), theta)
     t_once = time.perf_counter() - t0
-    n_layers = max(1, min(L, cores, 8))
+    n_layers = max(1, min(L, cores))              # the gather runs one thread per layer
     src = np.empty((n_layers, T, H, D), np.uint16)
     for l in range(n_layers):
         src[l].reshape(T // tile_rows, tile_rows, H * D)[:] = tile[None]

@@ -20,12 +20,14 @@ one launch and as dp_score_mask + dp_compact_index, and the CPU oracle timed
 on a bounded layer sample of the same workload on the host cores.
 
 Other workloads (--workload reindex | prefix | hs | append | steady |
-steady_lazy | attention | hs_attention | attention_lag) time the other shapes;
+steady_lazy | hs_ring | attention | hs_attention | attention_lag) time the
+other shapes;
 "append" is the same eviction step in the ring layout, where only the leaving
 chunk's kept rows move and the old keys are re-indexed in place; "steady" is a
 later step of the one-minute rollout in that layout (old keys moved by one
 uniform phase step), "steady_lazy" the same step with the old keys on the
-compressed time axis (none rewritten); the attention workloads time the next
+compressed time axis (none rewritten), "hs_ring" that step for the HS cache
+kept as one ring-layout cache per head class; the attention workloads time the next
 chunk's attention over the compacted (ragged HS, or compressed-axis) cache in
 TFLOP/s.
 """
@@ -57,6 +59,7 @@ KERNELS = {
     "steady": ("shift_kernel", ("rope.hip", "dp_device.h")),
     "steady_lazy": ("append_kernel", ("append.hip", "dp_device.h")),
     "attention_lag": ("attn_fwd_kernel", ("attention.hip", "dp_device.h")),
+    "hs_ring": ("append_kernel", ("append.hip", "dp_device.h")),
 }
 
 
@@ -71,7 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="eviction",
                     choices=["eviction", "reindex", "prefix", "hs", "append", "attention",
-                             "hs_attention", "steady", "steady_lazy", "attention_lag"])
+                             "hs_attention", "steady", "steady_lazy", "attention_lag", "hs_ring"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullkv", action="store_true",
                     help="skip the context timings that launch the dominant kernel outside the "
@@ -106,7 +109,7 @@ def kernel_sources_sha(workload):
 def profile_flags(workload):
     """bench.py flags of the profiling runs of a workload."""
     extra = " --no-fullkv" if workload in ("attention", "hs_attention", "attention_lag",
-                                            "steady_lazy") else ""
+                                            "steady_lazy", "hs_ring") else ""
     return "--no-cpu-baseline" + extra
 
 
@@ -137,14 +140,16 @@ class Timer:
         self.pairs = []
 
     def start(self):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(torch.cuda.current_stream())
-        self.pairs.append([e, None])
+        # both events exist before the start is recorded, so nothing but the
+        # record calls sits between them and the launch they bracket (creating
+        # the stop event after a short kernel's launch could delay its record
+        # past the kernel's end)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(torch.cuda.current_stream())
+        self.pairs.append([a, b])
 
     def stop(self):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(torch.cuda.current_stream())
-        self.pairs[-1][1] = e
+        self.pairs[-1][1].record(torch.cuda.current_stream())
 
     def mean_ms(self):
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
@@ -784,6 +789,144 @@ def setup_steady_lazy(dev):
     return run, gt, accounting, None
 
 
+def setup_hs_ring(dev):
+    """DeCoPrune-HS in the ring layout, at the HS workload's shape (40 layers,
+    20 static and 20 dynamic heads per layer, 128 dims, bf16): each layer's
+    heads are ordered class by class and each class keeps a token-major cache
+    of its own; static [sink | 4 chunk slots], dynamic [sink | 4 chunk slots |
+    history].  The history is a Bernoulli(0.15) sample of chunks 1-25 (the rate
+    the gamma mask keeps), chunk 26 in slot 0 leaves the window at q0 = 120.
+    Per step, on the compressed time axis: the leaving chunk is scored and
+    indexed in one launch, dp_rope_prepare writes the frame tables, and
+    dp_append_kept appends its kept rows to the dynamic caches of all layers
+    with the re-index fused; the static class only retires the slot.  The
+    tail, the row frames and the phase table are restored before each step.
+    For context the same step on the page's axis (the uniform shift of every
+    old key of both classes, then the same append) is timed on the same
+    buffers."""
+    import compaction_dp_score_amd as dp
+    import dpsynth
+    w = dpsynth.WORKLOADS["hs"]
+    H, D, L, C, tpf = w.n_heads, w.head_dim, w.n_layers, w.chunk_tokens, w.tokens_per_frame
+    HC = H // 2
+    keep_full = dpsynth.retained_keep(w)
+    hist_rows = np.flatnonzero(keep_full[C:26 * C]) + C          # retained rows of chunks 1..25
+    n_hist = hist_rows.shape[0]
+    hb = 5 * C                                                    # sink + 4 ring slots
+    cap = hb + n_hist + C
+    slot_begin = C                                                # ring slot 0: chunk 26
+    rf_host = np.full(cap, -1, np.int32)
+    rf_host[:C] = np.arange(C) // tpf
+    rf_host[C:hb] = (26 * C + np.arange(4 * C)) // tpf
+    rf_host[hb:hb + n_hist] = hist_rows // tpf
+
+    def fill(rows, stream_id):
+        out = []
+        for l in range(L):
+            t = torch.empty((rows, HC, D), dtype=torch.bfloat16, device=dev)
+            dpsynth.kv_fill_device(t, "bf16", w.seed, stream_id, l, rows, HC * D)
+            out.append(t)
+        return out
+
+    kd, vd = fill(cap, dpsynth.STREAM_K), fill(cap, dpsynth.STREAM_V)     # dynamic class
+    ks = fill(hb, dpsynth.STREAM_K + 16)                                  # static class, K
+    x0, xf = dpsynth.score_inputs(dpsynth.WORKLOADS["eviction"])          # one chunk of scores
+    x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
+    rf0 = torch.from_numpy(rf_host).to(dev)
+    rf = rf0.clone()
+    rf_s0 = torch.from_numpy(rf_host[:hb].copy()).to(dev)
+    rf_s = rf_s0.clone()
+    kv = dp.dp_kv_inplace()
+    arr_k, arr_v, arr_ks = dp.ptr_array(kd, dev), dp.ptr_array(vd, dev), dp.ptr_array(ks, dev)
+    kv.k_layers, kv.v_layers = arr_k.data_ptr(), arr_v.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, HC, D, dp.DP_BF16
+    kv.capacity = cap
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    tail0 = torch.tensor([hb + n_hist], dtype=torch.int64, device=dev)
+    tail = tail0.clone()
+    pol = dp.make_policy(C, 0, 0, 0, C, w.gamma)
+    keep = torch.empty(C, dtype=torch.uint8, device=dev)
+    idx = torch.empty(C, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64, device=dev)
+    theta = torch.from_numpy(dpsynth.rope_theta(w.rope_pairs, w.rope_base)).to(dev)
+    ft, fp = dpsynth.frame_tables(w)
+    ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(fp).to(dev)
+    ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    # the phases after the previous step (q0 = 116) on the compressed axis
+    dp.dp_rope_prepare(dp.make_rope(theta, ftd, fpd, w.q0 - 4, w.rope_knee, 1.0 / w.rope_factor,
+                                    axis=dp.DP_AXIS_COMPRESSED), D, dp.DP_BF16, ws_r)
+    phase0 = fpd.clone()
+    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
+                        axis=dp.DP_AXIS_COMPRESSED)
+    page_rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    step_frames = 4 * (1.0 - 1.0 / w.rope_factor)                 # 3.5
+    ws_s = torch.empty(dp.dp_rope_shift_workspace_bytes(w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    gt = Timer()
+    keep_alive = [arr_k, arr_v, arr_ks]
+
+    def restore():
+        tail.copy_(tail0)
+        rf.copy_(rf0)
+        rf_s.copy_(rf_s0)
+        fpd.copy_(phase0)
+
+    def run(timed):
+        restore()
+        dp.dp_score_index(x0d, xfd, w.d, w.d, pol, None, keep, idx, nk, None, None, ws_si, err)
+        dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+        if timed:
+            gt.start()
+        dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf, rope, ws_r)
+        if timed:
+            gt.stop()
+        rf_s[slot_begin:slot_begin + C].fill_(-1)                 # the static class drops it
+
+    def page_axis_ms(reps=5):
+        def once():
+            restore()
+            dp.dp_score_index(x0d, xfd, w.d, w.d, pol, None, keep, idx, nk, None, None, ws_si,
+                              err)
+            for arr in (arr_ks, arr_k):                            # both sinks
+                dp.dp_rope_shift(arr, L, HC, D, dp.DP_BF16, 0, C, None, theta, 0, w.rope_pairs,
+                                 step_frames, ws_s)
+            dp.dp_rope_shift(arr_k, L, HC, D, dp.DP_BF16, hb, cap, tail, theta, 0, w.rope_pairs,
+                             step_frames, ws_s)                    # dynamic history
+            dp.dp_rope_prepare(page_rope, D, dp.DP_BF16, ws_r)
+            dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf, page_rope, ws_r)
+            rf_s[slot_begin:slot_begin + C].fill_(-1)
+        once()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            once()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def accounting():
+        assert keep_alive and err.item() == 0
+        n = int(nk.item())
+        append = n * HC * D * 2 * 2 * 2 * L
+        score = C * (8 * w.d + 1)
+        return dict(n_kept=n, gather_bytes=append, step_bytes=append + score, n_scored=C,
+                    context=None if ARGS.no_fullkv else {"page_axis_step_ms":
+                                                         round(page_axis_ms(), 4)},
+                    config={"workload": "hs_ring",
+                            "layout": "per head class: static sink | 4 chunk slots; "
+                                      "dynamic sink | 4 chunk slots | history",
+                            "time_axis": "compressed (old keys at phase t/c)",
+                            "layers": L, "heads_per_class": HC, "head_dim": D,
+                            "kv_dtype": "bf16", "history_rows": int(n_hist), "scored_tokens": C,
+                            "kept_tokens": n, "appended_bytes": append,
+                            "rope_pairs": w.rope_pairs, "q0": w.q0})
+
+    return run, gt, accounting, None
+
+
 def setup_attention_lag(dev, layers=4):
     """Attention of the next chunk (6,240 queries, 40 heads x 128, bf16) over
     the same 83,412-row cache as the attention workload, in the ring layout
@@ -1222,7 +1365,8 @@ def main():
     setups = {"eviction": setup_eviction, "reindex": setup_reindex, "prefix": setup_prefix,
               "hs": setup_hs, "append": setup_append, "attention": setup_attention,
               "hs_attention": setup_hs_attention, "steady": setup_steady,
-              "steady_lazy": setup_steady_lazy, "attention_lag": setup_attention_lag}
+              "steady_lazy": setup_steady_lazy, "attention_lag": setup_attention_lag,
+              "hs_ring": setup_hs_ring}
     if args.workload not in setups:
         print("workload %s is not wired into bench.py yet" % args.workload, file=sys.stderr)
         sys.exit(2)

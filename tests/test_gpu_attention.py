@@ -106,6 +106,46 @@ def test_attention_eviction_shape_sampled():
           % (err, len(rows), H))
 
 
+def test_attention_one_minute_shape_sampled():
+    """The launch the attention benchmark times: 6,240 queries over the
+    83,412 rows a one-minute history leaves after compaction (sink + retained
+    history + window + the chunk), 40 heads x 128, the bench's own inputs.
+    Seven queries of three heads against the float64 oracle over all keys; the
+    checked heads' keys and values are read back from the generator's device
+    fill and tied to its host twin on probe rows."""
+    dev = device()
+    w = dpsynth.WORKLOADS["reindex"]
+    H, D, C = w.n_heads, w.head_dim, w.chunk_tokens
+    n = int(dpsynth.retained_keep(w).sum()) + C
+    q = torch.empty((C, H, D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((n, H, D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((n, H, D), dtype=torch.bfloat16, device=dev)
+    dpsynth.kv_fill_device(q, "bf16", w.seed, 3, 0, C, H * D)
+    dpsynth.kv_fill_device(k, "bf16", w.seed, dpsynth.STREAM_K, 0, n, H * D)
+    dpsynth.kv_fill_device(v, "bf16", w.seed, dpsynth.STREAM_V, 0, n, H * D)
+    o = torch.empty_like(q)
+    dp.dp_attention(q, k, v, o, C, n, None, H, D, dp.DP_BF16, 1.0 / np.sqrt(D))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 3000, 6111, 6239])
+    heads = np.array([0, 21, 39])
+    cols = (heads[:, None] * D + np.arange(D)[None, :]).ravel()
+    hd_idx = torch.from_numpy(heads).to(dev)
+    kh = bits(k.index_select(1, hd_idx))
+    vh = bits(v.index_select(1, hd_idx))
+    probe = np.array([0, 1, 255, 256, n // 3, n // 2, n - 2, n - 1])
+    for t_, stream in ((kh, dpsynth.STREAM_K), (vh, dpsynth.STREAM_V)):
+        host = dpsynth.kv_rows_host("bf16", w.seed, stream, 0, probe, n, H * D, cols)
+        assert np.array_equal(t_[probe].reshape(len(probe), -1), host)
+    qh = np.zeros((C, len(heads), D), np.uint16)
+    qh[rows] = dpsynth.kv_rows_host("bf16", w.seed, 3, 0, rows, C, H * D, cols).reshape(
+        len(rows), len(heads), D)
+    want = oracle.attention(qh, np.ascontiguousarray(kh), np.ascontiguousarray(vh), rows)
+    got = bits(o[torch.from_numpy(rows).to(dev)])[:, heads]
+    err = _check(got, want, "one-minute shape")
+    print("one-minute attention: %d keys, max |err| %.2e over %d queries x %d heads"
+          % (n, err, len(rows), len(heads)))
+
+
 def _ragged_case(rng, lens, H, D, pad):
     off = np.concatenate([[0], np.cumsum(np.asarray(lens, np.int64).ravel())]).astype(np.int64)
     kr = random_bf16_bits(rng, (int(off[-1]) + pad, D))

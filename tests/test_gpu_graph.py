@@ -10,7 +10,6 @@ import numpy as np
 import pytest
 import torch
 
-import compaction_dp_score_amd as dp
 import dpsynth
 import oracle
 from compaction_dp_score_amd.step import PruneStep

@@ -23,6 +23,11 @@ if not os.path.exists(LIB_PATH):
                       "python compaction_dp_score_amd/build.py)")
 
 _lib = ctypes.CDLL(LIB_PATH)
+ABI_VERSION = 1                # DP_ABI_VERSION of the include/decoprune.h this binding follows
+_lib.dp_abi_version.restype = ctypes.c_int
+if _lib.dp_abi_version() != ABI_VERSION:
+    raise ImportError("libdecoprune.so reports ABI %d, this binding follows ABI %d: rebuild it"
+                      % (_lib.dp_abi_version(), ABI_VERSION))
 
 DP_OK, DP_EINVAL, DP_EALIGN, DP_ERANGE, DP_ECAPACITY, DP_EHIP, DP_EUNSUPPORTED, DP_ESTALL = range(8)
 DP_F32, DP_BF16 = 0, 1

@@ -522,3 +522,63 @@ def test_tiny_workload_end_to_end():
     import __graft_entry__
     device()
     __graft_entry__.smoke()
+
+
+def test_compact_and_gather_at_the_int32_row_limit():
+    """Maximum size: 2^31 - 1 rows, the most an int32 row index addresses (the
+    API's limit).  A random keep mask (rows 0 and T - 1 kept) is compacted and
+    K and V rows of 16 bytes (one head of 8 bf16) are gathered; the index list
+    is checked to be ascending and to list exactly the kept rows, and every
+    gathered row against its source, in chunks, on the device."""
+    dev = device()
+    if torch.cuda.get_device_properties(0).total_memory < (200 << 30):
+        pytest.skip("needs about 140 GiB of device memory")
+    T = (1 << 31) - 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    keep = (torch.rand(T, device=dev, generator=g) < 0.3).to(torch.uint8)
+    keep[0] = 1
+    keep[T - 1] = 1
+    idx = torch.empty(T, dtype=torch.int32, device=dev)
+    n_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws = torch.empty(dp.dp_compact_workspace_bytes(T) // 4 + 1, dtype=torch.int32, device=dev)
+    dp.dp_compact_index(keep, T, idx, n_dev, None, None, ws)
+    torch.cuda.synchronize()
+    n = int(n_dev.item())
+    assert n == int(keep.sum(dtype=torch.int64).item())
+    assert int(idx[0].item()) == 0 and int(idx[n - 1].item()) == T - 1
+    step = 1 << 28
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        seg = idx[a:b].long()
+        assert bool((keep[seg] == 1).all().item())
+        if b - a > 1:
+            assert bool((seg[1:] > seg[:-1]).all().item())
+        if a > 0:
+            assert int(idx[a].item()) > int(idx[a - 1].item())
+        del seg
+    del ws
+    torch.cuda.empty_cache()
+
+    srcs = [torch.randint(-32768, 32767, (T, 1, 8), dtype=torch.int16, device=dev,
+                          generator=g).view(torch.bfloat16) for _ in range(2)]
+    dsts = [torch.empty((n, 1, 8), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    alive = []
+    kv = _kv_struct([srcs[0]], [srcs[1]], [dsts[0]], [dsts[1]], n, err, alive)
+    dp.dp_gather_kv(kv, idx, n_dev)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    # checked in chunks through the source window each chunk's (ascending)
+    # indices span, so no single torch launch sees a 2^31-row operand
+    step = 1 << 24
+    for s_, d_ in zip(srcs, dsts):
+        s16, d16 = s_.view(torch.int16), d_.view(torch.int16)
+        for a in range(0, n, step):
+            b = min(n, a + step)
+            lo, hi = int(idx[a].item()), int(idx[b - 1].item()) + 1
+            loc = idx[a:b].long() - lo
+            assert torch.equal(d16[a:b], s16[lo:hi].index_select(0, loc)), a
+    print("int32 row limit: %d rows, %d kept, gathered bit for bit" % (T, n))
+    del srcs, dsts, keep, idx
+    torch.cuda.empty_cache()

@@ -582,3 +582,55 @@ def test_compact_and_gather_at_the_int32_row_limit():
     print("int32 row limit: %d rows, %d kept, gathered bit for bit" % (T, n))
     del srcs, dsts, keep, idx
     torch.cuda.empty_cache()
+
+
+def test_score_mask_and_score_index_at_the_int32_row_limit():
+    """Maximum size for the mask and the one-call index: a 2^31 - 1 row
+    sequence with a sink, a window, one scored chunk (the eviction step's
+    6,240 scores) and history in between (kept in score mode).  dp_score_index
+    takes its separate-kernel path at this size; both calls must give the same
+    mask, and the index list the kept rows."""
+    dev = device()
+    if torch.cuda.get_device_properties(0).total_memory < (64 << 30):
+        pytest.skip("needs about 20 GiB of device memory")
+    T = (1 << 31) - 1
+    w = dpsynth.WORKLOADS["eviction"]
+    C, d = w.chunk_tokens, w.d
+    sink, window = C, 3 * C
+    x0, xf = dpsynth.score_inputs(w)
+    x0d, xfd = to_dev(x0, dev), to_dev(xf, dev)
+    pol = dp.make_policy(T, sink, window, sink, C, w.gamma)
+    keep = torch.empty(T, dtype=torch.uint8, device=dev)
+    dp.dp_score_mask(x0d, xfd, d, d, pol, None, keep)
+    want_sc = oracle.mask(oracle.score_f32(x0, xf, d), C, 0, 0, 0, C, w.gamma)
+    torch.cuda.synchronize()
+    assert np.array_equal(keep[sink:sink + C].cpu().numpy(), want_sc)
+    assert bool((keep[:sink] == 1).all().item()) and bool((keep[T - window:] == 1).all().item())
+    n_want = T - (C - int(want_sc.sum()))
+    assert int(keep.sum(dtype=torch.int64).item()) == n_want      # history rows all kept
+
+    keep2 = torch.empty(T, dtype=torch.uint8, device=dev)
+    idx = torch.empty(T, dtype=torch.int32, device=dev)
+    n_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws = torch.zeros(dp.dp_score_index_workspace_bytes(T) // 8 + 1, dtype=torch.int64, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dp.dp_score_index(x0d, xfd, d, d, pol, None, keep2, idx, n_dev, None, None, ws, err)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and int(n_dev.item()) == n_want
+    assert torch.equal(keep2, keep)
+    n = n_want
+    assert int(idx[0].item()) == 0 and int(idx[n - 1].item()) == T - 1
+    dropped = torch.from_numpy(np.flatnonzero(want_sc == 0) + sink).to(dev)
+    step = 1 << 24
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        seg = idx[a:b].long()
+        assert bool((keep[seg] == 1).all().item())
+        if b - a > 1:
+            assert bool((seg[1:] > seg[:-1]).all().item())
+        if a > 0:
+            assert int(idx[a].item()) > int(idx[a - 1].item())
+    assert not bool(torch.isin(dropped, idx[:sink + C].long()).any().item())
+    print("int32 row limit: mask and index over %d rows, %d kept" % (T, n))
+    del keep, keep2, idx, ws
+    torch.cuda.empty_cache()

@@ -634,3 +634,46 @@ def test_score_mask_and_score_index_at_the_int32_row_limit():
     print("int32 row limit: mask and index over %d rows, %d kept" % (T, n))
     del keep, keep2, idx, ws
     torch.cuda.empty_cache()
+
+
+def test_rope_reindex_at_the_int32_row_limit():
+    """Maximum size for the in-place re-index: 2^31 - 1 rows of one 8-dim bf16
+    head (4 temporal pairs, one 16-byte vector per row), 2,048 frames of 2^20
+    rows; the last frames lie within the knee and stay untouched.  Sampled rows
+    against the oracle."""
+    dev = device()
+    if torch.cuda.get_device_properties(0).total_memory < (64 << 30):
+        pytest.skip("needs about 40 GiB of device memory")
+    T, tpf, n_frames = (1 << 31) - 1, 1 << 20, 2048
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+    k = torch.randn((T, 1, 8), device=dev, generator=g, dtype=torch.bfloat16).mul_(2.0)
+    rf = torch.arange(T, device=dev, dtype=torch.int32) >> 20
+    theta = dpsynth.rope_theta(4)
+    ft = np.arange(n_frames, dtype=np.float32)
+    host = dict(theta=theta, frame_t=ft, frame_phase=ft.copy(), q0=float(n_frames), knee=6.0,
+                inv_factor=np.float32(0.125))
+    rows = np.unique(np.concatenate([[0, 1, tpf - 1, tpf, T // 2, T - tpf - 1, T - 2, T - 1],
+                                     np.random.default_rng(3).integers(0, T, 4000)]))
+    def sampled():                    # row views stacked: no launch sees a 2^31-row index
+        return bits(torch.stack([k[int(r)] for r in rows]))
+
+    before = sampled()
+    rope = dp.make_rope(to_dev(theta, dev), to_dev(ft, dev), to_dev(ft.copy(), dev), host["q0"],
+                        host["knee"], host["inv_factor"])
+    ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, 4) // 4 + 4, dtype=torch.float32,
+                     device=dev)
+    arr = dp.ptr_array([k], dev)
+    dp.dp_rope_reindex(arr, 1, 1, 8, dp.DP_BF16, T, None, rf, rope, ws)
+    torch.cuda.synchronize()
+    got = sampled()
+    tables = oracle.rope_frames(ft, ft.copy(), host["q0"], host["knee"], host["inv_factor"], theta)
+    want = before.copy()
+    oracle.rope_rows(want, (rows >> 20).astype(np.int32), 0, tables)
+    ok, worst, _ = keys_close(got, want, TOL[dp.DP_BF16])
+    assert ok, worst
+    recent = (n_frames - (rows >> 20)) <= host["knee"]
+    assert recent.any() and np.array_equal(got[recent], before[recent])
+    print("int32 row limit: re-index over %d rows, %d sampled" % (T, rows.shape[0]))
+    del k, rf, arr
+    torch.cuda.empty_cache()

@@ -255,3 +255,87 @@ def test_ring_rollout_matches_oracle_and_out_of_place():
     flat = canon(pk, pv, prf)
     assert np.array_equal(ring, flat)
     print("ring rollout: %d steps, %d live rows of %d slots+history" % (STEPS, live.shape[0], otail))
+
+
+@pytest.mark.parametrize("axis", [dp.DP_AXIS_PAGE, dp.DP_AXIS_COMPRESSED])
+def test_ring_step_helper_matches_the_calls(axis):
+    """compaction_dp_score_amd.step.RingStep enqueues the same calls as the
+    rollout above (page axis: append, prepare, re-index of the sink and the
+    history; compressed axis: prepare and the append with the re-index fused):
+    two rollouts on identical inputs, one through the helper and one through
+    the calls, agree bit for bit after every step (buffers, frames, tail,
+    phase table)."""
+    from compaction_dp_score_amd.step import RingStep
+    dev = device()
+    rng = np.random.default_rng(23)
+    n_frames = (R + 2 + STEPS) * F
+    theta = dpsynth.rope_theta(NPAIRS)
+    frame_t = np.arange(n_frames, dtype=np.float32)
+    cap = C + R * C + STEPS * C
+    kb = np.zeros((L, cap, H, D), np.uint16)
+    vb = np.zeros((L, cap, H, D), np.uint16)
+    kb[:, :(R + 1) * C] = random_bf16_bits(rng, (L, (R + 1) * C, H, D), 2.0)
+    vb[:, :(R + 1) * C] = random_bf16_bits(rng, (L, (R + 1) * C, H, D))
+    rf0 = np.full(cap, -1, np.int32)
+    rf0[:(R + 1) * C] = np.arange((R + 1) * C) // TPF
+    draws = []
+    for s in range(STEPS):
+        x0, xf = _scores(rng)
+        draws.append((to_dev(x0, dev), to_dev(xf, dev), random_bf16_bits(rng, (L, C, H, D), 2.0),
+                      random_bf16_bits(rng, (L, C, H, D))))
+    th_d, ft_d = to_dev(theta, dev), to_dev(frame_t, dev)
+
+    def fresh():
+        k, v = _dev(kb, dp.DP_BF16, dev), _dev(vb, dp.DP_BF16, dev)
+        return (k, v, to_dev(rf0, dev), torch.tensor([(R + 1) * C], dtype=torch.int64, device=dev),
+                to_dev(frame_t.copy(), dev))
+
+    # through the helper
+    hk, hv, hrf, htail, hphase = fresh()
+    step = RingStep(k_layers=hk, v_layers=hv, sink_len=C, chunk_rows=C, n_slots=R, row_frame=hrf,
+                    tail=htail, d=16, gamma=0.1,
+                    rope=dict(theta=th_d, frame_t=ft_d, frame_phase=hphase, knee=KNEE,
+                              inv_factor=1.0 / FACTOR), axis=axis)
+    # through the calls
+    mk, mv, mrf, mtail, mphase = fresh()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    alive = []
+    kv = _inplace(mk, mv, dp.DP_BF16, cap, err, alive)
+    arr_k = dp.ptr_array(mk, dev)
+    ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, NPAIRS) // 4 + 4, dtype=torch.float32,
+                     device=dev)
+    keep = torch.empty(C, dtype=torch.uint8, device=dev)
+    idx = torch.empty(C, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64,
+                        device=dev)
+    for s in range(STEPS):
+        x0d, xfd, k_new, v_new = draws[s]
+        slot = s % R
+        sb = C + slot * C
+        q0 = float((R + 1 + s) * F)
+        new_rf = torch.from_numpy((R + 1 + s) * F + np.arange(C, dtype=np.int32) // TPF).to(dev)
+        step.evict(slot, x0d, xfd, q0)
+        dp.dp_score_index(x0d, xfd, 16, 16, dp.make_policy(C, 0, 0, 0, C, 0.1), None, keep, idx,
+                          nk, None, None, ws_si, err)
+        rope = dp.make_rope(th_d, ft_d, mphase, q0, KNEE, 1.0 / FACTOR, axis=axis)
+        dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws)
+        if axis == dp.DP_AXIS_COMPRESSED:
+            dp.dp_append_kept(kv, sb, C, idx, nk, mtail, mrf, rope, ws)
+        else:
+            dp.dp_append_kept(kv, sb, C, idx, nk, mtail, mrf)
+            dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, 0, C, None, mrf, rope, ws)
+            dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, C + R * C, cap, mtail, mrf, rope, ws)
+        for l in range(L):                       # the model writes the next chunk into the slot
+            for k_, v_ in ((hk, hv), (mk, mv)):
+                k_[l][sb:sb + C] = bf16_from_bits(k_new[l], dev)
+                v_[l][sb:sb + C] = bf16_from_bits(v_new[l], dev)
+        step.write_chunk(slot, new_rf)
+        mrf[sb:sb + C] = new_rf
+        torch.cuda.synchronize()
+        assert err.item() == 0 and step.dev_error.item() == 0, s
+        assert htail.item() == mtail.item(), s
+        assert torch.equal(hrf, mrf) and torch.equal(hphase, mphase), s
+        for l in range(L):
+            assert torch.equal(hk[l].view(torch.int16), mk[l].view(torch.int16)), (s, l)
+            assert torch.equal(hv[l].view(torch.int16), mv[l].view(torch.int16)), (s, l)

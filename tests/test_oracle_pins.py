@@ -475,6 +475,49 @@ def test_hs_offsets_and_heads():
             assert np.array_equal(out[off[i]:off[i + 1]], src[l][rows, h]), (l, h)
 
 
+@pytest.mark.parametrize("dtype", [np.float32, np.uint16])
+def test_rope_headrows_equals_rope_rows_and_complex_rotation(dtype):
+    """The re-index of a per-head packed cache (DeCoPrune-HS, section 무엇과
+    다른가: the ragged per-head runs are re-indexed like the token-major
+    cache): on the [rows * H, D] view of a token-major cache, with every head
+    row carrying its token's frame, it equals rope_rows bit for bit; with a
+    frame of its own per head row (as the packed HS runs have) each head row
+    is its frame's float64 complex rotation (fp32 keys), dims outside the
+    temporal block and rows of frames with delta 0 stay bit for bit."""
+    rng = np.random.default_rng(31)
+    rows, H, D, npairs, pb = 48, 3, 64, 12, 2
+    theta = dpsynth.rope_theta(npairs)
+    t = np.arange(10, dtype=np.float32)
+    tab = oracle.rope_frames(t, t, 10.0, 2.0, 0.25, theta)     # frames 8, 9: delta 0
+    assert np.unique(tab[0]).shape[0] == 9
+    if dtype == np.float32:
+        k = rng.standard_normal((rows, H, D)).astype(np.float32)
+    else:
+        k = _bf16(rng, (rows, H, D), 2.0)
+    rf = rng.permutation(np.arange(rows) % 10).astype(np.int32)
+    tok = oracle.rope_rows(k.copy(), rf, pb, tab)
+    flat = oracle.rope_headrows(k.reshape(rows * H, D).copy(), np.repeat(rf, H), pb, tab)
+    assert np.array_equal(flat.reshape(rows, H, D), tok)
+    # a frame per head row
+    rfh = rng.integers(0, 10, rows * H).astype(np.int32)
+    got = oracle.rope_headrows(k.reshape(rows * H, D).copy(), rfh, pb, tab)
+    src = k.reshape(rows * H, D)
+    keep_dims = np.ones(D, bool)
+    keep_dims[2 * pb:2 * (pb + npairs)] = False
+    assert np.array_equal(got[:, keep_dims], src[:, keep_dims])
+    still = tab[0][rfh] == 0
+    assert np.array_equal(got[still], src[still])
+    if dtype == np.float32:
+        want = _rot_f64(src[:, None, :], rfh, pb, theta, tab[0].astype(np.float64))[:, 0]
+        assert np.max(np.abs(got.astype(np.float64) - want)) < 2e-6
+    else:
+        want = _rot_f64(_f(src)[:, None, :], rfh, pb, theta, tab[0].astype(np.float64))[:, 0]
+        # one bf16 rounding of each rotated element (half an ulp: at most 2^-8
+        # relative) on top of the fp32 products and sums (a few 2^-24 of the pair)
+        err = np.abs(_f(got) - want)
+        assert np.all(err <= np.abs(want) * 2.0 ** -8 + 4 * 2.0 ** -24 * np.abs(_f(src)).max())
+
+
 # --------------------------------------------------------------------------
 # Attention over the retained cache
 # --------------------------------------------------------------------------
@@ -566,6 +609,46 @@ def test_attention_invariants_and_two_key_closed_form():
                                rtol=1e-12, atol=1e-13)
 
 
+def test_attention_f64_equals_bf16_form_and_closed_forms():
+    """The float64-input attention (the reference for keys that are not rounded
+    to a storage type): on the exact float64 widening of bf16 inputs it is the
+    bf16-input attention bit for bit (the same sums in the same order); on
+    float64 inputs that no bf16 holds it satisfies the closed forms: a zero
+    query gives the mean of V, one key gives its value, two keys weigh by the
+    logistic function of their scaled score gap, adding c to every value row
+    adds c, and the order of keys does not matter."""
+    rng = np.random.default_rng(32)
+    nq, nk, H, D = 5, 41, 2, 16
+    q, k, v = _bf16(rng, (nq, H, D)), _bf16(rng, (nk, H, D)), _bf16(rng, (nk, H, D))
+    rows = np.array([0, 2, 4])
+    for scale in (None, 0.37):
+        a = oracle.attention(q, k, v, rows, n_kv=33, scale=scale)
+        b = oracle.attention(_f(q), _f(k), _f(v), rows, n_kv=33, scale=scale)
+        assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+    qd = rng.standard_normal((nq, H, D)) * 0.7
+    kd = rng.standard_normal((nk, H, D)) * 0.7
+    vd = rng.standard_normal((nk, H, D))
+    got = oracle.attention(np.zeros((1, H, D)), kd, vd, [0])
+    assert np.allclose(got[0], vd.mean(axis=0), rtol=1e-12, atol=1e-14)
+    got = oracle.attention(qd, kd, vd, [1], n_kv=1)
+    assert np.array_equal(got[0], vd[0])
+    sc = 0.37
+    got = oracle.attention(qd, kd[:2], vd[:2], np.arange(nq), scale=sc)
+    for i in range(nq):
+        for h in range(H):
+            gap = sc * (qd[i, h] @ kd[0, h] - qd[i, h] @ kd[1, h])
+            w0 = 1.0 / (1.0 + np.exp(-gap))
+            assert np.allclose(got[i, h], w0 * vd[0, h] + (1 - w0) * vd[1, h],
+                               rtol=1e-12, atol=1e-13)
+    base = oracle.attention(qd, kd, vd, np.arange(nq), scale=sc)
+    shift = rng.standard_normal(D)
+    assert np.allclose(oracle.attention(qd, kd, vd + shift, np.arange(nq), scale=sc),
+                       base + shift, rtol=1e-12, atol=1e-12)
+    perm = rng.permutation(nk)
+    assert np.allclose(oracle.attention(qd, kd[perm], vd[perm], np.arange(nq), scale=sc), base,
+                       rtol=1e-12, atol=1e-14)
+
+
 def test_hs_attention_per_head_runs_against_numpy():
     """Each head of the chosen layer sees exactly its own run followed by the
     chunk rows; a head with no rows gives zeros (numpy float64 softmax)."""
@@ -612,6 +695,60 @@ def test_hs_attention_with_shared_runs_equals_dense_attention():
     want = oracle.attention(q, np.concatenate([k[keep], kc]), np.concatenate([v[keep], vc]),
                             np.arange(nq))
     assert np.allclose(got, want, rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# One whole prune step
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("reversed_", [False, True])
+def test_prune_step_on_the_tiny_workload(reversed_):
+    """The composition the smoke check compares against, on the tiny workload
+    (1 layer, 2 heads x 64, fp32, 8 chunks of 64 rows, gamma 0.1, sink chunk 0,
+    chunks 1-5 scored, window of 2 chunks; 8 temporal pairs, q0 = 8, knee 2,
+    factor 4), against facts from outside the oracle: the mask from a float64
+    numpy score (no row lies within rounding of gamma), the index list from
+    numpy.flatnonzero, K and V rows by numpy advanced indexing (V and the
+    non-temporal dims of K bit for bit), the row frames likewise, the new
+    phases from exact rationals and the re-indexed key pairs from float64
+    complex rotation by theta_j (t~ - t) (DeCoPrune page, 어떻게 동작하나 and
+    무엇과 다른가)."""
+    w = dpsynth.WORKLOADS["tiny"]
+    T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
+    x0, xf = dpsynth.score_inputs(w)
+    k = np.stack([dpsynth.kv_layer_host("f32", w.seed, dpsynth.STREAM_K, l, T, H * D)
+                  for l in range(L)]).reshape(L, T, H, D)
+    v = np.stack([dpsynth.kv_layer_host("f32", w.seed, dpsynth.STREAM_V, l, T, H * D)
+                  for l in range(L)]).reshape(L, T, H, D)
+    rf = dpsynth.row_frame(w)
+    theta = dpsynth.rope_theta(w.rope_pairs, w.rope_base)
+    ft, fp = dpsynth.frame_tables(w)
+    got = oracle.prune_step(
+        x0, xf, w.d, dict(seq_len=T, sink_len=w.sink_len, window_len=w.window_len,
+                          scored_begin=w.scored_begin, n_scored=w.n_scored, gamma=w.gamma,
+                          reversed=reversed_),
+        k, v, rf, dict(theta=theta, frame_t=ft, frame_phase=fp, q0=w.q0, knee=w.rope_knee,
+                       inv_factor=np.float32(1.0 / w.rope_factor)))
+    ell = ((x0.astype(np.float64) - xf.astype(np.float64)) ** 2).mean(axis=1)
+    assert np.min(np.abs(ell - w.gamma)) > 1e-5 * w.gamma
+    big = ell >= w.gamma
+    keep = np.ones(T, np.uint8)
+    keep[w.scored_begin:w.scored_begin + w.n_scored] = (~big if reversed_ else big)
+    assert np.array_equal(got["keep"], keep)
+    idx = np.flatnonzero(keep)
+    assert np.array_equal(got["idx"], idx)
+    assert np.array_equal(got["v"].view(np.uint32), v[:, idx].view(np.uint32))
+    assert np.array_equal(got["row_frame"], rf[idx])
+    lo, hi = 0, 2 * w.rope_pairs
+    assert np.array_equal(got["k"][..., hi:].view(np.uint32), k[:, idx][..., hi:].view(np.uint32))
+    t_new = np.array([float(_t_new_exact(w.q0, w.rope_knee, Fraction(w.rope_factor), f))
+                      for f in range(w.n_frames)])
+    assert np.array_equal(got["tables"][3].astype(np.float64), t_new)
+    step = t_new - ft.astype(np.float64)
+    for l in range(L):
+        want = _rot_f64(k[l][idx], rf[idx], 0, theta, step)
+        assert np.max(np.abs(got["k"][l].astype(np.float64) - want)) < 2e-6
+    assert np.array_equal(got["k"][..., lo:hi][:, idx >= T - w.window_len],
+                          k[:, idx[idx >= T - w.window_len]][..., lo:hi])
 
 
 # --------------------------------------------------------------------------

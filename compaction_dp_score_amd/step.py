@@ -117,22 +117,42 @@ class RingStep:
       page axis        dp_rope_prepare, then dp_rope_apply over the sink and
                        over the history [history_begin, tail) (the appended
                        rows included);
-      compressed axis  dp_rope_prepare, and the leaving chunk's one re-index
-                       fused into the append; no old key is rewritten (the
-                       attention turns its query back by the common lag,
+      compressed axis  dp_rope_prepare, dp_rope_apply over the sink (its
+                       frames move from t to t/c once, when they pass the
+                       knee; rows whose frame does not move are neither read
+                       nor written), and the leaving chunk's one re-index
+                       fused into the append; no history key is rewritten
+                       (the attention turns its query back by the common lag,
                        dp_attention_lag).
+
+    The window slots are never re-indexed, which is right only while every
+    frame of the window lies within the knee: with F frames per chunk and
+    n_slots - 1 window chunks after an eviction, the knee must be at least
+    (n_slots - 1) F.  On the compressed axis the leaving chunk must also be
+    wholly past the knee when it is appended (knee < (n_slots - 1) F + 1),
+    since no history key is visited afterwards.  The constructor checks both.
 
     The model then writes the next chunk's K and V into the freed slot and
     calls ``write_chunk(slot, frames)`` with the rows' frames.  Nothing here
     computes; it allocates once and marshals arguments.
     """
 
-    def __init__(self, *, k_layers, v_layers, sink_len, chunk_rows, n_slots, row_frame, tail,
-                 d, gamma, rope, axis=0):
+    def __init__(self, *, k_layers, v_layers, sink_len, chunk_rows, n_slots, frames_per_chunk,
+                 row_frame, tail, d, gamma, rope, axis=0):
         """row_frame: device int32 [capacity]; tail: device int64 [1] (the end
-        of the visible rows); rope: dict with theta, frame_t, frame_phase
-        (device tensors), knee, inv_factor and optionally pair_begin (q0 is
-        given per eviction); axis: DP_AXIS_PAGE or DP_AXIS_COMPRESSED."""
+        of the visible rows); frames_per_chunk: latent frames of one chunk;
+        rope: dict with theta, frame_t, frame_phase (device tensors), knee,
+        inv_factor and optionally pair_begin (q0 is given per eviction); axis:
+        DP_AXIS_PAGE or DP_AXIS_COMPRESSED."""
+        span = (n_slots - 1) * frames_per_chunk          # frames of the window after an eviction
+        knee = float(rope["knee"])
+        if knee < span:
+            raise ValueError("RingStep: knee %g < window span %d frames: window keys would keep "
+                             "their phase past the knee" % (knee, span))
+        if axis == DP_AXIS_COMPRESSED and knee >= span + 1:
+            raise ValueError("RingStep: on the compressed axis the knee (%g) must lie below %d "
+                             "frames, so that the leaving chunk is past it when appended"
+                             % (knee, span + 1))
         dev = k_layers[0].device
         cap, heads, hd = k_layers[0].shape
         self.capacity, self.heads, self.head_dim = cap, heads, hd
@@ -179,6 +199,8 @@ class RingStep:
         rope = self._rope(q0)
         dp_rope_prepare(rope, self.head_dim, self.dtype, self.ws_rope, stream)
         if self.axis == DP_AXIS_COMPRESSED:
+            dp_rope_apply(self.arr_k, self.n_layers, self.heads, self.head_dim, self.dtype, 0,
+                          self.sink_len, None, self.row_frame, rope, self.ws_rope, stream)
             dp_append_kept(self.kv, begin, self.chunk_rows, self.idx, self.n_kept, self.tail,
                            self.row_frame, rope, self.ws_rope, stream)
             return

@@ -258,13 +258,17 @@ def test_ring_rollout_matches_oracle_and_out_of_place():
 
 
 @pytest.mark.parametrize("axis", [dp.DP_AXIS_PAGE, dp.DP_AXIS_COMPRESSED])
-def test_ring_step_helper_matches_the_calls(axis):
-    """compaction_dp_score_amd.step.RingStep enqueues the same calls as the
-    rollout above (page axis: append, prepare, re-index of the sink and the
-    history; compressed axis: prepare and the append with the re-index fused):
-    two rollouts on identical inputs, one through the helper and one through
-    the calls, agree bit for bit after every step (buffers, frames, tail,
-    phase table)."""
+def test_ring_step_helper_against_oracle(axis):
+    """compaction_dp_score_amd.step.RingStep rolled six evictions forward,
+    against the oracle's own rollout of the ring layout on the same inputs:
+    the leaving chunk's score, mask and index list, its append at the tail
+    (K, V and frames), then the page's re-index of every live key for the new
+    q0 (on the compressed axis the frames past the knee take the phase t/c),
+    the window rows included, with no assumption about which rows move.
+    After every step: tail, row frames and phase table exact, V bit for bit,
+    K within the re-index tolerance (DeCoPrune page, 어떻게 동작하나 and
+    무엇과 다른가).  On the compressed axis the sink crosses the knee at the
+    first step, so a helper that left it out fails here."""
     from compaction_dp_score_amd.step import RingStep
     dev = device()
     rng = np.random.default_rng(23)
@@ -278,64 +282,76 @@ def test_ring_step_helper_matches_the_calls(axis):
     vb[:, :(R + 1) * C] = random_bf16_bits(rng, (L, (R + 1) * C, H, D))
     rf0 = np.full(cap, -1, np.int32)
     rf0[:(R + 1) * C] = np.arange((R + 1) * C) // TPF
-    draws = []
-    for s in range(STEPS):
-        x0, xf = _scores(rng)
-        draws.append((to_dev(x0, dev), to_dev(xf, dev), random_bf16_bits(rng, (L, C, H, D), 2.0),
-                      random_bf16_bits(rng, (L, C, H, D))))
     th_d, ft_d = to_dev(theta, dev), to_dev(frame_t, dev)
-
-    def fresh():
-        k, v = _dev(kb, dp.DP_BF16, dev), _dev(vb, dp.DP_BF16, dev)
-        return (k, v, to_dev(rf0, dev), torch.tensor([(R + 1) * C], dtype=torch.int64, device=dev),
-                to_dev(frame_t.copy(), dev))
-
-    # through the helper
-    hk, hv, hrf, htail, hphase = fresh()
-    step = RingStep(k_layers=hk, v_layers=hv, sink_len=C, chunk_rows=C, n_slots=R, row_frame=hrf,
-                    tail=htail, d=16, gamma=0.1,
+    hk, hv = _dev(kb, dp.DP_BF16, dev), _dev(vb, dp.DP_BF16, dev)
+    hrf = to_dev(rf0, dev)
+    htail = torch.tensor([(R + 1) * C], dtype=torch.int64, device=dev)
+    hphase = to_dev(frame_t.copy(), dev)
+    step = RingStep(k_layers=hk, v_layers=hv, sink_len=C, chunk_rows=C, n_slots=R,
+                    frames_per_chunk=F, row_frame=hrf, tail=htail, d=16, gamma=0.1,
                     rope=dict(theta=th_d, frame_t=ft_d, frame_phase=hphase, knee=KNEE,
                               inv_factor=1.0 / FACTOR), axis=axis)
-    # through the calls
-    mk, mv, mrf, mtail, mphase = fresh()
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    alive = []
-    kv = _inplace(mk, mv, dp.DP_BF16, cap, err, alive)
-    arr_k = dp.ptr_array(mk, dev)
-    ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, NPAIRS) // 4 + 4, dtype=torch.float32,
-                     device=dev)
-    keep = torch.empty(C, dtype=torch.uint8, device=dev)
-    idx = torch.empty(C, dtype=torch.int32, device=dev)
-    nk = torch.zeros(1, dtype=torch.int64, device=dev)
-    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64,
-                        device=dev)
+    compressed = axis == dp.DP_AXIS_COMPRESSED
+    ok_, ov_, orf, otail, ophase = kb.copy(), vb.copy(), rf0.copy(), (R + 1) * C, frame_t.copy()
     for s in range(STEPS):
-        x0d, xfd, k_new, v_new = draws[s]
+        x0, xf = _scores(rng)
+        k_new = random_bf16_bits(rng, (L, C, H, D), 2.0)
+        v_new = random_bf16_bits(rng, (L, C, H, D))
         slot = s % R
         sb = C + slot * C
-        q0 = float((R + 1 + s) * F)
-        new_rf = torch.from_numpy((R + 1 + s) * F + np.arange(C, dtype=np.int32) // TPF).to(dev)
-        step.evict(slot, x0d, xfd, q0)
-        dp.dp_score_index(x0d, xfd, 16, 16, dp.make_policy(C, 0, 0, 0, C, 0.1), None, keep, idx,
-                          nk, None, None, ws_si, err)
-        rope = dp.make_rope(th_d, ft_d, mphase, q0, KNEE, 1.0 / FACTOR, axis=axis)
-        dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws)
-        if axis == dp.DP_AXIS_COMPRESSED:
-            dp.dp_append_kept(kv, sb, C, idx, nk, mtail, mrf, rope, ws)
-        else:
-            dp.dp_append_kept(kv, sb, C, idx, nk, mtail, mrf)
-            dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, 0, C, None, mrf, rope, ws)
-            dp.dp_rope_apply(arr_k, L, H, D, dp.DP_BF16, C + R * C, cap, mtail, mrf, rope, ws)
-        for l in range(L):                       # the model writes the next chunk into the slot
-            for k_, v_ in ((hk, hv), (mk, mv)):
-                k_[l][sb:sb + C] = bf16_from_bits(k_new[l], dev)
-                v_[l][sb:sb + C] = bf16_from_bits(v_new[l], dev)
-        step.write_chunk(slot, new_rf)
-        mrf[sb:sb + C] = new_rf
-        torch.cuda.synchronize()
-        assert err.item() == 0 and step.dev_error.item() == 0, s
-        assert htail.item() == mtail.item(), s
-        assert torch.equal(hrf, mrf) and torch.equal(hphase, mphase), s
+        q0 = float((R + 1 + s) * F)                 # first frame of the next chunk
+        new_frames = ((R + 1 + s) * F + np.arange(C) // TPF).astype(np.int32)
+        step.evict(slot, to_dev(x0, dev), to_dev(xf, dev), q0)
+        for l in range(L):                          # the model writes the next chunk
+            hk[l][sb:sb + C] = bf16_from_bits(k_new[l], dev)
+            hv[l][sb:sb + C] = bf16_from_bits(v_new[l], dev)
+        step.write_chunk(slot, to_dev(new_frames, dev))
+        # oracle
+        widx = oracle.compact(oracle.mask(oracle.score_f32(x0, xf), C, 0, 0, 0, C, 0.1))
+        t_before = otail
+        otail = oracle.append_kept(ok_, sb, C, widx, otail, orf)
+        oracle.append_kept(ov_, sb, C, widx, t_before, None)
+        tables = oracle.rope_frames(frame_t, ophase, q0, KNEE, np.float32(1.0 / FACTOR), theta,
+                                    compressed=compressed)
+        ophase = tables[3]
         for l in range(L):
-            assert torch.equal(hk[l].view(torch.int16), mk[l].view(torch.int16)), (s, l)
-            assert torch.equal(hv[l].view(torch.int16), mv[l].view(torch.int16)), (s, l)
+            view = ok_[l][:otail]
+            _rope_rows_valid(view, orf[:otail], tables)
+        ok_[:, sb:sb + C], ov_[:, sb:sb + C] = k_new, v_new
+        orf[sb:sb + C] = new_frames
+        torch.cuda.synchronize()
+        assert step.dev_error.item() == 0, s
+        assert htail.item() == otail, s
+        assert np.array_equal(hrf.cpu().numpy(), orf), s
+        assert np.array_equal(hphase.cpu().numpy(), ophase), s
+        for l in range(L):
+            assert np.array_equal(bits(hv[l]), ov_[l]), (s, l)
+            good, worst, _ = keys_close(bits(hk[l]), ok_[l], 2e-2)
+            assert good, (s, l, worst)
+    if compressed:                                  # every live key past the knee is at t/c
+        live = np.flatnonzero(orf[:otail] >= 0)
+        past = q0 - frame_t[orf[live]] > KNEE
+        assert np.array_equal(ophase[orf[live][past]], frame_t[orf[live][past]] / FACTOR)
+
+
+def test_ring_step_knee_must_cover_the_window():
+    """A knee below the window span would leave window keys at their written
+    phase past the knee; on the compressed axis a knee a frame or more above it
+    would append rows that cross it later in the history, where no key is
+    visited again: the helper refuses both."""
+    from compaction_dp_score_amd.step import RingStep
+    dev = device()
+    k = [torch.zeros((8 * C, H, D), dtype=torch.bfloat16, device=dev)]
+    args = dict(k_layers=k, v_layers=None, sink_len=C, chunk_rows=C, n_slots=R,
+                frames_per_chunk=F, row_frame=torch.full((8 * C,), -1, dtype=torch.int32,
+                                                         device=dev),
+                tail=torch.zeros(1, dtype=torch.int64, device=dev), d=16, gamma=0.1)
+    rope = dict(theta=torch.ones(NPAIRS, device=dev), frame_t=torch.zeros(4, device=dev),
+                frame_phase=torch.zeros(4, device=dev), inv_factor=0.25)
+    for axis in (dp.DP_AXIS_PAGE, dp.DP_AXIS_COMPRESSED):
+        with pytest.raises(ValueError):
+            RingStep(rope=dict(rope, knee=KNEE - 0.5), axis=axis, **args)
+        RingStep(rope=dict(rope, knee=KNEE), axis=axis, **args)
+    with pytest.raises(ValueError):
+        RingStep(rope=dict(rope, knee=KNEE + 1), axis=dp.DP_AXIS_COMPRESSED, **args)
+    RingStep(rope=dict(rope, knee=KNEE + 1), axis=dp.DP_AXIS_PAGE, **args)

@@ -178,3 +178,29 @@ def test_score_index_graph_replays():
         torch.cuda.synchronize()
         want = oracle.mask(oracle.score_f32(x0, xf), T, sink, window, sb, ns, 0.1)
         f.check(T, want)
+
+
+def test_score_index_reports_a_workspace_not_zero_filled():
+    """A workspace whose ticket word was never cleared hands every workgroup a
+    tile number past the launch's last tile: each one records DP_ESTALL and
+    returns at once, writing no mask, index or count (no wait is entered).
+    Zero-filling the workspace again makes the next call correct."""
+    dev = device()
+    rng = np.random.default_rng(41)
+    T, sink, window, d = 31200, 6240, 18720, 64
+    sb, ns = sink, 6240
+    x0, xf = _score_case(rng, ns, d, d, 0.05, 0.44)
+    x0d, xfd = to_dev(x0, dev), to_dev(xf, dev)
+    pol = dp.make_policy(T, sink, window, sb, ns, 0.1)
+    f = Fused(dev, T)
+    f.ws.view(torch.int32)[0] = 0x7FFF0000          # ticket word: far past any tile count
+    f.n.fill_(-5)
+    f.run(x0d, xfd, d, d, pol)
+    torch.cuda.synchronize()
+    assert int(f.err.item()) == dp.DP_ESTALL
+    assert int(f.n.item()) == -5
+    assert np.all(f.idx.cpu().numpy() == -7) and np.all(f.keep.cpu().numpy() == 9)
+    f.ws.zero_()
+    f.err.zero_()
+    f.run(x0d, xfd, d, d, pol)
+    f.check(T, oracle.mask(oracle.score_f32(x0, xf), T, sink, window, sb, ns, 0.1))

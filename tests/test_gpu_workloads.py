@@ -2,10 +2,16 @@
 configuration bench.py times (one gather launch over all layers, K and V).
 
 Mask, kept-index list, counts, offsets and frame phases are compared with the
-oracle on every row; gathered / re-indexed K and V on sampled rows, whose
-expected values the oracle computes one by one from inputs regenerated on the
-host (the key/value generator is counter-based).  Bars: bit-exact for masks,
-indices and V; keys within max-abs 2e-2 (bf16) / 1e-5 (fp32).
+oracle on every row.  Gathered / re-indexed K and V are compared on every
+element of every layer: on the device against the source rows at the oracle's
+index list (V and the dims outside the temporal block bit for bit, rows whose
+frame does not move bit for bit, temporal pairs within the bar of the float64
+rotation by the oracle's own cos/sin tables), and, for whole layers, on the
+host against the C oracle's gather and re-index of the source copied back.
+The sources are the seeded generator's fill (tied to its host twin on sampled
+rows); the in-place passes regenerate their source into a scratch buffer.
+Bars: bit-exact for masks, indices and V; keys within max-abs 2e-2 (bf16) /
+1e-5 (fp32).
 """
 import numpy as np
 import pytest
@@ -20,6 +26,7 @@ from gpu_helpers import bits, device, keys_close
 pytestmark = pytest.mark.gpu
 
 TOL_BF16 = 2e-2
+BLOCK_ELEMS = 1 << 24          # elements of one device comparison block
 
 
 def _free():
@@ -27,30 +34,26 @@ def _free():
     torch.cuda.empty_cache()
 
 
-def _sample_rows(n, boundaries, k=48, seed=0):
-    rng = np.random.default_rng(seed)
-    pts = {0, 1, n - 2, n - 1}
-    for b in boundaries:
-        for d in (-2, -1, 0, 1):
-            if 0 <= b + d < n:
-                pts.add(int(b + d))
-    pts.update(int(x) for x in rng.integers(0, n, k))
-    return np.array(sorted(p for p in pts if 0 <= p < n), np.int64)
-
-
-def _fill(dev, w, rows, layers, stream_id):
+def _fill(dev, w, rows, layers, stream_id, heads=None):
+    heads = w.n_heads if heads is None else heads
     out = []
     for l in layers:
-        t = torch.empty((rows, w.n_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-        dpsynth.kv_fill_device(t, "bf16", w.seed, stream_id, l, rows, w.n_heads * w.head_dim)
+        t = torch.empty((rows, heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        dpsynth.kv_fill_device(t, "bf16", w.seed, stream_id, l, rows, heads * w.head_dim)
         out.append(t)
     return out
 
 
-def _expected_rows(w, layer, stream_id, src_rows, total_rows):
-    r = dpsynth.kv_rows_host("bf16", w.seed, stream_id, layer, src_rows, total_rows,
-                             w.n_heads * w.head_dim)
-    return np.ascontiguousarray(r.reshape(len(src_rows), w.n_heads, w.head_dim))
+def _tie_to_host(t, w, layer, stream_id, rows_total, heads=None):
+    """The device fill of one layer equals the generator's host twin on
+    sampled rows (so the fill is the documented input)."""
+    heads = w.n_heads if heads is None else heads
+    n = t.shape[0]
+    rows = np.unique(np.array([0, 1, n // 3, n // 2, n - 2, n - 1], np.int64))
+    host = dpsynth.kv_rows_host("bf16", w.seed, stream_id, layer, rows, rows_total,
+                                heads * w.head_dim)
+    assert np.array_equal(bits(t[torch.from_numpy(rows).to(t.device)]).reshape(len(rows), -1),
+                          host), layer
 
 
 def _rope_host(w, q0=None):
@@ -67,14 +70,71 @@ def _rope_dev(host, dev):
                 q0=host["q0"], knee=host["knee"], inv_factor=float(host["inv_factor"]))
 
 
-def _tables(host):
+def _tables(host, compressed=False):
     return oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
-                              host["inv_factor"], host["theta"])
+                              host["inv_factor"], host["theta"], compressed=compressed)
+
+
+def _tables_dev(tables, dev):
+    return tuple(torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in tables[:3])
+
+
+def _i64(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(dev)
+
+
+def _same(a, b):
+    """Bit-for-bit equality of two bf16 device tensors."""
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def _check_rotated(got, src, frames, tabd, n_pairs, pair_begin=0, tol=TOL_BF16):
+    """Every element of got [n, H, D] (bf16, device) against src [n, H, D]
+    re-indexed for the frames ``frames`` (device int64 [n]) with the oracle's
+    tables tabd = (delta, cos, sin) on the device: dims outside the temporal
+    block and rows whose frame has delta 0 bit for bit; temporal pairs within
+    tol of the float64 rotation (a c - b s, a s + b c) by the oracle's cos/sin
+    entries.  Returns (max |error|, count of elements that differ from that
+    rotation rounded to bf16)."""
+    delta, ct, st = tabd
+    lo, hi = 2 * pair_begin, 2 * (pair_begin + n_pairs)
+    worst, inexact = 0.0, 0
+    rb = max(1, BLOCK_ELEMS // max(1, got[0].numel()))
+    for b in range(0, got.shape[0], rb):
+        g, x, f = got[b:b + rb], src[b:b + rb], frames[b:b + rb]
+        assert _same(g[..., :lo], x[..., :lo]) and _same(g[..., hi:], x[..., hi:])
+        still = delta[f] == 0
+        assert _same(g[still], x[still])
+        xd = x[..., lo:hi].double()
+        a, bb = xd[..., 0::2], xd[..., 1::2]
+        c, sn = ct[f][:, None, :].double(), st[f][:, None, :].double()
+        want = torch.empty_like(xd)
+        want[..., 0::2] = a * c - bb * sn
+        want[..., 1::2] = a * sn + bb * c
+        gd = g[..., lo:hi].double()
+        worst = max(worst, float((gd - want).abs().max().item()) if gd.numel() else 0.0)
+        inexact += int((gd != want.to(torch.bfloat16).double()).sum().item())
+    assert worst <= tol, worst
+    return worst, inexact
+
+
+def _oracle_layer(src_k, src_v, idx, got_k, got_v, rf2=None, tables=None, tol=TOL_BF16):
+    """One whole layer through the C oracle: gather of the source copied back
+    (K and V), the K re-index, every element compared."""
+    want_k = oracle.gather(bits(src_k)[None], idx)[0]
+    if tables is not None:
+        oracle.rope_rows(want_k, rf2, 0, tables)
+    ok, worst, ne = keys_close(bits(got_k), want_k, tol)
+    assert ok, worst
+    if src_v is not None:
+        assert np.array_equal(bits(got_v), oracle.gather(bits(src_v)[None], idx)[0])
+    return ne
 
 
 def test_eviction_step_full_size():
     """40 layers x 40 heads x 128 bf16, K and V, 31,200 tokens; score, mask,
-    index and gather with the fused re-index in one step."""
+    index and gather with the fused re-index in one step.  K and V of all 40
+    layers element by element; layers 0, 19 and 39 also through the C oracle."""
     dev = device()
     w = dpsynth.WORKLOADS["eviction"]
     T, L = w.seq_len, w.n_layers
@@ -110,26 +170,28 @@ def test_eviction_step_full_size():
     dp.dp_pr_add(c, L * w.n_heads * n, L * w.n_heads * T)
     assert abs(dp.dp_pr_value(c) - oracle.pr(n, T)) < 1e-15
 
-    js = _sample_rows(n, [w.sink_len, int(np.searchsorted(idx, T - w.window_len))])
-    inexact = 0
-    for l in (0, 13, 27, L - 1):
-        got_k = bits(k_dst[l][torch.from_numpy(js).to(dev)])
-        got_v = bits(v_dst[l][torch.from_numpy(js).to(dev)])
-        want_v = _expected_rows(w, l, dpsynth.STREAM_V, idx[js], T)
-        want_k = _expected_rows(w, l, dpsynth.STREAM_K, idx[js], T)
-        oracle.rope_rows(want_k, rf2[js], 0, tables)
-        assert np.array_equal(got_v, want_v), l
-        ok, worst, ne = keys_close(got_k, want_k, TOL_BF16)
-        assert ok, (l, worst)
-        inexact += ne
-    print("eviction: %d kept, %d non-identical sampled key elements" % (n, inexact))
+    idx_d, rf2_d, tabd = _i64(idx, dev), _i64(rf2, dev), _tables_dev(tables, dev)
+    worst, inexact = 0.0, 0
+    for l in range(L):
+        _tie_to_host(k_src[l], w, l, dpsynth.STREAM_K, T)
+        _tie_to_host(v_src[l], w, l, dpsynth.STREAM_V, T)
+        assert _same(v_dst[l][:n], v_src[l].index_select(0, idx_d)), l
+        e, ne = _check_rotated(k_dst[l][:n], k_src[l].index_select(0, idx_d), rf2_d, tabd,
+                               w.rope_pairs)
+        worst, inexact = max(worst, e), inexact + ne
+    for l in (0, 19, L - 1):
+        _oracle_layer(k_src[l], v_src[l], idx, k_dst[l][:n], v_dst[l][:n], rf2, tables)
+    print("eviction: %d kept x %d layers, max |key error| %.3g, %d key elements off the "
+          "float64 rotation's bf16" % (n, L, worst, inexact))
     del step, k_src, v_src, k_dst, v_dst
     _free()
 
 
 def test_reindex_full_size():
     """Re-index of the retained cache of a one-minute history: 40 x 40 x 128
-    bf16 keys, 240 frames, q0 = 240, knee 12, factor 8."""
+    bf16 keys, 240 frames, q0 = 240, knee 12, factor 8.  Every key of all 40
+    layers against its regenerated source; layers 0, 19 and 39 also through
+    the C oracle."""
     dev = device()
     w = dpsynth.WORKLOADS["reindex"]
     L, H, D = w.n_layers, w.n_heads, w.head_dim
@@ -148,37 +210,41 @@ def test_reindex_full_size():
     torch.cuda.synchronize()
     tables = _tables(host)
     assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
-    js = _sample_rows(rows, [w.sink_len, int(np.searchsorted(kept, w.seq_len - w.window_len))],
-                      seed=1)
-    inexact = 0
-    for l in (0, 19, L - 1):
-        got = bits(ks[l][torch.from_numpy(js).to(dev)])
-        want = _expected_rows(w, l, dpsynth.STREAM_K, js, rows)
-        oracle.rope_rows(want, rf[js], 0, tables)
-        ok, worst, ne = keys_close(got, want, TOL_BF16)
-        assert ok, (l, worst)
-        inexact += ne
-    print("reindex: %d retained rows, %d non-identical sampled key elements" % (rows, inexact))
-    del ks
+    rf_d, tabd = _i64(rf, dev), _tables_dev(tables, dev)
+    src = torch.empty_like(ks[0])
+    worst, inexact = 0.0, 0
+    for l in range(L):
+        dpsynth.kv_fill_device(src, "bf16", w.seed, dpsynth.STREAM_K, l, rows, H * D)
+        _tie_to_host(src, w, l, dpsynth.STREAM_K, rows)
+        e, ne = _check_rotated(ks[l], src, rf_d, tabd, w.rope_pairs)
+        worst, inexact = max(worst, e), inexact + ne
+        if l in (0, 19, L - 1):
+            _oracle_layer(src, None, np.arange(rows, dtype=np.int32), ks[l], None, rf, tables)
+    print("reindex: %d retained rows x %d layers, max |key error| %.3g, %d key elements off the "
+          "float64 rotation's bf16" % (rows, L, worst, inexact))
+    del ks, src
     _free()
 
 
-def test_prefix_full_size_slab():
+@pytest.mark.parametrize("slab", [0, 1])
+def test_prefix_full_size_slab(slab):
     """Prefix pruning: 361,920 tokens, 57 scored chunks, one 20-layer slab of
-    K and V (the 40-layer cache exceeds one GPU's memory)."""
+    K and V per call (the 40-layer cache exceeds one GPU's memory); both slabs
+    run.  Every kept row of every layer of the slab element by element; one
+    layer of the slab also through the C oracle."""
     dev = device()
     w = dpsynth.WORKLOADS["prefix"]
     T, H, D = w.seq_len, w.n_heads, w.head_dim
-    slab = list(range(20, 40))                 # the second slab
+    layers = list(range(20 * slab, 20 * slab + 20))
     x0, xf = dpsynth.score_inputs(w)
     ell = oracle.score_f32(x0, xf, w.d)
     keep = oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin, w.n_scored, w.gamma)
     idx = oracle.compact(keep)
     n = idx.shape[0]
-    k_src = _fill(dev, w, T, slab, dpsynth.STREAM_K)
-    v_src = _fill(dev, w, T, slab, dpsynth.STREAM_V)
-    k_dst = [torch.empty((n, H, D), dtype=torch.bfloat16, device=dev) for _ in slab]
-    v_dst = [torch.empty((n, H, D), dtype=torch.bfloat16, device=dev) for _ in slab]
+    k_src = _fill(dev, w, T, layers, dpsynth.STREAM_K)
+    v_src = _fill(dev, w, T, layers, dpsynth.STREAM_V)
+    k_dst = [torch.empty((n, H, D), dtype=torch.bfloat16, device=dev) for _ in layers]
+    v_dst = [torch.empty((n, H, D), dtype=torch.bfloat16, device=dev) for _ in layers]
     step = PruneStep(k_src=k_src, v_src=v_src, k_dst=k_dst, v_dst=v_dst, seq_len=T,
                      sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
                      n_scored=w.n_scored, gamma=w.gamma, d=w.d, keep_ell=True)
@@ -191,18 +257,25 @@ def test_prefix_full_size_slab():
     # per-chunk keep rates vary widely by construction
     rates = keep[w.sink_len:].reshape(-1, w.chunk_tokens).mean(axis=1)
     assert rates.min() < 0.05 and rates.max() > 0.4
-    js = _sample_rows(n, [w.sink_len, n // 2], seed=2)
-    for i, l in ((0, slab[0]), (len(slab) - 1, slab[-1])):
-        sel = torch.from_numpy(js).to(dev)
-        assert np.array_equal(bits(k_dst[i][sel]), _expected_rows(w, l, dpsynth.STREAM_K, idx[js], T))
-        assert np.array_equal(bits(v_dst[i][sel]), _expected_rows(w, l, dpsynth.STREAM_V, idx[js], T))
+    idx_d = _i64(idx, dev)
+    for i, l in enumerate(layers):
+        _tie_to_host(k_src[i], w, l, dpsynth.STREAM_K, T)
+        _tie_to_host(v_src[i], w, l, dpsynth.STREAM_V, T)
+        assert _same(k_dst[i], k_src[i].index_select(0, idx_d)), l
+        assert _same(v_dst[i], v_src[i].index_select(0, idx_d)), l
+    i = 0 if slab == 0 else len(layers) - 1
+    _oracle_layer(k_src[i], v_src[i], idx, k_dst[i], v_dst[i], tol=0.0)
+    print("prefix slab %d (layers %d-%d): %d of %d rows kept, every element checked"
+          % (slab, layers[0], layers[-1], n, T))
     del step, k_src, v_src, k_dst, v_dst
     _free()
 
 
 def test_hs_full_size():
     """DeCoPrune-HS: 40 x 40 x 128 bf16, 187,200 tokens, seeded half of the
-    heads static per layer; ragged per-head output with the fused re-index."""
+    heads static per layer; ragged per-head output with the fused re-index.
+    Every (layer, head) run element by element; layers 0 and 39 also through
+    the C oracle's per-head gather and re-index."""
     dev = device()
     w = dpsynth.WORKLOADS["hs"]
     T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
@@ -239,6 +312,9 @@ def test_hs_full_size():
     torch.cuda.synchronize()
     assert np.array_equal(glens.cpu().numpy(), lens)
     assert np.array_equal(offsets.cpu().numpy(), off)
+    for c, lst in enumerate((lst_s, lst_d)):
+        assert np.array_equal(lists[c][:len(lst)].cpu().numpy(), lst)
+        assert np.array_equal(rfs[c][:len(lst)].cpu().numpy(), rf[lst])
     total = int(off[-1])
     k_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
     v_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
@@ -262,24 +338,46 @@ def test_hs_full_size():
     assert err.item() == 0
     tables = _tables(host)
     assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
-    rng = np.random.default_rng(3)
-    inexact = 0
-    for l, h in [(0, 0), (7, 13), (21, 39), (L - 1, H - 1)] + [
-            (int(a), int(b)) for a, b in zip(rng.integers(0, L, 6), rng.integers(0, H, 6))]:
-        i = l * H + h
-        lst = lst_s if cls[l, h] == 0 else lst_d
-        js = _sample_rows(len(lst), [w.sink_len], k=24, seed=i)
-        src_rows = lst[js]
-        want_k = _expected_rows(w, l, dpsynth.STREAM_K, src_rows, T)[:, h, :].copy()
-        want_v = _expected_rows(w, l, dpsynth.STREAM_V, src_rows, T)[:, h, :].copy()
-        oracle.rope_headrows(want_k, rf[src_rows], 0, tables)
-        sel = torch.from_numpy(off[i] + js).to(dev)
-        assert np.array_equal(bits(v_out[sel]), want_v), (l, h)
-        ok, worst, ne = keys_close(bits(k_out[sel]), want_k, TOL_BF16)
-        assert ok, (l, h, worst)
-        inexact += ne
-    print("hs: %d head rows, PR %.4f, %d non-identical sampled key elements"
-          % (total, 1 - total / (L * H * T), inexact))
+    tabd = _tables_dev(tables, dev)
+    lst_dev = [_i64(lst_s, dev), _i64(lst_d, dev)]
+    worst, inexact = 0.0, 0
+    for l in range(L):
+        _tie_to_host(k_src[l], w, l, dpsynth.STREAM_K, T)
+        _tie_to_host(v_src[l], w, l, dpsynth.STREAM_V, T)
+        for c in range(2):
+            heads = np.flatnonzero(cls[l] == c)
+            if heads.size == 0:
+                continue
+            nc = int(lens[c])
+            # every run of this class, head-major: [heads, nc, D] -> [heads * nc, 1, D]
+            hsel = _i64(heads, dev)
+            src_k = k_src[l].index_select(0, lst_dev[c]).index_select(1, hsel)
+            src_v = v_src[l].index_select(0, lst_dev[c]).index_select(1, hsel)
+            src_k = src_k.permute(1, 0, 2).reshape(-1, 1, D)
+            src_v = src_v.permute(1, 0, 2).reshape(-1, 1, D)
+            out_rows = (off[l * H + heads][:, None] + np.arange(nc)[None, :]).ravel()
+            osel = _i64(out_rows, dev)
+            assert _same(v_out.index_select(0, osel).view(-1, 1, D), src_v), (l, c)
+            frames = lst_dev[c].new_tensor(np.tile(rf[(lst_s, lst_d)[c]], heads.size))
+            e, ne = _check_rotated(k_out.index_select(0, osel).view(-1, 1, D), src_k, frames, tabd,
+                                   w.rope_pairs)
+            worst, inexact = max(worst, e), inexact + ne
+    # whole layers through the C oracle's per-head gather and re-index
+    for l in (0, L - 1):
+        sk, sv = bits(k_src[l]), bits(v_src[l])
+        lo, hi = int(off[l * H]), int(off[(l + 1) * H])
+        wk = np.zeros((hi - lo, D), np.uint16)       # this layer's runs: offsets shifted to 0
+        wv = np.zeros((hi - lo, D), np.uint16)
+        oracle.hs_gather_layer(sk, l, cls, [lst_s, lst_d], off - lo, wk)
+        oracle.hs_gather_layer(sv, l, cls, [lst_s, lst_d], off - lo, wv)
+        frames = np.concatenate([rf[(lst_s, lst_d)[cls[l, h]]] for h in range(H)]).astype(np.int32)
+        oracle.rope_headrows(wk, frames, 0, tables)
+        assert np.array_equal(bits(v_out[lo:hi]), wv), l
+        ok, e, _ = keys_close(bits(k_out[lo:hi]), wk, TOL_BF16)
+        assert ok, (l, e)
+    print("hs: %d head rows, PR %.4f, every (layer, head) run checked, max |key error| %.3g, "
+          "%d key elements off the float64 rotation's bf16"
+          % (total, 1 - total / (L * H * T), worst, inexact))
     del k_src, v_src, k_out, v_out
     _free()
 
@@ -328,25 +426,91 @@ def test_tiny_workload_every_row(reversed_):
     print("tiny (reversed=%s): %d of %d kept, PR %.4f" % (reversed_, n, T, oracle.pr(n, T)))
 
 
+def _ring_setup(w, last_hist_chunk):
+    """Row frames of the one-step ring layout [sink | 4 slots | history of the
+    retained rows of chunks 1..last_hist_chunk | room for one chunk]."""
+    C, tpf = w.chunk_tokens, w.tokens_per_frame
+    hist_rows = np.flatnonzero(dpsynth.retained_keep(w)[C:(last_hist_chunk + 1) * C]) + C
+    n_hist = hist_rows.shape[0]
+    hb = 5 * C
+    cap = hb + n_hist + C
+    rf = np.full(cap, -1, np.int32)
+    rf[:C] = np.arange(C) // tpf
+    rf[C:hb] = ((last_hist_chunk + 1) * C + np.arange(4 * C)) // tpf
+    rf[hb:hb + n_hist] = hist_rows // tpf
+    return rf, n_hist, hb, cap
+
+
+def _check_ring_layer(w, l, heads, cap, ks, vs, hb, n_hist, slot_begin, widx, rf, old_tabd,
+                      tabd, dev, scratch):
+    """Every row of one layer of a ring-layout cache after one eviction step
+    against the regenerated fill: the old rows (sink, history) re-indexed by
+    old_tabd (None: untouched), the ring slots untouched, the appended rows =
+    the leaving slot's kept rows re-indexed by tabd, the rows past the new tail
+    untouched; V untouched except the appended rows, which are copies."""
+    C, D = w.chunk_tokens, w.head_dim
+    n = widx.shape[0]
+    tail = hb + n_hist + n
+    sk, sv = scratch
+    dpsynth.kv_fill_device(sk, "bf16", w.seed, dpsynth.STREAM_K, l, cap, heads * D)
+    dpsynth.kv_fill_device(sv, "bf16", w.seed, dpsynth.STREAM_V, l, cap, heads * D)
+    _tie_to_host(sk, w, l, dpsynth.STREAM_K, cap, heads)
+    _tie_to_host(sv, w, l, dpsynth.STREAM_V, cap, heads)
+    worst, inexact = 0.0, 0
+    for lo, hi in ((0, C), (hb, hb + n_hist)):
+        if old_tabd is None:
+            assert _same(ks[l][lo:hi], sk[lo:hi]), l
+        else:
+            zero = torch.zeros(hi - lo, dtype=torch.int64, device=dev)
+            e, ne = _check_rotated(ks[l][lo:hi], sk[lo:hi], zero, old_tabd, w.rope_pairs)
+            worst, inexact = max(worst, e), inexact + ne
+    assert _same(ks[l][C:hb], sk[C:hb]) and _same(ks[l][tail:], sk[tail:]), l
+    src = _i64(slot_begin + widx, dev)
+    e, ne = _check_rotated(ks[l][hb + n_hist:tail], sk.index_select(0, src),
+                           _i64(rf[slot_begin + widx], dev), tabd, w.rope_pairs)
+    worst, inexact = max(worst, e), inexact + ne
+    assert _same(vs[l][:hb + n_hist], sv[:hb + n_hist]) and _same(vs[l][tail:], sv[tail:]), l
+    assert _same(vs[l][hb + n_hist:tail], sv.index_select(0, src)), l
+    return worst, inexact
+
+
+def _append_step(w, dev, heads, cap, ks, vs, rf, tail0, x0, xf, d):
+    """The device buffers of one ring-layout eviction and the leaving chunk's
+    kept-index list (dp_score_index)."""
+    C, D, L = w.chunk_tokens, w.head_dim, w.n_layers
+    kv = dp.dp_kv_inplace()
+    ak, av = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
+    kv.k_layers, kv.v_layers = ak.data_ptr(), av.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, heads, D, dp.DP_BF16
+    kv.capacity = cap
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    keep = torch.empty(C, dtype=torch.uint8, device=dev)
+    idx = torch.empty(C, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64,
+                        device=dev)
+    dp.dp_score_index(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev), d, d,
+                      dp.make_policy(C, 0, 0, 0, C, w.gamma), None, keep, idx, nk, None, None,
+                      ws_si, err)
+    tail = torch.tensor([tail0], dtype=torch.int64, device=dev)
+    rf_d = torch.from_numpy(rf).to(dev)
+    return dict(kv=kv, ak=ak, av=av, err=err, idx=idx, nk=nk, tail=tail, rf_d=rf_d)
+
+
 def test_steady_step_full_size():
     """The steady-state step of the one-minute rollout in the ring layout, as
     bench.py times it: 40 x 40 x 128 bf16, [sink | 4 ring slots | history of
     the retained rows of chunks 1-55 | room]; chunk 56 leaves the window for
     q0 = 240.  The sink and history move by the uniform step 3.5 frames
     (dp_rope_shift), the leaving chunk's kept rows are appended with their
-    first re-index fused.  Sampled rows of three layers against the oracle."""
+    first re-index fused.  Every row of all 40 layers against the oracle's
+    tables applied to the regenerated fill."""
     dev = device()
     w = dpsynth.WORKLOADS["reindex"]
-    L, H, D, C, tpf = w.n_layers, w.n_heads, w.head_dim, w.chunk_tokens, w.tokens_per_frame
-    hist_rows = np.flatnonzero(dpsynth.retained_keep(w)[C:56 * C]) + C
-    n_hist = hist_rows.shape[0]
-    hb = 5 * C
-    cap = hb + n_hist + C
+    L, H, D, C = w.n_layers, w.n_heads, w.head_dim, w.chunk_tokens
+    rf, n_hist, hb, cap = _ring_setup(w, 55)
     slot_begin = C
-    rf = np.full(cap, -1, np.int32)
-    rf[:C] = np.arange(C) // tpf
-    rf[C:hb] = (56 * C + np.arange(4 * C)) // tpf
-    rf[hb:hb + n_hist] = hist_rows // tpf
     ks = _fill(dev, w, cap, range(L), dpsynth.STREAM_K)
     vs = _fill(dev, w, cap, range(L), dpsynth.STREAM_V)
     we = dpsynth.WORKLOADS["eviction"]
@@ -357,74 +521,40 @@ def test_steady_step_full_size():
     phase0 = _tables(host)[3]
     host = dict(host, q0=w.q0, frame_phase=phase0)
     rd = _rope_dev(host, dev)
-    # device step
-    kv = dp.dp_kv_inplace()
-    ak, av = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
-    kv.k_layers, kv.v_layers = ak.data_ptr(), av.data_ptr()
-    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dp.DP_BF16
-    kv.capacity = cap
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    kv.dev_error = err.data_ptr()
-    keep = torch.empty(C, dtype=torch.uint8, device=dev)
-    idx = torch.empty(C, dtype=torch.int32, device=dev)
-    nk = torch.zeros(1, dtype=torch.int64, device=dev)
-    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64,
-                        device=dev)
-    dp.dp_score_index(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev), we.d, we.d,
-                      dp.make_policy(C, 0, 0, 0, C, w.gamma), None, keep, idx, nk, None, None,
-                      ws_si, err)
-    tail = torch.tensor([hb + n_hist], dtype=torch.int64, device=dev)
-    rf_d = torch.from_numpy(rf).to(dev)
-    ws_s = torch.empty(dp.dp_rope_shift_workspace_bytes(w.rope_pairs) // 4 + 4,
-                       dtype=torch.float32, device=dev)
-    step = 4 * (1 - 1 / w.rope_factor)
-    dp.dp_rope_shift(ak, L, H, D, dp.DP_BF16, 0, C, None, rd["theta"], 0, w.rope_pairs, step, ws_s)
-    dp.dp_rope_shift(ak, L, H, D, dp.DP_BF16, hb, cap, tail, rd["theta"], 0, w.rope_pairs, step,
-                     ws_s)
     rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
                         host["inv_factor"])
     ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
+    st = _append_step(w, dev, H, cap, ks, vs, rf, hb + n_hist, x0, xf, we.d)
+    ws_s = torch.empty(dp.dp_rope_shift_workspace_bytes(w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    step = 4 * (1 - 1 / w.rope_factor)
+    ak = st["ak"]
+    dp.dp_rope_shift(ak, L, H, D, dp.DP_BF16, 0, C, None, rd["theta"], 0, w.rope_pairs, step, ws_s)
+    dp.dp_rope_shift(ak, L, H, D, dp.DP_BF16, hb, cap, st["tail"], rd["theta"], 0, w.rope_pairs,
+                     step, ws_s)
     dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
-    dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf_d, rope, ws_r)
+    dp.dp_append_kept(st["kv"], slot_begin, C, st["idx"], st["nk"], st["tail"], st["rf_d"], rope,
+                      ws_r)
     torch.cuda.synchronize()
-    assert err.item() == 0 and nk.item() == n and tail.item() == hb + n_hist + n
+    assert st["err"].item() == 0 and st["nk"].item() == n and st["tail"].item() == hb + n_hist + n
     tables = _tables(host)
     assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
-    uniform = oracle.rope_uniform(host["theta"], step)
-    old_rows = np.concatenate([_sample_rows(C, [], k=16, seed=2),
-                               hb + _sample_rows(n_hist, [], k=32, seed=3)])
-    ring_rows = C + _sample_rows(4 * C, [C, 2 * C, 3 * C], k=8, seed=4)
-    app = _sample_rows(n, [], k=24, seed=5)
-    src = slot_begin + widx[app]
-    assert np.array_equal(rf_d.cpu().numpy()[hb + n_hist + app], rf[src])
-    inexact = 0
-    for l in (0, 19, L - 1):
-        got = bits(ks[l][torch.from_numpy(old_rows).to(dev)])
-        want = _expected_rows(w, l, dpsynth.STREAM_K, old_rows, cap)
-        oracle.rope_rows(want, np.zeros(len(old_rows), np.int32), 0, uniform)
-        ok, worst, ne = keys_close(got, want, TOL_BF16)
-        assert ok, ("old keys", l, worst)
-        inexact += ne
-        got = bits(ks[l][torch.from_numpy(ring_rows).to(dev)])
-        assert np.array_equal(got, _expected_rows(w, l, dpsynth.STREAM_K, ring_rows, cap)), l
-        got = bits(ks[l][torch.from_numpy(hb + n_hist + app).to(dev)])
-        want = _expected_rows(w, l, dpsynth.STREAM_K, src, cap)
-        oracle.rope_rows(want, rf[src], 0, tables)
-        ok, worst, ne = keys_close(got, want, TOL_BF16)
-        assert ok, ("appended keys", l, worst)
-        inexact += ne
-        got = bits(vs[l][torch.from_numpy(hb + n_hist + app).to(dev)])
-        assert np.array_equal(got, _expected_rows(w, l, dpsynth.STREAM_V, src, cap)), l
-    print("steady step: %d history rows, %d appended, %d non-identical sampled key elements"
-          % (n_hist, n, inexact))
-    del ks, vs
+    rf_after = st["rf_d"].cpu().numpy()
+    assert np.all(rf_after[slot_begin:slot_begin + C] == -1)
+    assert np.array_equal(rf_after[hb + n_hist:hb + n_hist + n], rf[slot_begin + widx])
+    uniform = _tables_dev(oracle.rope_uniform(host["theta"], step), dev)
+    tabd = _tables_dev(tables, dev)
+    scratch = (torch.empty_like(ks[0]), torch.empty_like(vs[0]))
+    worst, inexact = 0.0, 0
+    for l in range(L):
+        e, ne = _check_ring_layer(w, l, H, cap, ks, vs, hb, n_hist, slot_begin, widx, rf, uniform,
+                                  tabd, dev, scratch)
+        worst, inexact = max(worst, e), inexact + ne
+    print("steady step: %d history rows, %d appended, every row of %d layers, max |key error| "
+          "%.3g, %d key elements off the float64 rotation's bf16" % (n_hist, n, L, worst, inexact))
+    del ks, vs, scratch
     _free()
-
-
-def _tables_compressed(host):
-    return oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
-                              host["inv_factor"], host["theta"], compressed=True)
 
 
 def test_steady_lazy_step_full_size():
@@ -432,20 +562,14 @@ def test_steady_lazy_step_full_size():
     (workload steady_lazy): 40 x 40 x 128 bf16, [sink | 4 ring slots | history
     of the retained rows of chunks 1-55 | room]; chunk 56 leaves the window for
     q0 = 240.  No old key is written; the leaving chunk's kept rows are
-    appended with its frames moved from phase t to t/c (fused).  Sampled rows
-    of three layers against the oracle's compressed-axis tables."""
+    appended with its frames moved from phase t to t/c (fused).  Every row of
+    all 40 layers against the oracle's compressed-axis tables applied to the
+    regenerated fill."""
     dev = device()
     w = dpsynth.WORKLOADS["reindex"]
-    L, H, D, C, tpf = w.n_layers, w.n_heads, w.head_dim, w.chunk_tokens, w.tokens_per_frame
-    hist_rows = np.flatnonzero(dpsynth.retained_keep(w)[C:56 * C]) + C
-    n_hist = hist_rows.shape[0]
-    hb = 5 * C
-    cap = hb + n_hist + C
+    L, H, D, C = w.n_layers, w.n_heads, w.head_dim, w.chunk_tokens
+    rf, n_hist, hb, cap = _ring_setup(w, 55)
     slot_begin = C
-    rf = np.full(cap, -1, np.int32)
-    rf[:C] = np.arange(C) // tpf
-    rf[C:hb] = (56 * C + np.arange(4 * C)) // tpf
-    rf[hb:hb + n_hist] = hist_rows // tpf
     ks = _fill(dev, w, cap, range(L), dpsynth.STREAM_K)
     vs = _fill(dev, w, cap, range(L), dpsynth.STREAM_V)
     we = dpsynth.WORKLOADS["eviction"]
@@ -453,60 +577,37 @@ def test_steady_lazy_step_full_size():
     widx = oracle.compact(oracle.mask(oracle.score_f32(x0, xf, we.d), C, 0, 0, 0, C, w.gamma))
     n = widx.shape[0]
     host = _rope_host(w, q0=w.q0 - 4)                 # phases after the previous step (q0 = 236)
-    phase0 = _tables_compressed(host)[3]
+    phase0 = _tables(host, compressed=True)[3]
     host = dict(host, q0=w.q0, frame_phase=phase0)
     rd = _rope_dev(host, dev)
-    kv = dp.dp_kv_inplace()
-    ak, av = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
-    kv.k_layers, kv.v_layers = ak.data_ptr(), av.data_ptr()
-    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dp.DP_BF16
-    kv.capacity = cap
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    kv.dev_error = err.data_ptr()
-    keep = torch.empty(C, dtype=torch.uint8, device=dev)
-    idx = torch.empty(C, dtype=torch.int32, device=dev)
-    nk = torch.zeros(1, dtype=torch.int64, device=dev)
-    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64,
-                        device=dev)
-    dp.dp_score_index(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev), we.d, we.d,
-                      dp.make_policy(C, 0, 0, 0, C, w.gamma), None, keep, idx, nk, None, None,
-                      ws_si, err)
-    tail = torch.tensor([hb + n_hist], dtype=torch.int64, device=dev)
-    rf_d = torch.from_numpy(rf).to(dev)
     rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
                         host["inv_factor"], axis=dp.DP_AXIS_COMPRESSED)
     ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
+    st = _append_step(w, dev, H, cap, ks, vs, rf, hb + n_hist, x0, xf, we.d)
     dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
-    dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf_d, rope, ws_r)
+    dp.dp_append_kept(st["kv"], slot_begin, C, st["idx"], st["nk"], st["tail"], st["rf_d"], rope,
+                      ws_r)
     torch.cuda.synchronize()
-    assert err.item() == 0 and nk.item() == n and tail.item() == hb + n_hist + n
-    tables = _tables_compressed(host)
+    assert st["err"].item() == 0 and st["nk"].item() == n and st["tail"].item() == hb + n_hist + n
+    tables = _tables(host, compressed=True)
     assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
     moved = np.flatnonzero(tables[0] != 0)                   # frames whose phase changes
     assert np.array_equal(moved, np.arange(224, 228))       # chunk 56 only: t -> t/c
-    old_rows = np.concatenate([_sample_rows(C, [], k=16, seed=2),
-                               hb + _sample_rows(n_hist, [], k=32, seed=3)])
-    ring_rows = C + _sample_rows(4 * C, [C, 2 * C, 3 * C], k=8, seed=4)
-    app = _sample_rows(n, [], k=24, seed=5)
-    src = slot_begin + widx[app]
-    assert np.array_equal(rf_d.cpu().numpy()[hb + n_hist + app], rf[src])
-    inexact = 0
-    for l in (0, 19, L - 1):
-        for rows in (old_rows, ring_rows):                   # never written
-            got = bits(ks[l][torch.from_numpy(rows).to(dev)])
-            assert np.array_equal(got, _expected_rows(w, l, dpsynth.STREAM_K, rows, cap)), l
-        got = bits(ks[l][torch.from_numpy(hb + n_hist + app).to(dev)])
-        want = _expected_rows(w, l, dpsynth.STREAM_K, src, cap)
-        oracle.rope_rows(want, rf[src], 0, tables)
-        ok, worst, ne = keys_close(got, want, TOL_BF16)
-        assert ok, ("appended keys", l, worst)
-        inexact += ne
-        got = bits(vs[l][torch.from_numpy(hb + n_hist + app).to(dev)])
-        assert np.array_equal(got, _expected_rows(w, l, dpsynth.STREAM_V, src, cap)), l
-    print("compressed-axis steady step: %d history rows, %d appended, %d non-identical sampled "
-          "key elements" % (n_hist, n, inexact))
-    del ks, vs
+    rf_after = st["rf_d"].cpu().numpy()
+    assert np.all(rf_after[slot_begin:slot_begin + C] == -1)
+    assert np.array_equal(rf_after[hb + n_hist:hb + n_hist + n], rf[slot_begin + widx])
+    tabd = _tables_dev(tables, dev)
+    scratch = (torch.empty_like(ks[0]), torch.empty_like(vs[0]))
+    worst, inexact = 0.0, 0
+    for l in range(L):
+        e, ne = _check_ring_layer(w, l, H, cap, ks, vs, hb, n_hist, slot_begin, widx, rf, None,
+                                  tabd, dev, scratch)
+        worst, inexact = max(worst, e), inexact + ne
+    print("compressed-axis steady step: %d history rows, %d appended, every row of %d layers, "
+          "max |key error| %.3g, %d key elements off the float64 rotation's bf16"
+          % (n_hist, n, L, worst, inexact))
+    del ks, vs, scratch
     _free()
 
 
@@ -516,94 +617,49 @@ def test_hs_ring_step_full_size():
     token-major cache [sink | 4 ring slots | history of the retained rows of
     chunks 1-25 | room] (20 x 128 bf16 per row, 40 layers); chunk 26 leaves the
     window for q0 = 120 and its kept rows are appended to every layer's dynamic
-    cache with the re-index fused on the compressed axis.  Sampled rows of three
+    cache with the re-index fused on the compressed axis.  Every row of all 40
     layers against the oracle; the static class's cache is not touched by the
     call."""
     dev = device()
     w = dpsynth.WORKLOADS["hs"]
-    L, D, C, tpf = w.n_layers, w.head_dim, w.chunk_tokens, w.tokens_per_frame
+    L, D, C = w.n_layers, w.head_dim, w.chunk_tokens
     HC = w.n_heads // 2
-    hist_rows = np.flatnonzero(dpsynth.retained_keep(w)[C:26 * C]) + C
-    n_hist = hist_rows.shape[0]
-    hb = 5 * C
-    cap = hb + n_hist + C
+    rf, n_hist, hb, cap = _ring_setup(w, 25)
     slot_begin = C
-    rf = np.full(cap, -1, np.int32)
-    rf[:C] = np.arange(C) // tpf
-    rf[C:hb] = (26 * C + np.arange(4 * C)) // tpf
-    rf[hb:hb + n_hist] = hist_rows // tpf
-
-    def fill(stream_id):
-        out = []
-        for l in range(L):
-            t = torch.empty((cap, HC, D), dtype=torch.bfloat16, device=dev)
-            dpsynth.kv_fill_device(t, "bf16", w.seed, stream_id, l, cap, HC * D)
-            out.append(t)
-        return out
-
-    def expected(layer, stream_id, rows):
-        r = dpsynth.kv_rows_host("bf16", w.seed, stream_id, layer, rows, cap, HC * D)
-        return np.ascontiguousarray(r.reshape(len(rows), HC, D))
-
-    ks, vs = fill(dpsynth.STREAM_K), fill(dpsynth.STREAM_V)
+    ks = _fill(dev, w, cap, range(L), dpsynth.STREAM_K, heads=HC)
+    vs = _fill(dev, w, cap, range(L), dpsynth.STREAM_V, heads=HC)
     we = dpsynth.WORKLOADS["eviction"]
     x0, xf = dpsynth.score_inputs(we)
     widx = oracle.compact(oracle.mask(oracle.score_f32(x0, xf, we.d), C, 0, 0, 0, C, w.gamma))
     n = widx.shape[0]
     host = _rope_host(w, q0=w.q0 - 4)                 # phases after the previous step (q0 = 116)
-    phase0 = _tables_compressed(host)[3]
+    phase0 = _tables(host, compressed=True)[3]
     host = dict(host, q0=w.q0, frame_phase=phase0)
     rd = _rope_dev(host, dev)
-    kv = dp.dp_kv_inplace()
-    ak, av = dp.ptr_array(ks, dev), dp.ptr_array(vs, dev)
-    kv.k_layers, kv.v_layers = ak.data_ptr(), av.data_ptr()
-    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, HC, D, dp.DP_BF16
-    kv.capacity = cap
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    kv.dev_error = err.data_ptr()
-    keep = torch.empty(C, dtype=torch.uint8, device=dev)
-    idx = torch.empty(C, dtype=torch.int32, device=dev)
-    nk = torch.zeros(1, dtype=torch.int64, device=dev)
-    ws_si = torch.zeros(dp.dp_score_index_workspace_bytes(C) // 8 + 1, dtype=torch.int64,
-                        device=dev)
-    dp.dp_score_index(torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev), we.d, we.d,
-                      dp.make_policy(C, 0, 0, 0, C, w.gamma), None, keep, idx, nk, None, None,
-                      ws_si, err)
-    tail = torch.tensor([hb + n_hist], dtype=torch.int64, device=dev)
-    rf_d = torch.from_numpy(rf).to(dev)
     rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
                         host["inv_factor"], axis=dp.DP_AXIS_COMPRESSED)
     ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
+    st = _append_step(w, dev, HC, cap, ks, vs, rf, hb + n_hist, x0, xf, we.d)
     dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
-    dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf_d, rope, ws_r)
+    dp.dp_append_kept(st["kv"], slot_begin, C, st["idx"], st["nk"], st["tail"], st["rf_d"], rope,
+                      ws_r)
     torch.cuda.synchronize()
-    assert err.item() == 0 and nk.item() == n and tail.item() == hb + n_hist + n
-    tables = _tables_compressed(host)
+    assert st["err"].item() == 0 and st["nk"].item() == n and st["tail"].item() == hb + n_hist + n
+    tables = _tables(host, compressed=True)
     assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
     assert np.array_equal(np.flatnonzero(tables[0] != 0), np.arange(104, 108))   # chunk 26 only
-    rf_after = rf_d.cpu().numpy()
+    rf_after = st["rf_d"].cpu().numpy()
     assert np.all(rf_after[slot_begin:slot_begin + C] == -1)                  # the slot is retired
-    old_rows = np.concatenate([_sample_rows(C, [], k=16, seed=12),
-                               hb + _sample_rows(n_hist, [], k=32, seed=13)])
-    ring_rows = C + _sample_rows(4 * C, [C, 2 * C, 3 * C], k=8, seed=14)
-    app = _sample_rows(n, [], k=24, seed=15)
-    src = slot_begin + widx[app]
-    assert np.array_equal(rf_after[hb + n_hist + app], rf[src])
-    inexact = 0
-    for l in (0, 19, L - 1):
-        for rows in (old_rows, ring_rows):                   # never written
-            got = bits(ks[l][torch.from_numpy(rows).to(dev)])
-            assert np.array_equal(got, expected(l, dpsynth.STREAM_K, rows)), l
-        got = bits(ks[l][torch.from_numpy(hb + n_hist + app).to(dev)])
-        want = expected(l, dpsynth.STREAM_K, src)
-        oracle.rope_rows(want, rf[src], 0, tables)
-        ok, worst, ne = keys_close(got, want, TOL_BF16)
-        assert ok, ("appended keys", l, worst)
-        inexact += ne
-        got = bits(vs[l][torch.from_numpy(hb + n_hist + app).to(dev)])
-        assert np.array_equal(got, expected(l, dpsynth.STREAM_V, src)), l
-    print("HS ring step: %d history rows, %d appended, %d non-identical sampled key elements"
-          % (n_hist, n, inexact))
-    del ks, vs
+    assert np.array_equal(rf_after[hb + n_hist:hb + n_hist + n], rf[slot_begin + widx])
+    tabd = _tables_dev(tables, dev)
+    scratch = (torch.empty_like(ks[0]), torch.empty_like(vs[0]))
+    worst, inexact = 0.0, 0
+    for l in range(L):
+        e, ne = _check_ring_layer(w, l, HC, cap, ks, vs, hb, n_hist, slot_begin, widx, rf, None,
+                                  tabd, dev, scratch)
+        worst, inexact = max(worst, e), inexact + ne
+    print("HS ring step: %d history rows, %d appended, every row of %d layers, max |key error| "
+          "%.3g, %d key elements off the float64 rotation's bf16" % (n_hist, n, L, worst, inexact))
+    del ks, vs, scratch
     _free()

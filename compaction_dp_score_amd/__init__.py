@@ -91,6 +91,7 @@ _lib_last_error = _sig("dp_last_error", [], ctypes.c_char_p)
 _lib_score_mask = _sig("dp_score_mask", [_P, _P, _i32, _i64, ctypes.POINTER(dp_mask_policy), _P, _P, _P])
 _lib_compact_ws = _sig("dp_compact_workspace_bytes", [_i64], ctypes.c_size_t)
 _lib_compact = _sig("dp_compact_index", [_P, _i64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P])
+_lib_compact_noalloc = _sig("dp_compact_index_noalloc", [_P, _i64, _P, _P, _P, _P, _P])
 _lib_rope_ws = _sig("dp_rope_workspace_bytes", [_i32, _i32], ctypes.c_size_t)
 _lib_gather = _sig("dp_gather_kv", [ctypes.POINTER(dp_kv), _P, _P, _P, ctypes.POINTER(dp_rope), _P,
                                     ctypes.c_size_t, _P])
@@ -126,7 +127,8 @@ _lib_pr_add = _sig("dp_pr_add", [ctypes.POINTER(dp_pr_counter), _i64, _i64])
 _lib_pr_value = _sig("dp_pr_value", [ctypes.POINTER(dp_pr_counter)], ctypes.c_double)
 
 EXPORTED = ["dp_abi_version", "dp_status_str", "dp_last_error", "dp_score_mask",
-            "dp_compact_workspace_bytes", "dp_compact_index", "dp_rope_workspace_bytes",
+            "dp_compact_workspace_bytes", "dp_compact_index", "dp_compact_index_noalloc",
+            "dp_rope_workspace_bytes",
             "dp_gather_kv", "dp_rope_reindex", "dp_rope_prepare", "dp_rope_apply", "dp_rope_shift_workspace_bytes",
             "dp_rope_shift", "dp_append_kept",
             "dp_hs_offsets", "dp_hs_gather_kv",
@@ -240,6 +242,14 @@ def dp_compact_index(keep, seq_len, idx_out, n_kept, row_frame_src, row_frame_ds
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib_compact(_ptr(keep), seq_len, _ptr(idx_out), _ptr(n_kept), _ptr(row_frame_src),
                         _ptr(row_frame_dst), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dp_compact_index_noalloc(keep, seq_len, idx_out, n_kept, row_frame_src, row_frame_dst,
+                             stream=None):
+    """dp_compact_index with the library's static scratch of the current device
+    (no workspace, nothing allocated)."""
+    _check(_lib_compact_noalloc(_ptr(keep), int(seq_len), _ptr(idx_out), _ptr(n_kept),
+                                _ptr(row_frame_src), _ptr(row_frame_dst), _stream(stream)))
 
 
 def dp_rope_workspace_bytes(n_frames, n_pairs):

@@ -196,6 +196,31 @@ dp_status dp_compact_index(const uint8_t* keep, int64_t seq_len, int32_t* idx_ou
   return st;
 }
 
+dp_status dp_compact_index_noalloc(const uint8_t* keep, int64_t seq_len, int32_t* idx_out,
+                                   int64_t* n_kept, const int32_t* row_frame_src,
+                                   int32_t* row_frame_dst, void* stream) {
+  const char* who = "dp_compact_index_noalloc";
+  if (seq_len < 0 || seq_len >= kMaxRows)
+    return fail(DP_ERANGE, "%s: seq_len %lld outside [0, 2^31)", who, (long long)seq_len);
+  if ((seq_len > 0 && (!keep || !idx_out)) || !n_kept)
+    return fail(DP_EINVAL, "%s: keep, idx_out and n_kept are required", who);
+  if ((row_frame_src == nullptr) != (row_frame_dst == nullptr))
+    return fail(DP_EINVAL, "%s: row_frame_src and row_frame_dst go together", who);
+  if (!aligned(n_kept, 8) || (idx_out && !aligned(idx_out, 4)))
+    return fail(DP_EALIGN, "%s: n_kept must be 8-byte, idx 4-byte aligned", who);
+  if (compact_ws_bytes(seq_len) > compact_scratch_bytes())
+    return fail(DP_ERANGE, "%s: %lld rows need %zu bytes of scratch, more than the %zu held",
+                who, (long long)seq_len, compact_ws_bytes(seq_len), compact_scratch_bytes());
+  (void)hipGetLastError();
+  int32_t* scratch_ptr = nullptr;
+  dp_status st = compact_scratch((hipStream_t)stream, &scratch_ptr);
+  if (st != DP_OK) return st;
+  st = launch_compact(keep, seq_len, idx_out, n_kept, row_frame_src, row_frame_dst, scratch_ptr,
+                      (hipStream_t)stream);
+  if (st == DP_OK) ok();
+  return st;
+}
+
 size_t dp_rope_workspace_bytes(int32_t n_frames, int32_t n_pairs) {
   if (n_frames < 0 || n_pairs < 0) return 0;
   return rope_ws_bytes(n_frames, n_pairs);

@@ -13,6 +13,8 @@
 //              slot is the popcount of the ballot below it (mbcnt); the 64
 //              (round, wavefront) counts of the tile get an exclusive prefix in
 //              LDS, so every kept row lands at its final position.
+#include <mutex>
+
 #include "dp_internal.h"
 
 namespace dp {
@@ -142,6 +144,53 @@ dp_status launch_compact(const uint8_t* keep, int64_t T, int32_t* idx, int64_t* 
 size_t compact_ws_bytes(int64_t T) {
   int64_t n_tiles = (T + kTile - 1) / kTile;
   return (size_t)(n_tiles > 0 ? n_tiles : 1) * sizeof(int32_t);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of dp_compact_index_noalloc: the per-tile counts (then offsets) of
+// one call, for up to 2^31 rows (524,288 tiles, 2 MiB).  Each device holds its
+// own copy until the process ends; every call on a device uses that copy.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): each device's address is looked up once,
+// with that device current, and kept.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int64_t kScratchTiles = (((int64_t)1 << 31) + kTile - 1) / kTile;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) int32_t scratch[kScratchTiles];
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t compact_scratch_bytes() { return sizeof(int32_t) * (size_t)kScratchTiles; }
+
+dp_status compact_scratch(hipStream_t s, int32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DP_EHIP, "dp_compact_index_noalloc: hipGetDevice: %s",
+                                   hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DP_EUNSUPPORTED, "dp_compact_index_noalloc: device %d beyond %d", dev, kMaxDevices);
+  if (s) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return fail(DP_EHIP, "dp_compact_index_noalloc: hipStreamGetDevice: %s",
+                                     hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(DP_EINVAL, "dp_compact_index_noalloc: the stream belongs to device %d, the "
+                             "current device is %d", (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DP_EHIP, "dp_compact_index_noalloc: hipGetSymbolAddress: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return DP_OK;
 }
 
 }  // namespace dp

@@ -25,6 +25,8 @@ dp_status launch_score_index(const float* x0, const float* xf, int32_t d, int64_
                              int64_t* n_kept, const int32_t* rf_src, int32_t* rf_dst, void* ws,
                              int32_t* dev_error, uint32_t spin_limit, hipStream_t s);
 size_t compact_ws_bytes(int64_t T);
+size_t compact_scratch_bytes();
+dp_status compact_scratch(hipStream_t s, int32_t** out);
 dp_status launch_compact(const uint8_t* keep, int64_t T, int32_t* idx, int64_t* n_kept,
                          const int32_t* rf_src, int32_t* rf_dst, int32_t* ws, hipStream_t s);
 dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dtype,

@@ -146,6 +146,26 @@ dp_status dp_compact_index(const uint8_t* keep, int64_t seq_len, int32_t* idx_ou
                            size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * 2'. Kept-index list without a workspace, for callers that cannot allocate
+ *     device memory (work under HIP graph capture, serving loops and
+ *     harnesses that forbid hipMalloc).
+ *
+ * Arguments, results and errors as dp_compact_index, without the workspace:
+ * the per-tile counts live in a static device array of the library, 2 MiB
+ * (one count per 4,096 rows, enough for every seq_len < 2^31), that every GPU
+ * the library runs on holds until the process ends.  The array of the current
+ * device (hipGetDevice) is used, and stream must belong to that device
+ * (DP_EINVAL otherwise); its address is looked up on the first call on each
+ * device.  Nothing is allocated.  Every call on one GPU uses the same array,
+ * so calls that overlap in time on one GPU (other streams, other threads)
+ * race and give wrong lists: order them on one stream.  Nothing in the array
+ * needs clearing between calls (each call writes every count it reads).
+ * ------------------------------------------------------------------------- */
+dp_status dp_compact_index_noalloc(const uint8_t* keep, int64_t seq_len, int32_t* idx_out,
+                                   int64_t* n_kept, const int32_t* row_frame_src,
+                                   int32_t* row_frame_dst, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * 1+2. Score, mask and kept-index list in one launch
  *                              [DeCoPrune page, 어떻게 동작하나]
  *

@@ -24,7 +24,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     lib = ctypes.CDLL(dp.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -112,6 +112,17 @@ def test_compact_rejects():
     assert _status("compact", FAKE, 10000, FAKE, FAKE + 4, None, None, FAKE, need, None) == dp.DP_EALIGN
     assert _status("compact", FAKE, 10000, FAKE, FAKE, FAKE, None, FAKE, need, None) == dp.DP_EINVAL
     assert _status("compact", None, 10000, FAKE, FAKE, None, None, FAKE, need, None) == dp.DP_EINVAL
+
+
+def test_compact_noalloc_rejects():
+    # host-side checks of the entry point without a workspace, before any HIP call
+    assert _status("compact_noalloc", FAKE, -1, FAKE, FAKE, None, None, None) == dp.DP_ERANGE
+    assert _status("compact_noalloc", FAKE, 1 << 31, FAKE, FAKE, None, None, None) == dp.DP_ERANGE
+    assert _status("compact_noalloc", FAKE, 10000, FAKE, FAKE + 4, None, None, None) == dp.DP_EALIGN
+    assert _status("compact_noalloc", FAKE, 10000, FAKE + 2, FAKE, None, None, None) == dp.DP_EALIGN
+    assert _status("compact_noalloc", FAKE, 10000, FAKE, FAKE, FAKE, None, None) == dp.DP_EINVAL
+    assert _status("compact_noalloc", None, 10000, FAKE, FAKE, None, None, None) == dp.DP_EINVAL
+    assert _status("compact_noalloc", FAKE, 10000, FAKE, None, None, None, None) == dp.DP_EINVAL
 
 
 def _kv(**kw):

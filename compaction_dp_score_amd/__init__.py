@@ -23,7 +23,7 @@ if not os.path.exists(LIB_PATH):
                       "python compaction_dp_score_amd/build.py)")
 
 _lib = ctypes.CDLL(LIB_PATH)
-ABI_VERSION = 1                # DP_ABI_VERSION of the include/decoprune.h this binding follows
+ABI_VERSION = 2                # DP_ABI_VERSION of the include/decoprune.h this binding follows
 _lib.dp_abi_version.restype = ctypes.c_int
 if _lib.dp_abi_version() != ABI_VERSION:
     raise ImportError("libdecoprune.so reports ABI %d, this binding follows ABI %d: rebuild it"
@@ -34,6 +34,7 @@ DP_F32, DP_BF16 = 0, 1
 DP_MODE_SCORE, DP_MODE_STREAMING = 0, 1
 DP_HS_MAX_CLASSES = 8
 DP_AXIS_PAGE, DP_AXIS_COMPRESSED = 0, 1
+DP_KEY_INTERLEAVED, DP_KEY_SPLIT = 0, 1
 
 _P = ctypes.c_void_p
 _i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -54,7 +55,7 @@ class dp_mask_policy(ctypes.Structure):
 class dp_rope(ctypes.Structure):
     _fields_ = [("pair_begin", _i32), ("n_pairs", _i32), ("theta", _P), ("n_frames", _i32),
                 ("axis", _i32), ("frame_t", _P), ("frame_phase", _P), ("q0", _f32),
-                ("knee", _f32), ("inv_factor", _f32)]
+                ("knee", _f32), ("inv_factor", _f32), ("key_layout", _i32)]
 
 
 class dp_kv(ctypes.Structure):
@@ -66,7 +67,8 @@ class dp_kv(ctypes.Structure):
 class dp_kv_hs(ctypes.Structure):
     _fields_ = [("k_src", _P), ("v_src", _P), ("k_out", _P), ("v_out", _P),
                 ("n_layers", _i32), ("n_heads", _i32), ("head_dim", _i32), ("dtype", _i32),
-                ("src_rows", _i64), ("out_capacity", _i64), ("dev_error", _P)]
+                ("src_rows", _i64), ("out_capacity", _i64), ("dev_error", _P),
+                ("key_layout", _i32), ("pair_begin", _i32), ("n_pairs", _i32)]
 
 
 class dp_kv_inplace(ctypes.Structure):
@@ -102,7 +104,7 @@ _lib_rope_apply = _sig("dp_rope_apply", [_P, _i32, _i32, _i32, _i32, _i64, _i64,
                                          ctypes.POINTER(dp_rope), _P, ctypes.c_size_t, _P])
 _lib_rope_shift_ws = _sig("dp_rope_shift_workspace_bytes", [_i32], ctypes.c_size_t)
 _lib_rope_shift = _sig("dp_rope_shift", [_P, _i32, _i32, _i32, _i32, _i64, _i64, _P, _P, _i32, _i32,
-                                         _f32, _P, ctypes.c_size_t, _P])
+                                         _i32, _f32, _P, ctypes.c_size_t, _P])
 _lib_append = _sig("dp_append_kept", [ctypes.POINTER(dp_kv_inplace), _i64, _i64, _P, _P, _P, _P,
                                         ctypes.POINTER(dp_rope), _P, ctypes.c_size_t, _P])
 _lib_hs_offsets = _sig("dp_hs_offsets", [_P, _i32, _i32, _P, _i32, _P, _P])
@@ -115,14 +117,15 @@ _lib_hs_reindex = _sig("dp_hs_rope_reindex", [_P, _i64, _i32, _i32, _i32, _i32, 
 _lib_si_ws = _sig("dp_score_index_workspace_bytes", [_i64], ctypes.c_size_t)
 _lib_score_index = _sig("dp_score_index", [_P, _P, _i32, _i64, ctypes.POINTER(dp_mask_policy), _P,
                                            _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P])
-_lib_attention = _sig("dp_attention", [_P, _P, _P, _P, _i64, _i64, _P, _i32, _i32, _i32, _f32, _P])
+_lib_attention = _sig("dp_attention", [_P, _P, _P, _P, _i64, _i64, _P, _i32, _i32, _i32, _f32,
+                                      _i32, _i32, _i32, _P])
 _lib_attention_lag = _sig("dp_attention_lag", [_P, _P, _P, _P, _i64, _i64, _P, _i64, _i64, _P,
-                                                _i32, _i32, _f32, _i32, _i32, _i32, _f32, _P])
+                                                _i32, _i32, _f32, _i32, _i32, _i32, _f32, _i32, _P])
 _lib_hs_attention = _sig("dp_hs_attention", [_P, _P, _P, _i64, _P, _i32, _P, _P, _i64, _P, _i64,
-                                              _i32, _i32, _i32, _f32, _P])
+                                              _i32, _i32, _i32, _f32, _i32, _i32, _i32, _P])
 _lib_hs_attention_lag = _sig("dp_hs_attention_lag", [_P, _P, _P, _i64, _P, _i32, _P, _P, _i64, _P,
                                                       _i64, _i32, _i32, _i32, _f32, _i64, _P, _i32,
-                                                      _i32, _f32, _P])
+                                                      _i32, _f32, _i32, _P])
 _lib_pr_add = _sig("dp_pr_add", [ctypes.POINTER(dp_pr_counter), _i64, _i64])
 _lib_pr_value = _sig("dp_pr_value", [ctypes.POINTER(dp_pr_counter)], ctypes.c_double)
 
@@ -184,10 +187,12 @@ def ptr_array(tensors, device):
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
 
 
-def make_rope(theta, frame_t, frame_phase, q0, knee, inv_factor, pair_begin=0, axis=0):
+def make_rope(theta, frame_t, frame_phase, q0, knee, inv_factor, pair_begin=0, axis=0,
+              key_layout=DP_KEY_INTERLEAVED):
     """A dp_rope over device tensors theta [n_pairs], frame_t/frame_phase [n_frames].
 
-    axis: DP_AXIS_PAGE (0) or DP_AXIS_COMPRESSED (1)."""
+    axis: DP_AXIS_PAGE (0) or DP_AXIS_COMPRESSED (1); key_layout: DP_KEY_INTERLEAVED
+    (0) or DP_KEY_SPLIT (1), the layout of the keys the re-index rotates."""
     r = dp_rope()
     r.pair_begin = pair_begin
     r.n_pairs = theta.numel()
@@ -197,6 +202,7 @@ def make_rope(theta, frame_t, frame_phase, q0, knee, inv_factor, pair_begin=0, a
     r.frame_t = frame_t.data_ptr()
     r.frame_phase = frame_phase.data_ptr()
     r.q0, r.knee, r.inv_factor = float(q0), float(knee), float(inv_factor)
+    r.key_layout = int(key_layout)
     r._tensors = (theta, frame_t, frame_phase)   # the struct holds raw pointers: keep them alive
     return r
 
@@ -290,12 +296,14 @@ def dp_rope_shift_workspace_bytes(n_pairs):
 
 
 def dp_rope_shift(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_capacity, n_rows,
-                  theta, pair_begin, n_pairs, delta, workspace, stream=None):
+                  theta, pair_begin, n_pairs, delta, workspace, stream=None,
+                  key_layout=DP_KEY_INTERLEAVED):
     """k_layers: device int64 tensor of layer base pointers (ptr_array)."""
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib_rope_shift(_ptr(k_layers), n_layers, n_heads, head_dim, dtype, int(row_begin),
                            int(rows_capacity), _ptr(n_rows), _ptr(theta), pair_begin, n_pairs,
-                           float(delta), _ptr(workspace), ws_bytes, _stream(stream)))
+                           int(key_layout), float(delta), _ptr(workspace), ws_bytes,
+                           _stream(stream)))
 
 
 def dp_append_kept(kv, slot_begin, slot_rows, idx, n_kept, tail, row_frame=None, fused_rope=None,
@@ -338,35 +346,38 @@ def dp_hs_rope_reindex(k_ragged, k_capacity, n_layers, n_heads, head_dim, dtype,
 
 
 def dp_attention(q, k, v, o, n_q, kv_capacity, n_kv, n_heads, head_dim, dtype, scale,
-                 stream=None):
+                 stream=None, key_layout=DP_KEY_INTERLEAVED, pair_begin=0, n_pairs=0):
     _check(_lib_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(n_q), int(kv_capacity),
-                          _ptr(n_kv), n_heads, head_dim, dtype, float(scale), _stream(stream)))
+                          _ptr(n_kv), n_heads, head_dim, dtype, float(scale), int(key_layout),
+                          int(pair_begin), int(n_pairs), _stream(stream)))
 
 
 def dp_attention_lag(q, k, v, o, n_q, kv_capacity, n_kv, plain_begin, plain_end, theta,
-                     pair_begin, n_pairs, lag, n_heads, head_dim, dtype, scale, stream=None):
+                     pair_begin, n_pairs, lag, n_heads, head_dim, dtype, scale, stream=None,
+                     key_layout=DP_KEY_INTERLEAVED):
     _check(_lib_attention_lag(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(n_q), int(kv_capacity),
                               _ptr(n_kv), int(plain_begin), int(plain_end), _ptr(theta),
                               int(pair_begin), int(n_pairs), float(lag), n_heads, head_dim, dtype,
-                              float(scale), _stream(stream)))
+                              float(scale), int(key_layout), _stream(stream)))
 
 
 def dp_hs_attention(q, k_ragged, v_ragged, ragged_capacity, offsets, layer, k_chunk, v_chunk,
-                    n_chunk, o, n_q, n_heads, head_dim, dtype, scale, stream=None):
+                    n_chunk, o, n_q, n_heads, head_dim, dtype, scale, stream=None,
+                    key_layout=DP_KEY_INTERLEAVED, pair_begin=0, n_pairs=0):
     _check(_lib_hs_attention(_ptr(q), _ptr(k_ragged), _ptr(v_ragged), int(ragged_capacity),
                              _ptr(offsets), int(layer), _ptr(k_chunk), _ptr(v_chunk), int(n_chunk),
                              _ptr(o), int(n_q), n_heads, head_dim, dtype, float(scale),
-                             _stream(stream)))
+                             int(key_layout), int(pair_begin), int(n_pairs), _stream(stream)))
 
 
 def dp_hs_attention_lag(q, k_ragged, v_ragged, ragged_capacity, offsets, layer, k_chunk, v_chunk,
                         n_chunk, o, n_q, n_heads, head_dim, dtype, scale, plain_tail, theta,
-                        pair_begin, n_pairs, lag, stream=None):
+                        pair_begin, n_pairs, lag, stream=None, key_layout=DP_KEY_INTERLEAVED):
     _check(_lib_hs_attention_lag(_ptr(q), _ptr(k_ragged), _ptr(v_ragged), int(ragged_capacity),
                                  _ptr(offsets), int(layer), _ptr(k_chunk), _ptr(v_chunk),
                                  int(n_chunk), _ptr(o), int(n_q), n_heads, head_dim, dtype,
                                  float(scale), int(plain_tail), _ptr(theta), int(pair_begin),
-                                 int(n_pairs), float(lag), _stream(stream)))
+                                 int(n_pairs), float(lag), int(key_layout), _stream(stream)))
 
 
 def dp_pr_add(counter, visible_positions, full_positions):

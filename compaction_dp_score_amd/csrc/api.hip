@@ -50,6 +50,22 @@ dp_status check_shape(int32_t n_layers, int32_t n_heads, int32_t head_dim, int32
   return DP_OK;
 }
 
+// Layout of the keys: DP_KEY_INTERLEAVED (the pairs are not read) or
+// DP_KEY_SPLIT with a temporal block of whole 16-byte vectors.
+dp_status check_key_layout(int32_t key_layout, int32_t pair_begin, int32_t n_pairs,
+                           int32_t head_dim, int32_t dtype, const char* who) {
+  if (key_layout == DP_KEY_INTERLEAVED) return DP_OK;
+  if (key_layout != DP_KEY_SPLIT) return fail(DP_EINVAL, "%s: unknown key_layout %d", who, key_layout);
+  if (n_pairs < 1 || pair_begin < 0 || 2 * ((int64_t)pair_begin + n_pairs) > head_dim)
+    return fail(DP_ERANGE, "%s: split keys need temporal pairs [%d, %d + %d) within head_dim/2",
+                who, pair_begin, pair_begin, n_pairs);
+  if ((2 * (int64_t)pair_begin * elem_size(dtype)) % 16 != 0 ||
+      (2 * (int64_t)n_pairs * elem_size(dtype)) % 16 != 0)
+    return fail(DP_EALIGN, "%s: split keys need the temporal block to start and end on 16-byte "
+                           "boundaries", who);
+  return DP_OK;
+}
+
 dp_status check_rope(const dp_rope* r, int32_t head_dim, int32_t dtype, const void* ws,
                      size_t ws_bytes, const char* who) {
   if (r->n_pairs < 1 || r->pair_begin < 0 || r->n_frames < 1 ||
@@ -68,7 +84,7 @@ dp_status check_rope(const dp_rope* r, int32_t head_dim, int32_t dtype, const vo
   if (ws_bytes < rope_ws_bytes(r->n_frames, r->n_pairs))
     return fail(DP_EINVAL, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes,
                 rope_ws_bytes(r->n_frames, r->n_pairs));
-  return DP_OK;
+  return check_key_layout(r->key_layout, r->pair_begin, r->n_pairs, head_dim, dtype, who);
 }
 
 
@@ -253,7 +269,7 @@ dp_status dp_gather_kv(const dp_kv* kv, const int32_t* idx, const int64_t* n_kep
   hipStream_t s = (hipStream_t)stream;
   RopeView view{};
   if (rope) {
-    st = launch_rope_prepare(*rope, ws, &view, kv->dtype, kv->head_dim, s);
+    st = launch_rope_prepare(*rope, ws, &view, kv->dtype, kv->head_dim, kv->n_heads, s);
     if (st != DP_OK) return st;
   }
   st = launch_gather(*kv, idx, n_kept, row_frame, rope ? &view : nullptr, s);
@@ -291,7 +307,7 @@ dp_status dp_rope_reindex(void* const* k_layers, int32_t n_layers, int32_t n_hea
   (void)hipGetLastError();
   hipStream_t s = (hipStream_t)stream;
   RopeView view{};
-  st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, s);
+  st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, n_heads, s);
   if (st != DP_OK) return st;
   st = launch_reindex(k_layers, n_layers, n_heads, head_dim, dtype, 0, rows_capacity, n_rows,
                       row_frame, view, s);
@@ -308,7 +324,7 @@ dp_status dp_rope_prepare(const dp_rope* rope, int32_t head_dim, int32_t dtype, 
   if (st != DP_OK) return st;
   (void)hipGetLastError();
   RopeView view{};
-  st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, (hipStream_t)stream);
+  st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, 1, (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }
@@ -327,7 +343,7 @@ dp_status dp_rope_apply(void* const* k_layers, int32_t n_layers, int32_t n_heads
   }
   (void)hipGetLastError();
   RopeView view{};
-  rope_view(*rope, ws, &view, dtype, head_dim);
+  rope_view(*rope, ws, &view, dtype, head_dim, n_heads);
   st = launch_reindex(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_capacity,
                       n_rows, row_frame, view, (hipStream_t)stream);
   if (st == DP_OK) ok();
@@ -341,8 +357,8 @@ size_t dp_rope_shift_workspace_bytes(int32_t n_pairs) {
 dp_status dp_rope_shift(void* const* k_layers, int32_t n_layers, int32_t n_heads,
                         int32_t head_dim, int32_t dtype, int64_t row_begin,
                         int64_t rows_capacity, const int64_t* n_rows, const float* theta,
-                        int32_t pair_begin, int32_t n_pairs, float delta, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        int32_t pair_begin, int32_t n_pairs, int32_t key_layout, float delta,
+                        void* ws, size_t ws_bytes, void* stream) {
   const char* who = "dp_rope_shift";
   if (!k_layers || !theta || !ws)
     return fail(DP_EINVAL, "%s: k_layers, theta and workspace are required", who);
@@ -355,6 +371,8 @@ dp_status dp_rope_shift(void* const* k_layers, int32_t n_layers, int32_t n_heads
                 pair_begin + n_pairs, head_dim / 2);
   if ((2 * (int64_t)pair_begin * elem_size(dtype)) % 16 != 0)
     return fail(DP_EALIGN, "%s: the temporal block must start on a 16-byte boundary", who);
+  st = check_key_layout(key_layout, pair_begin, n_pairs, head_dim, dtype, who);
+  if (st != DP_OK) return st;
   if (!(delta - delta == 0.0f)) return fail(DP_EINVAL, "%s: delta must be finite", who);
   const int64_t per_row = (int64_t)n_heads * (head_dim * elem_size(dtype) / 16);
   const int64_t span = rows_capacity - row_begin;
@@ -369,7 +387,8 @@ dp_status dp_rope_shift(void* const* k_layers, int32_t n_layers, int32_t n_heads
     return fail(DP_ERANGE, "%s: rows x layers out of range", who);
   (void)hipGetLastError();
   st = launch_rope_shift(k_layers, n_layers, n_heads, head_dim, dtype, row_begin, rows_capacity,
-                         n_rows, theta, pair_begin, n_pairs, delta, ws, (hipStream_t)stream);
+                         n_rows, theta, pair_begin, n_pairs, key_layout, delta, ws,
+                         (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }
@@ -399,7 +418,7 @@ dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t sl
     if (!row_frame) return fail(DP_EINVAL, "dp_append_kept: a fused re-index needs row_frame");
     st = check_rope(fused_rope, kv->head_dim, kv->dtype, ws, ws_bytes, "dp_append_kept");
     if (st != DP_OK) return st;
-    rope_view(*fused_rope, ws, &view, kv->dtype, kv->head_dim);
+    rope_view(*fused_rope, ws, &view, kv->dtype, kv->head_dim, kv->n_heads);
   }
   (void)hipGetLastError();
   st = launch_append(*kv, slot_begin, slot_rows, idx, n_kept, tail, row_frame,
@@ -460,16 +479,23 @@ dp_status dp_hs_gather_kv(const dp_kv_hs* kv, const uint8_t* head_class, int32_t
     return fail(DP_EALIGN, "dp_hs_gather_kv: outputs must be 16-byte aligned");
   if (kv->src_rows < 0 || kv->src_rows >= kMaxRows || kv->out_capacity < 0)
     return fail(DP_ERANGE, "dp_hs_gather_kv: src_rows or out_capacity out of range");
+  st = check_key_layout(kv->key_layout, kv->pair_begin, kv->n_pairs, kv->head_dim, kv->dtype,
+                        "dp_hs_gather_kv");
+  if (st != DP_OK) return st;
   if (rope) {
     st = check_rope(rope, kv->head_dim, kv->dtype, ws, ws_bytes, "dp_hs_gather_kv");
     if (st != DP_OK) return st;
     if (!class_rf) return fail(DP_EINVAL, "dp_hs_gather_kv: fused re-index needs class_row_frame");
+    if (rope->key_layout != kv->key_layout ||
+        (kv->key_layout == DP_KEY_SPLIT &&
+         (rope->pair_begin != kv->pair_begin || rope->n_pairs != kv->n_pairs)))
+      return fail(DP_EINVAL, "dp_hs_gather_kv: the rope and the cache name different key layouts");
   }
   (void)hipGetLastError();
   hipStream_t s = (hipStream_t)stream;
   RopeView view{};
   if (rope) {
-    st = launch_rope_prepare(*rope, ws, &view, kv->dtype, kv->head_dim, s);
+    st = launch_rope_prepare(*rope, ws, &view, kv->dtype, kv->head_dim, kv->n_heads, s);
     if (st != DP_OK) return st;
   }
   st = launch_hs_gather(*kv, head_class, n_classes, class_idx, class_len, class_cap, offsets,
@@ -495,7 +521,7 @@ dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layer
   (void)hipGetLastError();
   hipStream_t s = (hipStream_t)stream;
   RopeView view{};
-  st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, s);
+  st = launch_rope_prepare(*rope, ws, &view, dtype, head_dim, n_heads, s);
   if (st != DP_OK) return st;
   st = launch_hs_reindex(k_ragged, k_capacity, n_layers, n_heads, head_dim, dtype, head_class, n_classes,
                          class_len, class_cap, offsets, class_rf, view, s);
@@ -505,7 +531,8 @@ dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layer
 
 dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
                        int64_t kv_capacity, const int64_t* n_kv, int32_t n_heads,
-                       int32_t head_dim, int32_t dtype, float scale, void* stream) {
+                       int32_t head_dim, int32_t dtype, float scale, int32_t key_layout,
+                       int32_t pair_begin, int32_t n_pairs, void* stream) {
   if (!q || !k || !v || !o) return fail(DP_EINVAL, "dp_attention: q, k, v and o are required");
   if (dtype != DP_BF16 || head_dim != 128)
     return fail(DP_EUNSUPPORTED, "dp_attention: only bf16 with head_dim 128 is implemented");
@@ -519,9 +546,11 @@ dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int
     return fail(DP_EALIGN, "dp_attention: tensors must be 16-byte aligned");
   if (!(scale > 0.0f && scale <= 3.0e38f))
     return fail(DP_EINVAL, "dp_attention: scale must be positive and finite");
+  dp_status st = check_key_layout(key_layout, pair_begin, n_pairs, head_dim, dtype, "dp_attention");
+  if (st != DP_OK) return st;
   (void)hipGetLastError();
-  dp_status st = launch_attention(q, k, v, o, n_q, kv_capacity, n_kv, n_heads, scale,
-                                  (hipStream_t)stream);
+  st = launch_attention(q, k, v, o, n_q, kv_capacity, n_kv, n_heads, scale, key_layout,
+                        pair_begin, n_pairs, (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }
@@ -530,7 +559,7 @@ dp_status dp_attention_lag(const void* q, const void* k, const void* v, void* o,
                            int64_t kv_capacity, const int64_t* n_kv, int64_t plain_begin,
                            int64_t plain_end, const float* theta, int32_t pair_begin,
                            int32_t n_pairs, float lag, int32_t n_heads, int32_t head_dim,
-                           int32_t dtype, float scale, void* stream) {
+                           int32_t dtype, float scale, int32_t key_layout, void* stream) {
   if (!q || !k || !v || !o || !theta)
     return fail(DP_EINVAL, "dp_attention_lag: q, k, v, o and theta are required");
   if (dtype != DP_BF16 || head_dim != 128)
@@ -553,10 +582,13 @@ dp_status dp_attention_lag(const void* q, const void* k, const void* v, void* o,
     return fail(DP_EINVAL, "dp_attention_lag: scale must be positive and finite");
   if (!(lag >= -3.0e38f && lag <= 3.0e38f))
     return fail(DP_EINVAL, "dp_attention_lag: lag must be finite");
+  dp_status st = check_key_layout(key_layout, pair_begin, n_pairs, head_dim, dtype,
+                                  "dp_attention_lag");
+  if (st != DP_OK) return st;
   (void)hipGetLastError();
-  dp_status st = launch_attention_lag(q, k, v, o, n_q, kv_capacity, n_kv, plain_begin, plain_end,
-                                      theta, pair_begin, n_pairs, lag, n_heads, scale,
-                                      (hipStream_t)stream);
+  st = launch_attention_lag(q, k, v, o, n_q, kv_capacity, n_kv, plain_begin, plain_end, theta,
+                            pair_begin, n_pairs, lag, n_heads, scale, key_layout,
+                            (hipStream_t)stream);
   if (st == DP_OK) ok();
   return st;
 }
@@ -565,8 +597,9 @@ static dp_status hs_attention_impl(const char* who, const void* q, const void* k
                             const void* v_ragged, int64_t ragged_capacity, const int64_t* offsets,
                             int32_t layer, const void* k_chunk, const void* v_chunk,
                             int64_t n_chunk, void* o, int64_t n_q, int32_t n_heads,
-                            int32_t head_dim, int32_t dtype, float scale,
-                            const dp::HsLag* lag, void* stream) {
+                            int32_t head_dim, int32_t dtype, float scale, int32_t key_layout,
+                            int32_t pair_begin, int32_t n_pairs, const dp::HsLag* lag,
+                            void* stream) {
   if (!q || !k_ragged || !v_ragged || !offsets || !o)
     return fail(DP_EINVAL, "%s: q, k_ragged, v_ragged, offsets and o are required", who);
   if (!k_chunk != !v_chunk)
@@ -587,10 +620,13 @@ static dp_status hs_attention_impl(const char* who, const void* q, const void* k
     return fail(DP_EALIGN, "%s: tensors must be 16-byte aligned (offsets 8)", who);
   if (!(scale > 0.0f && scale <= 3.0e38f))
     return fail(DP_EINVAL, "%s: scale must be positive and finite", who);
+  dp_status st = check_key_layout(key_layout, pair_begin, n_pairs, head_dim, dtype, who);
+  if (st != DP_OK) return st;
   (void)hipGetLastError();
-  dp_status st = launch_hs_attention(q, k_ragged, v_ragged, ragged_capacity,
-                                     offsets + (int64_t)layer * n_heads, k_chunk, v_chunk,
-                                     n_chunk, o, n_q, n_heads, scale, (hipStream_t)stream, lag);
+  st = launch_hs_attention(q, k_ragged, v_ragged, ragged_capacity,
+                           offsets + (int64_t)layer * n_heads, k_chunk, v_chunk, n_chunk, o, n_q,
+                           n_heads, scale, key_layout, pair_begin, n_pairs, (hipStream_t)stream,
+                           lag);
   if (st == DP_OK) ok();
   return st;
 }
@@ -600,7 +636,8 @@ dp_status dp_hs_attention_lag(const void* q, const void* k_ragged, const void* v
                               const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
                               int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
                               float scale, int64_t plain_tail, const float* theta,
-                              int32_t pair_begin, int32_t n_pairs, float lag, void* stream) {
+                              int32_t pair_begin, int32_t n_pairs, float lag, int32_t key_layout,
+                              void* stream) {
   if (!theta) return fail(DP_EINVAL, "dp_hs_attention_lag: theta is required");
   if (dtype != DP_BF16 || head_dim != 128)
     return fail(DP_EUNSUPPORTED, "dp_hs_attention_lag: only bf16 with head_dim 128 is implemented");
@@ -614,17 +651,18 @@ dp_status dp_hs_attention_lag(const void* q, const void* k_ragged, const void* v
   const dp::HsLag hl{plain_tail, theta, pair_begin, n_pairs, lag};
   return hs_attention_impl("dp_hs_attention_lag", q, k_ragged, v_ragged, ragged_capacity, offsets,
                            layer, k_chunk, v_chunk, n_chunk, o, n_q, n_heads, head_dim, dtype,
-                           scale, &hl, stream);
+                           scale, key_layout, pair_begin, n_pairs, &hl, stream);
 }
 
 dp_status dp_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
                           int64_t ragged_capacity, const int64_t* offsets, int32_t layer,
                           const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
                           int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
-                          float scale, void* stream) {
+                          float scale, int32_t key_layout, int32_t pair_begin, int32_t n_pairs,
+                          void* stream) {
   return hs_attention_impl("dp_hs_attention", q, k_ragged, v_ragged, ragged_capacity, offsets,
                            layer, k_chunk, v_chunk, n_chunk, o, n_q, n_heads, head_dim, dtype,
-                           scale, nullptr, stream);
+                           scale, key_layout, pair_begin, n_pairs, nullptr, stream);
 }
 
 dp_status dp_pr_add(dp_pr_counter* acc, int64_t visible, int64_t full) {

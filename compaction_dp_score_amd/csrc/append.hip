@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendArgs a) {
       // data (vector loads retire in order); lanes outside the temporal block
       // read entry 0 and keep their data
       const uint32_t h = fdiv(c, a.div_head);
-      const int tv = (int)(c - h * a.div_head.d) - a.rope.tv_begin;
-      const bool in_block = tv >= 0 && tv < a.rope.tv_count;
+      const int tv = (int)(c - h * a.div_head.d) - a.rope.tv_off;
+      const bool in_block = tv >= 0 && tv < a.rope.tv_count && (int)c < a.rope.blk_end;
       const int32_t* frow = a.row_frame + a.slot_begin + (sv ? s : 0);
       const int f = one_row ? uniform_load(frow) : *frow;
       const bool fv = (uint32_t)f < (uint32_t)a.rope.n_frames;
@@ -143,7 +143,10 @@ dp_status launch_append(const dp_kv_inplace& kv, int64_t slot_begin, int64_t slo
   a.slot_begin = slot_begin;
   a.slot_rows = slot_rows;
   a.div_row = make_fastdiv((uint32_t)((int64_t)kv.n_heads * kv.head_dim * elem_size(kv.dtype) / 16));
-  a.div_head = make_fastdiv((uint32_t)(kv.head_dim * elem_size(kv.dtype) / 16));
+  // segment of the fused rotation's walk: the head row (interleaved keys) or
+  // the head's temporal block in the row's leading plane (split keys)
+  a.div_head = make_fastdiv(rope ? (uint32_t)rope->head_stride_v
+                                 : (uint32_t)(kv.head_dim * elem_size(kv.dtype) / 16));
   a.dtype = kv.dtype;
   a.has_rope = rope != nullptr;
   a.rope = rope ? *rope : RopeView{};

@@ -39,6 +39,13 @@
 // (dp_hs_attention_lag) each head's run is lagged except its last plain_tail
 // rows, which are streamed after it together with the chunk's own block, both
 // plain.
+//
+// Split keys (DP_KEY_SPLIT): a key row keeps the temporal blocks of all heads
+// first, so a head's key row is two pieces, its temporal block and its other
+// dims; in a ragged run the run's temporal blocks come first.  Only the
+// addresses the tile loads read from change: each lane fetches the 16-byte
+// chunk that belongs at its LDS position from the piece that holds it, and the
+// tile lands in LDS exactly as for interleaved keys.
 #include "dp_internal.h"
 
 namespace dp {
@@ -58,9 +65,10 @@ constexpr int kD = 128;          // head_dim
 // ragged cache uses 4 (two workgroups per CU: twice as many, smaller units of
 // work balance per-head runs of unequal length better).
 enum { kDense = 0, kRagged = 1, kLag = 2, kRaggedLag = 3 };
+constexpr int kSplit = 4;        // mode bit: split keys
 
 template <int MODE> struct Shape {
-  static constexpr int kWaves = (MODE == kRagged || MODE == kRaggedLag) ? 4 : 8;
+  static constexpr int kWaves = ((MODE & 3) == kRagged || (MODE & 3) == kRaggedLag) ? 4 : 8;
   static constexpr int kBlock = 64 * kWaves;
   static constexpr int kBM = 32 * kWaves;          // queries per workgroup
   static constexpr int kDmaPerWave = 16 / kWaves;  // 1 KiB tile blocks per operand and wavefront
@@ -97,6 +105,10 @@ struct AttnArgs {
   int32_t pair_begin;
   int32_t n_pairs;
   float lag;
+  // split keys: 16-byte chunks [tvb, tvb + tvc) of a head's key row are its
+  // temporal block (in the leading plane), the other 16 - tvc chunks follow
+  int32_t tvb;
+  int32_t tvc;
 };
 
 // The two values a lane and its partner 32 lanes away hold, in lane order
@@ -119,8 +131,9 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 template <int MODE>
 __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a) {
-  constexpr bool RAGGED = MODE == kRagged || MODE == kRaggedLag;
-  constexpr bool LAG = MODE == kLag || MODE == kRaggedLag;
+  constexpr bool RAGGED = (MODE & 3) == kRagged || (MODE & 3) == kRaggedLag;
+  constexpr bool LAG = (MODE & 3) == kLag || (MODE & 3) == kRaggedLag;
+  constexpr bool SPLIT = (MODE & kSplit) != 0;
   constexpr int kAttnBlock = Shape<MODE>::kBlock, kBM = Shape<MODE>::kBM;
   constexpr int kDmaPerWave = Shape<MODE>::kDmaPerWave;
   __shared__ __attribute__((aligned(1024))) uint8_t Kb0[kBN * 256], Kb1[kBN * 256];
@@ -194,6 +207,12 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
     n0 = a.cap0;
     if (a.n_kv) n0 = max(min(n0, *a.n_kv), (int64_t)0);
   }
+  // K pieces of split keys: elements of a temporal block and of the other dims
+  // of one head row; the K base of a dense segment is the token row (the head's
+  // pieces are found by the lanes' chunk offsets), of a ragged run its start,
+  // with its other dims n0 temporal blocks further
+  const int64_t kte = SPLIT ? (int64_t)a.tvc * 8 : 0, kse = SPLIT ? kD - kte : 0;
+  const int64_t kbase0 = SPLIT && !RAGGED ? 0 : base0;
   // kLag: rows [0, pa) and [pb, n) lagged, [pa, pb) plain
   const int64_t pa = LAG ? min(a.plain_begin, n0) : 0;
   const int64_t pb = LAG ? min(max(a.plain_end, a.plain_begin), n0) : 0;
@@ -253,21 +272,56 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
   // conflicts took a third of the LDS cycles).  Descriptors end at the range's
   // last row, so rows past it arrive as zeros.
   const int dma_row = wave * 4 * kDmaPerWave + (lane >> 4), dma_pos = lane & 15;
+  // Split keys: the chunk c = dma_pos ^ (r & 15) a lane loads is found in a
+  // dense token row at head h's temporal chunk h tvc + (c - tvb) or, for the
+  // other chunks, after all heads' temporal blocks at n_heads tvc +
+  // h (16 - tvc) + s (16-byte units; s counts the non-temporal chunks before
+  // c); in a ragged run, at c - tvb of the row's temporal piece or s of its
+  // other-dims piece.  (Recomputed per tile: a few integer operations.)
   // (which operands to load is a flag, not a null LDS pointer: LDS offset 0 is
   // a valid buffer address)
-  auto load_tile = [&](const uint16_t* kp, const uint16_t* vp, uint32_t st2, int64_t rows_left,
-                       lds_u8* kdst, lds_u8* vdst, bool do_k, bool do_v) {
-    const uint32_t bytes = (uint32_t)min(rows_left, (int64_t)kBN) * st2;
+  // planar: K is a ragged run of split keys (two pieces, kp and kp2)
+  auto load_tile = [&](const uint16_t* kp, const uint16_t* kp2, const uint16_t* vp, uint32_t st2,
+                       int64_t rows_left, lds_u8* kdst, lds_u8* vdst, bool do_k, bool do_v,
+                       bool planar) {
+    const uint32_t rows = (uint32_t)min(rows_left, (int64_t)kBN);
+    const uint32_t bytes = rows * st2;
 #pragma unroll
     for (int u = 0; u < kDmaPerWave; ++u) {
       const int r = dma_row + 4 * u;
       const uint32_t row_off = (uint32_t)r * st2;
       if (do_k) {
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)bytes, kBufferWord3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, kdst + (wave * kDmaPerWave + u) * 1024, 16,
-            row_off + ((dma_pos ^ (r & 15)) << 4), 0, 0, 0);
+        lds_u8* const kl = kdst + (wave * kDmaPerWave + u) * 1024;
+        const int c = dma_pos ^ (r & 15);
+        const bool tq = c >= a.tvb && c < a.tvb + a.tvc;
+        const int sidx = c < a.tvb ? c : c - a.tvc;
+        if (SPLIT && RAGGED && planar) {
+          // two pieces, each through a descriptor that ends at the tile's last
+          // row (rows past it read as zeros); a lane loads from the one holding
+          // its chunk
+          const uint32_t tb = (uint32_t)kte * 2, sb = (uint32_t)kse * 2;
+          if (tq) {
+            const __amdgpu_buffer_rsrc_t rt =
+                __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)(rows * tb), kBufferWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, kl, 16,
+                                                     (uint32_t)r * tb + ((uint32_t)(c - a.tvb) << 4),
+                                                     0, 0, 0);
+          } else {
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)kp2, 0, (int)(rows * sb), kBufferWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, kl, 16,
+                                                     (uint32_t)r * sb + ((uint32_t)sidx << 4), 0,
+                                                     0, 0);
+          }
+        } else {
+          const uint32_t koff =
+              SPLIT ? (uint32_t)(tq ? head * a.tvc + (c - a.tvb)
+                                    : a.n_heads * a.tvc + head * (16 - a.tvc) + sidx) << 4
+                    : (uint32_t)c << 4;
+          const __amdgpu_buffer_rsrc_t rk =
+              __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)bytes, kBufferWord3);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kl, 16, row_off + koff, 0, 0, 0);
+        }
       }
       if (do_v) {
         const __amdgpu_buffer_rsrc_t rv =
@@ -419,22 +473,27 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
   f32x16 sa[2], sb[2];
   bf16x8 pt[4];
   int q_state = -1;                            // query fragments held: -1 none, 0 plain, 1 lagged
-  auto run_pass = [&](const uint16_t* kp, const uint16_t* vp, int64_t stride, int64_t n_rows,
-                      int q_want) {
+  // (planar: K is a ragged run of split keys, kp its temporal piece and kp2 its
+  // other-dims piece at the pass's first row; otherwise kp2 is unused)
+  auto run_pass = [&](const uint16_t* kp, const uint16_t* kp2, const uint16_t* vp,
+                      int64_t stride, int64_t n_rows, int q_want, bool planar) {
     const int64_t n_tiles = (n_rows + kBN - 1) / kBN;
     if (n_tiles <= 0) return;
     const uint32_t st2 = (uint32_t)stride * 2u;
     const int64_t tile_elems = (int64_t)kBN * stride;
-    auto tk = [&](int64_t t) { return kp + t * tile_elems; };
+    auto tk = [&](int64_t t) { return kp + t * (planar ? kBN * kte : tile_elems); };
+    auto tk2 = [&](int64_t t) { return kp2 + t * (planar ? kBN * kse : tile_elems); };
     auto tv = [&](int64_t t) { return vp + t * tile_elems; };
     auto step = [&](int64_t t, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const lds_u8* k_next,
                     lds_u8* k_free, const lds_u8* v_cur, lds_u8* v_free) {
       __builtin_amdgcn_s_waitcnt(0);           // this wavefront's K(t + 1), V(t) have landed
       lds_barrier();                           // ... everyone's; K(t), V(t - 1) are free
       if (t + 2 < n_tiles)
-        load_tile(tk(t + 2), tv(t + 2), st2, n_rows - (t + 2) * kBN, k_free, v_free, true, false);
+        load_tile(tk(t + 2), tk2(t + 2), tv(t + 2), st2, n_rows - (t + 2) * kBN, k_free, v_free,
+                  true, false, planar);
       if (t + 1 < n_tiles)
-        load_tile(tk(t + 1), tv(t + 1), st2, n_rows - (t + 1) * kBN, k_free, v_free, false, true);
+        load_tile(tk(t + 1), tk2(t + 1), tv(t + 1), st2, n_rows - (t + 1) * kBN, k_free, v_free,
+                  false, true, planar);
       s_tile(k_next, s_nxt);     // past the last tile: stale LDS, result unused (keeps
                                  // the MFMAs in the same block as the softmax work)
       s_exp(s_cur, pt);
@@ -453,8 +512,9 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
       load_q(LAG && q_want == 1);
       q_state = q_want;
     }
-    load_tile(tk(0), tv(0), st2, n_rows, kb0, vb0, true, true);
-    if (n_tiles > 1) load_tile(tk(1), tv(1), st2, n_rows - kBN, kb1, vb1, true, false);
+    load_tile(tk(0), tk2(0), tv(0), st2, n_rows, kb0, vb0, true, true, planar);
+    if (n_tiles > 1)
+      load_tile(tk(1), tk2(1), tv(1), st2, n_rows - kBN, kb1, vb1, true, false, planar);
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
     s_tile(kb0, sa);
@@ -467,21 +527,32 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
     lds_barrier();                             // the next pass reuses the buffers
   };
   if (RAGGED) {
+    // K of the run: interleaved, head rows kD apart; split, n0 temporal blocks
+    // (kte elements each) then n0 other-dims pieces (kse each)
+    const uint16_t* kr = a.k0 + base0;
+    const uint16_t* kr2 = kr + n0 * kte;
+    const int64_t krs = SPLIT ? kte : stride0;
     if (LAG) {                                 // run: lagged rows, then the plain tail
       const int64_t tail = min(max(a.plain_tail, (int64_t)0), n0);
-      run_pass(a.k0 + base0, a.v0 + base0, stride0, n0 - tail, 1);
-      run_pass(a.k0 + base0 + (n0 - tail) * stride0, a.v0 + base0 + (n0 - tail) * stride0,
-               stride0, tail, 0);
+      run_pass(kr, kr2, a.v0 + base0, stride0, n0 - tail, 1, SPLIT);
+      run_pass(kr + (n0 - tail) * krs, kr2 + (n0 - tail) * kse,
+               a.v0 + base0 + (n0 - tail) * stride0, stride0, tail, 0, SPLIT);
     } else {
-      run_pass(a.k0 + base0, a.v0 + base0, stride0, n0, 0);
+      run_pass(kr, kr2, a.v0 + base0, stride0, n0, 0, SPLIT);
     }
-    if (a.k1) run_pass(a.k1 + (int64_t)head * kD, a.v1 + (int64_t)head * kD, a.row, a.n1, 0);
+    // the chunk block is dense token rows (split keys: the head's pieces are
+    // found by the lanes' row offsets from the token row)
+    if (a.k1)
+      run_pass(a.k1 + (SPLIT ? 0 : (int64_t)head * kD), a.k1, a.v1 + (int64_t)head * kD, a.row,
+               a.n1, 0, false);
   } else if (LAG) {
-    run_pass(a.k0 + base0, a.v0 + base0, a.row, pa, 1);                      // lagged, before
-    run_pass(a.k0 + base0 + pb * a.row, a.v0 + base0 + pb * a.row, a.row, n0 - pb, 1);  // after
-    run_pass(a.k0 + base0 + pa * a.row, a.v0 + base0 + pa * a.row, a.row, pb - pa, 0);  // plain
+    run_pass(a.k0 + kbase0, a.k0, a.v0 + base0, a.row, pa, 1, false);          // lagged, before
+    run_pass(a.k0 + kbase0 + pb * a.row, a.k0, a.v0 + base0 + pb * a.row, a.row, n0 - pb, 1,
+             false);                                                          // lagged, after
+    run_pass(a.k0 + kbase0 + pa * a.row, a.k0, a.v0 + base0 + pa * a.row, a.row, pb - pa, 0,
+             false);                                                          // plain
   } else {
-    run_pass(a.k0 + base0, a.v0 + base0, stride0, n0, 0);
+    run_pass(a.k0 + kbase0, a.k0, a.v0 + base0, stride0, n0, 0, false);
   }
 
   // ---- O[qi][head][d], d = 32 dt + 8 g + 4 hf + (0..3) ----
@@ -504,6 +575,13 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
 
 namespace {
 
+// Split keys: the head row's temporal 16-byte chunks [tvb, tvb + tvc) (bf16,
+// head_dim 128; pair_begin and n_pairs multiples of 4, checked by the caller).
+void set_split(AttnArgs& a, int32_t key_layout, int32_t pair_begin, int32_t n_pairs) {
+  a.tvb = key_layout == DP_KEY_SPLIT ? pair_begin / 4 : 0;
+  a.tvc = key_layout == DP_KEY_SPLIT ? n_pairs / 4 : 0;
+}
+
 dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_heads, float scale,
                  hipStream_t s) {
   a.q = reinterpret_cast<const uint16_t*>(q);
@@ -519,16 +597,30 @@ dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_hea
   a.c = scale * 1.4426950408889634f;
   const uint64_t blocks = (uint64_t)a.n_qt * n_heads;
   if (blocks == 0) return DP_OK;
-  if (mode == kLag)
-    hipLaunchKernelGGL(attn_fwd_kernel<kLag>, dim3((uint32_t)blocks), dim3(Shape<kLag>::kBlock), 0, s, a);
-  else if (mode == kRagged)
-    hipLaunchKernelGGL(attn_fwd_kernel<kRagged>, dim3((uint32_t)blocks), dim3(Shape<kRagged>::kBlock), 0, s,
-                       a);
-  else if (mode == kRaggedLag)
-    hipLaunchKernelGGL(attn_fwd_kernel<kRaggedLag>, dim3((uint32_t)blocks),
-                       dim3(Shape<kRaggedLag>::kBlock), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<kDense>, dim3((uint32_t)blocks), dim3(Shape<kDense>::kBlock), 0, s, a);
+  const dim3 grid((uint32_t)blocks);
+  if (a.tvc > 0) {
+    if (mode == kLag)
+      hipLaunchKernelGGL(attn_fwd_kernel<kLag | kSplit>, grid, dim3(Shape<kLag>::kBlock), 0, s, a);
+    else if (mode == kRagged)
+      hipLaunchKernelGGL(attn_fwd_kernel<kRagged | kSplit>, grid, dim3(Shape<kRagged>::kBlock), 0,
+                         s, a);
+    else if (mode == kRaggedLag)
+      hipLaunchKernelGGL(attn_fwd_kernel<kRaggedLag | kSplit>, grid,
+                         dim3(Shape<kRaggedLag>::kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_fwd_kernel<kDense | kSplit>, grid, dim3(Shape<kDense>::kBlock), 0, s,
+                         a);
+  } else {
+    if (mode == kLag)
+      hipLaunchKernelGGL(attn_fwd_kernel<kLag>, grid, dim3(Shape<kLag>::kBlock), 0, s, a);
+    else if (mode == kRagged)
+      hipLaunchKernelGGL(attn_fwd_kernel<kRagged>, grid, dim3(Shape<kRagged>::kBlock), 0, s, a);
+    else if (mode == kRaggedLag)
+      hipLaunchKernelGGL(attn_fwd_kernel<kRaggedLag>, grid, dim3(Shape<kRaggedLag>::kBlock), 0, s,
+                         a);
+    else
+      hipLaunchKernelGGL(attn_fwd_kernel<kDense>, grid, dim3(Shape<kDense>::kBlock), 0, s, a);
+  }
   return check_launch("attn_fwd_kernel");
 }
 
@@ -536,8 +628,10 @@ dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_hea
 
 dp_status launch_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
                            int64_t kv_cap, const int64_t* n_kv, int32_t n_heads, float scale,
+                           int32_t key_layout, int32_t pair_begin, int32_t n_pairs,
                            hipStream_t s) {
   AttnArgs a{};
+  set_split(a, key_layout, pair_begin, n_pairs);
   a.k0 = reinterpret_cast<const uint16_t*>(k);
   a.v0 = reinterpret_cast<const uint16_t*>(v);
   a.n_kv = n_kv;
@@ -549,8 +643,9 @@ dp_status launch_attention_lag(const void* q, const void* k, const void* v, void
                                int64_t n_q, int64_t kv_cap, const int64_t* n_kv,
                                int64_t plain_begin, int64_t plain_end, const float* theta,
                                int32_t pair_begin, int32_t n_pairs, float lag, int32_t n_heads,
-                               float scale, hipStream_t s) {
+                               float scale, int32_t key_layout, hipStream_t s) {
   AttnArgs a{};
+  set_split(a, key_layout, pair_begin, n_pairs);
   a.k0 = reinterpret_cast<const uint16_t*>(k);
   a.v0 = reinterpret_cast<const uint16_t*>(v);
   a.n_kv = n_kv;
@@ -567,9 +662,11 @@ dp_status launch_attention_lag(const void* q, const void* k, const void* v, void
 dp_status launch_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
                               int64_t ragged_capacity, const int64_t* head_offsets,
                               const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
-                              int64_t n_q, int32_t n_heads, float scale, hipStream_t s,
+                              int64_t n_q, int32_t n_heads, float scale, int32_t key_layout,
+                              int32_t pair_begin, int32_t n_pairs, hipStream_t s,
                               const HsLag* lag) {
   AttnArgs a{};
+  set_split(a, key_layout, pair_begin, n_pairs);
   if (lag) {
     a.plain_tail = lag->plain_tail;
     a.theta = lag->theta;

@@ -144,13 +144,25 @@ struct RopeView {
   int32_t tv_begin;    // first 16-byte vector of the temporal block in a head row
   int32_t tv_count;    // vectors touched by the temporal block
   int32_t ppv;         // pairs per 16-byte vector: 4 (bf16) or 2 (fp32)
-  // In-place passes rewrite whole 128-byte lines: vectors [wv_begin,
-  // wv_begin + wv_count) of a head row cover the temporal block rounded out to
-  // 128-byte boundaries (clamped to the head row); vectors outside the block
-  // are written back unchanged.  A partly written line costs the memory
-  // controller a read-modify-write, which measured slower than the extra bytes.
+  // In-place passes walk, for every head of a token row, vectors
+  // [wv_begin, wv_begin + wv_count) of that head's segment, the segments
+  // head_stride_v vectors apart; the temporal block starts tv_off vectors into
+  // a segment.  Interleaved keys: the segment is the head row and the walk
+  // covers the temporal block rounded out to 128-byte boundaries (clamped to
+  // the head row; vectors outside the block are written back unchanged: a
+  // partly written line costs the memory controller a read-modify-write,
+  // which measured slower than the extra bytes).  Split keys: the segment is
+  // the head's temporal block in the row's leading plane, walked exactly.
   int32_t wv_begin;
   int32_t wv_count;
+  int32_t head_stride_v;
+  int32_t tv_off;
+  // Whole-row passes (gather, append) locate vector c of a row by
+  // h = c / seg and tv = c - h seg - tv_off, with seg = head_stride_v; a
+  // vector is in a temporal block iff 0 <= tv < tv_count and c < blk_end
+  // (interleaved: every head row; split: the leading plane of n_heads blocks).
+  int32_t blk_end;
+  int32_t split;
 };
 
 }  // namespace dp

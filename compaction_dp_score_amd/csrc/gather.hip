@@ -34,7 +34,7 @@ struct GatherArgs {
   int64_t src_rows;
   int32_t* dev_error;
   FastDiv div_row;     // RV: 16-byte vectors per row
-  FastDiv div_head;    // vectors per head row
+  FastDiv div_head;    // segment of the fused rotation's walk (see RopeView)
   uint32_t total_cap;  // dst_cap * RV
   uint32_t n_slabs;    // n_layers * n_kv
   int32_t n_kv;        // 1 (K only) or 2
@@ -73,8 +73,8 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
     // in flight).  Lanes outside the temporal block read entry 0 and keep
     // their data.
     const uint32_t h = fdiv(c, a.div_head);
-    const int tv = (int)(c - h * a.div_head.d) - a.rope.tv_begin;
-    const bool in_block = tv >= 0 && tv < a.rope.tv_count;
+    const int tv = (int)(c - h * a.div_head.d) - a.rope.tv_off;
+    const bool in_block = tv >= 0 && tv < a.rope.tv_count && (int)c < a.rope.blk_end;
     const uint32_t j0 = __builtin_amdgcn_readfirstlane(j);
     const bool one_row = __builtin_amdgcn_ballot_w64(j != j0) == 0;
     int32_t s;
@@ -124,7 +124,10 @@ dp_status launch_gather(const dp_kv& kv, const int32_t* idx, const int64_t* n_ke
   a.dev_error = kv.dev_error;
   const uint32_t rv = (uint32_t)((int64_t)kv.n_heads * kv.head_dim * elem_size(kv.dtype) / 16);
   a.div_row = make_fastdiv(rv);
-  a.div_head = make_fastdiv((uint32_t)(kv.head_dim * elem_size(kv.dtype) / 16));
+  // segment of the fused rotation's walk: the head row (interleaved keys) or
+  // the head's temporal block in the row's leading plane (split keys)
+  a.div_head = make_fastdiv(rope ? (uint32_t)rope->head_stride_v
+                                 : (uint32_t)(kv.head_dim * elem_size(kv.dtype) / 16));
   a.total_cap = (uint32_t)(kv.dst_capacity * rv);
   a.n_kv = kv.v_src ? 2 : 1;
   a.dtype = kv.dtype;

@@ -15,6 +15,9 @@
 //   the way.
 // hs_reindex_kernel: the same walk over a packed ragged K cache, in place,
 //   rewriting the whole 128-byte lines that hold the temporal pairs.
+// Split keys: source rows hold the temporal blocks of all heads first, and each
+// output run of n head rows holds its n temporal blocks, then its n remaining
+// parts, so the re-index of a run is one contiguous span of whole lines.
 #include "dp_internal.h"
 
 namespace dp {
@@ -80,14 +83,18 @@ struct HsArgs {
   int32_t dtype;
   int32_t has_rope;
   uint32_t vph;                   // 16-byte vectors per head row
-  FastDiv div_inner;              // vectors walked per head row: vph (gather) or tv_count
+  FastDiv div_inner;              // vectors walked per head row: vph (gather) or wv_count
   RopeView rope;
+  // split keys: temporal vectors [tvb, tvb + tvc) of a head row, svc = vph - tvc
+  int32_t split;
+  uint32_t tvb, tvc, svc;
 };
 
 // Per-workgroup state shared by the gather and the re-index.
 struct HsTile {
   int cls;          // class of this tile
   int64_t j0;       // first entry of the class list
+  int64_t n_run;    // entries of the class list: the length of each of its heads' runs
   int rows;         // live entries in the tile (<= kRT)
   int nh;           // heads of the class in this layer
   int slab;         // (layer, K|V) index
@@ -131,6 +138,7 @@ __device__ bool hs_setup(const HsArgs& a, int n_slab_per_layer, HsTile& tl, int*
   tl.cls = cls;
   tl.slab = (int)slab;
   tl.j0 = (int64_t)(r - pre[cls]) * kRT;
+  tl.n_run = lens[cls];
   tl.rows = (int)min((int64_t)kRT, lens[cls] - tl.j0);
   const int layer = (int)slab / n_slab_per_layer;
 
@@ -210,10 +218,26 @@ __global__ __launch_bounds__(kBlock) void hs_gather_kernel(HsArgs a) {
         const int32_t s = s_src[r];
         if (r < tl.rows && (uint32_t)s < (uint64_t)a.src_rows) {
           const int64_t o = head_off[k] + tl.j0 + r;
-          if (o >= a.out_cap) {
+          const bool split_k = a.split && !is_v;
+          // a split run is placed whole, so all of it must fit
+          if (head_off[k] < 0 || (split_k ? head_off[k] + tl.n_run : o + 1) > a.out_cap) {
             overflow = true;
           } else {
+            // natural vector q of head row (s, h): its place in the source row
+            // and in the output run
+            const int h = heads[k];
+            const bool tq = q >= a.tvb && q < a.tvb + a.tvc;
+            const uint32_t sq = q < a.tvb ? q : q - a.tvc;   // index among the other vectors
+            int64_t src_i = ((int64_t)s * a.n_heads + h) * a.vph + q;
             dst_i[u] = o * a.vph + q;
+            if (split_k) {
+              const int64_t jr = tl.j0 + r;                  // row within the run
+              src_i = (int64_t)s * a.n_heads * a.vph +
+                      (tq ? (int64_t)h * a.tvc + (q - a.tvb)
+                          : (int64_t)a.n_heads * a.tvc + (int64_t)h * a.svc + sq);
+              dst_i[u] = head_off[k] * a.vph +
+                         (tq ? jr * a.tvc + (q - a.tvb) : tl.n_run * a.tvc + jr * a.svc + sq);
+            }
             if (rope) {
               const int tv = (int)q - a.rope.tv_begin;
               if (tv >= 0 && tv < a.rope.tv_count && s_dl[r] != 0.0f) {
@@ -226,7 +250,7 @@ __global__ __launch_bounds__(kBlock) void hs_gather_kernel(HsArgs a) {
                 rot[u] = true;
               }
             }
-            v[u] = __builtin_nontemporal_load(src + ((int64_t)s * a.n_heads + heads[k]) * a.vph + q);
+            v[u] = __builtin_nontemporal_load(src + src_i);
           }
         }
       }
@@ -268,14 +292,16 @@ __global__ __launch_bounds__(kBlock) void hs_reindex_kernel(HsArgs a) {
       at[u] = -1;
       if (i < total) {
         const uint32_t t = fdiv(i, a.div_inner);
-        const int wq = a.rope.wv_begin + (int)(i - t * a.div_inner.d);   // vector in the head row
+        const int wq = a.rope.wv_begin + (int)(i - t * a.div_inner.d);   // vector in the segment
         const int r = (int)(t & (kRT - 1));
         const int k = (int)(t >> kLogRT);
         if (r < tl.rows && s_dl[r] != 0.0f) {
           const int64_t o = head_off[k] + tl.j0 + r;
-          if (o < a.out_cap) {
-            at[u] = o * a.vph + wq;
-            const int tv = wq - a.rope.tv_begin;
+          // interleaved: the row's lines holding the block; split: the row's
+          // temporal block in the run's leading plane (the whole run must fit)
+          if (head_off[k] >= 0 && (a.split ? head_off[k] + tl.n_run <= a.out_cap : o < a.out_cap)) {
+            at[u] = a.split ? head_off[k] * a.vph + (tl.j0 + r) * a.tvc + wq : o * a.vph + wq;
+            const int tv = wq - a.rope.tv_off;
             const bool in_block = tv >= 0 && tv < a.rope.tv_count;
             const int p0 = in_block ? tv * a.rope.ppv : 0;
             nv[u] = in_block ? min(a.rope.ppv, a.rope.n_pairs - p0) : 0;
@@ -345,6 +371,13 @@ dp_status launch_hs_gather(const dp_kv_hs& kv, const uint8_t* head_class, int32_
   if (rope) a.rope = *rope;
   a.vph = (uint32_t)(kv.head_dim * elem_size(kv.dtype) / 16);
   a.div_inner = make_fastdiv(a.vph);
+  a.split = kv.key_layout == DP_KEY_SPLIT;
+  if (a.split) {
+    const int esz = elem_size(kv.dtype);
+    a.tvb = (uint32_t)(2 * kv.pair_begin * esz / 16);
+    a.tvc = (uint32_t)(2 * kv.n_pairs * esz / 16);
+    a.svc = a.vph - a.tvc;
+  }
   fill_caps(a, class_cap, n_classes);
   const uint64_t gx = hs_tiles(class_cap, n_classes) * (uint64_t)(kv.n_layers * a.n_kv);
   if (gx == 0) return DP_OK;
@@ -375,6 +408,10 @@ dp_status launch_hs_reindex(void* k, int64_t k_cap, int32_t L, int32_t H, int32_
   a.rope = rope;
   a.vph = (uint32_t)(head_dim * elem_size(dtype) / 16);
   a.div_inner = make_fastdiv((uint32_t)rope.wv_count);
+  a.split = rope.split;
+  a.tvb = (uint32_t)rope.tv_begin;
+  a.tvc = (uint32_t)rope.tv_count;
+  a.svc = a.vph - a.tvc;
   fill_caps(a, class_cap, n_classes);
   const uint64_t gx = hs_tiles(class_cap, n_classes) * (uint64_t)L;
   if (gx == 0) return DP_OK;

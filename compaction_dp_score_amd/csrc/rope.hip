@@ -11,8 +11,11 @@
 // reindex_kernel: in place over every (row, head) of each layer, touching the
 //   128-byte lines that hold the temporal pairs; rows of frames with delta == 0
 //   are neither read nor written.  HBM-bound: the method needs
-//   2 * 2*n_pairs*elem bytes per re-indexed head row; whole-line rewriting moves
-//   2 * (lines * 128) bytes (512 of 352 for 44 bf16 pairs).
+//   2 * 2*n_pairs*elem bytes per re-indexed head row.  With interleaved keys
+//   the temporal block of a head row straddles lines and whole-line rewriting
+//   moves 2 * (lines * 128) bytes (512 of 352 for 44 bf16 pairs); with split
+//   keys the blocks of all heads are the row's leading lines and exactly the
+//   method's bytes move.
 // shift_table_kernel + shift_kernel: the steady-state form.  Once a frame is
 //   past the knee before and after a step, its phase step is the same for every
 //   such frame (q0 advances F frames: F (1 - 1/c)), so a row range holding only
@@ -69,14 +72,13 @@ struct ReindexArgs {
   int64_t rows_cap;
   FastDiv div_row;    // vectors per row  = H * wv_count
   FastDiv div_head;   // vectors per head = wv_count
-  uint32_t vph;       // 16-byte vectors per head row
-  uint32_t n_heads;
+  uint32_t row_vec;   // 16-byte vectors per token row (H * vph)
   uint32_t n_layers;
   int32_t dtype;
   RopeView rope;
 };
 
-// One 16-byte vector per lane over the written span of every (row, head) of
+// One 16-byte vector per lane over the walked span of every (row, head) of
 // a layer; the 1-D grid is sized by capacity and each workgroup derives
 // (layer, tile) from the device-side row count, so surplus workgroups sit at
 // the tail.  With rows of >= kBlock vectors a workgroup spans at most two
@@ -123,15 +125,15 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
   if (dl == 0.0f) return;
   const uint32_t rem = i - j * per_row;
   const uint32_t h = fdiv(rem, a.div_head);
-  const int wq = a.rope.wv_begin + (int)(rem - h * a.div_head.d);   // vector in the head row
-  const int tv = wq - a.rope.tv_begin;
+  const int wq = a.rope.wv_begin + (int)(rem - h * a.div_head.d);   // vector in the segment
+  const int tv = wq - a.rope.tv_off;
   const bool in_block = tv >= 0 && tv < a.rope.tv_count;
   const int p0 = in_block ? tv * a.rope.ppv : 0;
   const f32x4* t = reinterpret_cast<const f32x4*>(a.rope.cs + (int64_t)f * a.rope.pairs_padded + p0);
   const f32x4 t01 = t[0];     // the table has a 32-byte tail, so t[1] is readable
   const f32x4 t23 = t[1];
   u32x4* __restrict__ p = reinterpret_cast<u32x4*>(a.layers[layer]) +
-                          ((a.row_begin + (int64_t)j) * a.n_heads + h) * a.vph + wq;
+                          (a.row_begin + (int64_t)j) * a.row_vec + h * a.rope.head_stride_v + wq;
   u32x4 v = __builtin_nontemporal_load(p);
   if (in_block) v = rotate_vec_tab(v, a.dtype, t01, t23, min(a.rope.ppv, a.rope.n_pairs - p0));
   __builtin_nontemporal_store(v, p);
@@ -163,16 +165,15 @@ struct ShiftArgs {
   int64_t rows_cap;
   const f32x2* cs;    // the step's table
   int32_t n_pairs;
-  FastDiv div_row;    // written vectors per row = H * wv_count
-  FastDiv div_head;   // written vectors per head row = wv_count
-  uint32_t vph;       // 16-byte vectors per head row
-  uint32_t n_heads;
+  FastDiv div_row;    // walked vectors per row = H * wv_count
+  FastDiv div_head;   // walked vectors per head = wv_count
+  uint32_t row_vec;   // 16-byte vectors per token row (H * vph)
   uint32_t n_layers;
   int32_t dtype;
-  int32_t tv_begin, tv_count, ppv, wv_begin;
+  int32_t tv_off, tv_count, ppv, wv_begin, head_stride_v;
 };
 
-// One 16-byte vector per lane over the written span of every (row, head) of a
+// One 16-byte vector per lane over the walked span of every (row, head) of a
 // layer, as reindex_kernel, with the same table for every row (no row frames).
 __global__ __launch_bounds__(kBlock) void shift_kernel(ShiftArgs a) {
   int64_t end = a.rows_cap;
@@ -189,15 +190,15 @@ __global__ __launch_bounds__(kBlock) void shift_kernel(ShiftArgs a) {
   const uint32_t j = fdiv(i, a.div_row);
   const uint32_t rem = i - j * per_row;
   const uint32_t h = fdiv(rem, a.div_head);
-  const int wq = a.wv_begin + (int)(rem - h * a.div_head.d);   // vector in the head row
-  const int tv = wq - a.tv_begin;
+  const int wq = a.wv_begin + (int)(rem - h * a.div_head.d);   // vector in the segment
+  const int tv = wq - a.tv_off;
   const bool in_block = tv >= 0 && tv < a.tv_count;
   const int p0 = in_block ? tv * a.ppv : 0;
   const f32x4* t = reinterpret_cast<const f32x4*>(a.cs + p0);
   const f32x4 t01 = t[0];     // the table is padded, so t[1] is readable
   const f32x4 t23 = t[1];
   u32x4* __restrict__ p = reinterpret_cast<u32x4*>(a.layers[layer]) +
-                          ((a.row_begin + (int64_t)j) * a.n_heads + h) * a.vph + wq;
+                          (a.row_begin + (int64_t)j) * a.row_vec + h * a.head_stride_v + wq;
   u32x4 v = __builtin_nontemporal_load(p);
   if (in_block) v = rotate_vec_tab(v, a.dtype, t01, t23, min(a.ppv, a.n_pairs - p0));
   __builtin_nontemporal_store(v, p);
@@ -211,7 +212,8 @@ size_t rope_ws_bytes(int32_t n_frames, int32_t n_pairs) {
   return dbytes + (size_t)n_frames * pp * sizeof(f32x2) + 32;   // 32-byte tail: see gather
 }
 
-void rope_view(const dp_rope& r, const void* ws, RopeView* view, int dtype, int head_dim) {
+void rope_view(const dp_rope& r, const void* ws, RopeView* view, int dtype, int head_dim,
+               int n_heads) {
   const int32_t pp = (r.n_pairs + 3) / 4 * 4;
   const size_t dbytes = ((size_t)r.n_frames * 4 + 15) / 16 * 16;
   const float* delta = reinterpret_cast<const float*>(ws);
@@ -228,15 +230,28 @@ void rope_view(const dp_rope& r, const void* ws, RopeView* view, int dtype, int 
   const int end_bytes = 2 * (r.pair_begin + r.n_pairs) * esz;
   view->tv_count = (end_bytes + 15) / 16 - view->tv_begin;
   const int vph = head_dim * esz / 16;
-  const int wb = view->tv_begin / 8 * 8;
-  int we = (view->tv_begin + view->tv_count + 7) / 8 * 8;
-  if (we > vph) we = vph;
-  view->wv_begin = wb;
-  view->wv_count = we - wb;
+  view->split = r.key_layout == DP_KEY_SPLIT;
+  if (view->split) {
+    // the head's temporal block, exactly (whole vectors, checked by the caller)
+    view->wv_begin = 0;
+    view->wv_count = view->tv_count;
+    view->head_stride_v = view->tv_count;
+    view->tv_off = 0;
+    view->blk_end = n_heads * view->tv_count;
+  } else {
+    const int wb = view->tv_begin / 8 * 8;
+    int we = (view->tv_begin + view->tv_count + 7) / 8 * 8;
+    if (we > vph) we = vph;
+    view->wv_begin = wb;
+    view->wv_count = we - wb;
+    view->head_stride_v = vph;
+    view->tv_off = view->tv_begin;
+    view->blk_end = 0x7FFFFFFF;
+  }
 }
 
 dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dtype,
-                              int head_dim, hipStream_t s) {
+                              int head_dim, int n_heads, hipStream_t s) {
   const int32_t pp = (r.n_pairs + 3) / 4 * 4;
   const size_t dbytes = ((size_t)r.n_frames * 4 + 15) / 16 * 16;
   float* delta = reinterpret_cast<float*>(ws);
@@ -245,7 +260,7 @@ dp_status launch_rope_prepare(const dp_rope& r, void* ws, RopeView* view, int dt
                      pp, r.frame_t, r.frame_phase, r.q0, r.knee, r.inv_factor, r.axis, delta, cs);
   dp_status st = check_launch("rope_prepare_kernel");
   if (st != DP_OK) return st;
-  rope_view(r, ws, view, dtype, head_dim);
+  rope_view(r, ws, view, dtype, head_dim, n_heads);
   return DP_OK;
 }
 
@@ -261,8 +276,7 @@ dp_status launch_reindex(void* const* k, int32_t n_layers, int32_t n_heads, int3
   a.rows_cap = rows_cap;
   a.div_row = make_fastdiv((uint32_t)(n_heads * rope.wv_count));
   a.div_head = make_fastdiv((uint32_t)rope.wv_count);
-  a.vph = (uint32_t)(head_dim * elem_size(dtype) / 16);
-  a.n_heads = (uint32_t)n_heads;
+  a.row_vec = (uint32_t)(n_heads * (head_dim * elem_size(dtype) / 16));
   a.n_layers = (uint32_t)n_layers;
   a.dtype = dtype;
   a.rope = rope;
@@ -283,14 +297,16 @@ size_t rope_shift_ws_bytes(int32_t n_pairs) {
 dp_status launch_rope_shift(void* const* k, int32_t n_layers, int32_t n_heads, int32_t head_dim,
                             int32_t dtype, int64_t row_begin, int64_t rows_cap,
                             const int64_t* n_rows, const float* theta, int32_t pair_begin,
-                            int32_t n_pairs, float delta, void* ws, hipStream_t s) {
+                            int32_t n_pairs, int32_t key_layout, float delta, void* ws,
+                            hipStream_t s) {
   if (delta == 0.0f || rows_cap <= row_begin) return DP_OK;   // nothing moves
   dp_rope r{};
   r.pair_begin = pair_begin;
   r.n_pairs = n_pairs;
   r.n_frames = 1;
+  r.key_layout = key_layout;
   RopeView view{};
-  rope_view(r, nullptr, &view, dtype, head_dim);               // pair layout only
+  rope_view(r, nullptr, &view, dtype, head_dim, n_heads);      // pair layout only
   f32x2* cs = reinterpret_cast<f32x2*>(ws);
   hipLaunchKernelGGL(shift_table_kernel, dim3(1), dim3(64), 0, s, theta, n_pairs,
                      view.pairs_padded + 4, delta, cs);
@@ -305,14 +321,14 @@ dp_status launch_rope_shift(void* const* k, int32_t n_layers, int32_t n_heads, i
   a.n_pairs = n_pairs;
   a.div_row = make_fastdiv((uint32_t)(n_heads * view.wv_count));
   a.div_head = make_fastdiv((uint32_t)view.wv_count);
-  a.vph = (uint32_t)(head_dim * elem_size(dtype) / 16);
-  a.n_heads = (uint32_t)n_heads;
+  a.row_vec = (uint32_t)(n_heads * (head_dim * elem_size(dtype) / 16));
   a.n_layers = (uint32_t)n_layers;
   a.dtype = dtype;
-  a.tv_begin = view.tv_begin;
+  a.tv_off = view.tv_off;
   a.tv_count = view.tv_count;
   a.ppv = view.ppv;
   a.wv_begin = view.wv_begin;
+  a.head_stride_v = view.head_stride_v;
   const uint64_t gx =
       ((uint64_t)(rows_cap - row_begin) * a.div_row.d + kBlock - 1) / kBlock * (uint64_t)n_layers;
   hipLaunchKernelGGL(shift_kernel, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define DP_ABI_VERSION 1
+#define DP_ABI_VERSION 2
 
 typedef enum {
   DP_OK = 0,
@@ -226,6 +226,27 @@ dp_status dp_score_index(const float* x0_hat, const float* x_final, int32_t d,
  * ------------------------------------------------------------------------- */
 typedef enum { DP_AXIS_PAGE = 0, DP_AXIS_COMPRESSED = 1 } dp_axis;
 
+/* Key layout (where a key row keeps its temporal pairs).  Keys are token-major,
+ * one row per token holding all n_heads heads; V is never permuted.
+ *   DP_KEY_INTERLEAVED: the row is [n_heads][head_dim], each head's dims in
+ *     order.
+ *   DP_KEY_SPLIT: the row holds first the temporal block of every head
+ *     (head h: dims [2 pair_begin, 2 (pair_begin + n_pairs)) at elements
+ *     [h * 2 n_pairs, (h + 1) * 2 n_pairs)), then the remaining dims of every
+ *     head (head h: dims [0, 2 pair_begin) and [2 (pair_begin + n_pairs),
+ *     head_dim), in order, at elements n_heads * 2 n_pairs +
+ *     h * (head_dim - 2 n_pairs) ...).  A fixed permutation of a key row's
+ *     elements, which a model absorbs into its key projection; attention
+ *     reads it back per head.  Only the key temporal phase changes in a
+ *     re-index [DeCoPrune page, 무엇과 다른가], so in this layout a re-index
+ *     reads and writes the rows' leading n_heads * 2 n_pairs elements, whole
+ *     128-byte lines, and nothing else.  Requires 2 n_pairs * elem_size to be
+ *     a multiple of 16 bytes (DP_EALIGN otherwise).
+ *   A packed per-head (HS) run of n head rows in this layout holds the n
+ *   temporal blocks, then the n remaining parts.
+ */
+typedef enum { DP_KEY_INTERLEAVED = 0, DP_KEY_SPLIT = 1 } dp_key_layout;
+
 typedef struct {
   int32_t      pair_begin;   /* first temporal pair                              */
   int32_t      n_pairs;      /* pairs in the temporal block, >= 1               */
@@ -237,6 +258,7 @@ typedef struct {
   float        q0;           /* query origin (frames)                            */
   float        knee;         /* offsets <= knee are left unchanged               */
   float        inv_factor;   /* 1/c, the linear compression of older offsets     */
+  int32_t      key_layout;   /* dp_key_layout of the keys the re-index rotates   */
 } dp_rope;
 
 /* Workspace of a re-index (per-frame delta and cos/sin table). */
@@ -328,14 +350,15 @@ dp_status dp_rope_apply(void* const* k_layers, int32_t n_layers, int32_t n_heads
  * dp_rope_shift_workspace_bytes(n_pairs) bytes (the step's {cos, sin} table;
  * calls that share it must be ordered on one stream).  Frame phases are not
  * touched: the caller's dp_rope_prepare of the step advances every frame.
- * Two launches (the table, then the rotation).
+ * key_layout: dp_key_layout of the keys.  Two launches (the table, then the
+ * rotation).
  * ------------------------------------------------------------------------- */
 size_t    dp_rope_shift_workspace_bytes(int32_t n_pairs);
 dp_status dp_rope_shift(void* const* k_layers, int32_t n_layers, int32_t n_heads,
                         int32_t head_dim, int32_t dtype, int64_t row_begin,
                         int64_t rows_capacity, const int64_t* n_rows, const float* theta,
-                        int32_t pair_begin, int32_t n_pairs, float delta, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        int32_t pair_begin, int32_t n_pairs, int32_t key_layout, float delta,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * 4b. Segment-append compaction in place     [DeCoPrune page, 어떻게 동작하나]
@@ -405,6 +428,11 @@ dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t sl
  * dp_hs_rope_reindex: in-place re-index of a ragged K cache laid out as above;
  *   k_capacity is the number of head rows in k_ragged (rows beyond it are
  *   skipped).
+ * Key layout (dp_kv_hs.key_layout, pair_begin, n_pairs; for the re-index the
+ *   rope's): DP_KEY_SPLIT sources are split token rows and each output run
+ *   holds its temporal blocks, then the remaining parts (a run's head rows
+ *   are then not head_dim apart); a fused_rope must name the same layout and
+ *   pairs (DP_EINVAL).  V is packed as plain head rows in either layout.
  * class_idx / class_row_frame are device arrays of n_classes device pointers;
  * class_len is device int64 [n_classes].  n_classes <= DP_HS_MAX_CLASSES.
  *
@@ -430,6 +458,9 @@ typedef struct {
   int64_t src_rows;          /* rows of each source layer                       */
   int64_t out_capacity;      /* head-rows available in k_out / v_out            */
   int32_t* dev_error;        /* device int32 or NULL                            */
+  int32_t key_layout;        /* dp_key_layout of k_src and k_out                */
+  int32_t pair_begin;        /* temporal pairs of the split layout              */
+  int32_t n_pairs;           /*   (ignored for DP_KEY_INTERLEAVED)               */
 } dp_kv_hs;
 
 dp_status dp_hs_offsets(const uint8_t* head_class, int32_t n_layers, int32_t n_heads,
@@ -466,11 +497,15 @@ dp_status dp_hs_rope_reindex(void* k_ragged, int64_t k_capacity, int32_t n_layer
  * aligned, o not overlapping the inputs; 1 <= n_heads <= 65536 (DP_ERANGE);
  * scale > 0 and finite (DP_EINVAL otherwise).  fp32 accumulation and softmax;
  * head_dim 128 and bf16 only (DP_EUNSUPPORTED otherwise).  No mask: every
- * query sees every cached row.  One launch.
+ * query sees every cached row.  key_layout: dp_key_layout of k, with the
+ * temporal pairs [pair_begin, pair_begin + n_pairs) of DP_KEY_SPLIT (ignored
+ * for DP_KEY_INTERLEAVED; checked as for dp_rope_shift); q, v and o are
+ * never permuted.  One launch.
  * ------------------------------------------------------------------------- */
 dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int64_t n_q,
                        int64_t kv_capacity, const int64_t* n_kv, int32_t n_heads,
-                       int32_t head_dim, int32_t dtype, float scale, void* stream);
+                       int32_t head_dim, int32_t dtype, float scale, int32_t key_layout,
+                       int32_t pair_begin, int32_t n_pairs, void* stream);
 
 /* dp_attention_lag: the same attention over a cache whose keys past the knee
  *   are kept on the compressed time axis (dp_rope.axis = DP_AXIS_COMPRESSED)
@@ -490,13 +525,13 @@ dp_status dp_attention(const void* q, const void* k, const void* v, void* o, int
  *   both clamped to n); n_pairs >= 1, pair_begin >= 0 and
  *   2 (pair_begin + n_pairs) <= head_dim (DP_ERANGE); lag finite (DP_EINVAL).
  *   With plain_begin = 0 and plain_end >= n this is dp_attention, bit for bit.
- *   One launch.
+ *   key_layout: as for dp_attention, with the same temporal pairs.  One launch.
  * ------------------------------------------------------------------------- */
 dp_status dp_attention_lag(const void* q, const void* k, const void* v, void* o, int64_t n_q,
                            int64_t kv_capacity, const int64_t* n_kv, int64_t plain_begin,
                            int64_t plain_end, const float* theta, int32_t pair_begin,
                            int32_t n_pairs, float lag, int32_t n_heads, int32_t head_dim,
-                           int32_t dtype, float scale, void* stream);
+                           int32_t dtype, float scale, int32_t key_layout, void* stream);
 
 /* dp_hs_attention: the same attention over the ragged DeCoPrune-HS cache
  *   [DeCoPrune page, 무엇인가 (DeCoPrune-HS: static heads see only the sink
@@ -509,13 +544,18 @@ dp_status dp_attention_lag(const void* q, const void* k, const void* v, void* o,
  *   rows of an optional dense block k_chunk, v_chunk [n_chunk][n_heads][head_dim]
  *   (the chunk's own keys; both NULL for none).  q, o: [n_q][n_heads][head_dim].
  *   bf16, head_dim 128 (DP_EUNSUPPORTED otherwise); scale as for dp_attention;
- *   fp32 accumulation and softmax; a head with no rows gives zeros.  One launch.
+ *   fp32 accumulation and softmax; a head with no rows gives zeros.
+ *   key_layout, pair_begin, n_pairs: as for dp_attention; with DP_KEY_SPLIT
+ *   each run of k_ragged holds its temporal blocks, then its remaining parts
+ *   (as dp_hs_gather_kv writes it), and k_chunk is split token rows.
+ *   One launch.
  * ------------------------------------------------------------------------- */
 dp_status dp_hs_attention(const void* q, const void* k_ragged, const void* v_ragged,
                           int64_t ragged_capacity, const int64_t* offsets, int32_t layer,
                           const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
                           int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
-                          float scale, void* stream);
+                          float scale, int32_t key_layout, int32_t pair_begin, int32_t n_pairs,
+                          void* stream);
 
 /* dp_hs_attention_lag: dp_hs_attention over a ragged cache whose keys past the
  *   knee are on the compressed time axis (see dp_attention_lag)
@@ -527,6 +567,7 @@ dp_status dp_hs_attention(const void* q, const void* k_ragged, const void* v_rag
  *   arguments, layout, limits and errors as for dp_hs_attention; plain_tail >= 0
  *   (DP_ERANGE); theta, pair_begin, n_pairs, lag as for dp_attention_lag.  With
  *   plain_tail >= every run's length this is dp_hs_attention, bit for bit.
+ *   key_layout: as for dp_hs_attention, with the same temporal pairs.
  *   One launch.
  * ------------------------------------------------------------------------- */
 dp_status dp_hs_attention_lag(const void* q, const void* k_ragged, const void* v_ragged,
@@ -534,7 +575,8 @@ dp_status dp_hs_attention_lag(const void* q, const void* k_ragged, const void* v
                               const void* k_chunk, const void* v_chunk, int64_t n_chunk, void* o,
                               int64_t n_q, int32_t n_heads, int32_t head_dim, int32_t dtype,
                               float scale, int64_t plain_tail, const float* theta,
-                              int32_t pair_begin, int32_t n_pairs, float lag, void* stream);
+                              int32_t pair_begin, int32_t n_pairs, float lag, int32_t key_layout,
+                              void* stream);
 
 /* ------------------------------------------------------------------------- *
  * 6. Pruning ratio             [DeCoPrune page, 어떻게 쓰나 and 전제와 한계]

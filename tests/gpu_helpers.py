@@ -56,3 +56,62 @@ def keys_close(got_bits, want_bits, tol):
     worst = float(d.max()) if d.size else 0.0
     exact = int(np.count_nonzero(got_bits != want_bits))
     return worst <= tol, worst, exact
+
+
+# ---------------------------------------------------------------------------
+# Split key layout (DP_KEY_SPLIT): a fixed permutation of a key row's elements,
+# the temporal blocks of all heads first, then every head's other dims.  These
+# helpers only move data; tests compare the library in either layout with the
+# oracle, which works in the natural layout.
+# ---------------------------------------------------------------------------
+def split_perm(H, D, pair_begin, n_pairs):
+    """Index p with split_row = natural_row[p] for a token row of H heads x D."""
+    t = np.arange(2 * pair_begin, 2 * (pair_begin + n_pairs))
+    other = np.concatenate([np.arange(0, 2 * pair_begin), np.arange(2 * (pair_begin + n_pairs), D)])
+    heads = np.arange(H)[:, None] * D
+    return np.concatenate([(heads + t[None, :]).ravel(), (heads + other[None, :]).ravel()])
+
+
+def to_split(k, pair_begin, n_pairs):
+    """[..., H, D] natural -> the same shape holding split rows (numpy or torch)."""
+    H, D = k.shape[-2], k.shape[-1]
+    p = split_perm(H, D, pair_begin, n_pairs)
+    if isinstance(k, torch.Tensor):
+        flat = k.reshape(k.shape[:-2] + (H * D,))
+        return flat.index_select(-1, torch.from_numpy(p).to(k.device)).reshape(k.shape)
+    return np.ascontiguousarray(k.reshape(k.shape[:-2] + (H * D,))[..., p].reshape(k.shape))
+
+
+def from_split(k, pair_begin, n_pairs):
+    """Inverse of to_split."""
+    H, D = k.shape[-2], k.shape[-1]
+    inv = np.argsort(split_perm(H, D, pair_begin, n_pairs))
+    if isinstance(k, torch.Tensor):
+        flat = k.reshape(k.shape[:-2] + (H * D,))
+        return flat.index_select(-1, torch.from_numpy(inv).to(k.device)).reshape(k.shape)
+    return np.ascontiguousarray(k.reshape(k.shape[:-2] + (H * D,))[..., inv].reshape(k.shape))
+
+
+def run_to_split(run, pair_begin, n_pairs):
+    """A packed per-head run [n, D] (natural head rows) -> its split form, the
+    same [n, D] buffer holding the n temporal blocks, then the n other parts."""
+    n, D = run.shape
+    t = slice(2 * pair_begin, 2 * (pair_begin + n_pairs))
+    other = np.concatenate([np.arange(0, 2 * pair_begin), np.arange(2 * (pair_begin + n_pairs), D)])
+    if isinstance(run, torch.Tensor):
+        o = torch.from_numpy(other).to(run.device)
+        return torch.cat([run[:, t].reshape(-1), run.index_select(1, o).reshape(-1)]).reshape(n, D)
+    return np.concatenate([run[:, t].reshape(-1), run[:, other].reshape(-1)]).reshape(n, D)
+
+
+def run_from_split(run, pair_begin, n_pairs):
+    """Inverse of run_to_split."""
+    n, D = run.shape
+    tw = 2 * n_pairs
+    flat = run.reshape(-1)
+    tpart = flat[:n * tw].reshape(n, tw)
+    opart = flat[n * tw:].reshape(n, D - tw)
+    lo = 2 * pair_begin
+    if isinstance(run, torch.Tensor):
+        return torch.cat([opart[:, :lo], tpart, opart[:, lo:]], dim=1)
+    return np.concatenate([opart[:, :lo], tpart, opart[:, lo:]], axis=1)

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert dp.dp_abi_version() == 1
+    assert dp.dp_abi_version() == 2
     assert dp.dp_status_str(dp.DP_OK) == "DP_OK"
     assert dp.dp_status_str(dp.DP_ECAPACITY) == "DP_ECAPACITY"
     assert dp.dp_status_str(dp.DP_ESTALL) == "DP_ESTALL"
@@ -216,6 +216,20 @@ def test_hs_rejects():
     r = _rope()
     assert _status("hs_reindex", FAKE, 100, 2, 4, 64, 1, FAKE, 2, FAKE, caps, FAKE, None,
                    ctypes.byref(r), FAKE, 4096, None) == dp.DP_EINVAL
+    # split keys: the cache's pairs must make whole 16-byte vectors, and a fused
+    # re-index must name the cache's layout and pairs
+    kv.k_out = FAKE
+    kv.key_layout, kv.pair_begin, kv.n_pairs = dp.DP_KEY_SPLIT, 0, 6
+    assert _status("hs_gather", ctypes.byref(kv), FAKE, 2, FAKE, FAKE, caps, FAKE, None, None,
+                   None, 0, None) == dp.DP_EALIGN
+    kv.n_pairs = 8
+    nb = dp.dp_rope_workspace_bytes(10, 8)
+    for rk in (_rope(), _rope(key_layout=dp.DP_KEY_SPLIT, n_pairs=4)):
+        assert _status("hs_gather", ctypes.byref(kv), FAKE, 2, FAKE, FAKE, caps, FAKE, FAKE,
+                       ctypes.byref(rk), FAKE, nb, None) == dp.DP_EINVAL
+    kv.key_layout = 5
+    assert _status("hs_gather", ctypes.byref(kv), FAKE, 2, FAKE, FAKE, caps, FAKE, None, None,
+                   None, 0, None) == dp.DP_EINVAL
 
 
 def test_pruning_ratio_counter():
@@ -281,8 +295,8 @@ def test_append_kept_fused_rope_and_shift_reject():
                    FAKE, 8, None) == dp.DP_EINVAL
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("k", FAKE), ("L", 2), ("H", 4), ("D", 64), ("dt", dp.DP_BF16), ("rb", 0), ("cap", 1000),
-        ("n", None), ("theta", FAKE), ("pb", 0), ("np", 12), ("delta", 3.5), ("ws", FAKE),
-        ("wsb", 4096), ("s", None))]
+        ("n", None), ("theta", FAKE), ("pb", 0), ("np", 12), ("kl", 0), ("delta", 3.5),
+        ("ws", FAKE), ("wsb", 4096), ("s", None))]
     assert _status("rope_shift", *args(theta=None)) == dp.DP_EINVAL
     assert _status("rope_shift", *args(np=0)) == dp.DP_EINVAL
     assert _status("rope_shift", *args(np=40)) == dp.DP_ERANGE            # past head_dim/2
@@ -297,6 +311,10 @@ def test_append_kept_fused_rope_and_shift_reject():
     assert _status("rope_shift", *args(ws=FAKE + 8)) == dp.DP_EALIGN
     assert dp.dp_rope_shift_workspace_bytes(44) == (44 + 4) * 8
     assert _status("rope_shift", *args(cap=0)) == dp.DP_OK                 # empty range: nothing
+    # split keys: the temporal block must be whole 16-byte vectors (bf16: pairs in fours)
+    assert _status("rope_shift", *args(kl=dp.DP_KEY_SPLIT, np=10)) == dp.DP_EALIGN
+    assert _status("rope_shift", *args(kl=dp.DP_KEY_SPLIT, np=12, cap=0)) == dp.DP_OK
+    assert _status("rope_shift", *args(kl=2)) == dp.DP_EINVAL
 
 
 def test_rope_prepare_and_apply_reject():
@@ -318,7 +336,8 @@ def test_attention_rejects():
     B = dp.DP_BF16
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("q", FAKE), ("k", FAKE), ("v", FAKE), ("o", FAKE), ("n_q", 100), ("cap", 100),
-        ("n_kv", None), ("H", 8), ("D", 128), ("dtype", B), ("scale", 0.1), ("s", None))]
+        ("n_kv", None), ("H", 8), ("D", 128), ("dtype", B), ("scale", 0.1), ("kl", 0), ("p0", 0),
+        ("np", 0), ("s", None))]
     assert _status("attention", *args(q=None)) == dp.DP_EINVAL
     assert _status("attention", *args(D=64)) == dp.DP_EUNSUPPORTED
     assert _status("attention", *args(dtype=dp.DP_F32)) == dp.DP_EUNSUPPORTED
@@ -330,6 +349,12 @@ def test_attention_rejects():
     assert _status("attention", *args(n_kv=FAKE + 4)) == dp.DP_EALIGN
     for bad in (float("nan"), 0.0, -0.5, float("inf")):
         assert _status("attention", *args(scale=bad)) == dp.DP_EINVAL
+    # split keys: a temporal block of whole 16-byte vectors within the head
+    assert _status("attention", *args(kl=dp.DP_KEY_SPLIT, np=0)) == dp.DP_ERANGE
+    assert _status("attention", *args(kl=dp.DP_KEY_SPLIT, np=44, p0=24)) == dp.DP_ERANGE
+    assert _status("attention", *args(kl=dp.DP_KEY_SPLIT, np=42)) == dp.DP_EALIGN
+    assert _status("attention", *args(kl=dp.DP_KEY_SPLIT, np=44, p0=2)) == dp.DP_EALIGN
+    assert _status("attention", *args(kl=7)) == dp.DP_EINVAL
 
 
 def test_attention_lag_rejects():
@@ -337,7 +362,7 @@ def test_attention_lag_rejects():
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("q", FAKE), ("k", FAKE), ("v", FAKE), ("o", FAKE), ("n_q", 100), ("cap", 100),
         ("n_kv", None), ("pb", 10), ("pe", 40), ("theta", FAKE), ("p0", 0), ("np", 44),
-        ("lag", 12.5), ("H", 8), ("D", 128), ("dtype", B), ("scale", 0.1), ("s", None))]
+        ("lag", 12.5), ("H", 8), ("D", 128), ("dtype", B), ("scale", 0.1), ("kl", 0), ("s", None))]
     f = lambda **kw: _status("attention_lag", *args(**kw))
     assert f(theta=None) == dp.DP_EINVAL
     assert f(o=None) == dp.DP_EINVAL
@@ -357,6 +382,7 @@ def test_attention_lag_rejects():
         assert f(scale=bad) == dp.DP_EINVAL
     for bad in (float("nan"), float("inf"), -float("inf")):
         assert f(lag=bad) == dp.DP_EINVAL
+    assert f(kl=dp.DP_KEY_SPLIT, np=42) == dp.DP_EALIGN
 
 
 def test_hs_attention_rejects():
@@ -364,7 +390,7 @@ def test_hs_attention_rejects():
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("q", FAKE), ("kr", FAKE), ("vr", FAKE), ("cap", 1000), ("off", FAKE), ("layer", 3),
         ("kc", FAKE), ("vc", FAKE), ("nc", 50), ("o", FAKE), ("n_q", 100), ("H", 8), ("D", 128),
-        ("dtype", B), ("scale", 0.1), ("s", None))]
+        ("dtype", B), ("scale", 0.1), ("kl", 0), ("p0", 0), ("np", 0), ("s", None))]
     assert _status("hs_attention", *args(off=None)) == dp.DP_EINVAL
     assert _status("hs_attention", *args(vc=None)) == dp.DP_EINVAL       # chunk K without V
     assert _status("hs_attention", *args(D=96)) == dp.DP_EUNSUPPORTED
@@ -377,6 +403,7 @@ def test_hs_attention_rejects():
     assert _status("hs_attention", *args(kc=FAKE + 2)) == dp.DP_EALIGN
     for bad in (float("nan"), 0.0, -0.5, float("inf")):
         assert _status("hs_attention", *args(scale=bad)) == dp.DP_EINVAL
+    assert _status("hs_attention", *args(kl=dp.DP_KEY_SPLIT, np=6)) == dp.DP_EALIGN
 
 
 def test_hs_attention_lag_rejects():
@@ -385,7 +412,7 @@ def test_hs_attention_lag_rejects():
         ("q", FAKE), ("kr", FAKE), ("vr", FAKE), ("cap", 1000), ("off", FAKE), ("layer", 3),
         ("kc", FAKE), ("vc", FAKE), ("nc", 50), ("o", FAKE), ("n_q", 100), ("H", 8), ("D", 128),
         ("dtype", B), ("scale", 0.1), ("tail", 30), ("theta", FAKE), ("p0", 0), ("np", 44),
-        ("lag", 2.5), ("s", None))]
+        ("lag", 2.5), ("kl", 0), ("s", None))]
     f = lambda **kw: _status("hs_attention_lag", *args(**kw))
     assert f(theta=None) == dp.DP_EINVAL
     assert f(off=None) == dp.DP_EINVAL
@@ -400,6 +427,7 @@ def test_hs_attention_lag_rejects():
     for bad in (float("nan"), float("inf")):
         assert f(lag=bad) == dp.DP_EINVAL
     assert f(scale=0.0) == dp.DP_EINVAL
+    assert f(kl=dp.DP_KEY_SPLIT, p0=2) == dp.DP_EALIGN
 
 
 def test_score_index_rejects():

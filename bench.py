@@ -44,12 +44,25 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s (10^9 B/s)
+KEY_LAYOUT = 1                 # of the workload being set up (layout_for)
+
+
+def make_rope(*args, **kw):
+    """dp.make_rope for keys in this run's layout (--key-layout)."""
+    import compaction_dp_score_amd as dp
+    return dp.make_rope(*args, key_layout=KEY_LAYOUT, **kw)
+
+
+def attn_layout(w):
+    """Key-layout arguments of the attention calls (the workload's temporal pairs)."""
+    return dict(key_layout=KEY_LAYOUT, pair_begin=0, n_pairs=w.rope_pairs)
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_BYTES = 8 << 30          # size of the calibration copy run in every bench process
 
 # dominant kernel of each workload: (rocprof name prefix, sources it is built from)
 KERNELS = {
     "eviction": ("gather_kernel", ("gather.hip", "dp_device.h")),
+    "tiny": ("gather_kernel", ("gather.hip", "dp_device.h")),
     "prefix": ("gather_kernel", ("gather.hip", "dp_device.h")),
     "reindex": ("reindex_kernel", ("rope.hip", "dp_device.h")),
     "hs": ("hs_gather_kernel", ("hs.hip", "dp_device.h")),
@@ -72,15 +85,23 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="eviction",
+    ap.add_argument("--workload", default=None,
+                    help="one workload; without it the eviction step is the headline record and "
+                         "the tiny, one-minute re-index, both prefix slabs and HS workloads follow "
+                         "under configs",
                     choices=["eviction", "reindex", "prefix", "hs", "append", "attention",
                              "hs_attention", "steady", "steady_lazy", "attention_lag", "hs_ring"])
+    ap.add_argument("--key-layout", default=None, choices=["split", "interleaved"],
+                    help="layout of the key rows: split (the temporal blocks of all heads first; "
+                         "the re-index writes whole lines) or interleaved ([heads][head_dim]); "
+                         "by default split, but interleaved packed runs for the HS workload "
+                         "(its gather is fastest so; the split-run figures go to its context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullkv", action="store_true",
                     help="skip the context timings that launch the dominant kernel outside the "
                          "timed steps (attention over the uncompacted cache, the page-axis "
                          "steady step): profiling runs, so that every dispatch is a timed one")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--summarize-stats", metavar="STATS_DIR",
                     help="write the kernel-statistics summary of --workload from a rocprofv3 "
@@ -186,18 +207,22 @@ def index_compare(step, x0d, xfd, d, reps=20):
     return out
 
 
-def setup_eviction(dev):
+def setup_eviction(dev, name="eviction"):
+    """The eviction step (or, name "tiny", the tiny workload's step: 1 layer, 2
+    heads x 64 fp32, 8 chunks of 64 rows, chunks 1-5 scored)."""
     import compaction_dp_score_amd as dp
     import dpsynth
     from compaction_dp_score_amd.step import PruneStep
-    w = dpsynth.WORKLOADS["eviction"]
+    w = dpsynth.WORKLOADS[name]
     T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    esz = w.elem_size
     k_src, v_src, k_dst, v_dst = [], [], [], []
     for l in range(L):
-        k = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
-        v = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
-        dpsynth.kv_fill_device(k, "bf16", w.seed, dpsynth.STREAM_K, l, T, H * D)
-        dpsynth.kv_fill_device(v, "bf16", w.seed, dpsynth.STREAM_V, l, T, H * D)
+        k = torch.empty((T, H, D), dtype=tdt, device=dev)
+        v = torch.empty((T, H, D), dtype=tdt, device=dev)
+        dpsynth.kv_fill_device(k, w.dtype, w.seed, dpsynth.STREAM_K, l, T, H * D)
+        dpsynth.kv_fill_device(v, w.dtype, w.seed, dpsynth.STREAM_V, l, T, H * D)
         k_src.append(k)
         v_src.append(v)
         k_dst.append(torch.empty_like(k))
@@ -207,7 +232,7 @@ def setup_eviction(dev):
     ft, fp = dpsynth.frame_tables(w)
     rope = dict(theta=torch.from_numpy(theta).to(dev), frame_t=torch.from_numpy(ft).to(dev),
                 frame_phase=torch.from_numpy(fp).to(dev), q0=w.q0, knee=w.rope_knee,
-                inv_factor=1.0 / w.rope_factor)
+                inv_factor=1.0 / w.rope_factor, key_layout=KEY_LAYOUT)
     phase0 = rope["frame_phase"].clone()
     step = PruneStep(k_src=k_src, v_src=v_src, k_dst=k_dst, v_dst=v_dst, seq_len=T,
                      sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
@@ -235,14 +260,14 @@ def setup_eviction(dev):
     def accounting():
         n = int(step.n_kept.item())
         assert int(step.dev_error.item()) == 0
-        row = H * D * 2
+        row = H * D * esz
         gather = n * row * 2 * 2 * L
         index = w.n_scored * (8 * w.d) + T + 12 * n        # scores in, keep out, idx + frames
         return dict(n_kept=n, gather_bytes=gather, score_timer=st, index_bytes=index,
                     index_compare=index_compare(step, x0d, xfd, w.d),
                     step_bytes=gather + index, n_scored=w.n_scored,
-                    config={"workload": "eviction", "layers": L, "heads": H, "head_dim": D,
-                            "kv_dtype": "bf16", "tokens": T, "chunk_tokens": w.chunk_tokens,
+                    config={"workload": name, "layers": L, "heads": H, "head_dim": D,
+                            "kv_dtype": w.dtype, "tokens": T, "chunk_tokens": w.chunk_tokens,
                             "sink_chunks": w.sink_chunks, "window_chunks": w.window_chunks,
                             "scored_tokens": w.n_scored, "d": w.d, "gamma": w.gamma,
                             "rope_pairs": w.rope_pairs, "rope_knee_frames": w.rope_knee,
@@ -250,58 +275,254 @@ def setup_eviction(dev):
                             "pr_step": 1 - n / T})
 
     def cpu_baseline(seconds):
+        if name == "tiny":
+            return cpu_baseline_tiny(w, seconds)
         return cpu_baseline_eviction(w, x0, xf, theta, ft, fp, seconds)
 
     return run, gt, accounting, cpu_baseline
 
 
+def host_info():
+    """The host the CPU legs run on: CPU model, available memory, the cores
+    this process may run on, and the OpenMP threads the oracle gets."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    mem = None
+    try:
+        with open("/proc/meminfo") as f:
+            mem = next(int(l.split()[1]) for l in f if l.startswith("MemAvailable")) / 1e6
+    except (OSError, StopIteration):
+        pass
+    cores = len(os.sched_getaffinity(0))
+    omp = int(os.environ.get("OMP_NUM_THREADS") or cores)
+    return {"cpu_model": model, "mem_available_gb": None if mem is None else round(mem, 1),
+            "affinity_cores": cores, "omp_threads": omp}
+
+
+def _timed(fn):
+    t0 = time.perf_counter()
+    out = fn()
+    return out, time.perf_counter() - t0
+
+
+def _tiled_layers(n_layers, rows, row_elems, seed, tile_rows=512):
+    """Host key/value stand-ins: one random bf16 tile repeated over the rows
+    (the oracle's work does not depend on the values)."""
+    rng = np.random.default_rng(seed)
+    tile = rng.integers(0, 1 << 16, (tile_rows, row_elems), dtype=np.uint16) & np.uint16(0xBFFF)
+    out = np.empty((n_layers, rows, row_elems), np.uint16)
+    for l in range(n_layers):
+        for r0 in range(0, rows, tile_rows):
+            n = min(tile_rows, rows - r0)
+            out[l, r0:r0 + n] = tile[:n]
+    return out
+
+
+def _cpu_record(step_bytes, total_s, threads, sample, steps, extra=None):
+    rec = {"value": step_bytes / total_s / 1e9, "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "sample": sample, "step_seconds": total_s,
+           "step_seconds_by_step": {k: round(v, 6) for k, v in steps.items()}}
+    rec.update(host_info())
+    if extra:
+        rec.update(extra)
+    return rec
+
+
 def cpu_baseline_eviction(w, x0, xf, theta, ft, fp, seconds):
     """Oracle (as it is) on a layer sample of the eviction step: score, mask
-    and index once, then gather of K and V plus the K re-index on as many
-    layers as fit the time budget; scaled to 40 layers."""
+    and index once, then gather of K and V and the K re-index on as many
+    layers as fit the time budget (the gather's parallel loop is over layers,
+    so as many layers at a time as the oracle has threads); scaled to 40
+    layers."""
     import dpsynth
     import oracle
     T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
-    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-    tile_rows = 624                                  # 1/50 of the cache, tiled over the layer
-    tile = dpsynth.kv_rows_host("bf16", w.seed, dpsynth.STREAM_K, 0, np.arange(tile_rows), T, H * D)
+    omp = host_info()["omp_threads"]
     rf = dpsynth.row_frame(w)
-    tables_in = (ft, fp)
-    t0 = time.perf_counter()
-    ell = oracle.score_f32(x0, xf, w.d)
-    keep = oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin, w.n_scored, w.gamma)
-    idx = oracle.compact(keep)
-    rf2 = oracle.gather_i32(rf, idx)
-    tables = oracle.rope_frames(tables_in[0], tables_in[1], w.q0, w.rope_knee,
-                                np.float32(1.0 / w.rope_factor), theta)
-    t_once = time.perf_counter() - t0
-    n_layers = max(1, min(L, cores))              # the gather runs one thread per layer
-    src = np.empty((n_layers, T, H, D), np.uint16)
-    for l in range(n_layers):
-        src[l].reshape(T // tile_rows, tile_rows, H * D)[:] = tile[None]
-    per_layer = []
+    ell, t_score = _timed(lambda: oracle.score_f32(x0, xf, w.d))
+    keep, t_mask = _timed(lambda: oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin,
+                                              w.n_scored, w.gamma))
+    (idx, rf2), t_index = _timed(lambda: (lambda i: (i, oracle.gather_i32(rf, i)))(
+        oracle.compact(keep)))
+    tables, t_tab = _timed(lambda: oracle.rope_frames(ft, fp, w.q0, w.rope_knee,
+                                                      np.float32(1.0 / w.rope_factor), theta))
+    n_layers = max(1, min(L, omp))
+    src = _tiled_layers(n_layers, T, H * D, 1).reshape(n_layers, T, H, D)
+    g_times, r_times = [], []
     done = 0
     t_start = time.perf_counter()
     while done < L:
-        t1 = time.perf_counter()
-        kd = oracle.gather(src, idx)                 # K of n_layers layers
-        vd = oracle.gather(src, idx)                 # V
-        for l in range(n_layers):
-            oracle.rope_rows(kd[l], rf2, 0, tables)
-        per_layer.append((time.perf_counter() - t1) / n_layers)
+        (kd, vd), tg = _timed(lambda: (oracle.gather(src, idx), oracle.gather(src, idx)))
+        _, tr = _timed(lambda: [oracle.rope_rows(kd[l], rf2, 0, tables) for l in range(n_layers)])
+        g_times.append(tg / n_layers)
+        r_times.append(tr / n_layers)
         done += n_layers
         del kd, vd
         if time.perf_counter() - t_start > seconds:
             break
-    t_layer = float(np.median(per_layer))
-    total = t_once + L * t_layer
+    steps = {"score": t_score, "mask": t_mask, "index": t_index,
+             "gather": L * float(np.median(g_times)),
+             "reindex": t_tab + L * float(np.median(r_times))}
+    total = sum(steps.values())
     n = idx.shape[0]
     step_bytes = n * H * D * 2 * 2 * 2 * L + w.n_scored * 8 * w.d + T + 2 * T + 12 * n
-    return {"value": step_bytes / total / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "score+mask+index of the full step once, then gather of K and V plus "
-                      "the K re-index on %d layers at a time (%d layer passes timed, median); "
-                      "time scaled to 40 layers: %.2f s per step" % (n_layers, done, total),
-            "step_seconds": total, "tokens_scored_per_s": w.n_scored / total}
+    return _cpu_record(step_bytes, total, omp,
+                       "score, mask and index of the full step once; gather of K and V and the "
+                       "K re-index on %d layers at a time (%d layer passes timed, median), scaled "
+                       "to 40 layers" % (n_layers, done), steps,
+                       {"tokens_scored_per_s": w.n_scored / total})
+
+
+def cpu_baseline_reindex(w, rows, rf_kept, moved_rows, seconds):
+    """Oracle re-index (per-frame tables, then every retained row of a layer)
+    on single layers of the one-minute cache until the time budget, scaled to
+    40 layers (the row loop is the parallel one)."""
+    import oracle
+    H, D, L = w.n_heads, w.head_dim, w.n_layers
+    omp = host_info()["omp_threads"]
+    theta = __import__("dpsynth").rope_theta(w.rope_pairs, w.rope_base)
+    ft = np.arange(w.n_frames, dtype=np.float32)
+    tables, t_tab = _timed(lambda: oracle.rope_frames(ft, ft, w.q0, w.rope_knee,
+                                                      np.float32(1.0 / w.rope_factor), theta))
+    src = _tiled_layers(1, rows, H * D, 2).reshape(rows, H, D)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < L:
+        k = src.copy()
+        _, tr = _timed(lambda: oracle.rope_rows(k, rf_kept, 0, tables))
+        times.append(tr)
+        if time.perf_counter() - t_start > seconds:
+            break
+    steps = {"reindex": t_tab + L * float(np.median(times))}
+    total = steps["reindex"]
+    b = moved_rows * H * (2 * w.rope_pairs * 2) * 2 * L
+    return _cpu_record(b, total, omp, "the K re-index of %d of 40 layers (%d retained rows each), "
+                       "median per layer, scaled to 40 layers" % (len(times), rows), steps)
+
+
+def cpu_baseline_prefix(w, x0, xf, slab_layers, seconds):
+    """Oracle prefix pruning: score, mask and index of all 355,680 scored
+    rows once; the K and V gather timed on a row sample (the first 1/16 of the
+    rows and their kept rows, as many layers at a time as the oracle has
+    threads), scaled by kept rows to the slab's 20 layers."""
+    import oracle
+    T, H, D = w.seq_len, w.n_heads, w.head_dim
+    omp = host_info()["omp_threads"]
+    ell, t_score = _timed(lambda: oracle.score_f32(x0, xf, w.d))
+    keep, t_mask = _timed(lambda: oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin,
+                                              w.n_scored, w.gamma))
+    idx, t_index = _timed(lambda: oracle.compact(keep))
+    ts = T // 16
+    sub = idx[idx < ts]
+    n_layers = max(1, min(slab_layers, omp))
+    src = _tiled_layers(n_layers, ts, H * D, 3).reshape(n_layers, ts, H, D)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        _, tg = _timed(lambda: (oracle.gather(src, sub), oracle.gather(src, sub)))
+        times.append(tg / n_layers / sub.shape[0])            # seconds per kept row and layer
+        if time.perf_counter() - t_start > seconds or len(times) >= 8:
+            break
+    n = idx.shape[0]
+    steps = {"score": t_score, "mask": t_mask, "index": t_index,
+             "gather": float(np.median(times)) * n * slab_layers}
+    total = sum(steps.values())
+    step_bytes = n * H * D * 2 * 2 * 2 * slab_layers + w.n_scored * 8 * w.d + T + 4 * n
+    return _cpu_record(step_bytes, total, omp,
+                       "score, mask and index of the full prefix once; the K and V gather of the "
+                       "%d kept rows among the first %d rows, %d layers at a time (%d passes, "
+                       "median per kept row), scaled to %d kept rows x %d layers"
+                       % (sub.shape[0], ts, n_layers, len(times), n, slab_layers), steps,
+                       {"tokens_scored_per_s": w.n_scored / total})
+
+
+def cpu_baseline_hs(w, x0, xf, cls, seconds):
+    """Oracle DeCoPrune-HS step: score, both class masks and index lists and
+    the per-head offsets of the full workload once; the per-head gather of K
+    and V and the per-head K re-index timed on one layer restricted to the
+    first 1/8 of the rows, scaled by head rows to 40 layers."""
+    import dpsynth
+    import oracle
+    T, H, D, L = w.seq_len, w.n_heads, w.head_dim, w.n_layers
+    omp = host_info()["omp_threads"]
+    ell, t_score = _timed(lambda: oracle.score_f32(x0, xf, w.d))
+
+    def masks():
+        return (oracle.mask(None, T, w.sink_len, w.window_len, w.scored_begin, w.n_scored,
+                            w.gamma, streaming=True),
+                oracle.mask(ell, T, w.sink_len, w.window_len, w.scored_begin, w.n_scored, w.gamma))
+    (ks, kd), t_mask = _timed(masks)
+    (lists, off), t_index = _timed(lambda: (lambda ls: (ls, oracle.hs_offsets(
+        cls, np.array([len(x) for x in ls], np.int64))))([oracle.compact(ks), oracle.compact(kd)]))
+    rf = dpsynth.row_frame(w)
+    theta = dpsynth.rope_theta(w.rope_pairs, w.rope_base)
+    ft = np.arange(w.n_frames, dtype=np.float32)
+    tables = oracle.rope_frames(ft, ft, w.q0, w.rope_knee, np.float32(1.0 / w.rope_factor), theta)
+    ts = T // 8
+    sub_lists = [x[x < ts] for x in lists]
+    sub_lens = np.array([len(x) for x in sub_lists], np.int64)
+    sub_off = oracle.hs_offsets(cls[:1], sub_lens)
+    src = _tiled_layers(1, ts, H * D, 4).reshape(ts, H, D)
+    frames = np.concatenate([rf[sub_lists[c]] for c in cls[0]]).astype(np.int32)
+    g_times, r_times = [], []
+    t_start = time.perf_counter()
+    while True:
+        out_k = np.empty((int(sub_off[-1]), D), np.uint16)
+        out_v = np.empty_like(out_k)
+        _, tg = _timed(lambda: (oracle.hs_gather_layer(src, 0, cls[:1], sub_lists, sub_off, out_k),
+                                oracle.hs_gather_layer(src, 0, cls[:1], sub_lists, sub_off, out_v)))
+        _, tr = _timed(lambda: oracle.rope_headrows(out_k, frames, 0, tables))
+        g_times.append(tg / sub_off[-1])
+        r_times.append(tr / sub_off[-1])
+        if time.perf_counter() - t_start > seconds or len(g_times) >= 8:
+            break
+    total_rows = int(off[-1])
+    steps = {"score": t_score, "mask": t_mask, "index": t_index,
+             "gather": float(np.median(g_times)) * total_rows,
+             "reindex": float(np.median(r_times)) * total_rows}
+    total = sum(steps.values())
+    step_bytes = total_rows * D * 2 * 2 * 2 + w.n_scored * 8 * w.d + 2 * T
+    return _cpu_record(step_bytes, total, omp,
+                       "score, masks, index lists and offsets of the full step once; the per-head "
+                       "gather of K and V and the K re-index of layer 0 over the first %d rows "
+                       "(%d head rows; %d passes, median per head row), scaled to %d head rows"
+                       % (ts, int(sub_off[-1]), len(g_times), total_rows), steps,
+                       {"tokens_scored_per_s": w.n_scored / total})
+
+
+def cpu_baseline_tiny(w, seconds):
+    """The whole tiny step through the oracle (prune_step), repeated for about
+    a second; median step time."""
+    import dpsynth
+    import oracle
+    T, H, D = w.seq_len, w.n_heads, w.head_dim
+    x0, xf = dpsynth.score_inputs(w)
+    kh = dpsynth.kv_layer_host("f32", w.seed, dpsynth.STREAM_K, 0, T, H * D).reshape(1, T, H, D)
+    vh = dpsynth.kv_layer_host("f32", w.seed, dpsynth.STREAM_V, 0, T, H * D).reshape(1, T, H, D)
+    rf = dpsynth.row_frame(w)
+    theta = dpsynth.rope_theta(w.rope_pairs, w.rope_base)
+    ft, fp = dpsynth.frame_tables(w)
+    pol = dict(seq_len=T, sink_len=w.sink_len, window_len=w.window_len,
+               scored_begin=w.scored_begin, n_scored=w.n_scored, gamma=w.gamma)
+    rope = dict(theta=theta, frame_t=ft, frame_phase=fp, q0=w.q0, knee=w.rope_knee,
+                inv_factor=np.float32(1.0 / w.rope_factor))
+    times = []
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < min(seconds, 1.0) or len(times) < 3:
+        out, t = _timed(lambda: oracle.prune_step(x0, xf, w.d, pol, kh, vh, rf, rope))
+        times.append(t)
+    n = out["idx"].shape[0]
+    total = float(np.median(times))
+    step_bytes = n * H * D * 4 * 2 * 2 + w.n_scored * 8 * w.d + T + 12 * n
+    return _cpu_record(step_bytes, total, host_info()["omp_threads"],
+                       "the whole step (score, mask, index, gather of K "
+                       "and V, K re-index) on the tiny workload, %d repetitions, median"
+                       % len(times), {"step": total},
+                       {"tokens_scored_per_s": w.n_scored / total})
 
 
 def setup_reindex(dev):
@@ -324,7 +545,7 @@ def setup_reindex(dev):
     ft, fp = dpsynth.frame_tables(w)
     ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(fp).to(dev)
     phase0 = fpd.clone()
-    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    rope = make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
     ws = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                      dtype=torch.float32, device=dev)
     gt = Timer()
@@ -343,9 +564,35 @@ def setup_reindex(dev):
         return dict(n_kept=rows, gather_bytes=b, step_bytes=b, n_scored=0,
                     config={"workload": "reindex", "layers": L, "heads": H, "head_dim": D,
                             "kv_dtype": "bf16", "retained_rows": rows, "reindexed_rows": moved_rows,
-                            "rope_pairs": w.rope_pairs, "q0": w.q0})
+                            "rope_pairs": w.rope_pairs, "q0": w.q0,
+                            "key_layout": "split" if KEY_LAYOUT else "interleaved"},
+                    context=None if ARGS.no_fullkv else other_layout_ms())
 
-    return run, gt, accounting, None
+    def other_layout_ms(reps=3):
+        # the same pass on the other key layout (the same bytes of keys, read as
+        # that layout), phase table restored before each call
+        other = 1 - KEY_LAYOUT
+        rope_o = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
+                              key_layout=other)
+        ms = []
+        for _ in range(reps + 1):
+            fpd.copy_(phase0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dp.dp_rope_reindex(arr, L, H, D, dp.DP_BF16, rows, None, rf, rope_o, ws)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        fpd.copy_(phase0)
+        t = float(np.median(ms[1:]))
+        b = moved_rows * H * (2 * w.rope_pairs * 2) * 2 * L
+        return {"other_layout": "split" if other else "interleaved", "ms": round(t, 4),
+                "gbs": round(b / t / 1e6, 1)}
+
+    def cpu_baseline(seconds):
+        return cpu_baseline_reindex(w, rows, rf_full[kept].astype(np.int32), moved_rows, seconds)
+
+    return run, gt, accounting, cpu_baseline
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
@@ -509,7 +756,7 @@ def setup_append(dev):
     ft, fp = dpsynth.frame_tables(w)
     ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(fp).to(dev)
     phase0 = fpd.clone()
-    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    rope = make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
     ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
     gt = Timer()
@@ -606,10 +853,10 @@ def setup_steady(dev):
     ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
     # the phases the old keys carry after the previous step (q0 = 236)
-    dp.dp_rope_prepare(dp.make_rope(theta, ftd, fpd, w.q0 - 4, w.rope_knee, 1.0 / w.rope_factor),
+    dp.dp_rope_prepare(make_rope(theta, ftd, fpd, w.q0 - 4, w.rope_knee, 1.0 / w.rope_factor),
                        D, dp.DP_BF16, ws_r)
     phase0 = fpd.clone()
-    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    rope = make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
     step_frames = 4 * (1.0 - 1.0 / w.rope_factor)                 # 3.5
     ws_s = torch.empty(dp.dp_rope_shift_workspace_bytes(w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
@@ -627,9 +874,9 @@ def setup_steady(dev):
         if timed:
             gt.start()
         dp.dp_rope_shift(arr_k, L, H, D, dp.DP_BF16, 0, C, None, theta, 0, w.rope_pairs,
-                         step_frames, ws_s)
+                         step_frames, ws_s, key_layout=KEY_LAYOUT)
         dp.dp_rope_shift(arr_k, L, H, D, dp.DP_BF16, hb, cap, tail, theta, 0, w.rope_pairs,
-                         step_frames, ws_s)
+                         step_frames, ws_s, key_layout=KEY_LAYOUT)
         if timed:
             gt.stop()
         dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
@@ -724,12 +971,12 @@ def setup_steady_lazy(dev):
     ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
     # the phases after the previous step (q0 = 236) on the compressed axis
-    dp.dp_rope_prepare(dp.make_rope(theta, ftd, fpd, w.q0 - 4, w.rope_knee, 1.0 / w.rope_factor,
+    dp.dp_rope_prepare(make_rope(theta, ftd, fpd, w.q0 - 4, w.rope_knee, 1.0 / w.rope_factor,
                                     axis=dp.DP_AXIS_COMPRESSED), D, dp.DP_BF16, ws_r)
     phase0 = fpd.clone()
-    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
+    rope = make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
                         axis=dp.DP_AXIS_COMPRESSED)
-    page_rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    page_rope = make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
     step_frames = 4 * (1.0 - 1.0 / w.rope_factor)                 # 3.5
     ws_s = torch.empty(dp.dp_rope_shift_workspace_bytes(w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
@@ -757,9 +1004,9 @@ def setup_steady_lazy(dev):
             dp.dp_score_index(x0d, xfd, w.d, w.d, pol, None, keep, idx, nk, None, None, ws_si,
                               err)
             dp.dp_rope_shift(arr_k, L, H, D, dp.DP_BF16, 0, C, None, theta, 0, w.rope_pairs,
-                             step_frames, ws_s)
+                             step_frames, ws_s, key_layout=KEY_LAYOUT)
             dp.dp_rope_shift(arr_k, L, H, D, dp.DP_BF16, hb, cap, tail, theta, 0, w.rope_pairs,
-                             step_frames, ws_s)
+                             step_frames, ws_s, key_layout=KEY_LAYOUT)
             dp.dp_rope_prepare(page_rope, D, dp.DP_BF16, ws_r)
             dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf, page_rope, ws_r)
         once()
@@ -856,12 +1103,12 @@ def setup_hs_ring(dev):
     ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
     # the phases after the previous step (q0 = 116) on the compressed axis
-    dp.dp_rope_prepare(dp.make_rope(theta, ftd, fpd, w.q0 - 4, w.rope_knee, 1.0 / w.rope_factor,
+    dp.dp_rope_prepare(make_rope(theta, ftd, fpd, w.q0 - 4, w.rope_knee, 1.0 / w.rope_factor,
                                     axis=dp.DP_AXIS_COMPRESSED), D, dp.DP_BF16, ws_r)
     phase0 = fpd.clone()
-    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
+    rope = make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
                         axis=dp.DP_AXIS_COMPRESSED)
-    page_rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    page_rope = make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
     step_frames = 4 * (1.0 - 1.0 / w.rope_factor)                 # 3.5
     ws_s = torch.empty(dp.dp_rope_shift_workspace_bytes(w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
@@ -892,9 +1139,9 @@ def setup_hs_ring(dev):
                               err)
             for arr in (arr_ks, arr_k):                            # both sinks
                 dp.dp_rope_shift(arr, L, HC, D, dp.DP_BF16, 0, C, None, theta, 0, w.rope_pairs,
-                                 step_frames, ws_s)
+                                 step_frames, ws_s, key_layout=KEY_LAYOUT)
             dp.dp_rope_shift(arr_k, L, HC, D, dp.DP_BF16, hb, cap, tail, theta, 0, w.rope_pairs,
-                             step_frames, ws_s)                    # dynamic history
+                             step_frames, ws_s, key_layout=KEY_LAYOUT)                    # dynamic history
             dp.dp_rope_prepare(page_rope, D, dp.DP_BF16, ws_r)
             dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf, page_rope, ws_r)
             rf_s[slot_begin:slot_begin + C].fill_(-1)
@@ -950,7 +1197,7 @@ def setup_attention_lag(dev, layers=4):
     n_frames = w.n_frames + w.frames_per_chunk           # through the chunk's own frames
     ft = np.arange(n_frames, dtype=np.float32)
     ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(ft.copy()).to(dev)
-    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
+    rope = make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
                         axis=dp.DP_AXIS_COMPRESSED)
     ws_r = torch.empty(dp.dp_rope_workspace_bytes(n_frames, w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
@@ -965,7 +1212,7 @@ def setup_attention_lag(dev, layers=4):
 
     def launch(l):
         dp.dp_attention_lag(q, ks[l], vs[l], o, C, n, None, plain_begin, plain_end, theta, 0,
-                            w.rope_pairs, lag, H, D, dp.DP_BF16, scale)
+                            w.rope_pairs, lag, H, D, dp.DP_BF16, scale, key_layout=KEY_LAYOUT)
 
     def run(timed):
         for l in range(layers):
@@ -976,11 +1223,11 @@ def setup_attention_lag(dev, layers=4):
                 gt.stop()
 
     def dense_ms(reps=3):
-        dp.dp_attention(q, ks[0], vs[0], o, C, n, None, H, D, dp.DP_BF16, scale)
+        dp.dp_attention(q, ks[0], vs[0], o, C, n, None, H, D, dp.DP_BF16, scale, **attn_layout(w))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
-            dp.dp_attention(q, ks[0], vs[0], o, C, n, None, H, D, dp.DP_BF16, scale)
+            dp.dp_attention(q, ks[0], vs[0], o, C, n, None, H, D, dp.DP_BF16, scale, **attn_layout(w))
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
@@ -1028,7 +1275,7 @@ def setup_attention(dev, layers=4):
         for l in range(layers):
             if timed and l == 0:
                 gt.start()
-            dp.dp_attention(q, ks[l], vs[l], o, C, n_ret, None, H, D, dp.DP_BF16, scale)
+            dp.dp_attention(q, ks[l], vs[l], o, C, n_ret, None, H, D, dp.DP_BF16, scale, **attn_layout(w))
             if timed and l == 0:
                 gt.stop()
 
@@ -1037,11 +1284,11 @@ def setup_attention(dev, layers=4):
         vf = torch.empty((n_full, H, D), dtype=torch.bfloat16, device=dev)
         dpsynth.kv_fill_device(kf, "bf16", w.seed, dpsynth.STREAM_K, 0, n_full, H * D)
         dpsynth.kv_fill_device(vf, "bf16", w.seed, dpsynth.STREAM_V, 0, n_full, H * D)
-        dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale)
+        dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale, **attn_layout(w))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
-            dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale)
+            dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale, **attn_layout(w))
         b.record()
         torch.cuda.synchronize()
         del kf, vf
@@ -1110,7 +1357,7 @@ def setup_hs_attention(dev, layers=4):
             gt.start()
         for l in range(layers):
             dp.dp_hs_attention(q, kr, vr, total, offsets, l, kc[l], vc[l], C, o, C, H, D,
-                               dp.DP_BF16, scale)
+                               dp.DP_BF16, scale, **attn_layout(w))
         if timed:
             gt.stop()
 
@@ -1119,11 +1366,11 @@ def setup_hs_attention(dev, layers=4):
         vf = torch.empty((n_full, H, D), dtype=torch.bfloat16, device=dev)
         dpsynth.kv_fill_device(kf, "bf16", w.seed, dpsynth.STREAM_K, 0, n_full, H * D)
         dpsynth.kv_fill_device(vf, "bf16", w.seed, dpsynth.STREAM_V, 0, n_full, H * D)
-        dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale)
+        dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale, **attn_layout(w))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
-            dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale)
+            dp.dp_attention(q, kf, vf, o, C, n_full, None, H, D, dp.DP_BF16, scale, **attn_layout(w))
         b.record()
         torch.cuda.synchronize()
         del kf, vf
@@ -1139,7 +1386,7 @@ def setup_hs_attention(dev, layers=4):
             for l in range(layers):
                 dp.dp_hs_attention_lag(q, kr, vr, total, offsets, l, kc[l], vc[l], C, o, C, H, D,
                                        dp.DP_BF16, scale, w.window_len, theta, 0, w.rope_pairs,
-                                       lag)
+                                       lag, key_layout=KEY_LAYOUT)
         once()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -1169,11 +1416,11 @@ def setup_hs_attention(dev, layers=4):
     return run, gt, accounting, None
 
 
-def setup_prefix(dev, slab_layers=20):
+def setup_prefix(dev, slab=0, slab_layers=20):
     """Prefix pruning of a 58-chunk observed context: all 57 non-sink chunks
     scored (d = 64) and compacted.  40 layers of K+V are 296.5 GB, more than
-    one GPU's 288 GB, so a step is timed on one 20-layer slab (the other slab
-    is the same launch on other layers)."""
+    one GPU's 288 GB, so a step runs on one 20-layer slab at a time (slab 0:
+    layers 0-19, slab 1: layers 20-39, each one batched launch)."""
     import compaction_dp_score_amd as dp
     import dpsynth
     from compaction_dp_score_amd.step import PruneStep
@@ -1181,8 +1428,9 @@ def setup_prefix(dev, slab_layers=20):
     T, H, D = w.seq_len, w.n_heads, w.head_dim
     x0, xf = dpsynth.score_inputs(w)
     x0d, xfd = torch.from_numpy(x0).to(dev), torch.from_numpy(xf).to(dev)
-    k_src = _fill_layers(dev, w, T, range(slab_layers), dpsynth.STREAM_K)
-    v_src = _fill_layers(dev, w, T, range(slab_layers), dpsynth.STREAM_V)
+    layers = range(slab * slab_layers, (slab + 1) * slab_layers)
+    k_src = _fill_layers(dev, w, T, layers, dpsynth.STREAM_K)
+    v_src = _fill_layers(dev, w, T, layers, dpsynth.STREAM_V)
     # the kept count sizes the destination (one host read, outside the timing)
     probe = PruneStep(k_src=k_src[:1], v_src=None, k_dst=[k_src[0][:1]], v_dst=None, seq_len=T,
                       sink_len=w.sink_len, window_len=w.window_len, scored_begin=w.scored_begin,
@@ -1219,12 +1467,16 @@ def setup_prefix(dev, slab_layers=20):
         return dict(n_kept=n, gather_bytes=gather, step_bytes=gather + index,
                     n_scored=w.n_scored, score_timer=st, index_bytes=index,
                     index_compare=index_compare(step, x0d, xfd, w.d),
-                    config={"workload": "prefix", "layers_in_slab": slab_layers, "layers": 40,
+                    config={"workload": "prefix", "slab": slab, "layers_in_slab": slab_layers,
+                            "slab_layers": [layers[0], layers[-1]], "layers": 40,
                             "heads": H, "head_dim": D, "kv_dtype": "bf16", "tokens": T,
                             "scored_tokens": w.n_scored, "d": w.d, "gamma": w.gamma,
                             "kept_tokens": n, "pr_step": 1 - n / T})
 
-    return run, gt, accounting, None
+    def cpu_baseline(seconds):
+        return cpu_baseline_prefix(w, x0, xf, slab_layers, seconds)
+
+    return run, gt, accounting, cpu_baseline
 
 
 def setup_hs(dev):
@@ -1274,11 +1526,16 @@ def setup_hs(dev):
     kv.src_rows, kv.out_capacity = T, total
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     kv.dev_error = err.data_ptr()
+    # the packed runs in this run's key layout; the source token rows stay
+    # interleaved (head rows on whole lines of their own, so the two classes of
+    # a layer share no source line)
+    kv.key_layout, kv.pair_begin, kv.n_pairs = KEY_LAYOUT, 0, w.rope_pairs
+    kv.src_key_layout = dp.DP_KEY_INTERLEAVED
     theta = torch.from_numpy(dpsynth.rope_theta(w.rope_pairs, w.rope_base)).to(dev)
     ft, fp = dpsynth.frame_tables(w)
     ftd, fpd = torch.from_numpy(ft).to(dev), torch.from_numpy(fp).to(dev)
     phase0 = fpd.clone()
-    rope = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
+    rope = make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor)
     ws = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                      dtype=torch.float32, device=dev)
     gt = Timer()
@@ -1293,29 +1550,50 @@ def setup_hs(dev):
         if timed:
             gt.stop()
 
-    def unfused_reindex(reps=3):
-        # the re-index as a pass of its own over the packed cache (the gather
-        # without the fused rotation leaves the keys at their old phases):
-        # dp_hs_rope_reindex, phase table restored before each call
-        dp.dp_hs_gather_kv(kv, head_class, 2, cidx, lens, caps, offsets)
+    def _median_ms(fn, reps):
         ms = []
         for _ in range(reps + 1):
             fpd.copy_(phase0)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            dp.dp_hs_rope_reindex(k_out, total, L, H, D, dp.DP_BF16, head_class, 2, lens, caps,
-                                  offsets, crf, rope, ws)
+            fn()
             b.record()
             torch.cuda.synchronize()
             ms.append(a.elapsed_time(b))
         fpd.copy_(phase0)
+        return float(np.median(ms[1:]))
+
+    def unfused_reindex(kvx, ropex, reps=3):
+        # the re-index as a pass of its own over the packed cache (the gather
+        # without the fused rotation leaves the keys at their old phases):
+        # dp_hs_rope_reindex, phase table restored before each call
+        dp.dp_hs_gather_kv(kvx, head_class, 2, cidx, lens, caps, offsets)
+        t = _median_ms(lambda: dp.dp_hs_rope_reindex(k_out, total, L, H, D, dp.DP_BF16,
+                                                     head_class, 2, lens, caps, offsets, crf,
+                                                     ropex, ws), reps)
         ln = lens.cpu().numpy()
         per_class = [(cls == c).sum() for c in range(2)]         # heads of each class
         rows = sum(int(per_class[c]) * int(ln[c] - w.window_len) for c in range(2))
         b = rows * 2 * w.rope_pairs * 2 * 2
-        t = float(np.median(ms[1:]))
         return {"unfused_reindex_ms": round(t, 4), "unfused_reindex_bytes": b,
                 "unfused_reindex_gbs": round(b / t / 1e6, 1)}
+
+    def context():
+        ctx = unfused_reindex(kv, rope)
+        if KEY_LAYOUT == dp.DP_KEY_INTERLEAVED:
+            # the same step writing split runs (each run's temporal blocks
+            # first): the fused gather, and the re-index of such runs as a pass
+            # of its own, which then rewrites whole lines only
+            kv_s = dp.dp_kv_hs.from_buffer_copy(kv)
+            kv_s.key_layout = dp.DP_KEY_SPLIT
+            rope_s = dp.make_rope(theta, ftd, fpd, w.q0, w.rope_knee, 1.0 / w.rope_factor,
+                                  key_layout=dp.DP_KEY_SPLIT)
+            t = _median_ms(lambda: dp.dp_hs_gather_kv(kv_s, head_class, 2, cidx, lens, caps,
+                                                      offsets, crf, rope_s, ws), 3)
+            gb = int(offsets[-1].item()) * D * 2 * 2 * 2
+            ctx["split_runs"] = dict(gather_ms=round(t, 4), gather_gbs=round(gb / t / 1e6, 1),
+                                     **unfused_reindex(kv_s, rope_s))
+        return ctx
 
     def accounting():
         assert keep_alive
@@ -1326,33 +1604,57 @@ def setup_hs(dev):
         index = 4 * T + 8 * int(ln.sum()) + 8 * (L * H + 1)
         return dict(n_kept=tot, gather_bytes=gather, step_bytes=gather + score + index,
                     n_scored=w.n_scored,
-                    context=None if ARGS.no_fullkv else unfused_reindex(),
+                    context=None if ARGS.no_fullkv else context(),
                     config={"workload": "hs", "layers": L, "heads": H, "head_dim": D,
                             "kv_dtype": "bf16", "tokens": T, "static_heads_per_layer": int(
                                 (cls == 0).sum(axis=1)[0]), "static_rows": int(ln[0]),
                             "dynamic_rows": int(ln[1]), "head_rows": tot,
                             "pr_step": 1 - tot / (L * H * T), "rope_pairs": w.rope_pairs,
-                            "q0": w.q0})
+                            "q0": w.q0, "key_layout": "split" if KEY_LAYOUT else "interleaved",
+                            "src_key_layout": "interleaved"})
 
-    return run, gt, accounting, None
+    def cpu_baseline(seconds):
+        return cpu_baseline_hs(w, x0, xf, cls, seconds)
+
+    return run, gt, accounting, cpu_baseline
 
 
-def summarize_stats(workload, stats_dir):
-    """Short text summary of rocprofv3's kernel statistics CSV."""
+def summarize_stats(workload, stats_dir, warmup):
+    """Short text summary of rocprofv3's kernel statistics CSV; the dominant
+    kernel's line is recomputed from the kernel trace without its first
+    `warmup` dispatches (the untimed warm-up steps), so its average is that of
+    the timed steps."""
     import csv
     import glob
     import re
     files = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
     assert files, "no kernel_stats.csv under %s" % stats_dir
     kname = KERNELS[workload][0]
+    flags = profile_flags(workload)
     lines = ["# rocprofv3 kernel statistics, %s workload (bench.py --workload %s)" % (workload, workload),
              "# commands (from the repository root):",
              "#   rocprofv3 --kernel-trace --stats -d %s -o run -f csv -- python bench.py "
-             "--workload %s %s --steps 10" % (stats_dir, workload, profile_flags(workload)),
-             "#   python bench.py --workload %s --summarize-stats %s" % (workload, stats_dir),
+             "--workload %s %s --warmup %d --steps 10" % (stats_dir, workload, flags, warmup),
+             "#   python bench.py --workload %s --warmup %d --summarize-stats %s"
+             % (workload, warmup, stats_dir),
              "# dominant kernel: %s; times in ns; fill_kernel and calib_copy_kernel are input" % kname,
-             "# generation and the copy-ceiling reference, not part of the step",
-             "kernel | calls | avg_ns | min_ns | max_ns | total_ns | pct"]
+             "# generation and the copy-ceiling reference, not part of the step"]
+    traces = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        durs = []
+        for r in csv.DictReader(open(traces[0])):
+            name = r["Kernel_Name"]
+            if ("::" + kname + "<") in name or ("::" + kname + "(") in name:
+                durs.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) -
+                             int(r["Start_Timestamp"])))
+        durs.sort()
+        timed = [d for _, d in durs[warmup:]]
+        if timed:
+            lines.append("# %s, timed steps only (first %d of %d dispatches are warm-up): "
+                         "calls %d | avg_ns %.0f | min_ns %d | max_ns %d"
+                         % (kname, warmup, len(durs), len(timed), sum(timed) / len(timed),
+                            min(timed), max(timed)))
+    lines.append("kernel | calls | avg_ns | min_ns | max_ns | total_ns | pct")
     for r in csv.DictReader(open(files[0])):
         name = r["Name"].replace("(anonymous namespace)", "anon")
         m = re.search(r"(\w+)(<[^>()]*>)?\(", name)
@@ -1369,11 +1671,19 @@ def summarize_stats(workload, stats_dir):
 ARGS = None   # parsed command line (the attention setups read --no-fullkv)
 
 
+def layout_for(workload, args):
+    """Key layout of a workload's records: --key-layout if given, else split,
+    except interleaved packed runs for the HS gather."""
+    if args.key_layout is not None:
+        return 1 if args.key_layout == "split" else 0
+    return 0 if workload == "hs" else 1
+
+
 def main():
-    global ARGS
+    global ARGS, KEY_LAYOUT
     args = ARGS = parse()
     if args.summarize_stats:
-        summarize_stats(args.workload, args.summarize_stats)
+        summarize_stats(args.workload, args.summarize_stats, args.warmup)
         return
     if args.summarize_pmc:
         summarize_pmc(args.workload, *args.summarize_pmc)
@@ -1392,10 +1702,37 @@ def main():
               "hs_attention": setup_hs_attention, "steady": setup_steady,
               "steady_lazy": setup_steady_lazy, "attention_lag": setup_attention_lag,
               "hs_ring": setup_hs_ring}
-    if args.workload not in setups:
-        print("workload %s is not wired into bench.py yet" % args.workload, file=sys.stderr)
-        sys.exit(2)
-    run, gt, accounting, cpu = setups[args.workload](dev)
+    if args.workload is not None:
+        rec = measure(args.workload, lambda: setups[args.workload](dev), dev, args)
+        print(json.dumps(rec), flush=True)
+        return
+    # default run: the eviction step is the headline record; the other four
+    # workloads (tiny, one-minute re-index, both prefix slabs, HS) follow under
+    # "configs", each measured after the previous one's buffers are freed
+    rec = measure("eviction", lambda: setup_eviction(dev), dev, args)
+    rec["configs"] = {}
+    for label, name, make in (
+            ("tiny", "tiny", lambda: setup_eviction(dev, "tiny")),
+            ("reindex", "reindex", lambda: setup_reindex(dev)),
+            ("prefix_slab0", "prefix", lambda: setup_prefix(dev, 0)),
+            ("prefix_slab1", "prefix", lambda: setup_prefix(dev, 1)),
+            ("hs", "hs", lambda: setup_hs(dev))):
+        r = measure(name, make, dev, args, copy_ceiling_too=False)
+        for k in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling",
+                  "vs_baseline", "data"):
+            r.pop(k, None)
+        rec["configs"][label] = r
+    print(json.dumps(rec), flush=True)
+
+
+def measure(workload, make, dev, args, copy_ceiling_too=True):
+    """Set up one workload, run args.warmup untimed and args.steps timed steps
+    (HIP events on the current stream around the steps), then build its JSON
+    record (and its CPU leg); the workload's buffers are freed on return."""
+    import gc
+    global KEY_LAYOUT
+    KEY_LAYOUT = layout_for(workload, args)
+    run, gt, accounting, cpu = make()
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         run(False)
@@ -1410,15 +1747,14 @@ def main():
     ms = t0.elapsed_time(t1) / args.steps
     acc = accounting()
     if acc.get("flops_per_launch"):
-        print(json.dumps(flops_record(args, acc, ms, gt.mean_ms())), flush=True)
-        return
+        return flops_record(args, acc, ms, gt.mean_ms())
     gbs = acc["step_bytes"] / (ms * 1e-3) / 1e9
     g_ms = gt.mean_ms()
     g_gbs = acc["gather_bytes"] / (g_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.workload)             # per dispatch
+    traffic = read_traffic(workload)                  # per dispatch
     if traffic is not None:
         traffic *= acc.get("timer_launches", 1)         # over the timed region
-    kernel = KERNELS[args.workload][0]
+    kernel = KERNELS[workload][0]
     rec = {
         "metric": "compacted KV GB/s (read+write) per prune step, % of HBM peak; tokens scored/s",
         "value": round(gbs, 2),
@@ -1430,7 +1766,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if acc["config"].get("kv_dtype", "bf16") == "bf16" else "f32",
         "data": "synthetic",
         "config": acc["config"],
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
@@ -1457,10 +1793,18 @@ def main():
                                 "gbs": round(acc["append_bytes"] / (a_ms * 1e-3) / 1e9, 2)}
     if acc.get("context"):
         rec["context"] = acc["context"]
-    rec["copy_ceiling_gbs"] = round(copy_ceiling(dev, CALIB_BYTES), 2)
+    if copy_ceiling_too:
+        rec["copy_ceiling_gbs"] = round(copy_ceiling(dev, CALIB_BYTES), 2)
+    del run, gt, accounting, acc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if cpu is not None and not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu(args.cpu_seconds)
-    print(json.dumps(rec), flush=True)
+    del cpu
+    gc.collect()
+    torch.cuda.empty_cache()
+    return rec
 
 
 if __name__ == "__main__":

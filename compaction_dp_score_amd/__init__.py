@@ -23,7 +23,7 @@ if not os.path.exists(LIB_PATH):
                       "python compaction_dp_score_amd/build.py)")
 
 _lib = ctypes.CDLL(LIB_PATH)
-ABI_VERSION = 2                # DP_ABI_VERSION of the include/decoprune.h this binding follows
+ABI_VERSION = 3                # DP_ABI_VERSION of the include/decoprune.h this binding follows
 _lib.dp_abi_version.restype = ctypes.c_int
 if _lib.dp_abi_version() != ABI_VERSION:
     raise ImportError("libdecoprune.so reports ABI %d, this binding follows ABI %d: rebuild it"
@@ -68,7 +68,8 @@ class dp_kv_hs(ctypes.Structure):
     _fields_ = [("k_src", _P), ("v_src", _P), ("k_out", _P), ("v_out", _P),
                 ("n_layers", _i32), ("n_heads", _i32), ("head_dim", _i32), ("dtype", _i32),
                 ("src_rows", _i64), ("out_capacity", _i64), ("dev_error", _P),
-                ("key_layout", _i32), ("pair_begin", _i32), ("n_pairs", _i32)]
+                ("key_layout", _i32), ("pair_begin", _i32), ("n_pairs", _i32),
+                ("src_key_layout", _i32)]
 
 
 class dp_kv_inplace(ctypes.Structure):

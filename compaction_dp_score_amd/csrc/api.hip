@@ -482,6 +482,9 @@ dp_status dp_hs_gather_kv(const dp_kv_hs* kv, const uint8_t* head_class, int32_t
   st = check_key_layout(kv->key_layout, kv->pair_begin, kv->n_pairs, kv->head_dim, kv->dtype,
                         "dp_hs_gather_kv");
   if (st != DP_OK) return st;
+  st = check_key_layout(kv->src_key_layout, kv->pair_begin, kv->n_pairs, kv->head_dim, kv->dtype,
+                        "dp_hs_gather_kv (source rows)");
+  if (st != DP_OK) return st;
   if (rope) {
     st = check_rope(rope, kv->head_dim, kv->dtype, ws, ws_bytes, "dp_hs_gather_kv");
     if (st != DP_OK) return st;

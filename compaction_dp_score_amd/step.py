@@ -29,7 +29,7 @@ class PruneStep:
         """k_src/v_src/k_dst/v_dst: lists of per-layer device tensors
         [rows, heads, head_dim]; v_* may be None.  rope: None or a dict with
         theta, frame_t, frame_phase (device tensors), q0, knee, inv_factor,
-        pair_begin."""
+        and optionally pair_begin and key_layout (dp_key_layout of the keys)."""
         dev = k_src[0].device
         self.device = dev
         self.seq_len = seq_len
@@ -71,7 +71,8 @@ class PruneStep:
             self._keep_alive += [rope["theta"], rope["frame_t"], rope["frame_phase"]]
             self.rope = make_rope(rope["theta"], rope["frame_t"], rope["frame_phase"],
                                   rope["q0"], rope["knee"], rope["inv_factor"],
-                                  rope.get("pair_begin", 0))
+                                  rope.get("pair_begin", 0),
+                                  key_layout=rope.get("key_layout", 0))
             nb = dp_rope_workspace_bytes(self.rope.n_frames, self.rope.n_pairs)
             self.ws_rope = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=dev)
 
@@ -143,8 +144,8 @@ class RingStep:
         """row_frame: device int32 [capacity]; tail: device int64 [1] (the end
         of the visible rows); frames_per_chunk: latent frames of one chunk;
         rope: dict with theta, frame_t, frame_phase (device tensors), knee,
-        inv_factor and optionally pair_begin (q0 is given per eviction); axis:
-        DP_AXIS_PAGE or DP_AXIS_COMPRESSED."""
+        inv_factor and optionally pair_begin and key_layout (q0 is given per
+        eviction); axis: DP_AXIS_PAGE or DP_AXIS_COMPRESSED."""
         span = (n_slots - 1) * frames_per_chunk          # frames of the window after an eviction
         knee = float(rope["knee"])
         if knee < span:
@@ -189,7 +190,8 @@ class RingStep:
     def _rope(self, q0):
         r = self.rope_args
         return make_rope(r["theta"], r["frame_t"], r["frame_phase"], q0, r["knee"],
-                         r["inv_factor"], r.get("pair_begin", 0), axis=self.axis)
+                         r["inv_factor"], r.get("pair_begin", 0), axis=self.axis,
+                         key_layout=r.get("key_layout", 0))
 
     def evict(self, slot, x0_hat, x_final, q0, row_stride=None, stream=None):
         """Enqueue the eviction of ring slot ``slot`` for query origin q0."""

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define DP_ABI_VERSION 2
+#define DP_ABI_VERSION 3
 
 typedef enum {
   DP_OK = 0,
@@ -428,11 +428,16 @@ dp_status dp_append_kept(const dp_kv_inplace* kv, int64_t slot_begin, int64_t sl
  * dp_hs_rope_reindex: in-place re-index of a ragged K cache laid out as above;
  *   k_capacity is the number of head rows in k_ragged (rows beyond it are
  *   skipped).
- * Key layout (dp_kv_hs.key_layout, pair_begin, n_pairs; for the re-index the
- *   rope's): DP_KEY_SPLIT sources are split token rows and each output run
- *   holds its temporal blocks, then the remaining parts (a run's head rows
- *   are then not head_dim apart); a fused_rope must name the same layout and
- *   pairs (DP_EINVAL).  V is packed as plain head rows in either layout.
+ * Key layouts (dp_kv_hs.src_key_layout for the source token rows,
+ *   dp_kv_hs.key_layout for the packed runs, one pair range for both; for the
+ *   re-index the rope's): with DP_KEY_SPLIT runs each output run holds its
+ *   temporal blocks, then the remaining parts (a run's head rows are then not
+ *   head_dim apart), so the re-index of a run rewrites only whole lines; with
+ *   DP_KEY_SPLIT sources the token rows are split rows.  Any pairing is
+ *   allowed: interleaved sources with split runs read whole head rows and
+ *   write split runs (the two classes of a layer then share no source line).
+ *   A fused_rope must name the runs' layout and pairs (DP_EINVAL).  V is
+ *   packed as plain head rows in every case.
  * class_idx / class_row_frame are device arrays of n_classes device pointers;
  * class_len is device int64 [n_classes].  n_classes <= DP_HS_MAX_CLASSES.
  *
@@ -458,9 +463,10 @@ typedef struct {
   int64_t src_rows;          /* rows of each source layer                       */
   int64_t out_capacity;      /* head-rows available in k_out / v_out            */
   int32_t* dev_error;        /* device int32 or NULL                            */
-  int32_t key_layout;        /* dp_key_layout of k_src and k_out                */
+  int32_t key_layout;        /* dp_key_layout of the packed runs in k_out       */
   int32_t pair_begin;        /* temporal pairs of the split layout              */
-  int32_t n_pairs;           /*   (ignored for DP_KEY_INTERLEAVED)               */
+  int32_t n_pairs;           /*   (ignored when neither layout is split)        */
+  int32_t src_key_layout;    /* dp_key_layout of the k_src token rows           */
 } dp_kv_hs;
 
 dp_status dp_hs_offsets(const uint8_t* head_class, int32_t n_layers, int32_t n_heads,

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert dp.dp_abi_version() == 2
+    assert dp.dp_abi_version() == 3
     assert dp.dp_status_str(dp.DP_OK) == "DP_OK"
     assert dp.dp_status_str(dp.DP_ECAPACITY) == "DP_ECAPACITY"
     assert dp.dp_status_str(dp.DP_ESTALL) == "DP_ESTALL"
@@ -230,6 +230,14 @@ def test_hs_rejects():
     kv.key_layout = 5
     assert _status("hs_gather", ctypes.byref(kv), FAKE, 2, FAKE, FAKE, caps, FAKE, None, None,
                    None, 0, None) == dp.DP_EINVAL
+    # the source rows' layout is checked on its own: unknown, or split with
+    # pairs that do not make whole vectors
+    kv.key_layout, kv.src_key_layout = dp.DP_KEY_INTERLEAVED, 7
+    assert _status("hs_gather", ctypes.byref(kv), FAKE, 2, FAKE, FAKE, caps, FAKE, None, None,
+                   None, 0, None) == dp.DP_EINVAL
+    kv.src_key_layout, kv.n_pairs = dp.DP_KEY_SPLIT, 6
+    assert _status("hs_gather", ctypes.byref(kv), FAKE, 2, FAKE, FAKE, caps, FAKE, None, None,
+                   None, 0, None) == dp.DP_EALIGN
 
 
 def test_pruning_ratio_counter():

@@ -50,9 +50,11 @@ def _dev(b, dtype, dev):
     return [to_dev(b[l].view(np.float32), dev) for l in range(b.shape[0])]
 
 
-def _rope_pair(rng, n_frames, npairs, q0, knee, factor, dev, pb, axis=dp.DP_AXIS_PAGE):
-    """Host tables and two device ropes (interleaved, split) with their own
-    phase tables and workspaces, so each layout advances its own phases."""
+def _rope_pair(rng, n_frames, npairs, q0, knee, factor, dev, pb, axis=dp.DP_AXIS_PAGE,
+               layouts=(dp.DP_KEY_INTERLEAVED, SPLIT)):
+    """Host tables and device ropes (by default one interleaved, one split)
+    with their own phase tables and workspaces, so each call advances its own
+    phases."""
     theta = dpsynth.rope_theta(npairs)
     ft = np.arange(n_frames, dtype=np.float32)
     fp = ft.copy()
@@ -60,7 +62,7 @@ def _rope_pair(rng, n_frames, npairs, q0, knee, factor, dev, pb, axis=dp.DP_AXIS
     host = dict(theta=theta, frame_t=ft, frame_phase=fp, q0=q0, knee=knee,
                 inv_factor=np.float32(1.0 / factor))
     out = []
-    for layout in (dp.DP_KEY_INTERLEAVED, SPLIT):
+    for layout in layouts:
         th, ftd, fpd = to_dev(theta, dev), to_dev(ft, dev), to_dev(fp.copy(), dev)
         r = dp.make_rope(th, ftd, fpd, q0, knee, 1.0 / factor, pb, axis=axis, key_layout=layout)
         ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, npairs) // 4 + 4,
@@ -278,9 +280,9 @@ def test_split_append_with_fused_reindex(L, T, H, D, dtype, tpf, pb, npairs):
 @pytest.mark.parametrize("fused", [False, True])
 def test_split_hs_gather_and_reindex(dtype, D, pb, npairs, fused):
     """The DeCoPrune-HS packed cache in the split layout: every run holds its
-    temporal blocks, then its other parts; gathered from split token rows, with
-    the re-index fused or as a pass of its own, it is the interleaved packed
-    cache run by run (V: plain head rows in both)."""
+    temporal blocks, then its other parts; gathered from split token rows or
+    from interleaved ones, with the re-index fused or as a pass of its own, it
+    is the interleaved packed cache run by run (V: plain head rows in all)."""
     dev = device()
     rng = np.random.default_rng(D + npairs + fused)
     L, H, T, tpf, sink, window = 3, 6, 3000, 50, 150, 450
@@ -299,8 +301,9 @@ def test_split_hs_gather_and_reindex(dtype, D, pb, npairs, fused):
     total = int(off_h[-1])
     rf = (np.arange(T) // tpf).astype(np.int32)
     n_frames = T // tpf
-    host, ((ri, _, wsi), (rs, _, wss)) = _rope_pair(rng, n_frames, npairs, float(n_frames), 9.0,
-                                                    4.0, dev, pb)
+    host, ((ri, _, wsi), (rs, _, wss), (rm, _, wsm)) = _rope_pair(
+        rng, n_frames, npairs, float(n_frames), 9.0, 4.0, dev, pb,
+        layouts=(dp.DP_KEY_INTERLEAVED, SPLIT, SPLIT))
     lists = [to_dev(x, dev) for x in lists_h]
     rfs = [to_dev(rf[x], dev) for x in lists_h]
     lens = to_dev(lens_h, dev)
@@ -308,9 +311,11 @@ def test_split_hs_gather_and_reindex(dtype, D, pb, npairs, fused):
     head_class = to_dev(cls.ravel(), dev)
     tdt = torch.bfloat16 if dtype == dp.DP_BF16 else torch.float32
     outs, alive = [], []
-    for layout, r, ws in ((dp.DP_KEY_INTERLEAVED, ri, wsi), (SPLIT, rs, wss)):
+    for src_layout, layout, r, ws in ((dp.DP_KEY_INTERLEAVED, dp.DP_KEY_INTERLEAVED, ri, wsi),
+                                      (SPLIT, SPLIT, rs, wss),
+                                      (dp.DP_KEY_INTERLEAVED, SPLIT, rm, wsm)):
         ksrc = _dev(kb, dtype, dev)
-        if layout == SPLIT:
+        if src_layout == SPLIT:
             ksrc = [to_split(t, pb, npairs).contiguous() for t in ksrc]
         vsrc = _dev(vb, dtype, dev)
         k_out = torch.zeros((total + 8, D), dtype=tdt, device=dev)
@@ -323,6 +328,7 @@ def test_split_hs_gather_and_reindex(dtype, D, pb, npairs, fused):
         kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dtype
         kv.src_rows, kv.out_capacity = T, total
         kv.key_layout, kv.pair_begin, kv.n_pairs = layout, pb, npairs
+        kv.src_key_layout = src_layout
         err = torch.zeros(1, dtype=torch.int32, device=dev)
         kv.dev_error = err.data_ptr()
         cidx, crf = dp.ptr_array(lists, dev), dp.ptr_array(rfs, dev)
@@ -335,15 +341,17 @@ def test_split_hs_gather_and_reindex(dtype, D, pb, npairs, fused):
                                   offsets, crf, r, ws)
         outs.append((k_out, v_out, err))
     torch.cuda.synchronize()
-    (ki, vi, ei), (ks, vs, es) = outs
-    assert ei.item() == 0 and es.item() == 0
-    assert torch.equal(vs.view(torch.int16 if dtype == dp.DP_BF16 else torch.int32),
-                       vi.view(torch.int16 if dtype == dp.DP_BF16 else torch.int32))
-    ki_h, ks_h = bits(ki), bits(ks)
-    for i in range(L * H):
-        lo, hi = int(off_h[i]), int(off_h[i + 1])
-        assert np.array_equal(run_from_split(ks_h[lo:hi], pb, npairs), ki_h[lo:hi]), i
-    assert np.all(ks_h[total:] == 0)
+    (ki, vi, ei) = outs[0]
+    ki_h = bits(ki)
+    iv = torch.int16 if dtype == dp.DP_BF16 else torch.int32
+    for ks, vs, es in outs[1:]:
+        assert ei.item() == 0 and es.item() == 0
+        assert torch.equal(vs.view(iv), vi.view(iv))
+        ks_h = bits(ks)
+        for i in range(L * H):
+            lo, hi = int(off_h[i]), int(off_h[i + 1])
+            assert np.array_equal(run_from_split(ks_h[lo:hi], pb, npairs), ki_h[lo:hi]), i
+        assert np.all(ks_h[total:] == 0)
     # the interleaved packed cache against the oracle
     tables = _tables(host)
     kk = kb.view(np.float32) if dtype == dp.DP_F32 else kb

@@ -115,3 +115,58 @@ def run_from_split(run, pair_begin, n_pairs):
     if isinstance(run, torch.Tensor):
         return torch.cat([opart[:, :lo], tpart, opart[:, lo:]], dim=1)
     return np.concatenate([opart[:, :lo], tpart, opart[:, lo:]], axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Error bound of the bf16 attention kernels against the float64 oracle.
+#
+# The kernel computes scores in fp32 from exact bf16 products, probabilities
+# p = exp2(s c - m) in fp32, their sum l in fp32 from the unrounded p, the
+# product P V from p rounded to bf16 (relative error <= u = 2^-8), and the
+# output O / l rounded to bf16 (<= u |o|).  With A = sum_j p_j |v_j| / l
+# (the oracle's attention over |V|):
+#   * probability rounding moves the output by at most u A;
+#   * the output rounding by at most u |o|;
+#   * a score error delta_j moves the output by at most
+#     max_j |delta_j| (A + |o|) (first order, o = sum p v / sum p); fp32 sums
+#     of D exact products err by at most D 2^-24 sum_i |q_i k_i|, which
+#     Cauchy-Schwarz bounds by D 2^-24 |q| max_j |k_j|, times the scale;
+#     exp2 and the fused scale add a few fp32 ulps (2^-21 covers them);
+#   * fp32 accumulation of O and l over n keys (16 keys per MFMA step, one
+#     rescale per 64-key tile at most) errs by at most (n/16 + 64) 2^-23
+#     relative to A + |o|.
+# bound = (u + delta + gamma_n) (A + |o|) + 1e-6.  A tile dropped, doubled
+# or paired with the wrong values moves an output by about its share of the
+# probability mass times |v - o|; the full-shape tile-coverage tests make that
+# share large on purpose.
+# ---------------------------------------------------------------------------
+def attention_bound(want, want_abs, q_norm, k_norm_max, scale, n_kv):
+    """Per-element bound for outputs `want` [rows, H, D] (float64 oracle)
+    given the oracle's attention over |V| `want_abs`, the query norms
+    q_norm [rows, H] and the largest key norm k_norm_max (scalar or [H])."""
+    D = want.shape[-1]
+    delta = D * 2.0 ** -24 * abs(scale) * np.asarray(q_norm)[..., None] * \
+        np.asarray(k_norm_max)[..., None] + 2.0 ** -21
+    gamma = (n_kv / 16.0 + 64.0) * 2.0 ** -23
+    return (2.0 ** -8 + delta + gamma) * (want_abs + np.abs(want)) + 1e-6
+
+
+def check_attention(got_bits, want, want_abs, q_norm, k_norm_max, scale, n_kv, tag):
+    """Assert |got - want| <= attention_bound elementwise; returns the
+    largest error and the largest error / bound ratio."""
+    got = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(got - want)
+    bound = attention_bound(want, want_abs, q_norm, k_norm_max, scale, n_kv)
+    assert np.all(err <= bound), (tag, float((err - bound).max()), float(err.max()))
+    return float(err.max()), float((err / bound).max())
+
+
+def bf16_abs(b):
+    """|x| of bf16 bit patterns (sign cleared; NaN stays NaN)."""
+    return np.asarray(b, np.uint16) & np.uint16(0x7FFF)
+
+
+def bf16_norms(b):
+    """Euclidean norms over the last axis of bf16 bit patterns (float64)."""
+    x = (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.sqrt((x * x).sum(-1))

@@ -89,18 +89,19 @@ def parse():
                     help="one workload; without it the eviction step is the headline record and "
                          "the tiny, one-minute re-index, both prefix slabs and HS workloads follow "
                          "under configs",
-                    choices=["eviction", "reindex", "prefix", "hs", "append", "attention",
+                    choices=["eviction", "tiny", "reindex", "prefix", "hs", "append", "attention",
                              "hs_attention", "steady", "steady_lazy", "attention_lag", "hs_ring"])
     ap.add_argument("--key-layout", default=None, choices=["split", "interleaved"],
                     help="layout of the key rows: split (the temporal blocks of all heads first; "
                          "the re-index writes whole lines) or interleaved ([heads][head_dim]); "
-                         "by default split, but interleaved packed runs for the HS workload "
-                         "(its gather is fastest so; the split-run figures go to its context)")
+                         "by default split for the re-index workloads (reindex, steady, append) "
+                         "and interleaved for the others (each record names its layout)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullkv", action="store_true",
                     help="skip the context timings that launch the dominant kernel outside the "
                          "timed steps (attention over the uncompacted cache, the page-axis "
-                         "steady step): profiling runs, so that every dispatch is a timed one")
+                         "steady step, the other key layout, the HS split runs): profiling "
+                         "runs, so that every dispatch is a timed one")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--summarize-stats", metavar="STATS_DIR",
@@ -128,10 +129,9 @@ def kernel_sources_sha(workload):
 
 
 def profile_flags(workload):
-    """bench.py flags of the profiling runs of a workload."""
-    extra = " --no-fullkv" if workload in ("attention", "hs_attention", "attention_lag",
-                                            "steady_lazy", "hs_ring") else ""
-    return "--no-cpu-baseline" + extra
+    """bench.py flags of the profiling runs of a workload (no context timings,
+    so that every dispatch of the dominant kernel is one of the steps')."""
+    return "--no-cpu-baseline --no-fullkv"
 
 
 def read_traffic(workload):
@@ -1671,12 +1671,21 @@ def summarize_stats(workload, stats_dir, warmup):
 ARGS = None   # parsed command line (the attention setups read --no-fullkv)
 
 
+# Workloads whose dominant kernel is an in-place re-index of old keys: split
+# keys let it rewrite whole lines only (the one-minute re-index: 6.0 against
+# 3.9 TB/s).  Elsewhere the layout is the model's natural one: attention over
+# split keys is 2.5 % slower (a head row is two pieces on lines it shares with
+# its neighbours), the HS gather from split rows reads shared lines twice, and
+# the gathers and appends move whole rows either way.
+SPLIT_WORKLOADS = ("reindex", "steady", "append")
+
+
 def layout_for(workload, args):
-    """Key layout of a workload's records: --key-layout if given, else split,
-    except interleaved packed runs for the HS gather."""
+    """Key layout of a workload's records: --key-layout if given, else split
+    for the re-index workloads and interleaved for the others."""
     if args.key_layout is not None:
         return 1 if args.key_layout == "split" else 0
-    return 0 if workload == "hs" else 1
+    return 1 if workload in SPLIT_WORKLOADS else 0
 
 
 def main():
@@ -1697,7 +1706,8 @@ def main():
         sys.exit(2)
     import compaction_dp_score_amd  # noqa: F401  (fails loudly if the library is missing)
     dev = torch.device("cuda:0")
-    setups = {"eviction": setup_eviction, "reindex": setup_reindex, "prefix": setup_prefix,
+    setups = {"eviction": setup_eviction, "tiny": lambda d: setup_eviction(d, "tiny"),
+              "reindex": setup_reindex, "prefix": setup_prefix,
               "hs": setup_hs, "append": setup_append, "attention": setup_attention,
               "hs_attention": setup_hs_attention, "steady": setup_steady,
               "steady_lazy": setup_steady_lazy, "attention_lag": setup_attention_lag,
@@ -1746,6 +1756,7 @@ def measure(workload, make, dev, args, copy_ceiling_too=True):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     acc = accounting()
+    acc["config"].setdefault("key_layout", "split" if KEY_LAYOUT else "interleaved")
     if acc.get("flops_per_launch"):
         return flops_record(args, acc, ms, gt.mean_ms())
     gbs = acc["step_bytes"] / (ms * 1e-3) / 1e9

@@ -187,7 +187,11 @@ __device__ bool hs_setup(const HsArgs& a, int n_slab_per_layer, HsTile& tl, int*
   return tl.nh > 0;
 }
 
-template <int U>
+// SD / SS: split output runs / split source rows (compile-time, so that each
+// instance carries only its own address arithmetic: with both layouts in one
+// body the interleaved gather needed 66 registers instead of 50, one wavefront
+// per SIMD fewer)
+template <int U, bool SD, bool SS>
 __global__ __launch_bounds__(kBlock) void hs_gather_kernel(HsArgs a) {
   __shared__ int heads[kMaxHeads];
   __shared__ int64_t head_off[kMaxHeads];
@@ -223,8 +227,8 @@ __global__ __launch_bounds__(kBlock) void hs_gather_kernel(HsArgs a) {
         const int32_t s = s_src[r];
         if (r < tl.rows && (uint32_t)s < (uint64_t)a.src_rows) {
           const int64_t o = head_off[k] + tl.j0 + r;
-          const bool split_k = a.split && !is_v;          // split output run
-          const bool split_s = a.split_src && !is_v;      // split source row
+          const bool split_k = SD && !is_v;               // split output run
+          const bool split_s = SS && !is_v;               // split source row
           // a split run is placed whole, so all of it must fit
           if (head_off[k] < 0 || (split_k ? head_off[k] + tl.n_run : o + 1) > a.out_cap) {
             overflow = true;
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(kBlock) void hs_gather_kernel(HsArgs a) {
   if (overflow && a.dev_error) *a.dev_error = DP_ECAPACITY;
 }
 
-template <int U>
+template <int U, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void hs_reindex_kernel(HsArgs a) {
   __shared__ int heads[kMaxHeads];
   __shared__ int64_t head_off[kMaxHeads];
@@ -306,8 +310,8 @@ __global__ __launch_bounds__(kBlock) void hs_reindex_kernel(HsArgs a) {
           const int64_t o = head_off[k] + tl.j0 + r;
           // interleaved: the row's lines holding the block; split: the row's
           // temporal block in the run's leading plane (the whole run must fit)
-          if (head_off[k] >= 0 && (a.split ? head_off[k] + tl.n_run <= a.out_cap : o < a.out_cap)) {
-            at[u] = a.split ? head_off[k] * a.vph + (tl.j0 + r) * a.tvc + wq : o * a.vph + wq;
+          if (head_off[k] >= 0 && (SPLIT ? head_off[k] + tl.n_run <= a.out_cap : o < a.out_cap)) {
+            at[u] = SPLIT ? head_off[k] * a.vph + (tl.j0 + r) * a.tvc + wq : o * a.vph + wq;
             const int tv = wq - a.rope.tv_off;
             const bool in_block = tv >= 0 && tv < a.rope.tv_count;
             const int p0 = in_block ? tv * a.rope.ppv : 0;
@@ -391,7 +395,14 @@ dp_status launch_hs_gather(const dp_kv_hs& kv, const uint8_t* head_class, int32_
   if (gx == 0) return DP_OK;
   // two vectors in flight per lane and pass: measured 2-4 % faster than four
   // on the HS workload, eight 21 % slower, one no better
-  hipLaunchKernelGGL(hs_gather_kernel<2>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  if (a.split && a.split_src)
+    hipLaunchKernelGGL((hs_gather_kernel<2, true, true>), dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  else if (a.split)
+    hipLaunchKernelGGL((hs_gather_kernel<2, true, false>), dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  else if (a.split_src)
+    hipLaunchKernelGGL((hs_gather_kernel<2, false, true>), dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((hs_gather_kernel<2, false, false>), dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("hs_gather_kernel");
 }
 
@@ -424,7 +435,10 @@ dp_status launch_hs_reindex(void* k, int64_t k_cap, int32_t L, int32_t H, int32_
   const uint64_t gx = hs_tiles(class_cap, n_classes) * (uint64_t)L;
   if (gx == 0) return DP_OK;
   // two vectors in flight per lane and pass, as for the gather (1.8 % faster than four)
-  hipLaunchKernelGGL(hs_reindex_kernel<2>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  if (a.split)
+    hipLaunchKernelGGL((hs_reindex_kernel<2, true>), dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((hs_reindex_kernel<2, false>), dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("hs_reindex_kernel");
 }
 

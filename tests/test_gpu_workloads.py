@@ -11,7 +11,9 @@ host against the C oracle's gather and re-index of the source copied back.
 The sources are the seeded generator's fill (tied to its host twin on sampled
 rows); the in-place passes regenerate their source into a scratch buffer.
 Bars: bit-exact for masks, indices and V; keys within max-abs 2e-2 (bf16) /
-1e-5 (fp32).
+1e-5 (fp32).  The re-index workloads run on both key layouts (split keys are
+what bench.py times for them): split caches are permuted from the fill before
+the call and back after it (data movement only), then checked as above.
 """
 import numpy as np
 import pytest
@@ -21,7 +23,7 @@ import compaction_dp_score_amd as dp
 import dpsynth
 import oracle
 from compaction_dp_score_amd.step import PruneStep
-from gpu_helpers import bits, device, keys_close
+from gpu_helpers import bits, device, from_split, keys_close, to_split
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +83,33 @@ def _tables_dev(tables, dev):
 
 def _i64(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(dev)
+
+
+LAYOUTS = [dp.DP_KEY_INTERLEAVED, dp.DP_KEY_SPLIT]
+
+
+def _to_layout(layers, layout, n_pairs):
+    """Permute natural key layers in place into `layout` (split: the temporal
+    blocks of all heads first)."""
+    if layout == dp.DP_KEY_SPLIT:
+        for t in layers:
+            t.copy_(to_split(t, 0, n_pairs))
+
+
+class _Natural:
+    """Key layers read back in the natural layout (one layer converted at a
+    time, the last one cached)."""
+
+    def __init__(self, layers, layout, n_pairs):
+        self.layers, self.layout, self.n_pairs = layers, layout, n_pairs
+        self.last = (None, None)
+
+    def __getitem__(self, l):
+        if self.layout != dp.DP_KEY_SPLIT:
+            return self.layers[l]
+        if self.last[0] != l:
+            self.last = (l, from_split(self.layers[l], 0, self.n_pairs))
+        return self.last[1]
 
 
 def _same(a, b):
@@ -187,11 +216,12 @@ def test_eviction_step_full_size():
     _free()
 
 
-def test_reindex_full_size():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_reindex_full_size(layout):
     """Re-index of the retained cache of a one-minute history: 40 x 40 x 128
-    bf16 keys, 240 frames, q0 = 240, knee 12, factor 8.  Every key of all 40
-    layers against its regenerated source; layers 0, 19 and 39 also through
-    the C oracle."""
+    bf16 keys, 240 frames, q0 = 240, knee 12, factor 8, on either key layout.
+    Every key of all 40 layers against its regenerated source; layers 0, 19
+    and 39 also through the C oracle."""
     dev = device()
     w = dpsynth.WORKLOADS["reindex"]
     L, H, D = w.n_layers, w.n_heads, w.head_dim
@@ -199,10 +229,11 @@ def test_reindex_full_size():
     rows = kept.shape[0]
     rf = dpsynth.row_frame(w)[kept].astype(np.int32)
     ks = _fill(dev, w, rows, range(L), dpsynth.STREAM_K)
+    _to_layout(ks, layout, w.rope_pairs)
     host = _rope_host(w)
     rd = _rope_dev(host, dev)
     rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
-                        host["inv_factor"])
+                        host["inv_factor"], key_layout=layout)
     ws = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                      dtype=torch.float32, device=dev)
     arr = dp.ptr_array(ks, dev)
@@ -212,16 +243,17 @@ def test_reindex_full_size():
     assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
     rf_d, tabd = _i64(rf, dev), _tables_dev(tables, dev)
     src = torch.empty_like(ks[0])
+    nat = _Natural(ks, layout, w.rope_pairs)
     worst, inexact = 0.0, 0
     for l in range(L):
         dpsynth.kv_fill_device(src, "bf16", w.seed, dpsynth.STREAM_K, l, rows, H * D)
         _tie_to_host(src, w, l, dpsynth.STREAM_K, rows)
-        e, ne = _check_rotated(ks[l], src, rf_d, tabd, w.rope_pairs)
+        e, ne = _check_rotated(nat[l], src, rf_d, tabd, w.rope_pairs)
         worst, inexact = max(worst, e), inexact + ne
         if l in (0, 19, L - 1):
-            _oracle_layer(src, None, np.arange(rows, dtype=np.int32), ks[l], None, rf, tables)
-    print("reindex: %d retained rows x %d layers, max |key error| %.3g, %d key elements off the "
-          "float64 rotation's bf16" % (rows, L, worst, inexact))
+            _oracle_layer(src, None, np.arange(rows, dtype=np.int32), nat[l], None, rf, tables)
+    print("reindex (layout %d): %d retained rows x %d layers, max |key error| %.3g, %d key "
+          "elements off the float64 rotation's bf16" % (layout, rows, L, worst, inexact))
     del ks, src
     _free()
 
@@ -498,20 +530,22 @@ def _append_step(w, dev, heads, cap, ks, vs, rf, tail0, x0, xf, d):
     return dict(kv=kv, ak=ak, av=av, err=err, idx=idx, nk=nk, tail=tail, rf_d=rf_d)
 
 
-def test_steady_step_full_size():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_steady_step_full_size(layout):
     """The steady-state step of the one-minute rollout in the ring layout, as
     bench.py times it: 40 x 40 x 128 bf16, [sink | 4 ring slots | history of
     the retained rows of chunks 1-55 | room]; chunk 56 leaves the window for
     q0 = 240.  The sink and history move by the uniform step 3.5 frames
     (dp_rope_shift), the leaving chunk's kept rows are appended with their
-    first re-index fused.  Every row of all 40 layers against the oracle's
-    tables applied to the regenerated fill."""
+    first re-index fused; either key layout.  Every row of all 40 layers
+    against the oracle's tables applied to the regenerated fill."""
     dev = device()
     w = dpsynth.WORKLOADS["reindex"]
     L, H, D, C = w.n_layers, w.n_heads, w.head_dim, w.chunk_tokens
     rf, n_hist, hb, cap = _ring_setup(w, 55)
     slot_begin = C
     ks = _fill(dev, w, cap, range(L), dpsynth.STREAM_K)
+    _to_layout(ks, layout, w.rope_pairs)
     vs = _fill(dev, w, cap, range(L), dpsynth.STREAM_V)
     we = dpsynth.WORKLOADS["eviction"]
     x0, xf = dpsynth.score_inputs(we)
@@ -522,7 +556,7 @@ def test_steady_step_full_size():
     host = dict(host, q0=w.q0, frame_phase=phase0)
     rd = _rope_dev(host, dev)
     rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
-                        host["inv_factor"])
+                        host["inv_factor"], key_layout=layout)
     ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                        dtype=torch.float32, device=dev)
     st = _append_step(w, dev, H, cap, ks, vs, rf, hb + n_hist, x0, xf, we.d)
@@ -530,9 +564,10 @@ def test_steady_step_full_size():
                        dtype=torch.float32, device=dev)
     step = 4 * (1 - 1 / w.rope_factor)
     ak = st["ak"]
-    dp.dp_rope_shift(ak, L, H, D, dp.DP_BF16, 0, C, None, rd["theta"], 0, w.rope_pairs, step, ws_s)
+    dp.dp_rope_shift(ak, L, H, D, dp.DP_BF16, 0, C, None, rd["theta"], 0, w.rope_pairs, step, ws_s,
+                     key_layout=layout)
     dp.dp_rope_shift(ak, L, H, D, dp.DP_BF16, hb, cap, st["tail"], rd["theta"], 0, w.rope_pairs,
-                     step, ws_s)
+                     step, ws_s, key_layout=layout)
     dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
     dp.dp_append_kept(st["kv"], slot_begin, C, st["idx"], st["nk"], st["tail"], st["rf_d"], rope,
                       ws_r)
@@ -546,14 +581,81 @@ def test_steady_step_full_size():
     uniform = _tables_dev(oracle.rope_uniform(host["theta"], step), dev)
     tabd = _tables_dev(tables, dev)
     scratch = (torch.empty_like(ks[0]), torch.empty_like(vs[0]))
+    nat = _Natural(ks, layout, w.rope_pairs)
     worst, inexact = 0.0, 0
     for l in range(L):
-        e, ne = _check_ring_layer(w, l, H, cap, ks, vs, hb, n_hist, slot_begin, widx, rf, uniform,
+        e, ne = _check_ring_layer(w, l, H, cap, nat, vs, hb, n_hist, slot_begin, widx, rf, uniform,
                                   tabd, dev, scratch)
         worst, inexact = max(worst, e), inexact + ne
-    print("steady step: %d history rows, %d appended, every row of %d layers, max |key error| "
-          "%.3g, %d key elements off the float64 rotation's bf16" % (n_hist, n, L, worst, inexact))
+    print("steady step (layout %d): %d history rows, %d appended, every row of %d layers, max "
+          "|key error| %.3g, %d key elements off the float64 rotation's bf16"
+          % (layout, n_hist, n, L, worst, inexact))
     del ks, vs, scratch
+    _free()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_append_step_full_size(layout):
+    """The eviction step in the ring layout as bench.py times it (the append
+    workload): 40 x 40 x 128 bf16 at the two-minute shape, one buffer per
+    layer [sink | 4 ring slots | room for one chunk of history]; the chunk in
+    ring slot 0 leaves the window: its kept rows are appended at the tail (K
+    and V, all layers), then dp_rope_prepare and dp_rope_apply over the sink
+    and over the history [T, tail) re-index the old keys for q0 = 20; either
+    key layout.  Every row of all 40 layers against the regenerated fill."""
+    dev = device()
+    w = dpsynth.WORKLOADS["eviction"]
+    T, H, D, L, C = w.seq_len, w.n_heads, w.head_dim, w.n_layers, w.chunk_tokens
+    cap, slot_begin = T + C, C
+    ks = _fill(dev, w, cap, range(L), dpsynth.STREAM_K)
+    _to_layout(ks, layout, w.rope_pairs)
+    vs = _fill(dev, w, cap, range(L), dpsynth.STREAM_V)
+    x0, xf = dpsynth.score_inputs(w)
+    widx = oracle.compact(oracle.mask(oracle.score_f32(x0, xf, w.d), C, 0, 0, 0, C, w.gamma))
+    n = widx.shape[0]
+    rf = np.full(cap, -1, np.int32)
+    rf[:T] = dpsynth.row_frame(w)
+    host = _rope_host(w)
+    rd = _rope_dev(host, dev)
+    rope = dp.make_rope(rd["theta"], rd["frame_t"], rd["frame_phase"], host["q0"], host["knee"],
+                        host["inv_factor"], key_layout=layout)
+    ws_r = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
+                       dtype=torch.float32, device=dev)
+    st = _append_step(w, dev, H, cap, ks, vs, rf, T, x0, xf, w.d)
+    dp.dp_append_kept(st["kv"], slot_begin, C, st["idx"], st["nk"], st["tail"], st["rf_d"])
+    dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+    dp.dp_rope_apply(st["ak"], L, H, D, dp.DP_BF16, 0, w.sink_len, None, st["rf_d"], rope, ws_r)
+    dp.dp_rope_apply(st["ak"], L, H, D, dp.DP_BF16, T, cap, st["tail"], st["rf_d"], rope, ws_r)
+    torch.cuda.synchronize()
+    assert st["err"].item() == 0 and st["nk"].item() == n and st["tail"].item() == T + n
+    tables = _tables(host)
+    assert np.array_equal(rd["frame_phase"].cpu().numpy(), tables[3])
+    rf_after = st["rf_d"].cpu().numpy()
+    assert np.all(rf_after[slot_begin:slot_begin + C] == -1)
+    assert np.array_equal(rf_after[T:T + n], rf[slot_begin + widx])
+    tabd = _tables_dev(tables, dev)
+    sk, sv = torch.empty_like(ks[0]), torch.empty_like(vs[0])
+    nat = _Natural(ks, layout, w.rope_pairs)
+    sink = w.sink_len
+    src = _i64(slot_begin + widx, dev)
+    rf_sink, rf_app = _i64(rf[:sink], dev), _i64(rf[slot_begin + widx], dev)
+    worst, inexact = 0.0, 0
+    for l in range(L):
+        dpsynth.kv_fill_device(sk, "bf16", w.seed, dpsynth.STREAM_K, l, cap, H * D)
+        dpsynth.kv_fill_device(sv, "bf16", w.seed, dpsynth.STREAM_V, l, cap, H * D)
+        _tie_to_host(sk, w, l, dpsynth.STREAM_K, cap)
+        _tie_to_host(sv, w, l, dpsynth.STREAM_V, cap)
+        g = nat[l]
+        e, ne = _check_rotated(g[:sink], sk[:sink], rf_sink, tabd, w.rope_pairs)
+        worst, inexact = max(worst, e), inexact + ne
+        assert _same(g[sink:T], sk[sink:T]) and _same(g[T + n:], sk[T + n:]), l
+        e, ne = _check_rotated(g[T:T + n], sk.index_select(0, src), rf_app, tabd, w.rope_pairs)
+        worst, inexact = max(worst, e), inexact + ne
+        assert _same(vs[l][:T], sv[:T]) and _same(vs[l][T + n:], sv[T + n:]), l
+        assert _same(vs[l][T:T + n], sv.index_select(0, src)), l
+    print("append step (layout %d): %d rows appended, every row of %d layers, max |key error| "
+          "%.3g, %d key elements off the float64 rotation's bf16" % (layout, n, L, worst, inexact))
+    del ks, vs, sk, sv
     _free()
 
 

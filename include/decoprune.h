@@ -29,7 +29,9 @@
  *     compute call only enqueues work on that stream and returns; results are
  *     visible to later work on the same stream.  No call synchronises the
  *     device, allocates memory, or keeps state between calls, except the
- *     thread-local error text of dp_last_error().
+ *     thread-local error text of dp_last_error() and the library's static
+ *     device array that dp_compact_index_noalloc uses instead of a workspace
+ *     (described at its declaration).
  *   - The caller owns every buffer.  Scratch memory comes from a caller
  *     workspace sized by the matching *_workspace_bytes() function.
  *   - All argument checks run on the host before the first HIP call.  A failed

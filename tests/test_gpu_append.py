@@ -91,6 +91,41 @@ def test_append_kept_matches_oracle(L, H, D, dtype, C, with_v):
             assert np.array_equal(bits(v[l]), vv[l]), l
 
 
+@pytest.mark.parametrize("rate", [0.0, 1.0])
+def test_append_kept_nothing_or_everything(rate):
+    """The leaving chunk keeps none of its rows (the tail stays, the slot's
+    frames are still retired) or all of them (the whole slot is appended)."""
+    dev = device()
+    rng = np.random.default_rng(int(rate * 10) + 5)
+    L, H, D, dtype, C, R = 2, 40, 128, dp.DP_BF16, 1560, 3
+    cap = C + R * C + 2 * C
+    kb, vb = _buf(rng, L, cap, H, D, dtype), _buf(rng, L, cap, H, D, dtype)
+    rf = rng.integers(0, 90, cap).astype(np.int32)
+    tail0 = C + R * C + 17
+    slot_begin = C + 2 * C
+    keep = np.full(C, 1 if rate else 0, np.uint8)
+    k, v = _dev(kb, dtype, dev), _dev(vb, dtype, dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    alive = []
+    kv = _inplace(k, v, dtype, cap, err, alive)
+    idx, n = _slot_index(keep, dev)
+    tail = torch.tensor([tail0], dtype=torch.int64, device=dev)
+    rf_d = to_dev(rf, dev)
+    dp.dp_append_kept(kv, slot_begin, C, idx, n, tail, rf_d)
+    torch.cuda.synchronize()
+    widx = oracle.compact(keep)
+    assert widx.shape[0] == (C if rate else 0)
+    kk, vv, rfo = kb.copy(), vb.copy(), rf.copy()
+    t1 = oracle.append_kept(kk, slot_begin, C, widx, tail0, rfo)
+    oracle.append_kept(vv, slot_begin, C, widx, tail0, None)
+    assert err.item() == 0 and tail.item() == t1 == tail0 + widx.shape[0]
+    assert np.array_equal(rf_d.cpu().numpy(), rfo)
+    assert np.all(rfo[slot_begin:slot_begin + C] == -1)
+    for l in range(L):
+        assert np.array_equal(bits(k[l]), kk[l]), l
+        assert np.array_equal(bits(v[l]), vv[l]), l
+
+
 @pytest.mark.parametrize("case", ["capacity", "overlap"])
 def test_append_kept_refuses_on_device(case):
     dev = device()

@@ -515,6 +515,75 @@ def test_hs_ragged_gather_and_reindex(dtype, D, fused, axis):
     assert np.all(bits(k_out[total:]) == 0) and np.all(bits(v_out[total:]) == 0)
 
 
+@pytest.mark.parametrize("static_cap", [0, 500])
+@pytest.mark.parametrize("fused", [False, True])
+def test_hs_gather_with_an_empty_class(static_cap, fused):
+    """One head class keeps no row (its heads' runs are empty; its list
+    capacity zero or not): the other class's runs are gathered and re-indexed
+    as usual, nothing is written past the total."""
+    dev = device()
+    rng = np.random.default_rng(40 + static_cap + fused)
+    L, H, T, D, tpf, dtype = 2, 5, 900, 128, 30, dp.DP_BF16
+    kb, vb = _layers(rng, L, T, H, D, dtype, scale=3.0), _layers(rng, L, T, H, D, dtype)
+    cls = np.array([[0, 1, 0, 1, 1], [1, 0, 0, 1, 0]], np.uint8)
+    lists_h = [np.zeros(0, np.int32), np.sort(rng.choice(T, 333, replace=False)).astype(np.int32)]
+    wlens = np.array([0, 333], np.int64)
+    woff = oracle.hs_offsets(cls, wlens)
+    total = int(woff[-1])
+    rf = (np.arange(T) // tpf).astype(np.int32)
+    n_frames = T // tpf
+    host, devt = _rope_inputs(rng, n_frames, 44, float(n_frames), 9.0, 4.0, dev, False)
+    lists = [torch.zeros(max(1, T), dtype=torch.int32, device=dev) for _ in range(2)]
+    rfs = [torch.zeros(max(1, T), dtype=torch.int32, device=dev) for _ in range(2)]
+    lists[1][:333] = to_dev(lists_h[1], dev)
+    rfs[1][:333] = to_dev(rf[lists_h[1]], dev)
+    lens = to_dev(wlens, dev)
+    head_class = to_dev(cls.ravel(), dev)
+    offsets = torch.empty(L * H + 1, dtype=torch.int64, device=dev)
+    dp.dp_hs_offsets(head_class, L, H, lens, 2, offsets)
+    k_out = torch.zeros((total + 8, D), dtype=torch.bfloat16, device=dev)
+    v_out = torch.zeros((total + 8, D), dtype=torch.bfloat16, device=dev)
+    k_src, v_src = _dev_layers(kb, dtype, dev), _dev_layers(vb, dtype, dev)
+    kv = dp.dp_kv_hs()
+    arrs = [dp.ptr_array(k_src, dev), dp.ptr_array(v_src, dev)]
+    kv.k_src, kv.v_src = arrs[0].data_ptr(), arrs[1].data_ptr()
+    kv.k_out, kv.v_out = k_out.data_ptr(), v_out.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dtype
+    kv.src_rows, kv.out_capacity = T, total
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    cidx, crf = dp.ptr_array(lists, dev), dp.ptr_array(rfs, dev)
+    caps = [static_cap, T]
+    rope = dp.make_rope(devt["theta"], devt["frame_t"], devt["frame_phase"], host["q0"],
+                        host["knee"], host["inv_factor"])
+    ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, 44) // 4, dtype=torch.float32,
+                     device=dev)
+    if fused:
+        dp.dp_hs_gather_kv(kv, head_class, 2, cidx, lens, caps, offsets, crf, rope, ws)
+    else:
+        dp.dp_hs_gather_kv(kv, head_class, 2, cidx, lens, caps, offsets)
+        dp.dp_hs_rope_reindex(k_out, total, L, H, D, dtype, head_class, 2, lens, caps, offsets,
+                              crf, rope, ws)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert np.array_equal(offsets.cpu().numpy(), woff)
+    w_k = np.zeros((total, D), kb.dtype)
+    w_v = np.zeros((total, D), vb.dtype)
+    for l in range(L):
+        oracle.hs_gather_layer(kb[l], l, cls, lists_h, woff, w_k)
+        oracle.hs_gather_layer(vb[l], l, cls, lists_h, woff, w_v)
+    assert np.array_equal(bits(v_out[:total]), w_v)
+    tables = oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
+                                host["inv_factor"], host["theta"])
+    w_rf = np.zeros(total, np.int32)
+    for i in range(L * H):
+        w_rf[woff[i]:woff[i + 1]] = rf[lists_h[cls.ravel()[i]]]
+    oracle.rope_headrows(w_k, w_rf, 0, tables)
+    ok, worst, _ = keys_close(bits(k_out[:total]), w_k, TOL[dtype])
+    assert ok, worst
+    assert np.all(bits(k_out[total:]) == 0) and np.all(bits(v_out[total:]) == 0)
+
+
 # --------------------------------------------------------------------------
 # whole tiny workload (1 layer, 2 heads, head_dim 64, fp32, 8 chunks of 64)
 # --------------------------------------------------------------------------

@@ -123,6 +123,13 @@ def test_score_index_many_tiles_and_changing_sizes():
         n = f.check(T, want)
         if T == 361920 and gamma == 0.10:
             assert 0.1 < n / T < 0.2                  # about 15 % kept
+    # the separate-launch path with the mask held in the workspace (keep_out
+    # NULL) and the row frames gathered, on the same workspace
+    T, ns = 361920, n_max
+    pol = dp.make_policy(T, sink, 0, sink, ns, 0.10)
+    rf = (np.arange(T) // 1560).astype(np.int32)
+    f.run(x0d, xfd, d, d, pol, rf_src=to_dev(rf, dev), keep=False)
+    f.check(T, oracle.mask(ell_o[:ns], T, sink, 0, sink, ns, 0.10), rf_src_host=rf, keep=False)
 
 
 def test_score_index_streaming_no_scores_and_optional_outputs():

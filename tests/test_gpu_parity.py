@@ -584,6 +584,101 @@ def test_hs_gather_with_an_empty_class(static_cap, fused):
     assert np.all(bits(k_out[total:]) == 0) and np.all(bits(v_out[total:]) == 0)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_hs_gather_with_many_classes(fused):
+    """More head classes than the page's two, each with its own policy (the
+    Streaming class, score masks at three thresholds, the reversed criterion
+    and a random mask), up to the ABI's limit of DP_HS_MAX_CLASSES: a class
+    with a single head in a layer, classes absent from a layer, a list filled
+    to its capacity exactly, and a class with no rows.  Every run is gathered
+    and re-indexed as the oracle does it class by class."""
+    dev = device()
+    rng = np.random.default_rng(77 + fused)
+    L, H, T, D, tpf, dtype = 3, 9, 1500, 128, 25, dp.DP_BF16
+    sink, window = 75, 300
+    ns = T - sink - window
+    nc = dp.DP_HS_MAX_CLASSES
+    kb, vb = _layers(rng, L, T, H, D, dtype, scale=3.0), _layers(rng, L, T, H, D, dtype)
+    x0, xf = _score_case(rng, ns, 32, 32)
+    ell = oracle.score_f32(x0, xf)
+    rand_keep = (rng.random(T) < 0.2).astype(np.uint8)
+    # class lists from the oracle (the index path is checked elsewhere)
+    lists_h = [oracle.compact(oracle.mask(None, T, sink, window, sink, ns, 0.1, streaming=True)),
+               oracle.compact(oracle.mask(ell, T, sink, window, sink, ns, 0.05)),
+               oracle.compact(oracle.mask(ell, T, sink, window, sink, ns, 0.1)),
+               oracle.compact(oracle.mask(ell, T, sink, window, sink, ns, 0.3)),
+               oracle.compact(oracle.mask(ell, T, sink, window, sink, ns, 0.1, reversed=True)),
+               oracle.compact(rand_keep),
+               np.zeros(0, np.int32),
+               oracle.compact(oracle.mask(ell, T, sink, window, sink, ns, 0.2))]
+    lists_h = [np.asarray(x, np.int32) for x in lists_h]
+    assert len(lists_h) == nc
+    cls = np.array([[0, 1, 2, 3, 4, 5, 6, 7, 2],      # every class, one head each but class 2
+                    [7, 7, 7, 1, 1, 1, 1, 7, 7],      # two classes only
+                    [3, 0, 5, 3, 0, 5, 3, 0, 4]],     # one head of class 4
+                   np.uint8)
+    wlens = np.array([len(x) for x in lists_h], np.int64)
+    woff = oracle.hs_offsets(cls, wlens)
+    total = int(woff[-1])
+    rf = (np.arange(T) // tpf).astype(np.int32)
+    n_frames = T // tpf
+    host, devt = _rope_inputs(rng, n_frames, 44, float(n_frames), 9.0, 4.0, dev, True)
+    caps = [T] * nc
+    caps[3] = int(wlens[3])                           # filled to its capacity exactly
+    caps[6] = 0
+    lists = [torch.zeros(max(1, caps[c]), dtype=torch.int32, device=dev) for c in range(nc)]
+    rfs = [torch.zeros(max(1, caps[c]), dtype=torch.int32, device=dev) for c in range(nc)]
+    for c in range(nc):
+        n = int(wlens[c])
+        if n:
+            lists[c][:n] = to_dev(lists_h[c], dev)
+            rfs[c][:n] = to_dev(rf[lists_h[c]], dev)
+    lens = to_dev(wlens, dev)
+    head_class = to_dev(cls.ravel(), dev)
+    offsets = torch.empty(L * H + 1, dtype=torch.int64, device=dev)
+    dp.dp_hs_offsets(head_class, L, H, lens, nc, offsets)
+    k_out = torch.zeros((total + 8, D), dtype=torch.bfloat16, device=dev)
+    v_out = torch.zeros((total + 8, D), dtype=torch.bfloat16, device=dev)
+    k_src, v_src = _dev_layers(kb, dtype, dev), _dev_layers(vb, dtype, dev)
+    kv = dp.dp_kv_hs()
+    arrs = [dp.ptr_array(k_src, dev), dp.ptr_array(v_src, dev)]
+    kv.k_src, kv.v_src = arrs[0].data_ptr(), arrs[1].data_ptr()
+    kv.k_out, kv.v_out = k_out.data_ptr(), v_out.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dtype
+    kv.src_rows, kv.out_capacity = T, total
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    cidx, crf = dp.ptr_array(lists, dev), dp.ptr_array(rfs, dev)
+    rope = dp.make_rope(devt["theta"], devt["frame_t"], devt["frame_phase"], host["q0"],
+                        host["knee"], host["inv_factor"])
+    ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, 44) // 4, dtype=torch.float32,
+                     device=dev)
+    if fused:
+        dp.dp_hs_gather_kv(kv, head_class, nc, cidx, lens, caps, offsets, crf, rope, ws)
+    else:
+        dp.dp_hs_gather_kv(kv, head_class, nc, cidx, lens, caps, offsets)
+        dp.dp_hs_rope_reindex(k_out, total, L, H, D, dtype, head_class, nc, lens, caps, offsets,
+                              crf, rope, ws)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert np.array_equal(offsets.cpu().numpy(), woff)
+    w_k = np.zeros((total, D), kb.dtype)
+    w_v = np.zeros((total, D), vb.dtype)
+    for l in range(L):
+        oracle.hs_gather_layer(kb[l], l, cls, lists_h, woff, w_k)
+        oracle.hs_gather_layer(vb[l], l, cls, lists_h, woff, w_v)
+    assert np.array_equal(bits(v_out[:total]), w_v)
+    tables = oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
+                                host["inv_factor"], host["theta"])
+    w_rf = np.zeros(total, np.int32)
+    for i in range(L * H):
+        w_rf[woff[i]:woff[i + 1]] = rf[lists_h[cls.ravel()[i]]]
+    oracle.rope_headrows(w_k, w_rf, 0, tables)
+    ok, worst, _ = keys_close(bits(k_out[:total]), w_k, TOL[dtype])
+    assert ok, worst
+    assert np.all(bits(k_out[total:]) == 0) and np.all(bits(v_out[total:]) == 0)
+
+
 # --------------------------------------------------------------------------
 # whole tiny workload (1 layer, 2 heads, head_dim 64, fp32, 8 chunks of 64)
 # --------------------------------------------------------------------------

@@ -1,0 +1,148 @@
+"""Seeded sweeps over shapes inside the ABI's contract.
+
+Each case draws a shape (layers, rows, heads, head_dim, dtype), a keep mask of
+a random rate with a sink and a window, a tokens-per-frame count and a
+temporal pair range, and checks one entry point against the oracle: the kept
+index list and the physical gather of K[m], V[m] (DeCoPrune page, section
+어떻게 동작하나), with or without the fused re-index of the key temporal
+phase (section 무엇과 다른가), and the in-place re-index over a row range
+whose end is a device count.  Bars as elsewhere: index lists, V and untouched
+keys bit for bit, re-indexed keys within 2e-2 (bf16) or 1e-5 (fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import compaction_dp_score_amd as dp
+import oracle
+from gpu_helpers import bits, device, keys_close, to_dev
+from test_gpu_parity import TOL, _dev_layers, _gpu_idx, _kv_struct, _layers, _rope_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(rng):
+    dtype = dp.DP_BF16 if rng.random() < 0.7 else dp.DP_F32
+    per16 = 8 if dtype == dp.DP_BF16 else 4            # elements per 16 bytes
+    D = per16 * int(rng.integers(1, 17))               # 16 .. 256 bytes per head row
+    H = int(rng.integers(1, 25))
+    T = int(rng.integers(1, 2500))
+    L = int(rng.integers(1, 4))
+    tpf = int(rng.integers(1, 150))
+    step = per16 // 2                                  # pairs per 16 bytes
+    pb = step * int(rng.integers(0, D // 2 // step))
+    npairs = int(rng.integers(1, D // 2 - pb + 1))
+    return L, T, H, D, dtype, tpf, pb, npairs
+
+
+CASES = list(range(24))
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_gather_sweep(case):
+    dev = device()
+    rng = np.random.default_rng(1000 + case)
+    L, T, H, D, dtype, tpf, pb, npairs = _draw(rng)
+    fused = case % 3 != 0
+    axis = dp.DP_AXIS_COMPRESSED if case % 4 == 1 else dp.DP_AXIS_PAGE
+    with_v = case % 5 != 0
+    sink, window = int(rng.integers(0, T + 1)), 0
+    window = int(rng.integers(0, T - sink + 1))
+    keep = (rng.random(T) < rng.random()).astype(np.uint8)
+    keep[:sink] = 1
+    keep[T - window:] = 1
+    kb = _layers(rng, L, T, H, D, dtype, scale=3.0)
+    vb = _layers(rng, L, T, H, D, dtype)
+    rf = (np.arange(T) // tpf).astype(np.int32)
+    n_frames = (T + tpf - 1) // tpf
+    cap = T if case % 2 == 0 else int(keep.sum())        # a destination of exactly the kept rows
+    k_src, v_src = _dev_layers(kb, dtype, dev), _dev_layers(vb, dtype, dev)
+    tdt = torch.bfloat16 if dtype == dp.DP_BF16 else torch.float32
+    k_dst = [torch.zeros((cap + 4, H, D), dtype=tdt, device=dev) for _ in range(L)]
+    v_dst = [torch.zeros((cap + 4, H, D), dtype=tdt, device=dev) for _ in range(L)] if with_v else None
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    alive = []
+    kv = _kv_struct(k_src, v_src if with_v else None, k_dst, v_dst, cap, err, alive)
+    idx, n, rf_out = _gpu_idx(keep, dev, rf)
+    host, devt = _rope_inputs(rng, n_frames, npairs, float(n_frames) + float(rng.random()),
+                              float(rng.integers(0, 8)), float(rng.integers(1, 9)), dev,
+                              bool(case % 2))
+    if fused:
+        rope = dp.make_rope(devt["theta"], devt["frame_t"], devt["frame_phase"], host["q0"],
+                            host["knee"], host["inv_factor"], pb, axis=axis)
+        ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, npairs) // 4 + 4,
+                         dtype=torch.float32, device=dev)
+        dp.dp_gather_kv(kv, idx, n, rf_out, rope, ws)
+    else:
+        dp.dp_gather_kv(kv, idx, n)
+    torch.cuda.synchronize()
+    widx = oracle.compact(keep)
+    m = widx.shape[0]
+    assert int(n.item()) == m and err.item() == 0, (case, m)
+    assert np.array_equal(idx[:m].cpu().numpy(), widx)
+    kk = kb.view(np.float32) if dtype == dp.DP_F32 else kb
+    wk = oracle.gather(kk, widx)
+    if fused:
+        tables = oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"],
+                                    host["knee"], host["inv_factor"], host["theta"],
+                                    compressed=axis == dp.DP_AXIS_COMPRESSED)
+        wrf = oracle.gather_i32(rf, widx)
+        for l in range(L):
+            oracle.rope_rows(wk[l], wrf, pb, tables)
+        assert np.array_equal(devt["frame_phase"].cpu().numpy(), tables[3])
+    wk_bits = wk.view(np.uint32) if dtype == dp.DP_F32 else wk
+    for l in range(L):
+        if fused:
+            ok, worst, _ = keys_close(bits(k_dst[l][:m]), wk_bits[l], TOL[dtype])
+            assert ok, (case, l, worst)
+        else:
+            assert np.array_equal(bits(k_dst[l][:m]), wk_bits[l]), (case, l)
+        assert np.all(bits(k_dst[l][m:]) == 0), (case, l)
+    if with_v:
+        wv = oracle.gather(vb, widx)
+        for l in range(L):
+            assert np.array_equal(bits(v_dst[l][:m]), wv[l]), (case, l)
+            assert np.all(bits(v_dst[l][m:]) == 0), (case, l)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_reindex_sweep(case):
+    dev = device()
+    rng = np.random.default_rng(2000 + case)
+    L, T, H, D, dtype, tpf, pb, npairs = _draw(rng)
+    kb = _layers(rng, L, T, H, D, dtype, scale=3.0)
+    rf = (np.arange(T) // tpf).astype(np.int32)
+    if case % 3 == 0:
+        rf[rng.random(T) < 0.05] = -1                  # rows with no key: left alone
+    n_frames = (T + tpf - 1) // tpf
+    n_rows = int(rng.integers(0, T + 1))               # device-side end of the visible rows
+    k = _dev_layers(kb, dtype, dev)
+    host, devt = _rope_inputs(rng, n_frames, npairs, float(n_frames) + float(rng.random()),
+                              float(rng.integers(0, 8)), float(rng.integers(1, 9)), dev,
+                              bool(case % 2))
+    axis = dp.DP_AXIS_COMPRESSED if case % 4 == 1 else dp.DP_AXIS_PAGE
+    rope = dp.make_rope(devt["theta"], devt["frame_t"], devt["frame_phase"], host["q0"],
+                        host["knee"], host["inv_factor"], pb, axis=axis)
+    ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, npairs) // 4 + 4, dtype=torch.float32,
+                     device=dev)
+    arr = dp.ptr_array(k, dev)
+    nr = torch.tensor([n_rows], dtype=torch.int64, device=dev)
+    dp.dp_rope_reindex(arr, L, H, D, dtype, T, nr, to_dev(rf, dev), rope, ws)
+    torch.cuda.synchronize()
+    kk = (kb.view(np.float32) if dtype == dp.DP_F32 else kb).copy()
+    tables = oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"], host["knee"],
+                                host["inv_factor"], host["theta"],
+                                compressed=axis == dp.DP_AXIS_COMPRESSED)
+    no_key = rf < 0                                    # the oracle takes frames in range only:
+    rf_in = np.where(no_key, 0, rf).astype(np.int32)   # such rows are restored afterwards
+    orig = kk.copy()
+    for l in range(L):
+        oracle.rope_rows(kk[l, :n_rows], rf_in[:n_rows], pb, tables)
+    kk[:, no_key] = orig[:, no_key]
+    want = kk.view(np.uint32) if dtype == dp.DP_F32 else kk
+    for l in range(L):
+        got = bits(k[l])
+        ok, worst, _ = keys_close(got[:n_rows], want[l, :n_rows], TOL[dtype])
+        assert ok, (case, l, worst)
+        assert np.array_equal(got[n_rows:], want[l, n_rows:]), (case, l)   # rows past the end
+    assert np.array_equal(devt["frame_phase"].cpu().numpy(), tables[3])

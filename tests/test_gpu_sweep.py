@@ -5,9 +5,10 @@ a random rate with a sink and a window, a tokens-per-frame count and a
 temporal pair range, and checks one entry point against the oracle: the kept
 index list and the physical gather of K[m], V[m] (DeCoPrune page, section
 어떻게 동작하나), with or without the fused re-index of the key temporal
-phase (section 무엇과 다른가), and the in-place re-index over a row range
-whose end is a device count.  Bars as elsewhere: index lists, V and untouched
-keys bit for bit, re-indexed keys within 2e-2 (bf16) or 1e-5 (fp32).
+phase (section 무엇과 다른가), the in-place re-index over a row range whose
+end is a device count, the ring-layout append and attention.  Bars as
+elsewhere: index lists, V and untouched keys bit for bit, re-indexed keys
+within 2e-2 (bf16) or 1e-5 (fp32), attention within the derived bound.
 """
 import numpy as np
 import pytest
@@ -146,3 +147,115 @@ def test_reindex_sweep(case):
         assert ok, (case, l, worst)
         assert np.array_equal(got[n_rows:], want[l, n_rows:]), (case, l)   # rows past the end
     assert np.array_equal(devt["frame_phase"].cpu().numpy(), tables[3])
+
+
+@pytest.mark.parametrize("case", list(range(16)))
+def test_append_sweep(case):
+    """dp_append_kept at random ring shapes: the slot's kept rows land at the
+    tail (all layers, K and V), the slot's frames are retired and the tail
+    advances (section 어떻게 동작하나); with the fused re-index the appended
+    keys also take their frames' phase step (section 무엇과 다른가)."""
+    from test_gpu_append import _buf, _dev, _inplace, _slot_index
+    dev = device()
+    rng = np.random.default_rng(3000 + case)
+    L, _, H, D, dtype, tpf, pb, npairs = _draw(rng)
+    C = int(rng.integers(1, 400))
+    R = int(rng.integers(1, 5))
+    sink = int(rng.integers(0, 100))
+    hist = int(rng.integers(C, 3 * C + 1))
+    cap = sink + R * C + hist
+    slot = int(rng.integers(0, R))
+    slot_begin = sink + slot * C
+    tail0 = int(rng.integers(sink + R * C, cap - C + 1))
+    fused = case % 2 == 1
+    with_v = case % 3 != 0
+    keep = (rng.random(C) < rng.random()).astype(np.uint8)
+    kb, vb = _buf(rng, L, cap, H, D, dtype), _buf(rng, L, cap, H, D, dtype)
+    n_frames = (cap + tpf - 1) // tpf
+    rf = (np.arange(cap) // tpf).astype(np.int32)
+    k, v = _dev(kb, dtype, dev), (_dev(vb, dtype, dev) if with_v else None)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    alive = []
+    kv = _inplace(k, v, dtype, cap, err, alive)
+    idx, n = _slot_index(keep, dev)
+    tail = torch.tensor([tail0], dtype=torch.int64, device=dev)
+    rf_d = to_dev(rf, dev)
+    host, devt = _rope_inputs(rng, n_frames, npairs, float(n_frames) + float(rng.random()),
+                              float(rng.integers(0, 8)), float(rng.integers(1, 9)), dev,
+                              bool(case % 4 == 0))
+    if fused:
+        rope = dp.make_rope(devt["theta"], devt["frame_t"], devt["frame_phase"], host["q0"],
+                            host["knee"], host["inv_factor"], pb)
+        ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, npairs) // 4 + 4,
+                         dtype=torch.float32, device=dev)
+        dp.dp_rope_prepare(rope, D, dtype, ws)
+        dp.dp_append_kept(kv, slot_begin, C, idx, n, tail, rf_d, rope, ws)
+    else:
+        dp.dp_append_kept(kv, slot_begin, C, idx, n, tail, rf_d)
+    torch.cuda.synchronize()
+    widx = oracle.compact(keep)
+    m = widx.shape[0]
+    assert err.item() == 0 and tail.item() == tail0 + m, case
+    kk = (kb.view(np.float32) if dtype == dp.DP_F32 else kb).copy()
+    rfo = rf.copy()
+    t1 = oracle.append_kept(kk, slot_begin, C, widx, tail0, rfo)
+    assert t1 == tail0 + m
+    assert np.array_equal(rf_d.cpu().numpy(), rfo), case
+    if fused:
+        tables = oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"],
+                                    host["knee"], host["inv_factor"], host["theta"])
+        for l in range(L):
+            sub = np.ascontiguousarray(kk[l, tail0:tail0 + m])
+            oracle.rope_rows(sub, rfo[tail0:tail0 + m], pb, tables)
+            kk[l, tail0:tail0 + m] = sub
+        assert np.array_equal(devt["frame_phase"].cpu().numpy(), tables[3])
+    want = kk.view(np.uint32) if dtype == dp.DP_F32 else kk
+    for l in range(L):
+        got = bits(k[l])
+        ok, worst, _ = keys_close(got[tail0:tail0 + m], want[l, tail0:tail0 + m], TOL[dtype])
+        assert ok, (case, l, worst)
+        rest = np.ones(cap, bool)
+        rest[tail0:tail0 + m] = False
+        assert np.array_equal(got[rest], want[l][rest]), (case, l)     # nothing else moves
+    if with_v:
+        vv = vb.copy()
+        oracle.append_kept(vv, slot_begin, C, widx, tail0, None)
+        for l in range(L):
+            assert np.array_equal(bits(v[l]), vv[l]), (case, l)
+
+
+@pytest.mark.parametrize("case", list(range(10)))
+def test_attention_sweep(case):
+    """dp_attention (the next chunk's queries over the compacted cache, the
+    step the page's continuation speed-up comes from, section 무엇인가) at
+    random query and key counts, head counts and scales, the key count on the
+    device or the host, every output against the float64 oracle under the
+    derived bound."""
+    from gpu_helpers import bf16_abs, bf16_from_bits, bf16_norms, check_attention, random_bf16_bits
+    dev = device()
+    rng = np.random.default_rng(4000 + case)
+    D = 128
+    n_q = int(rng.integers(1, 600))
+    n_kv = int(rng.integers(1, 1500))
+    H = int(rng.integers(1, 10))
+    scale = float(np.exp(rng.uniform(np.log(0.02), np.log(0.5))))
+    q = random_bf16_bits(rng, (n_q, H, D))
+    extra = int(rng.integers(0, 70))
+    k = random_bf16_bits(rng, (n_kv + extra, H, D))
+    v = random_bf16_bits(rng, (n_kv + extra, H, D))
+    k[n_kv:] = 0x7FC0                                 # rows past the count are never read
+    v[n_kv:] = 0x7FC0
+    qd, kd, vd = bf16_from_bits(q, dev), bf16_from_bits(k, dev), bf16_from_bits(v, dev)
+    od = torch.zeros((n_q, H, D), dtype=torch.bfloat16, device=dev)
+    if case % 2:
+        dp.dp_attention(qd, kd, vd, od, n_q, n_kv + extra,
+                        torch.tensor([n_kv], dtype=torch.int64, device=dev), H, D, dp.DP_BF16,
+                        scale)
+    else:
+        dp.dp_attention(qd, kd, vd, od, n_q, n_kv, None, H, D, dp.DP_BF16, scale)
+    torch.cuda.synchronize()
+    rows = np.arange(n_q)
+    want = oracle.attention(q, k, v, rows, n_kv=n_kv, scale=scale)
+    want_abs = oracle.attention(q, k, bf16_abs(v), rows, n_kv=n_kv, scale=scale)
+    kmax = bf16_norms(k[:n_kv]).max(axis=0)
+    check_attention(bits(od), want, want_abs, bf16_norms(q), kmax, scale, n_kv, ("sweep", case))

@@ -6,7 +6,8 @@ temporal pair range, and checks one entry point against the oracle: the kept
 index list and the physical gather of K[m], V[m] (DeCoPrune page, section
 어떻게 동작하나), with or without the fused re-index of the key temporal
 phase (section 무엇과 다른가), the in-place re-index over a row range whose
-end is a device count, the ring-layout append and attention.  Bars as
+end is a device count, the ring-layout append, attention, the one-launch
+index phase and the DeCoPrune-HS gather and re-index.  Bars as
 elsewhere: index lists, V and untouched keys bit for bit, re-indexed keys
 within 2e-2 (bf16) or 1e-5 (fp32), attention within the derived bound.
 """
@@ -259,3 +260,129 @@ def test_attention_sweep(case):
     want_abs = oracle.attention(q, k, bf16_abs(v), rows, n_kv=n_kv, scale=scale)
     kmax = bf16_norms(k[:n_kv]).max(axis=0)
     check_attention(bits(od), want, want_abs, bf16_norms(q), kmax, scale, n_kv, ("sweep", case))
+
+
+@pytest.mark.parametrize("case", list(range(16)))
+def test_score_index_sweep(case):
+    """dp_score_index (score, threshold mask, kept-index list in one launch;
+    section 어떻게 동작하나) at random sequence lengths, policies (sink,
+    window, scored range, threshold, reversed criterion, Streaming) and score
+    widths, one zero-filled workspace for all cases of a size: scores, mask,
+    list, count and gathered row frames bit for bit."""
+    from test_gpu_score_index import Fused, _score_case as score_case
+    dev = device()
+    rng = np.random.default_rng(5000 + case)
+    T = int(rng.integers(1, 40000))
+    sink = int(rng.integers(0, T + 1))
+    window = int(rng.integers(0, T - sink + 1))
+    sb = int(rng.integers(sink, T - window + 1))
+    ns = int(rng.integers(0, T - window - sb + 1))
+    d = int(rng.integers(1, 257))
+    stride = d + int(rng.integers(0, 9))
+    reversed_ = bool(case % 3 == 1)
+    streaming = bool(case % 5 == 4)
+    x0, xf = score_case(rng, max(ns, 1), d, stride)
+    x0, xf = x0[:ns], xf[:ns]
+    ell = oracle.score_f32(x0, xf, d) if ns else np.zeros(0, np.float32)
+    gamma = float(np.nanmedian(ell)) if ns and rng.random() < 0.5 else float(rng.random() * 2)
+    pol = dp.make_policy(T, sink, window, sb, ns, gamma, reversed_,
+                         dp.DP_MODE_STREAMING if streaming else dp.DP_MODE_SCORE)
+    want = oracle.mask(ell if ns else None, T, sink, window, sb, ns, gamma, reversed_, streaming)
+    rf = rng.integers(0, 1 << 30, T).astype(np.int32)
+    f = Fused(dev, T)
+    ell_d = torch.full((max(ns, 1),), -1.0, dtype=torch.float32, device=dev)
+    dummy = np.zeros((1, stride), np.float32)
+    x0d = to_dev(np.ascontiguousarray(x0) if ns else dummy, dev)
+    xfd = to_dev(np.ascontiguousarray(xf) if ns else dummy, dev)
+    for rep in range(2):                               # the workspace is left ready for the next call
+        f.run(x0d, xfd, d, stride, pol, ell_d, to_dev(rf, dev))
+        f.check(T, want, rf)
+    if ns and not streaming:
+        got = ell_d[:ns].cpu().numpy()
+        both_nan = np.isnan(got) & np.isnan(ell)
+        assert np.array_equal(got.view(np.uint32)[~both_nan], ell.view(np.uint32)[~both_nan]), case
+
+
+@pytest.mark.parametrize("case", list(range(12)))
+def test_hs_sweep(case):
+    """DeCoPrune-HS at random shapes (section 무엇과 다른가): 1 to 8 head
+    classes with their own kept-row lists, a random class per (layer, head),
+    list capacities with or without slack, the gather with or without the
+    fused re-index, or followed by the re-index of the packed cache."""
+    dev = device()
+    rng = np.random.default_rng(6000 + case)
+    L, T, H, D, dtype, tpf, pb, npairs = _draw(rng)
+    T = min(T, 1500)
+    nc = int(rng.integers(1, dp.DP_HS_MAX_CLASSES + 1))
+    mode = case % 3                                     # 0 plain, 1 fused, 2 separate re-index
+    lists_h = [np.flatnonzero(rng.random(T) < rng.random()).astype(np.int32) for _ in range(nc)]
+    cls = rng.integers(0, nc, (L, H)).astype(np.uint8)
+    wlens = np.array([len(x) for x in lists_h], np.int64)
+    woff = oracle.hs_offsets(cls, wlens)
+    total = int(woff[-1])
+    caps = [int(wlens[c]) + (int(rng.integers(0, 50)) if rng.random() < 0.5 else 0) for c in range(nc)]
+    rf = (np.arange(T) // tpf).astype(np.int32)
+    n_frames = (T + tpf - 1) // tpf
+    kb, vb = _layers(rng, L, T, H, D, dtype, scale=3.0), _layers(rng, L, T, H, D, dtype)
+    lists = [torch.zeros(max(1, caps[c]), dtype=torch.int32, device=dev) for c in range(nc)]
+    rfs = [torch.zeros(max(1, caps[c]), dtype=torch.int32, device=dev) for c in range(nc)]
+    for c in range(nc):
+        if wlens[c]:
+            lists[c][:wlens[c]] = to_dev(lists_h[c], dev)
+            rfs[c][:wlens[c]] = to_dev(rf[lists_h[c]], dev)
+    lens = to_dev(wlens, dev)
+    head_class = to_dev(cls.ravel(), dev)
+    offsets = torch.empty(L * H + 1, dtype=torch.int64, device=dev)
+    dp.dp_hs_offsets(head_class, L, H, lens, nc, offsets)
+    tdt = torch.bfloat16 if dtype == dp.DP_BF16 else torch.float32
+    k_out = torch.zeros((total + 8, D), dtype=tdt, device=dev)
+    v_out = torch.zeros((total + 8, D), dtype=tdt, device=dev)
+    k_src, v_src = _dev_layers(kb, dtype, dev), _dev_layers(vb, dtype, dev)
+    kv = dp.dp_kv_hs()
+    arrs = [dp.ptr_array(k_src, dev), dp.ptr_array(v_src, dev)]
+    kv.k_src, kv.v_src = arrs[0].data_ptr(), arrs[1].data_ptr()
+    kv.k_out, kv.v_out = k_out.data_ptr(), v_out.data_ptr()
+    kv.n_layers, kv.n_heads, kv.head_dim, kv.dtype = L, H, D, dtype
+    kv.src_rows, kv.out_capacity = T, total
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv.dev_error = err.data_ptr()
+    cidx, crf = dp.ptr_array(lists, dev), dp.ptr_array(rfs, dev)
+    host, devt = _rope_inputs(rng, n_frames, npairs, float(n_frames) + float(rng.random()),
+                              float(rng.integers(0, 8)), float(rng.integers(1, 9)), dev,
+                              bool(case % 2))
+    rope = dp.make_rope(devt["theta"], devt["frame_t"], devt["frame_phase"], host["q0"],
+                        host["knee"], host["inv_factor"], pb)
+    ws = torch.empty(dp.dp_rope_workspace_bytes(n_frames, npairs) // 4 + 4, dtype=torch.float32,
+                     device=dev)
+    if mode == 1:
+        dp.dp_hs_gather_kv(kv, head_class, nc, cidx, lens, caps, offsets, crf, rope, ws)
+    else:
+        dp.dp_hs_gather_kv(kv, head_class, nc, cidx, lens, caps, offsets)
+        if mode == 2:
+            dp.dp_hs_rope_reindex(k_out, total, L, H, D, dtype, head_class, nc, lens, caps,
+                                  offsets, crf, rope, ws)
+    torch.cuda.synchronize()
+    assert err.item() == 0, case
+    assert np.array_equal(offsets.cpu().numpy(), woff)
+    kk = kb.view(np.float32) if dtype == dp.DP_F32 else kb
+    w_k = np.zeros((total, D), kk.dtype)
+    w_v = np.zeros((total, D), vb.dtype)
+    for l in range(L):
+        oracle.hs_gather_layer(kk[l], l, cls, lists_h, woff, w_k)
+        oracle.hs_gather_layer(vb[l], l, cls, lists_h, woff, w_v)
+    assert np.array_equal(bits(v_out[:total]), w_v), case
+    if mode:
+        tables = oracle.rope_frames(host["frame_t"], host["frame_phase"], host["q0"],
+                                    host["knee"], host["inv_factor"], host["theta"])
+        w_rf = np.zeros(total, np.int32)
+        for i in range(L * H):
+            w_rf[woff[i]:woff[i + 1]] = rf[lists_h[cls.ravel()[i]]]
+        oracle.rope_headrows(w_k, w_rf, pb, tables)
+        assert np.array_equal(devt["frame_phase"].cpu().numpy(), tables[3])
+    want = w_k.view(np.uint32) if dtype == dp.DP_F32 else w_k
+    if mode:
+        ok, worst, _ = keys_close(bits(k_out[:total]), want, TOL[dtype])
+        assert ok, (case, worst)
+    else:
+        assert np.array_equal(bits(k_out[:total]), want), case
+    assert np.all(bits(k_out[total:]) == 0) and np.all(bits(v_out[total:]) == 0)

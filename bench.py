@@ -179,6 +179,17 @@ class Timer:
 # --------------------------------------------------------------------------
 # workloads
 # --------------------------------------------------------------------------
+def order_sensitive(x0, xf, d, gamma):
+    """Scored tokens whose float64 score lies within 1e-6 of the threshold
+    (relative): the only ones whose keep bit could depend on the order in which
+    the fp32 score sums its channels.  A property of the inputs, reported with
+    each scoring record."""
+    e = x0[:, :d].astype(np.float64) - xf[:, :d].astype(np.float64)
+    ell = (e * e).sum(axis=1) / d
+    g = float(np.float32(gamma))
+    return int(np.count_nonzero(np.abs(ell - g) < 1e-6 * g))
+
+
 def index_compare(step, x0d, xfd, d, reps=20):
     """Time the index phase both ways on the step's buffers (outside the timed
     steps): dp_score_index (one launch) and dp_score_mask + dp_compact_index
@@ -265,6 +276,7 @@ def setup_eviction(dev, name="eviction"):
         index = w.n_scored * (8 * w.d) + T + 12 * n        # scores in, keep out, idx + frames
         return dict(n_kept=n, gather_bytes=gather, score_timer=st, index_bytes=index,
                     index_compare=index_compare(step, x0d, xfd, w.d),
+                    order_sensitive=order_sensitive(x0, xf, w.d, w.gamma),
                     step_bytes=gather + index, n_scored=w.n_scored,
                     config={"workload": name, "layers": L, "heads": H, "head_dim": D,
                             "kv_dtype": w.dtype, "tokens": T, "chunk_tokens": w.chunk_tokens,
@@ -1467,6 +1479,7 @@ def setup_prefix(dev, slab=0, slab_layers=20):
         return dict(n_kept=n, gather_bytes=gather, step_bytes=gather + index,
                     n_scored=w.n_scored, score_timer=st, index_bytes=index,
                     index_compare=index_compare(step, x0d, xfd, w.d),
+                    order_sensitive=order_sensitive(x0, xf, w.d, w.gamma),
                     config={"workload": "prefix", "slab": slab, "layers_in_slab": slab_layers,
                             "slab_layers": [layers[0], layers[-1]], "layers": 40,
                             "heads": H, "head_dim": D, "kv_dtype": "bf16", "tokens": T,
@@ -1603,7 +1616,7 @@ def setup_hs(dev):
         score = w.n_scored * 8 * w.d + 2 * T
         index = 4 * T + 8 * int(ln.sum()) + 8 * (L * H + 1)
         return dict(n_kept=tot, gather_bytes=gather, step_bytes=gather + score + index,
-                    n_scored=w.n_scored,
+                    n_scored=w.n_scored, order_sensitive=order_sensitive(x0, xf, w.d, w.gamma),
                     context=None if ARGS.no_fullkv else context(),
                     config={"workload": "hs", "layers": L, "heads": H, "head_dim": D,
                             "kv_dtype": "bf16", "tokens": T, "static_heads_per_layer": int(
@@ -1802,6 +1815,8 @@ def measure(workload, make, dev, args, copy_ceiling_too=True):
         a_ms = acc["append_timer"].mean_ms()
         rec["append_kernel"] = {"ms": round(a_ms, 5), "bytes": acc["append_bytes"],
                                 "gbs": round(acc["append_bytes"] / (a_ms * 1e-3) / 1e9, 2)}
+    if acc.get("order_sensitive") is not None:
+        rec["order_sensitive_tokens"] = acc["order_sensitive"]
     if acc.get("context"):
         rec["context"] = acc["context"]
     if copy_ceiling_too:

@@ -85,18 +85,27 @@ struct ReindexArgs {
 // With rows of >= 128 walked vectors (WAVE_ROWS) a wavefront spans at most two
 // rows: their frames and phase steps are scalar loads, and a wavefront whose
 // rows both have delta == 0 (the recent window) leaves before touching the
-// keys; otherwise each lane looks its rows up.  The {cos, sin} loads go out
-// before the data loads (both vectors' loads are in flight together); vectors
-// outside the temporal block are written back unchanged so that whole 128-byte
-// lines are rewritten.  Measured on the one-minute cache with split keys: two
-// vectors per lane 4 % and the XCD order 3 % faster than one vector per lane
-// in plain order; three or four vectors per lane, 512-lane workgroups and
-// temporal (cached) loads or stores no better.
+// keys; otherwise each lane looks its rows up.  The {cos, sin} entries of a
+// wavefront's rows are then staged (STAGE, when a head row has at most kTabTv
+// temporal vectors): the wavefront's two frames need only 2 tv_count distinct
+// 32-byte entries, so lanes e < 2 tv_count load one each before the data loads
+// go out and write it to the wavefront's slot in LDS after them, and every
+// lane reads its vectors' entries from there (measured on the one-minute cache:
+// 1.3-1.5 % faster with split keys, 2 % with interleaved keys, than every lane
+// loading its own entries; outputs unchanged).  Otherwise each lane loads its
+// entries before the data.  Both vectors' data loads are in flight together;
+// vectors outside the temporal block are written back unchanged so that whole
+// 128-byte lines are rewritten.  Measured on the one-minute cache with split
+// keys: two vectors per lane 4 % and the XCD order 3 % faster than one vector
+// per lane in plain order; three or four vectors per lane, 512-lane
+// workgroups and temporal (cached) loads or stores no better.
 constexpr int kWaveSpan = 128;              // walked vectors per wavefront
 constexpr int kSpan = kBlock / 64 * kWaveSpan;
+constexpr int kTabTv = 32;                  // staged table: temporal vectors per head row
 
-template <bool WAVE_ROWS>
+template <bool WAVE_ROWS, bool STAGE>
 __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
+  __shared__ f32x4 tab_s[STAGE ? kBlock / 64 : 1][2][STAGE ? kTabTv : 1][2];
   int64_t end = a.rows_cap;
   if (a.n_rows) end = min(end, *a.n_rows);
   const int64_t n = end - a.row_begin;               // rows [row_begin, end)
@@ -126,11 +135,28 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
     db = (uint32_t)fb < nf ? uniform_load(a.rope.delta + fb) : 0.0f;
     if (da == 0.0f && db == 0.0f) return;
   }
+  // STAGE: lane e < 2 tv_count loads entry (frame a if e < tv_count else b,
+  // vector e mod tv_count) of the {cos, sin} table (entry 0 for a frame that
+  // does not move)
+  f32x4 st0 = {}, st1 = {};
+  int st_f = 0, st_v = 0;
+  const bool st_ld = STAGE && (int)lane < 2 * a.rope.tv_count;
+  if (STAGE && st_ld) {
+    st_f = (int)lane >= a.rope.tv_count;
+    st_v = (int)lane - st_f * a.rope.tv_count;
+    const int fx = st_f ? fb : fa;
+    const float dx = st_f ? db : da;
+    const f32x4* t = reinterpret_cast<const f32x4*>(
+        a.rope.cs + (int64_t)(dx != 0.0f ? fx : 0) * a.rope.pairs_padded + st_v * a.rope.ppv);
+    st0 = t[0];
+    st1 = t[1];
+  }
   u32x4* __restrict__ lay = reinterpret_cast<u32x4*>(a.layers[layer]);
   u32x4* p[2];
   f32x4 t01[2], t23[2];
   bool go[2], in_block[2];
   int nv[2];
+  int sel[2] = {0, 0}, tvs[2] = {0, 0};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const uint32_t i = w0 + u * 64 + lane;
@@ -153,16 +179,33 @@ __global__ __launch_bounds__(kBlock) void reindex_kernel(ReindexArgs a) {
     in_block[u] = tv >= 0 && tv < a.rope.tv_count;
     const int p0 = in_block[u] ? tv * a.rope.ppv : 0;
     nv[u] = min(a.rope.ppv, a.rope.n_pairs - p0);
-    const f32x4* t = reinterpret_cast<const f32x4*>(
-        a.rope.cs + (int64_t)(go[u] ? f : 0) * a.rope.pairs_padded + p0);
-    t01[u] = t[0];     // the table has a 32-byte tail, so t[1] is readable
-    t23[u] = t[1];
+    if (!STAGE) {
+      const f32x4* t = reinterpret_cast<const f32x4*>(
+          a.rope.cs + (int64_t)(go[u] ? f : 0) * a.rope.pairs_padded + p0);
+      t01[u] = t[0];     // the table has a 32-byte tail, so t[1] is readable
+      t23[u] = t[1];
+    } else {
+      sel[u] = j != ja;
+      tvs[u] = in_block[u] ? tv : 0;
+    }
     p[u] = lay + (a.row_begin + (int64_t)j) * a.row_vec + h * a.rope.head_stride_v + wq;
   }
   u32x4 v[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
     if (go[u]) v[u] = __builtin_nontemporal_load(p[u]);
+  if (STAGE) {
+    if (st_ld) {
+      tab_s[wave][st_f][st_v][0] = st0;
+      tab_s[wave][st_f][st_v][1] = st1;
+    }
+    __builtin_amdgcn_wave_barrier();     // LDS accesses of one wavefront stay in order
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      t01[u] = tab_s[wave][sel[u]][tvs[u]][0];
+      t23[u] = tab_s[wave][sel[u]][tvs[u]][1];
+    }
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (!go[u]) continue;
@@ -206,8 +249,12 @@ struct ShiftArgs {
 };
 
 // The walk of reindex_kernel (two vectors per lane, XCD-contiguous order) with
-// the same table for every row: no row frames.
+// the same table for every row: no row frames.  STAGE: lanes e < tv_count load
+// the table entry of vector e once and share it through the wavefront's LDS
+// slot, as reindex_kernel does.
+template <bool STAGE>
 __global__ __launch_bounds__(kBlock) void shift_kernel(ShiftArgs a) {
+  __shared__ f32x4 tab_s[STAGE ? kBlock / 64 : 1][STAGE ? kTabTv : 1][2];
   int64_t end = a.rows_cap;
   if (a.n_rows) end = min(end, *a.n_rows);
   const int64_t n = end - a.row_begin;                 // rows [row_begin, end)
@@ -222,11 +269,19 @@ __global__ __launch_bounds__(kBlock) void shift_kernel(ShiftArgs a) {
   const uint32_t w0 = (item - layer * tiles) * kSpan + wave * kWaveSpan;
   if (w0 >= per_layer) return;
   const uint32_t lane = threadIdx.x & 63;
+  f32x4 st0 = {}, st1 = {};
+  const bool st_ld = STAGE && (int)lane < a.tv_count;
+  if (STAGE && st_ld) {
+    const f32x4* t = reinterpret_cast<const f32x4*>(a.cs + (int)lane * a.ppv);
+    st0 = t[0];
+    st1 = t[1];
+  }
   u32x4* __restrict__ lay = reinterpret_cast<u32x4*>(a.layers[layer]);
   u32x4* p[2];
   f32x4 t01[2], t23[2];
   bool live[2], in_block[2];
   int nv[2];
+  int tvs[2] = {0, 0};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const uint32_t i = w0 + u * 64 + lane;
@@ -240,15 +295,31 @@ __global__ __launch_bounds__(kBlock) void shift_kernel(ShiftArgs a) {
     in_block[u] = tv >= 0 && tv < a.tv_count;
     const int p0 = in_block[u] ? tv * a.ppv : 0;
     nv[u] = min(a.ppv, a.n_pairs - p0);
-    const f32x4* t = reinterpret_cast<const f32x4*>(a.cs + p0);
-    t01[u] = t[0];     // the table is padded, so t[1] is readable
-    t23[u] = t[1];
+    if (!STAGE) {
+      const f32x4* t = reinterpret_cast<const f32x4*>(a.cs + p0);
+      t01[u] = t[0];     // the table is padded, so t[1] is readable
+      t23[u] = t[1];
+    } else {
+      tvs[u] = in_block[u] ? tv : 0;
+    }
     p[u] = lay + (a.row_begin + (int64_t)j) * a.row_vec + h * a.head_stride_v + wq;
   }
   u32x4 v[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
     if (live[u]) v[u] = __builtin_nontemporal_load(p[u]);
+  if (STAGE) {
+    if (st_ld) {
+      tab_s[wave][lane][0] = st0;
+      tab_s[wave][lane][1] = st1;
+    }
+    __builtin_amdgcn_wave_barrier();     // LDS accesses of one wavefront stay in order
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      t01[u] = tab_s[wave][tvs[u]][0];
+      t23[u] = tab_s[wave][tvs[u]][1];
+    }
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (!live[u]) continue;
@@ -336,10 +407,12 @@ dp_status launch_reindex(void* const* k, int32_t n_layers, int32_t n_heads, int3
   const uint64_t span = rows_cap > row_begin ? (uint64_t)(rows_cap - row_begin) : 0;
   const uint64_t gx = xcd_grid((span * a.div_row.d + kSpan - 1) / kSpan * (uint64_t)n_layers);
   if (gx == 0) return DP_OK;
-  if (a.div_row.d >= (uint32_t)kWaveSpan)
-    hipLaunchKernelGGL(reindex_kernel<true>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  if (a.div_row.d >= (uint32_t)kWaveSpan && rope.tv_count <= kTabTv)
+    hipLaunchKernelGGL((reindex_kernel<true, true>), dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  else if (a.div_row.d >= (uint32_t)kWaveSpan)
+    hipLaunchKernelGGL((reindex_kernel<true, false>), dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL(reindex_kernel<false>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((reindex_kernel<false, false>), dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("reindex_kernel");
 }
 
@@ -384,7 +457,10 @@ dp_status launch_rope_shift(void* const* k, int32_t n_layers, int32_t n_heads, i
   a.head_stride_v = view.head_stride_v;
   const uint64_t gx = xcd_grid(((uint64_t)(rows_cap - row_begin) * a.div_row.d + kSpan - 1) /
                                kSpan * (uint64_t)n_layers);
-  hipLaunchKernelGGL(shift_kernel, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  if (a.tv_count <= kTabTv)
+    hipLaunchKernelGGL(shift_kernel<true>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(shift_kernel<false>, dim3((uint32_t)gx), dim3(kBlock), 0, s, a);
   return check_launch("shift_kernel");
 }
 

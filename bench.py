@@ -1552,7 +1552,7 @@ def setup_hs(dev):
     ws = torch.empty(dp.dp_rope_workspace_bytes(w.n_frames, w.rope_pairs) // 4 + 4,
                      dtype=torch.float32, device=dev)
     gt = Timer()
-    keep_alive = [arrs, k_out, v_out, cidx, crf]
+    keep_alive = [arrs, k_out, v_out, cidx, crf, err]   # the kernels hold raw pointers to these
 
     def run(timed):
         fpd.copy_(phase0)

@@ -182,10 +182,21 @@ def dtype_code(t):
 
 
 def ptr_array(tensors, device):
-    """Device array of the data pointers of ``tensors`` (int64), or None."""
+    """Device array of the data pointers of ``tensors`` (int64), or None.
+
+    The array holds references to the tensors, so that memory it points at
+    lives as long as the array does: a tensor reachable only through a pointer
+    array would otherwise be freed into the caching allocator at once (its
+    memory still mapped, so kernels reading it seem to work) and released to
+    the driver by the next torch.cuda.empty_cache() (which entering
+    torch.cuda.graph calls), after which a kernel reaching it through the array
+    faults."""
     if tensors is None:
         return None
-    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+    tensors = list(tensors)
+    arr = torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+    arr._dp_targets = tensors
+    return arr
 
 
 def make_rope(theta, frame_t, frame_phase, q0, knee, inv_factor, pair_begin=0, axis=0,

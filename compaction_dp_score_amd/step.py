@@ -135,8 +135,9 @@ class RingStep:
 
     The model then writes the next chunk's K and V into the freed slot and
     calls ``write_chunk(slot, frames)`` with the rows' frames.  Nothing here
-    computes; it allocates once and marshals arguments.  Capturing ``evict``
-    into a HIP graph is not supported.
+    computes; it allocates once and marshals arguments, so ``evict`` can be
+    captured into a HIP graph and replayed (the model restores or advances
+    the tail, the slot's frames and the phase table between replays).
     """
 
     def __init__(self, *, k_layers, v_layers, sink_len, chunk_rows, n_slots, frames_per_chunk,

@@ -117,11 +117,6 @@ def test_random_mask_through_the_same_gather():
     assert abs(oracle.pr(n, T) - 0.8543) < 0.02
 
 
-@pytest.mark.skip(reason="graph capture of the ring-layout eviction is unsupported: a capture of "
-                         "the compressed-axis steady step (restore copies, dp_score_index, "
-                         "dp_rope_prepare, dp_append_kept with the fused re-index) faulted the GPU "
-                         "on its one run and no cause has been shown; this case stays off the GPU "
-                         "until one is")
 def test_ring_step_graph_replays_match_oracle():
     """RingStep.evict on the compressed axis captured once into a graph and
     replayed from the same starting cache (tail, row frames and phase table

@@ -456,3 +456,23 @@ def test_score_index_rejects():
     assert _status("score_index", *args(x0=None)) == dp.DP_EINVAL
     bad = _policy(scored_begin=50)                           # before the end of the sink
     assert _status("score_index", *args(pol=ctypes.byref(bad))) == dp.DP_EINVAL
+
+
+def test_pointer_array_keeps_its_tensors():
+    """A tensor reached only through a pointer array lives as long as the
+    array: otherwise it would be freed into torch's caching allocator and
+    released to the driver by the next empty_cache() (torch.cuda.graph runs
+    one on entry) while a kernel still holds its address."""
+    import gc
+    import weakref
+    import torch
+    ts = [torch.empty(16) for _ in range(3)]
+    ref = weakref.ref(ts[1])
+    arr = dp.ptr_array(ts, torch.device("cpu"))
+    assert arr.tolist() == [t.data_ptr() for t in ts]
+    del ts
+    gc.collect()
+    assert ref() is not None
+    del arr
+    gc.collect()
+    assert ref() is None

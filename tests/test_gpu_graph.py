@@ -2,9 +2,13 @@
 
 Every entry point only enqueues work on the caller's stream, allocates
 nothing and never synchronises, so score -> index -> gather (with the fused
-re-index) can be captured once and replayed.  The inputs change between
-replays (new scores, restored phase table), with eager work and
-synchronisations in between, and every replay is compared with the oracle.
+re-index), and the ring-layout eviction (score and index, table, sink
+re-index, append with the fused re-index), can be captured once and
+replayed.  The inputs change between replays (new scores, restored phase
+table and cache), with eager work and synchronisations in between, and
+every replay is compared with the oracle.  Entering torch.cuda.graph empties
+torch's allocator cache, so these tests also check that every buffer the
+captured kernels reach is still held (the pointer arrays hold their tensors).
 """
 import numpy as np
 import pytest

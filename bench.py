@@ -179,6 +179,35 @@ class Timer:
 # --------------------------------------------------------------------------
 # workloads
 # --------------------------------------------------------------------------
+def step_ms_eager_and_graph(step, restore, reps=20):
+    """Median time of one step enqueued call by call, and of the same step
+    captured once into a HIP graph and replayed (restore() runs eagerly before
+    each, outside the events).  Every buffer the step reaches must be held by
+    the caller: entering torch.cuda.graph empties torch's allocator cache."""
+    def timed(fn):
+        ms = []
+        for _ in range(reps + 1):
+            restore()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms[1:]))
+    eager = timed(step)
+    g = torch.cuda.CUDAGraph()
+    restore()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    graph = timed(g.replay)
+    restore()
+    torch.cuda.synchronize()
+    del g
+    return {"step_ms_eager": round(eager, 4), "step_ms_graph": round(graph, 4)}
+
+
 def order_sensitive(x0, xf, d, gamma):
     """Scored tokens whose float64 score lies within 1e-6 of the threshold
     (relative): the only ones whose keep bit could depend on the order in which
@@ -1010,6 +1039,11 @@ def setup_steady_lazy(dev):
         if timed:
             gt.stop()
 
+    def step():
+        dp.dp_score_index(x0d, xfd, w.d, w.d, pol, None, keep, idx, nk, None, None, ws_si, err)
+        dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+        dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf, rope, ws_r)
+
     def page_axis_ms(reps=5):
         def once():
             restore()
@@ -1036,8 +1070,9 @@ def setup_steady_lazy(dev):
         append = n * H * D * 2 * 2 * 2 * L
         score = C * (8 * w.d + 1)
         return dict(n_kept=n, gather_bytes=append, step_bytes=append + score, n_scored=C,
-                    context=None if ARGS.no_fullkv else {"page_axis_step_ms":
-                                                         round(page_axis_ms(), 4)},
+                    context=None if ARGS.no_fullkv else {
+                        "page_axis_step_ms": round(page_axis_ms(), 4),
+                        **step_ms_eager_and_graph(step, restore)},
                     config={"workload": "steady_lazy",
                             "layout": "sink | ring of 4 chunk slots | history",
                             "time_axis": "compressed (old keys at phase t/c)",
@@ -1144,6 +1179,12 @@ def setup_hs_ring(dev):
             gt.stop()
         rf_s[slot_begin:slot_begin + C].fill_(-1)                 # the static class drops it
 
+    def step():
+        dp.dp_score_index(x0d, xfd, w.d, w.d, pol, None, keep, idx, nk, None, None, ws_si, err)
+        dp.dp_rope_prepare(rope, D, dp.DP_BF16, ws_r)
+        dp.dp_append_kept(kv, slot_begin, C, idx, nk, tail, rf, rope, ws_r)
+        rf_s[slot_begin:slot_begin + C].fill_(-1)
+
     def page_axis_ms(reps=5):
         def once():
             restore()
@@ -1172,8 +1213,9 @@ def setup_hs_ring(dev):
         append = n * HC * D * 2 * 2 * 2 * L
         score = C * (8 * w.d + 1)
         return dict(n_kept=n, gather_bytes=append, step_bytes=append + score, n_scored=C,
-                    context=None if ARGS.no_fullkv else {"page_axis_step_ms":
-                                                         round(page_axis_ms(), 4)},
+                    context=None if ARGS.no_fullkv else {
+                        "page_axis_step_ms": round(page_axis_ms(), 4),
+                        **step_ms_eager_and_graph(step, restore)},
                     config={"workload": "hs_ring",
                             "layout": "per head class: static sink | 4 chunk slots; "
                                       "dynamic sink | 4 chunk slots | history",

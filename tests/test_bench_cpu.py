@@ -30,3 +30,16 @@ def test_code_changes_change_the_hash(tmp_path, monkeypatch):
     assert _sha(tmp_path, monkeypatch, BASE.replace("a + 1", "a + 2")) != h0
     assert _sha(tmp_path, monkeypatch, BASE.replace('"a // b"', '"a // c"')) != h0   # in a string
     assert os.path.basename(bench.__file__) == "bench.py"
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus N with N > 1 exits with a message
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.abspath(bench.__file__))
+    p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
+    assert p.stdout.strip() == ""

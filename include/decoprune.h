@@ -33,7 +33,12 @@
  *     device array that dp_compact_index_noalloc uses instead of a workspace
  *     (described at its declaration).
  *   - The caller owns every buffer.  Scratch memory comes from a caller
- *     workspace sized by the matching *_workspace_bytes() function.
+ *     workspace sized by the matching *_workspace_bytes() function.  Every
+ *     buffer a call reaches, the layer buffers named by device arrays of
+ *     pointers included, must stay allocated until the work enqueued on the
+ *     stream has finished (the library holds no references; with a caching
+ *     allocator, memory freed early may still read back intact until the
+ *     allocator returns it to the driver, after which the kernel faults).
  *   - All argument checks run on the host before the first HIP call.  A failed
  *     check returns DP_EINVAL / DP_EALIGN / DP_ERANGE / DP_EUNSUPPORTED and
  *     enqueues nothing.  A failed launch returns DP_EHIP.  dp_last_error()

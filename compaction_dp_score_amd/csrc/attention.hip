@@ -21,7 +21,8 @@
 // The MFMAs of the next tile's S^T are issued while the current tile's
 // probabilities are formed.
 // Query tiles of one head are placed on one XCD (workgroup i runs on XCD
-// i mod 8), so the key/value tiles they all stream are shared in that XCD's L2.
+// i mod 8), so the key/value tiles they all stream are shared in that XCD's L2;
+// over a ragged cache each half of a head's tiles is placed on one XCD.
 //
 // A head's keys come in up to two segments, streamed one after the other:
 // segment 0 is either the dense token-major cache [rows][heads][head_dim] or,
@@ -158,14 +159,17 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
   int head, qt;
   if (a.xcd_map) {
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-    const int j = slot / a.n_qt;                 // j-th head placed on this XCD
-    qt = slot % a.n_qt;
-    head = j * kXcds + xcd;
     if (RAGGED && a.n_heads <= kAttnBlock) {
-      // Ragged runs differ in length, so heads are ranked by length (longest
-      // first, ties by index) and dealt to the XCDs in snake order: every XCD
-      // gets the same number of heads and nearly the same number of keys, and
-      // the longest heads start first.
+      // Ragged runs differ in length.  Each head's query tiles are cut into two
+      // halves, the 2H halves ranked by run length (longest first, ties by
+      // head, so a head's halves are adjacent) and dealt to the XCDs in snake
+      // order: every XCD gets the same number of halves and nearly the same
+      // number of keys, a head's keys are read by at most two XCDs, and on
+      // each XCD the longest halves start first.  Whole heads dealt the same
+      // way leave the XCDs unequal when the heads per XCD are odd and the
+      // lengths bimodal (5 per XCD, static and dynamic heads: half the XCDs
+      // get three long heads); the halves were 5 % faster there and the same
+      // at equal lengths.  The grid holds 2H halves of ceil(tiles / 2) slots.
       __shared__ int64_t len_s[kAttnBlock];
       __shared__ int head_of_rank[kAttnBlock];
       const int t = threadIdx.x;
@@ -185,7 +189,17 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
         head_of_rank[rank] = t;
       }
       __syncthreads();
-      head = head_of_rank[j * kXcds + ((j & 1) ? kXcds - 1 - xcd : xcd)];
+      const int half_tiles = (a.n_qt + 1) >> 1;
+      const int j = slot / half_tiles, u = slot - j * half_tiles;
+      const int r = j * kXcds + ((j & 1) ? kXcds - 1 - xcd : xcd);   // rank of the half
+      if (r >= 2 * a.n_heads) return;
+      head = head_of_rank[r >> 1];
+      qt = (r & 1) * half_tiles + u;
+      if (qt >= a.n_qt) return;
+    } else {
+      const int j = slot / a.n_qt;               // j-th head placed on this XCD
+      qt = slot % a.n_qt;
+      head = j * kXcds + xcd;
     }
   } else {
     head = blockIdx.x / a.n_qt;
@@ -595,7 +609,11 @@ dp_status launch(AttnArgs& a, const void* q, void* o, int64_t n_q, int32_t n_hea
   a.n_qt = (int32_t)((n_q + bm - 1) / bm);
   a.xcd_map = n_heads % kXcds == 0;
   a.c = scale * 1.4426950408889634f;
-  const uint64_t blocks = (uint64_t)a.n_qt * n_heads;
+  // ragged caches on the XCD map: 2H halves of ceil(tiles / 2) slots each
+  const bool halves = (mode == kRagged || mode == kRaggedLag) && a.xcd_map &&
+                      n_heads <= Shape<kRagged>::kBlock;
+  const uint64_t blocks = halves ? (uint64_t)2 * n_heads * ((a.n_qt + 1) / 2)
+                                 : (uint64_t)a.n_qt * n_heads;
   if (blocks == 0) return DP_OK;
   const dim3 grid((uint32_t)blocks);
   if (a.tvc > 0) {

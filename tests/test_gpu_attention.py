@@ -234,6 +234,35 @@ def test_hs_attention_matches_oracle(H, n_chunk, layer):
           % (H, n_chunk, layer, err, ratio))
 
 
+@pytest.mark.parametrize("H,n_q", [(8, 64), (8, 300), (16, 545), (24, 257), (16, 1100)])
+def test_hs_attention_every_tile_once(H, n_q):
+    """With a head count divisible by the 8 XCDs, each head's query tiles are
+    cut in two halves dealt by run length; counts of 1, 3, 5 and 9 tiles leave
+    the second half one tile short.  Bimodal run lengths (short and long heads
+    in a seeded order, one empty) with the chunk's rows after them; every
+    query of every head is checked, so a tile computed twice into the wrong
+    place or never computed fails."""
+    dev = device()
+    rng = np.random.default_rng(31 * H + n_q)
+    D, n_chunk = 128, 50
+    lens = np.where(rng.permutation(H) < H // 2, 70, 333).astype(np.int64)[None, :]
+    lens[0, int(rng.integers(0, H))] = 0
+    off, kr, vr = _ragged_case(rng, lens, H, D, 8)
+    cap = int(off[-1])
+    kr[cap:] = 0x7FC0
+    vr[cap:] = 0x7FC0
+    q = random_bf16_bits(rng, (n_q, H, D))
+    kc = random_bf16_bits(rng, (n_chunk, H, D))
+    vc = random_bf16_bits(rng, (n_chunk, H, D))
+    od = torch.full((n_q, H, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    scale = 1.0 / np.sqrt(D)
+    dp.dp_hs_attention(bf16_from_bits(q, dev), bf16_from_bits(kr, dev), bf16_from_bits(vr, dev),
+                       cap, torch.from_numpy(off).to(dev), 0, bf16_from_bits(kc, dev),
+                       bf16_from_bits(vc, dev), n_chunk, od, n_q, H, D, dp.DP_BF16, scale)
+    torch.cuda.synchronize()
+    _check_hs(bits(od), q, kr, vr, off, 0, np.arange(n_q), kc, vc, scale, ("tiles", H, n_q))
+
+
 def test_hs_attention_clamps_runs_to_capacity():
     """Offsets past the capacity are clamped: the last heads see fewer rows."""
     dev = device()

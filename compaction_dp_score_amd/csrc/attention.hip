@@ -18,8 +18,8 @@
 //                  the B operand without moving between lanes: the order of the
 //                  contraction over keys is permuted to match, and the V^T
 //                  operand is read in the same order by transposing LDS reads.
-// The MFMAs of the next tile's S^T are issued while the current tile's
-// probabilities are formed.
+// The MFMAs of the next tile's S^T and of the previous tile's O^T update are
+// issued while the current tile's probabilities are formed.
 // Query tiles of one head are placed on one XCD (workgroup i runs on XCD
 // i mod 8), so the key/value tiles they all stream are shared in that XCD's L2;
 // over a ragged cache each half of a head's tiles is placed on one XCD.
@@ -47,6 +47,8 @@
 // addresses the tile loads read from change: each lane fetches the 16-byte
 // chunk that belongs at its LDS position from the piece that holds it, and the
 // tile lands in LDS exactly as for interleaved keys.
+#include <type_traits>
+
 #include "dp_internal.h"
 
 namespace dp {
@@ -77,6 +79,21 @@ template <int MODE> struct Shape {
 constexpr int kBN = 64;          // keys per tile
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor, dword 3
+
+// Placement of one pipeline step's instructions: N groups of one MFMA, one LDS
+// read and three VALU instructions (after eight LDS reads issued first).  The
+// compiler's own order issued the softmax VALU work beside the first half of
+// the MFMAs and left the rest of them without any; this spreads it over all
+// 32 (measured, outputs bit-identical: +1.6 % dense, +2 % on the ragged cache;
+// four or five VALU per MFMA, or 4 or 12 reads first, were slower).
+template <int N> __device__ __forceinline__ void step_schedule() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+    step_schedule<N - 1>();
+  }
+}
 
 
 struct AttnArgs {
@@ -479,14 +496,41 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
   };
 
   // ---- one pass: a software pipeline over rows [0, n_rows) of a range whose
-  // first K and V rows are at kp and vp, `stride` elements apart.  While the
-  // probabilities of tile t are formed the MFMAs of S(t + 1) run; tile t + 2's K
-  // and tile t + 1's V are in flight.  Buffers alternate with the parity of t
-  // (Kb[(t + 1) & 1] holds K(t + 1), Vb[t & 1] holds V(t)); the loop is unrolled
-  // twice so that every buffer and score array is named statically. ----
+  // first K and V rows are at kp and vp, `stride` elements apart.  Step t forms
+  // the probabilities P(t) of tile t while the MFMAs of S(t + 1) and of
+  // O += V(t - 1) P(t - 1) run: the three are independent, so every step holds
+  // 32 MFMAs beside the whole softmax.  Tile t + 2's K and tile t's V are in
+  // flight.  A rescale decided in step t (by the maximum of tile t + 1)
+  // multiplies l at once and O in step t + 1, after tile t's product is added,
+  // so O and l see the operations, and the order, of a loop that adds each
+  // tile's product in its own step.  Buffers alternate with the parity of t
+  // (Kb[(t + 1) & 1] holds K(t + 1), Vb[t & 1] holds V(t), P(t) is p0 or p1);
+  // the first step (no product yet) is peeled and the loop is unrolled twice so
+  // that every buffer and array is named statically. ----
   f32x16 sa[2], sb[2];
-  bf16x8 pt[4];
+  bf16x8 p0[4], p1[4];
   int q_state = -1;                            // query fragments held: -1 none, 0 plain, 1 lagged
+  bool pend = false;                           // O owes a rescale (wave-uniform)
+  float pend_corr = 1.0f;
+  auto update_m_late = [&](float mt) {         // update_m with O's factor deferred
+    if (__builtin_amdgcn_ballot_w64(mt > m + 8.0f)) {
+      const float mn = fmaxf(m, mt);
+      const float corr = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      l *= corr;
+      pend = true;
+      pend_corr = corr;
+    }
+  };
+  auto apply_pend = [&]() {
+    if (pend) {
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= pend_corr;
+      pend = false;
+    }
+  };
   // (planar: K is a ragged run of split keys, kp its temporal piece and kp2 its
   // other-dims piece at the pass's first row; otherwise kp2 is unused)
   auto run_pass = [&](const uint16_t* kp, const uint16_t* kp2, const uint16_t* vp,
@@ -498,46 +542,56 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
     auto tk = [&](int64_t t) { return kp + t * (planar ? kBN * kte : tile_elems); };
     auto tk2 = [&](int64_t t) { return kp2 + t * (planar ? kBN * kse : tile_elems); };
     auto tv = [&](int64_t t) { return vp + t * tile_elems; };
-    auto step = [&](int64_t t, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const lds_u8* k_next,
-                    lds_u8* k_free, const lds_u8* v_cur, lds_u8* v_free) {
-      __builtin_amdgcn_s_waitcnt(0);           // this wavefront's K(t + 1), V(t) have landed
-      lds_barrier();                           // ... everyone's; K(t), V(t - 1) are free
+    auto step = [&](auto with_o, int64_t t, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                    const lds_u8* k_next, lds_u8* k_free, const lds_u8* v_prev, lds_u8* v_free,
+                    const bf16x8 (&p_prev)[4], bf16x8 (&p_cur)[4]) {
+      __builtin_amdgcn_s_waitcnt(0);           // this wavefront's K(t + 1), V(t - 1) have landed
+      lds_barrier();                           // ... everyone's; K(t), V(t - 2) are free
       if (t + 2 < n_tiles)
         load_tile(tk(t + 2), tk2(t + 2), tv(t + 2), st2, n_rows - (t + 2) * kBN, k_free, v_free,
                   true, false, planar);
-      if (t + 1 < n_tiles)
-        load_tile(tk(t + 1), tk2(t + 1), tv(t + 1), st2, n_rows - (t + 1) * kBN, k_free, v_free,
-                  false, true, planar);
+      load_tile(tk(t), tk2(t), tv(t), st2, n_rows - t * kBN, k_free, v_free, false, true, planar);
       s_tile(k_next, s_nxt);     // past the last tile: stale LDS, result unused (keeps
                                  // the MFMAs in the same block as the softmax work)
-      s_exp(s_cur, pt);
+      if constexpr (decltype(with_o)::value) o_tile(v_prev, p_prev);
+      s_exp(s_cur, p_cur);
       float mt = tile_max(s_nxt);  // S(t + 1) as computed; corrected below for a last,
-      o_tile(v_cur, pt);           // partial tile
+                                   // partial tile
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      step_schedule<32>();
+      apply_pend();
       if (t + 1 < n_tiles) {
         const int64_t lim = n_rows - (t + 1) * kBN;
         if (lim < kBN) {
           s_mask(s_nxt, lim);
           mt = tile_max(s_nxt);
         }
-        update_m(mt);
+        update_m_late(mt);
       }
     };
     if (q_state != q_want) {
       load_q(LAG && q_want == 1);
       q_state = q_want;
     }
-    load_tile(tk(0), tk2(0), tv(0), st2, n_rows, kb0, vb0, true, true, planar);
+    load_tile(tk(0), tk2(0), tv(0), st2, n_rows, kb0, vb0, true, false, planar);
     if (n_tiles > 1)
       load_tile(tk(1), tk2(1), tv(1), st2, n_rows - kBN, kb1, vb1, true, false, planar);
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
     s_tile(kb0, sa);
     s_max(sa, n_rows);
-    for (int64_t t = 0; t < n_tiles; t += 2) {
-      step(t, sa, sb, kb1, kb0, vb0, vb1);
-      if (t + 1 < n_tiles) step(t + 1, sb, sa, kb0, kb1, vb1, vb0);
+    using no_o = std::integral_constant<bool, false>;
+    using with_o = std::integral_constant<bool, true>;
+    step(no_o{}, 0, sa, sb, kb1, kb0, vb1, vb0, p1, p0);
+    for (int64_t t = 1; t < n_tiles; t += 2) {
+      step(with_o{}, t, sb, sa, kb0, kb1, vb0, vb1, p0, p1);
+      if (t + 1 < n_tiles) step(with_o{}, t + 1, sa, sb, kb1, kb0, vb1, vb0, p1, p0);
     }
     __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();                             // V(n - 1) has landed everywhere
+    if ((n_tiles - 1) & 1) o_tile(vb1, p1);    // the last tile's product
+    else o_tile(vb0, p0);
+    apply_pend();
     lds_barrier();                             // the next pass reuses the buffers
   };
   if (RAGGED) {

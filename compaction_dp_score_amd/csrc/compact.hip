@@ -5,14 +5,20 @@
 // ascending positions with keep != 0.
 //
 // Three stream-ordered launches, no host synchronisation and no spinning:
-//   1. count:  one workgroup per tile of 4096 rows counts its kept rows;
+//   1. count:  one workgroup per tile of 4096 rows counts its kept rows
+//              (a whole tile at a 16-byte aligned address: one 16-byte load per
+//              thread);
 //   2. scan:   one workgroup turns the tile counts into exclusive offsets and
 //              writes the total to *n_kept;
-//   3. write:  each tile is re-read in 16 rounds of 256 rows; within a round
+//   3. write:  each tile is re-read (into LDS, as the count reads it) and
+//              taken in 16 rounds of 256 rows; within a round
 //              every wavefront takes a ballot of its keep bits and a lane's
 //              slot is the popcount of the ballot below it (mbcnt); the 64
 //              (round, wavefront) counts of the tile get an exclusive prefix in
 //              LDS, so every kept row lands at its final position.
+// Up to kFusedScanTiles tiles (8 M rows) the scan launch is left out: each
+// write workgroup sums the counts of the tiles before it itself (at most 8 per
+// thread) and the last one writes *n_kept.
 #include <mutex>
 
 #include "dp_internal.h"
@@ -23,6 +29,7 @@ namespace {
 constexpr int kRounds = 16;
 constexpr int kTile = kBlock * kRounds;   // 4096 rows per tile
 constexpr int kWaves = kBlock / 64;
+constexpr int64_t kFusedScanTiles = 2048;
 
 __device__ __forceinline__ int block_sum(int v, int* lds) {
   // wave reduction, then across the 4 waves through LDS
@@ -36,15 +43,27 @@ __device__ __forceinline__ int block_sum(int v, int* lds) {
   return total;
 }
 
+// Nonzero bytes of a 32-bit word: a byte's top bit is set in
+// (b & 0x7f) + 0x7f when its low seven bits are not all zero, or in b itself.
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+  return __popc((((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u);
+}
+
 __global__ __launch_bounds__(kBlock) void compact_count_kernel(const uint8_t* __restrict__ keep,
                                                                int64_t T,
                                                                int32_t* __restrict__ counts) {
   __shared__ int lds[kWaves];
   const int64_t base = (int64_t)blockIdx.x * kTile;
   int c = 0;
-  for (int r = 0; r < kRounds; ++r) {
-    int64_t t = base + r * kBlock + threadIdx.x;
-    if (t < T && keep[t] != 0) ++c;
+  if (base + kTile <= T && (((uintptr_t)(keep + base)) & 15u) == 0) {
+    // a whole, aligned tile: 16 consecutive bytes per thread in one load
+    const u32x4 v = reinterpret_cast<const u32x4*>(keep + base)[threadIdx.x];
+    c = nonzero_bytes(v[0]) + nonzero_bytes(v[1]) + nonzero_bytes(v[2]) + nonzero_bytes(v[3]);
+  } else {
+    for (int r = 0; r < kRounds; ++r) {
+      int64_t t = base + r * kBlock + threadIdx.x;
+      if (t < T && keep[t] != 0) ++c;
+    }
   }
   int total = block_sum(c, lds);
   if (threadIdx.x == 0) counts[blockIdx.x] = total;
@@ -82,19 +101,46 @@ __global__ __launch_bounds__(kBlock) void compact_scan_kernel(int32_t* __restric
   if (threadIdx.x == 0) *n_kept = carry_s;
 }
 
+// FUSED_SCAN: `offsets` holds the tile counts; the tile's offset is their sum
+// over the tiles before it, and the last tile writes the total to *n_kept.
+template <bool FUSED_SCAN>
 __global__ __launch_bounds__(kBlock) void compact_write_kernel(
     const uint8_t* __restrict__ keep, int64_t T, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ idx, const int32_t* __restrict__ rf_src, int32_t* __restrict__ rf_dst) {
+    int32_t* __restrict__ idx, const int32_t* __restrict__ rf_src, int32_t* __restrict__ rf_dst,
+    int64_t* __restrict__ n_kept) {
   __shared__ int cnt[kRounds * kWaves];
   __shared__ int pre[kRounds * kWaves];
+  __shared__ int red[kWaves];
   const int64_t base = (int64_t)blockIdx.x * kTile;
   const int lane = threadIdx.x & 63, wave = threadIdx.x / 64;
+  // the tile's keep bytes go through LDS: one 16-byte load per thread for a
+  // whole, aligned tile (byte loads otherwise), issued before the offset sum
+  __shared__ __attribute__((aligned(16))) uint8_t keep_s[kTile];
+  const bool whole = base + kTile <= T && (((uintptr_t)(keep + base)) & 15u) == 0;
+  u32x4 kv = {0u, 0u, 0u, 0u};
+  if (whole) kv = reinterpret_cast<const u32x4*>(keep + base)[threadIdx.x];
+  int tile_before = 0;
+  if (FUSED_SCAN) {
+    int part = 0;
+    for (uint32_t i = threadIdx.x; i < blockIdx.x; i += kBlock) part += offsets[i];
+    tile_before = block_sum(part, red);
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0)
+      *n_kept = (int64_t)tile_before + offsets[blockIdx.x];
+  }
+  if (whole) {
+    reinterpret_cast<u32x4*>(keep_s)[threadIdx.x] = kv;
+  } else {
+    for (int r = 0; r < kRounds; ++r) {
+      const int64_t t = base + r * kBlock + threadIdx.x;
+      keep_s[r * kBlock + threadIdx.x] = t < T ? keep[t] : 0;
+    }
+  }
+  __syncthreads();
   uint64_t ballots[kRounds];
   bool mine[kRounds];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
-    int64_t t = base + r * kBlock + threadIdx.x;
-    mine[r] = t < T && keep[t] != 0;
+    mine[r] = keep_s[r * kBlock + threadIdx.x] != 0;
     ballots[r] = __ballot(mine[r]);
     if (lane == 0) cnt[r * kWaves + wave] = __popcll(ballots[r]);
   }
@@ -109,7 +155,7 @@ __global__ __launch_bounds__(kBlock) void compact_write_kernel(
     pre[lane] = x - v;
   }
   __syncthreads();
-  const int64_t tile_off = offsets[blockIdx.x];
+  const int64_t tile_off = FUSED_SCAN ? (int64_t)tile_before : (int64_t)offsets[blockIdx.x];
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
@@ -133,11 +179,16 @@ dp_status launch_compact(const uint8_t* keep, int64_t T, int32_t* idx, int64_t* 
     dp_status st = check_launch("compact_count_kernel");
     if (st != DP_OK) return st;
   }
+  if (n_tiles > 0 && n_tiles <= kFusedScanTiles) {
+    hipLaunchKernelGGL(compact_write_kernel<true>, dim3((uint32_t)n_tiles), dim3(kBlock), 0, s,
+                       keep, T, ws, idx, rf_src, rf_dst, n_kept);
+    return check_launch("compact_write_kernel");
+  }
   hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(kBlock), 0, s, ws, n_tiles, n_kept);
   dp_status st = check_launch("compact_scan_kernel");
   if (st != DP_OK || n_tiles == 0) return st;
-  hipLaunchKernelGGL(compact_write_kernel, dim3((uint32_t)n_tiles), dim3(kBlock), 0, s, keep, T,
-                     ws, idx, rf_src, rf_dst);
+  hipLaunchKernelGGL(compact_write_kernel<false>, dim3((uint32_t)n_tiles), dim3(kBlock), 0, s,
+                     keep, T, ws, idx, rf_src, rf_dst, n_kept);
   return check_launch("compact_write_kernel");
 }
 

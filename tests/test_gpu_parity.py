@@ -112,6 +112,32 @@ def test_compact_index_matches_oracle(T, rate):
     assert np.array_equal(rf_out[:n].cpu().numpy(), oracle.gather_i32(rf, want))
 
 
+@pytest.mark.parametrize("T,offset", [(3 * 4096 + 77, 16), (3 * 4096 + 77, 5), (4096, 0),
+                                      (2048 * 4096, 0), (2050 * 4096 - 3, 7)])
+def test_compact_index_byte_values_and_alignment(T, offset):
+    """Kept bytes of every kind (1, 3, 127, 128, 255) at a keep address that is
+    16-byte aligned or not; tile counts on both sides of the count at which the
+    tile offsets are summed by the write launch itself (2,048 tiles of 4,096
+    rows) instead of a separate scan launch."""
+    dev = device()
+    rng = np.random.default_rng(T + offset)
+    keep = np.zeros(T, np.uint8)
+    pick = rng.random(T) < 0.3
+    keep[pick] = rng.choice(np.array([1, 3, 127, 128, 255], np.uint8), int(pick.sum()))
+    buf = torch.zeros(T + 32, dtype=torch.uint8, device=dev)
+    buf[offset:offset + T] = to_dev(keep, dev)
+    idx = torch.full((T,), -1, dtype=torch.int32, device=dev)
+    n_kept = torch.full((1,), -5, dtype=torch.int64, device=dev)
+    ws = torch.empty(dp.dp_compact_workspace_bytes(T) // 4, dtype=torch.int32, device=dev)
+    dp.dp_compact_index(buf[offset:], T, idx, n_kept, None, None, ws)
+    torch.cuda.synchronize()
+    want = oracle.compact(keep)
+    n = int(n_kept.item())
+    assert n == want.shape[0]
+    assert np.array_equal(idx[:n].cpu().numpy(), want)
+    assert np.all(idx[n:].cpu().numpy() == -1)
+
+
 def test_compact_index_empty_sequence():
     dev = device()
     n_kept = torch.full((1,), -5, dtype=torch.int64, device=dev)

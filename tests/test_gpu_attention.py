@@ -234,11 +234,13 @@ def test_hs_attention_matches_oracle(H, n_chunk, layer):
           % (H, n_chunk, layer, err, ratio))
 
 
-@pytest.mark.parametrize("H,n_q", [(8, 64), (8, 300), (16, 545), (24, 257), (16, 1100)])
+@pytest.mark.parametrize("H,n_q", [(8, 64), (8, 300), (16, 545), (24, 257), (16, 1100),
+                                   (256, 200), (264, 130)])
 def test_hs_attention_every_tile_once(H, n_q):
     """With a head count divisible by the 8 XCDs, each head's query tiles are
     cut in two halves dealt by run length; counts of 1, 3, 5 and 9 tiles leave
-    the second half one tile short.  Bimodal run lengths (short and long heads
+    the second half one tile short; 256 heads is the most the workgroup ranks,
+    264 takes whole heads in head order.  Bimodal run lengths (short and long heads
     in a seeded order, one empty) with the chunk's rows after them; every
     query of every head is checked, so a tile computed twice into the wrong
     place or never computed fails."""

@@ -85,13 +85,16 @@ constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor, dword 
 // compiler's own order issued the softmax VALU work beside the first half of
 // the MFMAs and left the rest of them without any; this spreads it over all
 // 32 (measured, outputs bit-identical: +1.6 % dense, +2 % on the ragged cache;
-// four or five VALU per MFMA, or 4 or 12 reads first, were slower).
-template <int N> __device__ __forceinline__ void step_schedule() {
+// four or five VALU per MFMA, or 4 or 12 reads first, were slower).  SALU: one
+// scalar instruction per group as well, which the ragged kernel (4 wavefronts)
+// gained 0-2 % from in two comparisons and the dense one lost 0.4 %.
+template <int N, bool SALU> __device__ __forceinline__ void step_schedule() {
   if constexpr (N > 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
-    step_schedule<N - 1>();
+    if constexpr (SALU) __builtin_amdgcn_sched_group_barrier(0x004, 1, 0);   // SALU
+    step_schedule<N - 1, SALU>();
   }
 }
 
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(Shape<MODE>::kBlock) __attribute__((amdgpu_waves_pe
       float mt = tile_max(s_nxt);  // S(t + 1) as computed; corrected below for a last,
                                    // partial tile
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      step_schedule<32>();
+      step_schedule<32, RAGGED>();
       apply_pend();
       if (t + 1 < n_tiles) {
         const int64_t lim = n_rows - (t + 1) * kBN;
